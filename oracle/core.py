@@ -1,0 +1,217 @@
+"""Per-group definitions of the sparse decode path, in fp64 NumPy (test infrastructure only).
+
+Conventions: a "group" is one (batch, KV head) pair.  Keys and values of a group
+are ``[n, d]`` arrays; query vectors are ``[m, d]``.  All arithmetic is fp64 on
+the exact values of the (fp32 or bf16) inputs.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------- inputs
+
+def decode_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact fp64 values: a bf16 is the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def to_f64(x) -> np.ndarray:
+    """Exact fp64 copy of a float array, or of bf16 bit patterns given as uint16."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return decode_bf16(x)
+    return x.astype(np.float64)
+
+
+# --------------------------------------------------------------------------- a0 / a1
+
+def block_pool(keys, block_size: int) -> np.ndarray:
+    """Mean of the keys of each complete block of ``block_size`` consecutive tokens.
+
+    SparDA, "Estratégia de Treinamento": the indexer scores keys compressed on a
+    block grid.  Reading taken: non-overlapping windows (kernel = stride =
+    block_size), mean pooling, only complete blocks.  Returns ``[n // bs, d]``.
+    """
+    k = to_f64(keys)
+    nb = k.shape[0] // block_size
+    return k[: nb * block_size].reshape(nb, block_size, k.shape[1]).mean(axis=1)
+
+
+def scores_token_group_mean(q_group, keys) -> np.ndarray:
+    """Token score of one GQA group: the mean over the group's query heads of q_h·k_j.
+
+    SparDA §2 "Indexador de Previsão Compacto": one score per GQA group instead of
+    a scoring loop per query head, and no softmax.  ``q_group`` is ``[G, d]``,
+    ``keys`` ``[n, d]``; returns ``[n]``.  Unscaled dot products.
+    """
+    q = to_f64(q_group)
+    k = to_f64(keys)
+    per_head = k @ q.T                      # [n, G]
+    return per_head.mean(axis=1)
+
+
+def scores_token_per_head(q_group, keys) -> np.ndarray:
+    """Per-query-head token scores q_h·k_j, ``[G, n]``.
+
+    "Esparsidade de Contexto ...", §2 "Oracle Top-K": exact scores of every token,
+    selected independently per query head (per-head sparsity patterns).
+    """
+    q = to_f64(q_group)
+    k = to_f64(keys)
+    return q @ k.T
+
+
+def scores_block(pred, kpool) -> np.ndarray:
+    """Block scores p·Kpool_j of one predictor vector (no softmax), ``[nb]``.
+
+    SparDA §2 "Indexador de Previsão Compacto" (one predictor head per GQA group)
+    and "Seleção Esparsa de Lookahead Treinável" (the predictor ranks KV blocks).
+    """
+    return to_f64(kpool) @ to_f64(pred)
+
+
+# --------------------------------------------------------------------------- a2
+
+def topk(x, k: int) -> np.ndarray:
+    """Exact top-k of a score row: the k largest scores, ties to the lowest index.
+
+    "Esparsidade de Contexto ...", §2 "Oracle Top-K" (exact top-k); the tie rule
+    and the ascending output order are this library's definition.  A stable sort
+    of -x keeps equal scores in index order; -0 and +0 compare equal; NaN sorts
+    after every number (NumPy puts NaN last).  k > n returns all n; k <= 0 none.
+    Returns the chosen indices in ascending order (int64).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[0]
+    k = max(0, min(int(k), n))
+    order = np.argsort(-x, kind="stable")
+    return np.sort(order[:k])
+
+
+# --------------------------------------------------------------------------- a3
+
+def selection_tokens(sel, granularity: int, n_tokens: int, n_sink: int = 0,
+                     n_recent: int = 0) -> np.ndarray:
+    """Token ids one selection row makes an attention query read, ascending and unique.
+
+    SparDA: selected blocks expand to their tokens; "Nem Todos os Pensamentos ...",
+    §1: attention sinks and the recent window are always kept.  Reading taken: the
+    union of the expanded selection with the first ``n_sink`` and the last
+    ``n_recent`` tokens, deduplicated.  Entries outside [0, n_tokens) are dropped.
+    """
+    toks = set()
+    for s in np.asarray(sel, dtype=np.int64).ravel():
+        for t in range(int(s) * granularity, int(s) * granularity + granularity):
+            if 0 <= t < n_tokens:
+                toks.add(t)
+    toks.update(range(0, min(n_sink, n_tokens)))
+    toks.update(range(max(0, n_tokens - n_recent), n_tokens))
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+# --------------------------------------------------------------------------- a4 / a5
+
+def attend(q_vecs, keys_sel, vals_sel, sm_scale: float):
+    """Exact softmax attention of each query vector over the gathered rows only.
+
+    "Esparsidade de Contexto ...", §3C: sparse decoding reads O(k·d) instead of
+    O(N·d) and the result is ordinary attention restricted to the selection.
+    o = softmax(sm_scale · q·K_Sᵀ) · V_S, computed textbook-style (max-shifted).
+
+    ``q_vecs`` ``[m, d]``; ``keys_sel``/``vals_sel`` ``[r, d]``.  Returns
+    (out ``[m, d]``, lse ``[m]`` natural-log sum-exp of the scaled logits,
+    logits ``[m, r]`` scaled).  With r = 0 the output is 0 and lse = -inf.
+    """
+    q = to_f64(q_vecs)
+    k = to_f64(keys_sel)
+    v = to_f64(vals_sel)
+    m = q.shape[0]
+    if k.shape[0] == 0:
+        return np.zeros((m, v.shape[1])), np.full(m, -np.inf), np.zeros((m, 0))
+    logits = sm_scale * (q @ k.T)                       # [m, r]
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    z = e.sum(axis=1, keepdims=True)
+    p = e / z
+    out = p @ v
+    lse = (mx + np.log(z))[:, 0]
+    return out, lse, logits
+
+
+# --------------------------------------------------------------------------- a6
+
+def importance_update(s_prev, alpha) -> np.ndarray:
+    """One step of cumulative attention importance.
+
+    "Nem Todos os Pensamentos Necessitam de HBM", §2 "Pontuação de Importância":
+    s_i(t) = s_i(t-1) + (1/|L|) Σ_ℓ (1/H) Σ_h α_ℓ,h(t)[i].
+
+    ``s_prev`` ``[n]`` (the fp32 state), ``alpha`` ``[L, H, n]`` attention
+    probabilities of this step (0 for rows not attended).  The increment is
+    formed in fp64 and the state is stored back as fp32.
+    """
+    a = np.asarray(alpha, dtype=np.float64)
+    L, H = a.shape[0], a.shape[1]
+    delta = np.zeros(a.shape[2])
+    for l in range(L):
+        delta += a[l].sum(axis=0) / H
+    delta /= L
+    return (np.asarray(s_prev, dtype=np.float64) + delta).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- a7
+
+def tier_classify(s, n_tokens: int, n_sink: int, n_recent: int, t0_permille: int = 250,
+                  t01_permille: int = 750, evicted=None):
+    """Four-tier classification by cumulative importance (T2 not used).
+
+    "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro
+    Níveis": protected tokens (attention sinks, recent window) and the most
+    important tokens stay in T0; middle importance goes to T1 (full precision,
+    fetched before attention); only the least important tail goes to T3
+    (evicted for good).  Readings taken:
+
+    * protected = tokens [0, n_sink) and [n_tokens - n_recent, n_tokens) -> T0;
+    * the M other tokens are ranked by (not evicted first, s descending, index
+      ascending); rank < floor(M·t0/1000) -> T0, rank < floor(M·t01/1000) -> T1,
+      every other token -> T3;
+    * an evicted token stays T3 whatever its rank (eviction is permanent).
+
+    Returns (tier ``[n_tokens]`` uint8 with 0/1/3, ascending int64 list of T0∪T1).
+    """
+    s = np.asarray(s, dtype=np.float64)[:n_tokens]
+    ev = np.zeros(n_tokens, dtype=bool) if evicted is None else \
+        np.asarray(evicted, dtype=bool)[:n_tokens]
+    prot = np.zeros(n_tokens, dtype=bool)
+    prot[: min(n_sink, n_tokens)] = True
+    prot[max(0, n_tokens - n_recent):] = True
+    tier = np.full(n_tokens, 3, dtype=np.uint8)
+    tier[prot] = 0
+    cand = np.nonzero(~prot)[0]
+    M = cand.shape[0]
+    n0 = (M * t0_permille) // 1000
+    n01 = (M * t01_permille) // 1000
+    # sort key: live before evicted, then larger s, then lower index.  A NaN score
+    # ranks with the evicted rows (after every number), by index.
+    def key(i):
+        last = bool(ev[i]) or bool(np.isnan(s[i]))
+        return (last, 0.0 if last else -s[i], i)
+    order = sorted(cand.tolist(), key=key)
+    for r, i in enumerate(order):
+        if ev[i]:
+            continue
+        if r < n0:
+            tier[i] = 0
+        elif r < n01:
+            tier[i] = 1
+    lst = np.nonzero(tier <= 1)[0].astype(np.int64)
+    return tier, lst
+
+
+def softmax_scale(d: int) -> float:
+    """Softmax temperature 1/sqrt(d) (the pages do not state one; the usual choice)."""
+    return 1.0 / math.sqrt(d)

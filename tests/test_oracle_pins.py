@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle to things other than itself: closed forms, invariants, brute
+force on tiny inputs and an independent library routine.  CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import steps
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+# ------------------------------------------------------------------ attention
+
+def _sdpa(q, k, v, scale):
+    """torch's own attention routine, fp64 on the CPU (independent of the oracle)."""
+    qt = torch.tensor(q, dtype=torch.float64)[None, :, None, :]      # [1, m, 1, d]
+    kt = torch.tensor(k, dtype=torch.float64)[None, None].expand(1, q.shape[0], *k.shape)
+    vt = torch.tensor(v, dtype=torch.float64)[None, None].expand(1, q.shape[0], *v.shape)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous(),
+                                                         scale=scale)
+    return o[0, :, 0].numpy()
+
+
+@pytest.mark.parametrize("m,r,d", [(4, 1, 8), (4, 37, 64), (7, 200, 128), (1, 5, 16)])
+def test_attend_matches_library_sdpa(m, r, d):
+    q = rng.standard_normal((m, d))
+    k = rng.standard_normal((r, d))
+    v = rng.standard_normal((r, d))
+    scale = 1 / math.sqrt(d)
+    out, lse, logits = oracle.attend(q, k, v, scale)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, scale), rtol=1e-12, atol=1e-12)
+    # lse is log Σ exp(logits); logits are the scaled dot products
+    np.testing.assert_allclose(logits, scale * (q @ k.T), rtol=1e-12)
+    ref_lse = torch.logsumexp(torch.tensor(logits), dim=1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12)
+
+
+def test_attend_identical_keys_is_mean_of_values():
+    d, r = 32, 9
+    k = np.tile(rng.standard_normal(d), (r, 1))
+    v = rng.standard_normal((r, d))
+    q = rng.standard_normal((3, d))
+    out, lse, _ = oracle.attend(q, k, v, 0.3)
+    np.testing.assert_allclose(out, np.tile(v.mean(axis=0), (3, 1)), rtol=1e-12)
+    np.testing.assert_allclose(lse, 0.3 * (q @ k[0]) + math.log(r), rtol=1e-12)
+
+
+def test_attend_dominant_key_returns_its_value():
+    d = 16
+    k = np.zeros((5, d))
+    k[3, 0] = 1000.0
+    v = rng.standard_normal((5, d))
+    q = np.zeros((1, d))
+    q[0, 0] = 1.0
+    out, _, _ = oracle.attend(q, k, v, 1.0)
+    np.testing.assert_allclose(out[0], v[3], rtol=1e-12, atol=1e-300)
+
+
+def test_attend_row_order_is_irrelevant_and_empty_set():
+    q = rng.standard_normal((2, 8))
+    k = rng.standard_normal((6, 8))
+    v = rng.standard_normal((6, 8))
+    p = rng.permutation(6)
+    a, la, _ = oracle.attend(q, k, v, 0.5)
+    b, lb, _ = oracle.attend(q, k[p], v[p], 0.5)
+    np.testing.assert_allclose(a, b, rtol=1e-13)
+    np.testing.assert_allclose(la, lb, rtol=1e-13)
+    o, l, lg = oracle.attend(q, k[:0], v[:0], 0.5)
+    assert np.all(o == 0) and np.all(np.isneginf(l)) and lg.shape == (2, 0)
+
+
+# ------------------------------------------------------------------ top-k
+
+def _brute_topk(x, k):
+    """Element i is chosen iff fewer than k elements beat it; j beats i when x_j > x_i,
+    or x_j == x_i and j < i.  NaN is beaten by every number and by earlier NaNs."""
+    n = len(x)
+
+    def beats(j, i):
+        xi, xj = x[i], x[j]
+        if math.isnan(xj) and math.isnan(xi):
+            return j < i
+        if math.isnan(xj):
+            return False
+        if math.isnan(xi):
+            return True
+        return xj > xi or (xj == xi and j < i)
+
+    return [i for i in range(n) if sum(beats(j, i) for j in range(n) if j != i) < k]
+
+
+@pytest.mark.parametrize("trial", range(40))
+def test_topk_brute_force_with_ties(trial):
+    r = np.random.default_rng(trial)
+    n = int(r.integers(1, 40))
+    x = r.integers(-3, 4, size=n).astype(np.float64)          # many ties
+    if trial % 4 == 1:
+        x = r.standard_normal(n)
+    if trial % 4 == 2:
+        x[r.integers(0, n, size=max(1, n // 4))] = -0.0
+        x[r.integers(0, n, size=max(1, n // 5))] = 0.0
+    if trial % 4 == 3:
+        x[r.integers(0, n, size=max(1, n // 6))] = np.inf
+        x[r.integers(0, n, size=max(1, n // 6))] = -np.inf
+        x[r.integers(0, n, size=max(1, n // 8))] = np.nan
+    for k in {0, 1, max(0, n - 1), n, n + 5, n // 2}:
+        got = oracle.topk(x, k).tolist()
+        assert got == _brute_topk(list(x), k), (x, k)
+
+
+def test_topk_adversarial_ties_and_order():
+    assert oracle.topk(np.zeros(10), 3).tolist() == [0, 1, 2]
+    assert oracle.topk(np.array([-0.0, 0.0, -0.0]), 1).tolist() == [0]
+    assert oracle.topk(np.array([1.0, np.nan, 5.0, -np.inf]), 3).tolist() == [0, 2, 3]
+    assert oracle.topk(np.array([2.0, 9.0, 9.0, 1.0, 9.0]), 2).tolist() == [1, 2]
+    out = oracle.topk(rng.standard_normal(100), 17)
+    assert np.all(np.diff(out) > 0) and len(out) == 17
+
+
+# ------------------------------------------------------------------ index scores
+
+def test_token_scores_one_hot_queries_pick_coordinates():
+    d, n, G = 16, 50, 4
+    keys = rng.standard_normal((n, d))
+    q = np.zeros((G, d))
+    for h in range(G):
+        q[h, h * 3] = 1.0
+    ph = oracle.scores_token_per_head(q, keys)
+    for h in range(G):
+        np.testing.assert_array_equal(ph[h], keys[:, h * 3])
+    gm = oracle.scores_token_group_mean(q, keys)
+    np.testing.assert_allclose(gm, keys[:, [0, 3, 6, 9]].sum(axis=1) / 4, rtol=1e-15)
+    # identical heads: the group mean equals the single head's score
+    q2 = np.tile(rng.standard_normal(d), (G, 1))
+    np.testing.assert_allclose(oracle.scores_token_group_mean(q2, keys),
+                               oracle.scores_token_per_head(q2[:1], keys)[0], rtol=1e-13)
+
+
+def test_block_pool_constant_blocks_and_tail():
+    d, bs = 8, 4
+    rows = rng.standard_normal((3, d))
+    keys = np.concatenate([np.tile(rows[i], (bs, 1)) for i in range(3)] + [rng.standard_normal((3, d))])
+    kp = oracle.block_pool(keys, bs)
+    assert kp.shape == (3, d)                       # the incomplete tail block is not pooled
+    np.testing.assert_allclose(kp, rows, rtol=1e-15)
+    # one-hot predictor reads one coordinate of the pooled keys
+    p = np.zeros(d)
+    p[5] = 1.0
+    np.testing.assert_allclose(oracle.scores_block(p, kp), rows[:, 5], rtol=1e-15)
+
+
+def test_block_score_linearity_matches_token_scores():
+    d, bs, nb = 32, 64, 10
+    keys = rng.standard_normal((nb * bs + 17, d))
+    p = rng.standard_normal(d)
+    blk = oracle.scores_block(p, oracle.block_pool(keys, bs))
+    tok = oracle.scores_token_per_head(p[None], keys)[0][: nb * bs].reshape(nb, bs).mean(axis=1)
+    np.testing.assert_allclose(blk, tok, rtol=1e-12)
+
+
+def test_bf16_decode_is_exact():
+    vals = np.array([1.0, -2.5, 0.0, -0.0, 3.140625, np.inf, 1e-38], dtype=np.float32)
+    t = torch.tensor(vals).to(torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.decode_bf16(bits), t.to(torch.float64).numpy())
+
+
+# ------------------------------------------------------------------ selection assembly
+
+def test_selection_tokens_hand_example():
+    # blocks 0 and 5 of size 4 in 30 tokens, 2 sinks, 3 recent:
+    # block 0 -> 0..3 (covers the sinks), block 5 -> 20..23, recent -> 27, 28, 29
+    got = oracle.selection_tokens([0, 5], 4, 30, n_sink=2, n_recent=3).tolist()
+    assert got == [0, 1, 2, 3, 20, 21, 22, 23, 27, 28, 29]
+    # block 7 covers 28..31, clipped at 30; out-of-range ids are dropped
+    got = oracle.selection_tokens([7, 99, -1], 4, 30, n_sink=1, n_recent=3).tolist()
+    assert got == [0, 27, 28, 29]
+
+
+def test_selection_size_bounds():
+    n, bs, k = 32768, 64, 32
+    for trial in range(5):
+        blocks = np.sort(np.random.default_rng(trial).choice(n // bs, k, replace=False))
+        toks = oracle.selection_tokens(blocks, bs, n, 4, 512)
+        assert k * bs <= len(toks) <= k * bs + 4 + 512
+        assert np.all(np.diff(toks) > 0)
+
+
+# ------------------------------------------------------------------ importance
+
+def test_importance_hand_example():
+    # L = 2 layers, H = 2 heads, 3 tokens, previous s = (0.5, 0, 0.25):
+    # layer 0: heads (1, 0, 0), (0.5, 0.5, 0) -> head mean (0.75, 0.25, 0)
+    # layer 1: heads (0, 0, 1), (0.25, 0.25, 0.5) -> head mean (0.125, 0.125, 0.75)
+    # layer mean (0.4375, 0.1875, 0.375); s = (0.9375, 0.1875, 0.625)
+    alpha = np.array([[[1, 0, 0], [0.5, 0.5, 0]], [[0, 0, 1], [0.25, 0.25, 0.5]]])
+    s = oracle.importance_update(np.array([0.5, 0, 0.25], np.float32), alpha)
+    assert s.dtype == np.float32
+    assert s.tolist() == [0.9375, 0.1875, 0.625]
+
+
+def test_importance_conservation_and_identical_keys_closed_form():
+    n, L, H, d = 40, 3, 4, 16
+    s = np.zeros(n, np.float32)
+    expect = [Fraction(0)] * n
+    key = rng.standard_normal(d)
+    for t in range(6):
+        sel = np.sort(rng.choice(n, size=5 + 3 * t, replace=False))
+        alpha = np.zeros((L, H, n))
+        for l in range(L):
+            for h in range(H):
+                q = rng.standard_normal((1, d))
+                _, lse, lg = oracle.attend(q, np.tile(key, (len(sel), 1)), np.zeros((len(sel), d)), 0.1)
+                alpha[l, h, sel] = np.exp(lg[0] - lse[0])
+        s = oracle.importance_update(s, alpha)
+        for i in sel:
+            expect[i] += Fraction(1, len(sel))
+        # each step adds exactly one unit of attention mass in total
+        assert abs(float(s.astype(np.float64).sum()) - (t + 1)) < 1e-5
+    np.testing.assert_allclose(s, [float(e) for e in expect], rtol=1e-6)
+
+
+# ------------------------------------------------------------------ tiers
+
+def _brute_tiers(s, n, n_sink, n_recent, p0, p01, ev):
+    prot = [i < n_sink or i >= n - n_recent for i in range(n)]
+    cand = [i for i in range(n) if not prot[i]]
+    M = len(cand)
+    n0, n01 = M * p0 // 1000, M * p01 // 1000
+
+    def before(j, i):  # j ranks ahead of i
+        if ev[j] != ev[i]:
+            return not ev[j]
+        if ev[j]:
+            return j < i
+        return s[j] > s[i] or (s[j] == s[i] and j < i)
+
+    tier = []
+    for i in range(n):
+        if prot[i]:
+            tier.append(0)
+            continue
+        r = sum(before(j, i) for j in cand if j != i)
+        if ev[i] or r >= n01:
+            tier.append(3)
+        else:
+            tier.append(0 if r < n0 else 1)
+    return tier
+
+
+@pytest.mark.parametrize("trial", range(30))
+def test_tiers_brute_force(trial):
+    r = np.random.default_rng(100 + trial)
+    n = int(r.integers(0, 60))
+    n_sink, n_recent = int(r.integers(0, 5)), int(r.integers(0, 12))
+    s = r.integers(0, 6, size=n).astype(np.float32) / 4          # ties on purpose
+    ev = r.random(n) < (0.3 if trial % 2 else 0.0)
+    p0, p01 = [(250, 750), (100, 900), (0, 1000), (500, 500)][trial % 4]
+    tier, lst = oracle.tier_classify(s, n, n_sink, n_recent, p0, p01, ev)
+    assert tier.tolist() == _brute_tiers(list(s), n, n_sink, n_recent, p0, p01, list(ev))
+    assert lst.tolist() == [i for i in range(n) if tier[i] <= 1]
+
+
+def test_tier_invariants_reasoning_shape():
+    n, ns, nr = 16384, 4, 512
+    s = rng.random(n).astype(np.float32)
+    tier, lst = oracle.tier_classify(s, n, ns, nr, 250, 750)
+    M = n - ns - nr
+    prot = np.zeros(n, bool)
+    prot[:ns] = prot[n - nr:] = True
+    assert np.all(tier[prot] == 0)
+    assert (tier[~prot] == 0).sum() == M // 4
+    assert (tier[~prot] == 1).sum() == 3 * M // 4 - M // 4
+    assert len(lst) == ns + nr + 3 * M // 4
+    assert s[~prot & (tier == 0)].min() >= s[tier == 1].max() >= s[tier == 3].max()
+
+
+def test_tier_hand_example_and_sticky_eviction():
+    # 12 tokens, 1 sink, 2 recent -> M = 9 candidates (1..9); quotas 25%/75% -> 2 and 6.
+    s = np.array([0, 5, 1, 7, 3, 3, 0, 2, 9, 4, 0, 0], np.float32)
+    # ranking of 1..9 by (s desc, index asc): 8(9) 3(7) 1(5) 9(4) 4(3) 5(3) 7(2) 2(1) 6(0)
+    tier, lst = oracle.tier_classify(s, 12, 1, 2, 250, 750)
+    assert tier.tolist() == [0, 1, 3, 0, 1, 1, 3, 3, 0, 1, 0, 0]
+    assert lst.tolist() == [0, 1, 3, 4, 5, 8, 9, 10, 11]
+    # token 8 evicted earlier: it stays T3 and drops to the bottom of the ranking
+    ev = np.zeros(12, bool)
+    ev[8] = True
+    tier, _ = oracle.tier_classify(s, 12, 1, 2, 250, 750, ev)
+    assert tier.tolist() == [0, 0, 3, 0, 1, 1, 3, 1, 3, 1, 0, 0]
+
+
+# ------------------------------------------------------------------ composite steps reduce to dense
+
+def _dense(q, k, v, scale):
+    return _sdpa(q, k, v, scale)
+
+
+def test_steps_with_everything_selected_equal_dense_attention():
+    d, n, G = 32, 256, 4
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    q = rng.standard_normal((G, d))
+    scale = oracle.softmax_scale(d)
+    dense = _dense(q, k, v, scale)
+    r = steps.group_mean_group(q[None], k, v, n, scale)
+    np.testing.assert_allclose(r["out"][0], dense, rtol=1e-11)
+    r = steps.per_head_group(q, k, v, n, scale)
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-11)
+    r = steps.block_group(rng.standard_normal(d), k, v, q, n // 64, 64, 0, 0, scale)
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-11)
+
+
+def test_block_step_forced_rows_and_counts():
+    d, n, bs = 16, 64 * 20 + 10, 64
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    r = steps.block_group(rng.standard_normal(d), k, v, rng.standard_normal((4, d)), 3, bs, 4, 100,
+                          0.25)
+    toks = set(r["tokens"].tolist())
+    assert set(range(4)) <= toks and set(range(n - 100, n)) <= toks
+    for b in r["blocks"]:
+        assert set(range(b * bs, b * bs + bs)) <= toks
+    assert len(r["blocks"]) == 3
+
+
+def test_tiered_step_dense_first_step_conserves_mass():
+    L, Hq, Hkv, d, n = 3, 8, 2, 16, 700
+    q = rng.standard_normal((L, Hq, d))
+    k = rng.standard_normal((L, Hkv, n, d))
+    v = rng.standard_normal((L, Hkv, n, d))
+    r = steps.tiered_sequence_step(np.zeros(n, np.float32), None, q, k, v, n, 0.25, 4, 64, dense=True)
+    assert abs(float(r["s"].astype(np.float64).sum()) - 1.0) < 1e-5
+    for l in range(L):
+        for h in range(Hq):
+            np.testing.assert_allclose(r["out"][l, h], _dense(q[l, h:h + 1], k[l, h // 4], v[l, h // 4], 0.25)[0],
+                                       rtol=1e-11)
+    r2 = steps.tiered_sequence_step(r["s"], r["evicted"], q, k, v, n, 0.25, 4, 64)
+    M = n - 68
+    assert len(r2["tokens"]) == 68 + 3 * M // 4
+    assert abs(float(r2["s"].astype(np.float64).sum()) - 2.0) < 1e-5
+    assert np.all(r2["s"][r2["tier"] == 3] == r["s"][r2["tier"] == 3])
+
+
+# ------------------------------------------------------------------ sizes printed on the pages
+
+def test_page_figures():
+    fig = json.load(open(os.path.join(GOLDEN, "page_figures.json")))
+    dens = fig["oracle_topk_density"]["value"]
+    assert math.ceil(dens * 131072) == 2622
+    assert 32 * 64 == 2048
+    kv = fig["kv_bytes_reasoning_chain"]
+    assert abs(kv["tokens"] * 28 * 28 * 128 * 2 * 2 - kv["value_bytes_approx"]) / kv["value_bytes_approx"] < 0.01
+    assert fig["tier_reassignment_period"]["value"] == 64
