@@ -1,0 +1,245 @@
+/*
+ * spk.h — C ABI of libspk: sparse top-k KV decode attention with GQA on AMD MI355X (gfx950).
+ *
+ * One decode step over a long KV cache reads only a chosen part of it:
+ *   sparse_index_score   a compact indexer scores cached keys (or pooled block keys), no softmax
+ *   topk_select          exact top-k of each score row, ties to the lowest index
+ *   sparse_decode_attn   gathers the chosen K/V rows once per GQA group (HBM or pinned host
+ *                        memory) and runs exact softmax attention over them only
+ *   importance_accumulate  cumulative attention importance s_i += mean over layers, heads of α[i]
+ *   tier_classify        T0/T1/T3 tiers by importance, sinks and recent window protected
+ *
+ * Conventions shared by every call
+ *   - Tensors are row-major with a contiguous last dimension; strides and leading dimensions
+ *     are in ELEMENTS of the tensor's own type.  "Device" pointers are HIP device memory (or
+ *     device-mapped pinned host memory where stated); "host" pointers are ordinary CPU memory.
+ *   - Shapes: B batch, T query tokens per sequence, Hq query heads, Hkv KV heads (Hq % Hkv == 0,
+ *     G = Hq / Hkv), d head dim (64 or 128), n_tokens cached tokens.  Query head h belongs to
+ *     KV head h / G.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns; nothing synchronises the host.  Faults during execution surface as HIP errors
+ *     at the caller's next synchronisation.
+ *   - Ownership: the caller owns every buffer (inputs, outputs, workspace, host pools).  The
+ *     library never allocates or frees memory and keeps no state between calls except a cached
+ *     per-device property table; calls are re-entrant and may run on concurrent streams when
+ *     their output buffers and workspaces are distinct.
+ *   - Errors: arguments are validated before any launch; on a non-OK return nothing was
+ *     launched and nothing was written, and spk_last_error() (thread-local) says why.
+ *       SPK_EINVAL       null required pointer, inconsistent shapes, bad strides or sizes
+ *       SPK_EUNSUPPORTED d not in {64, 128}, or a dtype combination without a kernel
+ *       SPK_EWORKSPACE   workspace smaller than the *_workspace_size query asks for
+ *       SPK_EHIP         a HIP launch failed (text in spk_last_error())
+ *   - Index entries that fall outside the valid range are skipped (never dereferenced).
+ */
+#ifndef SPK_H
+#define SPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SPK_API __attribute__((visibility("default")))
+#else
+#define SPK_API
+#endif
+
+typedef enum {
+  SPK_OK = 0,
+  SPK_EINVAL = 1,
+  SPK_EUNSUPPORTED = 2,
+  SPK_EWORKSPACE = 3,
+  SPK_EHIP = 4
+} spk_status;
+
+typedef enum { SPK_F32 = 0, SPK_BF16 = 1 } spk_dtype;
+
+typedef enum {
+  SPK_IDX_TOKEN_GROUP_MEAN = 0, /* score[b,t,kvh,j] = mean over the G heads of kvh of q[b,t,h]·k[b,kvh,j] */
+  SPK_IDX_TOKEN_PER_HEAD = 1,   /* score[b,t,h,j]   = q[b,t,h]·k[b,h/G,j]                               */
+  SPK_IDX_BLOCK_POOLED = 2,     /* score[b,t,kvh,j] = p[b,t,kvh]·Kpool[b,kvh,j]  (pooled keys given)     */
+  SPK_IDX_BLOCK_RAW = 3         /* same, pooling raw keys on the fly (optionally writing Kpool)        */
+} spk_index_mode;
+
+typedef enum {
+  SPK_SEL_PER_SEQ = 0,     /* one list per sequence b, read by every query vector of b            */
+  SPK_SEL_PER_KV_HEAD = 1, /* one list per (b, t, kvh), read by the G heads of kvh at token t      */
+  SPK_SEL_PER_Q_HEAD = 2   /* one list per (b, t, h), read by query head h at token t only         */
+} spk_sel_scope;
+
+/* Thread-local text describing the last non-OK status returned on this thread ("" if none). */
+SPK_API const char* spk_last_error(void);
+
+/* ABI version of this header (bumped on any incompatible change). */
+SPK_API int spk_version(void);
+#define SPK_VERSION 1
+
+/* ------------------------------------------------------------------------------------------
+ * sparse_index_score — compact indexer scores, no softmax.
+ *
+ * Passages: SparDA: Atenção Esparsa Desacoplada, §2 "Indexador de Previsão Compacto" (one
+ * predictor head per GQA group, i.e. per KV head, no per-query-head scoring loop, softmax
+ * skipped) and "Seleção Esparsa de Lookahead Treinável" (the predictor ranks KV blocks);
+ * "Esparsidade de Contexto no Tempo de Inferência", §2 "Oracle Top-K" (exact per-head token
+ * scores).  Scores are unscaled dot products in fp32.
+ *
+ *   q        device; TOKEN_* modes: Q [B,T,Hq,d] contiguous; BLOCK_* modes: predictor
+ *            [B,T,Hkv,d] contiguous.  q_dtype SPK_F32 or SPK_BF16.
+ *   keys     device; TOKEN_* and BLOCK_RAW: the key cache, row (b,kvh,j) at
+ *            keys + b*k_sb + kvh*k_sh + j*k_sn (k_dtype F32 or BF16); BLOCK_POOLED: pooled keys
+ *            with the same stride convention, one row per block (F32 or BF16).
+ *   n_tokens tokens in the cache.  Candidates: TOKEN_* -> n_tokens tokens; BLOCK_* ->
+ *            n_tokens / block_size complete blocks (the partial tail block is not a candidate).
+ *   scores   device fp32 [B,T,Hs,s_ld], Hs = Hq for TOKEN_PER_HEAD else Hkv; entries
+ *            [0, n_candidates) of each row are written.  s_ld >= n_candidates.
+ *   pooled_out  BLOCK_RAW only, optional: device fp32 [B,Hkv,n_tokens/block_size,d]
+ *            contiguous, receives the block means; NULL otherwise.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status sparse_index_score(spk_index_mode mode,
+                                      const void* q, spk_dtype q_dtype,
+                                      const void* keys, spk_dtype k_dtype,
+                                      int64_t k_sb, int64_t k_sh, int64_t k_sn,
+                                      int B, int T, int Hq, int Hkv, int d,
+                                      int n_tokens, int block_size,
+                                      float* scores, int64_t s_ld,
+                                      float* pooled_out,
+                                      void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * topk_select — exact top-k of each row of an fp32 score matrix.
+ *
+ * Passages: SparDA, §2 "Seleção Esparsa de Lookahead Treinável" (top-k blocks) and
+ * "Esparsidade de Contexto no Tempo de Inferência", §2 "Oracle Top-K" (exact top-k tokens).
+ * Definition: the min(k, n) entries with the largest scores; equal scores go to the lowest
+ * index; -0 equals +0; NaN ranks below -inf.  Indices are written in ASCENDING order.
+ *
+ *   scores   device fp32 [rows, s_ld]; entries [0, n) of each row are read.
+ *   idx      device int32 [rows, idx_ld]; entries [0, min(k,n)) written.  idx_ld >= min(k,n).
+ *   count    device int32 [rows] or NULL; receives min(k, n).
+ *   ws       device workspace of at least topk_select_workspace_size() bytes (may be NULL
+ *            when that size is 0).
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status topk_select_workspace_size(int rows, int n, int k, size_t* bytes);
+SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int rows, int n, int k,
+                               int32_t* idx, int64_t idx_ld, int32_t* count,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * sparse_decode_attn — gather the selected K/V rows and run exact attention over them only.
+ *
+ * Passages: "Esparsidade de Contexto no Tempo de Inferência", §3C (decode reads O(k·d) rows
+ * instead of O(N·d); irregular per-token, per-query and per-head sparsity, §2 "Implementação
+ * de Hardware"); "O Fim do Gargalo de Memória ... Adaptive DHiSparse", "A Inovação" (exact
+ * fused retrieval of non-resident rows) and "Metodologia e Eficiência de Carga" (queries
+ * verified together share the retrieval of missing rows); "Nem Todos os Pensamentos
+ * Necessitam de HBM", §3 Proposition 1 (rows fetched from host memory at full precision give
+ * exactly the result of HBM-resident rows: the output here is bit-identical whatever `loc`).
+ *
+ * For each query vector (b,t,h) the set S(b,t,h) of token ids it reads is the selection list
+ * chosen by `scope` (PER_SEQ: row b; PER_KV_HEAD: row (b*T+t)*Hkv + h/G; PER_Q_HEAD: row
+ * (b*T+t)*Hq + h), each entry e expanded to tokens [e*gran, e*gran + gran) ∩ [0, n_tokens),
+ * united with the sinks [0, n_sink) and the recent window [n_tokens - n_recent, n_tokens).
+ * Then out[b,t,h,:] = softmax(sm_scale · q·K_Sᵀ) · V_S with fp32 accumulation, and
+ * lse[b,t,h] = log Σ_{i∈S} exp(sm_scale · q·k_i) (natural log; -inf and out = 0 if S is empty).
+ * Each (b, kvh) group fetches every row of the union of its query vectors' sets exactly once.
+ *
+ *   q          device [B,T,Hq,d] contiguous, F32 or BF16.
+ *   k, v       device caches, row (b,kvh,slot) at k + b*kv_sb + kvh*kv_sh + slot*kv_sn
+ *              (same strides for v), slot < hbm_slots; kv_dtype F32 or BF16.  Without `loc`
+ *              n_tokens <= hbm_slots is required.
+ *   k_host, v_host  pinned host pools (hipHostMalloc'ed: page-locked and device-mapped; any
+ *              other memory is rejected with SPK_EINVAL), row (b,kvh,slot) at
+ *              k_host + b*host_sb + kvh*host_sh + slot*host_sn, slot < host_slots; NULL if unused.
+ *   loc        device int32 or NULL.  loc[b*loc_sb + kvh*loc_sh + tok] >= 0: token tok is HBM
+ *              slot loc (< hbm_slots); < 0: host slot ~loc (< host_slots; requires k_host and
+ *              v_host).  A slot outside its pool is treated as a missing row (not read).
+ *              NULL: every token is HBM slot tok.
+ *   sel_idx    device int32 [rows, sel_ld], strictly ascending entries (as topk_select and
+ *              tier_classify write them); sel_count device int32 [rows] (clamped to sel_ld).
+ *   gran       1 for token ids, or the block size for block ids.
+ *   out        device fp32 [B,T,Hq,d].  lse: device fp32 [B,T,Hq] or NULL.
+ *   logits     device fp32 [B,T,Hq,logits_ld] or NULL: the scaled logit sm_scale·q·k of every
+ *              row of the group's fetch list (the ascending union above), -inf for rows the
+ *              query vector does not read.  For PER_SEQ with gran 1 and no sinks/recent, the
+ *              fetch list is sel_idx itself.  logits_ld >= the fetch-list bound (see below).
+ *   ws         device workspace of at least sparse_decode_attn_workspace_size() bytes.
+ *
+ * The fetch-list bound per group is min(n_tokens, sets*sel_ld*gran + n_sink + n_recent) with
+ * sets = 1 (PER_SEQ), T (PER_KV_HEAD) or T*G (PER_Q_HEAD); at most 32 sets per group.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status sparse_decode_attn_workspace_size(spk_sel_scope scope, int B, int T, int Hq,
+                                                     int Hkv, int d, int n_tokens, int64_t sel_ld,
+                                                     int gran, int n_sink, int n_recent,
+                                                     size_t* bytes);
+SPK_API spk_status sparse_decode_attn(const void* q, spk_dtype q_dtype,
+                                      const void* k, const void* v, spk_dtype kv_dtype,
+                                      int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                                      const void* k_host, const void* v_host,
+                                      int64_t host_sb, int64_t host_sh, int64_t host_sn,
+                                      int64_t host_slots,
+                                      const int32_t* loc, int64_t loc_sb, int64_t loc_sh,
+                                      int64_t hbm_slots,
+                                      const int32_t* sel_idx, const int32_t* sel_count,
+                                      int64_t sel_ld, spk_sel_scope scope, int gran,
+                                      int n_sink, int n_recent,
+                                      int B, int T, int Hq, int Hkv, int d, int n_tokens,
+                                      float sm_scale,
+                                      float* out, float* lse, float* logits, int64_t logits_ld,
+                                      void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * importance_accumulate — cumulative attention importance, one decode step.
+ *
+ * Passage: "Nem Todos os Pensamentos Necessitam de HBM", §2 "Pontuação de Importância":
+ * s_i += (1/|L|) Σ_ℓ (1/H) Σ_h α_ℓ,h[i], with α the attention probabilities of this step.
+ * Here α_ℓ,h[u] = exp(logits[ℓ,b,h,u] - lse[ℓ,b,h]) for position u of sequence b's list;
+ * tokens not in the list (evicted or not read) receive nothing.  One query token per
+ * sequence (T = 1).
+ *
+ *   s        device fp32 [B, s_ld], updated in place for tokens sel_idx[b, u], u < count.
+ *   sel_idx, sel_count  device int32 [B, sel_ld] / [B]: the per-sequence lists the
+ *            attention read (PER_SEQ scope), strictly ascending.
+ *   logits   device fp32 [L, B, Hq, logits_ld]: sparse_decode_attn's logits of each layer.
+ *   lse      device fp32 [L, B, Hq].
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status importance_accumulate(float* s, int64_t s_ld, int B, int n_tokens,
+                                         const int32_t* sel_idx, const int32_t* sel_count,
+                                         int64_t sel_ld,
+                                         const float* logits, int64_t logits_ld,
+                                         const float* lse, int L, int Hq, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * tier_classify — tiers by cumulative importance, sinks and recent window protected.
+ *
+ * Passages: "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro
+ * Níveis" (T0 HBM: protected tokens and the most important; T1 host DDR at full precision,
+ * fetched before attention; T2 8-bit, not used here; T3 evicted for good) and §4 (tiers are
+ * reassigned periodically; the period is the caller's loop).
+ * Definition: protected = tokens [0, n_sink) and [n_tokens - n_recent, n_tokens) -> T0.  The
+ * M other tokens are ranked by (live before evicted, s descending, index ascending; NaN ranks
+ * with the evicted); rank < floor(M*t0_permille/1000) -> T0, rank < floor(M*t01_permille/1000)
+ * -> T1, the rest -> T3.  An evicted token is always T3.
+ *
+ *   s        device fp32 [B, s_ld].
+ *   evicted  device uint8 [B, ev_ld] or NULL: nonzero = evicted earlier (sticky).  On return,
+ *            every token classified T3 has evicted = 1.
+ *   tier     device uint8 [B, tier_ld]: 0 (T0), 1 (T1) or 3 (T3) for tokens [0, n_tokens).
+ *   sel_idx, sel_count  device int32 [B, sel_ld] / [B] or NULL: the ascending list of T0 ∪ T1
+ *            tokens (the rows attention reads).  sel_ld >= n_tokens.
+ *   ws       device workspace of at least tier_classify_workspace_size() bytes (NULL if 0).
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status tier_classify_workspace_size(int B, int n_tokens, size_t* bytes);
+SPK_API spk_status tier_classify(const float* s, int64_t s_ld, int B, int n_tokens,
+                                 int n_sink, int n_recent, int t0_permille, int t01_permille,
+                                 uint8_t* evicted, int64_t ev_ld,
+                                 uint8_t* tier, int64_t tier_ld,
+                                 int32_t* sel_idx, int32_t* sel_count, int64_t sel_ld,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPK_H */

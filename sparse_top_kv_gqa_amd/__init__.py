@@ -1,0 +1,285 @@
+"""Python binding of libspk — sparse top-k KV decode attention (GQA) for AMD MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of libspk.so.
+PyTorch supplies device memory, pinned host memory and the current HIP stream.  The
+library must be built (``python -m sparse_top_kv_gqa_amd._build``); importing works without
+it, but every call raises if it is missing — there is no fallback path.
+
+Entry points mirror include/spk.h: ``sparse_index_score``, ``topk_select``,
+``sparse_decode_attn``, ``importance_accumulate``, ``tier_classify``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspk.so")
+
+# enums of spk.h
+F32, BF16 = 0, 1
+IDX_TOKEN_GROUP_MEAN, IDX_TOKEN_PER_HEAD, IDX_BLOCK_POOLED, IDX_BLOCK_RAW = 0, 1, 2, 3
+SEL_PER_SEQ, SEL_PER_KV_HEAD, SEL_PER_Q_HEAD = 0, 1, 2
+STATUS = {0: "SPK_OK", 1: "SPK_EINVAL", 2: "SPK_EUNSUPPORTED", 3: "SPK_EWORKSPACE", 4: "SPK_EHIP"}
+
+MODES = {"token_group_mean": IDX_TOKEN_GROUP_MEAN, "token_per_head": IDX_TOKEN_PER_HEAD,
+         "block_pooled": IDX_BLOCK_POOLED, "block_raw": IDX_BLOCK_RAW}
+SCOPES = {"per_seq": SEL_PER_SEQ, "per_kv_head": SEL_PER_KV_HEAD, "per_q_head": SEL_PER_Q_HEAD}
+
+EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_workspace_size",
+           "topk_select", "sparse_decode_attn_workspace_size", "sparse_decode_attn",
+           "importance_accumulate", "tier_classify_workspace_size", "tier_classify")
+
+
+class SpkError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+
+P = ctypes.c_void_p
+I = ctypes.c_int
+I64 = ctypes.c_int64
+SZ = ctypes.c_size_t
+FL = ctypes.c_float
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspk.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_top_kv_gqa_amd._build` (no fallback path exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.spk_last_error.restype = ctypes.c_char_p
+    L.spk_last_error.argtypes = []
+    L.spk_version.restype = I
+    L.sparse_index_score.restype = I
+    L.sparse_index_score.argtypes = [I, P, I, P, I, I64, I64, I64, I, I, I, I, I, I, I, P, I64, P, P]
+    L.topk_select_workspace_size.restype = I
+    L.topk_select_workspace_size.argtypes = [I, I, I, ctypes.POINTER(SZ)]
+    L.topk_select.restype = I
+    L.topk_select.argtypes = [P, I64, I, I, I, P, I64, P, P, SZ, P]
+    L.sparse_decode_attn_workspace_size.restype = I
+    L.sparse_decode_attn_workspace_size.argtypes = [I, I, I, I, I, I, I, I64, I, I, I,
+                                                    ctypes.POINTER(SZ)]
+    L.sparse_decode_attn.restype = I
+    L.sparse_decode_attn.argtypes = [P, I, P, P, I, I64, I64, I64, P, P, I64, I64, I64, I64, P, I64,
+                                     I64, I64, P, P, I64, I, I, I, I, I, I, I, I, I, I, FL, P, P, P, I64, P,
+                                     SZ, P]
+    L.importance_accumulate.restype = I
+    L.importance_accumulate.argtypes = [P, I64, I, I, P, P, I64, P, I64, P, I, I, P]
+    L.tier_classify_workspace_size.restype = I
+    L.tier_classify_workspace_size.argtypes = [I, I, ctypes.POINTER(SZ)]
+    L.tier_classify.restype = I
+    L.tier_classify.argtypes = [P, I64, I, I, I, I, I, I, P, I64, P, I64, P, P, I64, P, SZ, P]
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SpkError(status, where, lib().spk_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _rows_view(t: torch.Tensor, name: str):
+    """(b, h, n, d) strides of a 4-D cache view whose last dim is contiguous."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name} must be a 4-D [B, H, N, d] view with a contiguous last dim")
+    return t.stride(0), t.stride(1), t.stride(2)
+
+
+def _contig(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+# ----------------------------------------------------------------------------- index scores
+
+def sparse_index_score(mode, q: torch.Tensor, keys: torch.Tensor, n_tokens: int,
+                       block_size: int = 1, Hq: Optional[int] = None,
+                       scores: Optional[torch.Tensor] = None,
+                       pooled_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Indexer scores (no softmax).  q: [B,T,Hq,d] (token modes) or predictor [B,T,Hkv,d]
+    (block modes); keys: [B,Hkv,*,d] cache view (or pooled keys).  Returns fp32
+    [B,T,Hs,n_cand] (Hs = Hq for per-head, else Hkv)."""
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    _contig(q, "q")
+    B, T, Hx, d = q.shape
+    Hkv = keys.shape[1]
+    block = m in (IDX_BLOCK_POOLED, IDX_BLOCK_RAW)
+    if Hq is None:
+        Hq = Hkv if block else Hx
+    n_cand = n_tokens // block_size if block else n_tokens
+    Hs = Hq if m == IDX_TOKEN_PER_HEAD else Hkv
+    if scores is None:
+        scores = torch.empty((B, T, Hs, n_cand), dtype=torch.float32, device=q.device)
+    sb, sh, sn = _rows_view(keys, "keys")
+    st = lib().sparse_index_score(m, _ptr(q), _dt(q), _ptr(keys), _dt(keys), sb, sh, sn, B, T, Hq,
+                                  Hkv, d, n_tokens, block_size, _ptr(scores), scores.stride(-2),
+                                  _ptr(pooled_out), _stream(stream))
+    _check(st, "sparse_index_score")
+    return scores
+
+
+# ----------------------------------------------------------------------------- top-k
+
+def topk_select(scores: torch.Tensor, k: int, n: Optional[int] = None,
+                idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                stream=None):
+    """Exact top-k of each row of ``scores`` (any leading shape, last dim contiguous).
+    Returns (idx int32 [..., min(k, n)] ascending, count int32 [...])."""
+    if scores.stride(-1) != 1:
+        raise ValueError("scores must have a contiguous last dim")
+    lead = scores.shape[:-1]
+    rows = int(math.prod(lead)) if len(lead) else 1
+    n = scores.shape[-1] if n is None else n
+    kk = max(0, min(k, n))
+    s2 = scores.reshape(rows, scores.shape[-1]) if rows else scores.reshape(0, scores.shape[-1])
+    if idx is None:
+        idx = torch.empty((*lead, kk), dtype=torch.int32, device=scores.device)
+    if count is None:
+        count = torch.empty(lead, dtype=torch.int32, device=scores.device)
+    i2 = idx.reshape(rows, idx.shape[-1])
+    st = lib().topk_select(_ptr(s2), s2.stride(0), rows, n, k, _ptr(i2), i2.stride(0), _ptr(count),
+                           None, 0, _stream(stream))
+    _check(st, "topk_select")
+    return idx, count
+
+
+# ----------------------------------------------------------------------------- attention
+
+def attn_workspace_size(scope, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran=1, n_sink=0,
+                        n_recent=0) -> int:
+    sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
+    out = SZ(0)
+    _check(lib().sparse_decode_attn_workspace_size(sc, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran,
+                                                   n_sink, n_recent, ctypes.byref(out)),
+           "sparse_decode_attn_workspace_size")
+    return out.value
+
+
+def fetch_list_bound(scope, T, G, sel_ld, gran, n_sink, n_recent, n_tokens) -> int:
+    """Upper bound of a group's fetch list (the rows of logits), as spk.h defines it."""
+    sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
+    sets = 1 if sc == SEL_PER_SEQ else (T if sc == SEL_PER_KV_HEAD else T * G)
+    return min(n_tokens, sets * sel_ld * gran + n_sink + n_recent)
+
+
+def sparse_decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel_idx: torch.Tensor,
+                       sel_count: torch.Tensor, scope, n_tokens: int, gran: int = 1,
+                       n_sink: int = 0, n_recent: int = 0, sm_scale: Optional[float] = None,
+                       k_host: Optional[torch.Tensor] = None, v_host: Optional[torch.Tensor] = None,
+                       loc: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None, stream=None):
+    """Exact attention over the selected rows.  q [B,T,Hq,d]; k, v [B,Hkv,*,d] views;
+    sel_idx [rows, sel_ld] int32 (rows per `scope`), sel_count [rows] int32.
+    Host pools k_host/v_host: pinned [B,Hkv,*,d] views, used where loc [B,Hkv,>=n_tokens] < 0.
+    Returns (out fp32 [B,T,Hq,d], lse fp32 [B,T,Hq])."""
+    sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
+    _contig(q, "q")
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    sel_ld = sel_idx.shape[-1]
+    if sel_idx.stride(-1) != 1 or sel_idx.dim() < 1:
+        raise ValueError("sel_idx must have a contiguous last dim")
+    sel2 = sel_idx.reshape(-1, sel_ld)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    kb, kh, kn = _rows_view(k, "k")
+    if _rows_view(v, "v") != (kb, kh, kn):
+        raise ValueError("k and v must share strides")
+    hb = hh = hn = host_slots = 0
+    if k_host is not None:
+        hb, hh, hn = _rows_view(k_host, "k_host")
+        if v_host is None or _rows_view(v_host, "v_host") != (hb, hh, hn):
+            raise ValueError("k_host and v_host must share strides")
+        host_slots = min(k_host.shape[2], v_host.shape[2])
+    lb = lh = 0
+    if loc is not None:
+        if loc.dtype != torch.int32 or loc.dim() != 3 or loc.stride(2) != 1:
+            raise ValueError("loc must be int32 [B, Hkv, N] with a contiguous last dim")
+        lb, lh = loc.stride(0), loc.stride(1)
+    hbm_slots = min(k.shape[2], v.shape[2])
+    if out is None:
+        out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    wsz = attn_workspace_size(sc, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent)
+    if ws is None or ws.numel() < wsz:
+        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=q.device)
+    lg_ld = logits.stride(-2) if logits is not None else 0
+    st = lib().sparse_decode_attn(_ptr(q), _dt(q), _ptr(k), _ptr(v), _dt(k), kb, kh, kn,
+                                  _ptr(k_host), _ptr(v_host), hb, hh, hn, host_slots, _ptr(loc),
+                                  lb, lh, hbm_slots,
+                                  _ptr(sel2), _ptr(sel_count), sel_ld, sc, gran, n_sink, n_recent,
+                                  B, T, Hq, Hkv, d, n_tokens, float(sm_scale), _ptr(out),
+                                  _ptr(lse), _ptr(logits), lg_ld, _ptr(ws), ws.numel(),
+                                  _stream(stream))
+    _check(st, "sparse_decode_attn")
+    return out, lse
+
+
+# ----------------------------------------------------------------------------- importance / tiers
+
+def importance_accumulate(s: torch.Tensor, sel_idx: torch.Tensor, sel_count: torch.Tensor,
+                          logits: torch.Tensor, lse: torch.Tensor, n_tokens: int, stream=None):
+    """s [B, s_ld] fp32 updated in place; sel_idx [B, sel_ld]; logits [L, B, Hq, logits_ld]
+    (or [L, B, 1, Hq, logits_ld]); lse [L, B, Hq] (or [L, B, 1, Hq])."""
+    B = s.shape[0]
+    L = logits.shape[0]
+    Hq = logits.shape[-2]
+    st = lib().importance_accumulate(_ptr(s), s.stride(0), B, n_tokens, _ptr(sel_idx),
+                                     _ptr(sel_count), sel_idx.shape[-1], _ptr(logits),
+                                     logits.stride(-2), _ptr(lse), L, Hq, _stream(stream))
+    _check(st, "importance_accumulate")
+    return s
+
+
+def tier_classify(s: torch.Tensor, n_tokens: int, n_sink: int, n_recent: int,
+                  t0_permille: int = 250, t01_permille: int = 750,
+                  evicted: Optional[torch.Tensor] = None, tier: Optional[torch.Tensor] = None,
+                  sel_idx: Optional[torch.Tensor] = None, sel_count: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Tiers of each sequence's tokens.  s [B, s_ld] fp32.  Returns (tier uint8 [B, n_tokens],
+    sel_idx int32 [B, n_tokens] (T0 ∪ T1 ascending), sel_count int32 [B])."""
+    B = s.shape[0]
+    dev = s.device
+    if tier is None:
+        tier = torch.empty((B, n_tokens), dtype=torch.uint8, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, max(n_tokens, 1)), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = lib().tier_classify(_ptr(s), s.stride(0), B, n_tokens, n_sink, n_recent, t0_permille,
+                             t01_permille, _ptr(evicted), evicted.stride(0) if evicted is not None else 0,
+                             _ptr(tier), tier.stride(0), _ptr(sel_idx), _ptr(sel_count),
+                             sel_idx.stride(0), None, 0, _stream(stream))
+    _check(st, "tier_classify")
+    return tier, sel_idx, sel_count

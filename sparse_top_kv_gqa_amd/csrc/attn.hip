@@ -1,0 +1,881 @@
+// sparse_decode_attn: gather the selected K/V rows once per GQA group and run exact softmax
+// attention over them only.
+//
+// "Esparsidade de Contexto no Tempo de Inferência", §3C: decoding over a selection reads O(k·d)
+// rows instead of O(N·d), and §2 "Implementação de Hardware": per-token, per-query and per-head
+// irregular sparsity.  "O Fim do Gargalo de Memória ... Adaptive DHiSparse": exact fused
+// retrieval of non-resident rows; queries verified together share the retrieval of missing rows.
+// "Nem Todos os Pensamentos Necessitam de HBM", §3 Proposition 1: rows that come back from host
+// memory at full precision contribute exactly what HBM rows would — the reduction order here
+// never depends on where a row lives, so the output is bit-identical for any `loc`.
+//
+// Pipeline (all on one stream):
+//  1. assemble  (only when a group has several selection lists, block granularity or forced
+//     rows): one workgroup per (b, kvh) sets one bit per token in an LDS bitmap per list, ORs
+//     the bitmaps and emits the ascending fetch list with a per-row mask of the lists holding it.
+//  2. partial   split-K over the fetch list: workgroup (split, group) walks rows
+//     [split*R, split*R + R).  D/8 lanes share a row (16 B each), so a wave reads 4 rows per load
+//     (d=128) and every query vector of the group (G heads x T tokens) is scored against each
+//     fetched row: the row is read from HBM (or host memory) once per group.  Each 16-lane slot
+//     keeps its own online-softmax state (m, l, acc in fp32, exp2 domain); slots and waves merge
+//     at the end and the split's (m, l, acc) go to the workspace.
+//  3. combine   one wave per query vector merges the splits in split order (deterministic, no
+//     atomics) into out and lse.
+#include "spk_internal.h"
+
+namespace spk {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kUnroll = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxSets = 32;
+constexpr size_t kAsmLdsMax = 60 * 1024;  // larger bitmaps live in the workspace
+constexpr int kMaxIntervals = 64;   // selection entries + 2 forced ranges, one per lane
+constexpr int kMaxRows = 4096;      // rows per workgroup (LDS row table)
+constexpr int kDead = INT32_MIN;    // row-table entry of a row that is not read
+
+struct Plan {
+  int groups = 0, sets = 1, nq = 0, nq_pad = 0, ubound = 0, R = 0, smax = 0, words = 0;
+  bool assemble = false, intervals = false, mask = false, bm_lds = true;
+  size_t off_list = 0, off_mask = 0, off_count = 0, off_bm = 0, off_ml = 0, off_acc = 0, bytes = 0;
+};
+
+int pad_nq(int nq) { return nq <= 1 ? 1 : nq <= 2 ? 2 : nq <= 4 ? 4 : nq <= 8 ? 8 : 16; }
+
+int partial_occupancy(int d, int nq_pad, bool mask, int mode);  // resident workgroups per CU
+
+// Fetch-list strategy, split size and workspace layout of one call.  A group with one selection
+// list expands it in the partial kernel itself (intervals mode) when the list is short; several
+// lists per group (per-head or per-token sets) are merged by the assemble kernel first.
+Plan make_plan(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_tokens,
+               int64_t sel_ld, int gran, int n_sink, int n_recent) {
+  Plan p;
+  const int G = Hq / Hkv;
+  p.groups = B * Hkv;
+  p.sets = scope == SPK_SEL_PER_SEQ ? 1 : scope == SPK_SEL_PER_KV_HEAD ? T : T * G;
+  p.nq = G * T;
+  p.nq_pad = pad_nq(p.nq);
+  p.mask = p.sets > 1;
+  const bool expand = gran > 1 || n_sink > 0 || n_recent > 0;
+  p.intervals = p.sets == 1 && expand && sel_ld + 2 <= 64;
+  p.assemble = p.sets > 1 || (expand && !p.intervals);
+  int64_t ub = (int64_t)p.sets * sel_ld * gran + n_sink + n_recent;
+  if (ub > n_tokens) ub = n_tokens;
+  p.ubound = (int)ub;
+  // rows per split: about one resident round of workgroups when every list is full
+  const int64_t rows = (int64_t)p.groups * (p.ubound > 0 ? p.ubound : 1);
+  const int occ = partial_occupancy(d, p.nq_pad, p.mask, p.intervals ? 1 : 0);
+  const int step = 64;
+  int64_t R = ceil_div(rows, (int64_t)occ * num_cus());
+  R = ceil_div(R, step) * step;
+  if (R < step) R = step;
+  if (R > kMaxRows) R = kMaxRows;
+  p.R = (int)R;
+  p.smax = p.ubound > 0 ? (int)ceil_div(p.ubound, p.R) : 1;
+  p.words = (int)ceil_div(n_tokens > 0 ? n_tokens : 1, 32);
+  p.bm_lds = (size_t)p.sets * p.words * 4 <= kAsmLdsMax;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  if (p.assemble) {
+    p.off_list = take((size_t)p.groups * p.ubound * 4);
+    p.off_mask = take(p.mask ? (size_t)p.groups * p.ubound * 4 : 0);
+    p.off_bm = take(p.bm_lds ? 0 : (size_t)p.groups * p.sets * p.words * 4);
+  }
+  if (p.assemble || p.intervals) p.off_count = take((size_t)p.groups * 4);
+  p.off_ml = take((size_t)p.groups * p.smax * p.nq_pad * 2 * 4);
+  p.off_acc = take((size_t)p.groups * p.smax * p.nq_pad * d * 4);
+  p.bytes = off;
+  return p;
+}
+
+// ------------------------------------------------------------------------------- assemble
+
+struct AsmArgs {
+  const int32_t* sel_idx;
+  const int32_t* sel_count;
+  int64_t sel_ld;
+  int scope, gran, n_sink, n_recent, T, Hq, Hkv, G, sets, n_tokens, words, ubound;
+  uint32_t* bm_global;
+  int32_t* ulist;
+  uint32_t* umask;
+  int32_t* ucount;
+};
+
+__global__ __launch_bounds__(kThreads) void assemble_kernel(AsmArgs a) {
+  extern __shared__ uint32_t bm_lds[];
+  __shared__ int scratch[kWaves + 1];
+  const int g = blockIdx.x;
+  const int b = g / a.Hkv, kvh = g % a.Hkv;
+  const int W = a.words;
+  uint32_t* bm = a.bm_global ? a.bm_global + (int64_t)g * a.sets * W : bm_lds;
+  for (int i = threadIdx.x; i < a.sets * W; i += kThreads) bm[i] = 0u;
+  __syncthreads();
+  const int n = a.n_tokens;
+  for (int r = 0; r < a.sets; ++r) {
+    int64_t row;
+    if (a.scope == SPK_SEL_PER_SEQ) row = b;
+    else if (a.scope == SPK_SEL_PER_KV_HEAD) row = (int64_t)(b * a.T + r) * a.Hkv + kvh;
+    else row = (int64_t)(b * a.T + r / a.G) * a.Hq + kvh * a.G + r % a.G;
+    int cnt = a.sel_count[row];
+    if (cnt > a.sel_ld) cnt = (int)a.sel_ld;
+    const int32_t* lst = a.sel_idx + row * a.sel_ld;
+    const int64_t total = (int64_t)(cnt > 0 ? cnt : 0) * a.gran;
+    for (int64_t e = threadIdx.x; e < total; e += kThreads) {
+      const int64_t tok = (int64_t)lst[e / a.gran] * a.gran + e % a.gran;
+      if (tok >= 0 && tok < n) atomicOr(&bm[r * W + (int)(tok >> 5)], 1u << (tok & 31));
+    }
+  }
+  // forced rows belong to every list
+  const int s_end = min(a.n_sink, n);
+  const int r_beg = max(0, n - a.n_recent);
+  for (int tok = threadIdx.x; tok < s_end + (n - r_beg); tok += kThreads) {
+    const int t = tok < s_end ? tok : r_beg + (tok - s_end);
+    for (int r = 0; r < a.sets; ++r) atomicOr(&bm[r * W + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  const int wpt = (W + kThreads - 1) / kThreads;
+  const int w0 = threadIdx.x * wpt;
+  const int w1 = min(w0 + wpt, W);
+  int local = 0;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t u = 0;
+    for (int r = 0; r < a.sets; ++r) u |= bm[r * W + w];
+    local += __popc(u);
+  }
+  int total;
+  int pos = block_excl_scan(local, scratch, &total);
+  int32_t* ul = a.ulist + (int64_t)g * a.ubound;
+  uint32_t* um = a.umask ? a.umask + (int64_t)g * a.ubound : nullptr;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t u = 0;
+    for (int r = 0; r < a.sets; ++r) u |= bm[r * W + w];
+    while (u) {
+      const int bit = __ffs(u) - 1;
+      u &= u - 1;
+      if (pos < a.ubound) {
+        ul[pos] = w * 32 + bit;
+        if (um) {
+          uint32_t m = 0;
+          for (int r = 0; r < a.sets; ++r) m |= ((bm[r * W + w] >> bit) & 1u) << r;
+          um[pos] = m;
+        }
+      }
+      ++pos;
+    }
+  }
+  if (threadIdx.x == 0) a.ucount[g] = min(total, a.ubound);
+}
+
+// ------------------------------------------------------------------------------- partial
+
+// How a partial workgroup learns the rows of its group's fetch list.
+enum ListMode {
+  kListExplicit = 0,   // list + count (caller's list, or the assembled one)
+  kListIntervals = 1,  // one selection row of ids expanded by `gran`, plus sinks and recent window
+};
+
+struct AttnArgs {
+  const void* q;
+  int q_bf16;
+  const void* k;
+  const void* v;
+  int64_t kv_sb, kv_sh, kv_sn;
+  const void* k_host;
+  const void* v_host;
+  int64_t host_sb, host_sh, host_sn, host_slots;
+  const int32_t* loc;
+  int64_t loc_sb, loc_sh, hbm_slots;
+  // explicit mode: rows of group g are list[lrow*list_ld + i], i < min(count[lrow], count_clamp)
+  // intervals mode: ids sel[lrow*list_ld + i], i < min(count[lrow], list_ld), expanded by gran
+  // lrow = b (PER_SEQ) or g
+  const int32_t* list;
+  const int32_t* count;
+  int64_t list_ld;
+  int count_clamp;
+  int lrow_is_batch;
+  int list_mode;
+  int gran, n_sink, n_recent;
+  int32_t* ucount;       // per-group fetch-list length (intervals mode writes it for combine)
+  const uint32_t* mask;  // per fetch-list row (assembled lists with several sets)
+  int mask_div;          // query vector n reads rows whose mask has bit n / mask_div
+  int T, Hq, Hkv, G, nq, n_tokens, R, smax;
+  float scale_log2;
+  float* ml;
+  float* acc;
+  float* logits;
+  int64_t logits_ld;
+};
+
+// Where token `tok` of group (b, kvh) lives: HBM slot (>= 0) or host slot (encoded ~slot < 0);
+// kDead when the slot lies outside its pool (the row is then not read).
+__device__ __forceinline__ int resolve_slot(const AttnArgs& a, int b, int kvh, int tok) {
+  if (tok < 0 || tok >= a.n_tokens) return kDead;
+  if (!a.loc) return tok;
+  const int l = a.loc[(int64_t)b * a.loc_sb + (int64_t)kvh * a.loc_sh + tok];
+  const bool ok = l >= 0 ? (int64_t)l < a.hbm_slots : (int64_t)(~l) < a.host_slots;
+  return ok ? l : kDead;
+}
+
+template <typename KT>
+__device__ __forceinline__ const KT* row_ptr(const AttnArgs& a, const void* base_hbm,
+                                             const void* base_host, int b, int kvh, int slot) {
+  if (slot < 0)
+    return reinterpret_cast<const KT*>(base_host) + (int64_t)b * a.host_sb +
+           (int64_t)kvh * a.host_sh + (int64_t)(~slot) * a.host_sn;
+  return reinterpret_cast<const KT*>(base_hbm) + (int64_t)b * a.kv_sb + (int64_t)kvh * a.kv_sh +
+         (int64_t)slot * a.kv_sn;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave 0: the ascending union of the selection row's expanded intervals, the sinks [0, s) and
+// the recent window [n - r, n) as <= 64 disjoint segments (start, first position); returns the
+// union size through *U.  Selection ids must be ascending (as topk_select writes them); ids that
+// expand outside [0, n) give empty intervals.
+__device__ void build_segments(const AttnArgs& a, const int32_t* sel, int cnt, int* seg_start,
+                               int* seg_pos, int* nseg, int* U) {
+  const int lane = lane_id();
+  const int n = a.n_tokens;
+  const int rs = max(0, n - a.n_recent);
+  // interval of this lane: 0 = sinks, 1..cnt = selection entries, cnt+1 = recent window
+  int lo = n, hi = n;
+  bool is_sel = false;
+  if (lane == 0) {
+    lo = 0;
+    hi = min(a.n_sink, n);
+  } else if (lane <= cnt) {
+    const int64_t e = sel[lane - 1];
+    const int64_t s0 = e * a.gran;
+    lo = (int)min<int64_t>(max<int64_t>(s0, 0), n);
+    hi = (int)min<int64_t>(max<int64_t>(s0 + a.gran, 0), n);
+    if (e < 0) lo = hi = n;
+    is_sel = true;
+  } else if (lane == cnt + 1) {
+    lo = rs;
+    hi = n;
+  }
+  // order by start: selection entries are ascending; the recent window slots in among them
+  const uint64_t before_rs = __ballot(is_sel && lo < rs);
+  const int n_before = __popcll(before_rs);
+  int rank;
+  if (lane == 0) rank = 0;
+  else if (is_sel) rank = lane + (lo < rs ? 0 : 1);
+  else if (lane == cnt + 1) rank = 1 + n_before;
+  else rank = lane;  // unused lanes keep their place (empty intervals at n)
+  const int total = cnt + 2;
+  int* ord_lo = seg_start;  // reuse the output arrays as sort scratch
+  int* ord_hi = seg_pos;
+  if (lane < total) {
+    ord_lo[rank] = lo;
+    ord_hi[rank] = hi;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  int mlo = n, mhi = n;
+  if (lane < total) {
+    mlo = ord_lo[lane];
+    mhi = ord_hi[lane];
+  }
+  // part of this interval not covered by earlier ones
+  int run_end = mhi;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(run_end, o, kWave);
+    if (lane >= o) run_end = max(run_end, y);
+  }
+  int prev_end = __shfl_up(run_end, 1, kWave);
+  if (lane == 0) prev_end = 0;
+  const int st = max(mlo, prev_end);
+  const int len = lane < total ? max(0, mhi - st) : 0;
+  const int incl = wave_incl_scan(len);
+  __builtin_amdgcn_wave_barrier();
+  if (lane < total) {
+    seg_start[lane] = st;
+    seg_pos[lane] = incl - len;
+  }
+  if (lane == kWave - 1) {
+    *U = incl;
+    *nseg = total;
+  }
+}
+
+// Token at union position p (0 <= p < U): the last segment whose first position is <= p.
+__device__ __forceinline__ int token_at(const int* seg_start, const int* seg_pos, int nseg, int p) {
+  int lo = 0, hi = nseg;  // find the last index with seg_pos <= p
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (seg_pos[mid] <= p) lo = mid;
+    else hi = mid;
+  }
+  return seg_start[lo] + (p - seg_pos[lo]);
+}
+
+template <int D, typename KT, int NQ, bool kMask, int MODE, int U>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
+  constexpr int LPR = D / 8;             // lanes per row
+  constexpr int SPW = kWave / LPR;       // slots (rows) per wave
+  constexpr int NSLOT = SPW * kWaves;    // slots per workgroup
+  constexpr int STEP = NSLOT * U;        // rows per workgroup per iteration
+  __shared__ float red[kWaves][NQ][D + 2];
+  __shared__ int32_t slot_s[kMaxRows];
+  __shared__ uint32_t mask_s[kMask ? kMaxRows : 1];
+  __shared__ int seg_start[kMaxIntervals], seg_pos[kMaxIntervals], seg_meta[2];
+
+  const int g = blockIdx.y;
+  const int split = blockIdx.x;
+  const int b = g / a.Hkv, kvh = g % a.Hkv;
+  const int lrow = a.lrow_is_batch ? b : g;
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  const int sub = lane % LPR, slot = lane / LPR;
+  const int sid = wid * SPW + slot;
+
+  int cnt;
+  if constexpr (MODE == kListIntervals) {
+    if (wid == 0) {
+      int c = a.count[lrow];
+      c = max(0, min(c, (int)min<int64_t>(a.list_ld, kMaxIntervals - 2)));
+      build_segments(a, a.list + (int64_t)lrow * a.list_ld, c, seg_start, seg_pos, &seg_meta[0],
+                     &seg_meta[1]);
+    }
+    __syncthreads();
+    cnt = seg_meta[1];
+    if (split == 0 && threadIdx.x == 0) a.ucount[g] = cnt;
+  } else {
+    cnt = a.count[lrow];
+    cnt = max(0, min(cnt, a.count_clamp));
+  }
+  const int r0 = split * a.R;
+  if (r0 >= cnt) return;
+  const int r1 = min(r0 + a.R, cnt);
+  const int nrows = r1 - r0;
+
+  // row table: every row's resolved slot (and list mask) staged once in LDS
+  {
+    const int32_t* list = a.list + (int64_t)lrow * a.list_ld;
+    const uint32_t* mrow = kMask ? a.mask + (int64_t)g * a.list_ld : nullptr;
+    for (int i = threadIdx.x; i < nrows; i += kThreads) {
+      int tok;
+      if constexpr (MODE == kListIntervals) tok = token_at(seg_start, seg_pos, seg_meta[0], r0 + i);
+      else tok = list[r0 + i];
+      slot_s[i] = resolve_slot(a, b, kvh, tok);
+      if constexpr (kMask) mask_s[i] = mrow[r0 + i];
+    }
+  }
+
+  // query slices, pre-scaled into the exp2 domain
+  float qs[NQ][8];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    if (n < a.nq) {
+      const int t = n / a.G, hl = n % a.G;
+      const int64_t off = ((int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl) * D + sub * 8;
+      if (a.q_bf16) load8f(reinterpret_cast<const uint16_t*>(a.q) + off, qs[n]);
+      else load8f(reinterpret_cast<const float*>(a.q) + off, qs[n]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qs[n][i] *= a.scale_log2;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qs[n][i] = 0.f;
+    }
+  }
+  float m[NQ], l[NQ], acc[NQ][8];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    m[n] = -INFINITY;
+    l[n] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[n][i] = 0.f;
+  }
+  __syncthreads();
+
+  const int iters = (nrows + STEP - 1) / STEP;
+  auto issue = [&](int it, Raw8<KT> (&rk)[U], Raw8<KT> (&rv)[U], int (&sl)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = it * STEP + u * NSLOT + sid;
+      sl[u] = p < nrows ? slot_s[p] : kDead;
+      if (sl[u] != kDead) {
+        rk[u].load(row_ptr<KT>(a, a.k, a.k_host, b, kvh, sl[u]) + sub * 8);
+        rv[u].load(row_ptr<KT>(a, a.v, a.v_host, b, kvh, sl[u]) + sub * 8);
+      } else {
+        rk[u].zero();
+        rv[u].zero();
+      }
+    }
+  };
+  auto consume = [&](int it, const Raw8<KT> (&rk)[U], const Raw8<KT> (&rv)[U],
+                     const int (&sl)[U]) {
+    float lg[U][NQ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = it * STEP + u * NSLOT + sid;
+      uint32_t mb = 0xFFFFFFFFu;
+      if constexpr (kMask) mb = p < nrows ? mask_s[p] : 0u;
+      float x[8];
+      rk[u].to_float(x);
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(qs[n][i], x[i], s);
+        s = group_sum<LPR>(s);
+        const bool reads = sl[u] != kDead && (!kMask || ((mb >> (n / a.mask_div)) & 1u));
+        lg[u][n] = reads ? s : -INFINITY;
+      }
+      if (a.logits && p < nrows) {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+          if (n % LPR == sub && n < a.nq) {
+            const int t = n / a.G, hl = n % a.G;
+            const int64_t row = (int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl;
+            a.logits[row * a.logits_ld + r0 + p] = lg[u][n] * kLn2;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      float mx = m[n];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, lg[u][n]);
+      const float sc = (mx == -INFINITY) ? 0.f : fast_exp2(m[n] - mx);
+      l[n] *= sc;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[n][i] *= sc;
+      m[n] = mx;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float y[8];
+      rv[u].to_float(y);
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        const float p = (m[n] == -INFINITY) ? 0.f : fast_exp2(lg[u][n] - m[n]);
+        l[n] += p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[n][i] = fmaf(p, y[i], acc[n][i]);
+      }
+    }
+  };
+
+  {
+    Raw8<KT> k0[U], v0[U], k1[U], v1[U];
+    int s0[U], s1[U];
+    issue(0, k0, v0, s0);
+    for (int it = 0; it < iters; it += 2) {
+      if (it + 1 < iters) issue(it + 1, k1, v1, s1);
+      consume(it, k0, v0, s0);
+      if (it + 1 >= iters) break;
+      if (it + 2 < iters) issue(it + 2, k0, v0, s0);
+      consume(it + 1, k1, v1, s1);
+    }
+  }
+
+  // merge the slots of this wave (lanes with equal `sub` hold the same dims)
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const float mo = __shfl_xor(m[n], off, kWave);
+      const float lo = __shfl_xor(l[n], off, kWave);
+      const float mx = fmaxf(m[n], mo);
+      const float sa = (mx == -INFINITY) ? 0.f : fast_exp2(m[n] - mx);
+      const float sb = (mx == -INFINITY) ? 0.f : fast_exp2(mo - mx);
+      l[n] = l[n] * sa + lo * sb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float ao = __shfl_xor(acc[n][i], off, kWave);
+        acc[n][i] = acc[n][i] * sa + ao * sb;
+      }
+      m[n] = mx;
+    }
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wid][n][2 + sub * 8 + i] = acc[n][i];
+      if (sub == 0) {
+        red[wid][n][0] = m[n];
+        red[wid][n][1] = l[n];
+      }
+    }
+  }
+  __syncthreads();
+  // merge the waves; thread -> (n, dim)
+  const int64_t pbase = ((int64_t)g * a.smax + split) * NQ;
+  for (int e = threadIdx.x; e < NQ * D; e += kThreads) {
+    const int n = e / D, dim = e % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w][n][0]);
+    float ls = 0.f, as = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = (mx == -INFINITY) ? 0.f : fast_exp2(red[w][n][0] - mx);
+      ls += red[w][n][1] * sc;
+      as += red[w][n][2 + dim] * sc;
+    }
+    a.acc[(pbase + n) * D + dim] = as;
+    if (dim == 0) {
+      a.ml[(pbase + n) * 2] = mx;
+      a.ml[(pbase + n) * 2 + 1] = ls;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------- combine
+
+// One wave per query vector: lanes fetch the splits' (m, l) in parallel, then each lane sums
+// its dims over the splits in split order (fixed order: deterministic).
+template <int D>
+__global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a, int nq_pad, float* out,
+                                                             float* lse) {
+  __shared__ float wsc[kWave];
+  const int g = blockIdx.x / a.nq;
+  const int n = blockIdx.x % a.nq;
+  const int b = g / a.Hkv, kvh = g % a.Hkv;
+  const int lane = lane_id();
+  int cnt;
+  if (a.list_mode == kListIntervals) {
+    cnt = a.ucount[g];
+  } else {
+    const int lrow = a.lrow_is_batch ? b : g;
+    cnt = max(0, min(a.count[lrow], a.count_clamp));
+  }
+  const int S = cnt > 0 ? (cnt + a.R - 1) / a.R : 0;
+  const int64_t pbase = (int64_t)g * a.smax * nq_pad + n;
+  constexpr int PER = D / kWave;
+  float o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  float mx = -INFINITY;
+  for (int s0 = lane; s0 < S; s0 += kWave) mx = fmaxf(mx, a.ml[(pbase + (int64_t)s0 * nq_pad) * 2]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+  float L = 0.f;
+  for (int c0 = 0; c0 < S; c0 += kWave) {
+    const int s = c0 + lane;
+    float w = 0.f;
+    if (s < S && mx != -INFINITY) {
+      const int64_t pi = pbase + (int64_t)s * nq_pad;
+      w = fast_exp2(a.ml[pi * 2] - mx);
+      L += a.ml[pi * 2 + 1] * w;
+    }
+    wsc[lane] = w;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const int cs = min(kWave, S - c0);
+    int j = 0;
+    for (; j + 4 <= cs; j += 4) {
+      float v[4][PER];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          v[jj][i] = a.acc[(pbase + (int64_t)(c0 + j + jj) * nq_pad) * D + lane + i * kWave];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] += v[jj][i] * wsc[j + jj];
+    }
+    for (; j < cs; ++j)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        o[i] += a.acc[(pbase + (int64_t)(c0 + j) * nq_pad) * D + lane + i * kWave] * wsc[j];
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, kWave);
+  const int t = n / a.G, hl = n % a.G;
+  const int64_t qrow = (int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl;
+  const bool empty = !(L > 0.f);
+  const float inv = empty ? 0.f : 1.0f / L;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) out[qrow * D + lane + i * kWave] = o[i] * inv;
+  if (lse && lane == 0) lse[qrow] = empty ? -INFINITY : (mx + log2f(L)) * kLn2;
+}
+
+template <int D, typename KT, int NQ, bool kMask, int MODE>
+void launch_partial(dim3 grid, hipStream_t st, const AttnArgs& a) {
+  constexpr int U = NQ <= 4 ? 4 : 2;
+  hipLaunchKernelGGL((attn_partial_kernel<D, KT, NQ, kMask, MODE, U>), grid, dim3(kThreads), 0, st,
+                     a);
+}
+
+template <int D, typename KT, int NQ>
+void dispatch_mode(bool mask, int mode, dim3 grid, hipStream_t st, const AttnArgs& a) {
+  if (mask) launch_partial<D, KT, NQ, true, kListExplicit>(grid, st, a);
+  else if (mode == kListIntervals) launch_partial<D, KT, NQ, false, kListIntervals>(grid, st, a);
+  else launch_partial<D, KT, NQ, false, kListExplicit>(grid, st, a);
+}
+
+template <int D, typename KT>
+void dispatch_nq(int nq_pad, bool mask, int mode, dim3 grid, hipStream_t st, const AttnArgs& a) {
+  switch (nq_pad) {
+    case 1: dispatch_mode<D, KT, 1>(mask, mode, grid, st, a); break;
+    case 2: dispatch_mode<D, KT, 2>(mask, mode, grid, st, a); break;
+    case 4: dispatch_mode<D, KT, 4>(mask, mode, grid, st, a); break;
+    case 8: dispatch_mode<D, KT, 8>(mask, mode, grid, st, a); break;
+    default: dispatch_mode<D, KT, 16>(mask, mode, grid, st, a); break;
+  }
+}
+
+// Resident partial workgroups per CU for the bf16 instance of a configuration (queried once).
+int partial_occupancy(int d, int nq_pad, bool mask, int mode) {
+  static int cache[2][5][2][2];
+  const int di = d == 128 ? 0 : 1;
+  const int ni = nq_pad == 1 ? 0 : nq_pad == 2 ? 1 : nq_pad == 4 ? 2 : nq_pad == 8 ? 3 : 4;
+  int& c = cache[di][ni][mask ? 1 : 0][mode ? 1 : 0];
+  if (c > 0) return c;
+  const void* fn = nullptr;
+#define SPK_FN(D, NQ)                                                                          \
+  fn = mask ? (const void*)attn_partial_kernel<D, uint16_t, NQ, true, kListExplicit, (NQ <= 4 ? 4 : 2)>   \
+       : mode ? (const void*)attn_partial_kernel<D, uint16_t, NQ, false, kListIntervals, (NQ <= 4 ? 4 : 2)> \
+              : (const void*)attn_partial_kernel<D, uint16_t, NQ, false, kListExplicit, (NQ <= 4 ? 4 : 2)>
+#define SPK_FN_D(D)                     \
+  switch (nq_pad) {                     \
+    case 1: SPK_FN(D, 1); break;        \
+    case 2: SPK_FN(D, 2); break;        \
+    case 4: SPK_FN(D, 4); break;        \
+    case 8: SPK_FN(D, 8); break;        \
+    default: SPK_FN(D, 16); break;      \
+  }
+  if (d == 128) {
+    SPK_FN_D(128)
+  } else {
+    SPK_FN_D(64)
+  }
+#undef SPK_FN_D
+#undef SPK_FN
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, 0) != hipSuccess ||
+      blocks <= 0) {
+    (void)hipGetLastError();
+    blocks = 2;
+  }
+  c = blocks;
+  return c;
+}
+
+}  // namespace
+}  // namespace spk
+
+using spk::Plan;
+
+// A host pool must be page-locked, device-mapped host memory; the kernel reads it through the
+// device address HIP reports for it.  Pageable memory would fault, so it is refused here.
+static spk_status resolve_host_pool(const void* p, const void** dev, const char* name) {
+  hipPointerAttribute_t at{};
+  const hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return spk::set_error(SPK_EINVAL, "sparse_decode_attn: %s is not memory known to HIP (%s)",
+                          name, hipGetErrorString(e));
+  }
+  if (at.type != hipMemoryTypeHost || at.devicePointer == nullptr)
+    return spk::set_error(SPK_EINVAL,
+                          "sparse_decode_attn: %s must be pinned, device-mapped host memory", name);
+  *dev = at.devicePointer;
+  return SPK_OK;
+}
+
+static spk_status check_common(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d,
+                               int n_tokens, int64_t sel_ld, int gran, int n_sink, int n_recent) {
+  using namespace spk;
+  SPK_REQUIRE(scope >= SPK_SEL_PER_SEQ && scope <= SPK_SEL_PER_Q_HEAD, SPK_EINVAL,
+              "sparse_decode_attn: unknown scope %d", (int)scope);
+  SPK_REQUIRE(B >= 0 && T > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0, SPK_EINVAL,
+              "sparse_decode_attn: bad shape B=%d T=%d Hq=%d Hkv=%d (Hq %% Hkv must be 0)", B, T,
+              Hq, Hkv);
+  SPK_REQUIRE(d == 64 || d == 128, SPK_EUNSUPPORTED, "sparse_decode_attn: d=%d not in {64,128}", d);
+  SPK_REQUIRE(n_tokens >= 0 && sel_ld >= 0 && gran >= 1 && n_sink >= 0 && n_recent >= 0,
+              SPK_EINVAL, "sparse_decode_attn: negative size or gran < 1");
+  SPK_REQUIRE(n_tokens < (1 << 30) && sel_ld < (1 << 30) && gran < (1 << 20), SPK_EINVAL,
+              "sparse_decode_attn: size out of range");
+  const int G = Hq / Hkv;
+  SPK_REQUIRE(G * T <= 16, SPK_EUNSUPPORTED,
+              "sparse_decode_attn: %d query vectors per KV head (max 16)", G * T);
+  const int sets = scope == SPK_SEL_PER_SEQ ? 1 : scope == SPK_SEL_PER_KV_HEAD ? T : T * G;
+  SPK_REQUIRE(sets <= spk::kMaxSets, SPK_EUNSUPPORTED,
+              "sparse_decode_attn: %d selection lists per group (max 32)", sets);
+  return SPK_OK;
+}
+
+extern "C" SPK_API spk_status sparse_decode_attn_workspace_size(
+    spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_tokens, int64_t sel_ld,
+    int gran, int n_sink, int n_recent, size_t* bytes) {
+  using namespace spk;
+  SPK_REQUIRE(bytes, SPK_EINVAL, "sparse_decode_attn_workspace_size: null bytes");
+  spk_status st = check_common(scope, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent);
+  if (st != SPK_OK) return st;
+  *bytes = make_plan(scope, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent).bytes;
+  clear_error();
+  return SPK_OK;
+}
+
+extern "C" SPK_API spk_status sparse_decode_attn(
+    const void* q, spk_dtype q_dtype, const void* k, const void* v, spk_dtype kv_dtype,
+    int64_t kv_sb, int64_t kv_sh, int64_t kv_sn, const void* k_host, const void* v_host,
+    int64_t host_sb, int64_t host_sh, int64_t host_sn, int64_t host_slots, const int32_t* loc,
+    int64_t loc_sb, int64_t loc_sh, int64_t hbm_slots, const int32_t* sel_idx, const int32_t* sel_count, int64_t sel_ld,
+    spk_sel_scope scope, int gran, int n_sink, int n_recent, int B, int T, int Hq, int Hkv, int d,
+    int n_tokens, float sm_scale, float* out, float* lse, float* logits, int64_t logits_ld,
+    void* ws, size_t ws_bytes, void* stream) {
+  using namespace spk;
+  spk_status st0 = check_common(scope, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent);
+  if (st0 != SPK_OK) return st0;
+  SPK_REQUIRE(dtype_ok(q_dtype) && dtype_ok(kv_dtype), SPK_EUNSUPPORTED,
+              "sparse_decode_attn: unsupported dtype");
+  SPK_REQUIRE(B == 0 || (q && k && v && out && sel_idx && sel_count), SPK_EINVAL,
+              "sparse_decode_attn: null q, k, v, out, sel_idx or sel_count");
+  SPK_REQUIRE(kv_sn >= d && kv_sb >= 0 && kv_sh >= 0 && kv_sn % 8 == 0 && kv_sh % 8 == 0 &&
+                  kv_sb % 8 == 0,
+              SPK_EINVAL, "sparse_decode_attn: kv strides must be multiples of 8 with kv_sn >= d");
+  SPK_REQUIRE(reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(k) % 16 == 0 &&
+                  reinterpret_cast<uintptr_t>(v) % 16 == 0,
+              SPK_EINVAL, "sparse_decode_attn: q, k, v must be 16-byte aligned");
+  if (loc) {
+    SPK_REQUIRE(k_host && v_host, SPK_EINVAL,
+                "sparse_decode_attn: loc given without host pools k_host/v_host");
+    SPK_REQUIRE(host_sn >= d && host_sb >= 0 && host_sh >= 0 && host_sn % 8 == 0 &&
+                    host_sh % 8 == 0 && host_sb % 8 == 0,
+                SPK_EINVAL, "sparse_decode_attn: host strides must be multiples of 8");
+    SPK_REQUIRE(reinterpret_cast<uintptr_t>(k_host) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(v_host) % 16 == 0,
+                SPK_EINVAL, "sparse_decode_attn: host pools must be 16-byte aligned");
+    SPK_REQUIRE(loc_sb >= 0 && loc_sh >= 0 && host_slots >= 0 && host_slots < INT32_MAX &&
+                    hbm_slots >= 0,
+                SPK_EINVAL,
+                "sparse_decode_attn: bad loc strides or slot counts");
+    spk_status hs = resolve_host_pool(k_host, &k_host, "k_host");
+    if (hs != SPK_OK) return hs;
+    hs = resolve_host_pool(v_host, &v_host, "v_host");
+    if (hs != SPK_OK) return hs;
+  }
+  SPK_REQUIRE(loc || n_tokens <= hbm_slots, SPK_EINVAL,
+              "sparse_decode_attn: n_tokens %d exceeds the %lld rows of the HBM caches", n_tokens,
+              (long long)hbm_slots);
+  SPK_REQUIRE(!(sm_scale != sm_scale), SPK_EINVAL, "sparse_decode_attn: sm_scale is NaN");
+  const Plan p = make_plan(scope, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent);
+  SPK_REQUIRE(!logits || logits_ld >= p.ubound, SPK_EINVAL,
+              "sparse_decode_attn: logits_ld %lld < fetch-list bound %d", (long long)logits_ld,
+              p.ubound);
+  SPK_REQUIRE(ws_bytes >= p.bytes && (p.bytes == 0 || ws), SPK_EWORKSPACE,
+              "sparse_decode_attn: workspace %zu bytes < %zu needed", ws_bytes, p.bytes);
+  clear_error();
+  if (B == 0) return SPK_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* w = reinterpret_cast<char*>(ws);
+  const int G = Hq / Hkv;
+
+  AttnArgs a{};
+  a.q = q;
+  a.q_bf16 = q_dtype == SPK_BF16;
+  a.k = k;
+  a.v = v;
+  a.kv_sb = kv_sb;
+  a.kv_sh = kv_sh;
+  a.kv_sn = kv_sn;
+  a.k_host = k_host;
+  a.v_host = v_host;
+  a.host_sb = host_sb;
+  a.host_sh = host_sh;
+  a.host_sn = host_sn;
+  a.host_slots = host_slots;
+  a.loc = loc;
+  a.loc_sb = loc_sb;
+  a.loc_sh = loc_sh;
+  a.hbm_slots = hbm_slots;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.nq = G * T;
+  a.n_tokens = n_tokens;
+  a.R = p.R;
+  a.smax = p.smax;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.ml = reinterpret_cast<float*>(w + p.off_ml);
+  a.acc = reinterpret_cast<float*>(w + p.off_acc);
+  a.logits = logits;
+  a.logits_ld = logits_ld;
+  a.mask = nullptr;
+  a.mask_div = scope == SPK_SEL_PER_KV_HEAD ? G : 1;
+
+  a.list_mode = kListExplicit;
+  a.gran = gran;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.ucount = p.assemble || p.intervals ? reinterpret_cast<int32_t*>(w + p.off_count) : nullptr;
+  if (p.assemble) {
+    AsmArgs as{};
+    as.sel_idx = sel_idx;
+    as.sel_count = sel_count;
+    as.sel_ld = sel_ld;
+    as.scope = scope;
+    as.gran = gran;
+    as.n_sink = n_sink;
+    as.n_recent = n_recent;
+    as.T = T;
+    as.Hq = Hq;
+    as.Hkv = Hkv;
+    as.G = G;
+    as.sets = p.sets;
+    as.n_tokens = n_tokens;
+    as.words = p.words;
+    as.ubound = p.ubound;
+    as.bm_global = p.bm_lds ? nullptr : reinterpret_cast<uint32_t*>(w + p.off_bm);
+    as.ulist = reinterpret_cast<int32_t*>(w + p.off_list);
+    as.umask = p.mask ? reinterpret_cast<uint32_t*>(w + p.off_mask) : nullptr;
+    as.ucount = a.ucount;
+    const size_t lds = p.bm_lds ? (size_t)p.sets * p.words * 4 : 0;
+    hipLaunchKernelGGL(assemble_kernel, dim3(p.groups), dim3(kThreads), lds, st, as);
+    spk_status e = check_launch("sparse_decode_attn/assemble");
+    if (e != SPK_OK) return e;
+    a.list = as.ulist;
+    a.count = as.ucount;
+    a.list_ld = p.ubound;
+    a.count_clamp = p.ubound;
+    a.lrow_is_batch = 0;
+    a.mask = as.umask;
+  } else if (p.intervals) {
+    a.list_mode = kListIntervals;
+    a.list = sel_idx;
+    a.count = sel_count;
+    a.list_ld = sel_ld;
+    a.count_clamp = p.ubound;
+    a.lrow_is_batch = scope == SPK_SEL_PER_SEQ;
+  } else {
+    a.list = sel_idx;
+    a.count = sel_count;
+    a.list_ld = sel_ld;
+    a.count_clamp = (int)(sel_ld < p.ubound ? sel_ld : p.ubound);
+    a.lrow_is_batch = scope == SPK_SEL_PER_SEQ;
+  }
+  dim3 grid(p.smax, p.groups);
+  const bool mask = p.mask;
+  if (d == 128) {
+    if (kv_dtype == SPK_BF16) dispatch_nq<128, uint16_t>(p.nq_pad, mask, a.list_mode, grid, st, a);
+    else dispatch_nq<128, float>(p.nq_pad, mask, a.list_mode, grid, st, a);
+  } else {
+    if (kv_dtype == SPK_BF16) dispatch_nq<64, uint16_t>(p.nq_pad, mask, a.list_mode, grid, st, a);
+    else dispatch_nq<64, float>(p.nq_pad, mask, a.list_mode, grid, st, a);
+  }
+  spk_status e = check_launch("sparse_decode_attn/partial");
+  if (e != SPK_OK) return e;
+  if (d == 128)
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(p.groups * a.nq), dim3(kWave), 0, st, a,
+                       p.nq_pad, out, lse);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(p.groups * a.nq), dim3(kWave), 0, st, a,
+                       p.nq_pad, out, lse);
+  return check_launch("sparse_decode_attn/combine");
+}

@@ -1,0 +1,335 @@
+// sparse_index_score: compact indexer scores (no softmax) for token and block candidates.
+//
+// SparDA: Atenção Esparsa Desacoplada, §2 "Indexador de Previsão Compacto": one predictor head
+// per GQA group (per KV head) scores the cached keys, with no per-query-head loop and no softmax;
+// "Seleção Esparsa de Lookahead Treinável": the predictor ranks KV blocks.
+// "Esparsidade de Contexto no Tempo de Inferência", §2 "Oracle Top-K": exact per-head scores.
+//
+// Work layout (HBM-bound streaming of key rows): a workgroup owns a run of candidate rows of one
+// (b, kvh) group.  D/8 lanes share a row, each loading 16 B (8 bf16) or 32 B (8 fp32) of it, so a
+// wave reads 4 (d=128) or 8 (d=64) rows per load instruction, fully coalesced.  Each lane keeps
+// the 8-dim slice of every query vector the group scores (NS <= 16 of them) in registers, forms
+// partial dots, and a 16-lane DPP reduction finishes them.  Scores are staged in LDS and written
+// back as contiguous runs per output row.
+#include "spk_internal.h"
+
+namespace spk {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int kMaxRowsPerWg = 256;
+
+// Fetch 8 elements [off, off+8) of the query tensor as floats.
+__device__ __forceinline__ void load_q8(const void* q, int q_bf16, int64_t off, float (&x)[8]) {
+  if (q_bf16) {
+    load8f(reinterpret_cast<const uint16_t*>(q) + off, x);
+  } else {
+    load8f(reinterpret_cast<const float*>(q) + off, x);
+  }
+}
+
+// The 8-dim slice `sub` of query vector n of group (b, kvh), per indexer mode.
+template <int D>
+__device__ __forceinline__ void query_slice(int mode, const void* q, int q_bf16, int b, int kvh,
+                                            int n, int T, int Hq, int Hkv, int G, int sub,
+                                            float (&x)[8]) {
+  if (mode == SPK_IDX_TOKEN_GROUP_MEAN) {
+    // mean over the G heads of kvh at token t = n
+    float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int hl = 0; hl < G; ++hl) {
+      float y[8];
+      load_q8(q, q_bf16, ((int64_t)(b * T + n) * Hq + kvh * G + hl) * D + sub * 8, y);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] += y[i];
+    }
+    const float inv = 1.0f / (float)G;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = s[i] * inv;
+  } else if (mode == SPK_IDX_TOKEN_PER_HEAD) {
+    const int t = n / G, hl = n % G;
+    load_q8(q, q_bf16, ((int64_t)(b * T + t) * Hq + kvh * G + hl) * D + sub * 8, x);
+  } else {  // block modes: one predictor per (b, t, kvh)
+    load_q8(q, q_bf16, ((int64_t)(b * T + n) * Hkv + kvh) * D + sub * 8, x);
+  }
+}
+
+// Output row of score vector n of group (b, kvh).
+__device__ __forceinline__ int64_t score_row(int mode, int b, int kvh, int n, int T, int Hq,
+                                             int Hkv, int G) {
+  if (mode == SPK_IDX_TOKEN_PER_HEAD) {
+    const int t = n / G, hl = n % G;
+    return (int64_t)(b * T + t) * Hq + kvh * G + hl;
+  }
+  return (int64_t)(b * T + n) * Hkv + kvh;
+}
+
+template <int D, typename KT, int NS>
+__global__ __launch_bounds__(kThreads) void index_rows_kernel(
+    int mode, const void* __restrict__ q, int q_bf16, const KT* __restrict__ keys, int64_t k_sb,
+    int64_t k_sh, int64_t k_sn, int T, int Hq, int Hkv, int G, int ns, int n_cand,
+    int rows_per_wg, float* __restrict__ scores, int64_t s_ld) {
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPS = kWave / LPR;    // rows per wave per load
+  constexpr int WAVES = kThreads / kWave;
+  constexpr int STEP = WAVES * RPS;   // rows per workgroup per load
+  __shared__ float tile[NS][kMaxRowsPerWg];
+
+  const int group = blockIdx.y;
+  const int b = group / Hkv, kvh = group % Hkv;
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  const int sub = lane % LPR, slot = lane / LPR;
+  const int row0 = blockIdx.x * rows_per_wg;
+  const int row1 = min(row0 + rows_per_wg, n_cand);
+  if (row0 >= n_cand) return;
+
+  float qv[NS][8];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    if (n < ns) {
+      query_slice<D>(mode, q, q_bf16, b, kvh, n, T, Hq, Hkv, G, sub, qv[n]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[n][i] = 0.f;
+    }
+  }
+
+  const KT* base_ptr = keys + (int64_t)b * k_sb + (int64_t)kvh * k_sh + sub * 8;
+  for (int base = row0; base < row1; base += STEP * kUnroll) {
+    Raw8<KT> raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int row = base + (u * WAVES + wid) * RPS + slot;
+      if (row < row1) raw[u].load(base_ptr + (int64_t)row * k_sn);
+      else raw[u].zero();
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int row = base + (u * WAVES + wid) * RPS + slot;
+      float x[8];
+      raw[u].to_float(x);
+      float acc[NS];
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaf(qv[n][i], x[i], a);
+        acc[n] = group_sum<LPR>(a);
+      }
+      if (row < row1) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n)
+          if (n % LPR == sub && n < ns) tile[n][row - row0] = acc[n];
+      }
+    }
+  }
+  __syncthreads();
+  const int cnt = row1 - row0;
+  for (int i = threadIdx.x; i < ns * cnt; i += kThreads) {
+    const int n = i / cnt, r = i % cnt;
+    scores[score_row(mode, b, kvh, n, T, Hq, Hkv, G) * s_ld + row0 + r] = tile[n][r];
+  }
+}
+
+// Block mode over raw keys: each 16-lane slot pools one block (mean of block_size rows), scores
+// it against the predictor(s) and optionally stores the pooled key.
+template <int D, typename KT, int NS>
+__global__ __launch_bounds__(kThreads) void index_blockraw_kernel(
+    const void* __restrict__ q, int q_bf16, const KT* __restrict__ keys, int64_t k_sb,
+    int64_t k_sh, int64_t k_sn, int T, int Hkv, int ns, int n_blocks, int bs,
+    int blocks_per_wg, float* __restrict__ scores, int64_t s_ld, float* __restrict__ pooled) {
+  constexpr int LPR = D / 8;
+  constexpr int RPS = kWave / LPR;
+  constexpr int WAVES = kThreads / kWave;
+  constexpr int STEP = WAVES * RPS;
+  __shared__ float tile[NS][kMaxRowsPerWg];
+
+  const int group = blockIdx.y;
+  const int b = group / Hkv, kvh = group % Hkv;
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  const int sub = lane % LPR, slot = lane / LPR;
+  const int j0 = blockIdx.x * blocks_per_wg;
+  const int j1 = min(j0 + blocks_per_wg, n_blocks);
+  if (j0 >= n_blocks) return;
+
+  float qv[NS][8];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    if (n < ns) {
+      query_slice<D>(SPK_IDX_BLOCK_RAW, q, q_bf16, b, kvh, n, T, 0, Hkv, 1, sub, qv[n]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[n][i] = 0.f;
+    }
+  }
+  const KT* gbase = keys + (int64_t)b * k_sb + (int64_t)kvh * k_sh + sub * 8;
+  for (int jb = j0; jb < j1; jb += STEP) {
+    const int j = jb + wid * RPS + slot;
+    const bool live = j < j1;
+    float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (live) {
+      const KT* p = gbase + (int64_t)j * bs * k_sn;
+      int r = 0;
+      for (; r + kUnroll <= bs; r += kUnroll) {
+        Raw8<KT> raw[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) raw[u].load(p + (int64_t)(r + u) * k_sn);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          float x[8];
+          raw[u].to_float(x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s[i] += x[i];
+        }
+      }
+      for (; r < bs; ++r) {
+        float x[8];
+        load8f(p + (int64_t)r * k_sn, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] += x[i];
+      }
+    }
+    float mean[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mean[i] = s[i] / (float)bs;
+    if (live && pooled) {
+      float* dst = pooled + ((int64_t)group * n_blocks + j) * D + sub * 8;
+      *reinterpret_cast<float4*>(dst) = make_float4(mean[0], mean[1], mean[2], mean[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(mean[4], mean[5], mean[6], mean[7]);
+    }
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaf(qv[n][i], mean[i], a);
+      a = group_sum<LPR>(a);
+      if (live && n % LPR == sub && n < ns) tile[n][j - j0] = a;
+    }
+  }
+  __syncthreads();
+  const int cnt = j1 - j0;
+  for (int i = threadIdx.x; i < ns * cnt; i += kThreads) {
+    const int n = i / cnt, r = i % cnt;
+    scores[((int64_t)(b * T + n) * Hkv + kvh) * s_ld + j0 + r] = tile[n][r];
+  }
+}
+
+template <int D, typename KT>
+spk_status launch_rows(int ns_pad, dim3 grid, hipStream_t st, int mode, const void* q, int q_bf16,
+                       const void* keys, int64_t k_sb, int64_t k_sh, int64_t k_sn, int T, int Hq,
+                       int Hkv, int G, int ns, int n_cand, int rpw, float* scores, int64_t s_ld) {
+  const KT* kp = reinterpret_cast<const KT*>(keys);
+#define SPK_ROWS(NSV)                                                                         \
+  hipLaunchKernelGGL((index_rows_kernel<D, KT, NSV>), grid, dim3(kThreads), 0, st, mode, q, \
+                     q_bf16, kp, k_sb, k_sh, k_sn, T, Hq, Hkv, G, ns, n_cand, rpw, scores, s_ld)
+  switch (ns_pad) {
+    case 1: SPK_ROWS(1); break;
+    case 4: SPK_ROWS(4); break;
+    case 8: SPK_ROWS(8); break;
+    default: SPK_ROWS(16); break;
+  }
+#undef SPK_ROWS
+  return check_launch("sparse_index_score");
+}
+
+template <int D, typename KT>
+spk_status launch_blockraw(int ns_pad, dim3 grid, hipStream_t st, const void* q, int q_bf16,
+                           const void* keys, int64_t k_sb, int64_t k_sh, int64_t k_sn, int T,
+                           int Hkv, int ns, int n_blocks, int bs, int bpw, float* scores,
+                           int64_t s_ld, float* pooled) {
+  const KT* kp = reinterpret_cast<const KT*>(keys);
+#define SPK_RAW(NSV)                                                                           \
+  hipLaunchKernelGGL((index_blockraw_kernel<D, KT, NSV>), grid, dim3(kThreads), 0, st, q,     \
+                     q_bf16, kp, k_sb, k_sh, k_sn, T, Hkv, ns, n_blocks, bs, bpw, scores, s_ld, \
+                     pooled)
+  switch (ns_pad) {
+    case 1: SPK_RAW(1); break;
+    case 4: SPK_RAW(4); break;
+    case 8: SPK_RAW(8); break;
+    default: SPK_RAW(16); break;
+  }
+#undef SPK_RAW
+  return check_launch("sparse_index_score");
+}
+
+int pad_ns(int ns) { return ns <= 1 ? 1 : ns <= 4 ? 4 : ns <= 8 ? 8 : 16; }
+
+// Rows per workgroup: enough workgroups to fill the chip several times over, within 16..256.
+int pick_rows_per_wg(int64_t rows_total, int step) {
+  const int64_t target_wgs = 4LL * num_cus();
+  int rpw = kMaxRowsPerWg;
+  while (rpw > step && rows_total / rpw < target_wgs) rpw /= 2;
+  return rpw;
+}
+
+}  // namespace
+}  // namespace spk
+
+extern "C" SPK_API spk_status sparse_index_score(spk_index_mode mode, const void* q,
+                                                 spk_dtype q_dtype, const void* keys,
+                                                 spk_dtype k_dtype, int64_t k_sb, int64_t k_sh,
+                                                 int64_t k_sn, int B, int T, int Hq, int Hkv,
+                                                 int d, int n_tokens, int block_size,
+                                                 float* scores, int64_t s_ld, float* pooled_out,
+                                                 void* stream) {
+  using namespace spk;
+  SPK_REQUIRE(mode >= SPK_IDX_TOKEN_GROUP_MEAN && mode <= SPK_IDX_BLOCK_RAW, SPK_EINVAL,
+              "sparse_index_score: unknown mode %d", (int)mode);
+  SPK_REQUIRE(q && keys && scores, SPK_EINVAL, "sparse_index_score: null q, keys or scores");
+  SPK_REQUIRE(B > 0 && T > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0, SPK_EINVAL,
+              "sparse_index_score: bad heads/batch B=%d T=%d Hq=%d Hkv=%d", B, T, Hq, Hkv);
+  SPK_REQUIRE(dtype_ok(q_dtype) && dtype_ok(k_dtype), SPK_EUNSUPPORTED,
+              "sparse_index_score: unsupported dtype");
+  SPK_REQUIRE(d == 64 || d == 128, SPK_EUNSUPPORTED, "sparse_index_score: d=%d not in {64,128}", d);
+  SPK_REQUIRE(n_tokens >= 0, SPK_EINVAL, "sparse_index_score: n_tokens < 0");
+  const bool block = mode == SPK_IDX_BLOCK_POOLED || mode == SPK_IDX_BLOCK_RAW;
+  SPK_REQUIRE(!block || block_size >= 1, SPK_EINVAL, "sparse_index_score: block_size < 1");
+  SPK_REQUIRE(pooled_out == nullptr || mode == SPK_IDX_BLOCK_RAW, SPK_EINVAL,
+              "sparse_index_score: pooled_out is only written in BLOCK_RAW mode");
+  SPK_REQUIRE(k_sn >= d && k_sb >= 0 && k_sh >= 0 && k_sn % 8 == 0 && k_sh % 8 == 0 && k_sb % 8 == 0,
+              SPK_EINVAL, "sparse_index_score: key strides must be multiples of 8 with k_sn >= d");
+  SPK_REQUIRE(reinterpret_cast<uintptr_t>(keys) % 16 == 0 && reinterpret_cast<uintptr_t>(q) % 16 == 0,
+              SPK_EINVAL, "sparse_index_score: q and keys must be 16-byte aligned");
+  const int G = Hq / Hkv;
+  const int ns = mode == SPK_IDX_TOKEN_PER_HEAD ? T * G : T;
+  SPK_REQUIRE(ns <= 16, SPK_EUNSUPPORTED,
+              "sparse_index_score: %d score vectors per KV head (max 16)", ns);
+  const int n_cand = block ? n_tokens / block_size : n_tokens;
+  SPK_REQUIRE(s_ld >= n_cand, SPK_EINVAL, "sparse_index_score: s_ld %lld < candidates %d",
+              (long long)s_ld, n_cand);
+  clear_error();
+  if (n_cand == 0) return SPK_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int q_bf16 = q_dtype == SPK_BF16;
+  const int ns_pad = pad_ns(ns);
+  const int groups = B * Hkv;
+  const int step = 4 * (64 / (d / 8));
+  if (mode == SPK_IDX_BLOCK_RAW) {
+    const int bpw = pick_rows_per_wg((int64_t)n_cand * groups, step);
+    dim3 grid(ceil_div(n_cand, bpw), groups);
+    if (d == 128)
+      return k_dtype == SPK_BF16
+                 ? launch_blockraw<128, uint16_t>(ns_pad, grid, st, q, q_bf16, keys, k_sb, k_sh, k_sn, T,
+                                                  Hkv, ns, n_cand, block_size, bpw, scores, s_ld, pooled_out)
+                 : launch_blockraw<128, float>(ns_pad, grid, st, q, q_bf16, keys, k_sb, k_sh, k_sn, T,
+                                               Hkv, ns, n_cand, block_size, bpw, scores, s_ld, pooled_out);
+    return k_dtype == SPK_BF16
+               ? launch_blockraw<64, uint16_t>(ns_pad, grid, st, q, q_bf16, keys, k_sb, k_sh, k_sn, T,
+                                               Hkv, ns, n_cand, block_size, bpw, scores, s_ld, pooled_out)
+               : launch_blockraw<64, float>(ns_pad, grid, st, q, q_bf16, keys, k_sb, k_sh, k_sn, T,
+                                            Hkv, ns, n_cand, block_size, bpw, scores, s_ld, pooled_out);
+  }
+  const int rpw = pick_rows_per_wg((int64_t)n_cand * groups, step * kUnroll);
+  dim3 grid(ceil_div(n_cand, rpw), groups);
+  if (d == 128)
+    return k_dtype == SPK_BF16
+               ? launch_rows<128, uint16_t>(ns_pad, grid, st, mode, q, q_bf16, keys, k_sb, k_sh, k_sn, T,
+                                            Hq, Hkv, G, ns, n_cand, rpw, scores, s_ld)
+               : launch_rows<128, float>(ns_pad, grid, st, mode, q, q_bf16, keys, k_sb, k_sh, k_sn, T, Hq,
+                                         Hkv, G, ns, n_cand, rpw, scores, s_ld);
+  return k_dtype == SPK_BF16
+             ? launch_rows<64, uint16_t>(ns_pad, grid, st, mode, q, q_bf16, keys, k_sb, k_sh, k_sn, T, Hq,
+                                         Hkv, G, ns, n_cand, rpw, scores, s_ld)
+             : launch_rows<64, float>(ns_pad, grid, st, mode, q, q_bf16, keys, k_sb, k_sh, k_sn, T, Hq,
+                                      Hkv, G, ns, n_cand, rpw, scores, s_ld);
+}

@@ -1,0 +1,161 @@
+// tier_classify: T0 / T1 / T3 tiers by cumulative importance, sinks and recent window protected.
+//
+// "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro Níveis": protected
+// tokens and the most important ones stay in T0 (HBM); the middle goes to T1 (full precision in
+// host DDR, fetched before attention); only the least important tail is T3 (evicted for good).
+// §4: the classification is redone periodically; the period is the caller's loop.
+//
+// One workgroup (1024 threads) per sequence.  The unprotected tokens get order-preserving keys
+// (evicted or NaN -> 0, the lowest), two radix selects find the keys at ranks floor(M*t0/1000)
+// and floor(M*t01/1000), and one pass in index order assigns tiers (ties to the lower index),
+// marks new evictions and compacts the ascending T0 ∪ T1 list with block prefix sums.
+#include "select_common.h"
+
+namespace spk {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kItems = 16;
+
+template <int ITEMS>
+__global__ __launch_bounds__(kThreads) void tier_kernel(
+    const float* __restrict__ s_all, int64_t s_ld, int n, int n_sink, int n_recent, int p0,
+    int p01, uint8_t* __restrict__ evicted, int64_t ev_ld, uint8_t* __restrict__ tier_all,
+    int64_t tier_ld, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
+    int64_t sel_ld) {
+  __shared__ uint32_t hist[kThreads / kWave * 256];
+  __shared__ int sh[2];
+  __shared__ int scratch[kThreads / kWave + 1];
+  const int b = blockIdx.x;
+  const float* s = s_all + (int64_t)b * s_ld;
+  uint8_t* ev = evicted ? evicted + (int64_t)b * ev_ld : nullptr;
+  uint8_t* tier = tier_all + (int64_t)b * tier_ld;
+  const int lo = min(n_sink, n);
+  const int hi = max(lo, n - n_recent);
+  const int M = hi - lo;
+  const int n0 = (int)(((int64_t)M * p0) / 1000);
+  const int n01 = (int)(((int64_t)M * p01) / 1000);
+
+  auto key_of = [&](int i) -> uint32_t {
+    if (ev && ev[i]) return 0u;
+    return order_key(s[i]);
+  };
+  uint32_t reg[ITEMS > 0 ? ITEMS : 1];
+  if constexpr (ITEMS > 0) {
+#pragma unroll
+    for (int c = 0; c < ITEMS; ++c) {
+      const int i = c * kThreads + threadIdx.x;
+      reg[c] = (i >= lo && i < hi) ? key_of(i) : 0u;
+    }
+  }
+  auto for_each = [&](auto&& visit) {
+    if constexpr (ITEMS > 0) {
+#pragma unroll
+      for (int c = 0; c < ITEMS; ++c) {
+        const int i = c * kThreads + threadIdx.x;
+        if (i >= lo && i < hi) visit(reg[c]);
+      }
+    } else {
+      for (int i = lo + threadIdx.x; i < hi; i += kThreads) visit(key_of(i));
+    }
+  };
+  uint32_t thr0 = 0xFFFFFFFFu, thr1 = 0xFFFFFFFFu;
+  int need0 = 0, need1 = 0;
+  if (n0 > 0) radix_select<kThreads>(for_each, n0, hist, sh, &thr0, &need0);
+  if (n01 > 0) radix_select<kThreads>(for_each, n01, hist, sh, &thr1, &need1);
+
+  int run_eq0 = 0, run_eq1 = 0, run_sel = 0;
+  const int chunks = (n + kThreads - 1) / kThreads;
+  for (int c = 0; c < chunks; ++c) {
+    const int i = c * kThreads + threadIdx.x;
+    const bool valid = i < n;
+    const bool cand = i >= lo && i < hi;
+    uint32_t key = 0;
+    if (cand) {
+      if constexpr (ITEMS > 0) {
+#pragma unroll
+        for (int cc = 0; cc < ITEMS; ++cc)
+          if (cc == c) key = reg[cc];
+      } else {
+        key = key_of(i);
+      }
+    }
+    // ties at each threshold, counted over candidates in index order (evicted ones included:
+    // they hold ranks too)
+    const int eq0 = cand && n0 > 0 && key == thr0;
+    const int eq1 = cand && n01 > 0 && key == thr1;
+    int tot;
+    const int pre = block_excl_scan(eq0 | (eq1 << 16), scratch, &tot);
+    const int eqrank0 = run_eq0 + (pre & 0xFFFF);
+    const int eqrank1 = run_eq1 + (pre >> 16);
+    const bool is_ev = cand && ev && ev[i];
+    const bool top0 = cand && n0 > 0 && (key > thr0 || (eq0 && eqrank0 < need0));
+    const bool top1 = cand && n01 > 0 && (key > thr1 || (eq1 && eqrank1 < need1));
+    uint8_t t = 3;
+    if (!cand) t = 0;
+    else if (is_ev) t = 3;
+    else if (top0) t = 0;
+    else if (top1) t = 1;
+    const int sel = valid && t <= 1;
+    int tot_sel;
+    const int pos = block_excl_scan(sel, scratch, &tot_sel);
+    if (valid) {
+      tier[i] = t;
+      if (ev && t == 3) ev[i] = 1;
+      if (sel && sel_idx) sel_idx[(int64_t)b * sel_ld + run_sel + pos] = i;
+    }
+    run_eq0 += tot & 0xFFFF;
+    run_eq1 += tot >> 16;
+    run_sel += tot_sel;
+  }
+  if (sel_count && threadIdx.x == 0) sel_count[b] = run_sel;
+}
+
+}  // namespace
+}  // namespace spk
+
+extern "C" SPK_API spk_status tier_classify_workspace_size(int B, int n_tokens, size_t* bytes) {
+  using namespace spk;
+  SPK_REQUIRE(bytes, SPK_EINVAL, "tier_classify_workspace_size: null bytes");
+  SPK_REQUIRE(B >= 0 && n_tokens >= 0, SPK_EINVAL, "tier_classify_workspace_size: negative size");
+  *bytes = 0;
+  clear_error();
+  return SPK_OK;
+}
+
+extern "C" SPK_API spk_status tier_classify(const float* s, int64_t s_ld, int B, int n_tokens,
+                                            int n_sink, int n_recent, int t0_permille,
+                                            int t01_permille, uint8_t* evicted, int64_t ev_ld,
+                                            uint8_t* tier, int64_t tier_ld, int32_t* sel_idx,
+                                            int32_t* sel_count, int64_t sel_ld, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  using namespace spk;
+  (void)ws;
+  (void)ws_bytes;
+  SPK_REQUIRE(B >= 0 && n_tokens >= 0 && n_sink >= 0 && n_recent >= 0, SPK_EINVAL,
+              "tier_classify: negative size");
+  SPK_REQUIRE(n_tokens < (1 << 30), SPK_EINVAL, "tier_classify: n_tokens too large");
+  SPK_REQUIRE(0 <= t0_permille && t0_permille <= t01_permille && t01_permille <= 1000, SPK_EINVAL,
+              "tier_classify: need 0 <= t0_permille (%d) <= t01_permille (%d) <= 1000",
+              t0_permille, t01_permille);
+  SPK_REQUIRE(B == 0 || n_tokens == 0 || (s && tier), SPK_EINVAL, "tier_classify: null s or tier");
+  SPK_REQUIRE(s_ld >= n_tokens && tier_ld >= n_tokens, SPK_EINVAL,
+              "tier_classify: s_ld/tier_ld smaller than n_tokens");
+  SPK_REQUIRE(!evicted || ev_ld >= n_tokens, SPK_EINVAL, "tier_classify: ev_ld < n_tokens");
+  SPK_REQUIRE(!sel_idx || sel_ld >= n_tokens, SPK_EINVAL, "tier_classify: sel_ld < n_tokens");
+  SPK_REQUIRE((sel_idx == nullptr) == (sel_count == nullptr), SPK_EINVAL,
+              "tier_classify: sel_idx and sel_count go together");
+  clear_error();
+  if (B == 0) return SPK_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (n_tokens <= kItems * kThreads) {
+    hipLaunchKernelGGL(tier_kernel<kItems>, dim3(B), dim3(kThreads), 0, st, s, s_ld, n_tokens,
+                       n_sink, n_recent, t0_permille, t01_permille, evicted, ev_ld, tier, tier_ld,
+                       sel_idx, sel_count, sel_ld);
+  } else {
+    hipLaunchKernelGGL(tier_kernel<0>, dim3(B), dim3(kThreads), 0, st, s, s_ld, n_tokens, n_sink,
+                       n_recent, t0_permille, t01_permille, evicted, ev_ld, tier, tier_ld, sel_idx,
+                       sel_count, sel_ld);
+  }
+  return check_launch("tier_classify");
+}

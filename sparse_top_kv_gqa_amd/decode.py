@@ -1,0 +1,156 @@
+"""Decode-step runners: the library's entry points chained on one stream with every buffer
+allocated up front, so a step can be captured in a HIP graph and replayed.  Orchestration
+only — each step of the path is a libspk call.
+
+BlockSparseDecode   predictor scores pooled blocks -> top-k blocks -> attention over the blocks
+                    plus sinks and recent window (SparDA-style compact indexer)
+TokenSparseDecode   per-head or group-mean token scores -> top-k tokens -> attention over each
+                    query's own set, the group's union fetched once (optionally with some rows in
+                    pinned host memory)
+TieredDecode        tier classification by cumulative importance -> attention over T0 ∪ T1 in
+                    every layer -> importance update
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import (fetch_list_bound, attn_workspace_size, sparse_decode_attn, sparse_index_score,
+               topk_select, importance_accumulate, tier_classify)
+
+
+class BlockSparseDecode:
+    """One layer's block-sparse decode step over a KV cache ``[B, Hkv, Ncap, d]``."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, n_tokens: int, Hq: int, block_size: int,
+                 k_blocks: int, n_sink: int, n_recent: int, sm_scale: Optional[float] = None):
+        self.k, self.v = k, v
+        B, Hkv, _, d = k.shape
+        self.B, self.Hkv, self.Hq, self.d = B, Hkv, Hq, d
+        self.n_tokens, self.bs, self.kb = n_tokens, block_size, k_blocks
+        self.n_sink, self.n_recent = n_sink, n_recent
+        self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+        self.nb = n_tokens // block_size
+        dev = k.device
+        self.kpool = torch.empty((B, Hkv, self.nb, d), dtype=torch.float32, device=dev)
+        self.scores = torch.empty((B, 1, Hkv, self.nb), dtype=torch.float32, device=dev)
+        kk = min(k_blocks, self.nb)
+        self.idx = torch.empty((B, 1, Hkv, max(kk, 1)), dtype=torch.int32, device=dev)
+        self.count = torch.empty((B, 1, Hkv), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
+        ws = attn_workspace_size("per_kv_head", B, 1, Hq, Hkv, d, n_tokens, self.idx.shape[-1],
+                                 block_size, n_sink, n_recent)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+
+    def pool(self, pred: torch.Tensor):
+        """Mean-pool every complete block of the keys into ``kpool`` (once per cache; the
+        scores of this call are a by-product)."""
+        sparse_index_score("block_raw", pred, self.k, self.n_tokens, self.bs, scores=self.scores,
+                           pooled_out=self.kpool)
+
+    def step(self, q: torch.Tensor, pred: torch.Tensor):
+        sparse_index_score("block_pooled", pred, self.kpool, self.n_tokens, self.bs,
+                           scores=self.scores)
+        topk_select(self.scores, self.kb, idx=self.idx, count=self.count)
+        sparse_decode_attn(q, self.k, self.v, self.idx, self.count, "per_kv_head", self.n_tokens,
+                           gran=self.bs, n_sink=self.n_sink, n_recent=self.n_recent,
+                           sm_scale=self.sm_scale, out=self.out, lse=self.lse, ws=self.ws)
+        return self.out, self.lse
+
+
+class TokenSparseDecode:
+    """Token-sparse decode step with ``T`` query tokens per sequence.
+
+    mode "token_per_head": every query head keeps its own top-k (scope per_q_head);
+    mode "token_group_mean": each (token, KV head) keeps the top-k of the group-mean score
+    (scope per_kv_head).  ``index_keys`` is the key array the indexer streams (defaults to k);
+    host pools and ``loc`` put some rows in pinned host memory for the attention gather.
+    """
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, n_tokens: int, Hq: int, T: int, topk: int,
+                 mode: str, sm_scale: Optional[float] = None,
+                 index_keys: Optional[torch.Tensor] = None, k_host=None, v_host=None, loc=None):
+        self.k, self.v = k, v
+        self.index_keys = k if index_keys is None else index_keys
+        self.k_host, self.v_host, self.loc = k_host, v_host, loc
+        B, Hkv, _, d = k.shape
+        self.B, self.Hkv, self.Hq, self.T, self.d = B, Hkv, Hq, T, d
+        self.n_tokens, self.topk, self.mode = n_tokens, topk, mode
+        self.scope = "per_q_head" if mode == "token_per_head" else "per_kv_head"
+        self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+        dev = k.device
+        Hs = Hq if mode == "token_per_head" else Hkv
+        self.scores = torch.empty((B, T, Hs, n_tokens), dtype=torch.float32, device=dev)
+        kk = max(1, min(topk, n_tokens))
+        self.idx = torch.empty((B, T, Hs, kk), dtype=torch.int32, device=dev)
+        self.count = torch.empty((B, T, Hs), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+        ws = attn_workspace_size(self.scope, B, T, Hq, Hkv, d, n_tokens, kk)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+
+    def select(self, q: torch.Tensor):
+        sparse_index_score(self.mode, q, self.index_keys, self.n_tokens, scores=self.scores)
+        topk_select(self.scores, self.topk, idx=self.idx, count=self.count)
+
+    def attend(self, q: torch.Tensor):
+        sparse_decode_attn(q, self.k, self.v, self.idx, self.count, self.scope, self.n_tokens,
+                           sm_scale=self.sm_scale, k_host=self.k_host, v_host=self.v_host,
+                           loc=self.loc, out=self.out, lse=self.lse, ws=self.ws)
+        return self.out, self.lse
+
+    def step(self, q: torch.Tensor):
+        self.select(q)
+        return self.attend(q)
+
+
+class TieredDecode:
+    """Decode steps of a batch of sequences under the T0/T1/T3 hierarchy, all layers.
+
+    caches: per-layer (k, v) ``[B, Hkv, Ncap, d]``.  State: importance ``s`` fp32
+    ``[B, Ncap]`` and the sticky evicted mask ``[B, Ncap]``.
+    """
+
+    def __init__(self, caches: Sequence, Hq: int, n_cap: int, n_sink: int, n_recent: int,
+                 t0_permille: int = 250, t01_permille: int = 750,
+                 sm_scale: Optional[float] = None):
+        self.caches = list(caches)
+        k0 = self.caches[0][0]
+        B, Hkv, _, d = k0.shape
+        self.B, self.Hkv, self.Hq, self.d, self.L = B, Hkv, Hq, d, len(self.caches)
+        self.n_cap, self.n_sink, self.n_recent = n_cap, n_sink, n_recent
+        self.p0, self.p01 = t0_permille, t01_permille
+        self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+        dev = k0.device
+        self.s = torch.zeros((B, n_cap), dtype=torch.float32, device=dev)
+        self.evicted = torch.zeros((B, n_cap), dtype=torch.uint8, device=dev)
+        self.tier = torch.zeros((B, n_cap), dtype=torch.uint8, device=dev)
+        self.sel = torch.empty((B, n_cap), dtype=torch.int32, device=dev)
+        self.count = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.dense_idx = torch.arange(n_cap, dtype=torch.int32, device=dev).repeat(B, 1)
+        self.logits = torch.empty((self.L, B, 1, Hq, n_cap), dtype=torch.float32, device=dev)
+        self.out = torch.empty((self.L, B, 1, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((self.L, B, 1, Hq), dtype=torch.float32, device=dev)
+        ws = attn_workspace_size("per_seq", B, 1, Hq, Hkv, d, n_cap, n_cap)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+
+    def step(self, qs: Sequence[torch.Tensor], n_tokens: int, dense: bool = False):
+        """One decode step at ``n_tokens`` cached tokens.  qs: per-layer Q ``[B, 1, Hq, d]``.
+        dense=True attends over every token (no importance exists yet)."""
+        if dense:
+            self.count.fill_(n_tokens)
+            sel = self.dense_idx
+        else:
+            tier_classify(self.s, n_tokens, self.n_sink, self.n_recent, self.p0, self.p01,
+                          evicted=self.evicted, tier=self.tier, sel_idx=self.sel,
+                          sel_count=self.count)
+            sel = self.sel
+        for l, (k, v) in enumerate(self.caches):
+            sparse_decode_attn(qs[l], k, v, sel, self.count, "per_seq", n_tokens,
+                               sm_scale=self.sm_scale, out=self.out[l], lse=self.lse[l],
+                               logits=self.logits[l], ws=self.ws)
+        importance_accumulate(self.s, sel, self.count, self.logits, self.lse, n_tokens)
+        return self.out, self.lse

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every entry point include/spk.h declares, and rejects bad
+arguments before launching anything.  CPU only: no call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_top_kv_gqa_amd as spk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spk.h")
+
+# Fake, 16-byte-aligned device addresses: validation must fail before anything touches them.
+A = ctypes.c_void_p(0x100000)
+Bp = ctypes.c_void_p(0x200000)
+
+
+def declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"SPK_API\s+[\w\s\*]+?\b(\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared()
+    assert set(names) == set(spk.EXPORTS), names
+    L = spk.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.spk_version() == 1
+
+
+def _err():
+    return spk.lib().spk_last_error().decode()
+
+
+def test_index_score_validation():
+    L = spk.lib()
+    # null q
+    assert L.sparse_index_score(0, None, 1, A, 1, 128 * 64, 128 * 64, 128, 1, 1, 4, 1, 128, 64, 1,
+                                Bp, 64, None, None) == 1
+    assert "null" in _err()
+    # Hq % Hkv != 0
+    assert L.sparse_index_score(0, A, 1, A, 1, 128 * 64, 128 * 64, 128, 1, 1, 6, 4, 128, 64, 1,
+                                Bp, 64, None, None) == 1
+    # unsupported d
+    assert L.sparse_index_score(0, A, 1, A, 1, 96 * 64, 96 * 64, 96, 1, 1, 4, 1, 96, 64, 1,
+                                Bp, 64, None, None) == 2
+    # unsupported dtype
+    assert L.sparse_index_score(0, A, 7, A, 1, 128 * 64, 128 * 64, 128, 1, 1, 4, 1, 128, 64, 1,
+                                Bp, 64, None, None) == 2
+    # score leading dim too small
+    assert L.sparse_index_score(0, A, 1, A, 1, 128 * 64, 128 * 64, 128, 1, 1, 4, 1, 128, 64, 1,
+                                Bp, 63, None, None) == 1
+    # pooled_out outside BLOCK_RAW
+    assert L.sparse_index_score(2, A, 1, A, 0, 128 * 64, 128 * 64, 128, 1, 1, 1, 1, 128, 64, 16,
+                                Bp, 64, Bp, None) == 1
+    # too many score vectors per KV head (per head, T*G = 32)
+    assert L.sparse_index_score(1, A, 1, A, 1, 128 * 64, 128 * 64, 128, 1, 8, 4, 1, 128, 64, 1,
+                                Bp, 64, None, None) == 2
+
+
+def test_topk_validation():
+    L = spk.lib()
+    assert L.topk_select(A, 100, 4, 100, -1, Bp, 10, None, None, 0, None) == 1
+    assert L.topk_select(A, 100, 4, 100, 10, Bp, 9, None, None, 0, None) == 1      # idx_ld < k
+    assert L.topk_select(A, 50, 4, 100, 10, Bp, 10, None, None, 0, None) == 1      # s_ld < n
+    assert L.topk_select(None, 100, 4, 100, 10, Bp, 10, None, None, 0, None) == 1
+    sz = ctypes.c_size_t(123)
+    assert L.topk_select_workspace_size(4, 100, 10, ctypes.byref(sz)) == 0 and sz.value == 0
+
+
+def _attn(**kw):
+    args = dict(q=A, q_dt=1, k=A, v=A, kv_dt=1, kv_sb=8 * 1024 * 128, kv_sh=1024 * 128, kv_sn=128,
+                k_host=None, v_host=None, host_sb=0, host_sh=0, host_sn=0, host_slots=0, loc=None,
+                loc_sb=0, loc_sh=0, hbm_slots=1024, sel_idx=Bp, sel_count=Bp, sel_ld=32, scope=1, gran=1, n_sink=0,
+                n_recent=0, B=2, T=1, Hq=32, Hkv=8, d=128, n=1024, scale=0.1, out=Bp, lse=None,
+                logits=None, logits_ld=0, ws=Bp, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return spk.lib().sparse_decode_attn(*args.values())
+
+
+def test_attn_validation():
+    assert _attn(Hq=30) == 1 and "Hq" in _err()
+    assert _attn(d=80, kv_sn=80) == 2
+    assert _attn(q=None) == 1
+    assert _attn(loc=Bp) == 1 and "host" in _err()                 # loc without host pools
+    assert _attn(ws_bytes=16) == 3                                   # workspace too small
+    assert _attn(scope=9) == 1
+    assert _attn(kv_sn=100) == 1                                     # stride not a multiple of 8
+    assert _attn(q=ctypes.c_void_p(0x100004)) == 1                   # misaligned
+    assert _attn(T=4, Hq=32, Hkv=4) == 2                             # 32 query vectors per group
+    assert _attn(logits=Bp, logits_ld=8) == 1                        # logits_ld below the bound
+    assert _attn(gran=0) == 1
+    assert _attn(hbm_slots=1000) == 1 and "exceeds" in _err()       # cache shorter than n_tokens
+    # host pools must be pinned host memory known to HIP: a plain malloc'ed buffer is refused
+    buf = ctypes.create_string_buffer(1 << 16)
+    addr = (ctypes.addressof(buf) + 15) // 16 * 16
+    assert _attn(loc=Bp, k_host=ctypes.c_void_p(addr), v_host=ctypes.c_void_p(addr), host_sb=128,
+                 host_sh=128, host_sn=128, host_slots=4) == 1
+
+
+def test_attn_workspace_query():
+    n = spk.attn_workspace_size("per_kv_head", 8, 1, 32, 8, 128, 32768, 32, 64, 4, 512)
+    assert n > 8 * 8 * 4 * 128 * 4          # at least one split of partial outputs per group
+    assert spk.fetch_list_bound("per_kv_head", 1, 4, 32, 64, 4, 512, 32768) == 2564
+    assert spk.fetch_list_bound("per_q_head", 1, 4, 2622, 1, 0, 0, 131072) == 10488
+
+
+def test_importance_and_tier_validation():
+    L = spk.lib()
+    assert L.importance_accumulate(A, 100, 2, 100, Bp, Bp, 50, A, 50, A, 0, 4, None) == 1
+    assert L.importance_accumulate(A, 100, 2, 100, Bp, Bp, 50, A, 50, A, 100, 100, None) == 2
+    assert L.importance_accumulate(A, 100, 2, 100, Bp, Bp, 50, A, 40, A, 2, 4, None) == 1
+    # t0 > t01
+    assert L.tier_classify(A, 100, 2, 100, 4, 8, 800, 700, None, 0, Bp, 100, None, None, 0,
+                           None, 0, None) == 1
+    # sel_ld < n_tokens
+    assert L.tier_classify(A, 100, 2, 100, 4, 8, 250, 750, None, 0, Bp, 100, Bp, Bp, 50,
+                           None, 0, None) == 1
+    # sel_idx without sel_count
+    assert L.tier_classify(A, 100, 2, 100, 4, 8, 250, 750, None, 0, Bp, 100, Bp, None, 100,
+                           None, 0, None) == 1
+
+
+def test_binding_raises_without_library(monkeypatch):
+    monkeypatch.setattr(spk, "_lib", None)
+    monkeypatch.setattr(spk, "LIB_PATH", "/nonexistent/libspk.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        spk.lib()

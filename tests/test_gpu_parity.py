@@ -1,0 +1,424 @@
+"""GPU parity: every libspk entry point against the fp64 CPU oracle on the same seeded inputs.
+
+Bars (stated per check): bit-exact for indices, counts and tiers; normwise relative error
+max|x-y|/max|y| <= 2e-3 per row for attention outputs, scores, lse and importance.  Selections
+produced on the GPU from GPU scores are checked two ways: exactly against the oracle's top-k
+of the same fp32 scores, and within the tie band against the oracle's own scores.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import steps as osteps
+import sparse_top_kv_gqa_amd as spk
+from sparse_top_kv_gqa_amd.decode import BlockSparseDecode, TieredDecode, TokenSparseDecode
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+DEV = "cuda"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t: torch.Tensor):
+    """CPU copy for the oracle: bf16 as raw uint16 bits, float as float32."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def rel(x, ref):
+    return osteps.rel_err(x, ref)
+
+
+def check_rows(x, ref, tol=TOL, what=""):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    x2 = x.reshape(-1, x.shape[-1])
+    r2 = ref.reshape(-1, ref.shape[-1])
+    worst = max(rel(a, b) for a, b in zip(x2, r2))
+    assert worst <= tol, f"{what}: normwise rel err {worst:.3e} > {tol}"
+    return worst
+
+
+# ------------------------------------------------------------------------------------ top-k
+
+def _rows(kind, n, rows, seed):
+    r = np.random.default_rng(seed)
+    if kind == "normal":
+        x = r.standard_normal((rows, n)).astype(np.float32)
+    elif kind == "ties":
+        x = r.integers(-4, 5, size=(rows, n)).astype(np.float32)
+    elif kind == "allsame":
+        x = np.full((rows, n), 1.5, np.float32)
+    else:  # "special": signed zeros, infinities, NaN among ties
+        x = r.integers(-2, 3, size=(rows, n)).astype(np.float32)
+        x[r.random((rows, n)) < 0.2] = -0.0
+        x[r.random((rows, n)) < 0.05] = np.inf
+        x[r.random((rows, n)) < 0.05] = -np.inf
+        x[r.random((rows, n)) < 0.05] = np.nan
+    return x
+
+
+@pytest.mark.parametrize("n", [1, 7, 64, 512, 1000, 4096, 4097, 10000, 16384, 16385, 70001])
+@pytest.mark.parametrize("kind", ["normal", "ties", "allsame", "special"])
+def test_topk_bit_exact(n, kind):
+    say("topk", n, kind)
+    x = _rows(kind, n, 3, seed=n)
+    xs = torch.tensor(x, device=DEV)
+    for k in sorted({0, 1, 5, 32, n // 3, n - 1, n, n + 3}):
+        if k < 0:
+            continue
+        idx, cnt = spk.topk_select(xs, k)
+        torch.cuda.synchronize()
+        kk = min(k, n)
+        assert cnt.cpu().tolist() == [kk] * 3
+        got = idx.cpu().numpy()
+        for r in range(3):
+            exp = oracle.topk(x[r], k)
+            assert got[r, :kk].tolist() == exp.tolist(), (n, kind, k, r)
+
+
+def test_topk_strided_rows_and_ld():
+    x = _rows("normal", 3000, 5, seed=9)
+    big = torch.zeros((5, 3100), device=DEV)
+    big[:, :3000] = torch.tensor(x, device=DEV)
+    idx, cnt = spk.topk_select(big[:, :3000], 100)
+    for r in range(5):
+        assert idx[r].cpu().tolist() == oracle.topk(x[r], 100).tolist()
+
+
+# ------------------------------------------------------------------------------------ tiny
+
+def test_tiny_workload_end_to_end_and_dense():
+    w = W.TINY
+    say("tiny", w.name)
+    q = W.queries(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    dec = TokenSparseDecode(k, v, w.N, w.Hq, w.T, w.k, "token_group_mean")
+    out, lse = dec.step(q)
+    torch.cuda.synchronize()
+    qh, kh, vh = host(q)[0, 0], host(k)[0, 0], host(v)[0, 0]
+    ref_scores = oracle.scores_token_group_mean(qh, kh)
+    gs = dec.scores.cpu().numpy()[0, 0, 0]
+    check_rows(gs, ref_scores, what="group-mean scores")
+    sel = dec.idx.cpu().numpy()[0, 0, 0]
+    assert sel.tolist() == oracle.topk(gs, w.k).tolist()
+    assert osteps.topk_band_ok(sel, ref_scores, w.k, TOL)
+    scale = oracle.softmax_scale(w.d)
+    o_ref, l_ref, _ = oracle.attend(qh, kh[sel], vh[sel], scale)
+    check_rows(out.cpu().numpy()[0, 0], o_ref, what="attention")
+    np.testing.assert_allclose(lse.cpu().numpy()[0, 0], l_ref, rtol=TOL)
+    # k = N: sparse attention is dense attention
+    dense = TokenSparseDecode(k, v, w.N, w.Hq, w.T, w.N, "token_group_mean")
+    out_d, lse_d = dense.step(q)
+    o_ref, l_ref, _ = oracle.attend(qh, kh, vh, scale)
+    check_rows(out_d.cpu().numpy()[0, 0], o_ref, what="dense attention")
+    np.testing.assert_allclose(lse_d.cpu().numpy()[0, 0], l_ref, rtol=TOL)
+
+
+# ------------------------------------------------------------------------------------ block
+
+def _block_case(w, groups=None, poison=False):
+    q = W.queries(w, device=DEV)
+    pred = W.predictors(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    dec = BlockSparseDecode(k, v, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent)
+    dec.pool(pred)
+    out, lse = dec.step(q, pred)
+    torch.cuda.synchronize()
+    return q, pred, k, v, dec, out.clone(), lse.clone()
+
+
+@pytest.mark.parametrize("N", [64 * 70 + 37, 64 * 40])
+def test_block_workload_small(N):
+    w = W.scaled(W.LLAMA8B_BLOCK, B=2, Hkv=2, Hq=8, N=N, k=9)
+    say("block-small", N)
+    q, pred, k, v, dec, out, lse = _block_case(w)
+    kp = dec.kpool.cpu().numpy()
+    sc = dec.scores.cpu().numpy()
+    idx = dec.idx.cpu().numpy()
+    scale = oracle.softmax_scale(w.d)
+    G = w.G
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kh, vh = host(k[b, h]), host(v[b, h])
+            check_rows(kp[b, h], oracle.block_pool(kh, w.block_size), what="pooled keys")
+            ref = oracle.scores_block(host(pred)[b, 0, h], oracle.block_pool(kh, w.block_size))
+            check_rows(sc[b, 0, h], ref, what="block scores")
+            blocks = idx[b, 0, h]
+            assert blocks.tolist() == oracle.topk(sc[b, 0, h], w.k).tolist()
+            assert osteps.topk_band_ok(blocks, ref, w.k, TOL)
+            toks = oracle.selection_tokens(blocks, w.block_size, w.N, w.n_sink, w.n_recent)
+            o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], kh[toks], vh[toks], scale)
+            check_rows(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="block attention")
+            np.testing.assert_allclose(lse.cpu().numpy()[b, 0, h * G:(h + 1) * G], l_ref, rtol=TOL)
+    # BLOCK_RAW scores equal BLOCK_POOLED scores up to rounding (pooling is linear)
+    raw = spk.sparse_index_score("block_raw", pred, k, w.N, w.block_size)
+    check_rows(raw.cpu().numpy(), sc, tol=1e-5, what="raw vs pooled")
+
+
+def test_block_workload_full_size_sampled_and_deterministic():
+    w = W.LLAMA8B_BLOCK
+    say("block-full", w.name)
+    q, pred, k, v, dec, out, lse = _block_case(w)
+    # determinism: a second step is bit-identical
+    out2, lse2 = dec.step(q, pred)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    sc = dec.scores.cpu().numpy()
+    idx = dec.idx.cpu().numpy()
+    scale = oracle.softmax_scale(w.d)
+    G = w.G
+    for (b, h) in [(0, 0), (3, 5), (7, 7)]:
+        kh, vh = host(k[b, h]), host(v[b, h])
+        kpool = oracle.block_pool(kh, w.block_size)
+        ref = oracle.scores_block(host(pred)[b, 0, h], kpool)
+        check_rows(sc[b, 0, h], ref, what="block scores")
+        blocks = idx[b, 0, h]
+        assert blocks.tolist() == oracle.topk(sc[b, 0, h], w.k).tolist()
+        assert osteps.topk_band_ok(blocks, ref, w.k, TOL)
+        toks = oracle.selection_tokens(blocks, w.block_size, w.N, w.n_sink, w.n_recent)
+        o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], kh[toks], vh[toks], scale)
+        check_rows(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="block attention")
+
+
+def test_block_nan_poisoning_unselected_rows():
+    """Rows outside the selection are NaN: a wrong read would poison the output."""
+    w = W.scaled(W.LLAMA8B_BLOCK, B=2, Hkv=2, Hq=8, N=64 * 50 + 10, k=6)
+    say("block-poison")
+    q, pred, k, v, dec, out, lse = _block_case(w)
+    idx = dec.idx.cpu().numpy()
+    kp, vp = k.clone(), v.clone()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            toks = oracle.selection_tokens(idx[b, 0, h], w.block_size, w.N, w.n_sink, w.n_recent)
+            keep = torch.zeros(w.N, dtype=torch.bool)
+            keep[torch.tensor(toks)] = True
+            kp[b, h, ~keep.to(DEV)] = float("nan")
+            vp[b, h, ~keep.to(DEV)] = float("nan")
+    out_p, lse_p = spk.sparse_decode_attn(q, kp, vp, dec.idx, dec.count, "per_kv_head", w.N,
+                                          gran=w.block_size, n_sink=w.n_sink, n_recent=w.n_recent)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_p).all()
+    assert torch.equal(out_p, out) and torch.equal(lse_p, lse)
+
+
+# ------------------------------------------------------------------------------------ per head
+
+@pytest.mark.parametrize("N", [8192 + 11, 20000])
+def test_per_head_workload_small(N):
+    w = W.scaled(W.PER_HEAD_2PCT, B=2, Hkv=2, Hq=8, N=N, k=math.ceil(0.02 * N))
+    say("per-head", N)
+    q = W.queries(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    dec = TokenSparseDecode(k, v, w.N, w.Hq, 1, w.k, "token_per_head")
+    out, lse = dec.step(q)
+    torch.cuda.synchronize()
+    sc, idx = dec.scores.cpu().numpy(), dec.idx.cpu().numpy()
+    scale = oracle.softmax_scale(w.d)
+    G = w.G
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kh, vh = host(k[b, h]), host(v[b, h])
+            qg = host(q)[b, 0, h * G:(h + 1) * G]
+            ref = oracle.scores_token_per_head(qg, kh)
+            for j in range(G):
+                hq = h * G + j
+                check_rows(sc[b, 0, hq], ref[j], what="per-head scores")
+                sel = idx[b, 0, hq]
+                assert sel.tolist() == oracle.topk(sc[b, 0, hq], w.k).tolist()
+                assert osteps.topk_band_ok(sel, ref[j], w.k, TOL)
+                o_ref, l_ref, _ = oracle.attend(qg[j:j + 1], kh[sel], vh[sel], scale)
+                check_rows(out.cpu().numpy()[b, 0, hq], o_ref[0], what="per-head attention")
+                assert abs(lse.cpu().numpy()[b, 0, hq] - l_ref[0]) <= TOL * abs(l_ref[0]) + 1e-6
+    # outliers present as built: exactly 1% of rows scaled by 4 in every group
+    assert W.outlier_rows(w, 0, 0).numel() == round(0.01 * w.N)
+
+
+# ------------------------------------------------------------------------------------ spec verify
+
+def _pinned_like(t: torch.Tensor):
+    return torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+
+
+@pytest.mark.parametrize("N", [4096 + 5, 12000])
+def test_spec_verify_union_host_rows_residency_invariance(N):
+    w = W.scaled(W.SPEC_VERIFY, B=2, Hkv=2, Hq=8, N=N, k=256)
+    say("spec-verify", N)
+    q = W.queries(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    dec = TokenSparseDecode(k, v, w.N, w.Hq, w.T, w.k, "token_group_mean")
+    out_hbm, lse_hbm = dec.step(q)
+    out_hbm, lse_hbm = out_hbm.clone(), lse_hbm.clone()
+    torch.cuda.synchronize()
+    idx = dec.idx.cpu().numpy()              # [B, T, Hkv, k]
+    # residency: exactly 10% of each group's union lives in pinned host memory
+    loc = torch.arange(w.N, dtype=torch.int32).repeat(w.B, w.Hkv, 1)
+    n_host_max = 0
+    host_sets = {}
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            union = torch.tensor(np.unique(idx[b, :, h].ravel()))
+            hr = W.host_rows(w, b, h, union)
+            host_sets[(b, h)] = hr
+            n_host_max = max(n_host_max, hr.numel())
+    kh_pool = torch.zeros((w.B, w.Hkv, max(n_host_max, 1), w.d), dtype=k.dtype, pin_memory=True)
+    vh_pool = torch.zeros_like(kh_pool).pin_memory()
+    k_att, v_att = k.clone(), v.clone()
+    for (b, h), hr in host_sets.items():
+        for slot, tok in enumerate(hr.tolist()):
+            kh_pool[b, h, slot] = k[b, h, tok].cpu()
+            vh_pool[b, h, slot] = v[b, h, tok].cpu()
+            loc[b, h, tok] = ~slot
+        # the HBM copies of host rows must never be read
+        k_att[b, h, hr.to(DEV)] = float("nan")
+        v_att[b, h, hr.to(DEV)] = float("nan")
+    frac = sum(hr.numel() for hr in host_sets.values()) / sum(
+        np.unique(idx[b, :, h].ravel()).size for b in range(w.B) for h in range(w.Hkv))
+    assert abs(frac - 0.10) < 0.01
+    out_h, lse_h = spk.sparse_decode_attn(q, k_att, v_att, dec.idx, dec.count, "per_kv_head", w.N,
+                                          k_host=kh_pool, v_host=vh_pool, loc=loc.to(DEV))
+    torch.cuda.synchronize()
+    # Proposition 1: residency changes nothing, to the bit
+    assert torch.equal(out_h, out_hbm) and torch.equal(lse_h, lse_hbm)
+    # against the oracle: each draft token's heads attend over that token's own set
+    scale = oracle.softmax_scale(w.d)
+    G = w.G
+    sc = dec.scores.cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kh, vh = host(k[b, h]), host(v[b, h])
+            qt = host(q)[b, :, h * G:(h + 1) * G]
+            r = osteps.group_mean_group(qt, kh, vh, w.k, scale)
+            for t in range(w.T):
+                check_rows(sc[b, t, h], r["scores"][t], what="group-mean scores")
+                sel = idx[b, t, h]
+                assert sel.tolist() == oracle.topk(sc[b, t, h], w.k).tolist()
+                assert osteps.topk_band_ok(sel, r["scores"][t], w.k, TOL)
+                o_ref, l_ref, _ = oracle.attend(qt[t], kh[sel], vh[sel], scale)
+                check_rows(out_h.cpu().numpy()[b, t, h * G:(h + 1) * G], o_ref, what="verify attention")
+
+
+# ------------------------------------------------------------------------------------ tiers
+
+def test_tier_classify_bit_exact_random():
+    say("tiers-random")
+    for trial, (B, n, ns, nr) in enumerate([(3, 1000, 4, 64), (2, 16384, 4, 512), (1, 20000, 4, 512),
+                                             (2, 10, 4, 8), (1, 0, 4, 8), (2, 517, 4, 512)]):
+        r = np.random.default_rng(trial)
+        s = (r.integers(0, 50, size=(B, max(n, 1))) / 7).astype(np.float32)
+        ev = (r.random((B, max(n, 1))) < 0.1).astype(np.uint8)
+        st = torch.tensor(s, device=DEV)
+        evt = torch.tensor(ev, device=DEV)
+        tier, sel, cnt = spk.tier_classify(st, n, ns, nr, 250, 750, evicted=evt)
+        torch.cuda.synchronize()
+        for b in range(B):
+            t_ref, l_ref = oracle.tier_classify(s[b], n, ns, nr, 250, 750, ev[b].astype(bool))
+            assert tier.cpu().numpy()[b, :n].tolist() == t_ref.tolist(), (trial, b)
+            c = int(cnt.cpu()[b])
+            assert c == len(l_ref)
+            assert sel.cpu().numpy()[b, :c].tolist() == l_ref.tolist()
+            ev_new = ev[b, :n].astype(bool) | (t_ref == 3)
+            assert (evt.cpu().numpy()[b, :n] != 0).tolist() == ev_new.tolist()
+
+
+def test_tiered_decode_small_matches_oracle():
+    w = W.scaled(W.REASONING_TIERS, B=3, layers=3, Hq=8, Hkv=2, N=900, n_start=600,
+                 grow_per_step=100, steps=4, n_recent=64)
+    say("tiered", w.name)
+    caches = [(W.kv_cache(w, "k", l, DEV, n_cap=w.N), W.kv_cache(w, "v", l, DEV, n_cap=w.N))
+              for l in range(w.layers)]
+    dec = TieredDecode(caches, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille)
+    scale = oracle.softmax_scale(w.d)
+    s_prev = np.zeros((w.B, w.N), np.float32)
+    ev_prev = np.zeros((w.B, w.N), bool)
+    for t in range(w.steps):
+        n = w.n_start + w.grow_per_step * t
+        qs = [W.queries(w, step=t, layer=l, device=DEV) for l in range(w.layers)]
+        s_in = dec.s.cpu().numpy().copy()
+        ev_in = dec.evicted.cpu().numpy().astype(bool)
+        out, lse = dec.step(qs, n, dense=(t == 0))
+        torch.cuda.synchronize()
+        for b in range(w.B):
+            qb = np.stack([host(qs[l])[b, 0] for l in range(w.layers)])
+            kb = np.stack([np.stack([host(caches[l][0][b, h]) for h in range(w.Hkv)]) for l in range(w.layers)])
+            vb = np.stack([np.stack([host(caches[l][1][b, h]) for h in range(w.Hkv)]) for l in range(w.layers)])
+            # the oracle starts from the GPU's own state, so tiers compare bit-exactly
+            r = osteps.tiered_sequence_step(s_in[b], ev_in[b], qb, kb, vb, n, scale, w.n_sink,
+                                            w.n_recent, w.t0_permille, w.t01_permille,
+                                            dense=(t == 0))
+            if t > 0:
+                assert dec.tier.cpu().numpy()[b, :n].tolist() == r["tier"].tolist()
+                c = int(dec.count.cpu()[b])
+                assert dec.sel.cpu().numpy()[b, :c].tolist() == r["tokens"].tolist()
+            check_rows(out.cpu().numpy()[:, b, 0], r["out"], what="tiered attention")
+            check_rows(dec.s.cpu().numpy()[b, :n][None], r["s"][None], what="importance")
+            assert abs(float(dec.s.cpu().numpy()[b, :n].astype(np.float64).sum()) - (t + 1)) < 1e-3
+
+
+def test_importance_accumulate_direct():
+    say("importance-direct")
+    r = np.random.default_rng(5)
+    L, B, Hq, n, ld = 4, 2, 6, 300, 320
+    cnt = np.array([250, 0], np.int32)
+    sel = np.zeros((B, ld), np.int32)
+    for b in range(B):
+        sel[b, :cnt[b]] = np.sort(r.choice(n, cnt[b], replace=False))
+    logits = r.standard_normal((L, B, Hq, ld)).astype(np.float32)
+    logits[0, 0, 1, 7] = -np.inf
+    lse = np.zeros((L, B, Hq), np.float32)
+    for l in range(L):
+        for b in range(B):
+            for h in range(Hq):
+                x = logits[l, b, h, :cnt[b]].astype(np.float64)
+                lse[l, b, h] = np.log(np.exp(x[np.isfinite(x)]).sum()) if cnt[b] else -np.inf
+    s0 = r.random((B, n)).astype(np.float32)
+    st = torch.tensor(s0, device=DEV)
+    spk.importance_accumulate(st, torch.tensor(sel, device=DEV), torch.tensor(cnt, device=DEV),
+                              torch.tensor(logits, device=DEV), torch.tensor(lse, device=DEV), n)
+    torch.cuda.synchronize()
+    for b in range(B):
+        alpha = np.zeros((L, Hq, n))
+        for l in range(L):
+            for h in range(Hq):
+                x = logits[l, b, h, :cnt[b]].astype(np.float64)
+                alpha[l, h, sel[b, :cnt[b]]] = np.exp(x - lse[l, b, h])
+        ref = oracle.importance_update(s0[b], alpha)
+        check_rows(st.cpu().numpy()[b][None], ref[None], tol=1e-5, what="importance")
+
+
+# ------------------------------------------------------------------------------------ edge cases
+
+def test_empty_and_degenerate_selections():
+    say("edge")
+    w = W.scaled(W.TINY, B=2, Hq=4, Hkv=1, N=300)
+    q = W.queries(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    sel = torch.zeros((2, 1, 1, 16), dtype=torch.int32, device=DEV)
+    cnt = torch.tensor([[[0]], [[3]]], dtype=torch.int32, device=DEV)
+    sel[1, 0, 0, :3] = torch.tensor([5, 299, 1000])    # 1000 is out of range: skipped
+    out, lse = spk.sparse_decode_attn(q, k, v, sel, cnt, "per_kv_head", w.N)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    kh, vh = host(k[1, 0]), host(v[1, 0])
+    o_ref, l_ref, _ = oracle.attend(host(q)[1, 0], kh[[5, 299]], vh[[5, 299]], oracle.softmax_scale(w.d))
+    check_rows(out.cpu().numpy()[1, 0], o_ref, what="ragged selection")
+    # no tokens at all
+    out0, lse0 = spk.sparse_decode_attn(q, k, v, sel, cnt, "per_kv_head", 0)
+    torch.cuda.synchronize()
+    assert torch.all(out0 == 0) and torch.all(torch.isneginf(lse0))
