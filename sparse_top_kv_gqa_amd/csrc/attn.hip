@@ -21,6 +21,8 @@
 //     at the end and the split's (m, l, acc) go to the workspace.
 //  3. combine   one wave per query vector merges the splits in split order (deterministic, no
 //     atomics) into out and lse.
+#include <type_traits>
+
 #include "spk_internal.h"
 
 namespace spk {
@@ -34,7 +36,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSets = 32;
 constexpr size_t kAsmLdsMax = 60 * 1024;  // larger bitmaps live in the workspace
 constexpr int kMaxIntervals = 64;   // selection entries + 2 forced ranges, one per lane
-constexpr int kMaxRows = 4096;      // rows per workgroup (LDS row table)
+constexpr int kMaxRows = 2048;      // rows per workgroup (LDS row table)
 constexpr int kDead = INT32_MIN;    // row-table entry of a row that is not read
 
 struct Plan {
@@ -223,15 +225,9 @@ __device__ __forceinline__ int resolve_slot(const AttnArgs& a, int b, int kvh, i
   return ok ? l : kDead;
 }
 
-template <typename KT>
-__device__ __forceinline__ const KT* row_ptr(const AttnArgs& a, const void* base_hbm,
-                                             const void* base_host, int b, int kvh, int slot) {
-  if (slot < 0)
-    return reinterpret_cast<const KT*>(base_host) + (int64_t)b * a.host_sb +
-           (int64_t)kvh * a.host_sh + (int64_t)(~slot) * a.host_sn;
-  return reinterpret_cast<const KT*>(base_hbm) + (int64_t)b * a.kv_sb + (int64_t)kvh * a.kv_sh +
-         (int64_t)slot * a.kv_sn;
-}
+// A readable, all-zero row: rows that are not read load from here, so every load in the main
+// loop is issued unconditionally (no divergent branches between loads and their waits).
+__device__ __align__(64) uint32_t g_zero_row[128];
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -317,15 +313,22 @@ __device__ __forceinline__ int token_at(const int* seg_start, const int* seg_pos
   return seg_start[lo] + (p - seg_pos[lo]);
 }
 
+#ifndef SPK_ATTN_MIN_WAVES
+#define SPK_ATTN_MIN_WAVES 2  // register budget: at least this many waves per SIMD
+#endif
 template <int D, typename KT, int NQ, bool kMask, int MODE, int U>
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(SPK_ATTN_MIN_WAVES))) void attn_partial_kernel(AttnArgs a) {
   constexpr int LPR = D / 8;             // lanes per row
   constexpr int SPW = kWave / LPR;       // slots (rows) per wave
   constexpr int NSLOT = SPW * kWaves;    // slots per workgroup
   constexpr int STEP = NSLOT * U;        // rows per workgroup per iteration
+  // row table: byte addresses of the row's K and V (HBM or host; rows not read point at the zero
+  // row), padded past the last row so every issue in the main loop is unconditional
+  constexpr int kTab = kMaxRows + 2 * STEP;
   __shared__ float red[kWaves][NQ][D + 2];
-  __shared__ int32_t slot_s[kMaxRows];
-  __shared__ uint32_t mask_s[kMask ? kMaxRows : 1];
+  __shared__ ulonglong2 addr_s[kTab];
+  __shared__ uint32_t mask_s[kMask ? kTab : 1];
   __shared__ int seg_start[kMaxIntervals], seg_pos[kMaxIntervals], seg_meta[2];
 
   const int g = blockIdx.y;
@@ -356,16 +359,40 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
   const int r1 = min(r0 + a.R, cnt);
   const int nrows = r1 - r0;
 
-  // row table: every row's resolved slot (and list mask) staged once in LDS
+  const int iters = (nrows + STEP - 1) / STEP;
+  const int tab_rows = (iters + 2) * STEP;
+  // group base addresses (byte), without the lane column
+  const uint64_t gk = reinterpret_cast<uint64_t>(a.k) +
+                      (uint64_t)(((int64_t)b * a.kv_sb + (int64_t)kvh * a.kv_sh) * (int64_t)sizeof(KT));
+  const uint64_t gkh = reinterpret_cast<uint64_t>(a.k_host) +
+                       (uint64_t)(((int64_t)b * a.host_sb + (int64_t)kvh * a.host_sh) * (int64_t)sizeof(KT));
+  const uint64_t zero_row = reinterpret_cast<uint64_t>(g_zero_row);
+  // V row = K row + (v - k) in HBM, + (v_host - k_host) in host memory
+  const uint64_t dd = reinterpret_cast<uint64_t>(a.v) - reinterpret_cast<uint64_t>(a.k);
+  const uint64_t dh = reinterpret_cast<uint64_t>(a.v_host) - reinterpret_cast<uint64_t>(a.k_host);
   {
     const int32_t* list = a.list + (int64_t)lrow * a.list_ld;
     const uint32_t* mrow = kMask ? a.mask + (int64_t)g * a.list_ld : nullptr;
-    for (int i = threadIdx.x; i < nrows; i += kThreads) {
-      int tok;
-      if constexpr (MODE == kListIntervals) tok = token_at(seg_start, seg_pos, seg_meta[0], r0 + i);
-      else tok = list[r0 + i];
-      slot_s[i] = resolve_slot(a, b, kvh, tok);
-      if constexpr (kMask) mask_s[i] = mrow[r0 + i];
+    for (int i = threadIdx.x; i < tab_rows; i += kThreads) {
+      int slot_v = kDead;
+      if (i < nrows) {
+        int tok;
+        if constexpr (MODE == kListIntervals) tok = token_at(seg_start, seg_pos, seg_meta[0], r0 + i);
+        else tok = list[r0 + i];
+        slot_v = resolve_slot(a, b, kvh, tok);
+      }
+      ulonglong2 ad;
+      if (slot_v == kDead) {
+        ad.x = ad.y = zero_row;
+      } else if (slot_v < 0) {
+        ad.x = gkh + (uint64_t)((int64_t)(~slot_v) * a.host_sn * (int64_t)sizeof(KT));
+        ad.y = ad.x + dh;
+      } else {
+        ad.x = gk + (uint64_t)((int64_t)slot_v * a.kv_sn * (int64_t)sizeof(KT));
+        ad.y = ad.x + dd;
+      }
+      addr_s[i] = ad;
+      if constexpr (kMask) mask_s[i] = i < nrows ? mrow[r0 + i] : 0u;
     }
   }
 
@@ -395,19 +422,16 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  const int iters = (nrows + STEP - 1) / STEP;
+  const uint64_t col = (uint64_t)(sub * 8 * (int)sizeof(KT));
   auto issue = [&](int it, Raw8<KT> (&rk)[U], Raw8<KT> (&rv)[U], int (&sl)[U]) {
+    ulonglong2 ad[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ad[u] = addr_s[it * STEP + u * NSLOT + sid];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int p = it * STEP + u * NSLOT + sid;
-      sl[u] = p < nrows ? slot_s[p] : kDead;
-      if (sl[u] != kDead) {
-        rk[u].load(row_ptr<KT>(a, a.k, a.k_host, b, kvh, sl[u]) + sub * 8);
-        rv[u].load(row_ptr<KT>(a, a.v, a.v_host, b, kvh, sl[u]) + sub * 8);
-      } else {
-        rk[u].zero();
-        rv[u].zero();
-      }
+      sl[u] = ad[u].x == zero_row ? kDead : 0;
+      rk[u].load_addr(ad[u].x + col);
+      rv[u].load_addr(ad[u].y + col);
     }
   };
   auto consume = [&](int it, const Raw8<KT> (&rk)[U], const Raw8<KT> (&rv)[U],
@@ -417,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
     for (int u = 0; u < U; ++u) {
       const int p = it * STEP + u * NSLOT + sid;
       uint32_t mb = 0xFFFFFFFFu;
-      if constexpr (kMask) mb = p < nrows ? mask_s[p] : 0u;
+      if constexpr (kMask) mb = mask_s[p];
       float x[8];
       rk[u].to_float(x);
 #pragma unroll
@@ -429,13 +453,18 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
         const bool reads = sl[u] != kDead && (!kMask || ((mb >> (n / a.mask_div)) & 1u));
         lg[u][n] = reads ? s : -INFINITY;
       }
-      if (a.logits && p < nrows) {
+      if (a.logits) {
+        // lane `sub` writes query vector n = sub (and sub + LPR when NQ > LPR)
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-          if (n % LPR == sub && n < a.nq) {
+        for (int n0 = 0; n0 < NQ; n0 += LPR) {
+          float val = lg[u][n0];
+#pragma unroll
+          for (int n = n0 + 1; n < n0 + LPR && n < NQ; ++n) val = (sub == n - n0) ? lg[u][n] : val;
+          const int n = n0 + sub;
+          if (p < nrows && n < a.nq) {
             const int t = n / a.G, hl = n % a.G;
             const int64_t row = (int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl;
-            a.logits[row * a.logits_ld + r0 + p] = lg[u][n] * kLn2;
+            a.logits[row * a.logits_ld + r0 + p] = val * kLn2;
           }
         }
       }
@@ -468,14 +497,31 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
   {
     Raw8<KT> k0[U], v0[U], k1[U], v1[U];
     int s0[U], s1[U];
+#ifndef SPK_ATTN_PIPELINE
+#define SPK_ATTN_PIPELINE 1
+#endif
+#if !SPK_ATTN_PIPELINE
+    for (int it = 0; it < iters; ++it) {
+      issue(it, k0, v0, s0);
+      consume(it, k0, v0, s0);
+    }
+    (void)k1; (void)v1; (void)s1;
+#else
+    // software pipeline: the next batch's loads are in flight while this batch is consumed;
+    // scheduling barriers keep the compiler from hoisting consumer work above the loads
     issue(0, k0, v0, s0);
     for (int it = 0; it < iters; it += 2) {
-      if (it + 1 < iters) issue(it + 1, k1, v1, s1);
+      issue(it + 1, k1, v1, s1);  // rows past the end read the zero row
+      __builtin_amdgcn_sched_barrier(0);
       consume(it, k0, v0, s0);
+      __builtin_amdgcn_sched_barrier(0);
       if (it + 1 >= iters) break;
-      if (it + 2 < iters) issue(it + 2, k0, v0, s0);
+      issue(it + 2, k0, v0, s0);
+      __builtin_amdgcn_sched_barrier(0);
       consume(it + 1, k1, v1, s1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+#endif
   }
 
   // merge the slots of this wave (lanes with equal `sub` hold the same dims)
@@ -510,6 +556,275 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
   }
   __syncthreads();
   // merge the waves; thread -> (n, dim)
+  const int64_t pbase = ((int64_t)g * a.smax + split) * NQ;
+  for (int e = threadIdx.x; e < NQ * D; e += kThreads) {
+    const int n = e / D, dim = e % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w][n][0]);
+    float ls = 0.f, as = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = (mx == -INFINITY) ? 0.f : fast_exp2(red[w][n][0] - mx);
+      ls += red[w][n][1] * sc;
+      as += red[w][n][2 + dim] * sc;
+    }
+    a.acc[(pbase + n) * D + dim] = as;
+    if (dim == 0) {
+      a.ml[(pbase + n) * 2] = mx;
+      a.ml[(pbase + n) * 2 + 1] = ls;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------- partial (MFMA)
+
+// bf16 K/V and bf16 queries: Q·Kᵀ runs on the matrix cores.  Each wave owns 16-row tiles; one
+// v_mfma_f32_16x16x32_bf16 per 32 dims takes A = the tile's K rows (lane l holds 16 bytes of
+// row l%16) and B = the group's query vectors (query l%16), giving every lane the logits of
+// rows 4(l/16)..+3 for query l%16.  The online softmax runs in that layout; the probabilities go
+// through LDS to a row-per-16-lanes layout where P·V accumulates in fp32 on the VALU.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#ifndef SPK_MFMA_MIN_WAVES
+#define SPK_MFMA_MIN_WAVES 2
+#endif
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+#ifndef SPK_MFMA_BATCH
+#define SPK_MFMA_BATCH 2
+#endif
+
+template <int D, int NQ, bool kMask, int MODE>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_kernel(AttnArgs a) {
+  constexpr int BATCH = NQ <= 8 ? SPK_MFMA_BATCH : 1;  // tiles in flight per wave
+  constexpr int TILE = 16;                // rows per wave per step
+  constexpr int STEP = TILE * kWaves;     // rows per workgroup per step
+  constexpr int KCH = D / 32;             // MFMA k-chunks per row
+  constexpr int LPR = D / 8;              // P·V layout: lanes per row
+  constexpr int RPI = kWave / LPR;        // P·V layout: rows per instruction
+  constexpr int PVI = TILE / RPI;         // P·V instructions per tile
+  constexpr int kTab = kMaxRows + 2 * STEP;
+  static_assert(NQ <= 16, "at most 16 query vectors per group");
+  static_assert(BATCH <= 2, "row table padding covers two steps past the last row");
+  __shared__ float red[kWaves][NQ][D + 2];
+  __shared__ ulonglong2 addr_s[kTab];
+  __shared__ uint32_t mask_s[kMask ? kTab : 1];
+  __shared__ int seg_start[kMaxIntervals], seg_pos[kMaxIntervals], seg_meta[2];
+  __shared__ float p_s[kWaves][TILE][16];
+  __shared__ float alpha_s[kWaves][16];
+
+  const int g = blockIdx.y;
+  const int split = blockIdx.x;
+  const int b = g / a.Hkv, kvh = g % a.Hkv;
+  const int lrow = a.lrow_is_batch ? b : g;
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  const int qc = lane % 16, rg = lane / 16;      // MFMA layout: query column, row group
+  const int sub = lane % LPR, slot = lane / LPR; // P·V layout
+
+  int cnt;
+  if constexpr (MODE == kListIntervals) {
+    if (wid == 0) {
+      int c = a.count[lrow];
+      c = max(0, min(c, (int)min<int64_t>(a.list_ld, kMaxIntervals - 2)));
+      build_segments(a, a.list + (int64_t)lrow * a.list_ld, c, seg_start, seg_pos, &seg_meta[0],
+                     &seg_meta[1]);
+    }
+    __syncthreads();
+    cnt = seg_meta[1];
+    if (split == 0 && threadIdx.x == 0) a.ucount[g] = cnt;
+  } else {
+    cnt = a.count[lrow];
+    cnt = max(0, min(cnt, a.count_clamp));
+  }
+  const int r0 = split * a.R;
+  if (r0 >= cnt) return;
+  const int r1 = min(r0 + a.R, cnt);
+  const int nrows = r1 - r0;
+  const int iters = (nrows + STEP - 1) / STEP;
+  const int tab_rows = (iters + 2) * STEP;
+  const uint64_t zero_row = reinterpret_cast<uint64_t>(g_zero_row);
+  {
+    const uint64_t gk = reinterpret_cast<uint64_t>(a.k) +
+                        (uint64_t)(((int64_t)b * a.kv_sb + (int64_t)kvh * a.kv_sh) * 2);
+    const uint64_t gkh = reinterpret_cast<uint64_t>(a.k_host) +
+                         (uint64_t)(((int64_t)b * a.host_sb + (int64_t)kvh * a.host_sh) * 2);
+    const uint64_t dd = reinterpret_cast<uint64_t>(a.v) - reinterpret_cast<uint64_t>(a.k);
+    const uint64_t dh = reinterpret_cast<uint64_t>(a.v_host) - reinterpret_cast<uint64_t>(a.k_host);
+    const int32_t* list = a.list + (int64_t)lrow * a.list_ld;
+    const uint32_t* mrow = kMask ? a.mask + (int64_t)g * a.list_ld : nullptr;
+    for (int i = threadIdx.x; i < tab_rows; i += kThreads) {
+      int slot_v = kDead;
+      if (i < nrows) {
+        int tok;
+        if constexpr (MODE == kListIntervals) tok = token_at(seg_start, seg_pos, seg_meta[0], r0 + i);
+        else tok = list[r0 + i];
+        slot_v = resolve_slot(a, b, kvh, tok);
+      }
+      ulonglong2 ad;
+      if (slot_v == kDead) {
+        ad.x = ad.y = zero_row;
+      } else if (slot_v < 0) {
+        ad.x = gkh + (uint64_t)((int64_t)(~slot_v) * a.host_sn * 2);
+        ad.y = ad.x + dh;
+      } else {
+        ad.x = gk + (uint64_t)((int64_t)slot_v * a.kv_sn * 2);
+        ad.y = ad.x + dd;
+      }
+      addr_s[i] = ad;
+      if constexpr (kMask) mask_s[i] = i < nrows ? mrow[r0 + i] : 0u;
+    }
+  }
+
+  // queries as the MFMA B operand: lane holds Q[query qc][32j + 8rg .. +7]
+  bf16x8 qb[KCH];
+  {
+    const bool have = qc < a.nq;
+    const int t = qc / a.G, hl = qc % a.G;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl) * D + 8 * rg;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (have) u = *reinterpret_cast<const uint4*>(qp + 32 * j);
+      qb[j] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  float m_q = -INFINITY, l_part = 0.f;  // query qc: running max (wave-uniform), own-row denominator
+  float acc[NQ][8];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[n][i] = 0.f;
+  __syncthreads();
+
+  const uint64_t kcol = (uint64_t)(16 * rg);
+  const uint64_t vcol = (uint64_t)(16 * sub);
+  const int qd = qc / a.mask_div;
+  int64_t lg_row = 0;
+  if (a.logits && qc < a.nq) {
+    const int t = qc / a.G, hl = qc % a.G;
+    lg_row = ((int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl) * a.logits_ld + r0;
+  }
+
+  auto issue = [&](int it, uint4 (&kr)[KCH], uint4 (&vr)[PVI], bool& klive) {
+    const int tb = it * STEP + wid * TILE;
+    const ulonglong2 e = addr_s[tb + qc];
+    klive = e.x != zero_row;
+    ulonglong2 ev[PVI];
+#pragma unroll
+    for (int i = 0; i < PVI; ++i) ev[i] = addr_s[tb + i * RPI + slot];
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) kr[j] = gload16(e.x + kcol + 64 * j);
+#pragma unroll
+    for (int i = 0; i < PVI; ++i) vr[i] = gload16(ev[i].y + vcol);
+  };
+  auto consume = [&](int it, const uint4 (&kr)[KCH], const uint4 (&vr)[PVI], bool klive) {
+    const int tb = it * STEP + wid * TILE;
+    const uint64_t liveb = __ballot(klive);  // bit r (< 16): row r of the tile is read
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KCH; ++j)
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[j]), qb[j], S, 0, 0, 0);
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * rg + i;
+      bool rd = ((liveb >> r) & 1ull) && qc < a.nq;
+      if constexpr (kMask) rd = rd && ((mask_s[tb + r] >> qd) & 1u);
+      sv[i] = rd ? S[i] * a.scale_log2 : -INFINITY;
+    }
+    if (a.logits && qc < a.nq) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = tb + 4 * rg + i;
+        if (p < nrows) a.logits[lg_row + p] = sv[i] * kLn2;
+      }
+    }
+    float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float m_new = fmaxf(m_q, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_q - m_new);
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = (sv[i] == -INFINITY) ? 0.f : fast_exp2(sv[i] - m_new);
+    l_part = l_part * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+    m_q = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p_s[wid][4 * rg + i][qc] = pv[i];
+    if (rg == 0) alpha_s[wid][qc] = alpha;
+    wave_lds_fence();
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        const float an = alpha_s[wid][n];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[n][i] *= an;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PVI; ++i) {
+      const int r = i * RPI + slot;
+      float pr[NQ];
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) pr[n] = p_s[wid][r][n];
+      float y[8];
+      y[0] = bf16_lo(vr[i].x); y[1] = bf16_hi(vr[i].x); y[2] = bf16_lo(vr[i].y); y[3] = bf16_hi(vr[i].y);
+      y[4] = bf16_lo(vr[i].z); y[5] = bf16_hi(vr[i].z); y[6] = bf16_lo(vr[i].w); y[7] = bf16_hi(vr[i].w);
+#pragma unroll
+      for (int n = 0; n < NQ; ++n)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[n][e] = fmaf(pr[n], y[e], acc[n][e]);
+    }
+    wave_lds_fence();
+  };
+
+  {
+    // Each iteration loads BATCH tiles per wave, then consumes them in order; no load is
+    // carried across iterations (loop-carried loads make the compiler drain at the loop head).
+    // Latency is covered by the other resident waves.
+    uint4 kb[BATCH][KCH], vb[BATCH][PVI];
+    bool lv[BATCH];
+    for (int it = 0; it < iters; it += BATCH) {
+#pragma unroll
+      for (int t = 0; t < BATCH; ++t) issue(it + t, kb[t], vb[t], lv[t]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < BATCH; ++t) {
+        consume(it + t, kb[t], vb[t], lv[t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // wave totals: denominators over the 4 row groups; P·V partials over the slots (every slot
+  // of the wave was scaled against the same running maxima)
+  l_part += __shfl_xor(l_part, 16, kWave);
+  l_part += __shfl_xor(l_part, 32, kWave);
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1)
+#pragma unroll
+    for (int n = 0; n < NQ; ++n)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[n][i] += __shfl_xor(acc[n][i], off, kWave);
+  if (lane < LPR) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wid][n][2 + sub * 8 + i] = acc[n][i];
+  }
+  if (rg == 0 && qc < NQ) {
+    red[wid][qc][0] = m_q;
+    red[wid][qc][1] = l_part;
+  }
+  __syncthreads();
   const int64_t pbase = ((int64_t)g * a.smax + split) * NQ;
   for (int e = threadIdx.x; e < NQ * D; e += kThreads) {
     const int n = e / D, dim = e % D;
@@ -603,15 +918,36 @@ __global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a, int nq_
   if (lse && lane == 0) lse[qrow] = empty ? -INFINITY : (mx + log2f(L)) * kLn2;
 }
 
+#ifndef SPK_ATTN_UNROLL_SMALL
+#define SPK_ATTN_UNROLL_SMALL 4
+#endif
+#ifndef SPK_ATTN_UNROLL_LARGE
+#define SPK_ATTN_UNROLL_LARGE 2
+#endif
+constexpr int attn_unroll(int nq) { return nq <= 4 ? SPK_ATTN_UNROLL_SMALL : SPK_ATTN_UNROLL_LARGE; }
+
 template <int D, typename KT, int NQ, bool kMask, int MODE>
 void launch_partial(dim3 grid, hipStream_t st, const AttnArgs& a) {
-  constexpr int U = NQ <= 4 ? 4 : 2;
+  constexpr int U = attn_unroll(NQ);
   hipLaunchKernelGGL((attn_partial_kernel<D, KT, NQ, kMask, MODE, U>), grid, dim3(kThreads), 0, st,
                      a);
 }
 
+template <int D, int NQ, bool kMask, int MODE>
+void launch_partial_mfma(dim3 grid, hipStream_t st, const AttnArgs& a) {
+  hipLaunchKernelGGL((attn_partial_mfma_kernel<D, NQ, kMask, MODE>), grid, dim3(kThreads), 0, st, a);
+}
+
 template <int D, typename KT, int NQ>
 void dispatch_mode(bool mask, int mode, dim3 grid, hipStream_t st, const AttnArgs& a) {
+  if constexpr (std::is_same<KT, uint16_t>::value) {
+    if (a.q_bf16) {
+      if (mask) launch_partial_mfma<D, NQ, true, kListExplicit>(grid, st, a);
+      else if (mode == kListIntervals) launch_partial_mfma<D, NQ, false, kListIntervals>(grid, st, a);
+      else launch_partial_mfma<D, NQ, false, kListExplicit>(grid, st, a);
+      return;
+    }
+  }
   if (mask) launch_partial<D, KT, NQ, true, kListExplicit>(grid, st, a);
   else if (mode == kListIntervals) launch_partial<D, KT, NQ, false, kListIntervals>(grid, st, a);
   else launch_partial<D, KT, NQ, false, kListExplicit>(grid, st, a);
@@ -628,7 +964,7 @@ void dispatch_nq(int nq_pad, bool mask, int mode, dim3 grid, hipStream_t st, con
   }
 }
 
-// Resident partial workgroups per CU for the bf16 instance of a configuration (queried once).
+// Resident partial workgroups per CU of the bf16 (MFMA) kernel of a configuration (queried once).
 int partial_occupancy(int d, int nq_pad, bool mask, int mode) {
   static int cache[2][5][2][2];
   const int di = d == 128 ? 0 : 1;
@@ -636,10 +972,10 @@ int partial_occupancy(int d, int nq_pad, bool mask, int mode) {
   int& c = cache[di][ni][mask ? 1 : 0][mode ? 1 : 0];
   if (c > 0) return c;
   const void* fn = nullptr;
-#define SPK_FN(D, NQ)                                                                          \
-  fn = mask ? (const void*)attn_partial_kernel<D, uint16_t, NQ, true, kListExplicit, (NQ <= 4 ? 4 : 2)>   \
-       : mode ? (const void*)attn_partial_kernel<D, uint16_t, NQ, false, kListIntervals, (NQ <= 4 ? 4 : 2)> \
-              : (const void*)attn_partial_kernel<D, uint16_t, NQ, false, kListExplicit, (NQ <= 4 ? 4 : 2)>
+#define SPK_FN(D, NQ)                                                                     \
+  fn = mask ? (const void*)attn_partial_mfma_kernel<D, NQ, true, kListExplicit>            \
+       : mode ? (const void*)attn_partial_mfma_kernel<D, NQ, false, kListIntervals>        \
+              : (const void*)attn_partial_mfma_kernel<D, NQ, false, kListExplicit>
 #define SPK_FN_D(D)                     \
   switch (nq_pad) {                     \
     case 1: SPK_FN(D, 1); break;        \

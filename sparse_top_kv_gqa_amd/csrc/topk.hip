@@ -4,6 +4,8 @@
 // Contexto no Tempo de Inferência", §2 "Oracle Top-K" (exact top-k tokens).
 //
 // One workgroup per row.  Scores map to order-preserving uint32 keys (-0 -> +0, NaN lowest).
+//  * n <= 4096: one wave holds the row in registers (up to 64 keys per lane) and needs no
+//    barrier at all.
 //  * n <= 16384: 256 threads hold the row in registers (up to 64 keys each).  The k-th largest
 //    key is found bit by bit from the top: a candidate threshold is kept when at least k keys
 //    reach it, the count coming from wave ballots (scalar popcounts) summed across the 4 waves.
@@ -23,6 +25,53 @@ constexpr int kSmallMax = 64 * kSmallThreads;  // 16384
 constexpr int kRadixThreads = 1024;
 
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
+
+// One wave per row (n <= 4096): item c of lane t is element c*64 + t.  Counting needs only
+// ballots and scalar popcounts, so the bit search runs without any barrier.
+template <int ITEMS>
+__global__ __launch_bounds__(kWave) void topk_wave_kernel(
+    const float* __restrict__ scores, int64_t s_ld, int n, int k, int32_t* __restrict__ idx,
+    int64_t idx_ld, int32_t* __restrict__ count) {
+  const int row = blockIdx.x;
+  const float* x = scores + (int64_t)row * s_ld;
+  const int kk = min(k, n);
+  const int lane = lane_id();
+  if (count && lane == 0) count[row] = kk;
+  if (kk <= 0) return;
+  int32_t* out = idx + (int64_t)row * idx_ld;
+  uint32_t key[ITEMS];
+#pragma unroll
+  for (int c = 0; c < ITEMS; ++c) {
+    const int i = c * kWave + lane;
+    key[c] = i < n ? order_key(x[i]) : 0u;
+  }
+  auto count_ge = [&](uint32_t cand) -> int {
+    int wc = 0;
+#pragma unroll
+    for (int c = 0; c < ITEMS; ++c) wc += __popcll(__ballot((c * kWave + lane < n) && key[c] >= cand));
+    return wc;
+  };
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    if (count_ge(cand) >= kk) thr = cand;
+  }
+  const int need = kk - (thr == 0xFFFFFFFFu ? 0 : count_ge(thr + 1u));
+  int run_gt = 0, run_eq = 0;
+  const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int c = 0; c < ITEMS; ++c) {
+    const int i = c * kWave + lane;
+    const bool valid = i < n;
+    const bool gt = valid && key[c] > thr;
+    const bool eq = valid && key[c] == thr;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    const int eq_rank = run_eq + __popcll(be & lt);
+    if (gt || (eq && eq_rank < need)) out[run_gt + __popcll(bg & lt) + min(eq_rank, need)] = i;
+    run_gt += __popcll(bg);
+    run_eq += __popcll(be);
+  }
+}
 
 // Keys of row `x` held in registers: item c of thread t is element c*256 + t.
 template <int ITEMS>
@@ -196,7 +245,19 @@ extern "C" SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int
   clear_error();
   if (rows == 0) return SPK_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (n <= kSmallMax) {
+  if (n <= 64 * kWave) {
+    const int items = (n + kWave - 1) / kWave;
+#define SPK_WAVE(IT) \
+  hipLaunchKernelGGL(topk_wave_kernel<IT>, dim3(rows), dim3(kWave), 0, st, scores, s_ld, n, k, idx, idx_ld, count)
+    if (items <= 1) SPK_WAVE(1);
+    else if (items <= 2) SPK_WAVE(2);
+    else if (items <= 4) SPK_WAVE(4);
+    else if (items <= 8) SPK_WAVE(8);
+    else if (items <= 16) SPK_WAVE(16);
+    else if (items <= 32) SPK_WAVE(32);
+    else SPK_WAVE(64);
+#undef SPK_WAVE
+  } else if (n <= kSmallMax) {
     const int items = (n + kSmallThreads - 1) / kSmallThreads;
 #define SPK_SMALL(IT)                                                                          \
   hipLaunchKernelGGL(topk_small_kernel<IT>, dim3(rows), dim3(kSmallThreads), 0, st, scores, s_ld, \
