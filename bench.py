@@ -3,20 +3,32 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input, with every input
-resident in HBM before the timed region.  Default workload: a Llama-3-8B-shaped layer (batch 8,
-32 query / 8 KV heads, d 128, 32768 cached tokens, bf16 K/V): predictor scores of mean-pooled
-64-token blocks -> top-32 blocks -> exact attention over the blocks plus 4 sinks and the 512
-most recent tokens.  Steps rotate through 8 independent layer caches and fresh queries, so
-no step finds the previous step's rows in the 256 MB last-level cache.
+resident in HBM (or, for host-resident rows, in pinned host memory) before the timed region.
+
+Workloads (default: block):
+  block        Llama-3-8B-shaped layer: batch 8, 32/8 heads, d 128, 32768 cached tokens, bf16.
+               Predictor scores of mean-pooled 64-token blocks -> top-32 blocks -> attention over
+               the blocks plus 4 sinks and the 512 most recent tokens.  Steps rotate through 8
+               layer caches with fresh queries, so no step finds the previous rows in the 256 MB
+               last-level cache.
+  per_head     batch 4, 32/8 heads, 131072 tokens, 1% outlier keys; every query head keeps its own
+               exact top-2% (2622) tokens; each KV group fetches the union of its heads' sets.
+  spec_verify  batch 16, 4 draft tokens, 32/8 heads, 65536 tokens; group-mean top-2048 per token;
+               the union per KV group is fetched once; 10% of each group's rows live in pinned
+               host memory and are read over PCIe inside the attention kernel.
+  tiers        batch 32, 28 layers, 28/4 heads, 64 decode steps growing 4096 -> 16384 tokens:
+               tier classification -> attention over T0 ∪ T1 in all layers -> importance update.
 
 Prints ONE JSON line.  `value` is the step's algorithmic bytes (index keys read + selected K/V
-rows) per second; `roofline` reports the attention kernel against the 8 TB/s HBM peak;
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+rows) per second; `roofline` reports the dominant kernel against the 8 TB/s HBM peak with its
+duration measured by HIP events on its own stream; `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -24,16 +36,18 @@ import time
 import torch
 
 HBM_PEAK_GBS = 8000.0
+METRIC = "sparse decode attn: selected-KV GB/s (% of HBM peak), decode steps/s"
+ROW_BYTES = 2 * 128 * 2  # one token's K and V for one KV head, bf16, d = 128
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="block", choices=["block", "per_head", "spec_verify",
-                                                            "tiers", "tiny"])
-    ap.add_argument("--layers", type=int, default=8, help="independent layer caches to rotate")
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="block",
+                    choices=["block", "per_head", "spec_verify", "tiers"])
+    ap.add_argument("--layers", type=int, default=8, help="block: layer caches to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
@@ -43,10 +57,85 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-# ------------------------------------------------------------------------------ block workload
+def host(t):
+    """CPU copy for the oracle: bf16 as raw uint16 bits, float as float32."""
+    import numpy as np
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
 
-def union_rows_block(idx, count, n_tokens, bs, n_sink, n_recent):
-    """Rows each (b, kvh) group fetches for a block selection (setup-time bookkeeping)."""
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n and n[0]:
+            return int(n[0])
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def event_time_ms(fn, reps, stream, per_call=None):
+    """Median duration of fn() bracketed by HIP events recorded on `stream`."""
+    evs = []
+    with torch.cuda.stream(stream):
+        for i in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    return t[len(t) // 2]
+
+
+def timed_loop(run_step, K, W, stream):
+    """W untimed steps, then exactly K steps bracketed by synchronisations and events."""
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            run_step(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(K):
+            run_step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1), wall
+
+
+def base_result(w, K, W, ms_step, step_bytes, config):
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_step, 5), "steps_per_s": round(1e3 / ms_step, 2),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16)", "config": config,
+    }
+
+
+def roofline(kernel, bytes_per_launch, ms, traffic=None, note=None):
+    gbs = bytes_per_launch / (ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+         "avg_launch_us": round(ms * 1e3, 3), "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+    if note:
+        r["note"] = note
+    return r
+
+
+# ------------------------------------------------------------------------------ block
+
+def union_rows_block(idx, n_tokens, bs, n_sink, n_recent):
+    """Rows the (b, kvh) groups fetch for a block selection (setup-time bookkeeping)."""
     G = idx.shape[0] * idx.shape[2]
     blocks = idx.reshape(G, -1).long()
     mask = torch.zeros((G, n_tokens), dtype=torch.bool, device=idx.device)
@@ -59,36 +148,34 @@ def union_rows_block(idx, count, n_tokens, bs, n_sink, n_recent):
 
 def bench_block(args):
     import workloads as W
+    from sparse_top_kv_gqa_amd import sparse_decode_attn
     from sparse_top_kv_gqa_amd.decode import BlockSparseDecode
 
     w = W.LLAMA8B_BLOCK
-    dev = "cuda"
+    K = args.steps or 400
+    Wm = args.warmup if args.warmup is not None else 40
     L = args.layers
     log(f"generating {L} layer caches of {w.name}")
     decs, qs, preds = [], [], []
     for l in range(L):
-        k = W.kv_cache(w, "k", layer=l, device=dev)
-        v = W.kv_cache(w, "v", layer=l, device=dev)
+        k = W.kv_cache(w, "k", layer=l, device="cuda")
+        v = W.kv_cache(w, "v", layer=l, device="cuda")
         d = BlockSparseDecode(k, v, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent)
-        d.pool(W.predictors(w, step=0, layer=l, device=dev))
+        d.pool(W.predictors(w, step=0, layer=l, device="cuda"))   # block pooling, once per cache
         decs.append(d)
-        qs.append(W.queries(w, step=1, layer=l, device=dev))
-        preds.append(W.predictors(w, step=1, layer=l, device=dev))
+        qs.append(W.queries(w, step=1, layer=l, device="cuda"))
+        preds.append(W.predictors(w, step=1, layer=l, device="cuda"))
     torch.cuda.synchronize()
-    # bytes of each step (selection depends on the step's predictor)
     rows = []
     for l in range(L):
         decs[l].step(qs[l], preds[l])
-        rows.append(union_rows_block(decs[l].idx, decs[l].count, w.N, w.block_size, w.n_sink,
-                                     w.n_recent))
-    row_bytes = 2 * w.d * 2                                     # K + V, bf16
-    index_bytes = w.B * w.Hkv * (w.N // w.block_size) * w.d * 4  # fp32 pooled keys
-    sel_bytes = [r * row_bytes for r in rows]
+        rows.append(union_rows_block(decs[l].idx, w.N, w.block_size, w.n_sink, w.n_recent))
+    index_bytes = w.B * w.Hkv * (w.N // w.block_size) * w.d * 4   # fp32 pooled keys
+    sel_bytes = [r * ROW_BYTES for r in rows]
     step_bytes = [index_bytes + s for s in sel_bytes]
 
-    # one HIP graph per layer slot: index -> top-k -> attention
-    graphs = []
     stream = torch.cuda.Stream()
+    graphs = []
     with torch.cuda.stream(stream):
         for l in range(L):
             decs[l].step(qs[l], preds[l])
@@ -99,117 +186,50 @@ def bench_block(args):
                 decs[l].step(qs[l], preds[l])
             graphs.append(g)
     torch.cuda.synchronize()
-
-    K, Wm = args.steps, args.warmup
-    with torch.cuda.stream(stream):
-        for i in range(Wm):
-            graphs[i % L].replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for i in range(K):
-            graphs[i % L].replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / K
-    # graph replays must reproduce an eager step bit for bit
-    ref = []
+    ms_total, wall = timed_loop(lambda i: graphs[i % L].replay(), K, Wm, stream)
+    ms_step = ms_total / K
+    # graph replays reproduce an eager step bit for bit
     for l in range(min(L, 2)):
         graphs[l].replay()
         torch.cuda.synchronize()
-        ref.append(decs[l].out.clone())
+        ref = decs[l].out.clone()
         decs[l].step(qs[l], preds[l])
         torch.cuda.synchronize()
-        assert torch.equal(ref[-1], decs[l].out), "graph replay differs from eager step"
+        assert torch.equal(ref, decs[l].out), "graph replay differs from eager step"
 
+    def attn(i):
+        d = decs[i % L]
+        sparse_decode_attn(qs[i % L], d.k, d.v, d.idx, d.count, "per_kv_head", d.n_tokens,
+                           gran=d.bs, n_sink=d.n_sink, n_recent=d.n_recent, sm_scale=d.sm_scale,
+                           out=d.out, lse=d.lse, ws=d.ws, stream=stream)
+    att_ms = event_time_ms(attn, 8 * L, stream)
+    att_bytes = sum(sel_bytes) / L
     bytes_avg = sum(step_bytes[i % L] for i in range(K)) / K
-    sel_avg = sum(sel_bytes[i % L] for i in range(K)) / K
-
-    # attention kernel alone, same stream, eager launches bracketed by events
-    att_ms = []
-    with torch.cuda.stream(stream):
-        for rep in range(3):
-            for l in range(L):
-                decs[l].step(qs[l], preds[l])
-        torch.cuda.synchronize()
-        n_rep = 0
-        tot = 0.0
-        from sparse_top_kv_gqa_amd import sparse_decode_attn
-        for rep in range(max(4, K // L // 4)):
-            for l in range(L):
-                d = decs[l]
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                sparse_decode_attn(qs[l], d.k, d.v, d.idx, d.count, "per_kv_head", d.n_tokens,
-                                   gran=d.bs, n_sink=d.n_sink, n_recent=d.n_recent,
-                                   sm_scale=d.sm_scale, out=d.out, lse=d.lse, ws=d.ws,
-                                   stream=stream)
-                b.record(stream)
-                att_ms.append((a, b, sel_bytes[l]))
-        torch.cuda.synchronize()
-    att_time = sum(a.elapsed_time(b) for a, b, _ in att_ms) / len(att_ms)
-    att_bytes = sum(x for _, _, x in att_ms) / len(att_ms)
-    att_gbs = att_bytes / (att_time * 1e-3) / 1e9
-
-    gbs = bytes_avg / (ms_step * 1e-3) / 1e9
-    res = {
-        "metric": "sparse decode attn: selected-KV GB/s (% of HBM peak), decode steps/s",
-        "value": round(gbs, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": Wm,
-        "ms_per_step": round(ms_step, 5),
-        "steps_per_s": round(1e3 / ms_step, 1),
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                   "head_dim": w.d, "context": w.N, "block_size": w.block_size,
-                   "top_blocks": w.k, "sinks": w.n_sink, "recent": w.n_recent,
-                   "layer_caches_rotated": L, "bytes_per_step": int(bytes_avg),
-                   "selected_rows_per_step": int(sel_avg / row_bytes),
-                   "wall_s_timed": round(wall, 4)},
-        "roofline": {"bound": "hbm", "kernel": "sparse_decode_attn", "achieved": round(att_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "avg_launch_us": round(att_time * 1e3, 3),
-                     "algorithmic_bytes_per_launch": int(att_bytes)},
-    }
-    ctx = dict(w=w, decs=decs, qs=qs, preds=preds)
+    res = base_result(w, K, Wm, ms_step, bytes_avg, {
+        "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+        "context": w.N, "block_size": w.block_size, "top_blocks": w.k, "sinks": w.n_sink,
+        "recent": w.n_recent, "layer_caches_rotated": L, "bytes_per_step": int(bytes_avg),
+        "selected_rows_per_step": int(att_bytes / ROW_BYTES), "wall_s_timed": round(wall, 4)})
+    res["roofline"] = roofline("sparse_decode_attn (partial + combine launches)", att_bytes, att_ms)
+    ctx = dict(w=w, dec=decs[0], q=qs[0], pred=preds[0])
     return res, ctx
 
 
-def cpu_baseline_block(ctx, seconds):
+def cpu_block(ctx, seconds):
     """The fp64 oracle, untuned, on a bounded sample: whole (b, kvh) groups of one step."""
-    import numpy as np
     import oracle
     from oracle import steps as osteps
-    w, d0 = ctx["w"], ctx["decs"][0]
-    q, pred = ctx["qs"][0], ctx["preds"][0]
-
-    def host(t):
-        t = t.detach().cpu().contiguous()
-        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
-
+    w, d0, q, pred = ctx["w"], ctx["dec"], ctx["q"], ctx["pred"]
     scale = oracle.softmax_scale(w.d)
     groups = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
-    done = 0
-    spent = 0.0
-    G = w.G
+    done, spent, G = 0, 0.0, w.G
+    qh, ph = host(q), host(pred)
     for (b, h) in groups:
         kh, vh = host(d0.k[b, h]), host(d0.v[b, h])
         kpool = d0.kpool[b, h].cpu().numpy()
         t0 = time.perf_counter()
-        osteps.block_group(host(pred)[b, 0, h], kh, vh, host(q)[b, 0, h * G:(h + 1) * G], w.k,
-                           w.block_size, w.n_sink, w.n_recent, scale, kpool=kpool)
+        osteps.block_group(ph[b, 0, h], kh, vh, qh[b, 0, h * G:(h + 1) * G], w.k, w.block_size,
+                           w.n_sink, w.n_recent, scale, kpool=kpool)
         spent += time.perf_counter() - t0
         done += 1
         if spent >= seconds:
@@ -221,37 +241,263 @@ def cpu_baseline_block(ctx, seconds):
                       f"({spent:.1f} s), scaled to the whole step"}
 
 
-def _cores():
-    try:
-        import numpy  # noqa: F401
-        from threadpoolctl import threadpool_info
-        n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n and n[0]:
-            return int(n[0])
-    except Exception:
-        pass
-    return len(os.sched_getaffinity(0))
+# ------------------------------------------------------------------------------ token sparse
+
+def union_rows_tokens(idx, count, per_group_rows, N):
+    """Rows each (b, kvh) group fetches: union of the selection rows that map to it.
+    idx [B, T, Hs, k] int32; per_group_rows: selection rows per group along (T, Hs/Hkv)."""
+    B, T, Hs, k = idx.shape
+    Hkv = Hs // per_group_rows
+    sel = idx.long().reshape(B, T, Hkv, per_group_rows, k).permute(0, 2, 1, 3, 4).reshape(B * Hkv, -1)
+    mask = torch.zeros((B * Hkv, N), dtype=torch.bool, device=idx.device)
+    mask.scatter_(1, sel, True)
+    return mask.sum(dim=1)
+
+
+def bench_token(args, which):
+    import workloads as W
+    import sparse_top_kv_gqa_amd as spk
+    from sparse_top_kv_gqa_amd.decode import TokenSparseDecode
+
+    w = W.PER_HEAD_2PCT if which == "per_head" else W.SPEC_VERIFY
+    K = args.steps or 20
+    Wm = args.warmup if args.warmup is not None else 3
+    P = 4  # query sets rotated through
+    log(f"generating {w.name}")
+    k = W.kv_cache(w, "k", device="cuda")
+    v = W.kv_cache(w, "v", device="cuda")
+    qs = [W.queries(w, step=s, device="cuda") for s in range(P)]
+    kh_pool = vh_pool = loc = None
+    host_rows_total = 0
+    if w.host_frac > 0:
+        # a seeded 10% of every group's rows live in pinned host memory
+        n_host = int(round(w.host_frac * w.N))
+        loc = torch.arange(w.N, dtype=torch.int32, device="cuda").repeat(w.B, w.Hkv, 1)
+        kh_pool = torch.empty((w.B, w.Hkv, n_host, w.d), dtype=torch.bfloat16, pin_memory=True)
+        vh_pool = torch.empty_like(kh_pool).pin_memory()
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                rows = W.host_rows(w, b, h, torch.arange(w.N)).to("cuda")
+                kh_pool[b, h].copy_(k[b, h, rows].cpu())
+                vh_pool[b, h].copy_(v[b, h, rows].cpu())
+                loc[b, h, rows] = ~torch.arange(rows.numel(), dtype=torch.int32, device="cuda")
+        host_rows_total = w.B * w.Hkv * n_host
+    mode = "token_per_head" if which == "per_head" else "token_group_mean"
+    dec = TokenSparseDecode(k, v, w.N, w.Hq, w.T, w.k, mode, k_host=kh_pool, v_host=vh_pool,
+                            loc=loc)
+    torch.cuda.synchronize()
+    # bytes: every key read by the indexer + the union rows of each step
+    per_group_rows = w.G if which == "per_head" else 1
+    union = []
+    host_frac = []
+    for s in range(P):
+        dec.step(qs[s])
+        u = union_rows_tokens(dec.idx, dec.count, per_group_rows if which == "per_head" else 1, w.N) \
+            if which == "per_head" else None
+        if which != "per_head":
+            # spec verify: rows of (b, kvh) = union over the T draft tokens
+            B, T, Hkv, kk = dec.idx.shape
+            sel = dec.idx.long().permute(0, 2, 1, 3).reshape(B * Hkv, T * kk)
+            m = torch.zeros((B * Hkv, w.N), dtype=torch.bool, device="cuda")
+            m.scatter_(1, sel, True)
+            u = m.sum(dim=1)
+            hm = (loc.reshape(B * Hkv, w.N) < 0) & m
+            host_frac.append(float(hm.sum()) / float(m.sum()))
+        union.append(int(u.sum()))
+    index_bytes = w.B * w.Hkv * w.N * w.d * 2
+    sel_bytes = [u * ROW_BYTES for u in union]
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    ms_total, wall = timed_loop(lambda i: dec.step(qs[i % P]), K, Wm, stream)
+    ms_step = ms_total / K
+    idx_ms = event_time_ms(lambda i: spk.sparse_index_score(mode, qs[i % P], dec.index_keys, w.N,
+                                                            scores=dec.scores, stream=stream),
+                           10, stream)
+    dec.select(qs[0])
+    torch.cuda.synchronize()
+    att_ms = event_time_ms(lambda i: dec.attend(qs[0]), 10, stream)
+    topk_ms = event_time_ms(lambda i: spk.topk_select(dec.scores, dec.topk, idx=dec.idx,
+                                                      count=dec.count, stream=stream), 10, stream)
+    bytes_avg = index_bytes + sum(sel_bytes) / P
+    cfg = {"workload": w.name, "batch": w.B, "query_tokens": w.T, "q_heads": w.Hq,
+           "kv_heads": w.Hkv, "head_dim": w.d, "context": w.N, "topk": w.k,
+           "bytes_per_step": int(bytes_avg), "index_bytes": index_bytes,
+           "selected_rows_per_step": int(sum(union) / P), "wall_s_timed": round(wall, 4),
+           "index_ms": round(idx_ms, 4), "topk_ms": round(topk_ms, 4),
+           "attention_ms": round(att_ms, 4),
+           "attention_selected_GBs": round(union[0] * ROW_BYTES / (att_ms * 1e-3) / 1e9, 1)}
+    if w.host_frac > 0:
+        cfg["host_fraction_of_selected_rows"] = round(sum(host_frac) / len(host_frac), 4)
+        cfg["host_rows_resident"] = host_rows_total
+        hb = sum(host_frac) / len(host_frac) * union[0] * ROW_BYTES
+        cfg["pcie_GBs_in_attention"] = round(hb / (att_ms * 1e-3) / 1e9, 2)
+    res = base_result(w, K, Wm, ms_step, bytes_avg, cfg)
+    res["roofline"] = roofline(f"sparse_index_score ({mode})", index_bytes, idx_ms)
+    ctx = dict(w=w, k=k, v=v, q=qs[0], which=which)
+    return res, ctx
+
+
+def cpu_token(ctx, seconds):
+    import oracle
+    from oracle import steps as osteps
+    w, k, v, q = ctx["w"], ctx["k"], ctx["v"], ctx["q"]
+    scale = oracle.softmax_scale(w.d)
+    groups = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    done, spent, G = 0, 0.0, w.G
+    qh = host(q)
+    for (b, h) in groups:
+        kh, vh = host(k[b, h]), host(v[b, h])
+        t0 = time.perf_counter()
+        if ctx["which"] == "per_head":
+            osteps.per_head_group(qh[b, 0, h * G:(h + 1) * G], kh, vh, w.k, scale)
+        else:
+            osteps.group_mean_group(qh[b, :, h * G:(h + 1) * G], kh, vh, w.k, scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= seconds:
+            break
+    per_step = spent / done * len(groups)
+    return {"value": round(1.0 / per_step, 5), "unit": "decode steps/s", "cores": _cores(),
+            "kind": "oracle",
+            "sample": f"{done} of {len(groups)} (batch, kv-head) groups of one step "
+                      f"({spent:.1f} s), scaled to the whole step"}
+
+
+# ------------------------------------------------------------------------------ tiers
+
+def bench_tiers(args):
+    import workloads as W
+    import sparse_top_kv_gqa_amd as spk
+    from sparse_top_kv_gqa_amd.decode import TieredDecode
+
+    w = W.REASONING_TIERS
+    steps = w.steps
+    K = args.steps or steps
+    Wm = args.warmup if args.warmup is not None else 0
+    log(f"generating {w.layers} layer caches of {w.name}")
+    caches = [(W.kv_cache(w, "k", l, "cuda", n_cap=w.N), W.kv_cache(w, "v", l, "cuda", n_cap=w.N))
+              for l in range(w.layers)]
+    qs = [[W.queries(w, step=t, layer=l, device="cuda") for l in range(w.layers)]
+          for t in range(steps)]
+    dec = TieredDecode(caches, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille)
+    torch.cuda.synchronize()
+    n_at = [w.n_start + w.grow_per_step * (t + 1) for t in range(steps)]
+    stream = torch.cuda.Stream()
+
+    def run_episode(record_rows=None):
+        dec.s.zero_()
+        dec.evicted.zero_()
+        for t in range(min(K, steps)):
+            dec.step(qs[t], n_at[t], dense=(t == 0))
+            if record_rows is not None:
+                record_rows.append(int(dec.count.sum()))
+
+    rows = []
+    with torch.cuda.stream(stream):
+        run_episode(rows)            # warm-up episode, records the rows each step reads
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        run_episode()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    n_steps = min(K, steps)
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / n_steps
+    # bytes per step: every layer's KV groups read their sequence's T0 ∪ T1 rows
+    sel_bytes = [r * w.Hkv * w.layers * ROW_BYTES for r in rows]
+    bytes_avg = sum(sel_bytes) / n_steps
+    # attention of one layer at the last step (largest N), events on the stream
+    k0, v0 = caches[0]
+    n_last = n_at[n_steps - 1]
+
+    def attn(i):
+        spk.sparse_decode_attn(qs[n_steps - 1][0], k0, v0, dec.sel, dec.count, "per_seq", n_last,
+                               out=dec.out[0], lse=dec.lse[0], logits=dec.logits[0], ws=dec.ws,
+                               stream=stream)
+    att_ms = event_time_ms(attn, 10, stream)
+    att_bytes = rows[n_steps - 1] * w.Hkv * ROW_BYTES
+    s_copy = dec.s.clone()
+    tb = torch.empty_like(dec.tier)
+    sb = torch.empty_like(dec.sel)
+    cb = torch.empty_like(dec.count)
+    tier_ms = event_time_ms(lambda i: spk.tier_classify(s_copy, n_last, w.n_sink, w.n_recent,
+                                                        w.t0_permille, w.t01_permille, tier=tb,
+                                                        sel_idx=sb, sel_count=cb, stream=stream),
+                            5, stream)
+    imp_ms = event_time_ms(lambda i: spk.importance_accumulate(s_copy, dec.sel, dec.count,
+                                                               dec.logits, dec.lse, n_last,
+                                                               stream=stream), 5, stream)
+    res = base_result(w, n_steps, Wm, ms_step, bytes_avg, {
+        "workload": w.name, "batch": w.B, "layers": w.layers, "q_heads": w.Hq, "kv_heads": w.Hkv,
+        "head_dim": w.d, "context_start": w.n_start, "context_end": n_at[n_steps - 1],
+        "grow_per_step": w.grow_per_step, "decode_steps": n_steps,
+        "bytes_per_step_avg": int(bytes_avg), "rows_last_step_per_layer_kvh": rows[n_steps - 1],
+        "episode_s": round(ms_total / 1e3, 4), "wall_s_timed": round(wall, 4),
+        "attention_layer_ms_last_step": round(att_ms, 4), "tier_classify_ms": round(tier_ms, 4),
+        "importance_ms": round(imp_ms, 4)})
+    res["roofline"] = roofline("sparse_decode_attn (one layer, partial + combine launches)",
+                               att_bytes, att_ms)
+    ctx = dict(w=w, caches=caches, qs=qs, n_last=n_last)
+    return res, ctx
+
+
+def cpu_tiers(ctx, seconds):
+    """One dense decode step of whole sequences (all layers), the oracle as it stands."""
+    import numpy as np
+    import oracle
+    from oracle import steps as osteps
+    w, caches, qs = ctx["w"], ctx["caches"], ctx["qs"]
+    n = ctx["n_last"]
+    scale = oracle.softmax_scale(w.d)
+    done, spent = 0, 0.0
+    for b in range(w.B):
+        qb = np.stack([host(qs[-1][l])[b, 0] for l in range(w.layers)])
+        kb = np.stack([host(caches[l][0][b, :, :n]) for l in range(w.layers)])
+        vb = np.stack([host(caches[l][1][b, :, :n]) for l in range(w.layers)])
+        s_prev = np.random.default_rng(b).random(n).astype(np.float32)
+        t0 = time.perf_counter()
+        osteps.tiered_sequence_step(s_prev, None, qb, kb, vb, n, scale, w.n_sink, w.n_recent,
+                                    w.t0_permille, w.t01_permille)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= seconds:
+            break
+    per_step = spent / done * w.B
+    return {"value": round(1.0 / per_step, 5), "unit": "decode steps/s", "cores": _cores(),
+            "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences of one tiered step at {n} tokens, all "
+                      f"{w.layers} layers ({spent:.1f} s), scaled to the whole batch"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sparse decode "
-              "path shards by (batch, KV head) with no exchange, so N GPUs would each run this "
-              "single-GPU step on their share.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the sparse decode "
+              "path shards by (batch, KV head) with no exchange between shards, so N GPUs would "
+              "each run this single-GPU step on their share; no multi-GPU figure is produced.",
+              file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import sparse_top_kv_gqa_amd as spk
     spk.lib()
-    if args.workload != "block":
-        print(f"workload {args.workload} is not wired into the bench yet", file=sys.stderr)
-        sys.exit(2)
-    res, ctx = bench_block(args)
+    if args.workload == "block":
+        res, ctx = bench_block(args)
+        cpu = cpu_block
+    elif args.workload in ("per_head", "spec_verify"):
+        res, ctx = bench_token(args, args.workload)
+        cpu = cpu_token
+    else:
+        res, ctx = bench_tiers(args)
+        cpu = cpu_tiers
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline_block(ctx, args.cpu_seconds)
+        res["cpu_baseline"] = cpu(ctx, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -165,7 +165,9 @@ SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int rows, int 
  *              row of the group's fetch list (the ascending union above), -inf for rows the
  *              query vector does not read.  For PER_SEQ with gran 1 and no sinks/recent, the
  *              fetch list is sel_idx itself.  logits_ld >= the fetch-list bound (see below).
- *   ws         device workspace of at least sparse_decode_attn_workspace_size() bytes.
+ *   ws         device workspace of at least sparse_decode_attn_workspace_size() bytes (no
+ *              initial contents needed).  Calls that may run concurrently need separate
+ *              workspaces.
  *
  * The fetch-list bound per group is min(n_tokens, sets*sel_ld*gran + n_sink + n_recent) with
  * sets = 1 (PER_SEQ), T (PER_KV_HEAD) or T*G (PER_Q_HEAD); at most 32 sets per group.

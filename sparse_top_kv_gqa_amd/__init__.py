@@ -233,7 +233,7 @@ def sparse_decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel_id
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
     wsz = attn_workspace_size(sc, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent)
     if ws is None or ws.numel() < wsz:
-        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(max(wsz, 1), dtype=torch.uint8, device=q.device)
     lg_ld = logits.stride(-2) if logits is not None else 0
     st = lib().sparse_decode_attn(_ptr(q), _dt(q), _ptr(k), _ptr(v), _dt(k), kb, kh, kn,
                                   _ptr(k_host), _ptr(v_host), hb, hh, hn, host_slots, _ptr(loc),

@@ -14,13 +14,15 @@
 //     rows): one workgroup per (b, kvh) sets one bit per token in an LDS bitmap per list, ORs
 //     the bitmaps and emits the ascending fetch list with a per-row mask of the lists holding it.
 //  2. partial   split-K over the fetch list: workgroup (split, group) walks rows
-//     [split*R, split*R + R).  D/8 lanes share a row (16 B each), so a wave reads 4 rows per load
-//     (d=128) and every query vector of the group (G heads x T tokens) is scored against each
-//     fetched row: the row is read from HBM (or host memory) once per group.  Each 16-lane slot
-//     keeps its own online-softmax state (m, l, acc in fp32, exp2 domain); slots and waves merge
-//     at the end and the split's (m, l, acc) go to the workspace.
-//  3. combine   one wave per query vector merges the splits in split order (deterministic, no
-//     atomics) into out and lse.
+//     [split*R, split*R + R) and scores every query vector of the group (G heads x T tokens)
+//     against each fetched row, so a row is read from HBM (or host memory) once per group.
+//     Online softmax in fp32 (exp2 domain); the waves merge at the end and the split's
+//     (m, l, acc) go to the workspace.  bf16 caches with bf16 queries run Q·K on MFMA; fp32 on
+//     the VALU.
+//  3. combine   one wave per query vector merges the group's splits in split order
+//     (deterministic, no atomics) into out and lse.  A separate launch: merging inside the
+//     partial kernel needs a device-scope release per workgroup, which writes back the XCD's
+//     whole L2 and costs far more than this launch.
 #include <type_traits>
 
 #include "spk_internal.h"
@@ -42,7 +44,8 @@ constexpr int kDead = INT32_MIN;    // row-table entry of a row that is not read
 struct Plan {
   int groups = 0, sets = 1, nq = 0, nq_pad = 0, ubound = 0, R = 0, smax = 0, words = 0;
   bool assemble = false, intervals = false, mask = false, bm_lds = true;
-  size_t off_list = 0, off_mask = 0, off_count = 0, off_bm = 0, off_ml = 0, off_acc = 0, bytes = 0;
+  size_t off_list = 0, off_mask = 0, off_count = 0, off_bm = 0, off_ml = 0, off_acc = 0,
+         bytes = 0;
 };
 
 int pad_nq(int nq) { return nq <= 1 ? 1 : nq <= 2 ? 2 : nq <= 4 ? 4 : nq <= 8 ? 8 : 16; }
@@ -204,7 +207,8 @@ struct AttnArgs {
   int lrow_is_batch;
   int list_mode;
   int gran, n_sink, n_recent;
-  int32_t* ucount;       // per-group fetch-list length (intervals mode writes it for combine)
+  int32_t* ucount;       // per-group fetch-list length (written by assemble or intervals mode)
+  int ucount_valid;      // ucount holds the lengths (assembled lists)
   const uint32_t* mask;  // per fetch-list row (assembled lists with several sets)
   int mask_div;          // query vector n reads rows whose mask has bit n / mask_div
   int T, Hq, Hkv, G, nq, n_tokens, R, smax;
@@ -214,6 +218,31 @@ struct AttnArgs {
   float* logits;
   int64_t logits_ld;
 };
+
+// End of a partial workgroup: merge the 4 waves' (m, l, acc) from `red` and store this split's
+// partial for the combine kernel.
+template <int D, int NQ, int NW>
+__device__ void finish_split(const AttnArgs& a, float (&red)[NW][NQ][D + 2], int g, int split) {
+  const int64_t pbase = ((int64_t)g * a.smax + split) * NQ;
+  for (int e = threadIdx.x; e < NQ * D; e += blockDim.x) {
+    const int n = e / D, dim = e % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red[w][n][0]);
+    float ls = 0.f, as = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sc = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(red[w][n][0] - mx);
+      ls += red[w][n][1] * sc;
+      as += red[w][n][2 + dim] * sc;
+    }
+    a.acc[(pbase + n) * D + dim] = as;
+    if (dim == 0) {
+      a.ml[(pbase + n) * 2] = mx;
+      a.ml[(pbase + n) * 2 + 1] = ls;
+    }
+  }
+}
 
 // Where token `tok` of group (b, kvh) lives: HBM slot (>= 0) or host slot (encoded ~slot < 0);
 // kDead when the slot lies outside its pool (the row is then not read).
@@ -235,11 +264,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the recent window [n - r, n) as <= 64 disjoint segments (start, first position); returns the
 // union size through *U.  Selection ids must be ascending (as topk_select writes them); ids that
 // expand outside [0, n) give empty intervals.
-__device__ void build_segments(const AttnArgs& a, const int32_t* sel, int cnt, int* seg_start,
-                               int* seg_pos, int* nseg, int* U) {
+__device__ void build_segments(const AttnArgs& a, const int32_t* sel, const int32_t* count_ptr,
+                               int* seg_start, int* seg_pos, int* nseg, int* U) {
   const int lane = lane_id();
   const int n = a.n_tokens;
   const int rs = max(0, n - a.n_recent);
+  // the list entries and their count load together (entries past the count are ignored)
+  const int cmax = (int)min<int64_t>(a.list_ld, kMaxIntervals - 2);
+  int64_t e_sel = -1;
+  if (lane >= 1 && lane <= cmax) e_sel = sel[lane - 1];
+  const int cnt = max(0, min(*count_ptr, cmax));
   // interval of this lane: 0 = sinks, 1..cnt = selection entries, cnt+1 = recent window
   int lo = n, hi = n;
   bool is_sel = false;
@@ -247,7 +281,7 @@ __device__ void build_segments(const AttnArgs& a, const int32_t* sel, int cnt, i
     lo = 0;
     hi = min(a.n_sink, n);
   } else if (lane <= cnt) {
-    const int64_t e = sel[lane - 1];
+    const int64_t e = e_sel;
     const int64_t s0 = e * a.gran;
     lo = (int)min<int64_t>(max<int64_t>(s0, 0), n);
     hi = (int)min<int64_t>(max<int64_t>(s0 + a.gran, 0), n);
@@ -341,12 +375,9 @@ __attribute__((amdgpu_waves_per_eu(SPK_ATTN_MIN_WAVES))) void attn_partial_kerne
 
   int cnt;
   if constexpr (MODE == kListIntervals) {
-    if (wid == 0) {
-      int c = a.count[lrow];
-      c = max(0, min(c, (int)min<int64_t>(a.list_ld, kMaxIntervals - 2)));
-      build_segments(a, a.list + (int64_t)lrow * a.list_ld, c, seg_start, seg_pos, &seg_meta[0],
-                     &seg_meta[1]);
-    }
+    if (wid == 0)
+      build_segments(a, a.list + (int64_t)lrow * a.list_ld, a.count + lrow, seg_start, seg_pos,
+                     &seg_meta[0], &seg_meta[1]);
     __syncthreads();
     cnt = seg_meta[1];
     if (split == 0 && threadIdx.x == 0) a.ucount[g] = cnt;
@@ -555,26 +586,7 @@ __attribute__((amdgpu_waves_per_eu(SPK_ATTN_MIN_WAVES))) void attn_partial_kerne
     }
   }
   __syncthreads();
-  // merge the waves; thread -> (n, dim)
-  const int64_t pbase = ((int64_t)g * a.smax + split) * NQ;
-  for (int e = threadIdx.x; e < NQ * D; e += kThreads) {
-    const int n = e / D, dim = e % D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w][n][0]);
-    float ls = 0.f, as = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = (mx == -INFINITY) ? 0.f : fast_exp2(red[w][n][0] - mx);
-      ls += red[w][n][1] * sc;
-      as += red[w][n][2 + dim] * sc;
-    }
-    a.acc[(pbase + n) * D + dim] = as;
-    if (dim == 0) {
-      a.ml[(pbase + n) * 2] = mx;
-      a.ml[(pbase + n) * 2 + 1] = ls;
-    }
-  }
+  finish_split<D, NQ, kWaves>(a, red, g, split);
 }
 
 // ------------------------------------------------------------------------------- partial (MFMA)
@@ -628,14 +640,25 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   const int qc = lane % 16, rg = lane / 16;      // MFMA layout: query column, row group
   const int sub = lane % LPR, slot = lane / LPR; // P·V layout
 
+  // queries as the MFMA B operand: lane holds Q[query qc][32j + 8rg .. +7]
+  bf16x8 qb[KCH];
+  {
+    const bool have = qc < a.nq;
+    const int t = qc / a.G, hl = qc % a.G;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl) * D + 8 * rg;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (have) u = *reinterpret_cast<const uint4*>(qp + 32 * j);
+      qb[j] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
   int cnt;
   if constexpr (MODE == kListIntervals) {
-    if (wid == 0) {
-      int c = a.count[lrow];
-      c = max(0, min(c, (int)min<int64_t>(a.list_ld, kMaxIntervals - 2)));
-      build_segments(a, a.list + (int64_t)lrow * a.list_ld, c, seg_start, seg_pos, &seg_meta[0],
-                     &seg_meta[1]);
-    }
+    if (wid == 0)
+      build_segments(a, a.list + (int64_t)lrow * a.list_ld, a.count + lrow, seg_start, seg_pos,
+                     &seg_meta[0], &seg_meta[1]);
     __syncthreads();
     cnt = seg_meta[1];
     if (split == 0 && threadIdx.x == 0) a.ucount[g] = cnt;
@@ -682,20 +705,6 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
     }
   }
 
-  // queries as the MFMA B operand: lane holds Q[query qc][32j + 8rg .. +7]
-  bf16x8 qb[KCH];
-  {
-    const bool have = qc < a.nq;
-    const int t = qc / a.G, hl = qc % a.G;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl) * D + 8 * rg;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (have) u = *reinterpret_cast<const uint4*>(qp + 32 * j);
-      qb[j] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
   float m_q = -INFINITY, l_part = 0.f;  // query qc: running max (wave-uniform), own-row denominator
   float acc[NQ][8];
 #pragma unroll
@@ -825,97 +834,75 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
     red[wid][qc][1] = l_part;
   }
   __syncthreads();
-  const int64_t pbase = ((int64_t)g * a.smax + split) * NQ;
-  for (int e = threadIdx.x; e < NQ * D; e += kThreads) {
-    const int n = e / D, dim = e % D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w][n][0]);
-    float ls = 0.f, as = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = (mx == -INFINITY) ? 0.f : fast_exp2(red[w][n][0] - mx);
-      ls += red[w][n][1] * sc;
-      as += red[w][n][2 + dim] * sc;
-    }
-    a.acc[(pbase + n) * D + dim] = as;
-    if (dim == 0) {
-      a.ml[(pbase + n) * 2] = mx;
-      a.ml[(pbase + n) * 2 + 1] = ls;
-    }
-  }
+  finish_split<D, NQ, kWaves>(a, red, g, split);
 }
 
 // ------------------------------------------------------------------------------- combine
 
-// One wave per query vector: lanes fetch the splits' (m, l) in parallel, then each lane sums
-// its dims over the splits in split order (fixed order: deterministic).
+// One wave per query vector.  Every load (the group's row count, each split's (m, l) and its
+// partial output) is issued up front for up to kCombineMax splits, so the kernel waits on memory
+// once; the splits are then merged in split order (deterministic).
+constexpr int kCombineMax = 16;
+
 template <int D>
 __global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a, int nq_pad, float* out,
                                                              float* lse) {
-  __shared__ float wsc[kWave];
   const int g = blockIdx.x / a.nq;
   const int n = blockIdx.x % a.nq;
   const int b = g / a.Hkv, kvh = g % a.Hkv;
   const int lane = lane_id();
+  constexpr int PER = D / kWave;
+  const int64_t pbase = (int64_t)g * a.smax * nq_pad + n;
   int cnt;
-  if (a.list_mode == kListIntervals) {
+  if (a.list_mode == kListIntervals || a.ucount_valid) {
     cnt = a.ucount[g];
   } else {
     const int lrow = a.lrow_is_batch ? b : g;
     cnt = max(0, min(a.count[lrow], a.count_clamp));
   }
-  const int S = cnt > 0 ? (cnt + a.R - 1) / a.R : 0;
-  const int64_t pbase = (int64_t)g * a.smax * nq_pad + n;
-  constexpr int PER = D / kWave;
-  float o[PER];
+  float o[PER], L = 0.f, mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  float mx = -INFINITY;
-  for (int s0 = lane; s0 < S; s0 += kWave) mx = fmaxf(mx, a.ml[(pbase + (int64_t)s0 * nq_pad) * 2]);
+  for (int s0 = 0; s0 < a.smax; s0 += kCombineMax) {
+    // speculative loads of every split slot of the plan (in bounds); slots past the row count
+    // are masked out afterwards
+    float ms[kCombineMax], ls[kCombineMax], ac[kCombineMax][PER];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-  float L = 0.f;
-  for (int c0 = 0; c0 < S; c0 += kWave) {
-    const int s = c0 + lane;
-    float w = 0.f;
-    if (s < S && mx != -INFINITY) {
+    for (int j = 0; j < kCombineMax; ++j) {
+      const int s = min(s0 + j, a.smax - 1);
       const int64_t pi = pbase + (int64_t)s * nq_pad;
-      w = fast_exp2(a.ml[pi * 2] - mx);
-      L += a.ml[pi * 2 + 1] * w;
+      ms[j] = a.ml[pi * 2];
+      ls[j] = a.ml[pi * 2 + 1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ac[j][i] = a.acc[pi * D + lane + i * kWave];
     }
-    wsc[lane] = w;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    const int cs = min(kWave, S - c0);
-    int j = 0;
-    for (; j + 4 <= cs; j += 4) {
-      float v[4][PER];
+    const int S = cnt > 0 ? (cnt + a.R - 1) / a.R : 0;
+    float cmx = mx;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+    for (int j = 0; j < kCombineMax; ++j)
+      if (s0 + j < S) cmx = fmaxf(cmx, ms[j]);
+    const float rs = (cmx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mx - cmx);
+    L *= rs;
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-          v[jj][i] = a.acc[(pbase + (int64_t)(c0 + j + jj) * nq_pad) * D + lane + i * kWave];
+    for (int i = 0; i < PER; ++i) o[i] *= rs;
+    mx = cmx;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+    for (int j = 0; j < kCombineMax; ++j) {
+      if (s0 + j < S && mx != -INFINITY) {
+        const float w = __builtin_amdgcn_exp2f(ms[j] - mx);
+        L += ls[j] * w;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) o[i] += v[jj][i] * wsc[j + jj];
+        for (int i = 0; i < PER; ++i) o[i] += ac[j][i] * w;
+      }
     }
-    for (; j < cs; ++j)
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        o[i] += a.acc[(pbase + (int64_t)(c0 + j) * nq_pad) * D + lane + i * kWave] * wsc[j];
-    __builtin_amdgcn_wave_barrier();
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, kWave);
   const int t = n / a.G, hl = n % a.G;
   const int64_t qrow = (int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl;
   const bool empty = !(L > 0.f);
   const float inv = empty ? 0.f : 1.0f / L;
 #pragma unroll
   for (int i = 0; i < PER; ++i) out[qrow * D + lane + i * kWave] = o[i] * inv;
-  if (lse && lane == 0) lse[qrow] = empty ? -INFINITY : (mx + log2f(L)) * kLn2;
+  if (lse && lane == 0) lse[qrow] = empty ? -INFINITY : (mx + __log2f(L)) * kLn2;
 }
 
 #ifndef SPK_ATTN_UNROLL_SMALL
@@ -1182,6 +1169,7 @@ extern "C" SPK_API spk_status sparse_decode_attn(
     a.count_clamp = p.ubound;
     a.lrow_is_batch = 0;
     a.mask = as.umask;
+    a.ucount_valid = 1;
   } else if (p.intervals) {
     a.list_mode = kListIntervals;
     a.list = sel_idx;

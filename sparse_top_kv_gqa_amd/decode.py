@@ -43,7 +43,7 @@ class BlockSparseDecode:
         self.lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
         ws = attn_workspace_size("per_kv_head", B, 1, Hq, Hkv, d, n_tokens, self.idx.shape[-1],
                                  block_size, n_sink, n_recent)
-        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
 
     def pool(self, pred: torch.Tensor):
         """Mean-pool every complete block of the keys into ``kpool`` (once per cache; the
@@ -90,7 +90,7 @@ class TokenSparseDecode:
         self.out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
         ws = attn_workspace_size(self.scope, B, T, Hq, Hkv, d, n_tokens, kk)
-        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
 
     def select(self, q: torch.Tensor):
         sparse_index_score(self.mode, q, self.index_keys, self.n_tokens, scores=self.scores)
@@ -135,7 +135,7 @@ class TieredDecode:
         self.out = torch.empty((self.L, B, 1, Hq, d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.L, B, 1, Hq), dtype=torch.float32, device=dev)
         ws = attn_workspace_size("per_seq", B, 1, Hq, Hkv, d, n_cap, n_cap)
-        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
 
     def step(self, qs: Sequence[torch.Tensor], n_tokens: int, dense: bool = False):
         """One decode step at ``n_tokens`` cached tokens.  qs: per-layer Q ``[B, 1, Hq, d]``.
