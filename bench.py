@@ -317,7 +317,8 @@ def bench_token(args, which):
     torch.cuda.synchronize()
     att_ms = event_time_ms(lambda i: dec.attend(qs[0]), 10, stream)
     topk_ms = event_time_ms(lambda i: spk.topk_select(dec.scores, dec.topk, idx=dec.idx,
-                                                      count=dec.count, stream=stream), 10, stream)
+                                                      count=dec.count, ws=dec.topk_ws,
+                                                      stream=stream), 10, stream)
     bytes_avg = index_bytes + sum(sel_bytes) / P
     cfg = {"workload": w.name, "batch": w.B, "query_tokens": w.T, "q_heads": w.Hq,
            "kv_heads": w.Hkv, "head_dim": w.d, "context": w.N, "topk": w.k,

@@ -149,9 +149,16 @@ def sparse_index_score(mode, q: torch.Tensor, keys: torch.Tensor, n_tokens: int,
 
 # ----------------------------------------------------------------------------- top-k
 
+def topk_workspace_size(rows: int, n: int, k: int) -> int:
+    out = SZ(0)
+    _check(lib().topk_select_workspace_size(rows, n, k, ctypes.byref(out)),
+           "topk_select_workspace_size")
+    return out.value
+
+
 def topk_select(scores: torch.Tensor, k: int, n: Optional[int] = None,
                 idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
-                stream=None):
+                ws: Optional[torch.Tensor] = None, stream=None):
     """Exact top-k of each row of ``scores`` (any leading shape, last dim contiguous).
     Returns (idx int32 [..., min(k, n)] ascending, count int32 [...])."""
     if scores.stride(-1) != 1:
@@ -166,8 +173,11 @@ def topk_select(scores: torch.Tensor, k: int, n: Optional[int] = None,
     if count is None:
         count = torch.empty(lead, dtype=torch.int32, device=scores.device)
     i2 = idx.reshape(rows, idx.shape[-1])
+    wsz = topk_workspace_size(rows, n, k)
+    if wsz and (ws is None or ws.numel() < wsz):
+        ws = torch.empty(wsz, dtype=torch.uint8, device=scores.device)
     st = lib().topk_select(_ptr(s2), s2.stride(0), rows, n, k, _ptr(i2), i2.stride(0), _ptr(count),
-                           None, 0, _stream(stream))
+                           _ptr(ws) if wsz else None, wsz, _stream(stream))
     _check(st, "topk_select")
     return idx, count
 

@@ -36,7 +36,8 @@ constexpr int kUnroll = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSets = 32;
-constexpr size_t kAsmLdsMax = 60 * 1024;  // larger bitmaps live in the workspace
+constexpr int kAsmThreads = 1024;
+constexpr int kAsmLdsWords = 32768;  // 128 KB of LDS bitmaps; larger ones live in the workspace
 constexpr int kMaxIntervals = 64;   // selection entries + 2 forced ranges, one per lane
 constexpr int kMaxRows = 2048;      // rows per workgroup (LDS row table)
 constexpr int kDead = INT32_MIN;    // row-table entry of a row that is not read
@@ -81,7 +82,7 @@ Plan make_plan(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_
   p.R = (int)R;
   p.smax = p.ubound > 0 ? (int)ceil_div(p.ubound, p.R) : 1;
   p.words = (int)ceil_div(n_tokens > 0 ? n_tokens : 1, 32);
-  p.bm_lds = (size_t)p.sets * p.words * 4 <= kAsmLdsMax;
+  p.bm_lds = (int64_t)p.sets * p.words <= kAsmLdsWords;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -113,14 +114,14 @@ struct AsmArgs {
   int32_t* ucount;
 };
 
-__global__ __launch_bounds__(kThreads) void assemble_kernel(AsmArgs a) {
-  extern __shared__ uint32_t bm_lds[];
-  __shared__ int scratch[kWaves + 1];
+__global__ __launch_bounds__(kAsmThreads) void assemble_kernel(AsmArgs a) {
+  __shared__ uint32_t bm_lds[kAsmLdsWords];
+  __shared__ int scratch[kAsmThreads / kWave + 1];
   const int g = blockIdx.x;
   const int b = g / a.Hkv, kvh = g % a.Hkv;
   const int W = a.words;
   uint32_t* bm = a.bm_global ? a.bm_global + (int64_t)g * a.sets * W : bm_lds;
-  for (int i = threadIdx.x; i < a.sets * W; i += kThreads) bm[i] = 0u;
+  for (int i = threadIdx.x; i < a.sets * W; i += kAsmThreads) bm[i] = 0u;
   __syncthreads();
   const int n = a.n_tokens;
   for (int r = 0; r < a.sets; ++r) {
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void assemble_kernel(AsmArgs a) {
     if (cnt > a.sel_ld) cnt = (int)a.sel_ld;
     const int32_t* lst = a.sel_idx + row * a.sel_ld;
     const int64_t total = (int64_t)(cnt > 0 ? cnt : 0) * a.gran;
-    for (int64_t e = threadIdx.x; e < total; e += kThreads) {
+    for (int64_t e = threadIdx.x; e < total; e += kAsmThreads) {
       const int64_t tok = (int64_t)lst[e / a.gran] * a.gran + e % a.gran;
       if (tok >= 0 && tok < n) atomicOr(&bm[r * W + (int)(tok >> 5)], 1u << (tok & 31));
     }
@@ -140,12 +141,12 @@ __global__ __launch_bounds__(kThreads) void assemble_kernel(AsmArgs a) {
   // forced rows belong to every list
   const int s_end = min(a.n_sink, n);
   const int r_beg = max(0, n - a.n_recent);
-  for (int tok = threadIdx.x; tok < s_end + (n - r_beg); tok += kThreads) {
+  for (int tok = threadIdx.x; tok < s_end + (n - r_beg); tok += kAsmThreads) {
     const int t = tok < s_end ? tok : r_beg + (tok - s_end);
     for (int r = 0; r < a.sets; ++r) atomicOr(&bm[r * W + (t >> 5)], 1u << (t & 31));
   }
   __syncthreads();
-  const int wpt = (W + kThreads - 1) / kThreads;
+  const int wpt = (W + kAsmThreads - 1) / kAsmThreads;
   const int w0 = threadIdx.x * wpt;
   const int w1 = min(w0 + wpt, W);
   int local = 0;
@@ -1159,8 +1160,7 @@ extern "C" SPK_API spk_status sparse_decode_attn(
     as.ulist = reinterpret_cast<int32_t*>(w + p.off_list);
     as.umask = p.mask ? reinterpret_cast<uint32_t*>(w + p.off_mask) : nullptr;
     as.ucount = a.ucount;
-    const size_t lds = p.bm_lds ? (size_t)p.sets * p.words * 4 : 0;
-    hipLaunchKernelGGL(assemble_kernel, dim3(p.groups), dim3(kThreads), lds, st, as);
+    hipLaunchKernelGGL(assemble_kernel, dim3(p.groups), dim3(kAsmThreads), 0, st, as);
     spk_status e = check_launch("sparse_decode_attn/assemble");
     if (e != SPK_OK) return e;
     a.list = as.ulist;

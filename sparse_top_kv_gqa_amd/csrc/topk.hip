@@ -9,8 +9,9 @@
 //  * n <= 16384: 256 threads hold the row in registers (up to 64 keys each).  The k-th largest
 //    key is found bit by bit from the top: a candidate threshold is kept when at least k keys
 //    reach it, the count coming from wave ballots (scalar popcounts) summed across the 4 waves.
-//  * larger n: a radix select (4 passes of 8-bit digits, per-wave LDS histograms) over keys
-//    re-read from the scores each pass.
+//  * larger n: a 12-bit histogram finds the bin of the k-th key, that bin's keys are gathered
+//    into LDS and bit-searched for the exact threshold (a full radix select when ties overflow
+//    the store), and each wave compacts its own contiguous segment in index order.
 // Both finish with one pass in index order that keeps every key above the threshold and the
 // first `need` keys equal to it, compacting indices with ballot prefix counts, so the output is
 // ascending and ties resolve to the lowest indices.
@@ -22,7 +23,6 @@ namespace {
 constexpr int kSmallThreads = 256;
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr int kSmallMax = 64 * kSmallThreads;  // 16384
-constexpr int kRadixThreads = 1024;
 
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
@@ -151,67 +151,293 @@ __global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
   }
 }
 
-template <int ITEMS>
-__global__ __launch_bounds__(kRadixThreads) void topk_radix_kernel(
-    const float* __restrict__ scores, int64_t s_ld, int n, int k, int32_t* __restrict__ idx,
-    int64_t idx_ld, int32_t* __restrict__ count) {
-  __shared__ uint32_t hist[kRadixThreads / kWave * 256];
-  __shared__ int sh[2];
-  __shared__ int scratch[kRadixThreads / kWave + 1];
+// ---------------------------------------------------------------- wide rows (n > 16384)
+//
+// Two launches.  (1) topk_hist_kernel: the row is cut into C chunks, one workgroup each, and
+// every chunk's histogram of the top 12 key bits goes to the workspace.  (2) topk_final_kernel,
+// one 1024-thread workgroup per row: sums the C histograms and finds the bin b* holding the k-th
+// largest key; one read of the row puts, per wave and in index order, the keys above bin b*
+// (all kept) and the keys of bin b* (candidates) into LDS lists; a bit search over the low 20
+// bits of the candidates finds the exact threshold; every wave then writes its kept entries
+// at offsets from prefix counts over the earlier waves — ascending, ties to the lowest index.
+// When bin b* or a wave's list overflows its LDS store (heavy ties, very large k) the row falls
+// back to a full radix select and a streaming compaction.
+constexpr int kLargeThreads = 1024;
+constexpr int kLargeWaves = kLargeThreads / kWave;
+constexpr int kBins = 4096;
+constexpr int kBinShift = 20;
+constexpr int kHistThreads = 256;
+constexpr int kListPerWave = 512;                     // LDS list entries per wave
+constexpr int kCandMax = kLargeWaves * kListPerWave;  // candidates the LDS lists can hold
+
+int hist_chunks(int rows) {
+  const int want = (4 * num_cus() + rows - 1) / (rows > 0 ? rows : 1);
+  return want < 1 ? 1 : (want > 32 ? 32 : want);
+}
+
+__device__ __forceinline__ uint4 keys4_at(const float* x, int i, int n, bool aligned) {
+  uint4 k;
+  if (aligned && i + 3 < n) {
+    const float4 v = *reinterpret_cast<const float4*>(x + i);
+    k = make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
+  } else {
+    k.x = i < n ? order_key(x[i]) : 0u;
+    k.y = i + 1 < n ? order_key(x[i + 1]) : 0u;
+    k.z = i + 2 < n ? order_key(x[i + 2]) : 0u;
+    k.w = i + 3 < n ? order_key(x[i + 3]) : 0u;
+  }
+  return k;
+}
+
+__global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(const float* __restrict__ scores,
+                                                                 int64_t s_ld, int n, int k,
+                                                                 int C, uint32_t* __restrict__ ws) {
+  __shared__ uint32_t hist[kBins];
+  const int row = blockIdx.y, c = blockIdx.x;
+  const int kk = min(k, n);
+  uint32_t* out = ws + ((int64_t)row * C + c) * kBins;
+  if (kk <= 0 || kk == n) return;  // the final kernel needs no histogram then
+  const float* x = scores + (int64_t)row * s_ld;
+  const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  const int chunk = ((n + C - 1) / C + 1023) / 1024 * 1024;
+  const int beg = min(n, c * chunk), end = min(n, beg + chunk);
+  for (int i = threadIdx.x; i < kBins; i += kHistThreads) hist[i] = 0u;
+  __syncthreads();
+  constexpr int UA = 4;
+  for (int i0 = beg + 4 * threadIdx.x; i0 < end; i0 += 4 * kHistThreads * UA) {
+    uint4 kq[UA];
+#pragma unroll
+    for (int u = 0; u < UA; ++u) kq[u] = keys4_at(x, i0 + u * 4 * kHistThreads, end, aligned);
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const int i = i0 + u * 4 * kHistThreads;
+      if (i < end) atomicAdd(&hist[kq[u].x >> kBinShift], 1u);
+      if (i + 1 < end) atomicAdd(&hist[kq[u].y >> kBinShift], 1u);
+      if (i + 2 < end) atomicAdd(&hist[kq[u].z >> kBinShift], 1u);
+      if (i + 3 < end) atomicAdd(&hist[kq[u].w >> kBinShift], 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += kHistThreads) out[i] = hist[i];
+}
+
+// Sum over the wave of one int per lane (every lane gets the total).
+__device__ __forceinline__ int wave_sum(int x) {
+  x = (int)group_sum<16>((float)x);  // exact: partial sums stay far below 2^24
+  x += __shfl_xor(x, 16, kWave);
+  x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
+__global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
+    const float* __restrict__ scores, int64_t s_ld, int n, int k, int C,
+    const uint32_t* __restrict__ ws, int32_t* __restrict__ idx, int64_t idx_ld,
+    int32_t* __restrict__ count) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t lkey[kLargeWaves * kListPerWave];
+  __shared__ int32_t lidx[kLargeWaves * kListPerWave];
+  __shared__ int wave_n[kLargeWaves], wave_gt[kLargeWaves], wave_eq[kLargeWaves];
+  __shared__ int sh[8];
+  __shared__ int red[kLargeWaves + 1];
   const int row = blockIdx.x;
   const float* x = scores + (int64_t)row * s_ld;
   const int kk = min(k, n);
-  if (count && threadIdx.x == 0) count[row] = kk;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  if (count && tid == 0) count[row] = kk;
   if (kk <= 0) return;
   int32_t* out = idx + (int64_t)row * idx_ld;
   if (kk == n) {
-    for (int i = threadIdx.x; i < n; i += kRadixThreads) out[i] = i;
+    for (int i = tid; i < n; i += kLargeThreads) out[i] = i;
     return;
   }
-  uint32_t reg[ITEMS > 0 ? ITEMS : 1];
-  if constexpr (ITEMS > 0) {
-#pragma unroll
-    for (int c = 0; c < ITEMS; ++c) {
-      const int i = c * kRadixThreads + threadIdx.x;
-      reg[c] = i < n ? order_key(x[i]) : 0u;
+  const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  // wave w's segment of the row: [w*seg, min(n, (w+1)*seg)), seg a multiple of 256
+  const int seg = ((n + kLargeWaves - 1) / kLargeWaves + 255) / 256 * 256;
+  const int sbeg = min(n, wid * seg), send = min(n, sbeg + seg);
+
+  // ---- sum the chunk histograms, find bin b*
+  const uint32_t* hrow = ws + (int64_t)row * C * kBins;
+  for (int i = tid; i < kBins; i += kLargeThreads) {
+    uint32_t t = 0;
+    for (int c = 0; c < C; ++c) t += hrow[(int64_t)c * kBins + i];
+    hist[i] = t;
+  }
+  if (tid == 0) sh[3] = 0;  // overflow flag
+  __syncthreads();
+  {
+    const int top = kBins - 1 - 4 * tid;
+    const int c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
+    const int sum = c0 + c1 + c2 + c3;
+    int total;
+    const int excl = block_excl_scan(sum, red, &total);
+    if (excl < kk && kk <= excl + sum) {
+      int acc = excl;
+      if (acc + c0 >= kk) { sh[0] = top; sh[1] = acc; }
+      else if ((acc += c0) + c1 >= kk) { sh[0] = top - 1; sh[1] = acc; }
+      else if ((acc += c1) + c2 >= kk) { sh[0] = top - 2; sh[1] = acc; }
+      else { acc += c2; sh[0] = top - 3; sh[1] = acc; }
     }
   }
-  auto for_each = [&](auto&& visit) {
-    if constexpr (ITEMS > 0) {
+  __syncthreads();
+  const uint32_t bstar = (uint32_t)sh[0];
+  const int kin = kk - sh[1];  // rank of the threshold inside bin b*
+  bool overflow = (int)hist[bstar] > kCandMax;
+
+  // ---- gather: per wave, in index order, keys above b* (flag bit 31 of the index) and keys of b*
+  uint32_t* mykey = lkey + wid * kListPerWave;
+  int32_t* myidx = lidx + wid * kListPerWave;
+  int nl = 0;
+  if (!overflow) {
+    constexpr int UB = 4;
+    for (int c0 = sbeg; c0 < send; c0 += 256 * UB) {
+      uint4 kq[UB];
 #pragma unroll
-      for (int c = 0; c < ITEMS; ++c)
-        if (c * kRadixThreads + (int)threadIdx.x < n) visit(reg[c]);
-    } else {
-      for (int i = threadIdx.x; i < n; i += kRadixThreads) visit(order_key(x[i]));
+      for (int u = 0; u < UB; ++u) kq[u] = keys4_at(x, c0 + 256 * u + 4 * lane, send, aligned);
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int i = c0 + 256 * u + 4 * lane;
+        const uint32_t kv[4] = {kq[u].x, kq[u].y, kq[u].z, kq[u].w};
+        bool take[4];
+        int tk = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          take[j] = i + j < send && (kv[j] >> kBinShift) >= bstar;
+          tk += take[j];
+        }
+        // this lane's entries go after those of lower lanes (index order: lane, then j)
+        uint64_t any = __ballot(tk > 0);
+        if (any) {
+          int before = 0;
+          // prefix of tk over lower lanes
+          int incl = tk;
+#pragma unroll
+          for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += y;
+          }
+          before = incl - tk;
+          const int tot = __shfl(incl, kWave - 1, kWave);
+          if (nl + tot <= kListPerWave) {
+            int p = nl + before;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (take[j]) {
+                mykey[p] = kv[j];
+                myidx[p] = i + j;
+                ++p;
+              }
+            }
+          } else {
+            overflow = true;
+          }
+          nl += tot;
+        }
+      }
     }
-  };
+    if (lane == 0) {
+      wave_n[wid] = nl;
+      if (overflow) sh[3] = 1;
+    }
+  }
+  __syncthreads();
+  overflow = overflow || sh[3] != 0;
+
   uint32_t thr;
   int need;
-  radix_select<kRadixThreads>(for_each, kk, hist, sh, &thr, &need);
-
-  // Compaction in index order: keep key > thr, and the first `need` keys == thr.
-  int run_gt = 0, run_eq = 0;
-  const int chunks = (n + kRadixThreads - 1) / kRadixThreads;
-  for (int c = 0; c < chunks; ++c) {
-    const int i = c * kRadixThreads + threadIdx.x;
-    uint32_t key = 0;
-    bool valid = i < n;
-    if constexpr (ITEMS > 0) {
+  if (!overflow) {
+    // ---- threshold: bit search over the low 20 bits; each wave counts its own candidates
+    thr = bstar << kBinShift;
+    int parity = 0;
+    __shared__ int cnt2[2][kLargeWaves];
+    for (int bit = kBinShift - 1; bit >= 0; --bit) {
+      const uint32_t cnd = thr | (1u << bit);
+      int c = 0;
+      for (int j = lane; j < nl; j += kWave) {
+        const uint32_t kv = mykey[j];
+        c += ((kv >> kBinShift) == bstar) && kv >= cnd;
+      }
+      c = wave_sum(c);
+      if (lane == 0) cnt2[parity][wid] = c;
+      __syncthreads();
+      int tot = 0;
 #pragma unroll
-      for (int cc = 0; cc < ITEMS; ++cc)
-        if (cc == c) key = reg[cc];
-    } else {
-      if (valid) key = order_key(x[i]);
+      for (int w = 0; w < kLargeWaves; ++w) tot += cnt2[parity][w];
+      if (tot >= kin) thr = cnd;
+      parity ^= 1;
     }
-    const int gt = valid && key > thr;
-    const int eq = valid && key == thr;
-    int total;
-    const int pre = block_excl_scan(gt | (eq << 16), scratch, &total);
-    const int pre_gt = pre & 0xFFFF, pre_eq = pre >> 16;
-    if (gt || (eq && run_eq + pre_eq < need))
-      out[run_gt + pre_gt + min(run_eq + pre_eq, need)] = i;
-    run_gt += total & 0xFFFF;
-    run_eq += total >> 16;
+    // per-wave kept counts: every entry above the threshold, and ties in index order up to need
+    int g = 0, e = 0;
+    for (int j = lane; j < nl; j += kWave) {
+      const uint32_t kv = mykey[j];
+      g += kv > thr;
+      e += kv == thr;
+    }
+    g = wave_sum(g);
+    e = wave_sum(e);
+    if (lane == 0) {
+      wave_gt[wid] = g;
+      wave_eq[wid] = e;
+    }
+    __syncthreads();
+    int gt_all = 0, run_gt = 0, run_eq = 0;
+#pragma unroll
+    for (int w = 0; w < kLargeWaves; ++w) {
+      gt_all += wave_gt[w];
+      if (w < wid) {
+        run_gt += wave_gt[w];
+        run_eq += wave_eq[w];
+      }
+    }
+    need = kk - gt_all;
+    // ---- write the kept entries of this wave's list, in index order
+    for (int j0 = 0; j0 < nl; j0 += kWave) {
+      const int j = j0 + lane;
+      const uint32_t kv = j < nl ? mykey[j] : 0u;
+      const bool gt = j < nl && kv > thr;
+      const bool eq = j < nl && kv == thr;
+      const uint64_t bg = __ballot(gt), be = __ballot(eq);
+      const int eq_rank = run_eq + __popcll(be & lt);
+      if (gt || (eq && eq_rank < need)) out[run_gt + __popcll(bg & lt) + min(eq_rank, need)] = myidx[j];
+      run_gt += __popcll(bg);
+      run_eq += __popcll(be);
+    }
+    return;
+  }
+
+  // ---- fallback: full radix select over the row and a streaming compaction
+  {
+    auto for_each = [&](auto&& visit) {
+      for (int i = tid; i < n; i += kLargeThreads) visit(order_key(x[i]));
+    };
+    radix_select<kLargeThreads>(for_each, kk, hist, sh, &thr, &need);
+    int g = 0, e = 0;
+    for (int c = sbeg; c < send; c += 64) {
+      const int i = c + lane;
+      const uint32_t kv = i < send ? order_key(x[i]) : 0u;
+      g += __popcll(__ballot(i < send && kv > thr));
+      e += __popcll(__ballot(i < send && kv == thr));
+    }
+    if (lane == 0) {
+      wave_gt[wid] = g;
+      wave_eq[wid] = e;
+    }
+    __syncthreads();
+    int run_gt = 0, run_eq = 0;
+    for (int w = 0; w < wid; ++w) {
+      run_gt += wave_gt[w];
+      run_eq += wave_eq[w];
+    }
+    for (int c = sbeg; c < send; c += 64) {
+      const int i = c + lane;
+      const uint32_t kv = i < send ? order_key(x[i]) : 0u;
+      const bool gt = i < send && kv > thr, eq = i < send && kv == thr;
+      const uint64_t bg = __ballot(gt), be = __ballot(eq);
+      const int eq_rank = run_eq + __popcll(be & lt);
+      if (gt || (eq && eq_rank < need)) out[run_gt + __popcll(bg & lt) + min(eq_rank, need)] = i;
+      run_gt += __popcll(bg);
+      run_eq += __popcll(be);
+    }
   }
 }
 
@@ -223,7 +449,7 @@ extern "C" SPK_API spk_status topk_select_workspace_size(int rows, int n, int k,
   SPK_REQUIRE(bytes, SPK_EINVAL, "topk_select_workspace_size: null bytes");
   SPK_REQUIRE(rows >= 0 && n >= 0, SPK_EINVAL, "topk_select_workspace_size: negative size");
   (void)k;
-  *bytes = 0;
+  *bytes = n > kSmallMax ? (size_t)rows * hist_chunks(rows) * kBins * sizeof(uint32_t) : 0;
   clear_error();
   return SPK_OK;
 }
@@ -232,8 +458,6 @@ extern "C" SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int
                                           int32_t* idx, int64_t idx_ld, int32_t* count, void* ws,
                                           size_t ws_bytes, void* stream) {
   using namespace spk;
-  (void)ws;
-  (void)ws_bytes;
   SPK_REQUIRE(rows >= 0 && n >= 0, SPK_EINVAL, "topk_select: rows=%d n=%d", rows, n);
   SPK_REQUIRE(k >= 0, SPK_EINVAL, "topk_select: k=%d < 0", k);
   SPK_REQUIRE(s_ld >= n, SPK_EINVAL, "topk_select: s_ld %lld < n %d", (long long)s_ld, n);
@@ -242,6 +466,9 @@ extern "C" SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int
               (long long)idx_ld, kk);
   SPK_REQUIRE(rows == 0 || ((idx || kk == 0) && (scores || n == 0)), SPK_EINVAL,
               "topk_select: null scores or idx");
+  const size_t need_ws = n > kSmallMax ? (size_t)rows * hist_chunks(rows) * kBins * sizeof(uint32_t) : 0;
+  SPK_REQUIRE(ws_bytes >= need_ws && (need_ws == 0 || ws), SPK_EWORKSPACE,
+              "topk_select: workspace %zu bytes < %zu needed", ws_bytes, need_ws);
   clear_error();
   if (rows == 0) return SPK_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -271,8 +498,14 @@ extern "C" SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int
     else SPK_SMALL(64);
 #undef SPK_SMALL
   } else {
-    hipLaunchKernelGGL(topk_radix_kernel<0>, dim3(rows), dim3(kRadixThreads), 0, st, scores, s_ld,
-                       n, k, idx, idx_ld, count);
+    const int C = hist_chunks(rows);
+    uint32_t* h = reinterpret_cast<uint32_t*>(ws);
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(C, rows), dim3(kHistThreads), 0, st, scores, s_ld, n, k,
+                       C, h);
+    spk_status e = check_launch("topk_select/histogram");
+    if (e != SPK_OK) return e;
+    hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kLargeThreads), 0, st, scores, s_ld, n, k,
+                       C, h, idx, idx_ld, count);
   }
   return check_launch("topk_select");
 }

@@ -17,8 +17,8 @@ from typing import List, Optional, Sequence
 
 import torch
 
-from . import (fetch_list_bound, attn_workspace_size, sparse_decode_attn, sparse_index_score,
-               topk_select, importance_accumulate, tier_classify)
+from . import (attn_workspace_size, sparse_decode_attn, sparse_index_score, topk_select,
+               topk_workspace_size, importance_accumulate, tier_classify)
 
 
 class BlockSparseDecode:
@@ -91,10 +91,12 @@ class TokenSparseDecode:
         self.lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
         ws = attn_workspace_size(self.scope, B, T, Hq, Hkv, d, n_tokens, kk)
         self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
+        tws = topk_workspace_size(B * T * Hs, n_tokens, topk)
+        self.topk_ws = torch.empty(max(tws, 1), dtype=torch.uint8, device=dev)
 
     def select(self, q: torch.Tensor):
         sparse_index_score(self.mode, q, self.index_keys, self.n_tokens, scores=self.scores)
-        topk_select(self.scores, self.topk, idx=self.idx, count=self.count)
+        topk_select(self.scores, self.topk, idx=self.idx, count=self.count, ws=self.topk_ws)
 
     def attend(self, q: torch.Tensor):
         sparse_decode_attn(q, self.k, self.v, self.idx, self.count, self.scope, self.n_tokens,

@@ -68,6 +68,9 @@ def test_topk_validation():
     assert L.topk_select(None, 100, 4, 100, 10, Bp, 10, None, None, 0, None) == 1
     sz = ctypes.c_size_t(123)
     assert L.topk_select_workspace_size(4, 100, 10, ctypes.byref(sz)) == 0 and sz.value == 0
+    # wide rows keep per-chunk histograms in the workspace
+    assert L.topk_select_workspace_size(128, 131072, 2622, ctypes.byref(sz)) == 0 and sz.value > 0
+    assert L.topk_select(A, 131072, 128, 131072, 2622, Bp, 2622, None, None, 0, None) == 3
 
 
 def _attn(**kw):
