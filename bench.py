@@ -36,6 +36,7 @@ import time
 import torch
 
 HBM_PEAK_GBS = 8000.0
+PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 METRIC = "sparse decode attn: selected-KV GB/s (% of HBM peak), decode steps/s"
 ROW_BYTES = 2 * 128 * 2  # one token's K and V for one KV head, bf16, d = 128
 
@@ -50,6 +51,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=8, help="block: layer caches to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MiB four times "
+                         "(the reference point for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -93,6 +97,75 @@ def event_time_ms(fn, reps, stream, per_call=None):
     return t[len(t) // 2]
 
 
+_HIP = None
+
+
+def _hip():
+    """The HIP runtime torch has loaded (ctypes), for events created with explicit flags."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = h
+    return _HIP
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def gather_kernel_ms(call, reps, stream):
+    """Median duration of the attention's gather kernel (the launch that reads the selected
+    K/V rows): the library records a pair of HIP events around that launch, on `stream`.  The
+    events skip the system-scope cache fence a default event record performs, which would
+    otherwise add about 2 us to a kernel of about 20 us."""
+    import ctypes
+    import sparse_top_kv_gqa_amd as spk
+    hip = _hip()
+    pairs = []
+    for _ in range(reps):
+        a, b = ctypes.c_void_p(), ctypes.c_void_p()
+        if (hip.hipEventCreateWithFlags(ctypes.byref(a), HIP_EVENT_DISABLE_SYSTEM_FENCE) or
+                hip.hipEventCreateWithFlags(ctypes.byref(b), HIP_EVENT_DISABLE_SYSTEM_FENCE)):
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        pairs.append((a, b))
+    L = spk.lib()
+    try:
+        with torch.cuda.stream(stream):
+            for i, (a, b) in enumerate(pairs):
+                if L.spk_set_attn_timing_events(a, b) != 0:
+                    raise RuntimeError(L.spk_last_error().decode())
+                call(i)
+    finally:
+        L.spk_set_attn_timing_events(None, None)
+    torch.cuda.synchronize()
+    t = []
+    for a, b in pairs:
+        f = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(f), a, b):
+            raise RuntimeError("hipEventElapsedTime failed")
+        t.append(f.value)
+        hip.hipEventDestroy(a)
+        hip.hipEventDestroy(b)
+    t.sort()
+    return t[len(t) // 2]
+
+
+def copy_calibration(mib):
+    """A plain copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counter readings."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {mib} MiB four times (calibration)")
+    del src, dst
+
+
 def timed_loop(run_step, K, W, stream):
     """W untimed steps, then exactly K steps bracketed by synchronisations and events."""
     with torch.cuda.stream(stream):
@@ -122,10 +195,11 @@ def base_result(w, K, W, ms_step, step_bytes, config):
     }
 
 
-def roofline(kernel, bytes_per_launch, ms, traffic=None, note=None):
+def roofline(kernel, bytes_per_launch, ms, traffic=None, note=None, bound="hbm",
+             peak=HBM_PEAK_GBS):
     gbs = bytes_per_launch / (ms * 1e-3) / 1e9
-    r = {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+    r = {"bound": bound, "kernel": kernel, "achieved": round(gbs, 1), "peak": peak,
+         "unit": "GB/s", "frac": round(gbs / peak, 4), "traffic": traffic,
          "avg_launch_us": round(ms * 1e3, 3), "algorithmic_bytes_per_launch": int(bytes_per_launch)}
     if note:
         r["note"] = note
@@ -203,14 +277,17 @@ def bench_block(args):
                            gran=d.bs, n_sink=d.n_sink, n_recent=d.n_recent, sm_scale=d.sm_scale,
                            out=d.out, lse=d.lse, ws=d.ws, stream=stream)
     att_ms = event_time_ms(attn, 8 * L, stream)
+    gather_ms = gather_kernel_ms(attn, 8 * L, stream)
     att_bytes = sum(sel_bytes) / L
     bytes_avg = sum(step_bytes[i % L] for i in range(K)) / K
     res = base_result(w, K, Wm, ms_step, bytes_avg, {
         "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
         "context": w.N, "block_size": w.block_size, "top_blocks": w.k, "sinks": w.n_sink,
         "recent": w.n_recent, "layer_caches_rotated": L, "bytes_per_step": int(bytes_avg),
-        "selected_rows_per_step": int(att_bytes / ROW_BYTES), "wall_s_timed": round(wall, 4)})
-    res["roofline"] = roofline("sparse_decode_attn (partial + combine launches)", att_bytes, att_ms)
+        "selected_rows_per_step": int(att_bytes / ROW_BYTES), "wall_s_timed": round(wall, 4),
+        "attention_call_ms": round(att_ms, 4)})
+    res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather)", att_bytes,
+                               gather_ms)
     ctx = dict(w=w, dec=decs[0], q=qs[0], pred=preds[0])
     return res, ctx
 
@@ -316,6 +393,7 @@ def bench_token(args, which):
     dec.select(qs[0])
     torch.cuda.synchronize()
     att_ms = event_time_ms(lambda i: dec.attend(qs[0]), 10, stream)
+    gather_ms = gather_kernel_ms(lambda i: dec.attend(qs[0]), 10, stream)
     topk_ms = event_time_ms(lambda i: spk.topk_select(dec.scores, dec.topk, idx=dec.idx,
                                                       count=dec.count, ws=dec.topk_ws,
                                                       stream=stream), 10, stream)
@@ -325,15 +403,23 @@ def bench_token(args, which):
            "bytes_per_step": int(bytes_avg), "index_bytes": index_bytes,
            "selected_rows_per_step": int(sum(union) / P), "wall_s_timed": round(wall, 4),
            "index_ms": round(idx_ms, 4), "topk_ms": round(topk_ms, 4),
-           "attention_ms": round(att_ms, 4),
-           "attention_selected_GBs": round(union[0] * ROW_BYTES / (att_ms * 1e-3) / 1e9, 1)}
+           "attention_ms": round(att_ms, 4), "attention_gather_kernel_ms": round(gather_ms, 4),
+           "attention_selected_GBs": round(union[0] * ROW_BYTES / (gather_ms * 1e-3) / 1e9, 1)}
+    res = base_result(w, K, Wm, ms_step, bytes_avg, cfg)
     if w.host_frac > 0:
+        # the gather kernel dominates; its host-resident rows cross PCIe inside it
+        hf = host_frac[0]
         cfg["host_fraction_of_selected_rows"] = round(sum(host_frac) / len(host_frac), 4)
         cfg["host_rows_resident"] = host_rows_total
-        hb = sum(host_frac) / len(host_frac) * union[0] * ROW_BYTES
-        cfg["pcie_GBs_in_attention"] = round(hb / (att_ms * 1e-3) / 1e9, 2)
-    res = base_result(w, K, Wm, ms_step, bytes_avg, cfg)
-    res["roofline"] = roofline(f"sparse_index_score ({mode})", index_bytes, idx_ms)
+        hb = hf * union[0] * ROW_BYTES
+        cfg["hbm_part_GBs_in_gather"] = round((1 - hf) * union[0] * ROW_BYTES /
+                                              (gather_ms * 1e-3) / 1e9, 1)
+        res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather), "
+                                   "host-resident rows", hb, gather_ms, bound="pcie",
+                                   peak=PCIE_PEAK_GBS)
+    else:
+        res["roofline"] = roofline(f"index_rows_kernel (sparse_index_score {mode})", index_bytes,
+                                   idx_ms)
     ctx = dict(w=w, k=k, v=v, q=qs[0], which=which)
     return res, ctx
 
@@ -420,6 +506,7 @@ def bench_tiers(args):
                                out=dec.out[0], lse=dec.lse[0], logits=dec.logits[0], ws=dec.ws,
                                stream=stream)
     att_ms = event_time_ms(attn, 10, stream)
+    gather_ms = gather_kernel_ms(attn, 10, stream)
     att_bytes = rows[n_steps - 1] * w.Hkv * ROW_BYTES
     s_copy = dec.s.clone()
     tb = torch.empty_like(dec.tier)
@@ -440,8 +527,8 @@ def bench_tiers(args):
         "episode_s": round(ms_total / 1e3, 4), "wall_s_timed": round(wall, 4),
         "attention_layer_ms_last_step": round(att_ms, 4), "tier_classify_ms": round(tier_ms, 4),
         "importance_ms": round(imp_ms, 4)})
-    res["roofline"] = roofline("sparse_decode_attn (one layer, partial + combine launches)",
-                               att_bytes, att_ms)
+    res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather, one layer at "
+                               f"{n_last} tokens)", att_bytes, gather_ms)
     ctx = dict(w=w, caches=caches, qs=qs, n_last=n_last)
     return res, ctx
 
@@ -487,6 +574,8 @@ def main():
         sys.exit(1)
     import sparse_top_kv_gqa_amd as spk
     spk.lib()
+    if args.calibrate_copy_mib > 0:
+        copy_calibration(args.calibrate_copy_mib)
     if args.workload == "block":
         res, ctx = bench_block(args)
         cpu = cpu_block

@@ -77,6 +77,17 @@ SPK_API const char* spk_last_error(void);
 SPK_API int spk_version(void);
 #define SPK_VERSION 1
 
+/* Measurement hook for the attention's gather kernel (the launch that reads the selected K/V
+ * rows).  `begin` and `end` are HIP events (hipEvent_t cast to void*, created and owned by the
+ * caller).  While both are non-null, every later sparse_decode_attn call records `begin` on its
+ * stream immediately before that launch and `end` immediately after it, so
+ * hipEventElapsedTime(begin, end) is the kernel's duration; the call's other launches (list
+ * assembly, split combine) fall outside the pair.  Pass two nulls to switch it off.
+ * Process-wide state: calls that overlap from several host threads while it is set race on the
+ * events.  Returns SPK_EINVAL if exactly one of the two is null; SPK_EHIP (from the attention
+ * call) if a record fails. */
+SPK_API spk_status spk_set_attn_timing_events(void* begin, void* end);
+
 /* ------------------------------------------------------------------------------------------
  * sparse_index_score — compact indexer scores, no softmax.
  *

@@ -31,7 +31,8 @@ SCOPES = {"per_seq": SEL_PER_SEQ, "per_kv_head": SEL_PER_KV_HEAD, "per_q_head": 
 
 EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_workspace_size",
            "topk_select", "sparse_decode_attn_workspace_size", "sparse_decode_attn",
-           "importance_accumulate", "tier_classify_workspace_size", "tier_classify")
+           "importance_accumulate", "tier_classify_workspace_size", "tier_classify",
+           "spk_set_attn_timing_events")
 
 
 class SpkError(RuntimeError):
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.tier_classify_workspace_size.argtypes = [I, I, ctypes.POINTER(SZ)]
     L.tier_classify.restype = I
     L.tier_classify.argtypes = [P, I64, I, I, I, I, I, I, P, I64, P, I64, P, P, I64, P, SZ, P]
+    L.spk_set_attn_timing_events.restype = I
+    L.spk_set_attn_timing_events.argtypes = [P, P]
     _lib = L
     return L
 
@@ -293,3 +296,17 @@ def tier_classify(s: torch.Tensor, n_tokens: int, n_sink: int, n_recent: int,
                              sel_idx.stride(0), None, 0, _stream(stream))
     _check(st, "tier_classify")
     return tier, sel_idx, sel_count
+
+
+def set_attn_timing_events(begin: Optional[torch.cuda.Event] = None,
+                           end: Optional[torch.cuda.Event] = None):
+    """Bracket the gather kernel of every following sparse_decode_attn call with two recorded
+    events (a measurement hook); call with no arguments to switch it off.  The events must have
+    been created with enable_timing=True and recorded once (torch creates them lazily)."""
+    if (begin is None) != (end is None):
+        raise ValueError("give both events or neither")
+    b = None if begin is None else ctypes.c_void_p(begin.cuda_event)
+    e = None if end is None else ctypes.c_void_p(end.cuda_event)
+    if begin is not None and (not b.value or not e.value):
+        raise ValueError("record the events once before handing them over")
+    _check(lib().spk_set_attn_timing_events(b, e), "spk_set_attn_timing_events")

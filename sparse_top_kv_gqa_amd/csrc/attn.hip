@@ -996,6 +996,20 @@ using spk::Plan;
 
 // A host pool must be page-locked, device-mapped host memory; the kernel reads it through the
 // device address HIP reports for it.  Pageable memory would fault, so it is refused here.
+// Events of spk_set_attn_timing_events (null: timing off).
+static hipEvent_t g_timing_begin = nullptr;
+static hipEvent_t g_timing_end = nullptr;
+
+extern "C" SPK_API spk_status spk_set_attn_timing_events(void* begin, void* end) {
+  using namespace spk;
+  clear_error();
+  SPK_REQUIRE((begin == nullptr) == (end == nullptr), SPK_EINVAL,
+              "spk_set_attn_timing_events: give both events or neither");
+  g_timing_begin = static_cast<hipEvent_t>(begin);
+  g_timing_end = static_cast<hipEvent_t>(end);
+  return SPK_OK;
+}
+
 static spk_status resolve_host_pool(const void* p, const void** dev, const char* name) {
   hipPointerAttribute_t at{};
   const hipError_t e = hipPointerGetAttributes(&at, p);
@@ -1186,6 +1200,9 @@ extern "C" SPK_API spk_status sparse_decode_attn(
   }
   dim3 grid(p.smax, p.groups);
   const bool mask = p.mask;
+  hipEvent_t ev_begin = g_timing_begin, ev_end = g_timing_end;
+  if (ev_begin && hipEventRecord(ev_begin, st) != hipSuccess)
+    return set_error(SPK_EHIP, "sparse_decode_attn: recording the timing event failed");
   if (d == 128) {
     if (kv_dtype == SPK_BF16) dispatch_nq<128, uint16_t>(p.nq_pad, mask, a.list_mode, grid, st, a);
     else dispatch_nq<128, float>(p.nq_pad, mask, a.list_mode, grid, st, a);
@@ -1195,6 +1212,8 @@ extern "C" SPK_API spk_status sparse_decode_attn(
   }
   spk_status e = check_launch("sparse_decode_attn/partial");
   if (e != SPK_OK) return e;
+  if (ev_end && hipEventRecord(ev_end, st) != hipSuccess)
+    return set_error(SPK_EHIP, "sparse_decode_attn: recording the timing event failed");
   if (d == 128)
     hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(p.groups * a.nq), dim3(kWave), 0, st, a,
                        p.nq_pad, out, lse);

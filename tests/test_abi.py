@@ -131,3 +131,10 @@ def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(spk, "LIB_PATH", "/nonexistent/libspk.so")
     with pytest.raises(RuntimeError, match="no fallback"):
         spk.lib()
+
+
+def test_timing_hook_validation():
+    L = spk.lib()
+    assert L.spk_set_attn_timing_events(ctypes.c_void_p(1), None) == 1
+    assert "both" in L.spk_last_error().decode()
+    assert L.spk_set_attn_timing_events(None, None) == 0

@@ -422,3 +422,124 @@ def test_empty_and_degenerate_selections():
     out0, lse0 = spk.sparse_decode_attn(q, k, v, sel, cnt, "per_kv_head", 0)
     torch.cuda.synchronize()
     assert torch.all(out0 == 0) and torch.all(torch.isneginf(lse0))
+
+
+# ------------------------------------------------------------------------------------ full sizes
+# The configurations bench.py times, checked on sampled (batch, kv-head) groups / sequences.
+
+def _free():
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_per_head_full_size_sampled():
+    w = W.PER_HEAD_2PCT
+    say("per-head-full", w.name)
+    q = W.queries(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    dec = TokenSparseDecode(k, v, w.N, w.Hq, 1, w.k, "token_per_head")
+    out, lse = dec.step(q)
+    torch.cuda.synchronize()
+    scale = oracle.softmax_scale(w.d)
+    G = w.G
+    for (b, h) in [(0, 0), (3, 6)]:
+        kh, vh = host(k[b, h]), host(v[b, h])
+        qg = host(q)[b, 0, h * G:(h + 1) * G]
+        ref = oracle.scores_token_per_head(qg, kh)
+        for j in range(G):
+            hq = h * G + j
+            gs = dec.scores[b, 0, hq].cpu().numpy()
+            check_rows(gs, ref[j], what="per-head scores")
+            sel = dec.idx[b, 0, hq].cpu().numpy()
+            assert sel.tolist() == oracle.topk(gs, w.k).tolist()
+            assert osteps.topk_band_ok(sel, ref[j], w.k, TOL)
+            o_ref, l_ref, _ = oracle.attend(qg[j:j + 1], kh[sel], vh[sel], scale)
+            check_rows(out[b, 0, hq].cpu().numpy(), o_ref[0], what="per-head attention")
+    del k, v, dec
+    _free()
+
+
+def test_spec_verify_full_size_sampled_with_host_rows():
+    w = W.SPEC_VERIFY
+    say("spec-verify-full", w.name)
+    q = W.queries(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    # as in the bench: a seeded 10% of every group's rows live in pinned host memory
+    n_host = int(round(w.host_frac * w.N))
+    loc = torch.arange(w.N, dtype=torch.int32, device=DEV).repeat(w.B, w.Hkv, 1)
+    kh_pool = torch.empty((w.B, w.Hkv, n_host, w.d), dtype=torch.bfloat16, pin_memory=True)
+    vh_pool = torch.empty_like(kh_pool).pin_memory()
+    k_att, v_att = k.clone(), v.clone()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            rows = W.host_rows(w, b, h, torch.arange(w.N)).to(DEV)
+            kh_pool[b, h].copy_(k[b, h, rows].cpu())
+            vh_pool[b, h].copy_(v[b, h, rows].cpu())
+            loc[b, h, rows] = ~torch.arange(rows.numel(), dtype=torch.int32, device=DEV)
+            k_att[b, h, rows] = float("nan")      # HBM copies of host rows are never read
+            v_att[b, h, rows] = float("nan")
+    dec = TokenSparseDecode(k_att, v_att, w.N, w.Hq, w.T, w.k, "token_group_mean", index_keys=k,
+                            k_host=kh_pool, v_host=vh_pool, loc=loc)
+    out, lse = dec.step(q)
+    out, lse = out.clone(), lse.clone()
+    # Proposition 1 at full size: the all-HBM run gives the same bits
+    ref_out, ref_lse = spk.sparse_decode_attn(q, k, v, dec.idx, dec.count, "per_kv_head", w.N)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+    scale = oracle.softmax_scale(w.d)
+    G = w.G
+    for (b, h) in [(0, 0), (15, 7)]:
+        kh, vh = host(k[b, h]), host(v[b, h])
+        qt = host(q)[b, :, h * G:(h + 1) * G]
+        for t in range(w.T):
+            gs = dec.scores[b, t, h].cpu().numpy()
+            ref = oracle.scores_token_group_mean(qt[t], kh)
+            check_rows(gs, ref, what="group-mean scores")
+            sel = dec.idx[b, t, h].cpu().numpy()
+            assert sel.tolist() == oracle.topk(gs, w.k).tolist()
+            assert osteps.topk_band_ok(sel, ref, w.k, TOL)
+            o_ref, _, _ = oracle.attend(qt[t], kh[sel], vh[sel], scale)
+            check_rows(out[b, t, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="verify attention")
+    del k, v, k_att, v_att, dec, kh_pool, vh_pool
+    _free()
+
+
+def test_tiered_full_size_sampled_steps():
+    w = W.REASONING_TIERS
+    say("tiered-full", w.name)
+    caches = [(W.kv_cache(w, "k", l, DEV, n_cap=w.N), W.kv_cache(w, "v", l, DEV, n_cap=w.N))
+              for l in range(w.layers)]
+    dec = TieredDecode(caches, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille)
+    scale = oracle.softmax_scale(w.d)
+    check_at = {0, 1, 2, w.steps - 1}
+    sample_b = [0, 21]
+    for t in range(w.steps):
+        n = w.n_start + w.grow_per_step * (t + 1)
+        qs = [W.queries(w, step=t, layer=l, device=DEV) for l in range(w.layers)]
+        if t in check_at:
+            s_in = dec.s.cpu().numpy().copy()
+            ev_in = dec.evicted.cpu().numpy().astype(bool)
+        out, lse = dec.step(qs, n, dense=(t == 0))
+        if t not in check_at:
+            continue
+        torch.cuda.synchronize()
+        say("tiered-full step", t, "n", n)
+        for b in sample_b:
+            qb = np.stack([host(qs[l])[b, 0] for l in range(w.layers)])
+            kb = np.stack([host(caches[l][0][b, :, :n]) for l in range(w.layers)])
+            vb = np.stack([host(caches[l][1][b, :, :n]) for l in range(w.layers)])
+            r = osteps.tiered_sequence_step(s_in[b], ev_in[b], qb, kb, vb, n, scale, w.n_sink,
+                                            w.n_recent, w.t0_permille, w.t01_permille,
+                                            dense=(t == 0))
+            if t > 0:
+                assert dec.tier[b, :n].cpu().numpy().tolist() == r["tier"].tolist()
+                c = int(dec.count[b])
+                assert dec.sel[b, :c].cpu().numpy().tolist() == r["tokens"].tolist()
+            check_rows(out[:, b, 0].cpu().numpy(), r["out"], what="tiered attention")
+            check_rows(dec.s[b, :n].cpu().numpy()[None], r["s"][None], what="importance")
+    del caches, dec
+    _free()
