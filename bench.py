@@ -195,6 +195,43 @@ def base_result(w, K, W, ms_step, step_bytes, config):
     }
 
 
+# Bytes the roofline kernel of each workload moves per launch, from two rocprofv3 --pmc runs of
+# this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over the dispatches of the
+# timed kernel loop).  Each counter is scaled by what it reads for a plain 512 MiB device copy
+# in the same runs (FETCH_SIZE 262162 KiB -> x2.0, WRITE_SIZE 524288 KiB -> x1.0).  A reading
+# belongs to the kernel sources it was taken on (digest of the files listed): once they change
+# it is reported as null until the counters are taken again.
+COPY_KIB = 512 * 1024
+FETCH_COPY_KIB, WRITE_COPY_KIB = 262162.0, 524288.0
+TRAFFIC = {
+    "block": (("attn.hip", "spk_internal.h"), "a347420eb0e8bed5", 40852.5, 1370.56),
+    "per_head": (("index_score.hip", "spk_internal.h"), "1a4452095e53323b", 524479.0, 65536.0),
+    "spec_verify": (("attn.hip", "spk_internal.h"), "a347420eb0e8bed5", 271033.0, 7232.0),
+    "tiers": (("attn.hip", "spk_internal.h"), "a347420eb0e8bed5", 399093.0, 50154.2),
+}
+
+
+def _src_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_top_kv_gqa_amd", "csrc")
+    for f in files:
+        with open(os.path.join(here, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the roofline kernel (counter readings scaled by the copy
+    calibration), or None when the kernel's sources changed since the readings."""
+    files, digest, fetch_kib, write_kib = TRAFFIC[workload]
+    if _src_digest(files) != digest:
+        return None
+    fetch = fetch_kib * COPY_KIB / FETCH_COPY_KIB
+    write = write_kib * COPY_KIB / WRITE_COPY_KIB
+    return int((fetch + write) * 1024)
+
+
 def roofline(kernel, bytes_per_launch, ms, traffic=None, note=None, bound="hbm",
              peak=HBM_PEAK_GBS):
     gbs = bytes_per_launch / (ms * 1e-3) / 1e9
@@ -287,7 +324,7 @@ def bench_block(args):
         "selected_rows_per_step": int(att_bytes / ROW_BYTES), "wall_s_timed": round(wall, 4),
         "attention_call_ms": round(att_ms, 4)})
     res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather)", att_bytes,
-                               gather_ms)
+                               gather_ms, traffic=measured_traffic("block"))
     ctx = dict(w=w, dec=decs[0], q=qs[0], pred=preds[0])
     return res, ctx
 
@@ -416,10 +453,12 @@ def bench_token(args, which):
                                               (gather_ms * 1e-3) / 1e9, 1)
         res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather), "
                                    "host-resident rows", hb, gather_ms, bound="pcie",
-                                   peak=PCIE_PEAK_GBS)
+                                   peak=PCIE_PEAK_GBS, traffic=measured_traffic(which),
+                                   note="traffic counts every byte the kernel reads (HBM rows "
+                                        "and host rows)")
     else:
         res["roofline"] = roofline(f"index_rows_kernel (sparse_index_score {mode})", index_bytes,
-                                   idx_ms)
+                                   idx_ms, traffic=measured_traffic(which))
     ctx = dict(w=w, k=k, v=v, q=qs[0], which=which)
     return res, ctx
 
@@ -528,7 +567,8 @@ def bench_tiers(args):
         "attention_layer_ms_last_step": round(att_ms, 4), "tier_classify_ms": round(tier_ms, 4),
         "importance_ms": round(imp_ms, 4)})
     res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather, one layer at "
-                               f"{n_last} tokens)", att_bytes, gather_ms)
+                               f"{n_last} tokens)", att_bytes, gather_ms,
+                               traffic=measured_traffic("tiers"))
     ctx = dict(w=w, caches=caches, qs=qs, n_last=n_last)
     return res, ctx
 
