@@ -23,6 +23,7 @@
 //     (deterministic, no atomics) into out and lse.  A separate launch: merging inside the
 //     partial kernel needs a device-scope release per workgroup, which writes back the XCD's
 //     whole L2 and costs far more than this launch.
+#include <mutex>
 #include <type_traits>
 
 #include "spk_internal.h"
@@ -39,7 +40,8 @@ constexpr int kMaxSets = 32;
 constexpr int kAsmThreads = 1024;
 constexpr int kAsmLdsWords = 32768;  // 128 KB of LDS bitmaps; larger ones live in the workspace
 constexpr int kMaxIntervals = 64;   // selection entries + 2 forced ranges, one per lane
-constexpr int kMaxRows = 2048;      // rows per workgroup (LDS row table)
+constexpr int kMaxRows = 8192;      // rows per split (LDS slot table)
+constexpr int kTabPad = 512;        // slot-table entries past a split's rows (dead padding)
 constexpr int kDead = INT32_MIN;    // row-table entry of a row that is not read
 
 struct Plan {
@@ -51,11 +53,31 @@ struct Plan {
 
 int pad_nq(int nq) { return nq <= 1 ? 1 : nq <= 2 ? 2 : nq <= 4 ? 4 : nq <= 8 ? 8 : 16; }
 
-int partial_occupancy(int d, int nq_pad, bool mask, int mode);  // resident workgroups per CU
+// Resources of the bf16 (MFMA) partial kernel of a configuration: resident workgroups per CU
+// without dynamic LDS, and its static LDS bytes (queried once per configuration).
+struct PartialInfo {
+  int occ = 2;
+  size_t static_lds = 0;
+};
+PartialInfo partial_info(int d, int nq_pad, bool mask, int mode);
+size_t lds_per_cu();
+size_t lds_per_block();
+
+#ifndef SPK_ATTN_WG_ROWS
+#define SPK_ATTN_WG_ROWS 128  // fixed cost of a split (set-up, merge), in rows of streaming
+#endif
+
+// Dynamic LDS of a partial workgroup: the slot table (and list masks) for R rows plus padding.
+inline size_t table_bytes(int R, bool mask) { return (size_t)(R + kTabPad) * 4 * (mask ? 2 : 1); }
 
 // Fetch-list strategy, split size and workspace layout of one call.  A group with one selection
 // list expands it in the partial kernel itself (intervals mode) when the list is short; several
 // lists per group (per-head or per-token sets) are merged by the assemble kernel first.
+//
+// Split size: R rows (a multiple of 64) per split, chosen to minimise
+// rounds(R) * (R + fixed cost), where rounds(R) is how many times the group's splits fill every
+// CU's resident workgroup slots (at the occupancy the slot table's LDS allows).  Workgroups
+// then see the same amount of work and the last round is not left half empty.
 Plan make_plan(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_tokens,
                int64_t sel_ld, int gran, int n_sink, int n_recent) {
   Plan p;
@@ -71,16 +93,29 @@ Plan make_plan(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_
   int64_t ub = (int64_t)p.sets * sel_ld * gran + n_sink + n_recent;
   if (ub > n_tokens) ub = n_tokens;
   p.ubound = (int)ub;
-  // rows per split: about one resident round of workgroups when every list is full
-  const int64_t rows = (int64_t)p.groups * (p.ubound > 0 ? p.ubound : 1);
-  const int occ = partial_occupancy(d, p.nq_pad, p.mask, p.intervals ? 1 : 0);
-  const int step = 64;
-  int64_t R = ceil_div(rows, (int64_t)occ * num_cus());
-  R = ceil_div(R, step) * step;
-  if (R < step) R = step;
-  if (R > kMaxRows) R = kMaxRows;
-  p.R = (int)R;
-  p.smax = p.ubound > 0 ? (int)ceil_div(p.ubound, p.R) : 1;
+  const PartialInfo info = partial_info(d, p.nq_pad, p.mask, p.intervals ? 1 : 0);
+  const int64_t cus = num_cus();
+  const size_t lds_cu = lds_per_cu(), lds_wg = lds_per_block();
+  const int ubound = p.ubound > 0 ? p.ubound : 1;
+  int best_R = 64;
+  double best = -1.0;
+  for (int R = 64; R <= kMaxRows; R += 64) {
+    const size_t lds = info.static_lds + table_bytes(R, p.mask);
+    if (lds > lds_wg && R > 64) break;
+    int occ = (int)(lds_cu / (lds > 0 ? lds : 1));
+    if (occ > info.occ) occ = info.occ;
+    if (occ < 1) occ = 1;
+    const int64_t wgs = (int64_t)p.groups * ceil_div(ubound, R);
+    const int64_t rounds = ceil_div(wgs, (int64_t)occ * cus);
+    const double cost = (double)rounds * (double)(R + SPK_ATTN_WG_ROWS);
+    if (best < 0 || cost < best) {
+      best = cost;
+      best_R = R;
+    }
+    if (R >= ubound) break;
+  }
+  p.R = best_R;
+  p.smax = (int)ceil_div(ubound, p.R);
   p.words = (int)ceil_div(n_tokens > 0 ? n_tokens : 1, 32);
   p.bm_lds = (int64_t)p.sets * p.words <= kAsmLdsWords;
   size_t off = 0;
@@ -212,7 +247,8 @@ struct AttnArgs {
   int ucount_valid;      // ucount holds the lengths (assembled lists)
   const uint32_t* mask;  // per fetch-list row (assembled lists with several sets)
   int mask_div;          // query vector n reads rows whose mask has bit n / mask_div
-  int T, Hq, Hkv, G, nq, n_tokens, R, smax;
+  int T, Hq, Hkv, G, nq, n_tokens, smax;
+  int tab_cap;           // slot-table entries of the dynamic LDS (plan R + padding)
   float scale_log2;
   float* ml;
   float* acc;
@@ -258,6 +294,42 @@ __device__ __forceinline__ int resolve_slot(const AttnArgs& a, int b, int kvh, i
 // A readable, all-zero row: rows that are not read load from here, so every load in the main
 // loop is issued unconditionally (no divergent branches between loads and their waits).
 __device__ __align__(64) uint32_t g_zero_row[128];
+
+// Rows per split of a group with `cnt` fetch-list rows: the group's rows spread evenly over the
+// plan's smax splits (a multiple of 16, at most the plan's R).  Partial and combine kernels agree
+// on it.
+__device__ __forceinline__ int split_rows(int cnt, int smax) {
+  const int r = (cnt + smax - 1) / smax;
+  return (r + 15) & ~15;
+}
+
+// Byte addresses of a row's K and V from its slot (see resolve_slot).
+struct RowBase {
+  uint64_t k_hbm, k_host, dv_hbm, dv_host, zero;
+  int64_t sn_hbm, sn_host;  // row strides in bytes
+};
+__device__ __forceinline__ void row_addr(const RowBase& rb, int slot, uint64_t& ka, uint64_t& va) {
+  const uint64_t h = rb.k_hbm + (uint64_t)((int64_t)slot * rb.sn_hbm);
+  const uint64_t o = rb.k_host + (uint64_t)((int64_t)(~slot) * rb.sn_host);
+  ka = slot == kDead ? rb.zero : (slot >= 0 ? h : o);
+  va = ka + (slot == kDead ? 0ull : (slot >= 0 ? rb.dv_hbm : rb.dv_host));
+}
+
+template <typename KT>
+__device__ __forceinline__ RowBase make_row_base(const AttnArgs& a, int b, int kvh) {
+  RowBase rb;
+  rb.k_hbm = reinterpret_cast<uint64_t>(a.k) +
+             (uint64_t)(((int64_t)b * a.kv_sb + (int64_t)kvh * a.kv_sh) * (int64_t)sizeof(KT));
+  rb.k_host = reinterpret_cast<uint64_t>(a.k_host) +
+              (uint64_t)(((int64_t)b * a.host_sb + (int64_t)kvh * a.host_sh) * (int64_t)sizeof(KT));
+  rb.dv_hbm = reinterpret_cast<uint64_t>(a.v) - reinterpret_cast<uint64_t>(a.k);
+  rb.dv_host = reinterpret_cast<uint64_t>(a.v_host) - reinterpret_cast<uint64_t>(a.k_host);
+  rb.zero = reinterpret_cast<uint64_t>(g_zero_row);
+  rb.sn_hbm = a.kv_sn * (int64_t)sizeof(KT);
+  rb.sn_host = a.host_sn * (int64_t)sizeof(KT);
+  return rb;
+}
+
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -348,6 +420,28 @@ __device__ __forceinline__ int token_at(const int* seg_start, const int* seg_pos
   return seg_start[lo] + (p - seg_pos[lo]);
 }
 
+// Fill the split's slot table (and per-row list masks) in LDS: entries [0, nrows) are the
+// split's rows, entries up to tab_rows are dead (they read the zero row).
+template <int MODE, bool kMask>
+__device__ __forceinline__ void fill_slot_table(const AttnArgs& a, int b, int kvh, int g, int lrow,
+                                                int r0, int nrows, int tab_rows, int32_t* slot_s,
+                                                uint32_t* mask_s, const int* seg_start,
+                                                const int* seg_pos, int nseg) {
+  const int32_t* list = a.list + (int64_t)lrow * a.list_ld;
+  const uint32_t* mrow = kMask ? a.mask + (int64_t)g * a.list_ld : nullptr;
+  for (int i = threadIdx.x; i < tab_rows; i += blockDim.x) {
+    int slot_v = kDead;
+    if (i < nrows) {
+      int tok;
+      if constexpr (MODE == kListIntervals) tok = token_at(seg_start, seg_pos, nseg, r0 + i);
+      else tok = list[r0 + i];
+      slot_v = resolve_slot(a, b, kvh, tok);
+    }
+    slot_s[i] = slot_v;
+    if constexpr (kMask) mask_s[i] = i < nrows ? mrow[r0 + i] : 0u;
+  }
+}
+
 #ifndef SPK_ATTN_MIN_WAVES
 #define SPK_ATTN_MIN_WAVES 2  // register budget: at least this many waves per SIMD
 #endif
@@ -358,13 +452,14 @@ __attribute__((amdgpu_waves_per_eu(SPK_ATTN_MIN_WAVES))) void attn_partial_kerne
   constexpr int SPW = kWave / LPR;       // slots (rows) per wave
   constexpr int NSLOT = SPW * kWaves;    // slots per workgroup
   constexpr int STEP = NSLOT * U;        // rows per workgroup per iteration
-  // row table: byte addresses of the row's K and V (HBM or host; rows not read point at the zero
-  // row), padded past the last row so every issue in the main loop is unconditional
-  constexpr int kTab = kMaxRows + 2 * STEP;
+  static_assert(3 * STEP <= kTabPad, "slot table padding");
   __shared__ float red[kWaves][NQ][D + 2];
-  __shared__ ulonglong2 addr_s[kTab];
-  __shared__ uint32_t mask_s[kMask ? kTab : 1];
   __shared__ int seg_start[kMaxIntervals], seg_pos[kMaxIntervals], seg_meta[2];
+  // row slots (HBM slot, ~host slot, or dead: read the zero row), padded past the last row so
+  // every issue in the main loop is unconditional; then the per-row list masks
+  extern __shared__ int32_t dyn_s[];
+  int32_t* slot_s = dyn_s;
+  uint32_t* mask_s = reinterpret_cast<uint32_t*>(dyn_s + a.tab_cap);
 
   const int g = blockIdx.y;
   const int split = blockIdx.x;
@@ -386,47 +481,17 @@ __attribute__((amdgpu_waves_per_eu(SPK_ATTN_MIN_WAVES))) void attn_partial_kerne
     cnt = a.count[lrow];
     cnt = max(0, min(cnt, a.count_clamp));
   }
-  const int r0 = split * a.R;
+  const int rs = split_rows(cnt, a.smax);
+  const int r0 = split * rs;
   if (r0 >= cnt) return;
-  const int r1 = min(r0 + a.R, cnt);
+  const int r1 = min(r0 + rs, cnt);
   const int nrows = r1 - r0;
 
   const int iters = (nrows + STEP - 1) / STEP;
   const int tab_rows = (iters + 2) * STEP;
-  // group base addresses (byte), without the lane column
-  const uint64_t gk = reinterpret_cast<uint64_t>(a.k) +
-                      (uint64_t)(((int64_t)b * a.kv_sb + (int64_t)kvh * a.kv_sh) * (int64_t)sizeof(KT));
-  const uint64_t gkh = reinterpret_cast<uint64_t>(a.k_host) +
-                       (uint64_t)(((int64_t)b * a.host_sb + (int64_t)kvh * a.host_sh) * (int64_t)sizeof(KT));
-  const uint64_t zero_row = reinterpret_cast<uint64_t>(g_zero_row);
-  // V row = K row + (v - k) in HBM, + (v_host - k_host) in host memory
-  const uint64_t dd = reinterpret_cast<uint64_t>(a.v) - reinterpret_cast<uint64_t>(a.k);
-  const uint64_t dh = reinterpret_cast<uint64_t>(a.v_host) - reinterpret_cast<uint64_t>(a.k_host);
-  {
-    const int32_t* list = a.list + (int64_t)lrow * a.list_ld;
-    const uint32_t* mrow = kMask ? a.mask + (int64_t)g * a.list_ld : nullptr;
-    for (int i = threadIdx.x; i < tab_rows; i += kThreads) {
-      int slot_v = kDead;
-      if (i < nrows) {
-        int tok;
-        if constexpr (MODE == kListIntervals) tok = token_at(seg_start, seg_pos, seg_meta[0], r0 + i);
-        else tok = list[r0 + i];
-        slot_v = resolve_slot(a, b, kvh, tok);
-      }
-      ulonglong2 ad;
-      if (slot_v == kDead) {
-        ad.x = ad.y = zero_row;
-      } else if (slot_v < 0) {
-        ad.x = gkh + (uint64_t)((int64_t)(~slot_v) * a.host_sn * (int64_t)sizeof(KT));
-        ad.y = ad.x + dh;
-      } else {
-        ad.x = gk + (uint64_t)((int64_t)slot_v * a.kv_sn * (int64_t)sizeof(KT));
-        ad.y = ad.x + dd;
-      }
-      addr_s[i] = ad;
-      if constexpr (kMask) mask_s[i] = i < nrows ? mrow[r0 + i] : 0u;
-    }
-  }
+  const RowBase rbase = make_row_base<KT>(a, b, kvh);
+  fill_slot_table<MODE, kMask>(a, b, kvh, g, lrow, r0, nrows, tab_rows, slot_s, mask_s, seg_start,
+                               seg_pos, seg_meta[0]);
 
   // query slices, pre-scaled into the exp2 domain
   float qs[NQ][8];
@@ -456,14 +521,14 @@ __attribute__((amdgpu_waves_per_eu(SPK_ATTN_MIN_WAVES))) void attn_partial_kerne
 
   const uint64_t col = (uint64_t)(sub * 8 * (int)sizeof(KT));
   auto issue = [&](int it, Raw8<KT> (&rk)[U], Raw8<KT> (&rv)[U], int (&sl)[U]) {
-    ulonglong2 ad[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) ad[u] = addr_s[it * STEP + u * NSLOT + sid];
+    for (int u = 0; u < U; ++u) sl[u] = slot_s[it * STEP + u * NSLOT + sid];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      sl[u] = ad[u].x == zero_row ? kDead : 0;
-      rk[u].load_addr(ad[u].x + col);
-      rv[u].load_addr(ad[u].y + col);
+      uint64_t ka, va;
+      row_addr(rbase, sl[u], ka, va);
+      rk[u].load_addr(ka + col);
+      rv[u].load_addr(va + col);
     }
   };
   auto consume = [&](int it, const Raw8<KT> (&rk)[U], const Raw8<KT> (&rv)[U],
@@ -615,7 +680,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 template <int D, int NQ, bool kMask, int MODE>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_kernel(AttnArgs a) {
+__attribute__((amdgpu_waves_per_eu(NQ <= 4 ? 3 : SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_kernel(AttnArgs a) {
   constexpr int BATCH = NQ <= 8 ? SPK_MFMA_BATCH : 1;  // tiles in flight per wave
   constexpr int TILE = 16;                // rows per wave per step
   constexpr int STEP = TILE * kWaves;     // rows per workgroup per step
@@ -623,13 +688,13 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   constexpr int LPR = D / 8;              // P·V layout: lanes per row
   constexpr int RPI = kWave / LPR;        // P·V layout: rows per instruction
   constexpr int PVI = TILE / RPI;         // P·V instructions per tile
-  constexpr int kTab = kMaxRows + 2 * STEP;
   static_assert(NQ <= 16, "at most 16 query vectors per group");
-  static_assert(BATCH <= 2, "row table padding covers two steps past the last row");
+  static_assert(BATCH <= 4 && 4 * STEP <= kTabPad, "slot table padding covers the last batch");
   __shared__ float red[kWaves][NQ][D + 2];
-  __shared__ ulonglong2 addr_s[kTab];
-  __shared__ uint32_t mask_s[kMask ? kTab : 1];
   __shared__ int seg_start[kMaxIntervals], seg_pos[kMaxIntervals], seg_meta[2];
+  extern __shared__ int32_t dyn_s[];
+  int32_t* slot_s = dyn_s;
+  uint32_t* mask_s = reinterpret_cast<uint32_t*>(dyn_s + a.tab_cap);
   __shared__ float p_s[kWaves][TILE][16];
   __shared__ float alpha_s[kWaves][16];
 
@@ -667,44 +732,16 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
     cnt = a.count[lrow];
     cnt = max(0, min(cnt, a.count_clamp));
   }
-  const int r0 = split * a.R;
+  const int rs = split_rows(cnt, a.smax);
+  const int r0 = split * rs;
   if (r0 >= cnt) return;
-  const int r1 = min(r0 + a.R, cnt);
+  const int r1 = min(r0 + rs, cnt);
   const int nrows = r1 - r0;
   const int iters = (nrows + STEP - 1) / STEP;
-  const int tab_rows = (iters + 2) * STEP;
-  const uint64_t zero_row = reinterpret_cast<uint64_t>(g_zero_row);
-  {
-    const uint64_t gk = reinterpret_cast<uint64_t>(a.k) +
-                        (uint64_t)(((int64_t)b * a.kv_sb + (int64_t)kvh * a.kv_sh) * 2);
-    const uint64_t gkh = reinterpret_cast<uint64_t>(a.k_host) +
-                         (uint64_t)(((int64_t)b * a.host_sb + (int64_t)kvh * a.host_sh) * 2);
-    const uint64_t dd = reinterpret_cast<uint64_t>(a.v) - reinterpret_cast<uint64_t>(a.k);
-    const uint64_t dh = reinterpret_cast<uint64_t>(a.v_host) - reinterpret_cast<uint64_t>(a.k_host);
-    const int32_t* list = a.list + (int64_t)lrow * a.list_ld;
-    const uint32_t* mrow = kMask ? a.mask + (int64_t)g * a.list_ld : nullptr;
-    for (int i = threadIdx.x; i < tab_rows; i += kThreads) {
-      int slot_v = kDead;
-      if (i < nrows) {
-        int tok;
-        if constexpr (MODE == kListIntervals) tok = token_at(seg_start, seg_pos, seg_meta[0], r0 + i);
-        else tok = list[r0 + i];
-        slot_v = resolve_slot(a, b, kvh, tok);
-      }
-      ulonglong2 ad;
-      if (slot_v == kDead) {
-        ad.x = ad.y = zero_row;
-      } else if (slot_v < 0) {
-        ad.x = gkh + (uint64_t)((int64_t)(~slot_v) * a.host_sn * 2);
-        ad.y = ad.x + dh;
-      } else {
-        ad.x = gk + (uint64_t)((int64_t)slot_v * a.kv_sn * 2);
-        ad.y = ad.x + dd;
-      }
-      addr_s[i] = ad;
-      if constexpr (kMask) mask_s[i] = i < nrows ? mrow[r0 + i] : 0u;
-    }
-  }
+  const int tab_rows = (iters + 3) * STEP;
+  const RowBase rbase = make_row_base<uint16_t>(a, b, kvh);
+  fill_slot_table<MODE, kMask>(a, b, kvh, g, lrow, r0, nrows, tab_rows, slot_s, mask_s, seg_start,
+                               seg_pos, seg_meta[0]);
 
   float m_q = -INFINITY, l_part = 0.f;  // query qc: running max (wave-uniform), own-row denominator
   float acc[NQ][8];
@@ -725,15 +762,20 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
 
   auto issue = [&](int it, uint4 (&kr)[KCH], uint4 (&vr)[PVI], bool& klive) {
     const int tb = it * STEP + wid * TILE;
-    const ulonglong2 e = addr_s[tb + qc];
-    klive = e.x != zero_row;
-    ulonglong2 ev[PVI];
+    const int sk = slot_s[tb + qc];
+    int sv[PVI];
 #pragma unroll
-    for (int i = 0; i < PVI; ++i) ev[i] = addr_s[tb + i * RPI + slot];
+    for (int i = 0; i < PVI; ++i) sv[i] = slot_s[tb + i * RPI + slot];
+    klive = sk != kDead;
+    uint64_t ka, va;
+    row_addr(rbase, sk, ka, va);
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) kr[j] = gload16(e.x + kcol + 64 * j);
+    for (int j = 0; j < KCH; ++j) kr[j] = gload16(ka + kcol + 64 * j);
 #pragma unroll
-    for (int i = 0; i < PVI; ++i) vr[i] = gload16(ev[i].y + vcol);
+    for (int i = 0; i < PVI; ++i) {
+      row_addr(rbase, sv[i], ka, va);
+      vr[i] = gload16(va + vcol);
+    }
   };
   auto consume = [&](int it, const uint4 (&kr)[KCH], const uint4 (&vr)[PVI], bool klive) {
     const int tb = it * STEP + wid * TILE;
@@ -877,7 +919,8 @@ __global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a, int nq_
 #pragma unroll
       for (int i = 0; i < PER; ++i) ac[j][i] = a.acc[pi * D + lane + i * kWave];
     }
-    const int S = cnt > 0 ? (cnt + a.R - 1) / a.R : 0;
+    const int per = cnt > 0 ? split_rows(cnt, a.smax) : 1;
+    const int S = cnt > 0 ? (cnt + per - 1) / per : 0;
     float cmx = mx;
 #pragma unroll
     for (int j = 0; j < kCombineMax; ++j)
@@ -917,13 +960,16 @@ constexpr int attn_unroll(int nq) { return nq <= 4 ? SPK_ATTN_UNROLL_SMALL : SPK
 template <int D, typename KT, int NQ, bool kMask, int MODE>
 void launch_partial(dim3 grid, hipStream_t st, const AttnArgs& a) {
   constexpr int U = attn_unroll(NQ);
-  hipLaunchKernelGGL((attn_partial_kernel<D, KT, NQ, kMask, MODE, U>), grid, dim3(kThreads), 0, st,
-                     a);
+  const size_t dyn = (size_t)a.tab_cap * 4 * (kMask ? 2 : 1);
+  hipLaunchKernelGGL((attn_partial_kernel<D, KT, NQ, kMask, MODE, U>), grid, dim3(kThreads), dyn,
+                     st, a);
 }
 
 template <int D, int NQ, bool kMask, int MODE>
 void launch_partial_mfma(dim3 grid, hipStream_t st, const AttnArgs& a) {
-  hipLaunchKernelGGL((attn_partial_mfma_kernel<D, NQ, kMask, MODE>), grid, dim3(kThreads), 0, st, a);
+  const size_t dyn = (size_t)a.tab_cap * 4 * (kMask ? 2 : 1);
+  hipLaunchKernelGGL((attn_partial_mfma_kernel<D, NQ, kMask, MODE>), grid, dim3(kThreads), dyn, st,
+                     a);
 }
 
 template <int D, typename KT, int NQ>
@@ -952,13 +998,15 @@ void dispatch_nq(int nq_pad, bool mask, int mode, dim3 grid, hipStream_t st, con
   }
 }
 
-// Resident partial workgroups per CU of the bf16 (MFMA) kernel of a configuration (queried once).
-int partial_occupancy(int d, int nq_pad, bool mask, int mode) {
-  static int cache[2][5][2][2];
+// Occupancy and static LDS of the bf16 (MFMA) partial kernel of a configuration (queried once).
+PartialInfo partial_info(int d, int nq_pad, bool mask, int mode) {
+  static PartialInfo cache[2][5][2][2];
+  static bool have[2][5][2][2];
+  static std::mutex mu;
   const int di = d == 128 ? 0 : 1;
   const int ni = nq_pad == 1 ? 0 : nq_pad == 2 ? 1 : nq_pad == 4 ? 2 : nq_pad == 8 ? 3 : 4;
-  int& c = cache[di][ni][mask ? 1 : 0][mode ? 1 : 0];
-  if (c > 0) return c;
+  std::lock_guard<std::mutex> lock(mu);
+  if (have[di][ni][mask ? 1 : 0][mode ? 1 : 0]) return cache[di][ni][mask ? 1 : 0][mode ? 1 : 0];
   const void* fn = nullptr;
 #define SPK_FN(D, NQ)                                                                     \
   fn = mask ? (const void*)attn_partial_mfma_kernel<D, NQ, true, kListExplicit>            \
@@ -979,23 +1027,42 @@ int partial_occupancy(int d, int nq_pad, bool mask, int mode) {
   }
 #undef SPK_FN_D
 #undef SPK_FN
+  PartialInfo info;
   int blocks = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, 0) != hipSuccess ||
       blocks <= 0) {
     (void)hipGetLastError();
     blocks = 2;
   }
-  c = blocks;
-  return c;
+  info.occ = blocks;
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, fn) == hipSuccess) info.static_lds = attr.sharedSizeBytes;
+  else (void)hipGetLastError();
+  cache[di][ni][mask ? 1 : 0][mode ? 1 : 0] = info;
+  have[di][ni][mask ? 1 : 0][mode ? 1 : 0] = true;
+  return info;
 }
+
+static size_t device_attr(hipDeviceAttribute_t attr, size_t fallback) {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, attr, dev) != hipSuccess ||
+      v <= 0) {
+    (void)hipGetLastError();
+    return fallback;
+  }
+  return (size_t)v;
+}
+
+size_t lds_per_cu() {
+  return device_attr(hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, 65536);
+}
+size_t lds_per_block() { return device_attr(hipDeviceAttributeMaxSharedMemoryPerBlock, 65536); }
 
 }  // namespace
 }  // namespace spk
 
 using spk::Plan;
 
-// A host pool must be page-locked, device-mapped host memory; the kernel reads it through the
-// device address HIP reports for it.  Pageable memory would fault, so it is refused here.
 // Events of spk_set_attn_timing_events (null: timing off).
 static hipEvent_t g_timing_begin = nullptr;
 static hipEvent_t g_timing_end = nullptr;
@@ -1010,6 +1077,8 @@ extern "C" SPK_API spk_status spk_set_attn_timing_events(void* begin, void* end)
   return SPK_OK;
 }
 
+// A host pool must be page-locked, device-mapped host memory; the kernel reads it through the
+// device address HIP reports for it.  Pageable memory would fault, so it is refused here.
 static spk_status resolve_host_pool(const void* p, const void** dev, const char* name) {
   hipPointerAttribute_t at{};
   const hipError_t e = hipPointerGetAttributes(&at, p);
@@ -1138,7 +1207,7 @@ extern "C" SPK_API spk_status sparse_decode_attn(
   a.G = G;
   a.nq = G * T;
   a.n_tokens = n_tokens;
-  a.R = p.R;
+  a.tab_cap = p.R + kTabPad;
   a.smax = p.smax;
   a.scale_log2 = sm_scale * kLog2e;
   a.ml = reinterpret_cast<float*>(w + p.off_ml);

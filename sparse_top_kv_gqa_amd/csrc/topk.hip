@@ -4,11 +4,8 @@
 // Contexto no Tempo de Inferência", §2 "Oracle Top-K" (exact top-k tokens).
 //
 // One workgroup per row.  Scores map to order-preserving uint32 keys (-0 -> +0, NaN lowest).
-//  * n <= 4096: one wave holds the row in registers (up to 64 keys per lane) and needs no
-//    barrier at all.
-//  * n <= 16384: 256 threads hold the row in registers (up to 64 keys each).  The k-th largest
-//    key is found bit by bit from the top: a candidate threshold is kept when at least k keys
-//    reach it, the count coming from wave ballots (scalar popcounts) summed across the 4 waves.
+//  * n <= 16384: 256 threads hold the row in registers (up to 64 keys each); a radix select
+//    (8-bit digits, per-wave LDS histograms) finds the k-th largest key in four passes.
 //  * larger n: a 12-bit histogram finds the bin of the k-th key, that bin's keys are gathered
 //    into LDS and bit-searched for the exact threshold (a full radix select when ties overflow
 //    the store), and each wave compacts its own contiguous segment in index order.
@@ -26,59 +23,14 @@ constexpr int kSmallMax = 64 * kSmallThreads;  // 16384
 
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
-// One wave per row (n <= 4096): item c of lane t is element c*64 + t.  Counting needs only
-// ballots and scalar popcounts, so the bit search runs without any barrier.
-template <int ITEMS>
-__global__ __launch_bounds__(kWave) void topk_wave_kernel(
-    const float* __restrict__ scores, int64_t s_ld, int n, int k, int32_t* __restrict__ idx,
-    int64_t idx_ld, int32_t* __restrict__ count) {
-  const int row = blockIdx.x;
-  const float* x = scores + (int64_t)row * s_ld;
-  const int kk = min(k, n);
-  const int lane = lane_id();
-  if (count && lane == 0) count[row] = kk;
-  if (kk <= 0) return;
-  int32_t* out = idx + (int64_t)row * idx_ld;
-  uint32_t key[ITEMS];
-#pragma unroll
-  for (int c = 0; c < ITEMS; ++c) {
-    const int i = c * kWave + lane;
-    key[c] = i < n ? order_key(x[i]) : 0u;
-  }
-  auto count_ge = [&](uint32_t cand) -> int {
-    int wc = 0;
-#pragma unroll
-    for (int c = 0; c < ITEMS; ++c) wc += __popcll(__ballot((c * kWave + lane < n) && key[c] >= cand));
-    return wc;
-  };
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    if (count_ge(cand) >= kk) thr = cand;
-  }
-  const int need = kk - (thr == 0xFFFFFFFFu ? 0 : count_ge(thr + 1u));
-  int run_gt = 0, run_eq = 0;
-  const uint64_t lt = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int c = 0; c < ITEMS; ++c) {
-    const int i = c * kWave + lane;
-    const bool valid = i < n;
-    const bool gt = valid && key[c] > thr;
-    const bool eq = valid && key[c] == thr;
-    const uint64_t bg = __ballot(gt), be = __ballot(eq);
-    const int eq_rank = run_eq + __popcll(be & lt);
-    if (gt || (eq && eq_rank < need)) out[run_gt + __popcll(bg & lt) + min(eq_rank, need)] = i;
-    run_gt += __popcll(bg);
-    run_eq += __popcll(be);
-  }
-}
-
 // Keys of row `x` held in registers: item c of thread t is element c*256 + t.
 template <int ITEMS>
 __global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
     const float* __restrict__ scores, int64_t s_ld, int n, int k, int32_t* __restrict__ idx,
     int64_t idx_ld, int32_t* __restrict__ count) {
   __shared__ int red[2][kSmallWaves][2];
+  __shared__ uint32_t hist[kSmallWaves * 256];
+  __shared__ int sh[2];
   const int row = blockIdx.x;
   const float* x = scores + (int64_t)row * s_ld;
   const int kk = min(k, n);
@@ -92,32 +44,17 @@ __global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
     const int i = c * kSmallThreads + t;
     key[c] = i < n ? order_key(x[i]) : 0u;
   }
-  // count of valid keys >= cand over the workgroup (one barrier, parity-buffered LDS)
-  auto count_ge = [&](uint32_t cand, int parity) -> int {
-    int wc = 0;
+  // thr = the kk-th largest key; `need` of the keys equal to it rank inside the top kk
+  uint32_t thr;
+  int need;
+  radix_select<kSmallThreads>(
+      [&](auto visit) {
 #pragma unroll
-    for (int c = 0; c < ITEMS; ++c) {
-      const bool v = (c * kSmallThreads + t < n) && key[c] >= cand;
-      wc += __popcll(__ballot(v));
-    }
-    if (lane == 0) red[parity][wid][0] = wc;
-    __syncthreads();
-    int tot = 0;
-#pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) tot += red[parity][w][0];
-    return tot;
-  };
-  uint32_t thr = 0;
+        for (int c = 0; c < ITEMS; ++c)
+          if (c * kSmallThreads + t < n) visit(key[c]);
+      },
+      kk, hist, sh, &thr, &need);
   int parity = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    if (count_ge(cand, parity) >= kk) thr = cand;
-    parity ^= 1;
-  }
-  // thr is the kk-th largest key; keys > thr all rank inside the top kk
-  const int n_gt = thr == 0xFFFFFFFFu ? 0 : count_ge(thr + 1u, parity);
-  parity ^= 1;
-  const int need = kk - n_gt;
   int run_gt = 0, run_eq = 0;
 #pragma unroll
   for (int c = 0; c < ITEMS; ++c) {
@@ -472,19 +409,7 @@ extern "C" SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int
   clear_error();
   if (rows == 0) return SPK_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (n <= 64 * kWave) {
-    const int items = (n + kWave - 1) / kWave;
-#define SPK_WAVE(IT) \
-  hipLaunchKernelGGL(topk_wave_kernel<IT>, dim3(rows), dim3(kWave), 0, st, scores, s_ld, n, k, idx, idx_ld, count)
-    if (items <= 1) SPK_WAVE(1);
-    else if (items <= 2) SPK_WAVE(2);
-    else if (items <= 4) SPK_WAVE(4);
-    else if (items <= 8) SPK_WAVE(8);
-    else if (items <= 16) SPK_WAVE(16);
-    else if (items <= 32) SPK_WAVE(32);
-    else SPK_WAVE(64);
-#undef SPK_WAVE
-  } else if (n <= kSmallMax) {
+  if (n <= kSmallMax) {
     const int items = (n + kSmallThreads - 1) / kSmallThreads;
 #define SPK_SMALL(IT)                                                                          \
   hipLaunchKernelGGL(topk_small_kernel<IT>, dim3(rows), dim3(kSmallThreads), 0, st, scores, s_ld, \
