@@ -657,16 +657,26 @@ __attribute__((amdgpu_waves_per_eu(SPK_ATTN_MIN_WAVES))) void attn_partial_kerne
 
 // ------------------------------------------------------------------------------- partial (MFMA)
 
-// bf16 K/V and bf16 queries: Q·Kᵀ runs on the matrix cores.  Each wave owns 16-row tiles; one
-// v_mfma_f32_16x16x32_bf16 per 32 dims takes A = the tile's K rows (lane l holds 16 bytes of
-// row l%16) and B = the group's query vectors (query l%16), giving every lane the logits of
-// rows 4(l/16)..+3 for query l%16.  The online softmax runs in that layout; the probabilities go
-// through LDS to a row-per-16-lanes layout where P·V accumulates in fp32 on the VALU.
+// bf16 K/V and bf16 queries: both contractions run on the matrix cores.  Each wave owns 16-row
+// tiles.
+//  * Q·Kᵀ: one v_mfma_f32_16x16x32_bf16 per 32 dims takes A = the tile's K rows (lane l holds
+//    16 bytes of row l%16) and B = the group's query vectors (query l%16), giving every lane the
+//    logits of rows 4(l/16)..+3 for query l%16.  The online softmax runs in that layout.
+//  * P·V: that layout is exactly the A operand of v_mfma_f32_16x16x16_bf16 (query l%16, rows
+//    4(l/16)..+3), so the probabilities feed the matrix core where they are.  P is split into a
+//    bf16 high part (truncation, exact) and a bf16 low part (the rounded remainder): two MFMAs
+//    keep P to about 16 bits, and V is used exactly as stored.  The B operand (4 rows of one V
+//    column per lane) comes from the tile staged row-major in LDS through the transposing read
+//    ds_read_b64_tr_b16: lane s of each 16-lane group points at 4 consecutive columns of one row
+//    and receives, per 16-lane group, the 4x4-transposed elements.
+//  The output accumulates in MFMA layout (lane l: queries 4(l/16)..+3, dim l%16 of each
+//  16-wide chunk).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #ifndef SPK_MFMA_MIN_WAVES
-#define SPK_MFMA_MIN_WAVES 2
+#define SPK_MFMA_MIN_WAVES 3
 #endif
 
 __device__ __forceinline__ void wave_lds_fence() {
@@ -678,25 +688,35 @@ __device__ __forceinline__ void wave_lds_fence() {
 #define SPK_MFMA_BATCH 2
 #endif
 
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 template <int D, int NQ, bool kMask, int MODE>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(NQ <= 4 ? 3 : SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_kernel(AttnArgs a) {
-  constexpr int BATCH = NQ <= 8 ? SPK_MFMA_BATCH : 1;  // tiles in flight per wave
+__attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_kernel(AttnArgs a) {
+  constexpr int BATCH = SPK_MFMA_BATCH;   // tiles in flight per wave
   constexpr int TILE = 16;                // rows per wave per step
   constexpr int STEP = TILE * kWaves;     // rows per workgroup per step
-  constexpr int KCH = D / 32;             // MFMA k-chunks per row
-  constexpr int LPR = D / 8;              // P·V layout: lanes per row
-  constexpr int RPI = kWave / LPR;        // P·V layout: rows per instruction
-  constexpr int PVI = TILE / RPI;         // P·V instructions per tile
+  constexpr int KCH = D / 32;             // Q·K MFMA k-chunks per row
+  constexpr int DCH = D / 16;             // P·V MFMA output chunks (16 dims each)
+  constexpr int LPR = D / 8;              // V load layout: lanes per row (16 bytes each)
+  constexpr int RPI = kWave / LPR;        // V load layout: rows per instruction
+  constexpr int PVI = TILE / RPI;         // V load instructions per tile
+  constexpr int VST = D * 2 + 32;         // LDS row stride of a staged V tile (bytes)
   static_assert(NQ <= 16, "at most 16 query vectors per group");
   static_assert(BATCH <= 4 && 4 * STEP <= kTabPad, "slot table padding covers the last batch");
-  __shared__ float red[kWaves][NQ][D + 2];
+  // the staged V tiles (main loop) and the wave merge area (end) share one LDS block
+  constexpr int kRedBytes = kWaves * NQ * (D + 2) * 4;
+  constexpr int kVtBytes = kWaves * TILE * VST;
+  __shared__ __align__(16) unsigned char work_s[kRedBytes > kVtBytes ? kRedBytes : kVtBytes];
+  auto& red = *reinterpret_cast<float (*)[kWaves][NQ][D + 2]>(work_s);
   __shared__ int seg_start[kMaxIntervals], seg_pos[kMaxIntervals], seg_meta[2];
   extern __shared__ int32_t dyn_s[];
   int32_t* slot_s = dyn_s;
   uint32_t* mask_s = reinterpret_cast<uint32_t*>(dyn_s + a.tab_cap);
-  __shared__ float p_s[kWaves][TILE][16];
-  __shared__ float alpha_s[kWaves][16];
 
   const int g = blockIdx.y;
   const int split = blockIdx.x;
@@ -704,7 +724,7 @@ __attribute__((amdgpu_waves_per_eu(NQ <= 4 ? 3 : SPK_MFMA_MIN_WAVES))) void attn
   const int lrow = a.lrow_is_batch ? b : g;
   const int lane = lane_id(), wid = threadIdx.x / kWave;
   const int qc = lane % 16, rg = lane / 16;      // MFMA layout: query column, row group
-  const int sub = lane % LPR, slot = lane / LPR; // P·V layout
+  const int sub = lane % LPR, slot = lane / LPR; // V load layout
 
   // queries as the MFMA B operand: lane holds Q[query qc][32j + 8rg .. +7]
   bf16x8 qb[KCH];
@@ -744,11 +764,9 @@ __attribute__((amdgpu_waves_per_eu(NQ <= 4 ? 3 : SPK_MFMA_MIN_WAVES))) void attn
                                seg_pos, seg_meta[0]);
 
   float m_q = -INFINITY, l_part = 0.f;  // query qc: running max (wave-uniform), own-row denominator
-  float acc[NQ][8];
+  f32x4 O[DCH];                         // queries 4rg..+3, dims 16c + qc
 #pragma unroll
-  for (int n = 0; n < NQ; ++n)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[n][i] = 0.f;
+  for (int c = 0; c < DCH; ++c) O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
   const uint64_t kcol = (uint64_t)(16 * rg);
@@ -759,6 +777,9 @@ __attribute__((amdgpu_waves_per_eu(NQ <= 4 ? 3 : SPK_MFMA_MIN_WAVES))) void attn
     const int t = qc / a.G, hl = qc % a.G;
     lg_row = ((int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl) * a.logits_ld + r0;
   }
+  unsigned char* vt = work_s + wid * TILE * VST;
+  // transposing read address: row 4rg + (lane%16)/4, columns 4(lane%4)..+3 of each 16-wide chunk
+  const unsigned char* vt_rd = vt + (4 * rg + (lane % 16) / 4) * VST + 8 * (lane % 4);
 
   auto issue = [&](int it, uint4 (&kr)[KCH], uint4 (&vr)[PVI], bool& klive) {
     const int tb = it * STEP + wid * TILE;
@@ -779,6 +800,10 @@ __attribute__((amdgpu_waves_per_eu(NQ <= 4 ? 3 : SPK_MFMA_MIN_WAVES))) void attn
   };
   auto consume = [&](int it, const uint4 (&kr)[KCH], const uint4 (&vr)[PVI], bool klive) {
     const int tb = it * STEP + wid * TILE;
+    // stage the V tile row-major in this wave's LDS slice
+#pragma unroll
+    for (int i = 0; i < PVI; ++i)
+      *reinterpret_cast<uint4*>(vt + (i * RPI + slot) * VST + 16 * sub) = vr[i];
     const uint64_t liveb = __ballot(klive);  // bit r (< 16): row r of the tile is read
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -809,31 +834,32 @@ __attribute__((amdgpu_waves_per_eu(NQ <= 4 ? 3 : SPK_MFMA_MIN_WAVES))) void attn
     for (int i = 0; i < 4; ++i) pv[i] = (sv[i] == -INFINITY) ? 0.f : fast_exp2(sv[i] - m_new);
     l_part = l_part * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
     m_q = m_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p_s[wid][4 * rg + i][qc] = pv[i];
-    if (rg == 0) alpha_s[wid][qc] = alpha;
-    wave_lds_fence();
     if (__ballot(alpha != 1.f)) {
+      // output rows are queries 4rg + i; their scale factors live in lanes 4rg + i
+      float as[4];
 #pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-        const float an = alpha_s[wid][n];
+      for (int i = 0; i < 4; ++i) as[i] = __shfl(alpha, 4 * rg + i, kWave);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[n][i] *= an;
-      }
+      for (int c = 0; c < DCH; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[c][i] *= as[i];
     }
+    // P as two bf16 operands: high = truncated bits (exact), low = rounded remainder
+    i16x4 ph, pl;
 #pragma unroll
-    for (int i = 0; i < PVI; ++i) {
-      const int r = i * RPI + slot;
-      float pr[NQ];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = __float_as_uint(pv[i]);
+      const float hi = __uint_as_float(u & 0xFFFF0000u);
+      ph[i] = (short)(u >> 16);
+      pl[i] = (short)bf16_rne_bits(pv[i] - hi);
+    }
+    wave_lds_fence();
 #pragma unroll
-      for (int n = 0; n < NQ; ++n) pr[n] = p_s[wid][r][n];
-      float y[8];
-      y[0] = bf16_lo(vr[i].x); y[1] = bf16_hi(vr[i].x); y[2] = bf16_lo(vr[i].y); y[3] = bf16_hi(vr[i].y);
-      y[4] = bf16_lo(vr[i].z); y[5] = bf16_hi(vr[i].z); y[6] = bf16_lo(vr[i].w); y[7] = bf16_hi(vr[i].w);
-#pragma unroll
-      for (int n = 0; n < NQ; ++n)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[n][e] = fmaf(pr[n], y[e], acc[n][e]);
+    for (int c = 0; c < DCH; ++c) {
+      const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vt_rd + 32 * c));
+      O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, O[c], 0, 0, 0);
+      O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, O[c], 0, 0, 0);
     }
     wave_lds_fence();
   };
@@ -856,21 +882,17 @@ __attribute__((amdgpu_waves_per_eu(NQ <= 4 ? 3 : SPK_MFMA_MIN_WAVES))) void attn
     }
   }
 
-  // wave totals: denominators over the 4 row groups; P·V partials over the slots (every slot
-  // of the wave was scaled against the same running maxima)
+  // wave totals: denominators over the 4 row groups; the output rows are already complete
   l_part += __shfl_xor(l_part, 16, kWave);
   l_part += __shfl_xor(l_part, 32, kWave);
+  __syncthreads();  // every wave is done with its staged V tiles
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1)
+  for (int i = 0; i < 4; ++i) {
+    const int q = 4 * rg + i;
+    if (q < NQ) {
 #pragma unroll
-    for (int n = 0; n < NQ; ++n)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[n][i] += __shfl_xor(acc[n][i], off, kWave);
-  if (lane < LPR) {
-#pragma unroll
-    for (int n = 0; n < NQ; ++n)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) red[wid][n][2 + sub * 8 + i] = acc[n][i];
+      for (int c = 0; c < DCH; ++c) red[wid][q][2 + 16 * c + qc] = O[c][i];
+    }
   }
   if (rg == 0 && qc < NQ) {
     red[wid][qc][0] = m_q;
