@@ -254,6 +254,7 @@ struct AttnArgs {
   float* acc;
   float* logits;
   int64_t logits_ld;
+  int logits_vec;        // logits rows are 16-byte aligned (base and row stride)
 };
 
 // End of a partial workgroup: merge the 4 waves' (m, l, acc) from `red` and store this split's
@@ -303,16 +304,28 @@ __device__ __forceinline__ int split_rows(int cnt, int smax) {
   return (r + 15) & ~15;
 }
 
-// Byte addresses of a row's K and V from its slot (see resolve_slot).
+// Byte addresses of a row's K and V from its slot (see resolve_slot): one select of base and
+// stride, one 32x32->64-bit multiply-add (row strides are below 4 GiB, checked on the host).
 struct RowBase {
   uint64_t k_hbm, k_host, dv_hbm, dv_host, zero;
-  int64_t sn_hbm, sn_host;  // row strides in bytes
+  uint32_t sn_hbm, sn_host;  // row strides in bytes
 };
-__device__ __forceinline__ void row_addr(const RowBase& rb, int slot, uint64_t& ka, uint64_t& va) {
-  const uint64_t h = rb.k_hbm + (uint64_t)((int64_t)slot * rb.sn_hbm);
-  const uint64_t o = rb.k_host + (uint64_t)((int64_t)(~slot) * rb.sn_host);
-  ka = slot == kDead ? rb.zero : (slot >= 0 ? h : o);
-  va = ka + (slot == kDead ? 0ull : (slot >= 0 ? rb.dv_hbm : rb.dv_host));
+__device__ __forceinline__ void row_addr(RowBase rb, int slot, uint64_t& ka, uint64_t& va) {
+  // selects on values (not on members through a reference, which the compiler may turn into a
+  // select of addresses into private memory)
+  const uint64_t k_hbm = rb.k_hbm, k_host = rb.k_host, zero = rb.zero;
+  const uint64_t dv_hbm = rb.dv_hbm, dv_host = rb.dv_host;
+  const uint32_t sn_hbm = rb.sn_hbm, sn_host = rb.sn_host;
+  const bool hbm = slot >= 0, dead = slot == kDead;
+  const uint32_t idx = hbm ? (uint32_t)slot : (uint32_t)(~slot);
+  uint32_t sn = hbm ? sn_hbm : sn_host;
+  sn = dead ? 0u : sn;
+  uint64_t base = hbm ? k_hbm : k_host;
+  base = dead ? zero : base;
+  uint64_t dv = hbm ? dv_hbm : dv_host;
+  dv = dead ? 0ull : dv;
+  ka = base + (uint64_t)idx * sn;
+  va = ka + dv;
 }
 
 template <typename KT>
@@ -325,8 +338,8 @@ __device__ __forceinline__ RowBase make_row_base(const AttnArgs& a, int b, int k
   rb.dv_hbm = reinterpret_cast<uint64_t>(a.v) - reinterpret_cast<uint64_t>(a.k);
   rb.dv_host = reinterpret_cast<uint64_t>(a.v_host) - reinterpret_cast<uint64_t>(a.k_host);
   rb.zero = reinterpret_cast<uint64_t>(g_zero_row);
-  rb.sn_hbm = a.kv_sn * (int64_t)sizeof(KT);
-  rb.sn_host = a.host_sn * (int64_t)sizeof(KT);
+  rb.sn_hbm = (uint32_t)(a.kv_sn * (int64_t)sizeof(KT));
+  rb.sn_host = (uint32_t)(a.host_sn * (int64_t)sizeof(KT));
   return rb;
 }
 
@@ -798,7 +811,23 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
       vr[i] = gload16(va + vcol);
     }
   };
-  auto consume = [&](int it, const uint4 (&kr)[KCH], const uint4 (&vr)[PVI], bool klive) {
+  // scaled logits of this lane's 4 rows (query qc)
+  auto store_logits = [&](int it, const float (&lg)[4]) {
+    if (a.logits && qc < a.nq) {
+      // rows 4rg..+3 of query qc are 4 consecutive floats: one 16-byte store when aligned
+      const int p0 = it * STEP + wid * TILE + 4 * rg;
+      float* dst = a.logits + lg_row + p0;
+      if (a.logits_vec && p0 + 3 < nrows) {
+        *reinterpret_cast<float4*>(dst) = make_float4(lg[0], lg[1], lg[2], lg[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (p0 + i < nrows) dst[i] = lg[i];
+      }
+    }
+  };
+  auto consume = [&](int it, const uint4 (&kr)[KCH], const uint4 (&vr)[PVI], bool klive,
+                     float (&lgo)[4]) {
     const int tb = it * STEP + wid * TILE;
     // stage the V tile row-major in this wave's LDS slice
 #pragma unroll
@@ -817,13 +846,8 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
       if constexpr (kMask) rd = rd && ((mask_s[tb + r] >> qd) & 1u);
       sv[i] = rd ? S[i] * a.scale_log2 : -INFINITY;
     }
-    if (a.logits && qc < a.nq) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = tb + 4 * rg + i;
-        if (p < nrows) a.logits[lg_row + p] = sv[i] * kLn2;
-      }
-    }
+    for (int i = 0; i < 4; ++i) lgo[i] = sv[i] * kLn2;
     float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
@@ -876,7 +900,9 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < BATCH; ++t) {
-        consume(it + t, kb[t], vb[t], lv[t]);
+        float lg[4];
+        consume(it + t, kb[t], vb[t], lv[t], lg);
+        store_logits(it + t, lg);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1168,6 +1194,8 @@ extern "C" SPK_API spk_status sparse_decode_attn(
   SPK_REQUIRE(kv_sn >= d && kv_sb >= 0 && kv_sh >= 0 && kv_sn % 8 == 0 && kv_sh % 8 == 0 &&
                   kv_sb % 8 == 0,
               SPK_EINVAL, "sparse_decode_attn: kv strides must be multiples of 8 with kv_sn >= d");
+  SPK_REQUIRE(kv_sn * (int64_t)dtype_size(kv_dtype) < (int64_t)1 << 32, SPK_EUNSUPPORTED,
+              "sparse_decode_attn: a KV row stride of 4 GiB or more is not supported");
   SPK_REQUIRE(reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(k) % 16 == 0 &&
                   reinterpret_cast<uintptr_t>(v) % 16 == 0,
               SPK_EINVAL, "sparse_decode_attn: q, k, v must be 16-byte aligned");
@@ -1177,6 +1205,8 @@ extern "C" SPK_API spk_status sparse_decode_attn(
     SPK_REQUIRE(host_sn >= d && host_sb >= 0 && host_sh >= 0 && host_sn % 8 == 0 &&
                     host_sh % 8 == 0 && host_sb % 8 == 0,
                 SPK_EINVAL, "sparse_decode_attn: host strides must be multiples of 8");
+    SPK_REQUIRE(host_sn * (int64_t)dtype_size(kv_dtype) < (int64_t)1 << 32, SPK_EUNSUPPORTED,
+                "sparse_decode_attn: a host row stride of 4 GiB or more is not supported");
     SPK_REQUIRE(reinterpret_cast<uintptr_t>(k_host) % 16 == 0 &&
                     reinterpret_cast<uintptr_t>(v_host) % 16 == 0,
                 SPK_EINVAL, "sparse_decode_attn: host pools must be 16-byte aligned");
@@ -1236,6 +1266,7 @@ extern "C" SPK_API spk_status sparse_decode_attn(
   a.acc = reinterpret_cast<float*>(w + p.off_acc);
   a.logits = logits;
   a.logits_ld = logits_ld;
+  a.logits_vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && logits_ld % 4 == 0;
   a.mask = nullptr;
   a.mask_div = scope == SPK_SEL_PER_KV_HEAD ? G : 1;
 
