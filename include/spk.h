@@ -4,6 +4,7 @@
  * One decode step over a long KV cache reads only a chosen part of it:
  *   sparse_index_score   a compact indexer scores cached keys (or pooled block keys), no softmax
  *   topk_select          exact top-k of each score row, ties to the lowest index
+ *   sparse_index_topk    both of the above in one launch, for short candidate rows
  *   sparse_decode_attn   gathers the chosen K/V rows once per GQA group (HBM or pinned host
  *                        memory) and runs exact softmax attention over them only
  *   importance_accumulate  cumulative attention importance s_i += mean over layers, heads of α[i]
@@ -137,6 +138,36 @@ SPK_API spk_status topk_select_workspace_size(int rows, int n, int k, size_t* by
 SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int rows, int n, int k,
                                int32_t* idx, int64_t idx_ld, int32_t* count,
                                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * sparse_index_topk — sparse_index_score followed by topk_select, in one launch, for short
+ * candidate rows.
+ *
+ * Passages: as for sparse_index_score and topk_select (SparDA, §2 "Indexador de Previsão
+ * Compacto" and "Seleção Esparsa de Lookahead Treinável").  The scores are those
+ * sparse_index_score defines (fp32, possibly differing from it in the last bits, since the
+ * dot products are summed in another order); the selection is exactly topk_select of these
+ * scores (ties to the lowest index, ascending output).
+ *
+ *   mode     TOKEN_GROUP_MEAN, TOKEN_PER_HEAD or BLOCK_POOLED (BLOCK_RAW: SPK_EUNSUPPORTED).
+ *   q, keys, strides, shapes, n_tokens, block_size: as sparse_index_score.
+ *   k        candidates kept per score row (>= 0).
+ *   scores   device fp32 [B,T,Hs,s_ld] or NULL (then not written; s_ld ignored).
+ *   idx      device int32 [B,T,Hs,idx_ld]; entries [0, min(k, n_candidates)) written.
+ *   count    device int32 [B,T,Hs] or NULL; receives min(k, n_candidates).
+ * Limits (SPK_EUNSUPPORTED beyond them; use the two calls instead): at most 4 score vectors
+ * per KV head (T for TOKEN_GROUP_MEAN and BLOCK_POOLED, T*G for TOKEN_PER_HEAD), at most 8192
+ * candidates per row and 16384 scores per KV head.  No workspace.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status sparse_index_topk(spk_index_mode mode,
+                                     const void* q, spk_dtype q_dtype,
+                                     const void* keys, spk_dtype k_dtype,
+                                     int64_t k_sb, int64_t k_sh, int64_t k_sn,
+                                     int B, int T, int Hq, int Hkv, int d,
+                                     int n_tokens, int block_size, int k,
+                                     float* scores, int64_t s_ld,
+                                     int32_t* idx, int64_t idx_ld, int32_t* count,
+                                     void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * sparse_decode_attn — gather the selected K/V rows and run exact attention over them only.

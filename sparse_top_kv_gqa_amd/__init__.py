@@ -32,7 +32,7 @@ SCOPES = {"per_seq": SEL_PER_SEQ, "per_kv_head": SEL_PER_KV_HEAD, "per_q_head": 
 EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_workspace_size",
            "topk_select", "sparse_decode_attn_workspace_size", "sparse_decode_attn",
            "importance_accumulate", "tier_classify_workspace_size", "tier_classify",
-           "spk_set_attn_timing_events")
+           "spk_set_attn_timing_events", "sparse_index_topk")
 
 
 class SpkError(RuntimeError):
@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.tier_classify.argtypes = [P, I64, I, I, I, I, I, I, P, I64, P, I64, P, P, I64, P, SZ, P]
     L.spk_set_attn_timing_events.restype = I
     L.spk_set_attn_timing_events.argtypes = [P, P]
+    L.sparse_index_topk.restype = I
+    L.sparse_index_topk.argtypes = [I, P, I, P, I, I64, I64, I64, I, I, I, I, I, I, I, I, P, I64,
+                                    P, I64, P, P]
     _lib = L
     return L
 
@@ -148,6 +151,49 @@ def sparse_index_score(mode, q: torch.Tensor, keys: torch.Tensor, n_tokens: int,
                                   _ptr(pooled_out), _stream(stream))
     _check(st, "sparse_index_score")
     return scores
+
+
+FUSED_MAX_VECTORS, FUSED_MAX_CAND, FUSED_MAX_SCORES = 4, 8192, 16384
+
+
+def fused_index_topk_ok(mode, T: int, G: int, n_cand: int) -> bool:
+    """Whether sparse_index_topk accepts this shape (else use the two separate calls)."""
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    ns = T * G if m == IDX_TOKEN_PER_HEAD else T
+    return (m != IDX_BLOCK_RAW and ns <= FUSED_MAX_VECTORS and n_cand <= FUSED_MAX_CAND
+            and ns * n_cand <= FUSED_MAX_SCORES)
+
+
+def sparse_index_topk(mode, q: torch.Tensor, keys: torch.Tensor, n_tokens: int, k: int,
+                      block_size: int = 1, Hq: Optional[int] = None,
+                      scores: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                      count: Optional[torch.Tensor] = None, want_scores: bool = False,
+                      stream=None):
+    """Indexer scores and their top-k in one launch (short candidate rows).  Returns
+    (idx int32 [B,T,Hs,min(k,n_cand)] ascending, count int32 [B,T,Hs], scores or None)."""
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    _contig(q, "q")
+    B, T, Hx, d = q.shape
+    Hkv = keys.shape[1]
+    block = m in (IDX_BLOCK_POOLED, IDX_BLOCK_RAW)
+    if Hq is None:
+        Hq = Hkv if block else Hx
+    n_cand = n_tokens // block_size if block else n_tokens
+    Hs = Hq if m == IDX_TOKEN_PER_HEAD else Hkv
+    kk = max(0, min(k, n_cand))
+    if scores is None and want_scores:
+        scores = torch.empty((B, T, Hs, max(n_cand, 1)), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, T, Hs, max(kk, 1)), dtype=torch.int32, device=q.device)
+    if count is None:
+        count = torch.empty((B, T, Hs), dtype=torch.int32, device=q.device)
+    sb, sh, sn = _rows_view(keys, "keys")
+    st = lib().sparse_index_topk(m, _ptr(q), _dt(q), _ptr(keys), _dt(keys), sb, sh, sn, B, T, Hq,
+                                 Hkv, d, n_tokens, block_size, k, _ptr(scores),
+                                 scores.stride(-2) if scores is not None else 0, _ptr(idx),
+                                 idx.stride(-2), _ptr(count), _stream(stream))
+    _check(st, "sparse_index_topk")
+    return idx, count, scores
 
 
 # ----------------------------------------------------------------------------- top-k

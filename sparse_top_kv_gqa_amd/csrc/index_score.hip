@@ -11,7 +11,7 @@
 // the 8-dim slice of every query vector the group scores (NS <= 16 of them) in registers, forms
 // partial dots, and a 16-lane DPP reduction finishes them.  Scores are staged in LDS and written
 // back as contiguous runs per output row.
-#include "spk_internal.h"
+#include "select_common.h"
 
 namespace spk {
 namespace {
@@ -254,6 +254,157 @@ spk_status launch_blockraw(int ns_pad, dim3 grid, hipStream_t st, const void* q,
 
 int pad_ns(int ns) { return ns <= 1 ? 1 : ns <= 4 ? 4 : ns <= 8 ? 8 : 16; }
 
+// ---------------------------------------------------------------- scores + top-k in one launch
+//
+// For short candidate rows (a block indexer's few hundred blocks, or a few thousand tokens) the
+// top-k of a row is worth less than a launch of its own.  One 1024-thread workgroup per (b, kvh)
+// group streams the group's candidate keys once (all of a pass's loads in flight), keeps every
+// score of its score vectors in LDS, then selects each vector's top-k there with the same radix
+// select and index-ordered compaction as topk_select.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedMaxCand = 8192;    // candidates per score row
+constexpr int kFusedLds = 16384;       // score vectors x candidates held in LDS
+constexpr int kFusedItems = kFusedMaxCand / kFusedThreads;
+constexpr int kFusedMaxVectors = 4;    // score vectors per (b, kvh) group
+
+template <int D, typename KT, int NS>
+__global__ __launch_bounds__(kFusedThreads) void index_topk_kernel(
+    int mode, const void* __restrict__ q, int q_bf16, const KT* __restrict__ keys, int64_t k_sb,
+    int64_t k_sh, int64_t k_sn, int T, int Hq, int Hkv, int G, int ns, int n_cand, int k,
+    float* __restrict__ scores, int64_t s_ld, int32_t* __restrict__ idx, int64_t idx_ld,
+    int32_t* __restrict__ count) {
+  constexpr int LPR = D / 8;          // lanes per key row
+  constexpr int RPS = kWave / LPR;    // rows per wave per load
+  constexpr int STEP = kFusedWaves * RPS;
+  constexpr int U = 8;                // loads in flight per lane
+  __shared__ float tile[kFusedLds];   // [ns][n_cand]
+  __shared__ uint32_t hist[kFusedWaves * 256];
+  __shared__ int sh[2];
+  __shared__ int wcnt[kFusedItems][kFusedWaves][2];
+
+  const int group = blockIdx.x;
+  const int b = group / Hkv, kvh = group % Hkv;
+  const int t = threadIdx.x, lane = lane_id(), wid = t / kWave;
+  const int sub = lane % LPR, slot = lane / LPR;
+
+  float qv[NS][8];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    if (n < ns) {
+      query_slice<D>(mode, q, q_bf16, b, kvh, n, T, Hq, Hkv, G, sub, qv[n]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[n][i] = 0.f;
+    }
+  }
+  const KT* base_ptr = keys + (int64_t)b * k_sb + (int64_t)kvh * k_sh + sub * 8;
+  for (int base = 0; base < n_cand; base += STEP * U) {
+    Raw8<KT> raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = base + (u * kFusedWaves + wid) * RPS + slot;
+      if (row < n_cand) raw[u].load(base_ptr + (int64_t)row * k_sn);
+      else raw[u].zero();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = base + (u * kFusedWaves + wid) * RPS + slot;
+      float x[8];
+      raw[u].to_float(x);
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaf(qv[n][i], x[i], a);
+        a = group_sum<LPR>(a);
+        if (row < n_cand && n < ns && n % LPR == sub) tile[n * n_cand + row] = a;
+      }
+    }
+  }
+  __syncthreads();
+  if (scores) {
+    for (int i = t; i < ns * n_cand; i += kFusedThreads) {
+      const int n = i / n_cand, j = i % n_cand;
+      scores[score_row(mode, b, kvh, n, T, Hq, Hkv, G) * s_ld + j] = tile[i];
+    }
+  }
+  const int kk = min(k, n_cand);
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int n = 0; n < ns; ++n) {
+    const int64_t orow = score_row(mode, b, kvh, n, T, Hq, Hkv, G);
+    if (count && t == 0) count[orow] = kk;
+    if (kk <= 0) continue;
+    uint32_t key[kFusedItems];
+#pragma unroll
+    for (int c = 0; c < kFusedItems; ++c) {
+      const int j = c * kFusedThreads + t;
+      key[c] = j < n_cand ? order_key(tile[n * n_cand + j]) : 0u;
+    }
+    uint32_t thr;
+    int need;
+    radix_select<kFusedThreads>(
+        [&](auto visit) {
+#pragma unroll
+          for (int c = 0; c < kFusedItems; ++c)
+            if (c * kFusedThreads + t < n_cand) visit(key[c]);
+        },
+        kk, hist, sh, &thr, &need);
+    // keep every key above thr and the first `need` keys equal to it, in index order
+    uint64_t bg[kFusedItems], be[kFusedItems];
+#pragma unroll
+    for (int c = 0; c < kFusedItems; ++c) {
+      const bool valid = c * kFusedThreads + t < n_cand;
+      bg[c] = __ballot(valid && key[c] > thr);
+      be[c] = __ballot(valid && key[c] == thr);
+      if (lane == 0) {
+        wcnt[c][wid][0] = __popcll(bg[c]);
+        wcnt[c][wid][1] = __popcll(be[c]);
+      }
+    }
+    __syncthreads();
+    int32_t* out = idx + orow * idx_ld;
+    int run_g = 0, run_e = 0;
+#pragma unroll
+    for (int c = 0; c < kFusedItems; ++c) {
+      if (c * kFusedThreads >= n_cand) break;
+      int pre_g = run_g + __popcll(bg[c] & lt), pre_e = run_e + __popcll(be[c] & lt);
+      int tot_g = 0, tot_e = 0;
+      for (int w = 0; w < kFusedWaves; ++w) {
+        const int cg = wcnt[c][w][0], ce = wcnt[c][w][1];
+        if (w < wid) {
+          pre_g += cg;
+          pre_e += ce;
+        }
+        tot_g += cg;
+        tot_e += ce;
+      }
+      const int j = c * kFusedThreads + t;
+      const bool gt = (bg[c] >> lane) & 1ull, eq = (be[c] >> lane) & 1ull;
+      if (gt || (eq && pre_e < need)) out[pre_g + min(pre_e, need)] = j;
+      run_g += tot_g;
+      run_e += tot_e;
+    }
+    __syncthreads();  // wcnt and hist are reused by the next score vector
+  }
+}
+
+template <int D, typename KT>
+spk_status launch_fused(int ns_pad, int groups, hipStream_t st, int mode, const void* q,
+                        int q_bf16, const void* keys, int64_t k_sb, int64_t k_sh, int64_t k_sn,
+                        int T, int Hq, int Hkv, int G, int ns, int n_cand, int k, float* scores,
+                        int64_t s_ld, int32_t* idx, int64_t idx_ld, int32_t* count) {
+  const KT* kp = reinterpret_cast<const KT*>(keys);
+#define SPK_FUSED(NSV)                                                                          \
+  hipLaunchKernelGGL((index_topk_kernel<D, KT, NSV>), dim3(groups), dim3(kFusedThreads), 0, st, \
+                     mode, q, q_bf16, kp, k_sb, k_sh, k_sn, T, Hq, Hkv, G, ns, n_cand, k, scores,  \
+                     s_ld, idx, idx_ld, count)
+  if (ns_pad == 1) SPK_FUSED(1);
+  else SPK_FUSED(4);
+#undef SPK_FUSED
+  return check_launch("sparse_index_topk");
+}
+
 // Rows per workgroup: enough workgroups to fill the chip several times over, within 16..256.
 int pick_rows_per_wg(int64_t rows_total, int step) {
   const int64_t target_wgs = 4LL * num_cus();
@@ -332,4 +483,66 @@ extern "C" SPK_API spk_status sparse_index_score(spk_index_mode mode, const void
                                          Hkv, G, ns, n_cand, rpw, scores, s_ld)
              : launch_rows<64, float>(ns_pad, grid, st, mode, q, q_bf16, keys, k_sb, k_sh, k_sn, T, Hq,
                                       Hkv, G, ns, n_cand, rpw, scores, s_ld);
+}
+
+extern "C" SPK_API spk_status sparse_index_topk(spk_index_mode mode, const void* q,
+                                                spk_dtype q_dtype, const void* keys,
+                                                spk_dtype k_dtype, int64_t k_sb, int64_t k_sh,
+                                                int64_t k_sn, int B, int T, int Hq, int Hkv,
+                                                int d, int n_tokens, int block_size, int k,
+                                                float* scores, int64_t s_ld, int32_t* idx,
+                                                int64_t idx_ld, int32_t* count, void* stream) {
+  using namespace spk;
+  SPK_REQUIRE(mode >= SPK_IDX_TOKEN_GROUP_MEAN && mode <= SPK_IDX_BLOCK_RAW, SPK_EINVAL,
+              "sparse_index_topk: unknown mode %d", (int)mode);
+  SPK_REQUIRE(mode != SPK_IDX_BLOCK_RAW, SPK_EUNSUPPORTED,
+              "sparse_index_topk: BLOCK_RAW is not fused (pool the keys first)");
+  SPK_REQUIRE(q && keys, SPK_EINVAL, "sparse_index_topk: null q or keys");
+  SPK_REQUIRE(B > 0 && T > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0, SPK_EINVAL,
+              "sparse_index_topk: bad heads/batch B=%d T=%d Hq=%d Hkv=%d", B, T, Hq, Hkv);
+  SPK_REQUIRE(dtype_ok(q_dtype) && dtype_ok(k_dtype), SPK_EUNSUPPORTED,
+              "sparse_index_topk: unsupported dtype");
+  SPK_REQUIRE(d == 64 || d == 128, SPK_EUNSUPPORTED, "sparse_index_topk: d=%d not in {64,128}", d);
+  SPK_REQUIRE(n_tokens >= 0 && k >= 0, SPK_EINVAL, "sparse_index_topk: n_tokens or k < 0");
+  const bool block = mode == SPK_IDX_BLOCK_POOLED;
+  SPK_REQUIRE(!block || block_size >= 1, SPK_EINVAL, "sparse_index_topk: block_size < 1");
+  SPK_REQUIRE(k_sn >= d && k_sb >= 0 && k_sh >= 0 && k_sn % 8 == 0 && k_sh % 8 == 0 && k_sb % 8 == 0,
+              SPK_EINVAL, "sparse_index_topk: key strides must be multiples of 8 with k_sn >= d");
+  SPK_REQUIRE(reinterpret_cast<uintptr_t>(keys) % 16 == 0 && reinterpret_cast<uintptr_t>(q) % 16 == 0,
+              SPK_EINVAL, "sparse_index_topk: q and keys must be 16-byte aligned");
+  const int G = Hq / Hkv;
+  const int ns = mode == SPK_IDX_TOKEN_PER_HEAD ? T * G : T;
+  const int n_cand = block ? n_tokens / block_size : n_tokens;
+  SPK_REQUIRE(ns <= kFusedMaxVectors && n_cand <= kFusedMaxCand &&
+                  (int64_t)ns * n_cand <= kFusedLds,
+              SPK_EUNSUPPORTED,
+              "sparse_index_topk: %d score vectors x %d candidates per KV head exceed the fused "
+              "limits (%d vectors, %d candidates, %d scores); use sparse_index_score + "
+              "topk_select",
+              ns, n_cand, kFusedMaxVectors, kFusedMaxCand, kFusedLds);
+  SPK_REQUIRE(scores == nullptr || s_ld >= n_cand, SPK_EINVAL,
+              "sparse_index_topk: s_ld %lld < candidates %d", (long long)s_ld, n_cand);
+  const int kk = k < n_cand ? k : n_cand;
+  SPK_REQUIRE(kk == 0 || (idx && idx_ld >= kk), SPK_EINVAL,
+              "sparse_index_topk: null idx or idx_ld %lld < min(k, candidates) %d",
+              (long long)idx_ld, kk);
+  clear_error();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int q_bf16 = q_dtype == SPK_BF16;
+  const int ns_pad = pad_ns(ns);
+  const int groups = B * Hkv;
+  if (d == 128)
+    return k_dtype == SPK_BF16
+               ? launch_fused<128, uint16_t>(ns_pad, groups, st, mode, q, q_bf16, keys, k_sb, k_sh,
+                                             k_sn, T, Hq, Hkv, G, ns, n_cand, k, scores, s_ld, idx,
+                                             idx_ld, count)
+               : launch_fused<128, float>(ns_pad, groups, st, mode, q, q_bf16, keys, k_sb, k_sh, k_sn,
+                                          T, Hq, Hkv, G, ns, n_cand, k, scores, s_ld, idx, idx_ld,
+                                          count);
+  return k_dtype == SPK_BF16
+             ? launch_fused<64, uint16_t>(ns_pad, groups, st, mode, q, q_bf16, keys, k_sb, k_sh, k_sn,
+                                          T, Hq, Hkv, G, ns, n_cand, k, scores, s_ld, idx, idx_ld,
+                                          count)
+             : launch_fused<64, float>(ns_pad, groups, st, mode, q, q_bf16, keys, k_sb, k_sh, k_sn, T,
+                                       Hq, Hkv, G, ns, n_cand, k, scores, s_ld, idx, idx_ld, count);
 }

@@ -17,15 +17,17 @@ from typing import List, Optional, Sequence
 
 import torch
 
-from . import (attn_workspace_size, sparse_decode_attn, sparse_index_score, topk_select,
-               topk_workspace_size, importance_accumulate, tier_classify)
+from . import (attn_workspace_size, fused_index_topk_ok, sparse_decode_attn, sparse_index_score,
+               sparse_index_topk, topk_select, topk_workspace_size, importance_accumulate,
+               tier_classify)
 
 
 class BlockSparseDecode:
     """One layer's block-sparse decode step over a KV cache ``[B, Hkv, Ncap, d]``."""
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, n_tokens: int, Hq: int, block_size: int,
-                 k_blocks: int, n_sink: int, n_recent: int, sm_scale: Optional[float] = None):
+                 k_blocks: int, n_sink: int, n_recent: int, sm_scale: Optional[float] = None,
+                 fused: bool = False):
         self.k, self.v = k, v
         B, Hkv, _, d = k.shape
         self.B, self.Hkv, self.Hq, self.d = B, Hkv, Hq, d
@@ -33,6 +35,10 @@ class BlockSparseDecode:
         self.n_sink, self.n_recent = n_sink, n_recent
         self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
         self.nb = n_tokens // block_size
+        # fused=True: scoring and top-k in one launch (one workgroup per KV group; it pays off
+        # when there are many groups with short rows, and loses to the two calls when a few
+        # dozen groups leave most of the chip idle)
+        self.fused = fused and fused_index_topk_ok("block_pooled", 1, 1, self.nb)
         dev = k.device
         self.kpool = torch.empty((B, Hkv, self.nb, d), dtype=torch.float32, device=dev)
         self.scores = torch.empty((B, 1, Hkv, self.nb), dtype=torch.float32, device=dev)
@@ -52,9 +58,13 @@ class BlockSparseDecode:
                            pooled_out=self.kpool)
 
     def step(self, q: torch.Tensor, pred: torch.Tensor):
-        sparse_index_score("block_pooled", pred, self.kpool, self.n_tokens, self.bs,
-                           scores=self.scores)
-        topk_select(self.scores, self.kb, idx=self.idx, count=self.count)
+        if self.fused:
+            sparse_index_topk("block_pooled", pred, self.kpool, self.n_tokens, self.kb, self.bs,
+                              scores=self.scores, idx=self.idx, count=self.count)
+        else:
+            sparse_index_score("block_pooled", pred, self.kpool, self.n_tokens, self.bs,
+                               scores=self.scores)
+            topk_select(self.scores, self.kb, idx=self.idx, count=self.count)
         sparse_decode_attn(q, self.k, self.v, self.idx, self.count, "per_kv_head", self.n_tokens,
                            gran=self.bs, n_sink=self.n_sink, n_recent=self.n_recent,
                            sm_scale=self.sm_scale, out=self.out, lse=self.lse, ws=self.ws)

@@ -138,3 +138,34 @@ def test_timing_hook_validation():
     assert L.spk_set_attn_timing_events(ctypes.c_void_p(1), None) == 1
     assert "both" in L.spk_last_error().decode()
     assert L.spk_set_attn_timing_events(None, None) == 0
+
+
+def test_index_topk_validation():
+    L = spk.lib()
+    P = ctypes.c_void_p
+    q = P(16)
+    keys = P(32)
+    idx = P(48)
+    # BLOCK_RAW is not fused
+    st = L.sparse_index_topk(3, q, 0, keys, 0, 64 * 128, 128, 128, 1, 1, 4, 1, 128, 4096, 64, 8,
+                             None, 0, idx, 8, None, None)
+    assert st == 2 and "BLOCK_RAW" in L.spk_last_error().decode()
+    # too many candidates per row
+    st = L.sparse_index_topk(0, q, 0, keys, 0, 1 << 24, 1 << 22, 128, 1, 1, 4, 1, 128, 9000, 1,
+                             8, None, 0, idx, 8, None, None)
+    assert st == 2
+    # too many score vectors (per-head with G = 8)
+    st = L.sparse_index_topk(1, q, 0, keys, 0, 1 << 20, 1 << 18, 128, 1, 1, 8, 1, 128, 1000, 1,
+                             8, None, 0, idx, 8, None, None)
+    assert st == 2
+    # idx_ld smaller than min(k, candidates)
+    st = L.sparse_index_topk(0, q, 0, keys, 0, 1 << 20, 1 << 18, 128, 1, 1, 4, 1, 128, 1000, 1,
+                             8, None, 0, idx, 4, None, None)
+    assert st == 1
+    # null idx with k > 0
+    st = L.sparse_index_topk(0, q, 0, keys, 0, 1 << 20, 1 << 18, 128, 1, 1, 4, 1, 128, 1000, 1,
+                             8, None, 0, None, 8, None, None)
+    assert st == 1
+    assert spk.fused_index_topk_ok("block_pooled", 1, 4, 512)
+    assert not spk.fused_index_topk_ok("token_per_head", 1, 8, 512)
+    assert not spk.fused_index_topk_ok("token_group_mean", 1, 4, 131072)

@@ -543,3 +543,93 @@ def test_tiered_full_size_sampled_steps():
             check_rows(dec.s[b, :n].cpu().numpy()[None], r["s"][None], what="importance")
     del caches, dec
     _free()
+
+
+# ------------------------------------------------------------------------------------ fused index + top-k
+
+@pytest.mark.parametrize("case", ["block", "block_d64_f32", "group_mean", "per_head", "ties"])
+def test_index_topk_fused(case):
+    say("index-topk", case)
+    if case.startswith("block"):
+        d = 64 if "d64" in case else 128
+        w = W.scaled(W.LLAMA8B_BLOCK, B=2, Hkv=2, Hq=8, d=d, N=64 * 300 + 17, k=9)
+        pred = W.predictors(w, device=DEV)
+        keys = W.kv_cache(w, "k", device=DEV)
+        pool = torch.empty((w.B, w.Hkv, w.N // 64, w.d), dtype=torch.float32, device=DEV)
+        spk.sparse_index_score("block_raw", pred, keys, w.N, 64, pooled_out=pool)
+        kp = pool if "f32" in case else pool.to(torch.bfloat16)
+        idx, cnt, sc = spk.sparse_index_topk("block_pooled", pred, kp, w.N, w.k, 64, want_scores=True)
+        torch.cuda.synchronize()
+        nb = w.N // 64
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                ref = oracle.scores_block(host(pred)[b, 0, h], host(kp[b, h]))
+                gs = sc[b, 0, h, :nb].cpu().numpy()
+                check_rows(gs, ref, what="fused block scores")
+                assert idx[b, 0, h].cpu().numpy().tolist() == oracle.topk(gs, w.k).tolist()
+                assert osteps.topk_band_ok(idx[b, 0, h].cpu().numpy(), ref, w.k, TOL)
+                assert int(cnt[b, 0, h]) == w.k
+        return
+    if case == "ties":
+        # every key identical: all scores equal, the lowest indices win
+        w = W.scaled(W.TINY, B=2, Hkv=2, Hq=8, N=700)
+        q = W.queries(w, device=DEV)
+        keys = W.kv_cache(w, "k", device=DEV)
+        keys[:] = keys[:, :, :1]
+        for k in (0, 1, 37, 700, 900):
+            idx, cnt, sc = spk.sparse_index_topk("token_group_mean", q, keys, w.N, k)
+            torch.cuda.synchronize()
+            kk = min(k, w.N)
+            assert cnt.cpu().flatten().tolist() == [kk] * (w.B * w.Hkv)
+            for b in range(w.B):
+                for h in range(w.Hkv):
+                    assert idx[b, 0, h, :kk].cpu().tolist() == list(range(kk))
+        return
+    mode = "token_group_mean" if case == "group_mean" else "token_per_head"
+    G = 4
+    w = W.scaled(W.PER_HEAD_2PCT, B=2, Hkv=2, Hq=2 * G, N=3001, k=97)
+    q = W.queries(w, device=DEV)
+    keys = W.kv_cache(w, "k", device=DEV)
+    idx, cnt, sc = spk.sparse_index_topk(mode, q, keys, w.N, w.k, want_scores=True)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            qg = host(q)[b, 0, h * G:(h + 1) * G]
+            kh = host(keys[b, h])
+            if mode == "token_group_mean":
+                refs = [(h, oracle.scores_token_group_mean(qg, kh))]
+            else:
+                ph = oracle.scores_token_per_head(qg, kh)
+                refs = [(h * G + j, ph[j]) for j in range(G)]
+            for row, ref in refs:
+                gs = sc[b, 0, row].cpu().numpy()
+                check_rows(gs, ref, what="fused token scores")
+                sel = idx[b, 0, row].cpu().numpy()
+                assert sel.tolist() == oracle.topk(gs, w.k).tolist()
+                assert osteps.topk_band_ok(sel, ref, w.k, TOL)
+
+
+def test_block_decode_fused_and_separate_paths_agree():
+    """The fused scoring+selection and the two-call path select the same blocks (up to score
+    rounding in near-ties, checked against the oracle) and give the same attention."""
+    w = W.scaled(W.LLAMA8B_BLOCK, B=2, Hkv=2, Hq=8, N=64 * 200 + 5, k=12)
+    say("block-fused-vs-separate")
+    q = W.queries(w, device=DEV)
+    pred = W.predictors(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    outs = []
+    for fused in (True, False):
+        dec = BlockSparseDecode(k, v, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent,
+                                fused=fused)
+        assert dec.fused == fused
+        dec.pool(pred)
+        out, lse = dec.step(q, pred)
+        torch.cuda.synchronize()
+        sc = dec.scores.cpu().numpy()
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                assert dec.idx[b, 0, h].cpu().numpy().tolist() == oracle.topk(sc[b, 0, h], w.k).tolist()
+        outs.append((dec.idx.clone(), out.clone()))
+    if torch.equal(outs[0][0], outs[1][0]):
+        assert torch.equal(outs[0][1], outs[1][1])
