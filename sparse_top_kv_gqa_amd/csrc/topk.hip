@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
   int32_t* myidx = lidx + wid * kListPerWave;
   int nl = 0;
   if (!overflow) {
-    constexpr int UB = 4;
+    constexpr int UB = 8;
     for (int c0 = sbeg; c0 < send; c0 += 256 * UB) {
       uint4 kq[UB];
 #pragma unroll
@@ -236,25 +236,16 @@ __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
         const int i = c0 + 256 * u + 4 * lane;
         const uint32_t kv[4] = {kq[u].x, kq[u].y, kq[u].z, kq[u].w};
         bool take[4];
-        int tk = 0;
+        int before = 0, tot = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           take[j] = i + j < send && (kv[j] >> kBinShift) >= bstar;
-          tk += take[j];
+          // index order is lane, then j: this lane's entries follow every entry of lower lanes
+          const uint64_t bj = __ballot(take[j]);
+          before += __popcll(bj & lt);
+          tot += __popcll(bj);
         }
-        // this lane's entries go after those of lower lanes (index order: lane, then j)
-        uint64_t any = __ballot(tk > 0);
-        if (any) {
-          int before = 0;
-          // prefix of tk over lower lanes
-          int incl = tk;
-#pragma unroll
-          for (int o = 1; o < kWave; o <<= 1) {
-            const int y = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += y;
-          }
-          before = incl - tk;
-          const int tot = __shfl(incl, kWave - 1, kWave);
+        if (tot > 0) {
           if (nl + tot <= kListPerWave) {
             int p = nl + before;
 #pragma unroll

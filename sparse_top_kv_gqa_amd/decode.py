@@ -57,7 +57,8 @@ class BlockSparseDecode:
         sparse_index_score("block_raw", pred, self.k, self.n_tokens, self.bs, scores=self.scores,
                            pooled_out=self.kpool)
 
-    def step(self, q: torch.Tensor, pred: torch.Tensor):
+    def select(self, pred: torch.Tensor):
+        """Predictor scores of the pooled blocks -> the top-k blocks (idx, count)."""
         if self.fused:
             sparse_index_topk("block_pooled", pred, self.kpool, self.n_tokens, self.kb, self.bs,
                               scores=self.scores, idx=self.idx, count=self.count)
@@ -65,10 +66,17 @@ class BlockSparseDecode:
             sparse_index_score("block_pooled", pred, self.kpool, self.n_tokens, self.bs,
                                scores=self.scores)
             topk_select(self.scores, self.kb, idx=self.idx, count=self.count)
+
+    def attend(self, q: torch.Tensor):
+        """Attention over the selected blocks, the sinks and the recent window."""
         sparse_decode_attn(q, self.k, self.v, self.idx, self.count, "per_kv_head", self.n_tokens,
                            gran=self.bs, n_sink=self.n_sink, n_recent=self.n_recent,
                            sm_scale=self.sm_scale, out=self.out, lse=self.lse, ws=self.ws)
         return self.out, self.lse
+
+    def step(self, q: torch.Tensor, pred: torch.Tensor):
+        self.select(pred)
+        return self.attend(q)
 
 
 class TokenSparseDecode:
