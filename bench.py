@@ -198,16 +198,16 @@ def base_result(w, K, W, ms_step, step_bytes, config):
 # Bytes the roofline kernel of each workload moves per launch, from two rocprofv3 --pmc runs of
 # this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over the dispatches of the
 # timed kernel loop).  Each counter is scaled by what it reads for a plain 512 MiB device copy
-# in the same runs (FETCH_SIZE 262162 KiB -> x2.0, WRITE_SIZE 524288 KiB -> x1.0).  A reading
+# in the same runs (FETCH_SIZE 262167 KiB -> x2.0, WRITE_SIZE 524288 KiB -> x1.0).  A reading
 # belongs to the kernel sources it was taken on (digest of the files listed): once they change
 # it is reported as null until the counters are taken again.
 COPY_KIB = 512 * 1024
-FETCH_COPY_KIB, WRITE_COPY_KIB = 262162.0, 524288.0
+FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
-    "block": (("attn.hip", "spk_internal.h"), "a347420eb0e8bed5", 40852.5, 1370.56),
-    "per_head": (("index_score.hip", "spk_internal.h"), "1a4452095e53323b", 524479.0, 65536.0),
-    "spec_verify": (("attn.hip", "spk_internal.h"), "a347420eb0e8bed5", 271033.0, 7232.0),
-    "tiers": (("attn.hip", "spk_internal.h"), "a347420eb0e8bed5", 399093.0, 50154.2),
+    "block": (("attn.hip", "spk_internal.h"), "c3590a1e8f458ed4", 40859.1, 1432.0),
+    "per_head": (("index_score.hip", "spk_internal.h"), "788931a87b7f8e45", 524476.0, 65536.0),
+    "spec_verify": (("attn.hip", "spk_internal.h"), "c3590a1e8f458ed4", 271809.0, 8545.0),
+    "tiers": (("attn.hip", "spk_internal.h"), "c3590a1e8f458ed4", 401312.0, 51483.4),
 }
 
 

@@ -213,6 +213,7 @@ SPK_API spk_status sparse_index_topk(spk_index_mode mode,
  *
  * The fetch-list bound per group is min(n_tokens, sets*sel_ld*gran + n_sink + n_recent) with
  * sets = 1 (PER_SEQ), T (PER_KV_HEAD) or T*G (PER_Q_HEAD); at most 32 sets per group.
+ * A KV or host-pool row stride of 4 GiB or more returns SPK_EUNSUPPORTED.
  * ------------------------------------------------------------------------------------------ */
 SPK_API spk_status sparse_decode_attn_workspace_size(spk_sel_scope scope, int B, int T, int Hq,
                                                      int Hkv, int d, int n_tokens, int64_t sel_ld,
