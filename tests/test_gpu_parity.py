@@ -633,3 +633,151 @@ def test_block_decode_fused_and_separate_paths_agree():
         outs.append((dec.idx.clone(), out.clone()))
     if torch.equal(outs[0][0], outs[1][0]):
         assert torch.equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------------------------------------------------ attention paths
+
+def _rand(shape, dtype, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g).to(dtype).to(DEV)
+
+
+def _sorted_sets(rows, n, k, seed):
+    r = np.random.default_rng(seed)
+    return np.stack([np.sort(r.choice(n, size=k, replace=False)) for _ in range(rows)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("qdt,kvdt", [("bf16", "bf16"), ("f32", "bf16"), ("f32", "f32")])
+def test_attention_kernel_paths(d, qdt, kvdt):
+    """bf16 q + bf16 K/V run the matrix-core kernel; fp32 queries or fp32 K/V the VALU kernel;
+    both head dims; token lists per (b, kvh) with one set per group (direct list)."""
+    say("attn-paths", d, qdt, kvdt)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    B, T, Hq, Hkv, N, k = 2, 1, 8, 2, 3000, 700
+    G = Hq // Hkv
+    q = _rand((B, T, Hq, d), dt[qdt], 11 + d)
+    kc = _rand((B, Hkv, N, d), dt[kvdt], 12 + d)
+    vc = _rand((B, Hkv, N, d), dt[kvdt], 13 + d)
+    sel = _sorted_sets(B * T * Hkv, N, k, 14)
+    cnt = np.full(B * T * Hkv, k, np.int32)
+    cnt[1] = 333                                   # a ragged list
+    selt = torch.tensor(sel.reshape(B, T, Hkv, k), device=DEV)
+    cntt = torch.tensor(cnt.reshape(B, T, Hkv), device=DEV)
+    out, lse = spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_kv_head", N)
+    torch.cuda.synchronize()
+    scale = oracle.softmax_scale(d)
+    for b in range(B):
+        for h in range(Hkv):
+            r = (b * T) * Hkv + h
+            toks = sel[r, :cnt[r]]
+            o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], host(kc[b, h])[toks],
+                                            host(vc[b, h])[toks], scale)
+            check_rows(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="attention")
+            np.testing.assert_allclose(lse[b, 0, h * G:(h + 1) * G].cpu().numpy(), l_ref, rtol=TOL)
+
+
+def test_long_block_list_with_forced_rows_uses_assembly():
+    """More block ids than the in-kernel interval expansion holds (> 62): the union of blocks,
+    sinks and recent window is assembled first."""
+    say("long-block-list")
+    B, Hq, Hkv, d, N, gran, nb_sel = 2, 8, 2, 128, 16 * 400 + 9, 16, 150
+    G = Hq // Hkv
+    q = _rand((B, 1, Hq, d), torch.bfloat16, 21)
+    kc = _rand((B, Hkv, N, d), torch.bfloat16, 22)
+    vc = _rand((B, Hkv, N, d), torch.bfloat16, 23)
+    sel = _sorted_sets(B * Hkv, N // gran, nb_sel, 24)
+    selt = torch.tensor(sel.reshape(B, 1, Hkv, nb_sel), device=DEV)
+    cntt = torch.full((B, 1, Hkv), nb_sel, dtype=torch.int32, device=DEV)
+    out, lse = spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_kv_head", N, gran=gran,
+                                      n_sink=4, n_recent=100)
+    torch.cuda.synchronize()
+    scale = oracle.softmax_scale(d)
+    for b in range(B):
+        for h in range(Hkv):
+            toks = oracle.selection_tokens(sel[b * Hkv + h], gran, N, 4, 100)
+            o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], host(kc[b, h])[toks],
+                                            host(vc[b, h])[toks], scale)
+            check_rows(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="assembled union")
+
+
+def test_block_intervals_logits_follow_union_order():
+    """Scaled logits come back at each row's position in the ascending union of blocks, sinks
+    and recent window."""
+    say("block-logits")
+    B, Hq, Hkv, d, N, gran, nb_sel = 2, 8, 2, 128, 64 * 90 + 21, 64, 12
+    G = Hq // Hkv
+    q = _rand((B, 1, Hq, d), torch.bfloat16, 31)
+    kc = _rand((B, Hkv, N, d), torch.bfloat16, 32)
+    vc = _rand((B, Hkv, N, d), torch.bfloat16, 33)
+    sel = _sorted_sets(B * Hkv, N // gran, nb_sel, 34)
+    # row 0 selects block 0 (overlaps the sinks) and the last complete block (overlaps the
+    # recent window)
+    r = np.random.default_rng(35)
+    mid = np.sort(r.choice(np.arange(1, N // gran - 1), size=nb_sel - 2, replace=False))
+    sel[0] = np.concatenate([[0], mid, [N // gran - 1]]).astype(np.int32)
+    selt = torch.tensor(sel.reshape(B, 1, Hkv, nb_sel), device=DEV)
+    cntt = torch.full((B, 1, Hkv), nb_sel, dtype=torch.int32, device=DEV)
+    ub = spk.fetch_list_bound("per_kv_head", 1, G, nb_sel, gran, 4, 256, N)
+    logits = torch.full((B, 1, Hq, ub + 8), 123.0, device=DEV)
+    out, lse = spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_kv_head", N, gran=gran,
+                                      n_sink=4, n_recent=256, logits=logits)
+    torch.cuda.synchronize()
+    scale = oracle.softmax_scale(d)
+    for b in range(B):
+        for h in range(Hkv):
+            toks = oracle.selection_tokens(sel[b * Hkv + h], gran, N, 4, 256)
+            o_ref, l_ref, lg_ref = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G],
+                                                 host(kc[b, h])[toks], host(vc[b, h])[toks], scale)
+            check_rows(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="block attention")
+            lg = logits[b, 0, h * G:(h + 1) * G, :len(toks)].cpu().numpy()
+            check_rows(lg, lg_ref, what="logits in union order")
+
+
+def test_per_seq_host_rows_with_logits_bit_identical():
+    """Tiered-style call (one list per sequence, logits written) with a third of the rows in
+    pinned host memory: outputs, lse and logits are bit-identical to the all-HBM call."""
+    say("per-seq-host-logits")
+    B, Hq, Hkv, d, N, k = 3, 28, 4, 128, 2500, 900
+    q = _rand((B, 1, Hq, d), torch.bfloat16, 41)
+    kc = _rand((B, Hkv, N, d), torch.bfloat16, 42)
+    vc = _rand((B, Hkv, N, d), torch.bfloat16, 43)
+    sel = _sorted_sets(B, N, k, 44)
+    selt = torch.tensor(sel, device=DEV)
+    cntt = torch.tensor([k, 700, k], dtype=torch.int32, device=DEV)
+    lg_a = torch.empty((B, 1, Hq, k), device=DEV)
+    lg_b = torch.empty((B, 1, Hq, k), device=DEV)
+    o_a, l_a = spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_seq", N, logits=lg_a)
+    # a seeded third of every group's rows move to pinned host memory
+    r = np.random.default_rng(45)
+    n_host = N // 3
+    loc = torch.arange(N, dtype=torch.int32).repeat(B, Hkv, 1)
+    kh = torch.empty((B, Hkv, n_host, d), dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty((B, Hkv, n_host, d), dtype=torch.bfloat16, pin_memory=True)
+    k2, v2 = kc.clone(), vc.clone()
+    for b in range(B):
+        for h in range(Hkv):
+            rows = torch.tensor(np.sort(r.choice(N, n_host, replace=False)))
+            kh[b, h].copy_(kc[b, h, rows.to(DEV)].cpu())
+            vh[b, h].copy_(vc[b, h, rows.to(DEV)].cpu())
+            loc[b, h, rows] = ~torch.arange(n_host, dtype=torch.int32)
+            k2[b, h, rows.to(DEV)] = float("nan")
+            v2[b, h, rows.to(DEV)] = float("nan")
+    o_b, l_b = spk.sparse_decode_attn(q, k2, v2, selt, cntt, "per_seq", N, k_host=kh, v_host=vh,
+                                      loc=loc.to(DEV), logits=lg_b)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+    for b in range(B):
+        c = int(cntt[b])
+        assert torch.equal(lg_a[b, ..., :c], lg_b[b, ..., :c])
+    scale = oracle.softmax_scale(d)
+    G = Hq // Hkv
+    for b in range(B):
+        c = int(cntt[b])
+        for h in range(Hkv):
+            toks = sel[b, :c]
+            o_ref, l_ref, lg_ref = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G],
+                                                 host(kc[b, h])[toks], host(vc[b, h])[toks], scale)
+            check_rows(o_a[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="per-seq attention")
+            check_rows(lg_a[b, 0, h * G:(h + 1) * G, :c].cpu().numpy(), lg_ref, what="per-seq logits")
