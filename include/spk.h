@@ -5,6 +5,7 @@
  *   sparse_index_score   a compact indexer scores cached keys (or pooled block keys), no softmax
  *   topk_select          exact top-k of each score row, ties to the lowest index
  *   sparse_index_topk    both of the above in one launch, for short candidate rows
+ *   sparse_topk_decode_attn  top-k of a score row and the attention over it, in one launch
  *   sparse_decode_attn   gathers the chosen K/V rows once per GQA group (HBM or pinned host
  *                        memory) and runs exact softmax attention over them only
  *   importance_accumulate  cumulative attention importance s_i += mean over layers, heads of α[i]
@@ -200,7 +201,8 @@ SPK_API spk_status sparse_index_topk(spk_index_mode mode,
  *              v_host).  A slot outside its pool is treated as a missing row (not read).
  *              NULL: every token is HBM slot tok.
  *   sel_idx    device int32 [rows, sel_ld], strictly ascending entries (as topk_select and
- *              tier_classify write them); sel_count device int32 [rows] (clamped to sel_ld).
+ *              tier_classify write them; may be NULL when sel_ld is 0); sel_count device int32
+ *              [rows] (clamped to sel_ld).
  *   gran       1 for token ids, or the block size for block ids.
  *   out        device fp32 [B,T,Hq,d].  lse: device fp32 [B,T,Hq] or NULL.
  *   logits     device fp32 [B,T,Hq,logits_ld] or NULL: the scaled logit sm_scale·q·k of every
@@ -234,6 +236,39 @@ SPK_API spk_status sparse_decode_attn(const void* q, spk_dtype q_dtype,
                                       float sm_scale,
                                       float* out, float* lse, float* logits, int64_t logits_ld,
                                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * sparse_topk_decode_attn — topk_select of one score row per (b, kvh) group followed by
+ * sparse_decode_attn over the selected ids, in the attention's own launch.
+ *
+ * Passages: as for topk_select and sparse_decode_attn (SparDA, §2 "Seleção Esparsa de Lookahead
+ * Treinável": the predictor's top-k blocks are the ones attention reads).  The selection is
+ * exactly topk_select of the score row (ties to the lowest index); the attention is exactly
+ * sparse_decode_attn with scope PER_KV_HEAD and T = 1 over that selection, with the same
+ * `gran`, sinks and recent window, so out and lse are bit-identical to the two calls.
+ *
+ *   scores   device fp32, row (b*Hkv + kvh) at scores + row*s_ld, entries [0, n_cand) read.
+ *   k        ids kept per row (0 <= k <= 62).  n_cand <= 4096.
+ *   q, kc, vc, strides, gran, n_sink, n_recent, shapes, n_tokens, sm_scale, out, lse: as
+ *            sparse_decode_attn with T = 1 (bf16 q and caches only; no host pools).
+ *   sel_idx  device int32 [B*Hkv, sel_ld] or NULL: receives the ascending selection.
+ *   sel_count device int32 [B*Hkv] or NULL: receives min(k, n_cand).
+ *   ws       device workspace of sparse_topk_decode_attn_workspace_size() bytes.
+ * SPK_EUNSUPPORTED for other dtypes, n_cand > 4096 or k > 62.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status sparse_topk_decode_attn_workspace_size(int B, int Hq, int Hkv, int d,
+                                                          int n_tokens, int n_cand, int k,
+                                                          int gran, int n_sink, int n_recent,
+                                                          size_t* bytes);
+SPK_API spk_status sparse_topk_decode_attn(const float* scores, int64_t s_ld, int n_cand, int k,
+                                           const void* q, spk_dtype q_dtype,
+                                           const void* kc, const void* vc, spk_dtype kv_dtype,
+                                           int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                                           int gran, int n_sink, int n_recent,
+                                           int B, int Hq, int Hkv, int d, int n_tokens,
+                                           float sm_scale, float* out, float* lse,
+                                           int32_t* sel_idx, int32_t* sel_count, int64_t sel_ld,
+                                           void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * importance_accumulate — cumulative attention importance, one decode step.

@@ -32,7 +32,8 @@ SCOPES = {"per_seq": SEL_PER_SEQ, "per_kv_head": SEL_PER_KV_HEAD, "per_q_head": 
 EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_workspace_size",
            "topk_select", "sparse_decode_attn_workspace_size", "sparse_decode_attn",
            "importance_accumulate", "tier_classify_workspace_size", "tier_classify",
-           "spk_set_attn_timing_events", "sparse_index_topk")
+           "spk_set_attn_timing_events", "sparse_index_topk",
+           "sparse_topk_decode_attn_workspace_size", "sparse_topk_decode_attn")
 
 
 class SpkError(RuntimeError):
@@ -83,6 +84,12 @@ def lib() -> ctypes.CDLL:
     L.tier_classify.argtypes = [P, I64, I, I, I, I, I, I, P, I64, P, I64, P, P, I64, P, SZ, P]
     L.spk_set_attn_timing_events.restype = I
     L.spk_set_attn_timing_events.argtypes = [P, P]
+    L.sparse_topk_decode_attn_workspace_size.restype = I
+    L.sparse_topk_decode_attn_workspace_size.argtypes = [I, I, I, I, I, I, I, I, I, I,
+                                                         ctypes.POINTER(SZ)]
+    L.sparse_topk_decode_attn.restype = I
+    L.sparse_topk_decode_attn.argtypes = [P, I64, I, I, P, I, P, P, I, I64, I64, I64, I, I, I, I, I,
+                                          I, I, I, FL, P, P, P, P, I64, P, SZ, P]
     L.sparse_index_topk.restype = I
     L.sparse_index_topk.argtypes = [I, P, I, P, I, I64, I64, I64, I, I, I, I, I, I, I, I, P, I64,
                                     P, I64, P, P]
@@ -268,7 +275,8 @@ def sparse_decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel_id
     sel_ld = sel_idx.shape[-1]
     if sel_idx.stride(-1) != 1 or sel_idx.dim() < 1:
         raise ValueError("sel_idx must have a contiguous last dim")
-    sel2 = sel_idx.reshape(-1, sel_ld)
+    sel_rows = int(math.prod(sel_idx.shape[:-1])) if sel_idx.dim() > 1 else 1
+    sel2 = sel_idx.reshape(sel_rows, sel_ld)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     kb, kh, kn = _rows_view(k, "k")
@@ -356,3 +364,52 @@ def set_attn_timing_events(begin: Optional[torch.cuda.Event] = None,
     if begin is not None and (not b.value or not e.value):
         raise ValueError("record the events once before handing them over")
     _check(lib().spk_set_attn_timing_events(b, e), "spk_set_attn_timing_events")
+
+
+def topk_attn_workspace_size(B, Hq, Hkv, d, n_tokens, n_cand, k, gran=1, n_sink=0,
+                             n_recent=0) -> int:
+    out = SZ(0)
+    _check(lib().sparse_topk_decode_attn_workspace_size(B, Hq, Hkv, d, n_tokens, n_cand, k, gran,
+                                                        n_sink, n_recent, ctypes.byref(out)),
+           "sparse_topk_decode_attn_workspace_size")
+    return out.value
+
+
+def sparse_topk_decode_attn(scores: torch.Tensor, k: int, q: torch.Tensor, kc: torch.Tensor,
+                            vc: torch.Tensor, n_tokens: int, gran: int = 1, n_sink: int = 0,
+                            n_recent: int = 0, sm_scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            sel_idx: Optional[torch.Tensor] = None,
+                            sel_count: Optional[torch.Tensor] = None,
+                            ws: Optional[torch.Tensor] = None, stream=None):
+    """Top-k of each (b, kvh) score row and exact attention over the selection, one launch.
+    scores [B, 1, Hkv, >=n_cand] fp32 (n_cand = scores.shape[-1]); q [B, 1, Hq, d] bf16.
+    Returns (out fp32 [B,1,Hq,d], lse fp32 [B,1,Hq])."""
+    _contig(q, "q")
+    B, T, Hq, d = q.shape
+    if T != 1:
+        raise ValueError("one query token per sequence")
+    Hkv = kc.shape[1]
+    n_cand = scores.shape[-1]
+    if scores.stride(-1) != 1:
+        raise ValueError("scores must have a contiguous last dim")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    kb, kh, kn = _rows_view(kc, "k")
+    if _rows_view(vc, "v") != (kb, kh, kn):
+        raise ValueError("k and v must share strides")
+    if out is None:
+        out = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=q.device)
+    wsz = topk_attn_workspace_size(B, Hq, Hkv, d, n_tokens, n_cand, k, gran, n_sink, n_recent)
+    if ws is None or ws.numel() < wsz:
+        ws = torch.zeros(max(wsz, 1), dtype=torch.uint8, device=q.device)
+    sl = sel_idx.stride(-2) if sel_idx is not None else 0
+    st = lib().sparse_topk_decode_attn(_ptr(scores), scores.stride(-2), n_cand, k, _ptr(q), _dt(q),
+                                       _ptr(kc), _ptr(vc), _dt(kc), kb, kh, kn, gran, n_sink,
+                                       n_recent, B, Hq, Hkv, d, n_tokens, float(sm_scale),
+                                       _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(sel_count), sl,
+                                       _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "sparse_topk_decode_attn")
+    return out, lse

@@ -26,7 +26,7 @@
 #include <mutex>
 #include <type_traits>
 
-#include "spk_internal.h"
+#include "select_common.h"
 
 namespace spk {
 namespace {
@@ -40,6 +40,7 @@ constexpr int kMaxSets = 32;
 constexpr int kAsmThreads = 1024;
 constexpr int kAsmLdsWords = 32768;  // 128 KB of LDS bitmaps; larger ones live in the workspace
 constexpr int kMaxIntervals = 64;   // selection entries + 2 forced ranges, one per lane
+constexpr int kScoresMax = 4096;    // candidates per score row selected inside the attention
 constexpr int kMaxRows = 8192;      // rows per split (LDS slot table)
 constexpr int kTabPad = 512;        // slot-table entries past a split's rows (dead padding)
 constexpr int kDead = INT32_MIN;    // row-table entry of a row that is not read
@@ -79,7 +80,7 @@ inline size_t table_bytes(int R, bool mask) { return (size_t)(R + kTabPad) * 4 *
 // CU's resident workgroup slots (at the occupancy the slot table's LDS allows).  Workgroups
 // then see the same amount of work and the last round is not left half empty.
 Plan make_plan(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_tokens,
-               int64_t sel_ld, int gran, int n_sink, int n_recent) {
+               int64_t sel_ld, int gran, int n_sink, int n_recent, bool from_scores = false) {
   Plan p;
   const int G = Hq / Hkv;
   p.groups = B * Hkv;
@@ -88,7 +89,8 @@ Plan make_plan(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_
   p.nq_pad = pad_nq(p.nq);
   p.mask = p.sets > 1;
   const bool expand = gran > 1 || n_sink > 0 || n_recent > 0;
-  p.intervals = p.sets == 1 && expand && sel_ld + 2 <= 64;
+  // a selection made from scores inside the attention is always expanded there
+  p.intervals = p.sets == 1 && (expand || from_scores) && sel_ld + 2 <= 64;
   p.assemble = p.sets > 1 || (expand && !p.intervals);
   int64_t ub = (int64_t)p.sets * sel_ld * gran + n_sink + n_recent;
   if (ub > n_tokens) ub = n_tokens;
@@ -220,6 +222,7 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_kernel(AsmArgs a) {
 enum ListMode {
   kListExplicit = 0,   // list + count (caller's list, or the assembled one)
   kListIntervals = 1,  // one selection row of ids expanded by `gran`, plus sinks and recent window
+  kListScores = 2,     // as kListIntervals, the ids being the top-k of the group's score row
 };
 
 struct AttnArgs {
@@ -255,6 +258,14 @@ struct AttnArgs {
   float* logits;
   int64_t logits_ld;
   int logits_vec;        // logits rows are 16-byte aligned (base and row stride)
+  // kListScores: score row g at sc_scores + g*sc_ld, sc_n candidates, keep sc_k; the selection
+  // is also written to sel_out row g (sel_out_ld) and count_out[g] when those are given
+  const float* sc_scores;
+  int64_t sc_ld;
+  int sc_n, sc_k;
+  int32_t* sel_out;
+  int32_t* count_out;
+  int64_t sel_out_ld;
 };
 
 // End of a partial workgroup: merge the 4 waves' (m, l, acc) from `red` and store this split's
@@ -446,7 +457,7 @@ __device__ __forceinline__ void fill_slot_table(const AttnArgs& a, int b, int kv
     int slot_v = kDead;
     if (i < nrows) {
       int tok;
-      if constexpr (MODE == kListIntervals) tok = token_at(seg_start, seg_pos, nseg, r0 + i);
+      if constexpr (MODE != kListExplicit) tok = token_at(seg_start, seg_pos, nseg, r0 + i);
       else tok = list[r0 + i];
       slot_v = resolve_slot(a, b, kvh, tok);
     }
@@ -727,6 +738,12 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   __shared__ __align__(16) unsigned char work_s[kRedBytes > kVtBytes ? kRedBytes : kVtBytes];
   auto& red = *reinterpret_cast<float (*)[kWaves][NQ][D + 2]>(work_s);
   __shared__ int seg_start[kMaxIntervals], seg_pos[kMaxIntervals], seg_meta[2];
+  // kListScores: radix-select histograms, per-wave counts and the selected ids
+  constexpr bool kSc = MODE == kListScores;
+  __shared__ uint32_t sc_hist[kSc ? kWaves * 256 : 1];
+  __shared__ int sc_sh[2], sc_cnt;
+  __shared__ int sc_w[2][kWaves][2];
+  __shared__ int32_t sc_list[kSc ? kMaxIntervals : 1];
   extern __shared__ int32_t dyn_s[];
   int32_t* slot_s = dyn_s;
   uint32_t* mask_s = reinterpret_cast<uint32_t*>(dyn_s + a.tab_cap);
@@ -754,7 +771,69 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
     }
   }
   int cnt;
-  if constexpr (MODE == kListIntervals) {
+  if constexpr (MODE == kListScores) {
+    // the group's selection: exact top-k of its score row (ties to the lowest index, ascending),
+    // as topk_select computes it, kept in LDS
+    constexpr int SI = kScoresMax / kThreads;
+    const float* srow = a.sc_scores + (int64_t)g * a.sc_ld;
+    const int n = a.sc_n, kk = min(a.sc_k, n);
+    const int tid = threadIdx.x;
+    uint32_t key[SI];
+#pragma unroll
+    for (int c = 0; c < SI; ++c) {
+      const int j = c * kThreads + tid;
+      key[c] = j < n ? order_key(srow[j]) : 0u;
+    }
+    if (kk > 0) {
+      uint32_t thr;
+      int need;
+      radix_select<kThreads>(
+          [&](auto visit) {
+#pragma unroll
+            for (int c = 0; c < SI; ++c)
+              if (c * kThreads + tid < n) visit(key[c]);
+          },
+          kk, sc_hist, sc_sh, &thr, &need);
+      const uint64_t lt = (1ull << lane) - 1ull;
+      int run_g = 0, run_e = 0;
+      for (int c = 0; c < SI; ++c) {
+        if (c * kThreads >= n) break;
+        const bool valid = c * kThreads + tid < n;
+        const bool gt = valid && key[c] > thr, eq = valid && key[c] == thr;
+        const uint64_t bg = __ballot(gt), be = __ballot(eq);
+        if (lane == 0) {
+          sc_w[c & 1][wid][0] = __popcll(bg);
+          sc_w[c & 1][wid][1] = __popcll(be);
+        }
+        __syncthreads();
+        int pre_g = run_g + __popcll(bg & lt), pre_e = run_e + __popcll(be & lt);
+        int tot_g = 0, tot_e = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const int cg = sc_w[c & 1][w][0], ce = sc_w[c & 1][w][1];
+          if (w < wid) {
+            pre_g += cg;
+            pre_e += ce;
+          }
+          tot_g += cg;
+          tot_e += ce;
+        }
+        if (gt || (eq && pre_e < need)) sc_list[pre_g + min(pre_e, need)] = c * kThreads + tid;
+        run_g += tot_g;
+        run_e += tot_e;
+      }
+    }
+    if (tid == 0) sc_cnt = kk;
+    __syncthreads();
+    if (split == 0 && a.sel_out) {
+      for (int i = tid; i < kk; i += kThreads) a.sel_out[(int64_t)g * a.sel_out_ld + i] = sc_list[i];
+      if (tid == 0 && a.count_out) a.count_out[g] = kk;
+    }
+    if (wid == 0) build_segments(a, sc_list, &sc_cnt, seg_start, seg_pos, &seg_meta[0], &seg_meta[1]);
+    __syncthreads();
+    cnt = seg_meta[1];
+    if (split == 0 && tid == 0) a.ucount[g] = cnt;
+  } else if constexpr (MODE == kListIntervals) {
     if (wid == 0)
       build_segments(a, a.list + (int64_t)lrow * a.list_ld, a.count + lrow, seg_start, seg_pos,
                      &seg_meta[0], &seg_meta[1]);
@@ -1035,6 +1114,17 @@ void dispatch_mode(bool mask, int mode, dim3 grid, hipStream_t st, const AttnArg
   else launch_partial<D, KT, NQ, false, kListExplicit>(grid, st, a);
 }
 
+template <int D>
+void dispatch_scores(int nq_pad, dim3 grid, hipStream_t st, const AttnArgs& a) {
+  switch (nq_pad) {
+    case 1: launch_partial_mfma<D, 1, false, kListScores>(grid, st, a); break;
+    case 2: launch_partial_mfma<D, 2, false, kListScores>(grid, st, a); break;
+    case 4: launch_partial_mfma<D, 4, false, kListScores>(grid, st, a); break;
+    case 8: launch_partial_mfma<D, 8, false, kListScores>(grid, st, a); break;
+    default: launch_partial_mfma<D, 16, false, kListScores>(grid, st, a); break;
+  }
+}
+
 template <int D, typename KT>
 void dispatch_nq(int nq_pad, bool mask, int mode, dim3 grid, hipStream_t st, const AttnArgs& a) {
   switch (nq_pad) {
@@ -1189,7 +1279,7 @@ extern "C" SPK_API spk_status sparse_decode_attn(
   if (st0 != SPK_OK) return st0;
   SPK_REQUIRE(dtype_ok(q_dtype) && dtype_ok(kv_dtype), SPK_EUNSUPPORTED,
               "sparse_decode_attn: unsupported dtype");
-  SPK_REQUIRE(B == 0 || (q && k && v && out && sel_idx && sel_count), SPK_EINVAL,
+  SPK_REQUIRE(B == 0 || (q && k && v && out && (sel_idx || sel_ld == 0) && sel_count), SPK_EINVAL,
               "sparse_decode_attn: null q, k, v, out, sel_idx or sel_count");
   SPK_REQUIRE(kv_sn >= d && kv_sb >= 0 && kv_sh >= 0 && kv_sn % 8 == 0 && kv_sh % 8 == 0 &&
                   kv_sb % 8 == 0,
@@ -1343,4 +1433,120 @@ extern "C" SPK_API spk_status sparse_decode_attn(
     hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(p.groups * a.nq), dim3(kWave), 0, st, a,
                        p.nq_pad, out, lse);
   return check_launch("sparse_decode_attn/combine");
+}
+
+extern "C" SPK_API spk_status sparse_topk_decode_attn_workspace_size(int B, int Hq, int Hkv,
+                                                                     int d, int n_tokens,
+                                                                     int n_cand, int k, int gran,
+                                                                     int n_sink, int n_recent,
+                                                                     size_t* bytes) {
+  using namespace spk;
+  SPK_REQUIRE(bytes, SPK_EINVAL, "sparse_topk_decode_attn_workspace_size: null bytes");
+  spk_status st0 = check_common(SPK_SEL_PER_KV_HEAD, B, 1, Hq, Hkv, d, n_tokens, k, gran, n_sink,
+                                n_recent);
+  if (st0 != SPK_OK) return st0;
+  SPK_REQUIRE(k >= 0 && k + 2 <= kMaxIntervals, SPK_EUNSUPPORTED,
+              "sparse_topk_decode_attn_workspace_size: k=%d (at most %d)", k, kMaxIntervals - 2);
+  SPK_REQUIRE(n_cand >= 0, SPK_EINVAL, "sparse_topk_decode_attn_workspace_size: n_cand < 0");
+  const int kk = k < n_cand ? k : n_cand;
+  *bytes = make_plan(SPK_SEL_PER_KV_HEAD, B, 1, Hq, Hkv, d, n_tokens, kk, gran, n_sink, n_recent,
+                     true).bytes;
+  clear_error();
+  return SPK_OK;
+}
+
+extern "C" SPK_API spk_status sparse_topk_decode_attn(
+    const float* scores, int64_t s_ld, int n_cand, int k, const void* q, spk_dtype q_dtype,
+    const void* kc, const void* vc, spk_dtype kv_dtype, int64_t kv_sb, int64_t kv_sh,
+    int64_t kv_sn, int gran, int n_sink, int n_recent, int B, int Hq, int Hkv, int d,
+    int n_tokens, float sm_scale, float* out, float* lse, int32_t* sel_idx, int32_t* sel_count,
+    int64_t sel_ld, void* ws, size_t ws_bytes, void* stream) {
+  using namespace spk;
+  spk_status st0 = check_common(SPK_SEL_PER_KV_HEAD, B, 1, Hq, Hkv, d, n_tokens, k, gran, n_sink,
+                                n_recent);
+  if (st0 != SPK_OK) return st0;
+  SPK_REQUIRE(q_dtype == SPK_BF16 && kv_dtype == SPK_BF16, SPK_EUNSUPPORTED,
+              "sparse_topk_decode_attn: bf16 queries and caches only");
+  SPK_REQUIRE(n_cand >= 0 && n_cand <= kScoresMax, SPK_EUNSUPPORTED,
+              "sparse_topk_decode_attn: %d candidates per row (max %d)", n_cand, kScoresMax);
+  SPK_REQUIRE(k >= 0 && k + 2 <= kMaxIntervals, SPK_EUNSUPPORTED,
+              "sparse_topk_decode_attn: k=%d (at most %d)", k, kMaxIntervals - 2);
+  SPK_REQUIRE(B == 0 || (scores && q && kc && vc && out), SPK_EINVAL,
+              "sparse_topk_decode_attn: null scores, q, k, v or out");
+  SPK_REQUIRE(s_ld >= n_cand, SPK_EINVAL, "sparse_topk_decode_attn: s_ld < n_cand");
+  const int kk = k < n_cand ? k : n_cand;
+  SPK_REQUIRE(!sel_idx || sel_ld >= kk, SPK_EINVAL, "sparse_topk_decode_attn: sel_ld < min(k, n)");
+  SPK_REQUIRE(kv_sn >= d && kv_sb >= 0 && kv_sh >= 0 && kv_sn % 8 == 0 && kv_sh % 8 == 0 &&
+                  kv_sb % 8 == 0,
+              SPK_EINVAL, "sparse_topk_decode_attn: kv strides must be multiples of 8 with kv_sn >= d");
+  SPK_REQUIRE(kv_sn * 2 < (int64_t)1 << 32, SPK_EUNSUPPORTED,
+              "sparse_topk_decode_attn: a KV row stride of 4 GiB or more is not supported");
+  SPK_REQUIRE(reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(kc) % 16 == 0 &&
+                  reinterpret_cast<uintptr_t>(vc) % 16 == 0,
+              SPK_EINVAL, "sparse_topk_decode_attn: q, k, v must be 16-byte aligned");
+  SPK_REQUIRE(!(sm_scale != sm_scale), SPK_EINVAL, "sparse_topk_decode_attn: sm_scale is NaN");
+  // planned as sparse_decode_attn plans the topk_select output (min(k, n_cand) ids per row),
+  // so both paths split the rows, and round, identically
+  const Plan p = make_plan(SPK_SEL_PER_KV_HEAD, B, 1, Hq, Hkv, d, n_tokens, kk, gran, n_sink,
+                           n_recent, true);
+  SPK_REQUIRE(ws_bytes >= p.bytes && (p.bytes == 0 || ws), SPK_EWORKSPACE,
+              "sparse_topk_decode_attn: workspace %zu bytes < %zu needed", ws_bytes, p.bytes);
+  clear_error();
+  if (B == 0) return SPK_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* w = reinterpret_cast<char*>(ws);
+  const int G = Hq / Hkv;
+  AttnArgs a{};
+  a.q = q;
+  a.q_bf16 = 1;
+  a.k = kc;
+  a.v = vc;
+  a.kv_sb = kv_sb;
+  a.kv_sh = kv_sh;
+  a.kv_sn = kv_sn;
+  a.hbm_slots = n_tokens;
+  a.T = 1;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.nq = G;
+  a.n_tokens = n_tokens;
+  a.tab_cap = p.R + kTabPad;
+  a.smax = p.smax;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.ml = reinterpret_cast<float*>(w + p.off_ml);
+  a.acc = reinterpret_cast<float*>(w + p.off_acc);
+  a.mask_div = G;
+  a.list_mode = kListScores;
+  a.list_ld = kk;
+  a.count_clamp = p.ubound;
+  a.gran = gran;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.ucount = reinterpret_cast<int32_t*>(w + p.off_count);
+  a.ucount_valid = 1;
+  a.sc_scores = scores;
+  a.sc_ld = s_ld;
+  a.sc_n = n_cand;
+  a.sc_k = k;
+  a.sel_out = sel_idx;
+  a.count_out = sel_count;
+  a.sel_out_ld = sel_ld;
+  dim3 grid(p.smax, p.groups);
+  hipEvent_t ev_begin = g_timing_begin, ev_end = g_timing_end;
+  if (ev_begin && hipEventRecord(ev_begin, st) != hipSuccess)
+    return set_error(SPK_EHIP, "sparse_topk_decode_attn: recording the timing event failed");
+  if (d == 128) dispatch_scores<128>(p.nq_pad, grid, st, a);
+  else dispatch_scores<64>(p.nq_pad, grid, st, a);
+  spk_status e = check_launch("sparse_topk_decode_attn/partial");
+  if (e != SPK_OK) return e;
+  if (ev_end && hipEventRecord(ev_end, st) != hipSuccess)
+    return set_error(SPK_EHIP, "sparse_topk_decode_attn: recording the timing event failed");
+  if (d == 128)
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(p.groups * a.nq), dim3(kWave), 0, st, a,
+                       p.nq_pad, out, lse);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(p.groups * a.nq), dim3(kWave), 0, st, a,
+                       p.nq_pad, out, lse);
+  return check_launch("sparse_topk_decode_attn/combine");
 }

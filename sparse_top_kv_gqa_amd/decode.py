@@ -18,8 +18,8 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import (attn_workspace_size, fused_index_topk_ok, sparse_decode_attn, sparse_index_score,
-               sparse_index_topk, topk_select, topk_workspace_size, importance_accumulate,
-               tier_classify)
+               sparse_index_topk, sparse_topk_decode_attn, topk_attn_workspace_size, topk_select,
+               topk_workspace_size, importance_accumulate, tier_classify)
 
 
 class BlockSparseDecode:
@@ -27,7 +27,7 @@ class BlockSparseDecode:
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, n_tokens: int, Hq: int, block_size: int,
                  k_blocks: int, n_sink: int, n_recent: int, sm_scale: Optional[float] = None,
-                 fused: bool = False):
+                 fused: bool = False, topk_in_attn: bool = False):
         self.k, self.v = k, v
         B, Hkv, _, d = k.shape
         self.B, self.Hkv, self.Hq, self.d = B, Hkv, Hq, d
@@ -39,6 +39,13 @@ class BlockSparseDecode:
         # when there are many groups with short rows, and loses to the two calls when a few
         # dozen groups leave most of the chip idle)
         self.fused = fused and fused_index_topk_ok("block_pooled", 1, 1, self.nb)
+        # topk_in_attn: the attention launch selects the top-k blocks from the scores itself
+        # (one launch fewer; at this size the selection in every split's prologue costs what
+        # the separate top-k launch costs, so it is off by default)
+        ok = k.dtype == torch.bfloat16 and self.nb <= 4096 and k_blocks <= 62
+        self.topk_in_attn = bool(topk_in_attn) and ok
+        if self.topk_in_attn:
+            self.fused = False
         dev = k.device
         self.kpool = torch.empty((B, Hkv, self.nb, d), dtype=torch.float32, device=dev)
         self.scores = torch.empty((B, 1, Hkv, self.nb), dtype=torch.float32, device=dev)
@@ -49,6 +56,9 @@ class BlockSparseDecode:
         self.lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
         ws = attn_workspace_size("per_kv_head", B, 1, Hq, Hkv, d, n_tokens, self.idx.shape[-1],
                                  block_size, n_sink, n_recent)
+        if self.topk_in_attn:
+            ws = max(ws, topk_attn_workspace_size(B, Hq, Hkv, d, n_tokens, self.nb, k_blocks,
+                                                  block_size, n_sink, n_recent))
         self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
 
     def pool(self, pred: torch.Tensor):
@@ -75,6 +85,15 @@ class BlockSparseDecode:
         return self.out, self.lse
 
     def step(self, q: torch.Tensor, pred: torch.Tensor):
+        if self.topk_in_attn:
+            sparse_index_score("block_pooled", pred, self.kpool, self.n_tokens, self.bs,
+                               scores=self.scores)
+            sparse_topk_decode_attn(self.scores, self.kb, q, self.k, self.v, self.n_tokens,
+                                    gran=self.bs, n_sink=self.n_sink, n_recent=self.n_recent,
+                                    sm_scale=self.sm_scale, out=self.out, lse=self.lse,
+                                    sel_idx=self.idx.view(-1, self.idx.shape[-1]),
+                                    sel_count=self.count.view(-1), ws=self.ws)
+            return self.out, self.lse
         self.select(pred)
         return self.attend(q)
 

@@ -621,7 +621,7 @@ def test_block_decode_fused_and_separate_paths_agree():
     outs = []
     for fused in (True, False):
         dec = BlockSparseDecode(k, v, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent,
-                                fused=fused)
+                                fused=fused, topk_in_attn=False)
         assert dec.fused == fused
         dec.pool(pred)
         out, lse = dec.step(q, pred)
@@ -781,3 +781,68 @@ def test_per_seq_host_rows_with_logits_bit_identical():
                                                  host(kc[b, h])[toks], host(vc[b, h])[toks], scale)
             check_rows(o_a[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="per-seq attention")
             check_rows(lg_a[b, 0, h * G:(h + 1) * G, :c].cpu().numpy(), lg_ref, what="per-seq logits")
+
+
+# ------------------------------------------------------------------------------------ top-k inside attention
+
+@pytest.mark.parametrize("case", ["block", "k0", "few_candidates", "ties"])
+def test_topk_decode_attn_matches_two_calls(case):
+    """Selecting inside the attention launch gives the selection topk_select gives and
+    bit-identical attention."""
+    say("topk-attn", case)
+    w = W.scaled(W.LLAMA8B_BLOCK, B=2, Hkv=2, Hq=8, N=64 * 70 + 37, k=9)
+    q = W.queries(w, device=DEV)
+    pred = W.predictors(w, device=DEV)
+    kc = W.kv_cache(w, "k", device=DEV)
+    vc = W.kv_cache(w, "v", device=DEV)
+    k = {"block": 9, "k0": 0, "few_candidates": 62, "ties": 9}[case]
+    nb = w.N // 64
+    if case == "few_candidates":
+        nb = 40                                      # fewer candidates than k
+    scores = torch.empty((w.B, 1, w.Hkv, nb), device=DEV)
+    pool = torch.empty((w.B, w.Hkv, w.N // 64, w.d), device=DEV)
+    full = spk.sparse_index_score("block_raw", pred, kc, w.N, 64, pooled_out=pool)
+    scores.copy_(full[..., :nb])
+    if case == "ties":
+        scores.copy_(torch.round(scores * 2) / 2)      # many equal scores
+    idx_a, cnt_a = spk.topk_select(scores, k)
+    out_a, lse_a = spk.sparse_decode_attn(q, kc, vc, idx_a, cnt_a, "per_kv_head", w.N, gran=64,
+                                          n_sink=4, n_recent=512)
+    sel_b = torch.full((w.B * w.Hkv, max(k, 1)), -7, dtype=torch.int32, device=DEV)
+    cnt_b = torch.empty((w.B * w.Hkv,), dtype=torch.int32, device=DEV)
+    out_b, lse_b = spk.sparse_topk_decode_attn(scores, k, q, kc, vc, w.N, gran=64, n_sink=4,
+                                               n_recent=512, sel_idx=sel_b, sel_count=cnt_b)
+    torch.cuda.synchronize()
+    kk = min(k, nb)
+    assert cnt_b.cpu().tolist() == [kk] * (w.B * w.Hkv)
+    sc = scores.cpu().numpy().reshape(w.B * w.Hkv, nb)
+    for r in range(w.B * w.Hkv):
+        assert sel_b[r, :kk].cpu().tolist() == oracle.topk(sc[r], k).tolist()
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+
+
+def test_block_decode_topk_in_attention_default_full_size():
+    """The block decoder with the top-k inside the attention at the full workload size:
+    selection equal to the oracle's top-k of the same scores, attention bit-identical to the
+    two-call path."""
+    w = W.LLAMA8B_BLOCK
+    say("block-topk-in-attn-full", w.name)
+    q = W.queries(w, device=DEV)
+    pred = W.predictors(w, device=DEV)
+    kc = W.kv_cache(w, "k", device=DEV)
+    vc = W.kv_cache(w, "v", device=DEV)
+    outs = []
+    for tia in (True, False):
+        dec = BlockSparseDecode(kc, vc, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent,
+                                topk_in_attn=tia)
+        assert dec.topk_in_attn == tia
+        dec.pool(pred)
+        out, lse = dec.step(q, pred)
+        torch.cuda.synchronize()
+        sc = dec.scores.cpu().numpy()
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                assert dec.idx[b, 0, h].cpu().numpy().tolist() == oracle.topk(sc[b, 0, h], w.k).tolist()
+        outs.append((dec.idx.clone(), out.clone(), lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][2], outs[1][2])
