@@ -222,7 +222,9 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_kernel(AsmArgs a) {
 enum ListMode {
   kListExplicit = 0,   // list + count (caller's list, or the assembled one)
   kListIntervals = 1,  // one selection row of ids expanded by `gran`, plus sinks and recent window
-  kListScores = 2,     // as kListIntervals, the ids being the top-k of the group's score row
+  kListScores = 2,     // the ids are the top-k of the group's score row (order as kListVirtual)
+  kListVirtual = 3,    // one selection row of ids expanded by `gran`, in list order, then the
+                       // sinks, then the recent window; rows a later part also holds are dead
 };
 
 struct AttnArgs {
@@ -248,6 +250,7 @@ struct AttnArgs {
   int gran, n_sink, n_recent;
   int32_t* ucount;       // per-group fetch-list length (written by assemble or intervals mode)
   int ucount_valid;      // ucount holds the lengths (assembled lists)
+  int split_bound;       // > 0: rows per split come from this bound, not from the group's count
   const uint32_t* mask;  // per fetch-list row (assembled lists with several sets)
   int mask_div;          // query vector n reads rows whose mask has bit n / mask_div
   int T, Hq, Hkv, G, nq, n_tokens, smax;
@@ -444,21 +447,54 @@ __device__ __forceinline__ int token_at(const int* seg_start, const int* seg_pos
   return seg_start[lo] + (p - seg_pos[lo]);
 }
 
+// Token at position p of a kListVirtual / kListScores fetch list: the selection's ids in list
+// order, each expanded to `gran` tokens, then the sinks [0, ns), then the recent window [rs, n).
+// A token that a later part also holds (block rows inside the sinks or the recent window, recent
+// rows inside the sinks) or that lies outside [0, n) is dead (-1), so each row is read once.
+// `entry` is the list entry covering p (ignored past the selection).
+__device__ __forceinline__ int virtual_token(int p, int n_sel, int gran, int entry, int ns,
+                                             int rs, int n) {
+  const int kb = n_sel * gran;
+  if (p < kb) {
+    const int64_t tok = (int64_t)entry * gran + p % gran;
+    return (entry < 0 || tok >= n || tok < ns || tok >= rs) ? -1 : (int)tok;
+  }
+  p -= kb;
+  if (p < ns) return p;
+  const int tok = rs + (p - ns);
+  return tok < ns ? -1 : tok;
+}
+
+// Rows of a kListVirtual / kListScores fetch list with n_sel ids.
+__device__ __forceinline__ int virtual_rows(int n_sel, int gran, int ns, int rs, int n) {
+  return n_sel * gran + ns + (n - rs);
+}
+
 // Fill the split's slot table (and per-row list masks) in LDS: entries [0, nrows) are the
 // split's rows, entries up to tab_rows are dead (they read the zero row).
 template <int MODE, bool kMask>
 __device__ __forceinline__ void fill_slot_table(const AttnArgs& a, int b, int kvh, int g, int lrow,
                                                 int r0, int nrows, int tab_rows, int32_t* slot_s,
                                                 uint32_t* mask_s, const int* seg_start,
-                                                const int* seg_pos, int nseg) {
+                                                const int* seg_pos, int nseg,
+                                                const int32_t* vlist = nullptr, int n_sel = 0) {
   const int32_t* list = a.list + (int64_t)lrow * a.list_ld;
   const uint32_t* mrow = kMask ? a.mask + (int64_t)g * a.list_ld : nullptr;
+  const int n = a.n_tokens;
+  const int ns = min(a.n_sink, n), rs = max(n - a.n_recent, 0);
   for (int i = threadIdx.x; i < tab_rows; i += blockDim.x) {
     int slot_v = kDead;
     if (i < nrows) {
       int tok;
-      if constexpr (MODE != kListExplicit) tok = token_at(seg_start, seg_pos, nseg, r0 + i);
-      else tok = list[r0 + i];
+      if constexpr (MODE == kListVirtual || MODE == kListScores) {
+        const int p = r0 + i;
+        const int e = p < n_sel * a.gran ? vlist[p / a.gran] : 0;
+        tok = virtual_token(p, n_sel, a.gran, e, ns, rs, n);
+      } else if constexpr (MODE == kListIntervals) {
+        tok = token_at(seg_start, seg_pos, nseg, r0 + i);
+      } else {
+        tok = list[r0 + i];
+      }
       slot_v = resolve_slot(a, b, kvh, tok);
     }
     slot_s[i] = slot_v;
@@ -756,21 +792,9 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   const int qc = lane % 16, rg = lane / 16;      // MFMA layout: query column, row group
   const int sub = lane % LPR, slot = lane / LPR; // V load layout
 
-  // queries as the MFMA B operand: lane holds Q[query qc][32j + 8rg .. +7]
-  bf16x8 qb[KCH];
-  {
-    const bool have = qc < a.nq;
-    const int t = qc / a.G, hl = qc % a.G;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl) * D + 8 * rg;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (have) u = *reinterpret_cast<const uint4*>(qp + 32 * j);
-      qb[j] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
   int cnt;
+  const int32_t* vlist = nullptr;  // kListVirtual / kListScores: the selection's ids
+  int n_sel = 0;
   if constexpr (MODE == kListScores) {
     // the group's selection: exact top-k of its score row (ties to the lowest index, ascending),
     // as topk_select computes it, kept in LDS
@@ -829,10 +853,17 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
       for (int i = tid; i < kk; i += kThreads) a.sel_out[(int64_t)g * a.sel_out_ld + i] = sc_list[i];
       if (tid == 0 && a.count_out) a.count_out[g] = kk;
     }
-    if (wid == 0) build_segments(a, sc_list, &sc_cnt, seg_start, seg_pos, &seg_meta[0], &seg_meta[1]);
-    __syncthreads();
-    cnt = seg_meta[1];
+    n_sel = kk;
+    vlist = sc_list;
+    cnt = virtual_rows(kk, a.gran, min(a.n_sink, a.n_tokens), max(a.n_tokens - a.n_recent, 0),
+                       a.n_tokens);
     if (split == 0 && tid == 0) a.ucount[g] = cnt;
+  } else if constexpr (MODE == kListVirtual) {
+    vlist = a.list + (int64_t)lrow * a.list_ld;
+    n_sel = (int)max(0, min(a.count[lrow], (int)a.list_ld));
+    cnt = virtual_rows(n_sel, a.gran, min(a.n_sink, a.n_tokens), max(a.n_tokens - a.n_recent, 0),
+                       a.n_tokens);
+    if (split == 0 && threadIdx.x == 0) a.ucount[g] = cnt;
   } else if constexpr (MODE == kListIntervals) {
     if (wid == 0)
       build_segments(a, a.list + (int64_t)lrow * a.list_ld, a.count + lrow, seg_start, seg_pos,
@@ -844,7 +875,7 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
     cnt = a.count[lrow];
     cnt = max(0, min(cnt, a.count_clamp));
   }
-  const int rs = split_rows(cnt, a.smax);
+  const int rs = split_rows(a.split_bound > 0 ? a.split_bound : cnt, a.smax);
   const int r0 = split * rs;
   if (r0 >= cnt) return;
   const int r1 = min(r0 + rs, cnt);
@@ -853,7 +884,7 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   const int tab_rows = (iters + 3) * STEP;
   const RowBase rbase = make_row_base<uint16_t>(a, b, kvh);
   fill_slot_table<MODE, kMask>(a, b, kvh, g, lrow, r0, nrows, tab_rows, slot_s, mask_s, seg_start,
-                               seg_pos, seg_meta[0]);
+                               seg_pos, seg_meta[0], vlist, n_sel);
 
   float m_q = -INFINITY, l_part = 0.f;  // query qc: running max (wave-uniform), own-row denominator
   f32x4 O[DCH];                         // queries 4rg..+3, dims 16c + qc
@@ -861,6 +892,21 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   for (int c = 0; c < DCH; ++c) O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
+  // queries as the MFMA B operand: lane holds Q[query qc][32j + 8rg .. +7].  Loaded after the
+  // selection list (the list's wait must not include them); they arrive with the first tiles.
+  bf16x8 qb[KCH];
+  {
+    const bool have = qc < a.nq;
+    const int t = qc / a.G, hl = qc % a.G;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(b * a.T + t) * a.Hq + kvh * a.G + hl) * D + 8 * rg;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (have) u = *reinterpret_cast<const uint4*>(qp + 32 * j);
+      qb[j] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
   const uint64_t kcol = (uint64_t)(16 * rg);
   const uint64_t vcol = (uint64_t)(16 * sub);
   const int qd = qc / a.mask_div;
@@ -1024,7 +1070,7 @@ __global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a, int nq_
   constexpr int PER = D / kWave;
   const int64_t pbase = (int64_t)g * a.smax * nq_pad + n;
   int cnt;
-  if (a.list_mode == kListIntervals || a.ucount_valid) {
+  if (a.list_mode != kListExplicit || a.ucount_valid) {
     cnt = a.ucount[g];
   } else {
     const int lrow = a.lrow_is_batch ? b : g;
@@ -1046,7 +1092,7 @@ __global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a, int nq_
 #pragma unroll
       for (int i = 0; i < PER; ++i) ac[j][i] = a.acc[pi * D + lane + i * kWave];
     }
-    const int per = cnt > 0 ? split_rows(cnt, a.smax) : 1;
+    const int per = cnt > 0 ? split_rows(a.split_bound > 0 ? a.split_bound : cnt, a.smax) : 1;
     const int S = cnt > 0 ? (cnt + per - 1) / per : 0;
     float cmx = mx;
 #pragma unroll
@@ -1105,6 +1151,7 @@ void dispatch_mode(bool mask, int mode, dim3 grid, hipStream_t st, const AttnArg
     if (a.q_bf16) {
       if (mask) launch_partial_mfma<D, NQ, true, kListExplicit>(grid, st, a);
       else if (mode == kListIntervals) launch_partial_mfma<D, NQ, false, kListIntervals>(grid, st, a);
+      else if (mode == kListVirtual) launch_partial_mfma<D, NQ, false, kListVirtual>(grid, st, a);
       else launch_partial_mfma<D, NQ, false, kListExplicit>(grid, st, a);
       return;
     }
@@ -1365,7 +1412,22 @@ extern "C" SPK_API spk_status sparse_decode_attn(
   a.n_sink = n_sink;
   a.n_recent = n_recent;
   a.ucount = p.assemble || p.intervals ? reinterpret_cast<int32_t*>(w + p.off_count) : nullptr;
-  if (p.assemble) {
+  // One list per group expanded by gran / sinks / recent window, no logits, on the matrix-core
+  // kernel: the rows follow the list order (no union to build; rows a later part also holds
+  // are skipped), and splits are sized from the bound so they are known before the count.
+  const bool expand = gran > 1 || n_sink > 0 || n_recent > 0;
+  const bool virt = !logits && kv_dtype == SPK_BF16 && q_dtype == SPK_BF16 && p.sets == 1 &&
+                    expand && (int64_t)n_tokens >= sel_ld * gran + n_sink + n_recent;
+  if (virt) {
+    a.list_mode = kListVirtual;
+    a.list = sel_idx;
+    a.count = sel_count;
+    a.list_ld = sel_ld;
+    a.count_clamp = p.ubound;
+    a.split_bound = p.ubound;
+    a.lrow_is_batch = scope == SPK_SEL_PER_SEQ;
+    a.ucount_valid = 1;
+  } else if (p.assemble) {
     AsmArgs as{};
     as.sel_idx = sel_idx;
     as.sel_count = sel_count;
@@ -1485,6 +1547,8 @@ extern "C" SPK_API spk_status sparse_topk_decode_attn(
                   reinterpret_cast<uintptr_t>(vc) % 16 == 0,
               SPK_EINVAL, "sparse_topk_decode_attn: q, k, v must be 16-byte aligned");
   SPK_REQUIRE(!(sm_scale != sm_scale), SPK_EINVAL, "sparse_topk_decode_attn: sm_scale is NaN");
+  SPK_REQUIRE((int64_t)n_tokens >= (int64_t)kk * gran + n_sink + n_recent, SPK_EUNSUPPORTED,
+              "sparse_topk_decode_attn: n_tokens %d below k*gran + n_sink + n_recent", n_tokens);
   // planned as sparse_decode_attn plans the topk_select output (min(k, n_cand) ids per row),
   // so both paths split the rows, and round, identically
   const Plan p = make_plan(SPK_SEL_PER_KV_HEAD, B, 1, Hq, Hkv, d, n_tokens, kk, gran, n_sink,
@@ -1520,6 +1584,7 @@ extern "C" SPK_API spk_status sparse_topk_decode_attn(
   a.list_mode = kListScores;
   a.list_ld = kk;
   a.count_clamp = p.ubound;
+  a.split_bound = p.ubound;
   a.gran = gran;
   a.n_sink = n_sink;
   a.n_recent = n_recent;
