@@ -16,9 +16,15 @@
 namespace spk {
 namespace {
 
+#ifndef SPK_INDEX_UNROLL
+#define SPK_INDEX_UNROLL 4        // key loads in flight per lane
+#endif
+#ifndef SPK_INDEX_MAX_ROWS
+#define SPK_INDEX_MAX_ROWS 256    // candidate rows per workgroup (LDS score tile)
+#endif
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
-constexpr int kMaxRowsPerWg = 256;
+constexpr int kUnroll = SPK_INDEX_UNROLL;
+constexpr int kMaxRowsPerWg = SPK_INDEX_MAX_ROWS;
 
 // Fetch 8 elements [off, off+8) of the query tensor as floats.
 __device__ __forceinline__ void load_q8(const void* q, int q_bf16, int64_t off, float (&x)[8]) {
