@@ -204,10 +204,10 @@ def base_result(w, K, W, ms_step, step_bytes, config):
 COPY_KIB = 512 * 1024
 FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
-    "block": (("attn.hip", "spk_internal.h"), "c3590a1e8f458ed4", 40859.1, 1432.0),
-    "per_head": (("index_score.hip", "spk_internal.h"), "788931a87b7f8e45", 524476.0, 65536.0),
-    "spec_verify": (("attn.hip", "spk_internal.h"), "c3590a1e8f458ed4", 271809.0, 8545.0),
-    "tiers": (("attn.hip", "spk_internal.h"), "c3590a1e8f458ed4", 401312.0, 51483.4),
+    "block": (("attn.hip", "spk_internal.h"), "3da6f2e0d68a6feb", 40851.7, 1432.0),
+    "per_head": (("index_score.hip", "spk_internal.h"), "1abbb5de8b313b95", 524476.0, 65536.0),
+    "spec_verify": (("attn.hip", "spk_internal.h"), "3da6f2e0d68a6feb", 271804.0, 8544.76),
+    "tiers": (("attn.hip", "spk_internal.h"), "3da6f2e0d68a6feb", 401360.0, 51456.3),
 }
 
 
