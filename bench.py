@@ -308,23 +308,33 @@ def bench_block(args):
         torch.cuda.synchronize()
         assert torch.equal(ref, decs[l].out), "graph replay differs from eager step"
 
+    # the step's attention launch: with the selection inside it (the default) it also reads the
+    # group's score row, which counts among its algorithmic bytes
+    in_attn = decs[0].topk_in_attn
+    score_bytes = w.B * w.Hkv * (w.N // w.block_size) * 4 if in_attn else 0
+
     def attn(i):
         d = decs[i % L]
-        sparse_decode_attn(qs[i % L], d.k, d.v, d.idx, d.count, "per_kv_head", d.n_tokens,
-                           gran=d.bs, n_sink=d.n_sink, n_recent=d.n_recent, sm_scale=d.sm_scale,
-                           out=d.out, lse=d.lse, ws=d.ws, stream=stream)
+        if in_attn:
+            d.attend_scores(qs[i % L], stream=stream)
+        else:
+            sparse_decode_attn(qs[i % L], d.k, d.v, d.idx, d.count, "per_kv_head", d.n_tokens,
+                               gran=d.bs, n_sink=d.n_sink, n_recent=d.n_recent,
+                               sm_scale=d.sm_scale, out=d.out, lse=d.lse, ws=d.ws, stream=stream)
     att_ms = event_time_ms(attn, 8 * L, stream)
     gather_ms = gather_kernel_ms(attn, 8 * L, stream)
-    att_bytes = sum(sel_bytes) / L
+    att_bytes = sum(sel_bytes) / L + score_bytes
     bytes_avg = sum(step_bytes[i % L] for i in range(K)) / K
     res = base_result(w, K, Wm, ms_step, bytes_avg, {
         "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
         "context": w.N, "block_size": w.block_size, "top_blocks": w.k, "sinks": w.n_sink,
         "recent": w.n_recent, "layer_caches_rotated": L, "bytes_per_step": int(bytes_avg),
-        "selected_rows_per_step": int(att_bytes / ROW_BYTES), "wall_s_timed": round(wall, 4),
+        "selected_rows_per_step": int(sum(sel_bytes) / L / ROW_BYTES),
+        "wall_s_timed": round(wall, 4),
         "attention_call_ms": round(att_ms, 4)})
-    res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather)", att_bytes,
-                               gather_ms, traffic=measured_traffic("block"))
+    kname = ("attn_partial_mfma_kernel (sparse_topk_decode_attn: top-k + gather)" if in_attn
+             else "attn_partial_mfma_kernel (sparse_decode_attn gather)")
+    res["roofline"] = roofline(kname, att_bytes, gather_ms, traffic=measured_traffic("block"))
     ctx = dict(w=w, dec=decs[0], q=qs[0], pred=preds[0])
     return res, ctx
 

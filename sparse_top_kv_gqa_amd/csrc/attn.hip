@@ -477,18 +477,21 @@ __device__ __forceinline__ void fill_slot_table(const AttnArgs& a, int b, int kv
                                                 int r0, int nrows, int tab_rows, int32_t* slot_s,
                                                 uint32_t* mask_s, const int* seg_start,
                                                 const int* seg_pos, int nseg,
-                                                const int32_t* vlist = nullptr, int n_sel = 0) {
+                                                const int32_t* vlist = nullptr, int n_sel = 0,
+                                                const int* pre_e = nullptr, int n_pre = 0) {
   const int32_t* list = a.list + (int64_t)lrow * a.list_ld;
   const uint32_t* mrow = kMask ? a.mask + (int64_t)g * a.list_ld : nullptr;
   const int n = a.n_tokens;
   const int ns = min(a.n_sink, n), rs = max(n - a.n_recent, 0);
-  for (int i = threadIdx.x; i < tab_rows; i += blockDim.x) {
+  for (int it = 0, i = threadIdx.x; i < tab_rows; ++it, i += blockDim.x) {
     int slot_v = kDead;
     if (i < nrows) {
       int tok;
       if constexpr (MODE == kListVirtual || MODE == kListScores) {
         const int p = r0 + i;
-        const int e = p < n_sel * a.gran ? vlist[p / a.gran] : 0;
+        // pre_e[it]: the entry of row r0 + threadIdx.x + it*blockDim.x, read earlier
+        const int e = it < n_pre ? (it == 0 ? pre_e[0] : pre_e[1])
+                                 : (p < n_sel * a.gran ? vlist[p / a.gran] : 0);
         tok = virtual_token(p, n_sel, a.gran, e, ns, rs, n);
       } else if constexpr (MODE == kListIntervals) {
         tok = token_at(seg_start, seg_pos, nseg, r0 + i);
@@ -769,16 +772,20 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   static_assert(NQ <= 16, "at most 16 query vectors per group");
   static_assert(BATCH <= 4 && 4 * STEP <= kTabPad, "slot table padding covers the last batch");
   // the staged V tiles (main loop) and the wave merge area (end) share one LDS block
+  // kListScores: the score row's keys live in the same block before the main loop
+  constexpr bool kSc = MODE == kListScores;
   constexpr int kRedBytes = kWaves * NQ * (D + 2) * 4;
   constexpr int kVtBytes = kWaves * TILE * VST;
-  __shared__ __align__(16) unsigned char work_s[kRedBytes > kVtBytes ? kRedBytes : kVtBytes];
+  constexpr int kScBytes = kSc ? kScoresMax * 4 : 0;
+  constexpr int kWorkBytes = kRedBytes > kVtBytes ? (kRedBytes > kScBytes ? kRedBytes : kScBytes)
+                                                  : (kVtBytes > kScBytes ? kVtBytes : kScBytes);
+  __shared__ __align__(16) unsigned char work_s[kWorkBytes];
   auto& red = *reinterpret_cast<float (*)[kWaves][NQ][D + 2]>(work_s);
   __shared__ int seg_start[kMaxIntervals], seg_pos[kMaxIntervals], seg_meta[2];
-  // kListScores: radix-select histograms, per-wave counts and the selected ids
-  constexpr bool kSc = MODE == kListScores;
-  __shared__ uint32_t sc_hist[kSc ? kWaves * 256 : 1];
-  __shared__ int sc_sh[2], sc_cnt;
-  __shared__ int sc_w[2][kWaves][2];
+  // kListScores: one histogram per radix digit, per-wave counts and the selected ids
+  __shared__ __align__(16) uint32_t sc_hist[kSc ? 4 * 256 : 4];
+  constexpr int kScRegKeys = 4;  // score rows up to 4*256 candidates select from registers
+  __shared__ int sc_wsum[2 * kScRegKeys * kWaves];
   __shared__ int32_t sc_list[kSc ? kMaxIntervals : 1];
   extern __shared__ int32_t dyn_s[];
   int32_t* slot_s = dyn_s;
@@ -795,96 +802,84 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   int cnt;
   const int32_t* vlist = nullptr;  // kListVirtual / kListScores: the selection's ids
   int n_sel = 0;
+  int pre_e[2] = {0, 0}, n_pre = 0;  // kListVirtual: entries read ahead of the count
   if constexpr (MODE == kListScores) {
     // the group's selection: exact top-k of its score row (ties to the lowest index, ascending),
     // as topk_select computes it, kept in LDS
-    constexpr int SI = kScoresMax / kThreads;
     const float* srow = a.sc_scores + (int64_t)g * a.sc_ld;
     const int n = a.sc_n, kk = min(a.sc_k, n);
     const int tid = threadIdx.x;
-    uint32_t key[SI];
+    auto keep = [&](int pos, int i) { sc_list[pos] = i; };
+    if (n <= kScRegKeys * kThreads) {
+      // the usual case: each thread holds its keys in registers
+      uint32_t key[kScRegKeys];
 #pragma unroll
-    for (int c = 0; c < SI; ++c) {
-      const int j = c * kThreads + tid;
-      key[c] = j < n ? order_key(srow[j]) : 0u;
-    }
-    if (kk > 0) {
-      uint32_t thr;
-      int need;
-      radix_select<kThreads>(
-          [&](auto visit) {
-#pragma unroll
-            for (int c = 0; c < SI; ++c)
-              if (c * kThreads + tid < n) visit(key[c]);
-          },
-          kk, sc_hist, sc_sh, &thr, &need);
-      const uint64_t lt = (1ull << lane) - 1ull;
-      int run_g = 0, run_e = 0;
-      for (int c = 0; c < SI; ++c) {
-        if (c * kThreads >= n) break;
-        const bool valid = c * kThreads + tid < n;
-        const bool gt = valid && key[c] > thr, eq = valid && key[c] == thr;
-        const uint64_t bg = __ballot(gt), be = __ballot(eq);
-        if (lane == 0) {
-          sc_w[c & 1][wid][0] = __popcll(bg);
-          sc_w[c & 1][wid][1] = __popcll(be);
-        }
-        __syncthreads();
-        int pre_g = run_g + __popcll(bg & lt), pre_e = run_e + __popcll(be & lt);
-        int tot_g = 0, tot_e = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const int cg = sc_w[c & 1][w][0], ce = sc_w[c & 1][w][1];
-          if (w < wid) {
-            pre_g += cg;
-            pre_e += ce;
-          }
-          tot_g += cg;
-          tot_e += ce;
-        }
-        if (gt || (eq && pre_e < need)) sc_list[pre_g + min(pre_e, need)] = c * kThreads + tid;
-        run_g += tot_g;
-        run_e += tot_e;
+      for (int j = 0; j < kScRegKeys; ++j) {
+        const int i = j * kThreads + tid;
+        key[j] = i < n ? order_key(srow[i]) : 0u;
       }
-    }
-    if (tid == 0) sc_cnt = kk;
-    __syncthreads();
-    if (split == 0 && a.sel_out) {
-      for (int i = tid; i < kk; i += kThreads) a.sel_out[(int64_t)g * a.sel_out_ld + i] = sc_list[i];
-      if (tid == 0 && a.count_out) a.count_out[g] = kk;
+      if (kk > 0) reg_topk<kThreads>(key, n, kk, sc_hist, sc_wsum, keep);
+      __syncthreads();
+    } else {
+      uint32_t* keys = reinterpret_cast<uint32_t*>(work_s);
+      for (int j = tid; j < n; j += kThreads) keys[j] = order_key(srow[j]);
+      if (kk > 0) lds_topk<kThreads>(keys, n, kk, sc_hist, sc_wsum, keep);
     }
     n_sel = kk;
     vlist = sc_list;
     cnt = virtual_rows(kk, a.gran, min(a.n_sink, a.n_tokens), max(a.n_tokens - a.n_recent, 0),
                        a.n_tokens);
-    if (split == 0 && tid == 0) a.ucount[g] = cnt;
   } else if constexpr (MODE == kListVirtual) {
     vlist = a.list + (int64_t)lrow * a.list_ld;
+    if (a.split_bound > 0 && a.list_ld > 0) {
+      // the list entries of this thread's first two table rows are read together with the
+      // count (clamped in bounds; an entry past the selection is never used)
+      const int p0 = split * split_rows(a.split_bound, a.smax) + (int)threadIdx.x;
+      const int lmax = (int)a.list_ld - 1;
+      pre_e[0] = vlist[min(p0 / a.gran, lmax)];
+      pre_e[1] = vlist[min((p0 + kThreads) / a.gran, lmax)];
+      n_pre = 2;
+    }
     n_sel = (int)max(0, min(a.count[lrow], (int)a.list_ld));
     cnt = virtual_rows(n_sel, a.gran, min(a.n_sink, a.n_tokens), max(a.n_tokens - a.n_recent, 0),
                        a.n_tokens);
-    if (split == 0 && threadIdx.x == 0) a.ucount[g] = cnt;
   } else if constexpr (MODE == kListIntervals) {
     if (wid == 0)
       build_segments(a, a.list + (int64_t)lrow * a.list_ld, a.count + lrow, seg_start, seg_pos,
                      &seg_meta[0], &seg_meta[1]);
     __syncthreads();
     cnt = seg_meta[1];
-    if (split == 0 && threadIdx.x == 0) a.ucount[g] = cnt;
   } else {
     cnt = a.count[lrow];
     cnt = max(0, min(cnt, a.count_clamp));
   }
+  // split 0 publishes the group's row count (and, selecting from scores, the selection) once its
+  // work is done: a barrier waits for every earlier global store, so none are issued before it
+  auto publish = [&]() {
+    if (split != 0) return;
+    if constexpr (MODE != kListExplicit) {
+      if (threadIdx.x == 0) a.ucount[g] = cnt;
+    }
+    if constexpr (MODE == kListScores) {
+      if (a.sel_out)
+        for (int i = threadIdx.x; i < n_sel; i += kThreads)
+          a.sel_out[(int64_t)g * a.sel_out_ld + i] = sc_list[i];
+      if (threadIdx.x == 0 && a.count_out) a.count_out[g] = n_sel;
+    }
+  };
   const int rs = split_rows(a.split_bound > 0 ? a.split_bound : cnt, a.smax);
   const int r0 = split * rs;
-  if (r0 >= cnt) return;
+  if (r0 >= cnt) {
+    publish();
+    return;
+  }
   const int r1 = min(r0 + rs, cnt);
   const int nrows = r1 - r0;
   const int iters = (nrows + STEP - 1) / STEP;
   const int tab_rows = (iters + 3) * STEP;
   const RowBase rbase = make_row_base<uint16_t>(a, b, kvh);
   fill_slot_table<MODE, kMask>(a, b, kvh, g, lrow, r0, nrows, tab_rows, slot_s, mask_s, seg_start,
-                               seg_pos, seg_meta[0], vlist, n_sel);
+                               seg_pos, seg_meta[0], vlist, n_sel, pre_e, n_pre);
 
   float m_q = -INFINITY, l_part = 0.f;  // query qc: running max (wave-uniform), own-row denominator
   f32x4 O[DCH];                         // queries 4rg..+3, dims 16c + qc
@@ -1051,6 +1046,7 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   }
   __syncthreads();
   finish_split<D, NQ, kWaves>(a, red, g, split);
+  publish();
 }
 
 // ------------------------------------------------------------------------------- combine

@@ -68,6 +68,188 @@ __device__ void radix_select(const ForEach& for_each, int kk, uint32_t* hist, in
   *need = kk;
 }
 
+// One radix step, run by every wave on its own: from the 256-bin histogram h of the candidate
+// keys' current digit, the digit of the rem-th largest candidate (dsel), the number of candidates
+// with a larger digit (above) and with that digit (in_bin); wave-uniform results.
+__device__ __forceinline__ void digit_of_rank(const uint32_t* h, int rem, int& dsel, int& above,
+                                              int& in_bin) {
+  // lane l holds digits 255-4l down to 252-4l; counts run from the largest digit down
+  const int lane = lane_id();
+  const int d0 = 255 - 4 * lane;
+  const uint4 c4 = *reinterpret_cast<const uint4*>(h + d0 - 3);
+  const int s = (int)(c4.x + c4.y + c4.z + c4.w);
+  const int incl = wave_incl_scan_dpp(s);
+  const int excl = incl - s;
+  const uint64_t hit = __ballot(excl < rem && rem <= incl);
+  int acc = excl, dd, cb;
+  if (acc + (int)c4.w >= rem) {
+    dd = d0;
+    cb = (int)c4.w;
+  } else if ((acc += (int)c4.w) + (int)c4.z >= rem) {
+    dd = d0 - 1;
+    cb = (int)c4.z;
+  } else if ((acc += (int)c4.z) + (int)c4.y >= rem) {
+    dd = d0 - 2;
+    cb = (int)c4.y;
+  } else {
+    acc += (int)c4.y;
+    dd = d0 - 3;
+    cb = (int)c4.x;
+  }
+  const int src = (int)__builtin_ctzll(hit | (1ull << 63));
+  dsel = __builtin_amdgcn_readlane(dd, src);
+  above = __builtin_amdgcn_readlane(acc, src);
+  in_bin = __builtin_amdgcn_readlane(cb, src);
+}
+
+// Radix search for the threshold of an exact top-kk (8-bit digits, most significant first).
+// Every thread calls it; `for_each(visit)` calls visit(key) for each candidate key the thread
+// owns.  hist: 4*256 uint32 of LDS, zero on entry (one histogram per digit, so a pass needs one
+// barrier and nothing is cleared between passes).  Returns the kk-th largest key as *thr with
+// *need, the number of keys equal to it that are kept (the first ones in index order); or, when
+// a digit's bin holds exactly the keys still missing, *whole = true: keep every key >= *thr.
+template <typename ForEach>
+__device__ __forceinline__ void radix_threshold(const ForEach& for_each, int kk, uint32_t* hist,
+                                                uint32_t* thr, int* need, bool* whole) {
+  uint32_t prefix = 0, pmask = 0;
+  int rem = kk;
+  bool wh = false;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    uint32_t* h = hist + pass * 256;
+    for_each([&](uint32_t key) {
+      if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    int dsel, above, in_bin;
+    digit_of_rank(h, rem, dsel, above, in_bin);
+    rem -= above;
+    prefix |= (uint32_t)dsel << shift;
+    pmask |= 0xFFu << shift;
+    if (in_bin == rem) {
+      wh = true;
+      break;
+    }
+  }
+  *thr = prefix;
+  *need = rem;
+  *whole = wh;
+}
+
+__device__ __forceinline__ void keep_class(uint32_t key, bool valid, uint32_t thr, bool whole,
+                                           bool& gt, bool& eq) {
+  gt = valid && (whole ? key >= thr : key > thr);
+  eq = valid && !whole && key == thr;
+}
+
+// Exact top-kk of n keys held in registers by a workgroup of NT threads (1 <= kk <= n <= KPT*NT):
+// key[j] of thread t is element j*NT + t.  Ties go to the lowest index; calls out(position,
+// index) for every kept element, positions 0..kk-1 in ascending index order.  hist: 4*256 uint32
+// of LDS; wsum: 2*KPT*NT/64 ints of LDS.  Barriers: one to clear, one per radix pass, one for the
+// per-wave counts; the caller waits (barrier) before reading what out wrote to LDS.
+template <int NT, int KPT, typename Out>
+__device__ void reg_topk(const uint32_t (&key)[KPT], int n, int kk, uint32_t* hist, int* wsum,
+                         const Out& out) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  for (int i = tid; i < 4 * 256; i += NT) hist[i] = 0u;
+  __syncthreads();
+  uint32_t thr;
+  int need;
+  bool whole;
+  radix_threshold(
+      [&](auto visit) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          if (j * NT + tid < n) visit(key[j]);
+      },
+      kk, hist, &thr, &need, &whole);
+  // element order: chunk j (indices j*NT ..), inside it wave w (64 indices), inside it the lane
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    bool gt, eq;
+    keep_class(key[j], j * NT + tid < n, thr, whole, gt, eq);
+    const int cg = __popcll(__ballot(gt)), ce = __popcll(__ballot(eq));
+    if (lane == 0) {
+      wsum[2 * (j * NW + wid)] = cg;
+      wsum[2 * (j * NW + wid) + 1] = ce;
+    }
+  }
+  __syncthreads();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int run_g = 0, run_e = 0;  // kept counts of the (chunk, wave) pairs before the current one
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    for (int w = 0; w < NW; ++w) {
+      if (w == wid) {
+        bool gt, eq;
+        keep_class(key[j], j * NT + tid < n, thr, whole, gt, eq);
+        const uint64_t bg = __ballot(gt), be = __ballot(eq);
+        const int pe = run_e + __popcll(be & lt);
+        const int pos = run_g + __popcll(bg & lt) + min(pe, need);
+        if ((gt || (eq && pe < need)) && pos < kk) out(pos, j * NT + tid);
+      }
+      run_g += wsum[2 * (j * NW + w)];
+      run_e += wsum[2 * (j * NW + w) + 1];
+    }
+  }
+}
+
+// Exact top-kk of the n order keys keys[0..n) that a workgroup of NT threads holds in LDS
+// (1 <= kk <= n), ties to the lowest index: calls out(position, index) once for every kept
+// element, positions 0..kk-1 in ascending index order.  hist: 4*256 uint32 of LDS; wsum: 2*NT/64
+// ints of LDS.  Every thread calls it after writing its keys; it begins and ends with a barrier.
+template <int NT, typename Out>
+__device__ void lds_topk(const uint32_t* keys, int n, int kk, uint32_t* hist, int* wsum,
+                         const Out& out) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  for (int i = tid; i < 4 * 256; i += NT) hist[i] = 0u;
+  __syncthreads();
+  uint32_t thr;
+  int need;
+  bool whole;
+  radix_threshold(
+      [&](auto visit) {
+        for (int i = tid; i < n; i += NT) visit(keys[i]);
+      },
+      kk, hist, &thr, &need, &whole);
+  // wave w compacts the contiguous index range [w*seg, w*seg + seg)
+  const int seg = ((n + NW - 1) / NW + kWave - 1) / kWave * kWave;
+  const int lo = wid * seg, hi = min(n, lo + seg);
+  int cg = 0, ce = 0;
+  for (int i0 = lo; i0 < hi; i0 += kWave) {
+    const int i = i0 + lane;
+    bool gt, eq;
+    keep_class(i < hi ? keys[i] : 0u, i < hi, thr, whole, gt, eq);
+    cg += __popcll(__ballot(gt));
+    ce += __popcll(__ballot(eq));
+  }
+  if (lane == 0) {
+    wsum[2 * wid] = cg;
+    wsum[2 * wid + 1] = ce;
+  }
+  __syncthreads();
+  int run_g = 0, run_e = 0;
+  for (int w = 0; w < wid; ++w) {
+    run_g += wsum[2 * w];
+    run_e += wsum[2 * w + 1];
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int i0 = lo; i0 < hi; i0 += kWave) {
+    const int i = i0 + lane;
+    bool gt, eq;
+    keep_class(i < hi ? keys[i] : 0u, i < hi, thr, whole, gt, eq);
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    const int pe = run_e + __popcll(be & lt);
+    const int pos = run_g + __popcll(bg & lt) + min(pe, need);
+    if ((gt || (eq && pe < need)) && pos < kk) out(pos, i);
+    run_g += __popcll(bg);
+    run_e += __popcll(be);
+  }
+  __syncthreads();
+}
+
 // In-place descending bitonic sort of P (a power of two) 64-bit values in LDS.
 __device__ __forceinline__ void bitonic_sort_desc(uint64_t* s, int P) {
   for (int size = 2; size <= P; size <<= 1) {

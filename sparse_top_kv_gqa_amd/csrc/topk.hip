@@ -4,8 +4,9 @@
 // Contexto no Tempo de Inferência", §2 "Oracle Top-K" (exact top-k tokens).
 //
 // One workgroup per row.  Scores map to order-preserving uint32 keys (-0 -> +0, NaN lowest).
-//  * n <= 16384: 256 threads hold the row in registers (up to 64 keys each); a radix select
-//    (8-bit digits, per-wave LDS histograms) finds the k-th largest key in four passes.
+//  * n <= 16384: 256 threads hold the row in registers (up to 64 keys each); a radix search
+//    (8-bit digits, one LDS histogram per digit, one barrier per pass, stopping once a digit's
+//    bin holds exactly the keys still missing) finds the k-th largest key.
 //  * larger n: a 12-bit histogram finds the bin of the k-th key, that bin's keys are gathered
 //    into LDS and bit-searched for the exact threshold (a full radix select when ties overflow
 //    the store), and each wave compacts its own contiguous segment in index order.
@@ -23,69 +24,27 @@ constexpr int kSmallMax = 64 * kSmallThreads;  // 16384
 
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
-// Keys of row `x` held in registers: item c of thread t is element c*256 + t.
-template <int ITEMS>
-__global__ __launch_bounds__(kSmallThreads) void topk_small_kernel(
+// Rows of up to 64*256 keys held in registers (KPT per thread); reg_topk selects with one
+// barrier per radix pass and one for the compaction counts.
+template <int KPT>
+__global__ __launch_bounds__(kSmallThreads) void topk_reg_kernel(
     const float* __restrict__ scores, int64_t s_ld, int n, int k, int32_t* __restrict__ idx,
     int64_t idx_ld, int32_t* __restrict__ count) {
-  __shared__ int red[2][kSmallWaves][2];
-  __shared__ uint32_t hist[kSmallWaves * 256];
-  __shared__ int sh[2];
+  __shared__ __align__(16) uint32_t hist[4 * 256];
+  __shared__ int wsum[2 * KPT * kSmallWaves];
   const int row = blockIdx.x;
-  const float* x = scores + (int64_t)row * s_ld;
   const int kk = min(k, n);
   if (count && threadIdx.x == 0) count[row] = kk;
   if (kk <= 0) return;
+  const float* x = scores + (int64_t)row * s_ld;
   int32_t* out = idx + (int64_t)row * idx_ld;
-  const int t = threadIdx.x, wid = t / kWave, lane = lane_id();
-  uint32_t key[ITEMS];
+  uint32_t key[KPT];
 #pragma unroll
-  for (int c = 0; c < ITEMS; ++c) {
-    const int i = c * kSmallThreads + t;
-    key[c] = i < n ? order_key(x[i]) : 0u;
+  for (int j = 0; j < KPT; ++j) {
+    const int i = j * kSmallThreads + (int)threadIdx.x;
+    key[j] = i < n ? order_key(x[i]) : 0u;
   }
-  // thr = the kk-th largest key; `need` of the keys equal to it rank inside the top kk
-  uint32_t thr;
-  int need;
-  radix_select<kSmallThreads>(
-      [&](auto visit) {
-#pragma unroll
-        for (int c = 0; c < ITEMS; ++c)
-          if (c * kSmallThreads + t < n) visit(key[c]);
-      },
-      kk, hist, sh, &thr, &need);
-  int parity = 0;
-  int run_gt = 0, run_eq = 0;
-#pragma unroll
-  for (int c = 0; c < ITEMS; ++c) {
-    const int i = c * kSmallThreads + t;
-    const bool valid = i < n;
-    const bool gt = valid && key[c] > thr;
-    const bool eq = valid && key[c] == thr;
-    const uint64_t bg = __ballot(gt), be = __ballot(eq);
-    if (lane == 0) {
-      red[parity][wid][0] = __popcll(bg);
-      red[parity][wid][1] = __popcll(be);
-    }
-    __syncthreads();
-    int pre_gt = __popcll(bg & lanemask_lt()), pre_eq = __popcll(be & lanemask_lt());
-    int tot_gt = 0, tot_eq = 0;
-#pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) {
-      const int g = red[parity][w][0], e = red[parity][w][1];
-      if (w < wid) {
-        pre_gt += g;
-        pre_eq += e;
-      }
-      tot_gt += g;
-      tot_eq += e;
-    }
-    const int eq_rank = run_eq + pre_eq;
-    if (gt || (eq && eq_rank < need)) out[run_gt + pre_gt + min(eq_rank, need)] = i;
-    run_gt += tot_gt;
-    run_eq += tot_eq;
-    parity ^= 1;
-  }
+  reg_topk<kSmallThreads>(key, n, kk, hist, wsum, [&](int pos, int i) { out[pos] = i; });
 }
 
 // ---------------------------------------------------------------- wide rows (n > 16384)
@@ -401,18 +360,18 @@ extern "C" SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int
   if (rows == 0) return SPK_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (n <= kSmallMax) {
-    const int items = (n + kSmallThreads - 1) / kSmallThreads;
-#define SPK_SMALL(IT)                                                                          \
-  hipLaunchKernelGGL(topk_small_kernel<IT>, dim3(rows), dim3(kSmallThreads), 0, st, scores, s_ld, \
+    const int kpt = (n + kSmallThreads - 1) / kSmallThreads;
+#define SPK_REG(KPT)                                                                           \
+  hipLaunchKernelGGL(topk_reg_kernel<KPT>, dim3(rows), dim3(kSmallThreads), 0, st, scores, s_ld, \
                      n, k, idx, idx_ld, count)
-    if (items <= 1) SPK_SMALL(1);
-    else if (items <= 2) SPK_SMALL(2);
-    else if (items <= 4) SPK_SMALL(4);
-    else if (items <= 8) SPK_SMALL(8);
-    else if (items <= 16) SPK_SMALL(16);
-    else if (items <= 32) SPK_SMALL(32);
-    else SPK_SMALL(64);
-#undef SPK_SMALL
+    if (kpt <= 1) SPK_REG(1);
+    else if (kpt <= 2) SPK_REG(2);
+    else if (kpt <= 4) SPK_REG(4);
+    else if (kpt <= 8) SPK_REG(8);
+    else if (kpt <= 16) SPK_REG(16);
+    else if (kpt <= 32) SPK_REG(32);
+    else SPK_REG(64);
+#undef SPK_REG
   } else {
     const int C = hist_chunks(rows);
     uint32_t* h = reinterpret_cast<uint32_t*>(ws);

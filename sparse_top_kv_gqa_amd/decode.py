@@ -27,7 +27,7 @@ class BlockSparseDecode:
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, n_tokens: int, Hq: int, block_size: int,
                  k_blocks: int, n_sink: int, n_recent: int, sm_scale: Optional[float] = None,
-                 fused: bool = False, topk_in_attn: bool = False):
+                 fused: bool = False, topk_in_attn: bool = True):
         self.k, self.v = k, v
         B, Hkv, _, d = k.shape
         self.B, self.Hkv, self.Hq, self.d = B, Hkv, Hq, d
@@ -39,9 +39,10 @@ class BlockSparseDecode:
         # when there are many groups with short rows, and loses to the two calls when a few
         # dozen groups leave most of the chip idle)
         self.fused = fused and fused_index_topk_ok("block_pooled", 1, 1, self.nb)
-        # topk_in_attn: the attention launch selects the top-k blocks from the scores itself
-        # (one launch fewer; at this size the selection in every split's prologue costs what
-        # the separate top-k launch costs, so it is off by default)
+        # topk_in_attn (default): the attention launch selects the top-k blocks from the scores
+        # itself, one launch fewer; every split workgroup repeats the selection of its group's
+        # short score row in its prologue (registers, one barrier per radix pass), which costs
+        # less than the separate top-k launch and the gap before the attention
         ok = k.dtype == torch.bfloat16 and self.nb <= 4096 and k_blocks <= 62
         self.topk_in_attn = bool(topk_in_attn) and ok
         if self.topk_in_attn:
@@ -84,16 +85,21 @@ class BlockSparseDecode:
                            sm_scale=self.sm_scale, out=self.out, lse=self.lse, ws=self.ws)
         return self.out, self.lse
 
+    def attend_scores(self, q: torch.Tensor, stream=None):
+        """Top-k of ``scores`` and the attention over the chosen blocks, the sinks and the
+        recent window in one launch (also writes idx and count)."""
+        sparse_topk_decode_attn(self.scores, self.kb, q, self.k, self.v, self.n_tokens,
+                                gran=self.bs, n_sink=self.n_sink, n_recent=self.n_recent,
+                                sm_scale=self.sm_scale, out=self.out, lse=self.lse,
+                                sel_idx=self.idx.view(-1, self.idx.shape[-1]),
+                                sel_count=self.count.view(-1), ws=self.ws, stream=stream)
+        return self.out, self.lse
+
     def step(self, q: torch.Tensor, pred: torch.Tensor):
         if self.topk_in_attn:
             sparse_index_score("block_pooled", pred, self.kpool, self.n_tokens, self.bs,
                                scores=self.scores)
-            sparse_topk_decode_attn(self.scores, self.kb, q, self.k, self.v, self.n_tokens,
-                                    gran=self.bs, n_sink=self.n_sink, n_recent=self.n_recent,
-                                    sm_scale=self.sm_scale, out=self.out, lse=self.lse,
-                                    sel_idx=self.idx.view(-1, self.idx.shape[-1]),
-                                    sel_count=self.count.view(-1), ws=self.ws)
-            return self.out, self.lse
+            return self.attend_scores(q)
         self.select(pred)
         return self.attend(q)
 
