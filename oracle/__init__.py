@@ -11,7 +11,8 @@ Every function cites the passage it follows by page title and section:
 * "SparDA: Atenção Esparsa Desacoplada ..." — §2 Metodologia, subsection
   "Indexador de Previsão Compacto" (one predictor head per GQA group, no
   softmax) and "Seleção Esparsa de Lookahead Treinável" (top-k blocks);
-  "Estratégia de Treinamento" (the compression window of the block grid).
+  "Estratégia de Treinamento" (the compression window of the block grid, and
+  the overlapping (32, 16) compression windows max-pooled onto another grid).
 * "Esparsidade de Contexto no Tempo de Inferência: Ilusão ou Oportunidade?"
   — §2 Metodologia "Oracle Top-K" (exact top-k tokens) and "Implementação de
   Hardware" (per-token, per-query, per-head sparsity); §3C (traffic O(k·d)).
@@ -30,6 +31,9 @@ from .core import (  # noqa: F401
     decode_bf16,
     to_f64,
     block_pool,
+    window_count,
+    window_pool,
+    scores_block_windowed,
     scores_token_group_mean,
     scores_token_per_head,
     scores_block,

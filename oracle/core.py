@@ -74,6 +74,49 @@ def scores_block(pred, kpool) -> np.ndarray:
     return to_f64(kpool) @ to_f64(pred)
 
 
+def window_count(n_tokens: int, window: int, stride: int) -> int:
+    """Number of complete compression windows [stride*w, stride*w + window) inside n tokens."""
+    return 0 if n_tokens < window else (n_tokens - window) // stride + 1
+
+
+def window_pool(keys, window: int, stride: int) -> np.ndarray:
+    """Mean of the keys of every complete compression window.
+
+    SparDA, "Estratégia de Treinamento": at inference the keys are compressed with
+    overlapping windows of kernel 32 and stride 16.  Window w covers tokens
+    [stride*w, stride*w + window); only complete windows exist.  Returns ``[nw, d]``.
+    """
+    k = to_f64(keys)
+    nw = window_count(k.shape[0], window, stride)
+    out = np.empty((nw, k.shape[1]))
+    for w in range(nw):
+        out[w] = k[stride * w: stride * w + window].mean(axis=0)
+    return out
+
+
+def scores_block_windowed(pred, kwin, n_tokens: int, window: int, stride: int,
+                          block_size: int) -> np.ndarray:
+    """Block scores on the selection grid from scores on the compression grid.
+
+    SparDA, "Estratégia de Treinamento": scores on one window grid are max-pooled onto
+    another grid.  Reading taken for the block indexer: the predictor scores every
+    complete compression window (p·Kwin_w, no softmax), and the score of block j
+    (tokens [bs*j, bs*j + bs), complete blocks only) is the largest score among the
+    windows that share at least one token with the block; -inf if there is none.
+    Returns ``[n_tokens // block_size]``.
+    """
+    ws = to_f64(kwin) @ to_f64(pred)
+    nw = ws.shape[0]
+    nb = n_tokens // block_size
+    out = np.full(nb, -np.inf)
+    for j in range(nb):
+        lo_tok, hi_tok = block_size * j, block_size * j + block_size     # [lo, hi)
+        for w in range(nw):
+            if stride * w < hi_tok and stride * w + window > lo_tok:
+                out[j] = max(out[j], ws[w])
+    return out
+
+
 # --------------------------------------------------------------------------- a2
 
 def topk(x, k: int) -> np.ndarray:

@@ -7,7 +7,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .core import (attend, block_pool, importance_update, scores_block,
+from .core import (attend, block_pool, importance_update, scores_block, scores_block_windowed,
+                   window_pool,
                    scores_token_group_mean, scores_token_per_head, selection_tokens,
                    tier_classify, to_f64, topk)
 
@@ -30,6 +31,22 @@ def block_group(pred, keys, vals, q_group, k_blocks, block_size, n_sink, n_recen
     kf, vf = to_f64(keys), to_f64(vals)
     out, lse, _ = attend(q_group, kf[toks], vf[toks], sm_scale)
     return dict(kpool=kp, scores=sc, blocks=blocks, tokens=toks, out=out, lse=lse)
+
+
+def block_windowed_group(pred, keys, vals, q_group, k_blocks, block_size, window, stride,
+                         n_sink, n_recent, sm_scale, kwin=None):
+    """Block-sparse step of one GQA group with the predictor scoring overlapping compression
+    windows (SparDA, "Estratégia de Treinamento": kernel 32, stride 16 at inference) whose
+    scores are max-pooled onto the block grid; then as ``block_group``.
+    """
+    n = np.asarray(keys).shape[0]
+    kw = window_pool(keys, window, stride) if kwin is None else to_f64(kwin)
+    sc = scores_block_windowed(pred, kw, n, window, stride, block_size)
+    blocks = topk(sc, k_blocks)
+    toks = selection_tokens(blocks, block_size, n, n_sink, n_recent)
+    kf, vf = to_f64(keys), to_f64(vals)
+    out, lse, _ = attend(q_group, kf[toks], vf[toks], sm_scale)
+    return dict(kwin=kw, scores=sc, blocks=blocks, tokens=toks, out=out, lse=lse)
 
 
 def group_mean_group(q_tokens, keys, vals, k, sm_scale, n_sink=0, n_recent=0):

@@ -165,6 +165,55 @@ def test_block_score_linearity_matches_token_scores():
     np.testing.assert_allclose(blk, tok, rtol=1e-12)
 
 
+def test_window_grid_equal_to_block_grid_reduces_to_block_scores():
+    # kernel = stride = block size: each block overlaps exactly its own window
+    d, bs = 16, 8
+    keys = rng.standard_normal((5 * bs + 3, d))
+    p = rng.standard_normal(d)
+    kw = oracle.window_pool(keys, bs, bs)
+    np.testing.assert_array_equal(kw, oracle.block_pool(keys, bs))
+    np.testing.assert_array_equal(oracle.scores_block_windowed(p, kw, keys.shape[0], bs, bs, bs),
+                                  oracle.scores_block(p, oracle.block_pool(keys, bs)))
+
+
+@pytest.mark.parametrize("n", [64, 100, 128, 1000, 1024, 1056])
+def test_windowed_scores_match_library_pooling(n):
+    # window scores are torch's avg_pool1d (kernel 32, stride 16) of the token scores; block
+    # scores are torch's max_pool1d (kernel 5, stride 4) of the window scores padded with one
+    # -inf in front: block j of 64 tokens overlaps windows 4j-1 .. 4j+3
+    d, window, stride, bs = 24, 32, 16, 64
+    keys = rng.standard_normal((n, d))
+    p = rng.standard_normal(d)
+    kw = oracle.window_pool(keys, window, stride)
+    assert kw.shape[0] == oracle.window_count(n, window, stride) == (n - window) // stride + 1
+    tok = torch.tensor(keys @ p)[None, None]
+    ws_lib = torch.nn.functional.avg_pool1d(tok, window, stride)[0, 0].numpy()
+    np.testing.assert_allclose(kw @ p, ws_lib, rtol=1e-12, atol=1e-12)
+    nb = n // bs
+    got = oracle.scores_block_windowed(p, kw, n, window, stride, bs)
+    pad = torch.cat([torch.tensor([-math.inf]), torch.tensor(kw @ p),
+                     torch.full((8,), -math.inf)]).to(torch.float64)
+    ref = torch.nn.functional.max_pool1d(pad[None, None], 5, 4)[0, 0].numpy()[:nb]
+    np.testing.assert_allclose(got, ref, rtol=1e-12)
+
+
+def test_windowed_block_score_bounds_each_contained_window():
+    d, window, stride, bs, n = 8, 32, 16, 64, 640
+    keys = rng.standard_normal((n, d))
+    p = rng.standard_normal(d)
+    kw = oracle.window_pool(keys, window, stride)
+    ws = kw @ p
+    blk = oracle.scores_block_windowed(p, kw, n, window, stride, bs)
+    for j in range(n // bs):
+        inside = [w for w in range(len(ws)) if stride * w >= bs * j and stride * w + window <= bs * j + bs]
+        assert len(inside) == 3 and all(blk[j] >= ws[w] for w in inside)
+        assert blk[j] in ws      # the maximum is attained by a window
+    # identical keys: every window and every block scores p·k
+    same = np.tile(rng.standard_normal(d), (n, 1))
+    b2 = oracle.scores_block_windowed(p, oracle.window_pool(same, window, stride), n, window, stride, bs)
+    np.testing.assert_allclose(b2, np.full(n // bs, same[0] @ p), rtol=1e-13)
+
+
 def test_bf16_decode_is_exact():
     vals = np.array([1.0, -2.5, 0.0, -0.0, 3.140625, np.inf, 1e-38], dtype=np.float32)
     t = torch.tensor(vals).to(torch.bfloat16)
