@@ -11,6 +11,9 @@ Workloads (default: block):
                the blocks plus 4 sinks and the 512 most recent tokens.  Steps rotate through 8
                layer caches with fresh queries, so no step finds the previous rows in the 256 MB
                last-level cache.
+  block_windowed  the same layer with the predictor scoring overlapping compression windows
+               (kernel 32, stride 16) of the keys; each 64-token block takes the largest score
+               of the windows it overlaps -> top-32 blocks -> the same attention.
   per_head     batch 4, 32/8 heads, 131072 tokens, 1% outlier keys; every query head keeps its own
                exact top-2% (2622) tokens; each KV group fetches the union of its heads' sets.
   spec_verify  batch 16, 4 draft tokens, 32/8 heads, 65536 tokens; group-mean top-2048 per token;
@@ -47,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="block",
-                    choices=["block", "per_head", "spec_verify", "tiers"])
+                    choices=["block", "block_windowed", "per_head", "spec_verify", "tiers"])
     ap.add_argument("--layers", type=int, default=8, help="block: layer caches to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -224,6 +227,8 @@ def _src_digest(files):
 def measured_traffic(workload):
     """HBM bytes per launch of the roofline kernel (counter readings scaled by the copy
     calibration), or None when the kernel's sources changed since the readings."""
+    if workload not in TRAFFIC:
+        return None
     files, digest, fetch_kib, write_kib = TRAFFIC[workload]
     if _src_digest(files) != digest:
         return None
@@ -257,12 +262,12 @@ def union_rows_block(idx, n_tokens, bs, n_sink, n_recent):
     return int(mask.sum())
 
 
-def bench_block(args):
+def bench_block(args, windowed=False):
     import workloads as W
-    from sparse_top_kv_gqa_amd import sparse_decode_attn
+    from sparse_top_kv_gqa_amd import sparse_decode_attn, window_count
     from sparse_top_kv_gqa_amd.decode import BlockSparseDecode
 
-    w = W.LLAMA8B_BLOCK
+    w = W.LLAMA8B_BLOCK_WIN if windowed else W.LLAMA8B_BLOCK
     K = args.steps or 400
     Wm = args.warmup if args.warmup is not None else 40
     L = args.layers
@@ -271,8 +276,9 @@ def bench_block(args):
     for l in range(L):
         k = W.kv_cache(w, "k", layer=l, device="cuda")
         v = W.kv_cache(w, "v", layer=l, device="cuda")
-        d = BlockSparseDecode(k, v, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent)
-        d.pool(W.predictors(w, step=0, layer=l, device="cuda"))   # block pooling, once per cache
+        d = BlockSparseDecode(k, v, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent,
+                              window=w.window, stride=w.stride)
+        d.pool(W.predictors(w, step=0, layer=l, device="cuda"))   # key pooling, once per cache
         decs.append(d)
         qs.append(W.queries(w, step=1, layer=l, device="cuda"))
         preds.append(W.predictors(w, step=1, layer=l, device="cuda"))
@@ -281,7 +287,9 @@ def bench_block(args):
     for l in range(L):
         decs[l].step(qs[l], preds[l])
         rows.append(union_rows_block(decs[l].idx, w.N, w.block_size, w.n_sink, w.n_recent))
-    index_bytes = w.B * w.Hkv * (w.N // w.block_size) * w.d * 4   # fp32 pooled keys
+    # fp32 pooled keys: one per block, or one per overlapping compression window
+    n_keys = window_count(w.N, w.window, w.stride) if windowed else w.N // w.block_size
+    index_bytes = w.B * w.Hkv * n_keys * w.d * 4
     sel_bytes = [r * ROW_BYTES for r in rows]
     step_bytes = [index_bytes + s for s in sel_bytes]
 
@@ -324,6 +332,7 @@ def bench_block(args):
     att_ms = event_time_ms(attn, 8 * L, stream)
     gather_ms = gather_kernel_ms(attn, 8 * L, stream)
     att_bytes = sum(sel_bytes) / L + score_bytes
+    idx_ms = event_time_ms(lambda i: decs[i % L].score(preds[i % L]), 8 * L, stream)
     bytes_avg = sum(step_bytes[i % L] for i in range(K)) / K
     res = base_result(w, K, Wm, ms_step, bytes_avg, {
         "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
@@ -331,11 +340,16 @@ def bench_block(args):
         "recent": w.n_recent, "layer_caches_rotated": L, "bytes_per_step": int(bytes_avg),
         "selected_rows_per_step": int(sum(sel_bytes) / L / ROW_BYTES),
         "wall_s_timed": round(wall, 4),
-        "attention_call_ms": round(att_ms, 4)})
+        "attention_call_ms": round(att_ms, 4), "index_call_ms": round(idx_ms, 4),
+        "index_GBs": round(index_bytes / (idx_ms * 1e-3) / 1e9, 1)})
+    if windowed:
+        res["config"].update({"window": w.window, "stride": w.stride,
+                              "windows_per_group": n_keys})
     kname = ("attn_partial_mfma_kernel (sparse_topk_decode_attn: top-k + gather)" if in_attn
              else "attn_partial_mfma_kernel (sparse_decode_attn gather)")
-    res["roofline"] = roofline(kname, att_bytes, gather_ms, traffic=measured_traffic("block"))
-    ctx = dict(w=w, dec=decs[0], q=qs[0], pred=preds[0])
+    res["roofline"] = roofline(kname, att_bytes, gather_ms,
+                               traffic=measured_traffic("block_windowed" if windowed else "block"))
+    ctx = dict(w=w, dec=decs[0], q=qs[0], pred=preds[0], windowed=windowed)
     return res, ctx
 
 
@@ -352,8 +366,14 @@ def cpu_block(ctx, seconds):
         kh, vh = host(d0.k[b, h]), host(d0.v[b, h])
         kpool = d0.kpool[b, h].cpu().numpy()
         t0 = time.perf_counter()
-        osteps.block_group(ph[b, 0, h], kh, vh, qh[b, 0, h * G:(h + 1) * G], w.k, w.block_size,
-                           w.n_sink, w.n_recent, scale, kpool=kpool)
+        if ctx.get("windowed"):
+            nw = oracle.window_count(w.N, w.window, w.stride)
+            osteps.block_windowed_group(ph[b, 0, h], kh, vh, qh[b, 0, h * G:(h + 1) * G], w.k,
+                                        w.block_size, w.window, w.stride, w.n_sink, w.n_recent,
+                                        scale, kwin=kpool[:nw])
+        else:
+            osteps.block_group(ph[b, 0, h], kh, vh, qh[b, 0, h * G:(h + 1) * G], w.k,
+                               w.block_size, w.n_sink, w.n_recent, scale, kpool=kpool)
         spent += time.perf_counter() - t0
         done += 1
         if spent >= seconds:
@@ -626,8 +646,8 @@ def main():
     spk.lib()
     if args.calibrate_copy_mib > 0:
         copy_calibration(args.calibrate_copy_mib)
-    if args.workload == "block":
-        res, ctx = bench_block(args)
+    if args.workload in ("block", "block_windowed"):
+        res, ctx = bench_block(args, windowed=args.workload == "block_windowed")
         cpu = cpu_block
     elif args.workload in ("per_head", "spec_verify"):
         res, ctx = bench_token(args, args.workload)

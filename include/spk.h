@@ -171,6 +171,54 @@ SPK_API spk_status sparse_index_topk(spk_index_mode mode,
                                      void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * sparse_window_pool — mean of the keys of every overlapping compression window.
+ *
+ * Passage: SparDA, §2 "Estratégia de Treinamento" (at inference the keys are compressed with
+ * overlapping windows of kernel 32 and stride 16).  Window w of group (b, kvh) covers tokens
+ * [stride*w, stride*w + window); only complete windows exist, nw = (n_tokens - window)/stride + 1
+ * of them (0 when n_tokens < window).  kwin[b,kvh,w,:] = mean of those keys (fp32 sum, then
+ * one multiply by 1/window).  Done once per cache (or per completed window), off the step.
+ *
+ *   keys     device cache [B,Hkv,*,d] with row strides k_sb, k_sh, k_sn (elements, multiples
+ *            of 8, k_sn >= d), 16-byte aligned; F32 or BF16; rows [0, n_tokens) are read.
+ *   window, stride  >= 1, at most 65536.
+ *   kwin     device fp32 [B,Hkv,w_cap,d] contiguous, 16-byte aligned, w_cap >= nw; rows
+ *            [0, nw) of each group written.
+ * Errors: SPK_EINVAL (null pointer, shape, strides, alignment, w_cap < nw), SPK_EUNSUPPORTED
+ * (d not 64/128, dtype).  Enqueues one launch on `stream`; nothing when nw = 0.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status sparse_window_pool(const void* keys, spk_dtype k_dtype,
+                                      int64_t k_sb, int64_t k_sh, int64_t k_sn,
+                                      int B, int Hkv, int d, int n_tokens, int window, int stride,
+                                      float* kwin, int64_t w_cap, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * sparse_index_score_windowed — block scores of the predictor from overlapping windows.
+ *
+ * Passages: SparDA, §2 "Indexador de Previsão Compacto" (one predictor head per GQA group, no
+ * softmax) and "Estratégia de Treinamento" (overlapping (32, 16) compression windows; scores
+ * of one window grid max-pooled onto another).  Reading taken: the predictor p[b,t,kvh]
+ * scores every complete window, p·kwin_w (fp32), and block j — tokens
+ * [block_size*j, block_size*j + block_size), complete blocks only — scores the largest of the
+ * windows that share at least one token with it (-inf when none does).  With window = stride =
+ * block_size this is sparse_index_score in BLOCK_POOLED mode.
+ *
+ *   pred     device [B,T,Hkv,d] contiguous, F32 or BF16, 16-byte aligned; 1 <= T <= 16.
+ *   kwin     device fp32 [B,Hkv,w_cap,d] from sparse_window_pool with the same window/stride.
+ *   window, stride, block_size  >= 1, at most 65536; one block may overlap at most 1021
+ *            windows ((block_size + window)/stride + 3 <= 1024, else SPK_EUNSUPPORTED).
+ *   scores   device fp32 [B,T,Hkv,s_ld], s_ld >= n_tokens / block_size; entries
+ *            [0, n_tokens / block_size) of each row written.
+ * Errors as sparse_window_pool.  One launch; the scores feed topk_select or
+ * sparse_topk_decode_attn exactly like BLOCK_POOLED scores.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status sparse_index_score_windowed(const void* pred, spk_dtype p_dtype,
+                                               const float* kwin, int64_t w_cap,
+                                               int B, int T, int Hkv, int d, int n_tokens,
+                                               int window, int stride, int block_size,
+                                               float* scores, int64_t s_ld, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * sparse_decode_attn — gather the selected K/V rows and run exact attention over them only.
  *
  * Passages: "Esparsidade de Contexto no Tempo de Inferência", §3C (decode reads O(k·d) rows

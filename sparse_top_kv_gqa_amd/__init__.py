@@ -33,7 +33,8 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "topk_select", "sparse_decode_attn_workspace_size", "sparse_decode_attn",
            "importance_accumulate", "tier_classify_workspace_size", "tier_classify",
            "spk_set_attn_timing_events", "sparse_index_topk",
-           "sparse_topk_decode_attn_workspace_size", "sparse_topk_decode_attn")
+           "sparse_topk_decode_attn_workspace_size", "sparse_topk_decode_attn",
+           "sparse_window_pool", "sparse_index_score_windowed")
 
 
 class SpkError(RuntimeError):
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
     L.sparse_index_topk.restype = I
     L.sparse_index_topk.argtypes = [I, P, I, P, I, I64, I64, I64, I, I, I, I, I, I, I, I, P, I64,
                                     P, I64, P, P]
+    L.sparse_window_pool.restype = I
+    L.sparse_window_pool.argtypes = [P, I, I64, I64, I64, I, I, I, I, I, I, P, I64, P]
+    L.sparse_index_score_windowed.restype = I
+    L.sparse_index_score_windowed.argtypes = [P, I, P, I64, I, I, I, I, I, I, I, I, P, I64, P]
     _lib = L
     return L
 
@@ -157,6 +162,47 @@ def sparse_index_score(mode, q: torch.Tensor, keys: torch.Tensor, n_tokens: int,
                                   Hkv, d, n_tokens, block_size, _ptr(scores), scores.stride(-2),
                                   _ptr(pooled_out), _stream(stream))
     _check(st, "sparse_index_score")
+    return scores
+
+
+def window_count(n_tokens: int, window: int, stride: int) -> int:
+    """Complete compression windows [stride*w, stride*w + window) inside n_tokens tokens."""
+    return 0 if n_tokens < window else (n_tokens - window) // stride + 1
+
+
+def sparse_window_pool(keys: torch.Tensor, n_tokens: int, window: int, stride: int,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Mean of the keys of every complete overlapping compression window.  keys: [B,Hkv,*,d]
+    cache view; returns fp32 [B,Hkv,w_cap,d] (w_cap >= the window count; rows past it are not
+    written)."""
+    B, Hkv, _, d = keys.shape
+    nw = window_count(n_tokens, window, stride)
+    if out is None:
+        out = torch.empty((B, Hkv, max(nw, 1), d), dtype=torch.float32, device=keys.device)
+    _contig(out, "out")
+    sb, sh, sn = _rows_view(keys, "keys")
+    st = lib().sparse_window_pool(_ptr(keys), _dt(keys), sb, sh, sn, B, Hkv, d, n_tokens, window,
+                                  stride, _ptr(out), out.shape[2], _stream(stream))
+    _check(st, "sparse_window_pool")
+    return out
+
+
+def sparse_index_score_windowed(pred: torch.Tensor, kwin: torch.Tensor, n_tokens: int, window: int,
+                                stride: int, block_size: int,
+                                scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Block scores from overlapping compression windows: the predictor [B,T,Hkv,d] scores
+    every window of kwin [B,Hkv,w_cap,d] (fp32) and each block takes the largest score of the
+    windows it overlaps.  Returns fp32 [B,T,Hkv,n_tokens // block_size]."""
+    _contig(pred, "pred")
+    _contig(kwin, "kwin")
+    B, T, Hkv, d = pred.shape
+    nb = n_tokens // block_size
+    if scores is None:
+        scores = torch.empty((B, T, Hkv, max(nb, 1)), dtype=torch.float32, device=pred.device)
+    st = lib().sparse_index_score_windowed(_ptr(pred), _dt(pred), _ptr(kwin), kwin.shape[2], B, T,
+                                           Hkv, d, n_tokens, window, stride, block_size,
+                                           _ptr(scores), scores.stride(-2), _stream(stream))
+    _check(st, "sparse_index_score_windowed")
     return scores
 
 

@@ -260,6 +260,146 @@ spk_status launch_blockraw(int ns_pad, dim3 grid, hipStream_t st, const void* q,
 
 int pad_ns(int ns) { return ns <= 1 ? 1 : ns <= 4 ? 4 : ns <= 8 ? 8 : 16; }
 
+// ---------------------------------------------------------------- overlapping compression windows
+//
+// SparDA, "Estratégia de Treinamento": the inference grid compresses the keys with overlapping
+// windows (kernel 32, stride 16), and window scores are max-pooled onto another grid.  Window w
+// covers tokens [stride*w, stride*w + window) (complete windows only); block j covers
+// [bs*j, bs*j + bs) and takes the largest score of the windows that share a token with it.
+
+// Windows overlapping block j: [first, last] (empty when first > last or last < 0).
+__host__ __device__ inline int win_first(int j, int bs, int window, int stride) {
+  const int64_t t = (int64_t)bs * j - window;  // w must satisfy stride*w > t
+  return t < 0 ? 0 : (int)(t / stride + 1);
+}
+__host__ __device__ inline int win_last(int j, int bs, int stride, int nw) {
+  const int64_t w = ((int64_t)bs * (j + 1) - 1) / stride;
+  return (int)(w < nw - 1 ? w : nw - 1);
+}
+
+constexpr int kWinTile = 1024;  // window scores of one workgroup held in LDS (per score vector)
+
+// Pooling: each D/8-lane slot sums one window's rows (8 dims per lane) and stores the mean.
+template <int D, typename KT>
+__global__ __launch_bounds__(kThreads) void window_pool_kernel(
+    const KT* __restrict__ keys, int64_t k_sb, int64_t k_sh, int64_t k_sn, int Hkv, int nw,
+    int window, int stride, int wpw, float* __restrict__ kwin, int64_t w_cap) {
+  constexpr int LPR = D / 8;
+  constexpr int RPS = kWave / LPR;
+  constexpr int STEP = (kThreads / kWave) * RPS;
+  const int group = blockIdx.y;
+  const int b = group / Hkv, kvh = group % Hkv;
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  const int sub = lane % LPR, slot = lane / LPR;
+  const int w0 = blockIdx.x * wpw, w1 = min(w0 + wpw, nw);
+  const KT* gbase = keys + (int64_t)b * k_sb + (int64_t)kvh * k_sh + sub * 8;
+  const float inv = 1.0f / (float)window;
+  for (int wb = w0; wb < w1; wb += STEP) {
+    const int w = wb + wid * RPS + slot;
+    if (w >= w1) continue;
+    const KT* p = gbase + (int64_t)w * stride * k_sn;
+    float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int r = 0;
+    for (; r + kUnroll <= window; r += kUnroll) {
+      Raw8<KT> raw[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) raw[u].load(p + (int64_t)(r + u) * k_sn);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float x[8];
+        raw[u].to_float(x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] += x[i];
+      }
+    }
+    for (; r < window; ++r) {
+      float x[8];
+      load8f(p + (int64_t)r * k_sn, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] += x[i];
+    }
+    float* dst = kwin + ((int64_t)group * w_cap + w) * D + sub * 8;
+    *reinterpret_cast<float4*>(dst) = make_float4(s[0] * inv, s[1] * inv, s[2] * inv, s[3] * inv);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(s[4] * inv, s[5] * inv, s[6] * inv, s[7] * inv);
+  }
+}
+
+// Scoring: a workgroup owns blocks [j0, j1) of one group, scores every window overlapping them
+// (fp32 window keys streamed once, all of a pass's loads in flight) into LDS, then writes each
+// block's maximum.
+template <int D, int NS>
+__global__ __launch_bounds__(kThreads) void index_windowed_kernel(
+    const void* __restrict__ q, int q_bf16, const float* __restrict__ kwin, int64_t w_cap, int T,
+    int Hkv, int ns, int nw, int nb, int window, int stride, int bs, int bpw,
+    float* __restrict__ scores, int64_t s_ld) {
+  constexpr int LPR = D / 8;
+  constexpr int RPS = kWave / LPR;
+  constexpr int WAVES = kThreads / kWave;
+  constexpr int STEP = WAVES * RPS;
+  __shared__ float tile[NS][kWinTile];
+  const int group = blockIdx.y;
+  const int b = group / Hkv, kvh = group % Hkv;
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  const int sub = lane % LPR, slot = lane / LPR;
+  const int j0 = blockIdx.x * bpw, j1 = min(j0 + bpw, nb);
+  if (j0 >= nb) return;
+  const int W0 = win_first(j0, bs, window, stride);
+  const int W1 = win_last(j1 - 1, bs, stride, nw);  // W1 - W0 + 1 <= kWinTile (host sizing)
+
+  float qv[NS][8];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    if (n < ns) {
+      query_slice<D>(SPK_IDX_BLOCK_POOLED, q, q_bf16, b, kvh, n, T, 0, Hkv, 1, sub, qv[n]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[n][i] = 0.f;
+    }
+  }
+  const float* base_ptr = kwin + (int64_t)group * w_cap * D + sub * 8;
+  for (int base = W0; base <= W1; base += STEP * kUnroll) {
+    Raw8<float> raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int w = base + (u * WAVES + wid) * RPS + slot;
+      if (w <= W1) raw[u].load(base_ptr + (int64_t)w * D);
+      else raw[u].zero();
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int w = base + (u * WAVES + wid) * RPS + slot;
+      float x[8];
+      raw[u].to_float(x);
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaf(qv[n][i], x[i], a);
+        a = group_sum<LPR>(a);
+        if (w <= W1 && n % LPR == sub && n < ns) tile[n][w - W0] = a;
+      }
+    }
+  }
+  __syncthreads();
+  const int cnt = j1 - j0;
+  for (int i = threadIdx.x; i < ns * cnt; i += kThreads) {
+    const int n = i / cnt, j = j0 + i % cnt;
+    const int lo = win_first(j, bs, window, stride), hi = win_last(j, bs, stride, nw);
+    float m = -INFINITY;
+    for (int w = lo; w <= hi; ++w) m = fmaxf(m, tile[n][w - W0]);
+    scores[((int64_t)(b * T + n) * Hkv + kvh) * s_ld + j] = m;
+  }
+}
+
+// Blocks per workgroup for the windowed scorer: about four workgroups per CU, and the windows
+// of a workgroup's blocks fit the LDS tile.
+int pick_blocks_per_wg(int nb, int groups, int bs, int window, int stride) {
+  int bpw = 64;
+  while (bpw > 4 && (int64_t)groups * ceil_div(nb, bpw) < 4LL * num_cus()) bpw /= 2;
+  while (bpw > 1 && ((int64_t)bpw * bs + window) / stride + 2 > kWinTile) bpw /= 2;
+  return bpw;
+}
+
 // ---------------------------------------------------------------- scores + top-k in one launch
 //
 // For short candidate rows (a block indexer's few hundred blocks, or a few thousand tokens) the
@@ -551,4 +691,103 @@ extern "C" SPK_API spk_status sparse_index_topk(spk_index_mode mode, const void*
                                           count)
              : launch_fused<64, float>(ns_pad, groups, st, mode, q, q_bf16, keys, k_sb, k_sh, k_sn, T,
                                        Hq, Hkv, G, ns, n_cand, k, scores, s_ld, idx, idx_ld, count);
+}
+
+extern "C" SPK_API spk_status sparse_window_pool(const void* keys, spk_dtype k_dtype, int64_t k_sb,
+                                                 int64_t k_sh, int64_t k_sn, int B, int Hkv, int d,
+                                                 int n_tokens, int window, int stride,
+                                                 float* kwin, int64_t w_cap, void* stream) {
+  using namespace spk;
+  SPK_REQUIRE(keys && kwin, SPK_EINVAL, "sparse_window_pool: null keys or kwin");
+  SPK_REQUIRE(B > 0 && Hkv > 0 && n_tokens >= 0, SPK_EINVAL,
+              "sparse_window_pool: bad shape B=%d Hkv=%d n_tokens=%d", B, Hkv, n_tokens);
+  SPK_REQUIRE(dtype_ok(k_dtype), SPK_EUNSUPPORTED, "sparse_window_pool: unsupported dtype");
+  SPK_REQUIRE(d == 64 || d == 128, SPK_EUNSUPPORTED, "sparse_window_pool: d=%d not in {64,128}", d);
+  SPK_REQUIRE(window >= 1 && stride >= 1 && window <= (1 << 16) && stride <= (1 << 16), SPK_EINVAL,
+              "sparse_window_pool: window %d / stride %d out of range", window, stride);
+  SPK_REQUIRE(k_sn >= d && k_sb >= 0 && k_sh >= 0 && k_sn % 8 == 0 && k_sh % 8 == 0 && k_sb % 8 == 0,
+              SPK_EINVAL, "sparse_window_pool: key strides must be multiples of 8 with k_sn >= d");
+  SPK_REQUIRE(reinterpret_cast<uintptr_t>(keys) % 16 == 0 && reinterpret_cast<uintptr_t>(kwin) % 16 == 0,
+              SPK_EINVAL, "sparse_window_pool: keys and kwin must be 16-byte aligned");
+  const int nw = n_tokens < window ? 0 : (n_tokens - window) / stride + 1;
+  SPK_REQUIRE(w_cap >= nw, SPK_EINVAL, "sparse_window_pool: w_cap %lld < windows %d",
+              (long long)w_cap, nw);
+  clear_error();
+  if (nw == 0) return SPK_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int groups = B * Hkv;
+  const int wpw = pick_rows_per_wg((int64_t)nw * groups, 4 * (64 / (d / 8)));
+  dim3 grid(ceil_div(nw, wpw), groups);
+#define SPK_POOL(DV, KT)                                                                        \
+  hipLaunchKernelGGL((window_pool_kernel<DV, KT>), grid, dim3(kThreads), 0, st,                \
+                     reinterpret_cast<const KT*>(keys), k_sb, k_sh, k_sn, Hkv, nw, window, stride, \
+                     wpw, kwin, w_cap)
+  if (d == 128) {
+    if (k_dtype == SPK_BF16) SPK_POOL(128, uint16_t);
+    else SPK_POOL(128, float);
+  } else {
+    if (k_dtype == SPK_BF16) SPK_POOL(64, uint16_t);
+    else SPK_POOL(64, float);
+  }
+#undef SPK_POOL
+  return check_launch("sparse_window_pool");
+}
+
+extern "C" SPK_API spk_status sparse_index_score_windowed(const void* pred, spk_dtype p_dtype,
+                                                          const float* kwin, int64_t w_cap, int B,
+                                                          int T, int Hkv, int d, int n_tokens,
+                                                          int window, int stride, int block_size,
+                                                          float* scores, int64_t s_ld,
+                                                          void* stream) {
+  using namespace spk;
+  SPK_REQUIRE(pred && kwin && scores, SPK_EINVAL,
+              "sparse_index_score_windowed: null pred, kwin or scores");
+  SPK_REQUIRE(B > 0 && T > 0 && T <= 16 && Hkv > 0 && n_tokens >= 0, SPK_EINVAL,
+              "sparse_index_score_windowed: bad shape B=%d T=%d (1..16) Hkv=%d n_tokens=%d", B, T,
+              Hkv, n_tokens);
+  SPK_REQUIRE(dtype_ok(p_dtype), SPK_EUNSUPPORTED, "sparse_index_score_windowed: unsupported dtype");
+  SPK_REQUIRE(d == 64 || d == 128, SPK_EUNSUPPORTED,
+              "sparse_index_score_windowed: d=%d not in {64,128}", d);
+  SPK_REQUIRE(window >= 1 && stride >= 1 && block_size >= 1 && window <= (1 << 16) &&
+                  stride <= (1 << 16) && block_size <= (1 << 16),
+              SPK_EINVAL, "sparse_index_score_windowed: window %d / stride %d / block %d out of range",
+              window, stride, block_size);
+  SPK_REQUIRE(((int64_t)block_size + window) / stride + 3 <= kWinTile, SPK_EUNSUPPORTED,
+              "sparse_index_score_windowed: a block overlaps more than %d windows", kWinTile - 3);
+  SPK_REQUIRE(reinterpret_cast<uintptr_t>(kwin) % 16 == 0 && reinterpret_cast<uintptr_t>(pred) % 16 == 0,
+              SPK_EINVAL, "sparse_index_score_windowed: pred and kwin must be 16-byte aligned");
+  const int nw = n_tokens < window ? 0 : (n_tokens - window) / stride + 1;
+  const int nb = n_tokens / block_size;
+  SPK_REQUIRE(w_cap >= nw, SPK_EINVAL, "sparse_index_score_windowed: w_cap %lld < windows %d",
+              (long long)w_cap, nw);
+  SPK_REQUIRE(s_ld >= nb, SPK_EINVAL, "sparse_index_score_windowed: s_ld %lld < blocks %d",
+              (long long)s_ld, nb);
+  clear_error();
+  if (nb == 0) return SPK_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int groups = B * Hkv;
+  const int bpw = pick_blocks_per_wg(nb, groups, block_size, window, stride);
+  dim3 grid(ceil_div(nb, bpw), groups);
+  const int q_bf16 = p_dtype == SPK_BF16;
+#define SPK_WIN(DV, NSV)                                                                         \
+  hipLaunchKernelGGL((index_windowed_kernel<DV, NSV>), grid, dim3(kThreads), 0, st, pred, q_bf16, \
+                     kwin, w_cap, T, Hkv, T, nw, nb, window, stride, block_size, bpw, scores, s_ld)
+  const int ns_pad = pad_ns(T);
+  if (d == 128) {
+    switch (ns_pad) {
+      case 1: SPK_WIN(128, 1); break;
+      case 4: SPK_WIN(128, 4); break;
+      case 8: SPK_WIN(128, 8); break;
+      default: SPK_WIN(128, 16); break;
+    }
+  } else {
+    switch (ns_pad) {
+      case 1: SPK_WIN(64, 1); break;
+      case 4: SPK_WIN(64, 4); break;
+      case 8: SPK_WIN(64, 8); break;
+      default: SPK_WIN(64, 16); break;
+    }
+  }
+#undef SPK_WIN
+  return check_launch("sparse_index_score_windowed");
 }

@@ -18,8 +18,9 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import (attn_workspace_size, fused_index_topk_ok, sparse_decode_attn, sparse_index_score,
-               sparse_index_topk, sparse_topk_decode_attn, topk_attn_workspace_size, topk_select,
-               topk_workspace_size, importance_accumulate, tier_classify)
+               sparse_index_score_windowed, sparse_index_topk, sparse_topk_decode_attn,
+               sparse_window_pool, topk_attn_workspace_size, topk_select, topk_workspace_size,
+               importance_accumulate, tier_classify, window_count)
 
 
 class BlockSparseDecode:
@@ -27,8 +28,12 @@ class BlockSparseDecode:
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, n_tokens: int, Hq: int, block_size: int,
                  k_blocks: int, n_sink: int, n_recent: int, sm_scale: Optional[float] = None,
-                 fused: bool = False, topk_in_attn: bool = True):
+                 fused: bool = False, topk_in_attn: bool = True, window: int = 0,
+                 stride: int = 0):
         self.k, self.v = k, v
+        # window > 0: the predictor scores overlapping compression windows (kernel window,
+        # stride stride) and each block takes the largest score of the windows it overlaps
+        self.window, self.stride = window, stride
         B, Hkv, _, d = k.shape
         self.B, self.Hkv, self.Hq, self.d = B, Hkv, Hq, d
         self.n_tokens, self.bs, self.kb = n_tokens, block_size, k_blocks
@@ -38,17 +43,24 @@ class BlockSparseDecode:
         # fused=True: scoring and top-k in one launch (one workgroup per KV group; it pays off
         # when there are many groups with short rows, and loses to the two calls when a few
         # dozen groups leave most of the chip idle)
-        self.fused = fused and fused_index_topk_ok("block_pooled", 1, 1, self.nb)
+        self.fused = fused and window == 0 and fused_index_topk_ok("block_pooled", 1, 1, self.nb)
         # topk_in_attn (default): the attention launch selects the top-k blocks from the scores
         # itself, one launch fewer; every split workgroup repeats the selection of its group's
         # short score row in its prologue (registers, one barrier per radix pass), which costs
         # less than the separate top-k launch and the gap before the attention
-        ok = k.dtype == torch.bfloat16 and self.nb <= 4096 and k_blocks <= 62
+        # (the fused launch walks the blocks, sinks and recent window in list order, which
+        # needs room for all of them in the context)
+        ok = (k.dtype == torch.bfloat16 and self.nb <= 4096 and k_blocks <= 62
+              and n_tokens >= k_blocks * block_size + n_sink + n_recent)
         self.topk_in_attn = bool(topk_in_attn) and ok
         if self.topk_in_attn:
             self.fused = False
         dev = k.device
-        self.kpool = torch.empty((B, Hkv, self.nb, d), dtype=torch.float32, device=dev)
+        if window > 0:
+            self.kpool = torch.empty((B, Hkv, max(window_count(n_tokens, window, stride), 1), d),
+                                     dtype=torch.float32, device=dev)
+        else:
+            self.kpool = torch.empty((B, Hkv, self.nb, d), dtype=torch.float32, device=dev)
         self.scores = torch.empty((B, 1, Hkv, self.nb), dtype=torch.float32, device=dev)
         kk = min(k_blocks, self.nb)
         self.idx = torch.empty((B, 1, Hkv, max(kk, 1)), dtype=torch.int32, device=dev)
@@ -63,10 +75,22 @@ class BlockSparseDecode:
         self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
 
     def pool(self, pred: torch.Tensor):
-        """Mean-pool every complete block of the keys into ``kpool`` (once per cache; the
-        scores of this call are a by-product)."""
+        """Mean-pool every complete block (or compression window) of the keys into ``kpool``
+        (once per cache; block pooling also scores ``pred`` as a by-product)."""
+        if self.window > 0:
+            sparse_window_pool(self.k, self.n_tokens, self.window, self.stride, out=self.kpool)
+            return
         sparse_index_score("block_raw", pred, self.k, self.n_tokens, self.bs, scores=self.scores,
                            pooled_out=self.kpool)
+
+    def score(self, pred: torch.Tensor):
+        """Predictor scores of the blocks (pooled blocks, or windows max-pooled onto blocks)."""
+        if self.window > 0:
+            sparse_index_score_windowed(pred, self.kpool, self.n_tokens, self.window, self.stride,
+                                        self.bs, scores=self.scores)
+        else:
+            sparse_index_score("block_pooled", pred, self.kpool, self.n_tokens, self.bs,
+                               scores=self.scores)
 
     def select(self, pred: torch.Tensor):
         """Predictor scores of the pooled blocks -> the top-k blocks (idx, count)."""
@@ -74,8 +98,7 @@ class BlockSparseDecode:
             sparse_index_topk("block_pooled", pred, self.kpool, self.n_tokens, self.kb, self.bs,
                               scores=self.scores, idx=self.idx, count=self.count)
         else:
-            sparse_index_score("block_pooled", pred, self.kpool, self.n_tokens, self.bs,
-                               scores=self.scores)
+            self.score(pred)
             topk_select(self.scores, self.kb, idx=self.idx, count=self.count)
 
     def attend(self, q: torch.Tensor):
@@ -97,8 +120,7 @@ class BlockSparseDecode:
 
     def step(self, q: torch.Tensor, pred: torch.Tensor):
         if self.topk_in_attn:
-            sparse_index_score("block_pooled", pred, self.kpool, self.n_tokens, self.bs,
-                               scores=self.scores)
+            self.score(pred)
             return self.attend_scores(q)
         self.select(pred)
         return self.attend(q)

@@ -169,3 +169,28 @@ def test_index_topk_validation():
     assert spk.fused_index_topk_ok("block_pooled", 1, 4, 512)
     assert not spk.fused_index_topk_ok("token_per_head", 1, 8, 512)
     assert not spk.fused_index_topk_ok("token_group_mean", 1, 4, 131072)
+
+
+def test_window_entries_validation():
+    L = spk.lib()
+    # sparse_window_pool: null keys; d = 96; w_cap smaller than the window count; stride 0
+    assert L.sparse_window_pool(None, 1, 128 * 64, 128 * 64, 128, 1, 1, 128, 64, 32, 16, Bp, 3,
+                                None) == 1
+    assert L.sparse_window_pool(A, 1, 96 * 64, 96 * 64, 96, 1, 1, 96, 64, 32, 16, Bp, 3, None) == 2
+    assert L.sparse_window_pool(A, 1, 128 * 64, 128 * 64, 128, 1, 1, 128, 64, 32, 16, Bp, 2,
+                                None) == 1
+    assert "w_cap" in _err()
+    assert L.sparse_window_pool(A, 1, 128 * 64, 128 * 64, 128, 1, 1, 128, 64, 32, 0, Bp, 3,
+                                None) == 1
+    # sparse_index_score_windowed: T = 17; s_ld < blocks; a block over too many windows
+    assert L.sparse_index_score_windowed(A, 1, Bp, 3, 1, 17, 1, 128, 64, 32, 16, 64, A, 1,
+                                         None) == 1
+    assert L.sparse_index_score_windowed(A, 1, Bp, 3, 1, 1, 1, 128, 128, 32, 16, 64, A, 2,
+                                         None) == 1
+    assert "w_cap" in _err()
+    assert L.sparse_index_score_windowed(A, 1, Bp, 7, 1, 1, 1, 128, 128, 32, 16, 64, A, 1,
+                                         None) == 1
+    assert "s_ld" in _err()
+    assert L.sparse_index_score_windowed(A, 1, Bp, 1 << 20, 1, 1, 1, 128, 1 << 16, 32, 1, 4096, A,
+                                         64, None) == 2
+    assert spk.window_count(64, 32, 16) == 3 and spk.window_count(31, 32, 16) == 0

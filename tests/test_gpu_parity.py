@@ -846,3 +846,96 @@ def test_block_decode_topk_in_attention_default_full_size():
         outs.append((dec.idx.clone(), out.clone(), lse.clone()))
     assert torch.equal(outs[0][0], outs[1][0])
     assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][2], outs[1][2])
+
+
+# ---------------------------------------------------------------- overlapping compression windows
+
+def _check_scores_with_inf(got, ref, what):
+    """Scores that may hold -inf (blocks no complete window overlaps): the -inf entries must
+    match exactly, the rest within the normwise bar."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{what}: -inf entries differ"
+    fin = np.isfinite(ref)
+    if fin.any():
+        assert rel(got[fin], ref[fin]) <= TOL, f"{what}: {rel(got[fin], ref[fin]):.3e}"
+
+
+@pytest.mark.parametrize("N,window,stride,bs,k", [
+    (64 * 70 + 37, 32, 16, 64, 9),      # the inference grid, ragged tail
+    (64 * 40, 32, 16, 64, 40),          # every block selected (k = blocks)
+    (64 * 33 + 5, 48, 16, 64, 7),       # windows spanning block edges unevenly
+    (64 * 30, 64, 64, 64, 5),           # kernel = stride = block: the block grid itself
+    (32 * 21, 16, 64, 32, 4),           # gaps between windows: some blocks have none (-inf)
+])
+def test_block_windowed_small(N, window, stride, bs, k):
+    w = W.scaled(W.LLAMA8B_BLOCK_WIN, B=2, Hkv=2, Hq=8, N=N, k=k, window=window, stride=stride,
+                 block_size=bs, n_recent=min(512, N // 4))
+    say("block-windowed-small", N, window, stride, bs, k)
+    q = W.queries(w, device=DEV)
+    pred = W.predictors(w, device=DEV)
+    kc = W.kv_cache(w, "k", device=DEV)
+    vc = W.kv_cache(w, "v", device=DEV)
+    dec = BlockSparseDecode(kc, vc, w.N, w.Hq, bs, w.k, w.n_sink, w.n_recent, window=window,
+                            stride=stride)
+    dec.pool(pred)
+    out, lse = dec.step(q, pred)
+    torch.cuda.synchronize()
+    kw = dec.kpool.cpu().numpy()
+    sc = dec.scores.cpu().numpy()
+    idx = dec.idx.cpu().numpy()
+    nw = oracle.window_count(N, window, stride)
+    scale = oracle.softmax_scale(w.d)
+    G = w.G
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kh, vh = host(kc[b, h]), host(vc[b, h])
+            kw_ref = oracle.window_pool(kh, window, stride)
+            check_rows(kw[b, h, :nw], kw_ref, what="window keys")
+            ref = oracle.scores_block_windowed(host(pred)[b, 0, h], kw_ref, N, window, stride, bs)
+            _check_scores_with_inf(sc[b, 0, h], ref, "windowed block scores")
+            blocks = idx[b, 0, h]
+            assert blocks.tolist() == oracle.topk(sc[b, 0, h], w.k).tolist()
+            toks = oracle.selection_tokens(blocks, bs, N, w.n_sink, w.n_recent)
+            o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], kh[toks], vh[toks],
+                                            scale)
+            check_rows(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="attention")
+            np.testing.assert_allclose(lse.cpu().numpy()[b, 0, h * G:(h + 1) * G], l_ref, rtol=TOL)
+    if window == stride == bs:
+        # the block grid itself: the same scores as pooled blocks, up to rounding
+        pooled = spk.sparse_index_score("block_raw", pred, kc, N, bs)
+        check_rows(sc, pooled.cpu().numpy(), tol=1e-5, what="windowed vs pooled")
+
+
+def test_block_windowed_full_size_sampled():
+    w = W.LLAMA8B_BLOCK_WIN
+    say("block-windowed-full", w.name)
+    q = W.queries(w, device=DEV)
+    pred = W.predictors(w, device=DEV)
+    kc = W.kv_cache(w, "k", device=DEV)
+    vc = W.kv_cache(w, "v", device=DEV)
+    dec = BlockSparseDecode(kc, vc, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent,
+                            window=w.window, stride=w.stride)
+    dec.pool(pred)
+    out, lse = dec.step(q, pred)
+    torch.cuda.synchronize()
+    out2, _ = dec.step(q, pred)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    sc = dec.scores.cpu().numpy()
+    idx = dec.idx.cpu().numpy()
+    scale = oracle.softmax_scale(w.d)
+    G = w.G
+    for (b, h) in [(0, 0), (4, 3), (7, 7)]:
+        kh, vh = host(kc[b, h]), host(vc[b, h])
+        r = osteps.block_windowed_group(host(pred)[b, 0, h], kh, vh, host(q)[b, 0, h * G:(h + 1) * G],
+                                        w.k, w.block_size, w.window, w.stride, w.n_sink,
+                                        w.n_recent, scale)
+        check_rows(dec.kpool.cpu().numpy()[b, h, :r["kwin"].shape[0]], r["kwin"], what="window keys")
+        check_rows(sc[b, 0, h], r["scores"], what="windowed block scores")
+        blocks = idx[b, 0, h]
+        assert blocks.tolist() == oracle.topk(sc[b, 0, h], w.k).tolist()
+        assert osteps.topk_band_ok(blocks, r["scores"], w.k, TOL)
+        toks = oracle.selection_tokens(blocks, w.block_size, w.N, w.n_sink, w.n_recent)
+        o_ref, _, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], kh[toks], vh[toks], scale)
+        check_rows(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="attention")

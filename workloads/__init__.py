@@ -48,6 +48,7 @@ class Workload:
     k            top-k (tokens, or blocks when block_size > 1)
     block_size   1 for token selection, else the pooling block
     n_sink, n_recent   always-kept rows
+    window, stride     overlapping compression windows scored instead of whole blocks (0: none)
     """
 
     name: str
@@ -74,6 +75,8 @@ class Workload:
     steps: int = 1
     t0_permille: int = 250
     t01_permille: int = 750
+    window: int = 0
+    stride: int = 0
 
     @property
     def G(self) -> int:
@@ -86,6 +89,11 @@ TINY = Workload("tiny_b1_h4x1_d64_n1024", B=1, T=1, Hq=4, Hkv=1, d=64, N=1024,
 LLAMA8B_BLOCK = Workload("llama3_8b_b8_n32k_block64_top32", B=8, T=1, Hq=32, Hkv=8, d=128,
                          N=32768, kv_dtype="bf16", index_mode="block_pooled",
                          scope="per_kv_head", k=32, block_size=64, n_sink=4, n_recent=512)
+
+LLAMA8B_BLOCK_WIN = Workload("llama3_8b_b8_n32k_win32s16_block64_top32", B=8, T=1, Hq=32, Hkv=8,
+                             d=128, N=32768, kv_dtype="bf16", index_mode="block_windowed",
+                             scope="per_kv_head", k=32, block_size=64, n_sink=4, n_recent=512,
+                             window=32, stride=16)
 
 PER_HEAD_2PCT = Workload("per_head_b4_n128k_top2pct", B=4, T=1, Hq=32, Hkv=8, d=128,
                          N=131072, kv_dtype="bf16", index_mode="token_per_head",
@@ -101,7 +109,8 @@ REASONING_TIERS = Workload("tiers_b32_l28_h28x4_n4k_to_16k", B=32, T=1, Hq=28, H
                            k=0, n_sink=4, n_recent=512, layers=28, n_start=4096,
                            grow_per_step=192, steps=64)
 
-ALL = {w.name: w for w in (TINY, LLAMA8B_BLOCK, PER_HEAD_2PCT, SPEC_VERIFY, REASONING_TIERS)}
+ALL = {w.name: w for w in (TINY, LLAMA8B_BLOCK, LLAMA8B_BLOCK_WIN, PER_HEAD_2PCT, SPEC_VERIFY,
+                           REASONING_TIERS)}
 
 
 def scaled(w: Workload, **changes) -> Workload:
