@@ -20,7 +20,10 @@ Every function cites the passage it follows by page title and section:
   classification), §2 (cumulative importance equation), §3 (Proposition 1),
   §4 (reassignment period Δ).
 * "O Fim do Gargalo de Memória: ... Adaptive DHiSparse" — "Metodologia e
-  Eficiência de Carga" (queries share the retrieval of missing rows).
+  Eficiência de Carga" (queries share the retrieval of missing rows), "A Inovação"
+  (optional residency of rows in HBM while memory allows).
+* "Nem Todos os Pensamentos Necessitam de HBM" §4 "Implementação do Sistema"
+  (differential prefetch of newly promoted rows) — residency_update.
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
 closed forms, invariants, brute force on tiny inputs or an independent library
@@ -42,6 +45,7 @@ from .core import (  # noqa: F401
     attend,
     importance_update,
     tier_classify,
+    residency_update,
     softmax_scale,
 )
 from . import steps  # noqa: F401

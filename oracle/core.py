@@ -255,6 +255,53 @@ def tier_classify(s, n_tokens: int, n_sink: int, n_recent: int, t0_permille: int
     return tier, lst
 
 
+def residency_update(tier, s, loc_old, n_tokens: int, capacity: int):
+    """HBM residency of one sequence's rows after a tier reassignment, and the rows to copy.
+
+    "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro Níveis" (T0
+    stays in HBM; T1 lives in host DDR at full precision and reaches the attention from there)
+    and §4 "Implementação do Sistema" (asynchronous differential prefetch: only newly promoted
+    rows cross PCIe); "O Fim do Gargalo de Memória ...", "A Inovação" (optional residency:
+    rows stay in HBM while memory allows).  Readings taken:
+
+    * HBM holds at most ``capacity`` rows of the sequence, in slots 0..capacity-1 (the same
+      slot in every layer and KV head); every row also lives in host memory at its token index.
+    * the resident set R: the rows of T0 ∪ T1 ranked by (tier ascending, s descending, index
+      ascending), the first min(capacity, |T0 ∪ T1|) of them — T0 first, then the most
+      important T1 rows while slots remain.  A NaN score ranks last in its tier, by index.
+    * a row of R that already holds a slot (0 <= loc_old < capacity) keeps it; the other rows
+      of R, in ascending token order, take the slots no kept row holds, in ascending slot
+      order, and are copied host -> HBM.
+    * loc[tok] = slot for tok in R, else ~tok (the row is read from host slot tok).
+
+    Returns (loc_new ``[n_tokens]`` int64, copies: list of (tok, slot), ascending tok).
+    """
+    tier = np.asarray(tier)[:n_tokens]
+    sv = np.asarray(s, dtype=np.float64)[:n_tokens]
+    old = np.asarray(loc_old, dtype=np.int64)[:n_tokens]
+
+    def key(i):
+        bad = bool(np.isnan(sv[i]))
+        return (int(tier[i]), bad, 0.0 if bad else -sv[i], i)
+
+    live = [i for i in range(n_tokens) if tier[i] <= 1]
+    ranked = sorted(live, key=key)
+    R = sorted(ranked[: min(capacity, len(ranked))])
+    held = {i: int(old[i]) for i in R if 0 <= old[i] < capacity}
+    taken = set(held.values())
+    free = [sl for sl in range(capacity) if sl not in taken]
+    loc = np.array([~i for i in range(n_tokens)], dtype=np.int64)
+    copies = []
+    for i in R:
+        if i in held:
+            loc[i] = held[i]
+        else:
+            sl = free[len(copies)]
+            loc[i] = sl
+            copies.append((i, sl))
+    return loc, copies
+
+
 def softmax_scale(d: int) -> float:
     """Softmax temperature 1/sqrt(d) (the pages do not state one; the usual choice)."""
     return 1.0 / math.sqrt(d)

@@ -407,3 +407,91 @@ def test_page_figures():
     kv = fig["kv_bytes_reasoning_chain"]
     assert abs(kv["tokens"] * 28 * 28 * 128 * 2 * 2 - kv["value_bytes_approx"]) / kv["value_bytes_approx"] < 0.01
     assert fig["tier_reassignment_period"]["value"] == 64
+
+
+# ------------------------------------------------------------------ residency (T1 in host memory)
+
+def _residency_brute(tier, s, loc_old, n, cap):
+    """Independent formulation: pick the best remaining live row `cap` times (T0 before T1,
+    larger s first, NaN last, lower index first), then hand out free slots one by one."""
+    remaining = [i for i in range(n) if tier[i] <= 1]
+    chosen = []
+    while remaining and len(chosen) < cap:
+        def better(a, b):
+            if tier[a] != tier[b]:
+                return tier[a] < tier[b]
+            na, nb = math.isnan(s[a]), math.isnan(s[b])
+            if na != nb:
+                return nb
+            if not na and s[a] != s[b]:
+                return s[a] > s[b]
+            return a < b
+        best = remaining[0]
+        for i in remaining[1:]:
+            if better(i, best):
+                best = i
+        chosen.append(best)
+        remaining.remove(best)
+    loc = [~i for i in range(n)]
+    used = set()
+    for i in chosen:
+        if 0 <= loc_old[i] < cap:
+            loc[i] = int(loc_old[i])
+            used.add(loc[i])
+    nxt = 0
+    copies = []
+    for i in sorted(chosen):
+        if loc[i] < 0:
+            while nxt in used:
+                nxt += 1
+            loc[i] = nxt
+            used.add(nxt)
+            copies.append((i, nxt))
+    return loc, copies
+
+
+@pytest.mark.parametrize("n,cap,seed", [(40, 12, 0), (40, 40, 1), (64, 5, 2), (97, 60, 3),
+                                        (33, 0, 4), (50, 50, 5)])
+def test_residency_update_matches_brute_force(n, cap, seed):
+    r = np.random.default_rng(seed)
+    tier = r.choice(np.array([0, 1, 3], dtype=np.uint8), size=n, p=[0.3, 0.5, 0.2])
+    s = r.integers(0, 6, size=n).astype(np.float32)          # many ties
+    s[r.integers(0, n, 2)] = np.nan
+    # an earlier residency: some rows hold distinct slots below and above the capacity
+    loc_old = np.array([~i for i in range(n)], dtype=np.int64)
+    held = r.choice(n, size=min(n, cap + 3), replace=False)
+    loc_old[held] = r.permutation(cap + 3)[: len(held)]
+    loc, copies = oracle.residency_update(tier, s, loc_old, n, cap)
+    bl, bc = _residency_brute(tier, s, loc_old, n, cap)
+    assert loc.tolist() == bl and copies == bc
+
+
+def test_residency_update_invariants_and_idempotence():
+    r = np.random.default_rng(7)
+    n, cap = 300, 120
+    tier = r.choice(np.array([0, 1, 3], dtype=np.uint8), size=n, p=[0.25, 0.5, 0.25])
+    s = r.standard_normal(n).astype(np.float32)
+    loc0 = np.array([~i for i in range(n)], dtype=np.int64)
+    loc1, c1 = oracle.residency_update(tier, s, loc0, n, cap)
+    R = [i for i in range(n) if loc1[i] >= 0]
+    live = [i for i in range(n) if tier[i] <= 1]
+    assert len(R) == min(cap, len(live))
+    assert all(tier[i] <= 1 for i in R)
+    assert all(loc1[i] >= 0 for i in range(n) if tier[i] == 0)      # |T0| < cap here
+    slots = sorted(int(loc1[i]) for i in R)
+    assert slots == list(range(len(R)))                              # from empty: 0..|R|-1
+    assert [t for t, _ in c1] == R                                   # everything was copied
+    assert all(loc1[i] == ~i for i in range(n) if i not in R)
+    # the same tiers again: nothing moves
+    loc2, c2 = oracle.residency_update(tier, s, loc1, n, cap)
+    assert c2 == [] and loc2.tolist() == loc1.tolist()
+    # importance shifts: kept rows keep their slots, only new rows are copied, into freed slots
+    s2 = s + r.standard_normal(n).astype(np.float32)
+    loc3, c3 = oracle.residency_update(tier, s2, loc1, n, cap)
+    R3 = {i for i in range(n) if loc3[i] >= 0}
+    for i in R3 & set(R):
+        assert loc3[i] == loc1[i]
+    assert {t for t, _ in c3} == R3 - set(R)
+    freed = {int(loc1[i]) for i in set(R) - R3}
+    assert {sl for _, sl in c3} == set(sorted(freed)[: len(c3)])
+    assert len({int(loc3[i]) for i in R3}) == len(R3)
