@@ -21,6 +21,10 @@ Workloads (default: block):
                host memory and are read over PCIe inside the attention kernel.
   tiers        batch 32, 28 layers, 28/4 heads, 64 decode steps growing 4096 -> 16384 tokens:
                tier classification -> attention over T0 ∪ T1 in all layers -> importance update.
+  tiers_offload  the same episode with every row in pinned host memory and --hbm-rows slots
+               per sequence in HBM (default 8192): every --reassign-every steps (default 8) the
+               resident set is recomputed and only newly resident rows are copied over PCIe;
+               the attention reads the other selected rows from host memory.
 
 Prints ONE JSON line.  `value` is the step's algorithmic bytes (index keys read + selected K/V
 rows) per second; `roofline` reports the dominant kernel against the 8 TB/s HBM peak with its
@@ -50,7 +54,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="block",
-                    choices=["block", "block_windowed", "per_head", "spec_verify", "tiers"])
+                    choices=["block", "block_windowed", "per_head", "spec_verify", "tiers",
+                             "tiers_offload"])
+    ap.add_argument("--hbm-rows", type=int, default=8192,
+                    help="tiers_offload: HBM slots per sequence (the rest stays in host memory)")
+    ap.add_argument("--reassign-every", type=int, default=8,
+                    help="tiers_offload: tiered steps between residency reassignments")
     ap.add_argument("--layers", type=int, default=8, help="block: layer caches to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -603,6 +612,110 @@ def bench_tiers(args):
     return res, ctx
 
 
+def bench_tiers_offload(args):
+    """The tiered episode with the memory hierarchy: every row lives in pinned host memory
+    (the DDR tier), HBM holds HBM_ROWS slots per sequence; every REASSIGN tiered steps the
+    resident set is recomputed (T0, then the most important T1 rows while slots remain) and
+    only rows that newly need a slot are copied host -> HBM.  The attention reads every other
+    selected row over PCIe.  Rows appended since the last reassignment have no slot yet and are
+    read from host memory until the next one."""
+    import workloads as W
+    import sparse_top_kv_gqa_amd as spk
+    from sparse_top_kv_gqa_amd.decode import TieredDecode
+
+    w = W.REASONING_TIERS
+    steps = w.steps
+    K = args.steps or steps
+    cap, every = args.hbm_rows, args.reassign_every
+    log(f"generating {w.layers} layer caches of {w.name} into pinned host memory")
+    host_pools, hbm = [], []
+    for l in range(w.layers):
+        pair = []
+        for which in ("k", "v"):
+            t = W.kv_cache(w, which, l, "cuda", n_cap=w.N)
+            h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+            h.copy_(t)
+            pair.append(h)
+            del t
+        host_pools.append(tuple(pair))
+        hbm.append((torch.zeros((w.B, w.Hkv, cap, w.d), dtype=torch.bfloat16, device="cuda"),
+                    torch.zeros((w.B, w.Hkv, cap, w.d), dtype=torch.bfloat16, device="cuda")))
+    torch.cuda.synchronize()
+    qs = [[W.queries(w, step=t, layer=l, device="cuda") for l in range(w.layers)]
+          for t in range(steps)]
+    dec = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
+                       host_caches=host_pools, hbm_rows=cap, reassign_every=every)
+    n_at = [w.n_start + w.grow_per_step * (t + 1) for t in range(steps)]
+    n_steps = min(K, steps)
+    stream = torch.cuda.Stream()
+
+    def run_episode(record=None):
+        dec.s.zero_()
+        dec.evicted.zero_()
+        dec.loc.copy_(~torch.arange(w.N, dtype=torch.int32, device="cuda").repeat(w.B, 1))
+        dec.tiered_steps = 0
+        dec.copies.zero_()
+        for t in range(n_steps):
+            dec.step(qs[t], n_at[t], dense=(t == 0))
+            if record is not None:
+                sel = dec.dense_idx if t == 0 else dec.sel
+                m = torch.arange(w.N, device="cuda")[None, :] < dec.count[:, None].long()
+                ids = sel.long().clamp(0, w.N - 1)     # entries past the count are unused
+                host_rows = ((torch.gather(dec.loc, 1, ids) < 0) & m).sum()
+                record.append((int(dec.count.sum()), int(host_rows), int(dec.copies)))
+
+    rec = []
+    with torch.cuda.stream(stream):
+        run_episode(rec)            # warm-up episode: rows read, rows read from host, copies
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        run_episode()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / n_steps
+    per_layer = w.Hkv * w.layers * ROW_BYTES
+    sel_bytes = [r * per_layer for r, _, _ in rec]
+    pcie_attn = sum(h for _, h, _ in rec) * per_layer
+    copies = rec[-1][2]
+    pcie_copy = copies * per_layer
+    bytes_avg = sum(sel_bytes) / n_steps
+    # the last step's attention in one layer: its host rows cross PCIe inside the gather
+    n_last = n_at[n_steps - 1]
+    (k0, v0), (kh0, vh0) = hbm[0], host_pools[0]
+
+    def attn(i):
+        spk.sparse_decode_attn(qs[n_steps - 1][0], k0, v0, dec.sel, dec.count, "per_seq", n_last,
+                               out=dec.out[0], lse=dec.lse[0], logits=dec.logits[0], ws=dec.ws,
+                               k_host=kh0, v_host=vh0, loc=dec.loc_view, stream=stream)
+    att_ms = event_time_ms(attn, 5, stream)
+    gather_ms = gather_kernel_ms(attn, 5, stream)
+    host_last = rec[-1][1] * w.Hkv * ROW_BYTES
+    res = base_result(w, n_steps, 0, ms_step, bytes_avg, {
+        "workload": w.name + "_offload", "batch": w.B, "layers": w.layers, "q_heads": w.Hq,
+        "kv_heads": w.Hkv, "head_dim": w.d, "context_start": w.n_start,
+        "context_end": n_last, "grow_per_step": w.grow_per_step, "decode_steps": n_steps,
+        "hbm_rows_per_sequence": cap, "reassign_every": every,
+        "bytes_per_step_avg": int(bytes_avg),
+        "host_fetch_fraction": round(sum(h for _, h, _ in rec) / max(1, sum(r for r, _, _ in rec)), 4),
+        "pcie_attention_bytes_per_step": int(pcie_attn / n_steps),
+        "prefetch_bytes_episode": int(pcie_copy), "rows_copied_episode": copies,
+        "episode_s": round(ms_total / 1e3, 4), "wall_s_timed": round(wall, 4),
+        "attention_layer_ms_last_step": round(att_ms, 4),
+        "pcie_GBs_episode": round((pcie_attn + pcie_copy) / (ms_total * 1e-3) / 1e9, 2)})
+    res["roofline"] = roofline(f"attn_partial_mfma_kernel (host rows of one layer at {n_last} "
+                               "tokens, over PCIe)", host_last, gather_ms, bound="pcie",
+                               peak=PCIE_PEAK_GBS,
+                               note=f"HBM rows of the same launch: "
+                                    f"{(rec[-1][0] - rec[-1][1]) * w.Hkv * ROW_BYTES} bytes")
+    ctx = dict(w=w, caches=host_pools, qs=qs, n_last=n_last)
+    return res, ctx
+
+
 def cpu_tiers(ctx, seconds):
     """One dense decode step of whole sequences (all layers), the oracle as it stands."""
     import numpy as np
@@ -652,6 +765,9 @@ def main():
     elif args.workload in ("per_head", "spec_verify"):
         res, ctx = bench_token(args, args.workload)
         cpu = cpu_token
+    elif args.workload == "tiers_offload":
+        res, ctx = bench_tiers_offload(args)
+        cpu = cpu_tiers
     else:
         res, ctx = bench_tiers(args)
         cpu = cpu_tiers

@@ -367,6 +367,63 @@ SPK_API spk_status tier_classify(const float* s, int64_t s_ld, int B, int n_toke
                                  int32_t* sel_idx, int32_t* sel_count, int64_t sel_ld,
                                  void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * residency_update — which rows of each sequence hold an HBM slot after a tier reassignment,
+ * and the list of rows to copy there (differential prefetch).
+ *
+ * Passages: "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro Níveis"
+ * (T0 stays in HBM; T1 lives in host DDR at full precision and reaches the attention from
+ * there) and §4 "Implementação do Sistema" (periodic reassignment; asynchronous differential
+ * prefetch: only newly promoted rows cross PCIe); "O Fim do Gargalo de Memória ...", "A
+ * Inovação" (optional residency: rows stay in HBM while memory allows).  Reading taken: HBM
+ * holds at most `capacity` rows of a sequence, in slots 0..capacity-1 shared by every layer and
+ * KV head; every row also lives in host memory at its token index.  The resident set R is the
+ * first min(capacity, |T0 ∪ T1|) rows of T0 ∪ T1 ranked by (tier ascending, s descending, index
+ * ascending; NaN last in its tier).  A row of R that already holds a slot (0 <= loc < capacity)
+ * keeps it; the other rows of R, in ascending token order, take the slots no kept row holds,
+ * in ascending slot order, and are listed for the copy.  Afterwards loc[tok] = slot for tok in
+ * R and ~tok otherwise, for tok < n_tokens — the form sparse_decode_attn's `loc` reads.
+ *
+ *   tier       device uint8 [B,tier_ld] from tier_classify (0, 1 or 3).
+ *   s          device fp32 [B,s_ld] importance.
+ *   loc        device int32 [B,loc_ld], in/out.  On entry the previous residency (start with
+ *              ~tok everywhere); the slots held must be distinct (else a row may end up read
+ *              from host memory).  Entries >= n_tokens are not touched.
+ *   copy_tok, copy_slot  device int32 [B,copy_ld]: the r-th newly resident row and its slot,
+ *              r < min(copy_count[b], copy_ld) (copy_ld >= capacity lists every copy).
+ *   copy_count device int32 [B]: number of newly resident rows.
+ * Limits: n_tokens and capacity at most 16384 (SPK_EUNSUPPORTED).  One launch, one workgroup
+ * per sequence; no workspace.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier_ld,
+                                    const float* s, int64_t s_ld, int B, int n_tokens,
+                                    int capacity, int32_t* loc, int64_t loc_ld,
+                                    int32_t* copy_tok, int32_t* copy_slot, int64_t copy_ld,
+                                    int32_t* copy_count, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * residency_prefetch — copy the rows residency_update listed from the host pools into their
+ * HBM slots, for every KV head of one layer (the differential prefetch of §4 "Implementação do
+ * Sistema", "Nem Todos os Pensamentos Necessitam de HBM": rows cross PCIe only when they newly
+ * need HBM; full precision, so the attention result is unchanged — Proposition 1).
+ *
+ *   k_host, v_host  pinned host pools (hipHostMalloc'ed; other memory: SPK_EINVAL), row
+ *              (b,kvh,tok) at k_host + b*host_sb + kvh*host_sh + tok*host_sn, tok < host_slots.
+ *   k_hbm, v_hbm    device pools, row (b,kvh,slot) at k_hbm + b*hbm_sb + kvh*hbm_sh +
+ *              slot*hbm_sn, slot < hbm_slots.  Strides in elements; rows 16-byte aligned.
+ *   copy_tok, copy_slot, copy_ld, copy_count: as residency_update wrote them.
+ *   max_copies upper bound on copy_count (sizes the launch; capacity is always enough).
+ * Entries whose token or slot lies outside its pool are skipped.  One launch.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status residency_prefetch(const void* k_host, const void* v_host,
+                                      int64_t host_sb, int64_t host_sh, int64_t host_sn,
+                                      int64_t host_slots, void* k_hbm, void* v_hbm,
+                                      int64_t hbm_sb, int64_t hbm_sh, int64_t hbm_sn,
+                                      int64_t hbm_slots, spk_dtype kv_dtype, int B, int Hkv, int d,
+                                      const int32_t* copy_tok, const int32_t* copy_slot,
+                                      int64_t copy_ld, const int32_t* copy_count, int max_copies,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,8 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "importance_accumulate", "tier_classify_workspace_size", "tier_classify",
            "spk_set_attn_timing_events", "sparse_index_topk",
            "sparse_topk_decode_attn_workspace_size", "sparse_topk_decode_attn",
-           "sparse_window_pool", "sparse_index_score_windowed")
+           "sparse_window_pool", "sparse_index_score_windowed", "residency_update",
+           "residency_prefetch")
 
 
 class SpkError(RuntimeError):
@@ -98,6 +99,11 @@ def lib() -> ctypes.CDLL:
     L.sparse_window_pool.argtypes = [P, I, I64, I64, I64, I, I, I, I, I, I, P, I64, P]
     L.sparse_index_score_windowed.restype = I
     L.sparse_index_score_windowed.argtypes = [P, I, P, I64, I, I, I, I, I, I, I, I, P, I64, P]
+    L.residency_update.restype = I
+    L.residency_update.argtypes = [P, I64, P, I64, I, I, I, P, I64, P, P, I64, P, P]
+    L.residency_prefetch.restype = I
+    L.residency_prefetch.argtypes = [P, P, I64, I64, I64, I64, P, P, I64, I64, I64, I64, I, I, I,
+                                     I, P, P, I64, P, I, P]
     _lib = L
     return L
 
@@ -459,3 +465,38 @@ def sparse_topk_decode_attn(scores: torch.Tensor, k: int, q: torch.Tensor, kc: t
                                        _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "sparse_topk_decode_attn")
     return out, lse
+
+
+# ----------------------------------------------------------------------------- residency
+
+def residency_update(tier: torch.Tensor, s: torch.Tensor, n_tokens: int, capacity: int,
+                     loc: torch.Tensor, copy_tok: torch.Tensor, copy_slot: torch.Tensor,
+                     copy_count: torch.Tensor, stream=None):
+    """HBM slots after a tier reassignment (loc updated in place) and the rows to copy.
+    tier uint8 [B,*], s fp32 [B,*], loc int32 [B,*]; copy_tok/copy_slot int32 [B,copy_ld],
+    copy_count int32 [B]."""
+    B = tier.shape[0]
+    for t, nm in ((tier, "tier"), (s, "s"), (loc, "loc"), (copy_tok, "copy_tok"),
+                  (copy_slot, "copy_slot"), (copy_count, "copy_count")):
+        _contig(t, nm)
+    st = lib().residency_update(_ptr(tier), tier.shape[1], _ptr(s), s.shape[1], B, n_tokens,
+                                capacity, _ptr(loc), loc.shape[1], _ptr(copy_tok), _ptr(copy_slot),
+                                copy_tok.shape[1], _ptr(copy_count), _stream(stream))
+    _check(st, "residency_update")
+
+
+def residency_prefetch(k_host: torch.Tensor, v_host: torch.Tensor, k_hbm: torch.Tensor,
+                       v_hbm: torch.Tensor, copy_tok: torch.Tensor, copy_slot: torch.Tensor,
+                       copy_count: torch.Tensor, max_copies: int, stream=None):
+    """Copy the listed rows of the pinned host pools [B,Hkv,Nh,d] into their slots of the HBM
+    pools [B,Hkv,C,d] (one layer, every KV head)."""
+    hsb, hsh, hsn = _rows_view(k_host, "k_host")
+    dsb, dsh, dsn = _rows_view(k_hbm, "k_hbm")
+    if _rows_view(v_host, "v_host") != (hsb, hsh, hsn) or _rows_view(v_hbm, "v_hbm") != (dsb, dsh, dsn):
+        raise ValueError("k and v pools must share their strides")
+    B, Hkv, _, d = k_hbm.shape
+    st = lib().residency_prefetch(_ptr(k_host), _ptr(v_host), hsb, hsh, hsn, k_host.shape[2],
+                                  _ptr(k_hbm), _ptr(v_hbm), dsb, dsh, dsn, k_hbm.shape[2],
+                                  _dt(k_hbm), B, Hkv, d, _ptr(copy_tok), _ptr(copy_slot),
+                                  copy_tok.shape[1], _ptr(copy_count), max_copies, _stream(stream))
+    _check(st, "residency_prefetch")

@@ -1,0 +1,289 @@
+// residency_update and residency_prefetch: which rows of a sequence hold an HBM slot after a
+// tier reassignment, and the copy of newly resident rows from host memory into their slots.
+//
+// "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro Níveis": T0 stays in
+// HBM, T1 lives in host DDR at full precision and reaches the attention from there; §4
+// "Implementação do Sistema": tiers are reassigned periodically and the prefetch is
+// differential — only rows that newly need HBM cross PCIe.  "O Fim do Gargalo de Memória ...",
+// "A Inovação": rows may stay resident in HBM while memory allows (load-adaptive residency).
+//
+// The resident set of a sequence is the first `capacity` rows of T0 ∪ T1 ranked by (tier
+// ascending, importance descending, index ascending).  A resident row that already holds a
+// slot keeps it; the other resident rows, in ascending token order, take the free slots in
+// ascending order.  Every row also lives in host memory at its token index, so loc[tok] is the
+// HBM slot of a resident row and ~tok otherwise — the form sparse_decode_attn reads.
+#include "select_common.h"
+
+namespace spk {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kItems = 16;                        // tokens per thread: n_tokens <= 16384
+constexpr int kMaxTokens = kItems * kThreads;
+constexpr int kSlotWords = kMaxTokens / 32;       // slot bitmap: capacity <= 16384
+
+// The k-th zero bit (k counted from 0, least significant first) of w.
+__device__ __forceinline__ int nth_zero_bit(uint32_t w, int k) {
+  uint32_t z = ~w;
+  for (int i = 0; i < k; ++i) z &= z - 1;  // drop the k lowest zero bits
+  return __builtin_ctz(z);
+}
+
+__global__ __launch_bounds__(kThreads) void residency_kernel(
+    const uint8_t* __restrict__ tier_all, int64_t tier_ld, const float* __restrict__ s_all,
+    int64_t s_ld, int n, int capacity, int32_t* __restrict__ loc_all, int64_t loc_ld,
+    int32_t* __restrict__ copy_tok, int32_t* __restrict__ copy_slot, int64_t copy_ld,
+    int32_t* __restrict__ copy_count) {
+  __shared__ __align__(16) uint32_t hist[4 * 256];
+  __shared__ uint32_t held_bits[kSlotWords];
+  __shared__ int free_pre[kSlotWords + 1];   // free slots before each bitmap word
+  __shared__ int scratch[kWaves + 1];
+  __shared__ int counts[2];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint8_t* tier = tier_all + (int64_t)b * tier_ld;
+  const float* s = s_all + (int64_t)b * s_ld;
+  int32_t* loc = loc_all + (int64_t)b * loc_ld;
+
+  // tiers and importance keys of this thread's tokens (NaN -> 0, the lowest key)
+  uint8_t tr[kItems];
+  uint32_t key[kItems];
+  int c0 = 0, c1 = 0;
+#pragma unroll
+  for (int c = 0; c < kItems; ++c) {
+    const int i = c * kThreads + tid;
+    tr[c] = i < n ? tier[i] : (uint8_t)3;
+    key[c] = i < n ? order_key(s[i]) : 0u;
+    c0 += tr[c] == 0;
+    c1 += tr[c] == 1;
+  }
+  for (int i = tid; i < 4 * 256; i += kThreads) hist[i] = 0u;
+  for (int i = tid; i < kSlotWords; i += kThreads) held_bits[i] = 0u;
+  if (tid == 0) counts[0] = counts[1] = 0;
+  __syncthreads();
+  atomicAdd(&counts[0], c0);
+  atomicAdd(&counts[1], c1);
+  __syncthreads();
+  const int n0 = counts[0], n1 = counts[1];
+
+  // Which tier is cut by the capacity, and how many of its rows are kept: all of T0 and the
+  // top `cut` of T1, or the top `cut` of T0 alone; a tier kept whole needs no threshold.
+  const int cut_tier = capacity >= n0 + n1 ? -1 : (capacity >= n0 ? 1 : 0);
+  const int cut = cut_tier == 1 ? capacity - n0 : (cut_tier == 0 ? capacity : 0);
+  uint32_t thr = 0;
+  int need = 0;
+  bool whole = false;
+  if (cut > 0) {
+    radix_threshold(
+        [&](auto visit) {
+#pragma unroll
+          for (int c = 0; c < kItems; ++c)
+            if (tr[c] == cut_tier) visit(key[c]);
+        },
+        cut, hist, &thr, &need, &whole);
+  }
+
+  // Pass A, in index order: the resident set, the slots kept rows hold, loc of non-resident
+  // rows; `fresh` marks resident rows that need a slot (bit c: item c).
+  uint32_t fresh = 0;
+  int run_eq = 0;
+#pragma unroll
+  for (int c = 0; c < kItems; ++c) {
+    const int i = c * kThreads + tid;
+    const bool in_cut = tr[c] == cut_tier && cut_tier >= 0;
+    const bool gt = in_cut && cut > 0 && (whole ? key[c] >= thr : key[c] > thr);
+    const bool eq = in_cut && cut > 0 && !whole && key[c] == thr;
+    int tot_eq;
+    const int pre = block_excl_scan(eq ? 1 : 0, scratch, &tot_eq);
+    const bool kept_cut = gt || (eq && run_eq + pre < need);
+    run_eq += tot_eq;
+    bool res;
+    if (cut_tier < 0) res = tr[c] <= 1;
+    else if (cut_tier == 1) res = tr[c] == 0 || kept_cut;
+    else res = kept_cut;
+    if (i < n) {
+      const int old = loc[i];
+      const bool held = res && old >= 0 && old < capacity;
+      if (held) atomicOr(&held_bits[old >> 5], 1u << (old & 31));
+      if (!res) loc[i] = ~i;
+      if (res && !held) fresh |= 1u << c;
+    }
+  }
+  __syncthreads();
+  // free slots per bitmap word (slots >= capacity are not free), then their prefix
+  const int words = (capacity + 31) / 32;
+  int fz = 0;
+  if (tid < words) {
+    const int lim = min(32, capacity - tid * 32);
+    const uint32_t valid = lim == 32 ? 0xFFFFFFFFu : ((1u << lim) - 1u);
+    fz = __popc(~held_bits[tid] & valid);
+  }
+  int tot_free;
+  const int fp = block_excl_scan(tid < kSlotWords ? fz : 0, scratch, &tot_free);
+  if (tid < kSlotWords) free_pre[tid] = fp;
+  if (tid == 0) free_pre[kSlotWords] = tot_free;
+  __syncthreads();
+
+  // Pass B, in index order: the r-th fresh row takes the r-th free slot
+  int run = 0;
+#pragma unroll
+  for (int c = 0; c < kItems; ++c) {
+    const int i = c * kThreads + tid;
+    const bool f = (fresh >> c) & 1u;
+    int tot;
+    const int r = run + block_excl_scan(f ? 1 : 0, scratch, &tot);
+    run += tot;
+    if (f && r < tot_free) {
+      // word w with free_pre[w] <= r < free_pre[w + 1]
+      int lo = 0, hi = words;  // free_pre[lo] <= r < free_pre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (free_pre[mid] <= r) lo = mid;
+        else hi = mid;
+      }
+      const int slot = lo * 32 + nth_zero_bit(held_bits[lo], r - free_pre[lo]);
+      loc[i] = slot;
+      if (r < copy_ld) {
+        copy_tok[(int64_t)b * copy_ld + r] = i;
+        copy_slot[(int64_t)b * copy_ld + r] = slot;
+      }
+    } else if (f && i < n) {
+      loc[i] = ~i;  // no slot left (only when loc held a slot twice): read from host memory
+    }
+  }
+  if (tid == 0) copy_count[b] = run;
+}
+
+// Copy of newly resident rows: row copy_tok[b, r] of the host pools to slot copy_slot[b, r] of
+// the HBM pools, for every KV head; D/8 lanes move one row of K or V with 16-byte accesses.
+template <int D, typename KT>
+__global__ __launch_bounds__(256) void prefetch_kernel(
+    const KT* __restrict__ k_host, const KT* __restrict__ v_host, int64_t h_sb, int64_t h_sh,
+    int64_t h_sn, int64_t host_slots, KT* __restrict__ k_hbm, KT* __restrict__ v_hbm,
+    int64_t d_sb, int64_t d_sh, int64_t d_sn, int64_t hbm_slots,
+    const int32_t* __restrict__ copy_tok, const int32_t* __restrict__ copy_slot, int64_t copy_ld,
+    const int32_t* __restrict__ copy_count, int Hkv, int rows_per_wg) {
+  constexpr int EPL = 16 / sizeof(KT);        // elements per lane and access
+  constexpr int LPR = D / EPL;                // lanes per row
+  constexpr int RPI = 256 / LPR;              // rows per workgroup and pass
+  const int g = blockIdx.y, b = g / Hkv, kvh = g % Hkv;
+  const int cnt = min((int64_t)copy_count[b], copy_ld);
+  const int r0 = blockIdx.x * rows_per_wg;
+  if (r0 >= cnt) return;
+  const int r1 = min(r0 + rows_per_wg, cnt);
+  const int sub = threadIdx.x % LPR;
+  for (int r = r0 + (int)threadIdx.x / LPR; r < r1; r += RPI) {
+    const int tok = copy_tok[(int64_t)b * copy_ld + r];
+    const int slot = copy_slot[(int64_t)b * copy_ld + r];
+    if (tok < 0 || tok >= host_slots || slot < 0 || slot >= hbm_slots) continue;
+    const int64_t hs = (int64_t)b * h_sb + (int64_t)kvh * h_sh + (int64_t)tok * h_sn + sub * EPL;
+    const int64_t ds = (int64_t)b * d_sb + (int64_t)kvh * d_sh + (int64_t)slot * d_sn + sub * EPL;
+    const uint4 kx = *reinterpret_cast<const uint4*>(k_host + hs);
+    const uint4 vx = *reinterpret_cast<const uint4*>(v_host + hs);
+    *reinterpret_cast<uint4*>(k_hbm + ds) = kx;
+    *reinterpret_cast<uint4*>(v_hbm + ds) = vx;
+  }
+}
+
+// A host pool must be page-locked, device-mapped host memory; the kernel reads it through the
+// device address HIP reports for it.
+spk_status host_device_ptr(const void* p, const void** dev, const char* name) {
+  hipPointerAttribute_t at{};
+  const hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(SPK_EINVAL, "residency_prefetch: %s is not memory known to HIP (%s)", name,
+                     hipGetErrorString(e));
+  }
+  if (at.type != hipMemoryTypeHost || at.devicePointer == nullptr)
+    return set_error(SPK_EINVAL, "residency_prefetch: %s must be pinned, device-mapped host memory",
+                     name);
+  *dev = at.devicePointer;
+  return SPK_OK;
+}
+
+}  // namespace
+}  // namespace spk
+
+extern "C" SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier_ld,
+                                               const float* s, int64_t s_ld, int B, int n_tokens,
+                                               int capacity, int32_t* loc, int64_t loc_ld,
+                                               int32_t* copy_tok, int32_t* copy_slot,
+                                               int64_t copy_ld, int32_t* copy_count,
+                                               void* stream) {
+  using namespace spk;
+  SPK_REQUIRE(B >= 0 && n_tokens >= 0 && capacity >= 0, SPK_EINVAL,
+              "residency_update: negative size");
+  SPK_REQUIRE(n_tokens <= kMaxTokens && capacity <= kMaxTokens, SPK_EUNSUPPORTED,
+              "residency_update: n_tokens %d / capacity %d above %d", n_tokens, capacity,
+              kMaxTokens);
+  SPK_REQUIRE(B == 0 || (tier && s && loc && copy_count), SPK_EINVAL,
+              "residency_update: null tier, s, loc or copy_count");
+  SPK_REQUIRE(tier_ld >= n_tokens && s_ld >= n_tokens && loc_ld >= n_tokens, SPK_EINVAL,
+              "residency_update: tier_ld / s_ld / loc_ld smaller than n_tokens");
+  SPK_REQUIRE(copy_ld >= 0 && (copy_ld == 0 || (copy_tok && copy_slot)), SPK_EINVAL,
+              "residency_update: null copy list with copy_ld > 0");
+  clear_error();
+  if (B == 0) return SPK_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(residency_kernel, dim3(B), dim3(kThreads), 0, st, tier, tier_ld, s, s_ld,
+                     n_tokens, capacity, loc, loc_ld, copy_tok, copy_slot, copy_ld, copy_count);
+  return check_launch("residency_update");
+}
+
+extern "C" SPK_API spk_status residency_prefetch(
+    const void* k_host, const void* v_host, int64_t host_sb, int64_t host_sh, int64_t host_sn,
+    int64_t host_slots, void* k_hbm, void* v_hbm, int64_t hbm_sb, int64_t hbm_sh, int64_t hbm_sn,
+    int64_t hbm_slots, spk_dtype kv_dtype, int B, int Hkv, int d, const int32_t* copy_tok,
+    const int32_t* copy_slot, int64_t copy_ld, const int32_t* copy_count, int max_copies,
+    void* stream) {
+  using namespace spk;
+  SPK_REQUIRE(B >= 0 && Hkv > 0 && max_copies >= 0 && copy_ld >= 0, SPK_EINVAL,
+              "residency_prefetch: negative size");
+  SPK_REQUIRE(d == 64 || d == 128, SPK_EUNSUPPORTED, "residency_prefetch: d=%d not in {64,128}", d);
+  SPK_REQUIRE(kv_dtype == SPK_BF16 || kv_dtype == SPK_F32, SPK_EUNSUPPORTED,
+              "residency_prefetch: unsupported dtype");
+  SPK_REQUIRE(B == 0 || max_copies == 0 ||
+                  (k_host && v_host && k_hbm && v_hbm && copy_tok && copy_slot && copy_count),
+              SPK_EINVAL, "residency_prefetch: null pointer");
+  const int64_t align = kv_dtype == SPK_BF16 ? 8 : 4;  // elements in 16 bytes
+  SPK_REQUIRE(host_sn >= d && hbm_sn >= d && host_sb >= 0 && host_sh >= 0 && hbm_sb >= 0 &&
+                  hbm_sh >= 0 && host_sn % align == 0 && host_sh % align == 0 &&
+                  host_sb % align == 0 && hbm_sn % align == 0 && hbm_sh % align == 0 &&
+                  hbm_sb % align == 0,
+              SPK_EINVAL, "residency_prefetch: row strides must cover d and keep 16-byte rows");
+  SPK_REQUIRE(host_slots >= 0 && hbm_slots >= 0, SPK_EINVAL, "residency_prefetch: negative pool");
+  clear_error();
+  if (B == 0 || max_copies == 0) return SPK_OK;
+  const void* kh = nullptr;
+  const void* vh = nullptr;
+  spk_status hs = host_device_ptr(k_host, &kh, "k_host");
+  if (hs != SPK_OK) return hs;
+  hs = host_device_ptr(v_host, &vh, "v_host");
+  if (hs != SPK_OK) return hs;
+  SPK_REQUIRE(reinterpret_cast<uintptr_t>(kh) % 16 == 0 && reinterpret_cast<uintptr_t>(vh) % 16 == 0 &&
+                  reinterpret_cast<uintptr_t>(k_hbm) % 16 == 0 &&
+                  reinterpret_cast<uintptr_t>(v_hbm) % 16 == 0,
+              SPK_EINVAL, "residency_prefetch: pools must be 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int rows_per_wg = 64;
+  const int mc = (int)(max_copies < copy_ld ? max_copies : copy_ld);
+  if (mc == 0) return SPK_OK;
+  dim3 grid((unsigned)((mc + rows_per_wg - 1) / rows_per_wg), (unsigned)(B * Hkv));
+#define SPK_PF(DV, KT)                                                                          \
+  hipLaunchKernelGGL((prefetch_kernel<DV, KT>), grid, dim3(256), 0, st,                         \
+                     reinterpret_cast<const KT*>(kh), reinterpret_cast<const KT*>(vh), host_sb,    \
+                     host_sh, host_sn, host_slots, reinterpret_cast<KT*>(k_hbm),                  \
+                     reinterpret_cast<KT*>(v_hbm), hbm_sb, hbm_sh, hbm_sn, hbm_slots, copy_tok,    \
+                     copy_slot, copy_ld, copy_count, Hkv, rows_per_wg)
+  if (d == 128) {
+    if (kv_dtype == SPK_BF16) SPK_PF(128, uint16_t);
+    else SPK_PF(128, float);
+  } else {
+    if (kv_dtype == SPK_BF16) SPK_PF(64, uint16_t);
+    else SPK_PF(64, float);
+  }
+#undef SPK_PF
+  return check_launch("residency_prefetch");
+}

@@ -20,7 +20,8 @@ import torch
 from . import (attn_workspace_size, fused_index_topk_ok, sparse_decode_attn, sparse_index_score,
                sparse_index_score_windowed, sparse_index_topk, sparse_topk_decode_attn,
                sparse_window_pool, topk_attn_workspace_size, topk_select, topk_workspace_size,
-               importance_accumulate, tier_classify, window_count)
+               importance_accumulate, tier_classify, window_count, residency_update,
+               residency_prefetch)
 
 
 class BlockSparseDecode:
@@ -179,11 +180,20 @@ class TieredDecode:
 
     caches: per-layer (k, v) ``[B, Hkv, Ncap, d]``.  State: importance ``s`` fp32
     ``[B, Ncap]`` and the sticky evicted mask ``[B, Ncap]``.
+
+    host_caches / hbm_rows: the hierarchy in memory.  ``host_caches`` are per-layer pinned
+    (k, v) host pools holding every row (the DDR tier); HBM then holds ``hbm_rows`` slots per
+    sequence (the same slots in every layer and KV head, ``caches`` are those HBM pools, shape
+    ``[B, Hkv, hbm_rows, d]``).  Every ``reassign_every`` tiered steps the resident set is
+    recomputed (T0 first, then the most important T1 rows while slots remain) and only rows
+    that newly need a slot are copied host -> HBM; the attention reads every other selected
+    row from the host pools over PCIe.  The results are bit-identical to the all-HBM layout.
     """
 
     def __init__(self, caches: Sequence, Hq: int, n_cap: int, n_sink: int, n_recent: int,
                  t0_permille: int = 250, t01_permille: int = 750,
-                 sm_scale: Optional[float] = None):
+                 sm_scale: Optional[float] = None, host_caches: Optional[Sequence] = None,
+                 hbm_rows: int = 0, reassign_every: int = 1):
         self.caches = list(caches)
         k0 = self.caches[0][0]
         B, Hkv, _, d = k0.shape
@@ -203,6 +213,29 @@ class TieredDecode:
         self.lse = torch.empty((self.L, B, 1, Hq), dtype=torch.float32, device=dev)
         ws = attn_workspace_size("per_seq", B, 1, Hq, Hkv, d, n_cap, n_cap)
         self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.host = list(host_caches) if host_caches is not None else None
+        self.hbm_rows, self.reassign_every = hbm_rows, max(1, reassign_every)
+        self.tiered_steps = 0
+        if self.host is not None:
+            if len(self.host) != self.L or self.caches[0][0].shape[2] < hbm_rows:
+                raise ValueError("one host pool per layer and HBM pools of hbm_rows slots")
+            # every row starts in host memory only
+            self.loc = (~torch.arange(n_cap, dtype=torch.int32, device=dev)).repeat(B, 1)
+            self.loc_view = self.loc.unsqueeze(1).expand(B, Hkv, n_cap)   # shared by KV heads
+            self.copy_tok = torch.zeros((B, max(hbm_rows, 1)), dtype=torch.int32, device=dev)
+            self.copy_slot = torch.zeros((B, max(hbm_rows, 1)), dtype=torch.int32, device=dev)
+            self.copy_count = torch.zeros((B,), dtype=torch.int32, device=dev)
+            self.copies = torch.zeros((), dtype=torch.int64, device=dev)   # rows copied so far
+
+    def reassign(self, n_tokens: int):
+        """Resident set of every sequence for the current tiers, and the differential copy of
+        the rows that newly hold a slot, in every layer."""
+        residency_update(self.tier, self.s, n_tokens, self.hbm_rows, self.loc, self.copy_tok,
+                         self.copy_slot, self.copy_count)
+        for (kh, vh), (k, v) in zip(self.host, self.caches):
+            residency_prefetch(kh, vh, k, v, self.copy_tok, self.copy_slot, self.copy_count,
+                               self.hbm_rows)
+        self.copies += self.copy_count.sum()
 
     def step(self, qs: Sequence[torch.Tensor], n_tokens: int, dense: bool = False):
         """One decode step at ``n_tokens`` cached tokens.  qs: per-layer Q ``[B, 1, Hq, d]``.
@@ -215,9 +248,19 @@ class TieredDecode:
                           evicted=self.evicted, tier=self.tier, sel_idx=self.sel,
                           sel_count=self.count)
             sel = self.sel
+            if self.host is not None and self.tiered_steps % self.reassign_every == 0:
+                self.reassign(n_tokens)
+            self.tiered_steps += 1
         for l, (k, v) in enumerate(self.caches):
-            sparse_decode_attn(qs[l], k, v, sel, self.count, "per_seq", n_tokens,
-                               sm_scale=self.sm_scale, out=self.out[l], lse=self.lse[l],
-                               logits=self.logits[l], ws=self.ws)
+            if self.host is not None:
+                kh, vh = self.host[l]
+                sparse_decode_attn(qs[l], k, v, sel, self.count, "per_seq", n_tokens,
+                                   sm_scale=self.sm_scale, out=self.out[l], lse=self.lse[l],
+                                   logits=self.logits[l], ws=self.ws, k_host=kh, v_host=vh,
+                                   loc=self.loc_view)
+            else:
+                sparse_decode_attn(qs[l], k, v, sel, self.count, "per_seq", n_tokens,
+                                   sm_scale=self.sm_scale, out=self.out[l], lse=self.lse[l],
+                                   logits=self.logits[l], ws=self.ws)
         importance_accumulate(self.s, sel, self.count, self.logits, self.lse, n_tokens)
         return self.out, self.lse

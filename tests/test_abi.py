@@ -194,3 +194,23 @@ def test_window_entries_validation():
     assert L.sparse_index_score_windowed(A, 1, Bp, 1 << 20, 1, 1, 1, 128, 1 << 16, 32, 1, 4096, A,
                                          64, None) == 2
     assert spk.window_count(64, 32, 16) == 3 and spk.window_count(31, 32, 16) == 0
+
+
+def test_residency_validation():
+    L = spk.lib()
+    # residency_update: n_tokens above the limit; loc_ld < n_tokens; null loc
+    assert L.residency_update(A, 20000, A, 20000, 1, 20000, 100, A, 20000, A, A, 100, A,
+                              None) == 2
+    assert L.residency_update(A, 64, A, 64, 1, 64, 16, A, 32, A, A, 16, A, None) == 1
+    assert "loc_ld" in _err()
+    assert L.residency_update(A, 64, A, 64, 1, 64, 16, None, 64, A, A, 16, A, None) == 1
+    # residency_prefetch: d = 96; strides not keeping 16-byte rows; pageable host pool
+    assert L.residency_prefetch(A, A, 128, 128, 128, 8, Bp, Bp, 128, 128, 128, 8, 1, 1, 1, 96, A,
+                                A, 8, A, 8, None) == 2
+    assert L.residency_prefetch(A, A, 128, 128, 130, 8, Bp, Bp, 128, 128, 128, 8, 1, 1, 1, 128, A,
+                                A, 8, A, 8, None) == 1
+    host = ctypes.create_string_buffer(1 << 16)     # ordinary (pageable) memory
+    hp = ctypes.c_void_p(ctypes.addressof(host))
+    st = L.residency_prefetch(hp, hp, 128, 128, 128, 8, Bp, Bp, 128, 128, 128, 8, 1, 1, 1, 128, A,
+                              A, 8, A, 8, None)
+    assert st in (1, 4) and "k_host" in _err()

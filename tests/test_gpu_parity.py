@@ -939,3 +939,111 @@ def test_block_windowed_full_size_sampled():
         toks = oracle.selection_tokens(blocks, w.block_size, w.N, w.n_sink, w.n_recent)
         o_ref, _, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], kh[toks], vh[toks], scale)
         check_rows(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="attention")
+
+
+# ---------------------------------------------------------------- T1 in host memory, residency
+
+def _random_tiers(r, B, n, p=(0.3, 0.45, 0.25)):
+    tier = r.choice(np.array([0, 1, 3], dtype=np.uint8), size=(B, n), p=list(p))
+    s = r.integers(0, 50, size=(B, n)).astype(np.float32) / 7     # ties
+    s[r.random((B, n)) < 0.002] = np.nan
+    return tier, s
+
+
+@pytest.mark.parametrize("n,cap", [(1000, 300), (1000, 1000), (5000, 700), (16384, 8192),
+                                   (16384, 16384), (777, 0), (3000, 64)])
+def test_residency_update_matches_oracle(n, cap):
+    """Three reassignments in a row (importance and tiers change between them): resident
+    set, slots and copy list bit-exact against the oracle, from the GPU's own previous loc."""
+    say("residency", n, cap)
+    r = np.random.default_rng(n + cap)
+    B = 3
+    loc = torch.tensor(np.array([[~i for i in range(n)]] * B, np.int32), device=DEV)
+    ct = torch.full((B, max(cap, 1)), -7, dtype=torch.int32, device=DEV)
+    cs = torch.full((B, max(cap, 1)), -7, dtype=torch.int32, device=DEV)
+    cc = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    for it in range(3):
+        tier, s = _random_tiers(r, B, n)
+        loc_in = loc.cpu().numpy().copy()
+        spk.residency_update(torch.tensor(tier, device=DEV), torch.tensor(s, device=DEV), n, cap,
+                             loc, ct, cs, cc)
+        torch.cuda.synchronize()
+        for b in range(B):
+            ref_loc, ref_cp = oracle.residency_update(tier[b], s[b], loc_in[b], n, cap)
+            assert loc.cpu().numpy()[b].tolist() == ref_loc.tolist(), (it, b)
+            k = int(cc[b])
+            assert k == len(ref_cp)
+            got = list(zip(ct.cpu().numpy()[b, :k].tolist(), cs.cpu().numpy()[b, :k].tolist()))
+            assert got == ref_cp
+    # the same tiers once more: nothing moves
+    spk.residency_update(torch.tensor(tier, device=DEV), torch.tensor(s, device=DEV), n, cap, loc,
+                         ct, cs, cc)
+    torch.cuda.synchronize()
+    assert int(cc.sum()) == 0
+
+
+def test_residency_prefetch_copies_rows_bit_exact():
+    say("residency-prefetch")
+    B, Hkv, n, d, cap = 2, 3, 600, 128, 250
+    g = torch.Generator(device="cpu").manual_seed(11)
+    kh = torch.randn((B, Hkv, n, d), generator=g).to(torch.bfloat16).pin_memory()
+    vh = torch.randn((B, Hkv, n, d), generator=g).to(torch.bfloat16).pin_memory()
+    kd = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device=DEV)
+    vd = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device=DEV)
+    r = np.random.default_rng(3)
+    tier, s = _random_tiers(r, B, n)
+    loc = torch.tensor(np.array([[~i for i in range(n)]] * B, np.int32), device=DEV)
+    ct = torch.zeros((B, cap), dtype=torch.int32, device=DEV)
+    cs = torch.zeros((B, cap), dtype=torch.int32, device=DEV)
+    cc = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    spk.residency_update(torch.tensor(tier, device=DEV), torch.tensor(s, device=DEV), n, cap, loc,
+                         ct, cs, cc)
+    spk.residency_prefetch(kh, vh, kd, vd, ct, cs, cc, cap)
+    torch.cuda.synchronize()
+    L = loc.cpu().numpy()
+    for b in range(B):
+        res = [i for i in range(n) if L[b, i] >= 0]
+        assert len(res) == min(cap, int((tier[b] <= 1).sum()))
+        slots = torch.tensor([int(L[b, i]) for i in res])
+        toks = torch.tensor(res)
+        assert torch.equal(kd[b][:, slots].cpu(), kh[b][:, toks])
+        assert torch.equal(vd[b][:, slots].cpu(), vh[b][:, toks])
+
+
+@pytest.mark.parametrize("hbm_rows,every", [(700, 1), (300, 2), (1200, 3)])
+def test_tiered_offload_bit_identical_to_all_hbm(hbm_rows, every):
+    """Proposition 1: with T1 (and whatever does not fit) read from pinned host memory, every
+    output, lse, logit and the importance state equal the all-HBM run bit for bit."""
+    w = W.scaled(W.REASONING_TIERS, B=3, layers=3, Hq=8, Hkv=2, N=1200, n_start=600,
+                 grow_per_step=100, steps=6, n_recent=64)
+    say("tiered-offload", hbm_rows, every)
+    caches = [(W.kv_cache(w, "k", l, DEV, n_cap=w.N), W.kv_cache(w, "v", l, DEV, n_cap=w.N))
+              for l in range(w.layers)]
+    host_pools = [(k.cpu().pin_memory(), v.cpu().pin_memory()) for k, v in caches]
+    hbm = [(torch.zeros((w.B, w.Hkv, hbm_rows, w.d), dtype=torch.bfloat16, device=DEV),
+            torch.zeros((w.B, w.Hkv, hbm_rows, w.d), dtype=torch.bfloat16, device=DEV))
+           for _ in range(w.layers)]
+    ref = TieredDecode(caches, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille)
+    off = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
+                       host_caches=host_pools, hbm_rows=hbm_rows, reassign_every=every)
+    for t in range(w.steps):
+        n = w.n_start + w.grow_per_step * t
+        qs = [W.queries(w, step=t, layer=l, device=DEV) for l in range(w.layers)]
+        o1, l1 = ref.step(qs, n, dense=(t == 0))
+        o1, l1, lg1 = o1.clone(), l1.clone(), ref.logits.clone()
+        o2, l2 = off.step(qs, n, dense=(t == 0))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), t
+        for b in range(w.B):
+            c = int(ref.count[b])
+            assert torch.equal(lg1[:, b, ..., :c], off.logits[:, b, ..., :c]), (t, b)
+        assert torch.equal(ref.s, off.s) and torch.equal(ref.tier, off.tier), t
+        if t > 0:
+            # resident rows hold their own K/V in HBM
+            L = off.loc.cpu().numpy()
+            for b in range(w.B):
+                res = np.nonzero(L[b, :n] >= 0)[0]
+                if len(res):
+                    sl = torch.tensor(L[b, res].astype(np.int64))
+                    assert torch.equal(hbm[0][0][b][:, sl].cpu(), caches[0][0][b][:, torch.tensor(res)].cpu())
+    assert int(off.copies) > 0
