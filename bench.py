@@ -216,10 +216,15 @@ def base_result(w, K, W, ms_step, step_bytes, config):
 COPY_KIB = 512 * 1024
 FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
-    "block": (("attn.hip", "spk_internal.h"), "3da6f2e0d68a6feb", 40851.7, 1432.0),
-    "per_head": (("index_score.hip", "spk_internal.h"), "1abbb5de8b313b95", 524476.0, 65536.0),
-    "spec_verify": (("attn.hip", "spk_internal.h"), "3da6f2e0d68a6feb", 271804.0, 8544.76),
-    "tiers": (("attn.hip", "spk_internal.h"), "3da6f2e0d68a6feb", 401360.0, 51456.3),
+    "block": (("attn.hip", "spk_internal.h", "select_common.h"), "d78c422fbe5cb898", 41400.1, 1442.29),
+    "block_windowed": (("attn.hip", "spk_internal.h", "select_common.h"), "d78c422fbe5cb898",
+                       41523.2, 1442.27),
+    "per_head": (("index_score.hip", "spk_internal.h", "select_common.h"), "5ced0021d9d433b8",
+                 524479.0, 65536.0),
+    "spec_verify": (("attn.hip", "spk_internal.h", "select_common.h"), "d78c422fbe5cb898",
+                    271796.0, 8544.93),
+    "tiers": (("attn.hip", "spk_internal.h", "select_common.h"), "d78c422fbe5cb898", 401312.0,
+              51414.2),
 }
 
 
