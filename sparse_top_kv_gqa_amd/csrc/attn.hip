@@ -151,13 +151,19 @@ struct AsmArgs {
   int32_t* ucount;
 };
 
+// kLds: the bitmaps live in LDS.  The two cases are separate instantiations so the LDS case
+// uses LDS instructions: through one generic pointer every bitmap access is a flat access whose
+// wait also covers the list stores in flight, which serialises the compaction loop.
+template <bool kLds>
 __global__ __launch_bounds__(kAsmThreads) void assemble_kernel(AsmArgs a) {
-  __shared__ uint32_t bm_lds[kAsmLdsWords];
+  __shared__ uint32_t bm_lds[kLds ? kAsmLdsWords : 1];
   __shared__ int scratch[kAsmThreads / kWave + 1];
   const int g = blockIdx.x;
   const int b = g / a.Hkv, kvh = g % a.Hkv;
   const int W = a.words;
-  uint32_t* bm = a.bm_global ? a.bm_global + (int64_t)g * a.sets * W : bm_lds;
+  uint32_t* bm;
+  if constexpr (kLds) bm = bm_lds;
+  else bm = a.bm_global + (int64_t)g * a.sets * W;
   for (int i = threadIdx.x; i < a.sets * W; i += kAsmThreads) bm[i] = 0u;
   __syncthreads();
   const int n = a.n_tokens;
@@ -1444,7 +1450,8 @@ extern "C" SPK_API spk_status sparse_decode_attn(
     as.ulist = reinterpret_cast<int32_t*>(w + p.off_list);
     as.umask = p.mask ? reinterpret_cast<uint32_t*>(w + p.off_mask) : nullptr;
     as.ucount = a.ucount;
-    hipLaunchKernelGGL(assemble_kernel, dim3(p.groups), dim3(kAsmThreads), 0, st, as);
+    if (p.bm_lds) hipLaunchKernelGGL(assemble_kernel<true>, dim3(p.groups), dim3(kAsmThreads), 0, st, as);
+    else hipLaunchKernelGGL(assemble_kernel<false>, dim3(p.groups), dim3(kAsmThreads), 0, st, as);
     spk_status e = check_launch("sparse_decode_attn/assemble");
     if (e != SPK_OK) return e;
     a.list = as.ulist;
