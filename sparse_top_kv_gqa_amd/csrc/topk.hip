@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
     const float* __restrict__ scores, int64_t s_ld, int n, int k, int C,
     const uint32_t* __restrict__ ws, int32_t* __restrict__ idx, int64_t idx_ld,
     int32_t* __restrict__ count) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ __align__(16) uint32_t hist[kBins];
   __shared__ uint32_t lkey[kLargeWaves * kListPerWave];
   __shared__ int32_t lidx[kLargeWaves * kListPerWave];
   __shared__ int wave_n[kLargeWaves], wave_gt[kLargeWaves], wave_eq[kLargeWaves];
@@ -152,12 +152,27 @@ __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
   const int seg = ((n + kLargeWaves - 1) / kLargeWaves + 255) / 256 * 256;
   const int sbeg = min(n, wid * seg), send = min(n, sbeg + seg);
 
-  // ---- sum the chunk histograms, find bin b*
+  // ---- sum the chunk histograms (every load of a chunk pair in flight at once), find bin b*
   const uint32_t* hrow = ws + (int64_t)row * C * kBins;
-  for (int i = tid; i < kBins; i += kLargeThreads) {
-    uint32_t t = 0;
-    for (int c = 0; c < C; ++c) t += hrow[(int64_t)c * kBins + i];
-    hist[i] = t;
+  {
+    constexpr int BPT = kBins / kLargeThreads;  // bins per thread
+    uint32_t t[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) t[j] = 0u;
+    for (int c = 0; c < C; c += 2) {
+      uint32_t v[2][BPT];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int j = 0; j < BPT; ++j)
+          v[cc][j] = c + cc < C ? hrow[(int64_t)(c + cc) * kBins + j * kLargeThreads + tid] : 0u;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) t[j] += v[cc][j];
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) hist[j * kLargeThreads + tid] = t[j];
   }
   if (tid == 0) sh[3] = 0;  // overflow flag
   __syncthreads();
@@ -233,32 +248,33 @@ __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
   uint32_t thr;
   int need;
   if (!overflow) {
-    // ---- threshold: bit search over the low 20 bits; each wave counts its own candidates
-    thr = bstar << kBinShift;
-    int parity = 0;
-    __shared__ int cnt2[2][kLargeWaves];
-    for (int bit = kBinShift - 1; bit >= 0; --bit) {
-      const uint32_t cnd = thr | (1u << bit);
-      int c = 0;
-      for (int j = lane; j < nl; j += kWave) {
-        const uint32_t kv = mykey[j];
-        c += ((kv >> kBinShift) == bstar) && kv >= cnd;
-      }
-      c = wave_sum(c);
-      if (lane == 0) cnt2[parity][wid] = c;
-      __syncthreads();
-      int tot = 0;
-#pragma unroll
-      for (int w = 0; w < kLargeWaves; ++w) tot += cnt2[parity][w];
-      if (tot >= kin) thr = cnd;
-      parity ^= 1;
+    // ---- threshold inside bin b*: radix search over the candidates' low 20 bits (moved to the
+    // top of the key), one LDS histogram per digit and one barrier per pass
+    // the bin histogram is no longer read (a barrier followed the gather): reuse it
+    for (int i = tid; i < 4 * 256; i += kLargeThreads) hist[i] = 0u;
+    __syncthreads();
+    bool whole;
+    {
+      uint32_t tthr;
+      int tneed;
+      radix_threshold(
+          [&](auto visit) {
+            for (int j = lane; j < nl; j += kWave) {
+              const uint32_t kv = mykey[j];
+              if ((kv >> kBinShift) == bstar) visit(kv << (32 - kBinShift));
+            }
+          },
+          kin, hist, &tthr, &tneed, &whole);
+      thr = (bstar << kBinShift) | (tthr >> (32 - kBinShift));
+      need = tneed;
     }
     // per-wave kept counts: every entry above the threshold, and ties in index order up to need
+    // (when the search ended on a bin holding exactly the missing keys, every key >= thr)
     int g = 0, e = 0;
     for (int j = lane; j < nl; j += kWave) {
       const uint32_t kv = mykey[j];
-      g += kv > thr;
-      e += kv == thr;
+      g += whole ? kv >= thr : kv > thr;
+      e += !whole && kv == thr;
     }
     g = wave_sum(g);
     e = wave_sum(e);
@@ -281,8 +297,8 @@ __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
     for (int j0 = 0; j0 < nl; j0 += kWave) {
       const int j = j0 + lane;
       const uint32_t kv = j < nl ? mykey[j] : 0u;
-      const bool gt = j < nl && kv > thr;
-      const bool eq = j < nl && kv == thr;
+      const bool gt = j < nl && (whole ? kv >= thr : kv > thr);
+      const bool eq = j < nl && !whole && kv == thr;
       const uint64_t bg = __ballot(gt), be = __ballot(eq);
       const int eq_rank = run_eq + __popcll(be & lt);
       if (gt || (eq && eq_rank < need)) out[run_gt + __popcll(bg & lt) + min(eq_rank, need)] = myidx[j];
