@@ -148,7 +148,7 @@ __device__ __forceinline__ void keep_class(uint32_t key, bool valid, uint32_t th
 // of LDS; wsum: 2*KPT*NT/64 ints of LDS.  Barriers: one to clear, one per radix pass, one for the
 // per-wave counts; the caller waits (barrier) before reading what out wrote to LDS.
 template <int NT, int KPT, typename Out>
-__device__ void reg_topk(const uint32_t (&key)[KPT], int n, int kk, uint32_t* hist, int* wsum,
+__device__ __forceinline__ void reg_topk(const uint32_t (&key)[KPT], int n, int kk, uint32_t* hist, int* wsum,
                          const Out& out) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
@@ -200,7 +200,7 @@ __device__ void reg_topk(const uint32_t (&key)[KPT], int n, int kk, uint32_t* hi
 // element, positions 0..kk-1 in ascending index order.  hist: 4*256 uint32 of LDS; wsum: 2*NT/64
 // ints of LDS.  Every thread calls it after writing its keys; it begins and ends with a barrier.
 template <int NT, typename Out>
-__device__ void lds_topk(const uint32_t* keys, int n, int kk, uint32_t* hist, int* wsum,
+__device__ __forceinline__ void lds_topk(const uint32_t* keys, int n, int kk, uint32_t* hist, int* wsum,
                          const Out& out) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
