@@ -818,17 +818,29 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
     auto keep = [&](int pos, int i) { sc_list[pos] = i; };
     if (n <= kScRegKeys * kThreads) {
       // the usual case: each thread holds its keys in registers
+      // every load issued before any is used (clamped in bounds): one wait
+      float sv[kScRegKeys];
+#pragma unroll
+      for (int j = 0; j < kScRegKeys; ++j) sv[j] = 0.f;
+      if (n > 0) {
+#pragma unroll
+        for (int j = 0; j < kScRegKeys; ++j) sv[j] = srow[min(j * kThreads + tid, n - 1)];
+      }
       uint32_t key[kScRegKeys];
 #pragma unroll
-      for (int j = 0; j < kScRegKeys; ++j) {
-        const int i = j * kThreads + tid;
-        key[j] = i < n ? order_key(srow[i]) : 0u;
-      }
+      for (int j = 0; j < kScRegKeys; ++j) key[j] = j * kThreads + tid < n ? order_key(sv[j]) : 0u;
       if (kk > 0) reg_topk<kThreads>(key, n, kk, sc_hist, sc_wsum, keep);
       __syncthreads();
     } else {
       uint32_t* keys = reinterpret_cast<uint32_t*>(work_s);
-      for (int j = tid; j < n; j += kThreads) keys[j] = order_key(srow[j]);
+      for (int j0 = 0; j0 < n; j0 += 4 * kThreads) {
+        float sv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sv[u] = srow[min(j0 + u * kThreads + tid, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (j0 + u * kThreads + tid < n) keys[j0 + u * kThreads + tid] = order_key(sv[u]);
+      }
       if (kk > 0) lds_topk<kThreads>(keys, n, kk, sc_hist, sc_wsum, keep);
     }
     n_sel = kk;

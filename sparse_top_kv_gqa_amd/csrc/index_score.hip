@@ -106,8 +106,7 @@ __global__ __launch_bounds__(kThreads) void index_rows_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int row = base + (u * WAVES + wid) * RPS + slot;
-      if (row < row1) raw[u].load(base_ptr + (int64_t)row * k_sn);
-      else raw[u].zero();
+      raw[u].load(base_ptr + (int64_t)min(row, row1 - 1) * k_sn);  // past the end: re-read, unused
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {

@@ -50,13 +50,31 @@ __global__ __launch_bounds__(kThreads) void residency_kernel(
   uint8_t tr[kItems];
   uint32_t key[kItems];
   int c0 = 0, c1 = 0;
+  {
+    // every load issued before any is used (clamped in bounds): one wait for the sequence
+    uint8_t tv[kItems];
+    float sv[kItems];
 #pragma unroll
-  for (int c = 0; c < kItems; ++c) {
-    const int i = c * kThreads + tid;
-    tr[c] = i < n ? tier[i] : (uint8_t)3;
-    key[c] = i < n ? order_key(s[i]) : 0u;
-    c0 += tr[c] == 0;
-    c1 += tr[c] == 1;
+    for (int c = 0; c < kItems; ++c) {
+      tv[c] = 3;
+      sv[c] = 0.f;
+    }
+    if (n > 0) {
+#pragma unroll
+      for (int c = 0; c < kItems; ++c) {
+        const int ic = min(c * kThreads + tid, n - 1);
+        tv[c] = tier[ic];
+        sv[c] = s[ic];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kItems; ++c) {
+      const bool in = c * kThreads + tid < n;
+      tr[c] = in ? tv[c] : (uint8_t)3;
+      key[c] = in ? order_key(sv[c]) : 0u;
+      c0 += tr[c] == 0;
+      c1 += tr[c] == 1;
+    }
   }
   for (int i = tid; i < 4 * 256; i += kThreads) hist[i] = 0u;
   for (int i = tid; i < kSlotWords; i += kThreads) held_bits[i] = 0u;

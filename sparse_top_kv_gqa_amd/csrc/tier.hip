@@ -27,6 +27,10 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
   __shared__ int sh[2];
   __shared__ int scratch[kThreads / kWave + 1];
   const int b = blockIdx.x;
+  if (n <= 0) {
+    if (sel_count && threadIdx.x == 0) sel_count[b] = 0;
+    return;
+  }
   const float* s = s_all + (int64_t)b * s_ld;
   uint8_t* ev = evicted ? evicted + (int64_t)b * ev_ld : nullptr;
   uint8_t* tier = tier_all + (int64_t)b * tier_ld;
@@ -42,10 +46,19 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
   };
   uint32_t reg[ITEMS > 0 ? ITEMS : 1];
   if constexpr (ITEMS > 0) {
+    // every load issued before any is used (clamped in bounds): one wait for the sequence
+    float sv[ITEMS];
+    uint8_t ev_v[ITEMS];
+#pragma unroll
+    for (int c = 0; c < ITEMS; ++c) {
+      const int ic = min(c * kThreads + (int)threadIdx.x, n - 1);
+      sv[c] = s[ic];
+      ev_v[c] = ev ? ev[ic] : (uint8_t)0;
+    }
 #pragma unroll
     for (int c = 0; c < ITEMS; ++c) {
       const int i = c * kThreads + threadIdx.x;
-      reg[c] = (i >= lo && i < hi) ? key_of(i) : 0u;
+      reg[c] = (i >= lo && i < hi && !ev_v[c]) ? order_key(sv[c]) : 0u;
     }
   }
   auto for_each = [&](auto&& visit) {

@@ -38,12 +38,14 @@ __global__ __launch_bounds__(kSmallThreads) void topk_reg_kernel(
   if (kk <= 0) return;
   const float* x = scores + (int64_t)row * s_ld;
   int32_t* out = idx + (int64_t)row * idx_ld;
+  // every load issued before any is used (clamped in bounds): one wait for the row
+  float v[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) v[j] = x[min(j * kSmallThreads + (int)threadIdx.x, n - 1)];
   uint32_t key[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int i = j * kSmallThreads + (int)threadIdx.x;
-    key[j] = i < n ? order_key(x[i]) : 0u;
-  }
+  for (int j = 0; j < KPT; ++j)
+    key[j] = j * kSmallThreads + (int)threadIdx.x < n ? order_key(v[j]) : 0u;
   reg_topk<kSmallThreads>(key, n, kk, hist, wsum, [&](int pos, int i) { out[pos] = i; });
 }
 
@@ -71,20 +73,33 @@ int hist_chunks(int rows) {
   return want < 1 ? 1 : (want > 32 ? 32 : want);
 }
 
-__device__ __forceinline__ uint4 keys4_at(const float* x, int i, int n, bool aligned) {
-  uint4 k;
-  if (aligned && i + 3 < n) {
-    const float4 v = *reinterpret_cast<const float4*>(x + i);
-    k = make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
+// Keys of elements i..i+3 of a row of n >= 4 elements, loaded without branches, so a batch of
+// calls issues all its loads before the first wait.  ALIGNED (16-byte aligned rows): one 16-byte
+// load from min(i, last), last = the start of the row's last full group of four; the group past
+// it (the row's final n % 4 elements) reads that last group back instead, so the caller takes
+// those few elements with keys_tail.  Unaligned rows: four clamped 4-byte loads.
+template <bool ALIGNED>
+__device__ __forceinline__ uint4 keys4_load(const float* x, int i, int n) {
+  if constexpr (ALIGNED) {
+    const float4 v = *reinterpret_cast<const float4*>(x + min(i, (n - 4) & ~3));
+    return make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
   } else {
-    k.x = i < n ? order_key(x[i]) : 0u;
-    k.y = i + 1 < n ? order_key(x[i + 1]) : 0u;
-    k.z = i + 2 < n ? order_key(x[i + 2]) : 0u;
-    k.w = i + 3 < n ? order_key(x[i + 3]) : 0u;
+    return make_uint4(order_key(x[min(i, n - 1)]), order_key(x[min(i + 1, n - 1)]),
+                      order_key(x[min(i + 2, n - 1)]), order_key(x[min(i + 3, n - 1)]));
   }
-  return k;
+}
+// Whether the group at i holds its own elements under keys4_load.
+template <bool ALIGNED>
+__device__ __forceinline__ bool keys4_own(int i, int n) {
+  return !ALIGNED || i <= ((n - 4) & ~3);
+}
+// First element keys4_load does not deliver (n when it delivers all of them).
+template <bool ALIGNED>
+__device__ __forceinline__ int keys4_tail(int n) {
+  return ALIGNED ? ((n - 4) & ~3) + 4 : n;
 }
 
+template <bool ALIGNED>
 __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(const float* __restrict__ scores,
                                                                  int64_t s_ld, int n, int k,
                                                                  int C, uint32_t* __restrict__ ws) {
@@ -94,7 +109,6 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(const float* __
   uint32_t* out = ws + ((int64_t)row * C + c) * kBins;
   if (kk <= 0 || kk == n) return;  // the final kernel needs no histogram then
   const float* x = scores + (int64_t)row * s_ld;
-  const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   const int chunk = ((n + C - 1) / C + 1023) / 1024 * 1024;
   const int beg = min(n, c * chunk), end = min(n, beg + chunk);
   for (int i = threadIdx.x; i < kBins; i += kHistThreads) hist[i] = 0u;
@@ -103,15 +117,22 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(const float* __
   for (int i0 = beg + 4 * threadIdx.x; i0 < end; i0 += 4 * kHistThreads * UA) {
     uint4 kq[UA];
 #pragma unroll
-    for (int u = 0; u < UA; ++u) kq[u] = keys4_at(x, i0 + u * 4 * kHistThreads, end, aligned);
+    for (int u = 0; u < UA; ++u) kq[u] = keys4_load<ALIGNED>(x, i0 + u * 4 * kHistThreads, n);
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
       const int i = i0 + u * 4 * kHistThreads;
+      if (!keys4_own<ALIGNED>(i, n)) continue;
       if (i < end) atomicAdd(&hist[kq[u].x >> kBinShift], 1u);
       if (i + 1 < end) atomicAdd(&hist[kq[u].y >> kBinShift], 1u);
       if (i + 2 < end) atomicAdd(&hist[kq[u].z >> kBinShift], 1u);
       if (i + 3 < end) atomicAdd(&hist[kq[u].w >> kBinShift], 1u);
     }
+  }
+  {
+    // the row's final n % 4 elements, when keys4_load did not deliver them
+    const int t = keys4_tail<ALIGNED>(n) + (int)threadIdx.x;
+    if (threadIdx.x < 3 && t < n && t >= beg && t < end)
+      atomicAdd(&hist[order_key(x[t]) >> kBinShift], 1u);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kBins; i += kHistThreads) out[i] = hist[i];
@@ -125,6 +146,7 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
+template <bool ALIGNED>
 __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
     const float* __restrict__ scores, int64_t s_ld, int n, int k, int C,
     const uint32_t* __restrict__ ws, int32_t* __restrict__ idx, int64_t idx_ld,
@@ -146,7 +168,6 @@ __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
     for (int i = tid; i < n; i += kLargeThreads) out[i] = i;
     return;
   }
-  const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   const uint64_t lt = (1ull << lane) - 1ull;
   // wave w's segment of the row: [w*seg, min(n, (w+1)*seg)), seg a multiple of 256
   const int seg = ((n + kLargeWaves - 1) / kLargeWaves + 255) / 256 * 256;
@@ -204,16 +225,17 @@ __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
     for (int c0 = sbeg; c0 < send; c0 += 256 * UB) {
       uint4 kq[UB];
 #pragma unroll
-      for (int u = 0; u < UB; ++u) kq[u] = keys4_at(x, c0 + 256 * u + 4 * lane, send, aligned);
+      for (int u = 0; u < UB; ++u) kq[u] = keys4_load<ALIGNED>(x, c0 + 256 * u + 4 * lane, n);
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int i = c0 + 256 * u + 4 * lane;
+        const bool own = keys4_own<ALIGNED>(i, n);
         const uint32_t kv[4] = {kq[u].x, kq[u].y, kq[u].z, kq[u].w};
         bool take[4];
         int before = 0, tot = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          take[j] = i + j < send && (kv[j] >> kBinShift) >= bstar;
+          take[j] = own && i + j < send && (kv[j] >> kBinShift) >= bstar;
           // index order is lane, then j: this lane's entries follow every entry of lower lanes
           const uint64_t bj = __ballot(take[j]);
           before += __popcll(bj & lt);
@@ -235,6 +257,26 @@ __global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
           }
           nl += tot;
         }
+      }
+    }
+    {
+      // the row's final n % 4 elements, when keys4_load did not deliver them (index order: they
+      // follow everything this wave took)
+      const int t = keys4_tail<ALIGNED>(n) + lane;
+      const uint32_t kv = lane < 3 && t < n ? order_key(x[t]) : 0u;
+      const bool take = lane < 3 && t < n && t >= sbeg && t < send && (kv >> kBinShift) >= bstar;
+      const uint64_t bt = __ballot(take);
+      if (bt) {
+        const int tot = __popcll(bt);
+        if (nl + tot <= kListPerWave) {
+          if (take) {
+            mykey[nl + __popcll(bt & lt)] = kv;
+            myidx[nl + __popcll(bt & lt)] = t;
+          }
+        } else {
+          overflow = true;
+        }
+        nl += tot;
       }
     }
     if (lane == 0) {
@@ -391,12 +433,22 @@ extern "C" SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int
   } else {
     const int C = hist_chunks(rows);
     uint32_t* h = reinterpret_cast<uint32_t*>(ws);
-    hipLaunchKernelGGL(topk_hist_kernel, dim3(C, rows), dim3(kHistThreads), 0, st, scores, s_ld, n, k,
-                       C, h);
+    // rows start 16-byte aligned when the base is and the row stride is a multiple of 4
+    const bool aligned = (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && s_ld % 4 == 0;
+    if (aligned)
+      hipLaunchKernelGGL(topk_hist_kernel<true>, dim3(C, rows), dim3(kHistThreads), 0, st, scores,
+                         s_ld, n, k, C, h);
+    else
+      hipLaunchKernelGGL(topk_hist_kernel<false>, dim3(C, rows), dim3(kHistThreads), 0, st, scores,
+                         s_ld, n, k, C, h);
     spk_status e = check_launch("topk_select/histogram");
     if (e != SPK_OK) return e;
-    hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kLargeThreads), 0, st, scores, s_ld, n, k,
-                       C, h, idx, idx_ld, count);
+    if (aligned)
+      hipLaunchKernelGGL(topk_final_kernel<true>, dim3(rows), dim3(kLargeThreads), 0, st, scores,
+                         s_ld, n, k, C, h, idx, idx_ld, count);
+    else
+      hipLaunchKernelGGL(topk_final_kernel<false>, dim3(rows), dim3(kLargeThreads), 0, st, scores,
+                         s_ld, n, k, C, h, idx, idx_ld, count);
   }
   return check_launch("topk_select");
 }
