@@ -216,15 +216,11 @@ def base_result(w, K, W, ms_step, step_bytes, config):
 COPY_KIB = 512 * 1024
 FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
-    "block": (("attn.hip", "spk_internal.h", "select_common.h"), "d78c422fbe5cb898", 41400.1, 1442.29),
-    "block_windowed": (("attn.hip", "spk_internal.h", "select_common.h"), "d78c422fbe5cb898",
-                       41523.2, 1442.27),
-    "per_head": (("index_score.hip", "spk_internal.h", "select_common.h"), "5ced0021d9d433b8",
-                 524479.0, 65536.0),
-    "spec_verify": (("attn.hip", "spk_internal.h", "select_common.h"), "d78c422fbe5cb898",
-                    271796.0, 8544.93),
-    "tiers": (("attn.hip", "spk_internal.h", "select_common.h"), "d78c422fbe5cb898", 401312.0,
-              51414.2),
+    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "bdfcb036e030b00c", 41388.7, 1442.23),
+    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "bdfcb036e030b00c", 41512.1, 1442.31),
+    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "1e6d5e9e7811c2f5", 524481.0, 65536.0),
+    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "bdfcb036e030b00c", 271798.0, 8545.06),
+    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "bdfcb036e030b00c", 401316.0, 51431.7),
 }
 
 

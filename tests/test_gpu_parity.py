@@ -1047,3 +1047,83 @@ def test_tiered_offload_bit_identical_to_all_hbm(hbm_rows, every):
                     sl = torch.tensor(L[b, res].astype(np.int64))
                     assert torch.equal(hbm[0][0][b][:, sl].cpu(), caches[0][0][b][:, torch.tensor(res)].cpu())
     assert int(off.copies) > 0
+
+
+def test_windowed_scores_several_predictors_and_d64():
+    """Windowed scoring with T = 3 predictor vectors per KV head (several score rows per
+    group), d = 64 and fp32 predictors: every score row against the oracle."""
+    say("windowed-T3-d64")
+    r = np.random.default_rng(21)
+    B, T, Hkv, d, N, window, stride, bs = 2, 3, 2, 64, 64 * 37 + 20, 32, 16, 64
+    k = torch.tensor(r.standard_normal((B, Hkv, N, d)), dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    pred = torch.tensor(r.standard_normal((B, T, Hkv, d)), dtype=torch.float32, device=DEV)
+    kw = spk.sparse_window_pool(k, N, window, stride)
+    sc = spk.sparse_index_score_windowed(pred, kw, N, window, stride, bs)
+    torch.cuda.synchronize()
+    nw = oracle.window_count(N, window, stride)
+    for b in range(B):
+        for h in range(Hkv):
+            kw_ref = oracle.window_pool(host(k[b, h]), window, stride)
+            check_rows(kw.cpu().numpy()[b, h, :nw], kw_ref, what="window keys d64")
+            for t in range(T):
+                ref = oracle.scores_block_windowed(host(pred)[b, t, h], kw_ref, N, window, stride, bs)
+                check_rows(sc.cpu().numpy()[b, t, h][None], ref[None], what="windowed scores T3")
+
+
+@pytest.mark.parametrize("d,dtype", [(64, torch.bfloat16), (128, torch.float32), (64, torch.float32)])
+def test_residency_prefetch_other_shapes(d, dtype):
+    """The copy for d = 64 and fp32 pools, capacity above the live rows, n not a multiple of
+    32: resident rows hold their host rows bit for bit."""
+    say("residency-prefetch-shapes", d, dtype)
+    B, Hkv, n, cap = 2, 2, 333, 400
+    g = torch.Generator(device="cpu").manual_seed(d)
+    kh = torch.randn((B, Hkv, n, d), generator=g).to(dtype).pin_memory()
+    vh = torch.randn((B, Hkv, n, d), generator=g).to(dtype).pin_memory()
+    kd = torch.zeros((B, Hkv, cap, d), dtype=dtype, device=DEV)
+    vd = torch.zeros((B, Hkv, cap, d), dtype=dtype, device=DEV)
+    r = np.random.default_rng(d)
+    tier, s = _random_tiers(r, B, n)
+    loc = torch.tensor(np.array([[~i for i in range(n)]] * B, np.int32), device=DEV)
+    ct = torch.zeros((B, cap), dtype=torch.int32, device=DEV)
+    cs = torch.zeros((B, cap), dtype=torch.int32, device=DEV)
+    cc = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    spk.residency_update(torch.tensor(tier, device=DEV), torch.tensor(s, device=DEV), n, cap, loc,
+                         ct, cs, cc)
+    spk.residency_prefetch(kh, vh, kd, vd, ct, cs, cc, cap)
+    torch.cuda.synchronize()
+    L = loc.cpu().numpy()
+    for b in range(B):
+        ref_loc, _ = oracle.residency_update(tier[b], s[b], np.array([~i for i in range(n)]), n, cap)
+        assert L[b].tolist() == ref_loc.tolist()
+        res = [i for i in range(n) if L[b, i] >= 0]
+        assert len(res) == int((tier[b] <= 1).sum())          # capacity above the live rows
+        slots = torch.tensor([int(L[b, i]) for i in res])
+        toks = torch.tensor(res)
+        assert torch.equal(kd[b][:, slots].cpu(), kh[b][:, toks])
+        assert torch.equal(vd[b][:, slots].cpu(), vh[b][:, toks])
+
+
+def test_topk_decode_attn_d64_and_bound():
+    """sparse_topk_decode_attn at d = 64, and with the candidate row longer than 1024 (the
+    selection keeps its keys in LDS instead of registers): bit-identical to the two calls."""
+    say("topk-decode-attn-d64-lds")
+    r = np.random.default_rng(8)
+    for d, nb in ((64, 300), (128, 3000)):
+        B, Hq, Hkv, bs, k = 2, 8, 2, 16, 20
+        N = nb * bs
+        q = torch.tensor(r.standard_normal((B, 1, Hq, d)), dtype=torch.float32).to(torch.bfloat16).to(DEV)
+        kc = torch.tensor(r.standard_normal((B, Hkv, N, d)), dtype=torch.float32).to(torch.bfloat16).to(DEV)
+        vc = torch.tensor(r.standard_normal((B, Hkv, N, d)), dtype=torch.float32).to(torch.bfloat16).to(DEV)
+        sc = torch.tensor(r.standard_normal((B, 1, Hkv, nb)), dtype=torch.float32, device=DEV)
+        o1, l1 = torch.empty((B, 1, Hq, d), device=DEV), torch.empty((B, 1, Hq), device=DEV)
+        sel = torch.empty((B * Hkv, k), dtype=torch.int32, device=DEV)
+        cnt = torch.empty((B * Hkv,), dtype=torch.int32, device=DEV)
+        spk.sparse_topk_decode_attn(sc, k, q, kc, vc, N, gran=bs, n_sink=4, n_recent=64,
+                                    out=o1, lse=l1, sel_idx=sel, sel_count=cnt)
+        idx, icount = spk.topk_select(sc, k)
+        o2, l2 = spk.sparse_decode_attn(q, kc, vc, idx, icount, "per_kv_head", N, gran=bs,
+                                        n_sink=4, n_recent=64)
+        torch.cuda.synchronize()
+        i2 = idx.reshape(B * Hkv, k)
+        assert torch.equal(sel, i2)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
