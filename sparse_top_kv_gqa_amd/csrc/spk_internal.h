@@ -107,20 +107,6 @@ constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 
-// Inclusive prefix sum of an int over the wave with DPP lane moves (no LDS round trips): a
-// scan inside each row of 16 lanes (shifts by 1, 2, 4, 8; lanes shifted in from outside the row
-// add 0), then the row totals carried forward with the broadcasts of lane 15 (into rows 1 and 3)
-// and of lane 31 (into rows 2 and 3).
-__device__ __forceinline__ int wave_incl_scan_dpp(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return x;
-}
-
 // Sum over aligned groups of kLanes (2, 4, 8 or 16) lanes; every lane of the group gets the
 // same bits (each step adds a lane's value and its partner's, which commute).
 template <int kLanes>
@@ -144,16 +130,22 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Inclusive prefix sum of an int over the wave.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+// Inclusive prefix sum of an int over the wave with DPP lane moves (no LDS round trips): a
+// scan inside each row of 16 lanes (shifts by 1, 2, 4, 8; lanes shifted in from outside the row
+// add 0), then the row totals carried forward with the broadcasts of lane 15 (into rows 1 and 3)
+// and of lane 31 (into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan_dpp(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
 }
+
+// Inclusive prefix sum of an int over the wave.
+__device__ __forceinline__ int wave_incl_scan(int x) { return wave_incl_scan_dpp(x); }
 
 // Block-wide exclusive scan of one int per thread; returns the exclusive prefix and writes
 // the block total to *total.  `scratch` holds at least blockDim.x/64 + 1 ints of LDS.
