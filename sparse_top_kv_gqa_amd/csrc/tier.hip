@@ -6,8 +6,9 @@
 // §4: the classification is redone periodically; the period is the caller's loop.
 //
 // One workgroup (1024 threads) per sequence.  The unprotected tokens get order-preserving keys
-// (evicted or NaN -> 0, the lowest), two radix selects find the keys at ranks floor(M*t0/1000)
-// and floor(M*t01/1000), and one pass in index order assigns tiers (ties to the lower index),
+// (evicted or NaN -> 0, the lowest), two radix searches (8-bit digits, one barrier per pass)
+// find the keys at ranks floor(M*t0/1000) and floor(M*t01/1000), and one pass in index order
+// assigns tiers (ties to the lower index),
 // marks new evictions and compacts the ascending T0 ∪ T1 list with block prefix sums.
 #include "select_common.h"
 
@@ -23,8 +24,7 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
     int p01, uint8_t* __restrict__ evicted, int64_t ev_ld, uint8_t* __restrict__ tier_all,
     int64_t tier_ld, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
     int64_t sel_ld) {
-  __shared__ uint32_t hist[kThreads / kWave * 256];
-  __shared__ int sh[2];
+  __shared__ __align__(16) uint32_t hist[4 * 256];
   __shared__ int scratch[kThreads / kWave + 1];
   const int b = blockIdx.x;
   if (n <= 0) {
@@ -72,10 +72,20 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
       for (int i = lo + threadIdx.x; i < hi; i += kThreads) visit(key_of(i));
     }
   };
+  // thresholds at ranks n0 and n01: one-barrier-per-pass radix searches; when a search ends on
+  // a bin that holds exactly the missing keys, every key >= the threshold is kept (need = all)
   uint32_t thr0 = 0xFFFFFFFFu, thr1 = 0xFFFFFFFFu;
   int need0 = 0, need1 = 0;
-  if (n0 > 0) radix_select<kThreads>(for_each, n0, hist, sh, &thr0, &need0);
-  if (n01 > 0) radix_select<kThreads>(for_each, n01, hist, sh, &thr1, &need1);
+  auto search = [&](int rank, uint32_t* thr, int* need) {
+    for (int i = threadIdx.x; i < 4 * 256; i += kThreads) hist[i] = 0u;
+    __syncthreads();
+    bool whole;
+    radix_threshold(for_each, rank, hist, thr, need, &whole);
+    if (whole) *need = 0x7FFFFFFF;
+    __syncthreads();  // every wave is done reading the histograms
+  };
+  if (n0 > 0) search(n0, &thr0, &need0);
+  if (n01 > 0) search(n01, &thr1, &need1);
 
   int run_eq0 = 0, run_eq1 = 0, run_sel = 0;
   const int chunks = (n + kThreads - 1) / kThreads;
