@@ -229,8 +229,8 @@ enum ListMode {
   kListExplicit = 0,   // list + count (caller's list, or the assembled one)
   kListIntervals = 1,  // one selection row of ids expanded by `gran`, plus sinks and recent window
   kListScores = 2,     // the ids are the top-k of the group's score row (order as kListVirtual)
-  kListVirtual = 3,    // one selection row of ids expanded by `gran`, in list order, then the
-                       // sinks, then the recent window; rows a later part also holds are dead
+  kListVirtual = 3,    // the sinks, then the recent window, then one selection row of ids
+                       // expanded by `gran` in list order; rows an earlier part holds are dead
 };
 
 struct AttnArgs {
@@ -453,27 +453,29 @@ __device__ __forceinline__ int token_at(const int* seg_start, const int* seg_pos
   return seg_start[lo] + (p - seg_pos[lo]);
 }
 
-// Token at position p of a kListVirtual / kListScores fetch list: the selection's ids in list
-// order, each expanded to `gran` tokens, then the sinks [0, ns), then the recent window [rs, n).
-// A token that a later part also holds (block rows inside the sinks or the recent window, recent
-// rows inside the sinks) or that lies outside [0, n) is dead (-1), so each row is read once.
-// `entry` is the list entry covering p (ignored past the selection).
-__device__ __forceinline__ int virtual_token(int p, int n_sel, int gran, int entry, int ns,
-                                             int rs, int n) {
-  const int kb = n_sel * gran;
-  if (p < kb) {
-    const int64_t tok = (int64_t)entry * gran + p % gran;
-    return (entry < 0 || tok >= n || tok < ns || tok >= rs) ? -1 : (int)tok;
-  }
-  p -= kb;
+// Position layout of a kListVirtual / kListScores fetch list: the forced rows first (the sinks
+// [0, ns), then the recent window [rs, n)), then the selection's ids in list order, each expanded
+// to `gran` tokens.  With the forced rows in front, a split that holds only them depends on no
+// selection and starts reading at once.  A token that an earlier part also holds (recent rows
+// inside the sinks, block rows inside the sinks or the recent window) or that lies outside
+// [0, n) is dead (-1), so each row is read once.
+__device__ __forceinline__ int forced_rows(int ns, int rs, int n) { return ns + (n - rs); }
+
+// Token at position p; `entry` is the list entry covering p (ignored for forced positions).
+__device__ __forceinline__ int virtual_token(int p, int gran, int entry, int ns, int rs, int n) {
   if (p < ns) return p;
-  const int tok = rs + (p - ns);
-  return tok < ns ? -1 : tok;
+  const int nf = forced_rows(ns, rs, n);
+  if (p < nf) {
+    const int tok = rs + (p - ns);
+    return tok < ns ? -1 : tok;
+  }
+  const int64_t tok = (int64_t)entry * gran + (p - nf) % gran;
+  return (entry < 0 || tok >= n || tok < ns || tok >= rs) ? -1 : (int)tok;
 }
 
 // Rows of a kListVirtual / kListScores fetch list with n_sel ids.
 __device__ __forceinline__ int virtual_rows(int n_sel, int gran, int ns, int rs, int n) {
-  return n_sel * gran + ns + (n - rs);
+  return forced_rows(ns, rs, n) + n_sel * gran;
 }
 
 // Fill the split's slot table (and per-row list masks) in LDS: entries [0, nrows) are the
@@ -495,10 +497,11 @@ __device__ __forceinline__ void fill_slot_table(const AttnArgs& a, int b, int kv
       int tok;
       if constexpr (MODE == kListVirtual || MODE == kListScores) {
         const int p = r0 + i;
+        const int ps = p - forced_rows(ns, rs, n);  // position in the selection part
         // pre_e[it]: the entry of row r0 + threadIdx.x + it*blockDim.x, read earlier
         const int e = it < n_pre ? (it == 0 ? pre_e[0] : pre_e[1])
-                                 : (p < n_sel * a.gran ? vlist[p / a.gran] : 0);
-        tok = virtual_token(p, n_sel, a.gran, e, ns, rs, n);
+                                 : (ps >= 0 && ps < n_sel * a.gran ? vlist[ps / a.gran] : 0);
+        tok = virtual_token(p, a.gran, e, ns, rs, n);
       } else if constexpr (MODE == kListIntervals) {
         tok = token_at(seg_start, seg_pos, nseg, r0 + i);
       } else {
@@ -809,58 +812,67 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   const int32_t* vlist = nullptr;  // kListVirtual / kListScores: the selection's ids
   int n_sel = 0;
   int pre_e[2] = {0, 0}, n_pre = 0;  // kListVirtual: entries read ahead of the count
+  // the split that publishes the group's row count (and, selecting from scores, the selection)
+  const int pub_split = MODE == kListScores ? (int)gridDim.x - 1 : 0;
   if constexpr (MODE == kListScores) {
-    // the group's selection: exact top-k of its score row (ties to the lowest index, ascending),
-    // as topk_select computes it, kept in LDS
     const float* srow = a.sc_scores + (int64_t)g * a.sc_ld;
     const int n = a.sc_n, kk = min(a.sc_k, n);
-    const int tid = threadIdx.x;
-    auto keep = [&](int pos, int i) { sc_list[pos] = i; };
-    if (n <= kScRegKeys * kThreads) {
-      // the usual case: each thread holds its keys in registers
-      // every load issued before any is used (clamped in bounds): one wait
-      float sv[kScRegKeys];
-#pragma unroll
-      for (int j = 0; j < kScRegKeys; ++j) sv[j] = 0.f;
-      if (n > 0) {
-#pragma unroll
-        for (int j = 0; j < kScRegKeys; ++j) sv[j] = srow[min(j * kThreads + tid, n - 1)];
-      }
-      uint32_t key[kScRegKeys];
-#pragma unroll
-      for (int j = 0; j < kScRegKeys; ++j) key[j] = j * kThreads + tid < n ? order_key(sv[j]) : 0u;
-      if (kk > 0) reg_topk<kThreads>(key, n, kk, sc_hist, sc_wsum, keep);
-      __syncthreads();
-    } else {
-      uint32_t* keys = reinterpret_cast<uint32_t*>(work_s);
-      for (int j0 = 0; j0 < n; j0 += 4 * kThreads) {
-        float sv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sv[u] = srow[min(j0 + u * kThreads + tid, n - 1)];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (j0 + u * kThreads + tid < n) keys[j0 + u * kThreads + tid] = order_key(sv[u]);
-      }
-      if (kk > 0) lds_topk<kThreads>(keys, n, kk, sc_hist, sc_wsum, keep);
-    }
+    const int ns_tok = min(a.n_sink, a.n_tokens), rs_tok = max(a.n_tokens - a.n_recent, 0);
+    cnt = virtual_rows(kk, a.gran, ns_tok, rs_tok, a.n_tokens);
     n_sel = kk;
     vlist = sc_list;
-    cnt = virtual_rows(kk, a.gran, min(a.n_sink, a.n_tokens), max(a.n_tokens - a.n_recent, 0),
-                       a.n_tokens);
+    // a split whose rows are all forced needs no selection (the publisher always selects)
+    const int rs_ = split_rows(a.split_bound > 0 ? a.split_bound : cnt, a.smax);
+    const bool selects = split == pub_split ||
+                         min(split * rs_ + rs_, cnt) > forced_rows(ns_tok, rs_tok, a.n_tokens);
+    if (selects) {
+      // the group's selection: exact top-k of its score row (ties to the lowest index,
+      // ascending), as topk_select computes it, kept in LDS
+      const int tid = threadIdx.x;
+      auto keep = [&](int pos, int i) { sc_list[pos] = i; };
+      if (n <= kScRegKeys * kThreads) {
+        // the usual case: each thread holds its keys in registers
+        // every load issued before any is used (clamped in bounds): one wait
+        float sv[kScRegKeys];
+#pragma unroll
+        for (int j = 0; j < kScRegKeys; ++j) sv[j] = 0.f;
+        if (n > 0) {
+#pragma unroll
+          for (int j = 0; j < kScRegKeys; ++j) sv[j] = srow[min(j * kThreads + tid, n - 1)];
+        }
+        uint32_t key[kScRegKeys];
+#pragma unroll
+        for (int j = 0; j < kScRegKeys; ++j) key[j] = j * kThreads + tid < n ? order_key(sv[j]) : 0u;
+        if (kk > 0) reg_topk<kThreads>(key, n, kk, sc_hist, sc_wsum, keep);
+        __syncthreads();
+      } else {
+        uint32_t* keys = reinterpret_cast<uint32_t*>(work_s);
+        for (int j0 = 0; j0 < n; j0 += 4 * kThreads) {
+          float sv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sv[u] = srow[min(j0 + u * kThreads + tid, n - 1)];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (j0 + u * kThreads + tid < n) keys[j0 + u * kThreads + tid] = order_key(sv[u]);
+        }
+        if (kk > 0) lds_topk<kThreads>(keys, n, kk, sc_hist, sc_wsum, keep);
+      }
+    }
   } else if constexpr (MODE == kListVirtual) {
     vlist = a.list + (int64_t)lrow * a.list_ld;
+    const int ns_tok = min(a.n_sink, a.n_tokens), rs_tok = max(a.n_tokens - a.n_recent, 0);
     if (a.split_bound > 0 && a.list_ld > 0) {
       // the list entries of this thread's first two table rows are read together with the
-      // count (clamped in bounds; an entry past the selection is never used)
-      const int p0 = split * split_rows(a.split_bound, a.smax) + (int)threadIdx.x;
+      // count (clamped in bounds; an entry past the selection, or of a forced row, is unused)
+      const int p0 = split * split_rows(a.split_bound, a.smax) + (int)threadIdx.x -
+                     forced_rows(ns_tok, rs_tok, a.n_tokens);
       const int lmax = (int)a.list_ld - 1;
-      pre_e[0] = vlist[min(p0 / a.gran, lmax)];
-      pre_e[1] = vlist[min((p0 + kThreads) / a.gran, lmax)];
+      pre_e[0] = vlist[min(max(p0, 0) / a.gran, lmax)];
+      pre_e[1] = vlist[min(max(p0 + kThreads, 0) / a.gran, lmax)];
       n_pre = 2;
     }
     n_sel = (int)max(0, min(a.count[lrow], (int)a.list_ld));
-    cnt = virtual_rows(n_sel, a.gran, min(a.n_sink, a.n_tokens), max(a.n_tokens - a.n_recent, 0),
-                       a.n_tokens);
+    cnt = virtual_rows(n_sel, a.gran, ns_tok, rs_tok, a.n_tokens);
   } else if constexpr (MODE == kListIntervals) {
     if (wid == 0)
       build_segments(a, a.list + (int64_t)lrow * a.list_ld, a.count + lrow, seg_start, seg_pos,
@@ -871,10 +883,10 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
     cnt = a.count[lrow];
     cnt = max(0, min(cnt, a.count_clamp));
   }
-  // split 0 publishes the group's row count (and, selecting from scores, the selection) once its
-  // work is done: a barrier waits for every earlier global store, so none are issued before it
+  // the publishing split writes once its work is done: a barrier waits for every earlier global
+  // store, so none are issued before it
   auto publish = [&]() {
-    if (split != 0) return;
+    if (split != pub_split) return;
     if constexpr (MODE != kListExplicit) {
       if (threadIdx.x == 0) a.ucount[g] = cnt;
     }
@@ -1427,8 +1439,9 @@ extern "C" SPK_API spk_status sparse_decode_attn(
   a.n_recent = n_recent;
   a.ucount = p.assemble || p.intervals ? reinterpret_cast<int32_t*>(w + p.off_count) : nullptr;
   // One list per group expanded by gran / sinks / recent window, no logits, on the matrix-core
-  // kernel: the rows follow the list order (no union to build; rows a later part also holds
-  // are skipped), and splits are sized from the bound so they are known before the count.
+  // kernel: the forced rows, then the ids' rows in list order (no union to build; rows an earlier
+  // part also holds are skipped), and splits are sized from the bound so they are known before
+  // the count.
   const bool expand = gran > 1 || n_sink > 0 || n_recent > 0;
   const bool virt = !logits && kv_dtype == SPK_BF16 && q_dtype == SPK_BF16 && p.sets == 1 &&
                     expand && (int64_t)n_tokens >= sel_ld * gran + n_sink + n_recent;

@@ -49,8 +49,8 @@ class BlockSparseDecode:
         # itself, one launch fewer; every split workgroup repeats the selection of its group's
         # short score row in its prologue (registers, one barrier per radix pass), which costs
         # less than the separate top-k launch and the gap before the attention
-        # (the fused launch walks the blocks, sinks and recent window in list order, which
-        # needs room for all of them in the context)
+        # (the fused launch walks the sinks, the recent window and the blocks in list order,
+        # which needs room for all of them in the context)
         ok = (k.dtype == torch.bfloat16 and self.nb <= 4096 and k_blocks <= 62
               and n_tokens >= k_blocks * block_size + n_sink + n_recent)
         self.topk_in_attn = bool(topk_in_attn) and ok
