@@ -166,6 +166,64 @@ def gather_kernel_ms(call, reps, stream):
     return t[len(t) // 2]
 
 
+def stream_ceiling_gbs(nbytes, stream, reps=12):
+    """HBM read ceiling at this size: the best median rate of the library's plain streaming read
+    (spk_stream_read) over a buffer of `nbytes`, across workgroup counts.  The buffers cycle
+    through at least 768 MiB so none is still in the 256 MB last-level cache, and a long read
+    queued first lets the host enqueue every timed launch ahead of the GPU, so each event pair
+    brackets one kernel and no host time."""
+    import ctypes
+    import sparse_top_kv_gqa_amd as spk
+    hip = _hip()
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = (int(nbytes) + 15) // 16 * 16
+    nbuf = max(4, -(-(768 << 20) // nbytes))
+    pool = torch.empty(nbuf * nbytes, dtype=torch.uint8, device="cuda")
+    bufs = [pool[i * nbytes:(i + 1) * nbytes] for i in range(nbuf)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    best = 0.0
+    for wgs in (1024, 2048, 4096, 8192, 16384):
+        pairs = []
+        for _ in range(reps):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if (hip.hipEventCreateWithFlags(ctypes.byref(a), HIP_EVENT_DISABLE_SYSTEM_FENCE) or
+                    hip.hipEventCreateWithFlags(ctypes.byref(b), HIP_EVENT_DISABLE_SYSTEM_FENCE)):
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            pairs.append((a, b))
+        for i in range(nbuf):
+            spk.stream_read(bufs[i], wgs, sink, stream)          # first touch of every page
+        spk.stream_read(pool, 96, sink, stream)                  # long read: the host runs ahead
+        for i, (a, b) in enumerate(pairs):
+            hip.hipEventRecord(a, sh)
+            spk.stream_read(bufs[i % nbuf], wgs, sink, stream)
+            hip.hipEventRecord(b, sh)
+        torch.cuda.synchronize()
+        t = []
+        for a, b in pairs:
+            f = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(f), a, b):
+                raise RuntimeError("hipEventElapsedTime failed")
+            t.append(f.value)
+            hip.hipEventDestroy(a)
+            hip.hipEventDestroy(b)
+        t.sort()
+        best = max(best, nbytes / (t[len(t) // 2] * 1e-3) / 1e9)
+    del bufs, pool
+    torch.cuda.empty_cache()
+    return round(best, 1)
+
+
+def with_ceiling(roof, stream):
+    """Adds the measured HBM read ceiling at the roofline kernel's byte count to an HBM-bound
+    roofline record."""
+    if roof.get("bound") == "hbm":
+        c = stream_ceiling_gbs(roof["algorithmic_bytes_per_launch"], stream)
+        roof["stream_read_ceiling_GBs"] = c
+        roof["frac_of_stream_ceiling"] = round(roof["achieved"] / c, 4) if c > 0 else None
+    return roof
+
+
 def copy_calibration(mib):
     """A plain copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counter readings."""
     n = mib << 20
@@ -216,11 +274,11 @@ def base_result(w, K, W, ms_step, step_bytes, config):
 COPY_KIB = 512 * 1024
 FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
-    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "bdfcb036e030b00c", 41388.7, 1442.23),
-    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "bdfcb036e030b00c", 41512.1, 1442.31),
-    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "1e6d5e9e7811c2f5", 524481.0, 65536.0),
-    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "bdfcb036e030b00c", 271798.0, 8545.06),
-    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "bdfcb036e030b00c", 401316.0, 51431.7),
+    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "0e8ae462b6a874e1", 41398.9, 1442.31),
+    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "0e8ae462b6a874e1", 41523.5, 1442.27),
+    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "df66777984c8f245", 524481.0, 65536.0),
+    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "0e8ae462b6a874e1", 271789.0, 8545.08),
+    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "0e8ae462b6a874e1", 401310.0, 51446.9),
 }
 
 
@@ -772,6 +830,8 @@ def main():
     else:
         res, ctx = bench_tiers(args)
         cpu = cpu_tiers
+    log("measuring the HBM read ceiling at the roofline kernel's size")
+    res["roofline"] = with_ceiling(res["roofline"], torch.cuda.Stream())
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu(ctx, args.cpu_seconds)

@@ -90,6 +90,17 @@ SPK_API int spk_version(void);
  * call) if a record fails. */
 SPK_API spk_status spk_set_attn_timing_events(void* begin, void* end);
 
+/* Measurement reference: a plain streaming read of `bytes` bytes of device memory at `p`, split
+ * into `workgroups` contiguous chunks (each workgroup reads its chunk with 16-byte loads).  It
+ * computes nothing of the method; its rate is the HBM read ceiling a kernel of this library
+ * reaches on the device at hand, reported beside the vendor's peak.  `sink` is one device
+ * uint32 that is written only in the rare case the folded words equal a fixed constant (it keeps
+ * the loads live; its value means nothing).  Enqueues on `stream` and returns.  SPK_EINVAL on a
+ * null pointer, a pointer or size that is not a multiple of 16 bytes, or workgroups outside
+ * [1, 2^20]; bytes = 0 launches nothing. */
+SPK_API spk_status spk_stream_read(const void* p, size_t bytes, int workgroups, uint32_t* sink,
+                                   void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * sparse_index_score — compact indexer scores, no softmax.
  *

@@ -35,7 +35,7 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "spk_set_attn_timing_events", "sparse_index_topk",
            "sparse_topk_decode_attn_workspace_size", "sparse_topk_decode_attn",
            "sparse_window_pool", "sparse_index_score_windowed", "residency_update",
-           "residency_prefetch")
+           "residency_prefetch", "spk_stream_read")
 
 
 class SpkError(RuntimeError):
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.tier_classify.argtypes = [P, I64, I, I, I, I, I, I, P, I64, P, I64, P, P, I64, P, SZ, P]
     L.spk_set_attn_timing_events.restype = I
     L.spk_set_attn_timing_events.argtypes = [P, P]
+    L.spk_stream_read.restype = I
+    L.spk_stream_read.argtypes = [P, SZ, I, P, P]
     L.sparse_topk_decode_attn_workspace_size.restype = I
     L.sparse_topk_decode_attn_workspace_size.argtypes = [I, I, I, I, I, I, I, I, I, I,
                                                          ctypes.POINTER(SZ)]
@@ -416,6 +418,16 @@ def set_attn_timing_events(begin: Optional[torch.cuda.Event] = None,
     if begin is not None and (not b.value or not e.value):
         raise ValueError("record the events once before handing them over")
     _check(lib().spk_set_attn_timing_events(b, e), "spk_set_attn_timing_events")
+
+
+def stream_read(buf: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=None):
+    """Measurement reference: a plain streaming read of the whole device tensor ``buf`` split
+    into ``workgroups`` chunks (``sink``: one int32 device element, written practically never)."""
+    _contig(buf, "buf")
+    if not buf.is_cuda or not sink.is_cuda:
+        raise ValueError("stream_read: buf and sink must be device tensors")
+    _check(lib().spk_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(workgroups),
+                                 _ptr(sink), _stream(stream)), "spk_stream_read")
 
 
 def topk_attn_workspace_size(B, Hq, Hkv, d, n_tokens, n_cand, k, gran=1, n_sink=0,

@@ -140,6 +140,20 @@ def test_timing_hook_validation():
     assert L.spk_set_attn_timing_events(None, None) == 0
 
 
+def test_stream_read_validation():
+    L = spk.lib()
+    assert L.spk_stream_read(None, 1024, 8, A, None) == 1
+    assert "null" in _err()
+    assert L.spk_stream_read(A, 1024, 8, None, None) == 1
+    assert L.spk_stream_read(ctypes.c_void_p(0x100004), 1024, 8, A, None) == 1
+    assert "16" in _err()
+    assert L.spk_stream_read(A, 1000, 8, A, None) == 1
+    assert L.spk_stream_read(A, 1024, 0, A, None) == 1
+    assert L.spk_stream_read(A, 1024, (1 << 20) + 1, A, None) == 1
+    assert "workgroups" in _err()
+    assert L.spk_stream_read(A, 0, 8, A, None) == 0      # nothing to read: no launch
+
+
 def test_index_topk_validation():
     L = spk.lib()
     P = ctypes.c_void_p

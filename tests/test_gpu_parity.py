@@ -1127,3 +1127,25 @@ def test_topk_decode_attn_d64_and_bound():
         i2 = idx.reshape(B * Hkv, k)
         assert torch.equal(sel, i2)
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------------- measurement reference
+
+def test_stream_read_reference_reads_every_word():
+    """The streaming-read reference reads the whole buffer in any chunking (ragged tails
+    included): its sink stays untouched unless the folded words hit the constant, which a
+    planted word makes them do."""
+    say("stream-read")
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    buf = torch.zeros(10 * 4096 + 48, dtype=torch.uint8, device=DEV)
+    for wgs in (1, 7, 1000, 1 << 20):
+        spk.stream_read(buf, wgs, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    words = torch.zeros(4 * 1024, dtype=torch.int32)
+    words[-1] = 0x9E3779B9 - (1 << 32)                  # the last word of the last chunk
+    dev = words.to(DEV)
+    spk.stream_read(dev, 3, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) & 0xFFFFFFFF == 0x9E3779B9
+
