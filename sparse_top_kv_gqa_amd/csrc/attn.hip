@@ -794,7 +794,7 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   // kListScores: one histogram per radix digit, per-wave counts and the selected ids
   __shared__ __align__(16) uint32_t sc_hist[kSc ? 4 * 256 : 4];
   constexpr int kScRegKeys = 4;  // score rows up to 4*256 candidates select from registers
-  __shared__ int sc_wsum[2 * kScRegKeys * kWaves];
+  __shared__ int sc_wsum[kScRegKeys * kWaves];  // >= 2 * kWaves for the LDS path
   __shared__ int32_t sc_list[kSc ? kMaxIntervals : 1];
   extern __shared__ int32_t dyn_s[];
   int32_t* slot_s = dyn_s;
@@ -830,21 +830,27 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
       // ascending), as topk_select computes it, kept in LDS
       const int tid = threadIdx.x;
       auto keep = [&](int pos, int i) { sc_list[pos] = i; };
-      if (n <= kScRegKeys * kThreads) {
-        // the usual case: each thread holds its keys in registers
-        // every load issued before any is used (clamped in bounds): one wait
-        float sv[kScRegKeys];
+      // the usual case: each thread holds its keys in registers (2 or 4 of them); every load
+      // is issued before any is used (clamped in bounds): one wait
+      auto reg_path = [&](auto kpt) {
+        constexpr int KP = decltype(kpt)::value;
+        float sv[KP];
 #pragma unroll
-        for (int j = 0; j < kScRegKeys; ++j) sv[j] = 0.f;
+        for (int j = 0; j < KP; ++j) sv[j] = 0.f;
         if (n > 0) {
 #pragma unroll
-          for (int j = 0; j < kScRegKeys; ++j) sv[j] = srow[min(j * kThreads + tid, n - 1)];
+          for (int j = 0; j < KP; ++j) sv[j] = srow[min(j * kThreads + tid, n - 1)];
         }
-        uint32_t key[kScRegKeys];
+        uint32_t key[KP];
 #pragma unroll
-        for (int j = 0; j < kScRegKeys; ++j) key[j] = j * kThreads + tid < n ? order_key(sv[j]) : 0u;
+        for (int j = 0; j < KP; ++j) key[j] = j * kThreads + tid < n ? order_key(sv[j]) : 0u;
         if (kk > 0) reg_topk<kThreads>(key, n, kk, sc_hist, sc_wsum, keep);
         __syncthreads();
+      };
+      if (n <= 2 * kThreads) {
+        reg_path(std::integral_constant<int, 2>{});
+      } else if (n <= kScRegKeys * kThreads) {
+        reg_path(std::integral_constant<int, kScRegKeys>{});
       } else {
         uint32_t* keys = reinterpret_cast<uint32_t*>(work_s);
         for (int j0 = 0; j0 < n; j0 += 4 * kThreads) {

@@ -145,12 +145,15 @@ __device__ __forceinline__ void keep_class(uint32_t key, bool valid, uint32_t th
 // Exact top-kk of n keys held in registers by a workgroup of NT threads (1 <= kk <= n <= KPT*NT):
 // key[j] of thread t is element j*NT + t.  Ties go to the lowest index; calls out(position,
 // index) for every kept element, positions 0..kk-1 in ascending index order.  hist: 4*256 uint32
-// of LDS; wsum: 2*KPT*NT/64 ints of LDS.  Barriers: one to clear, one per radix pass, one for the
-// per-wave counts; the caller waits (barrier) before reading what out wrote to LDS.
+// of LDS; wsum: KPT*NT/64 ints of LDS (KPT*NT/64 <= 256).  Barriers: one to clear, one per radix
+// pass, two for the per-(chunk, wave) counts; the caller waits (barrier) before reading what out
+// wrote to LDS.
 template <int NT, int KPT, typename Out>
 __device__ __forceinline__ void reg_topk(const uint32_t (&key)[KPT], int n, int kk, uint32_t* hist, int* wsum,
                          const Out& out) {
   constexpr int NW = NT / kWave;
+  constexpr int NC = KPT * NW;  // (chunk, wave) pairs, in index order
+  static_assert(NC <= 4 * kWave, "per-(chunk, wave) counts: at most 256");
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   for (int i = tid; i < 4 * 256; i += NT) hist[i] = 0u;
   __syncthreads();
@@ -164,34 +167,42 @@ __device__ __forceinline__ void reg_topk(const uint32_t (&key)[KPT], int n, int 
           if (j * NT + tid < n) visit(key[j]);
       },
       kk, hist, &thr, &need, &whole);
-  // element order: chunk j (indices j*NT ..), inside it wave w (64 indices), inside it the lane
+  // element order: chunk j (indices j*NT ..), inside it wave w (64 indices), inside it the lane.
+  // Kept counts per (chunk, wave), packed: greater-than in the low 16 bits, equal in the high
+  // 16 (each total <= n <= 16384)
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     bool gt, eq;
     keep_class(key[j], j * NT + tid < n, thr, whole, gt, eq);
-    const int cg = __popcll(__ballot(gt)), ce = __popcll(__ballot(eq));
-    if (lane == 0) {
-      wsum[2 * (j * NW + wid)] = cg;
-      wsum[2 * (j * NW + wid) + 1] = ce;
+    const int c = __popcll(__ballot(gt)) | (__popcll(__ballot(eq)) << 16);
+    if (lane == 0) wsum[j * NW + wid] = c;
+  }
+  __syncthreads();
+  // wave 0 turns the counts into exclusive prefixes (one wave scan per 64 pairs)
+  if (wid == 0) {
+    int carry = 0;
+#pragma unroll
+    for (int base = 0; base < NC; base += kWave) {
+      const int i = base + lane;
+      const int c = i < NC ? wsum[i] : 0;
+      const int incl = wave_incl_scan(c);
+      if (i < NC) wsum[i] = carry + incl - c;
+      carry += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
   }
   __syncthreads();
+  int pre[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) pre[j] = wsum[j * NW + wid];
   const uint64_t lt = (1ull << lane) - 1ull;
-  int run_g = 0, run_e = 0;  // kept counts of the (chunk, wave) pairs before the current one
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    for (int w = 0; w < NW; ++w) {
-      if (w == wid) {
-        bool gt, eq;
-        keep_class(key[j], j * NT + tid < n, thr, whole, gt, eq);
-        const uint64_t bg = __ballot(gt), be = __ballot(eq);
-        const int pe = run_e + __popcll(be & lt);
-        const int pos = run_g + __popcll(bg & lt) + min(pe, need);
-        if ((gt || (eq && pe < need)) && pos < kk) out(pos, j * NT + tid);
-      }
-      run_g += wsum[2 * (j * NW + w)];
-      run_e += wsum[2 * (j * NW + w) + 1];
-    }
+    bool gt, eq;
+    keep_class(key[j], j * NT + tid < n, thr, whole, gt, eq);
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    const int pe = (pre[j] >> 16) + __popcll(be & lt);
+    const int pos = (pre[j] & 0xFFFF) + __popcll(bg & lt) + min(pe, need);
+    if ((gt || (eq && pe < need)) && pos < kk) out(pos, j * NT + tid);
   }
 }
 
