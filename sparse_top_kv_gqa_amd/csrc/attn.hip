@@ -794,7 +794,7 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   // kListScores: one histogram per radix digit, per-wave counts and the selected ids
   __shared__ __align__(16) uint32_t sc_hist[kSc ? 4 * 256 : 4];
   constexpr int kScRegKeys = 4;  // score rows up to 4*256 candidates select from registers
-  __shared__ int sc_wsum[kScRegKeys * kWaves];  // >= 2 * kWaves for the LDS path
+  __shared__ __align__(16) int sc_wsum[kScRegKeys * kWaves];  // >= 2 * kWaves (LDS path)
   __shared__ int32_t sc_list[kSc ? kMaxIntervals : 1];
   extern __shared__ int32_t dyn_s[];
   int32_t* slot_s = dyn_s;
@@ -841,10 +841,12 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
 #pragma unroll
           for (int j = 0; j < KP; ++j) sv[j] = srow[min(j * kThreads + tid, n - 1)];
         }
+        // the histograms are cleared while the scores are on their way
+        for (int i = tid; i < 4 * 256; i += kThreads) sc_hist[i] = 0u;
         uint32_t key[KP];
 #pragma unroll
         for (int j = 0; j < KP; ++j) key[j] = j * kThreads + tid < n ? order_key(sv[j]) : 0u;
-        if (kk > 0) reg_topk<kThreads>(key, n, kk, sc_hist, sc_wsum, keep);
+        if (kk > 0) reg_topk<kThreads, KP, true>(key, n, kk, sc_hist, sc_wsum, keep);
         __syncthreads();
       };
       if (n <= 2 * kThreads) {

@@ -146,16 +146,17 @@ __device__ __forceinline__ void keep_class(uint32_t key, bool valid, uint32_t th
 // key[j] of thread t is element j*NT + t.  Ties go to the lowest index; calls out(position,
 // index) for every kept element, positions 0..kk-1 in ascending index order.  hist: 4*256 uint32
 // of LDS; wsum: KPT*NT/64 ints of LDS (KPT*NT/64 <= 256).  Barriers: one to clear, one per radix
-// pass, two for the per-(chunk, wave) counts; the caller waits (barrier) before reading what out
-// wrote to LDS.
-template <int NT, int KPT, typename Out>
+// pass, one for the per-(chunk, wave) counts (two above 16 pairs); the caller waits (barrier)
+// before reading what out wrote to LDS.
+template <int NT, int KPT, bool kCleared = false, typename Out>
 __device__ __forceinline__ void reg_topk(const uint32_t (&key)[KPT], int n, int kk, uint32_t* hist, int* wsum,
                          const Out& out) {
   constexpr int NW = NT / kWave;
   constexpr int NC = KPT * NW;  // (chunk, wave) pairs, in index order
   static_assert(NC <= 4 * kWave, "per-(chunk, wave) counts: at most 256");
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  for (int i = tid; i < 4 * 256; i += NT) hist[i] = 0u;
+  if constexpr (!kCleared)  // kCleared: the caller zeroed hist (no barrier needed after it)
+    for (int i = tid; i < 4 * 256; i += NT) hist[i] = 0u;
   __syncthreads();
   uint32_t thr;
   int need;
@@ -178,22 +179,36 @@ __device__ __forceinline__ void reg_topk(const uint32_t (&key)[KPT], int n, int 
     if (lane == 0) wsum[j * NW + wid] = c;
   }
   __syncthreads();
-  // wave 0 turns the counts into exclusive prefixes (one wave scan per 64 pairs)
-  if (wid == 0) {
-    int carry = 0;
-#pragma unroll
-    for (int base = 0; base < NC; base += kWave) {
-      const int i = base + lane;
-      const int c = i < NC ? wsum[i] : 0;
-      const int incl = wave_incl_scan(c);
-      if (i < NC) wsum[i] = carry + incl - c;
-      carry += __builtin_amdgcn_readlane(incl, kWave - 1);
-    }
-  }
-  __syncthreads();
   int pre[KPT];
+  if constexpr (NC <= 16) {
+    // few pairs: every thread reads all counts at once and sums its prefixes in registers
+    int c[NC];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) pre[j] = wsum[j * NW + wid];
+    for (int i = 0; i < NC; ++i) c[i] = wsum[i];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      int p = 0;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) p += i < j * NW + wid ? c[i] : 0;
+      pre[j] = p;
+    }
+  } else {
+    // wave 0 turns the counts into exclusive prefixes (one wave scan per 64 pairs)
+    if (wid == 0) {
+      int carry = 0;
+#pragma unroll
+      for (int base = 0; base < NC; base += kWave) {
+        const int i = base + lane;
+        const int c = i < NC ? wsum[i] : 0;
+        const int incl = wave_incl_scan(c);
+        if (i < NC) wsum[i] = carry + incl - c;
+        carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) pre[j] = wsum[j * NW + wid];
+  }
   const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {

@@ -25,13 +25,13 @@ constexpr int kSmallMax = 64 * kSmallThreads;  // 16384
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
 // Rows of up to 64*256 keys held in registers (KPT per thread); reg_topk selects with one
-// barrier per radix pass and two for the compaction counts.
+// barrier per radix pass and one or two for the compaction counts.
 template <int KPT>
 __global__ __launch_bounds__(kSmallThreads) void topk_reg_kernel(
     const float* __restrict__ scores, int64_t s_ld, int n, int k, int32_t* __restrict__ idx,
     int64_t idx_ld, int32_t* __restrict__ count) {
   __shared__ __align__(16) uint32_t hist[4 * 256];
-  __shared__ int wsum[KPT * kSmallWaves];
+  __shared__ __align__(16) int wsum[KPT * kSmallWaves];
   const int row = blockIdx.x;
   const int kk = min(k, n);
   if (count && threadIdx.x == 0) count[row] = kk;
