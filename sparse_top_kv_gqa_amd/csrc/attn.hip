@@ -36,9 +36,9 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kMaxSets = 32;
 constexpr int kAsmThreads = 1024;
-constexpr int kAsmLdsWords = 32768;  // 128 KB of LDS bitmaps; larger ones live in the workspace
+constexpr int kAsmLdsWords = 26624;  // 104 KB of LDS bitmaps; larger ones live in the workspace
+constexpr int kAsmStaticLds = 48 * 1024;  // the assembly kernel's static LDS, rounded up
 constexpr int kMaxIntervals = 64;   // selection entries + 2 forced ranges, one per lane
 constexpr int kScoresMax = 4096;    // candidates per score row selected inside the attention
 constexpr int kMaxRows = 8192;      // rows per split (LDS slot table)
@@ -119,7 +119,8 @@ Plan make_plan(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_
   p.R = best_R;
   p.smax = (int)ceil_div(ubound, p.R);
   p.words = (int)ceil_div(n_tokens > 0 ? n_tokens : 1, 32);
-  p.bm_lds = (int64_t)p.sets * p.words <= kAsmLdsWords;
+  p.bm_lds = (int64_t)p.sets * p.words <= kAsmLdsWords &&
+             (size_t)p.sets * p.words * 4 + kAsmStaticLds <= lds_wg;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -151,75 +152,196 @@ struct AsmArgs {
   int32_t* ucount;
 };
 
-// kLds: the bitmaps live in LDS.  The two cases are separate instantiations so the LDS case
-// uses LDS instructions: through one generic pointer every bitmap access is a flat access whose
-// wait also covers the list stores in flight, which serialises the compaction loop.
+// kLds: the bitmaps live in (dynamic) LDS.  The two cases are separate instantiations so the
+// LDS case uses LDS instructions: through one generic pointer every bitmap access is a flat
+// access whose wait also covers the list stores in flight, which serialises the compaction.
+//
+// One workgroup per group does all of the group's work, so the kernel is bound by instruction
+// issue on a few CUs and every phase keeps its lanes busy: (1) the sets' list lengths; (2) per
+// set, kAsmBatch entries per thread are read at once (clamped addresses, one wait) and their
+// bits set; (3) forced rows; (4) wave v owns a contiguous run of bitmap words, 64 at a time (lane
+// l: word base + l); the lanes' entry offsets, union words and set words go to LDS, and then
+// every lane produces one output entry: each word's first entry marks its lane in a 64-slot
+// table, a wave prefix maximum gives every entry the lane (word) holding it, and a popcount
+// search the bit, so the list is written with full, consecutive stores (per-wave totals give
+// each wave its output offset).
+constexpr int kAsmBatch = 4;
+constexpr int kAsmSets = 16;     // sets per group the kernel handles (G * T <= 16)
+constexpr int kAsmRegSets = 8;   // up to this many sets, a word's set bitmaps are staged
+
+// Position of the k-th set bit (k < popcount(u)) of u, by halving popcount search.
+__device__ __forceinline__ int nth_set_bit(uint32_t u, int k) {
+  int pos = 0;
+#pragma unroll
+  for (int width = 16; width > 0; width >>= 1) {
+    const uint32_t low = u & ((1u << width) - 1u);
+    const int c = __popc(low);
+    const bool up = k >= c;
+    k -= up ? c : 0;
+    pos += up ? width : 0;
+    u = up ? (u >> width) : low;
+  }
+  return pos;
+}
+
 template <bool kLds>
 __global__ __launch_bounds__(kAsmThreads) void assemble_kernel(AsmArgs a) {
-  __shared__ uint32_t bm_lds[kLds ? kAsmLdsWords : 1];
-  __shared__ int scratch[kAsmThreads / kWave + 1];
+  constexpr int NWV = kAsmThreads / kWave;
+  extern __shared__ uint32_t bm_dyn[];
+  __shared__ int scratch[NWV];
+  __shared__ int set_off[kAsmSets + 1];   // first entry of each set in a flat numbering
+  __shared__ int64_t set_row[kAsmSets];   // offset of each set's list row in sel_idx
+  __shared__ int st_pre[NWV][kWave];      // per lane: first entry of its word in the batch
+  __shared__ uint32_t st_u[NWV][kWave];   // per lane: its word of the union
+  __shared__ uint32_t st_sw[NWV][kAsmRegSets][kWave];  // per lane: its word of every set
+  __shared__ int st_own[NWV][kWave];      // per output slot of a chunk: the lane starting there
   const int g = blockIdx.x;
   const int b = g / a.Hkv, kvh = g % a.Hkv;
-  const int W = a.words;
+  const int W = a.words, S = a.sets;
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
   uint32_t* bm;
-  if constexpr (kLds) bm = bm_lds;
-  else bm = a.bm_global + (int64_t)g * a.sets * W;
-  for (int i = threadIdx.x; i < a.sets * W; i += kAsmThreads) bm[i] = 0u;
+  if constexpr (kLds) bm = bm_dyn;
+  else bm = a.bm_global + (int64_t)g * S * W;
+  for (int i = threadIdx.x; i < S * W; i += kAsmThreads) bm[i] = 0u;
+  // (1) wave 0: lane r reads set r's count (the host bounds the total below 2^31)
+  if (wid == 0) {
+    int len = 0;
+    if (lane < S) {
+      const int r = lane;
+      int64_t row;
+      if (a.scope == SPK_SEL_PER_SEQ) row = b;
+      else if (a.scope == SPK_SEL_PER_KV_HEAD) row = (int64_t)(b * a.T + r) * a.Hkv + kvh;
+      else row = (int64_t)(b * a.T + r / a.G) * a.Hq + kvh * a.G + r % a.G;
+      const int cnt = max(0, min(a.sel_count[row], (int)a.sel_ld));
+      len = cnt * a.gran;
+      set_row[r] = row * a.sel_ld;
+    }
+    const int incl = wave_incl_scan(len);
+    if (lane <= S) set_off[lane] = incl - len;
+  }
   __syncthreads();
-  const int n = a.n_tokens;
-  for (int r = 0; r < a.sets; ++r) {
-    int64_t row;
-    if (a.scope == SPK_SEL_PER_SEQ) row = b;
-    else if (a.scope == SPK_SEL_PER_KV_HEAD) row = (int64_t)(b * a.T + r) * a.Hkv + kvh;
-    else row = (int64_t)(b * a.T + r / a.G) * a.Hq + kvh * a.G + r % a.G;
-    int cnt = a.sel_count[row];
-    if (cnt > a.sel_ld) cnt = (int)a.sel_ld;
-    const int32_t* lst = a.sel_idx + row * a.sel_ld;
-    const int64_t total = (int64_t)(cnt > 0 ? cnt : 0) * a.gran;
-    for (int64_t e = threadIdx.x; e < total; e += kAsmThreads) {
-      const int64_t tok = (int64_t)lst[e / a.gran] * a.gran + e % a.gran;
-      if (tok >= 0 && tok < n) atomicOr(&bm[r * W + (int)(tok >> 5)], 1u << (tok & 31));
+  const int n = a.n_tokens, gran = a.gran;
+  // (2) the selected tokens' bits, set by set, kAsmBatch entries per thread in flight
+  for (int r = 0; r < S; ++r) {
+    const int len = set_off[r + 1] - set_off[r];
+    const int32_t* lst = a.sel_idx + set_row[r];
+    for (int e0 = threadIdx.x; e0 < len; e0 += kAsmBatch * kAsmThreads) {
+      int32_t ent[kAsmBatch];
+#pragma unroll
+      for (int u = 0; u < kAsmBatch; ++u) {
+        const int e = min(e0 + u * kAsmThreads, len - 1);
+        ent[u] = lst[gran == 1 ? e : e / gran];
+      }
+#pragma unroll
+      for (int u = 0; u < kAsmBatch; ++u) {
+        const int e = e0 + u * kAsmThreads;
+        if (e < len) {
+          const int64_t tok = (int64_t)ent[u] * gran + (gran == 1 ? 0 : e % gran);
+          if (tok >= 0 && tok < n) atomicOr(&bm[r * W + (int)(tok >> 5)], 1u << (tok & 31));
+        }
+      }
     }
   }
-  // forced rows belong to every list
+  // (3) forced rows belong to every list
   const int s_end = min(a.n_sink, n);
   const int r_beg = max(0, n - a.n_recent);
   for (int tok = threadIdx.x; tok < s_end + (n - r_beg); tok += kAsmThreads) {
     const int t = tok < s_end ? tok : r_beg + (tok - s_end);
-    for (int r = 0; r < a.sets; ++r) atomicOr(&bm[r * W + (t >> 5)], 1u << (t & 31));
+    for (int r = 0; r < S; ++r) atomicOr(&bm[r * W + (t >> 5)], 1u << (t & 31));
   }
   __syncthreads();
-  const int wpt = (W + kAsmThreads - 1) / kAsmThreads;
-  const int w0 = threadIdx.x * wpt;
-  const int w1 = min(w0 + wpt, W);
-  int local = 0;
-  for (int w = w0; w < w1; ++w) {
+  // (4) compaction: wave wid owns words [wb, we), 64 at a time
+  const int wpw = (W + NWV * kWave - 1) / (NWV * kWave) * kWave;
+  const int wb = min(W, wid * wpw), we = min(W, wb + wpw);
+  auto union_word = [&](int w) {
     uint32_t u = 0;
-    for (int r = 0; r < a.sets; ++r) u |= bm[r * W + w];
-    local += __popc(u);
+    if (w < we)
+      for (int r = 0; r < S; ++r) u |= bm[r * W + w];
+    return u;
+  };
+  int cnt = 0;
+  for (int w0 = wb; w0 < we; w0 += kWave) cnt += __popc(union_word(w0 + lane));
+  // wave totals -> each wave's first output position
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, kWave);
+  if (lane == 0) scratch[wid] = cnt;
+  __syncthreads();
+  int run = 0, total_u = 0;
+  for (int v = 0; v < NWV; ++v) {
+    const int c = scratch[v];
+    run += v < wid ? c : 0;
+    total_u += c;
   }
-  int total;
-  int pos = block_excl_scan(local, scratch, &total);
   int32_t* ul = a.ulist + (int64_t)g * a.ubound;
   uint32_t* um = a.umask ? a.umask + (int64_t)g * a.ubound : nullptr;
-  for (int w = w0; w < w1; ++w) {
+  const bool reg_sets = S <= kAsmRegSets;
+  for (int w0 = wb; w0 < we; w0 += kWave) {
+    const int w = w0 + lane;
+    uint32_t sw[kAsmRegSets];
     uint32_t u = 0;
-    for (int r = 0; r < a.sets; ++r) u |= bm[r * W + w];
-    while (u) {
-      const int bit = __ffs(u) - 1;
-      u &= u - 1;
-      if (pos < a.ubound) {
-        ul[pos] = w * 32 + bit;
-        if (um) {
-          uint32_t m = 0;
-          for (int r = 0; r < a.sets; ++r) m |= ((bm[r * W + w] >> bit) & 1u) << r;
-          um[pos] = m;
+#pragma unroll
+    for (int r = 0; r < kAsmRegSets; ++r) sw[r] = 0u;
+    if (w < we) {
+      if (reg_sets) {
+        // every set word read before any is used: one wait
+#pragma unroll
+        for (int r = 0; r < kAsmRegSets; ++r) sw[r] = r < S ? bm[r * W + w] : 0u;
+#pragma unroll
+        for (int r = 0; r < kAsmRegSets; ++r) u |= sw[r];
+      } else {
+        for (int r = 0; r < S; ++r) u |= bm[r * W + w];
+      }
+    }
+    const int c = __popc(u);
+    const int incl = wave_incl_scan(c);
+    const int btot = __builtin_amdgcn_readlane(incl, kWave - 1);
+    const int pre = incl - c;  // this lane's first entry within the batch
+    if (reg_sets) {
+#pragma unroll
+      for (int r = 0; r < kAsmRegSets; ++r)
+        if (r < S) st_sw[wid][r][lane] = sw[r];
+    }
+    st_pre[wid][lane] = pre;
+    st_u[wid][lane] = u;
+    int carry = 0;  // the lane holding the entry before the current chunk
+    for (int i0 = 0; i0 < btot; i0 += kWave) {
+      st_own[wid][lane] = -1;
+      __builtin_amdgcn_wave_barrier();
+      if (c > 0 && pre >= i0 && pre < i0 + kWave) st_own[wid][pre - i0] = lane;
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const int o = max(wave_incl_max(st_own[wid][lane]), carry);
+      carry = __builtin_amdgcn_readlane(o, kWave - 1);
+      const int i = i0 + lane;
+      if (i < btot) {
+        const uint32_t uo = st_u[wid][o];
+        const int bit = nth_set_bit(uo, i - st_pre[wid][o]);
+        const int pos = run + i;
+        if (pos < a.ubound) {
+          ul[pos] = (w0 + o) * 32 + bit;
+          if (um) {
+            uint32_t m = 0;
+            if (reg_sets) {
+              uint32_t x[kAsmRegSets];
+#pragma unroll
+              for (int r = 0; r < kAsmRegSets; ++r) x[r] = r < S ? st_sw[wid][r][o] : 0u;
+#pragma unroll
+              for (int r = 0; r < kAsmRegSets; ++r) m |= ((x[r] >> bit) & 1u) << r;
+            } else {
+              for (int r = 0; r < S; ++r) m |= ((bm[r * W + w0 + o] >> bit) & 1u) << r;
+            }
+            um[pos] = m;
+          }
         }
       }
-      ++pos;
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // slots read before reuse
+      __builtin_amdgcn_wave_barrier();
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    run += btot;
   }
-  if (threadIdx.x == 0) a.ucount[g] = min(total, a.ubound);
+  if (threadIdx.x == 0) a.ucount[g] = min(total_u, a.ubound);
 }
 
 // ------------------------------------------------------------------------------- partial
@@ -1330,8 +1452,11 @@ static spk_status check_common(spk_sel_scope scope, int B, int T, int Hq, int Hk
   SPK_REQUIRE(G * T <= 16, SPK_EUNSUPPORTED,
               "sparse_decode_attn: %d query vectors per KV head (max 16)", G * T);
   const int sets = scope == SPK_SEL_PER_SEQ ? 1 : scope == SPK_SEL_PER_KV_HEAD ? T : T * G;
-  SPK_REQUIRE(sets <= spk::kMaxSets, SPK_EUNSUPPORTED,
-              "sparse_decode_attn: %d selection lists per group (max 32)", sets);
+  SPK_REQUIRE(sets <= spk::kAsmSets, SPK_EUNSUPPORTED,
+              "sparse_decode_attn: %d selection lists per group (max 16)", sets);
+  SPK_REQUIRE((int64_t)sets * sel_ld * gran < ((int64_t)1 << 31), SPK_EUNSUPPORTED,
+              "sparse_decode_attn: %d lists x %lld entries x granularity %d exceed 2^31 rows",
+              sets, (long long)sel_ld, gran);
   return SPK_OK;
 }
 
@@ -1483,7 +1608,9 @@ extern "C" SPK_API spk_status sparse_decode_attn(
     as.ulist = reinterpret_cast<int32_t*>(w + p.off_list);
     as.umask = p.mask ? reinterpret_cast<uint32_t*>(w + p.off_mask) : nullptr;
     as.ucount = a.ucount;
-    if (p.bm_lds) hipLaunchKernelGGL(assemble_kernel<true>, dim3(p.groups), dim3(kAsmThreads), 0, st, as);
+    if (p.bm_lds)
+      hipLaunchKernelGGL(assemble_kernel<true>, dim3(p.groups), dim3(kAsmThreads),
+                         (size_t)p.sets * p.words * 4, st, as);
     else hipLaunchKernelGGL(assemble_kernel<false>, dim3(p.groups), dim3(kAsmThreads), 0, st, as);
     spk_status e = check_launch("sparse_decode_attn/assemble");
     if (e != SPK_OK) return e;

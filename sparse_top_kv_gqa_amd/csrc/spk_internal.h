@@ -144,6 +144,18 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int x) {
   return x;
 }
 
+// Inclusive prefix maximum over the wave of values >= -1 (the DPP steps of wave_incl_scan_dpp
+// with max, and -1 where a lane has no source).
+__device__ __forceinline__ int wave_incl_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x111, 0xF, 0xF, false));  // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x112, 0xF, 0xF, false));  // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x114, 0xF, 0xF, false));  // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x118, 0xF, 0xF, false));  // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(-1, x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return x;
+}
+
 // Inclusive prefix sum of an int over the wave.
 __device__ __forceinline__ int wave_incl_scan(int x) { return wave_incl_scan_dpp(x); }
 

@@ -702,6 +702,44 @@ def test_long_block_list_with_forced_rows_uses_assembly():
             check_rows(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="assembled union")
 
 
+@pytest.mark.parametrize("N", [3000 + 7, 70001])
+def test_union_assembly_sixteen_sets_ragged_lists(N):
+    """Per-query-head token lists of 4 draft tokens x 4 heads (16 sets per group) with ragged and
+    empty lists and forced rows: each query vector attends over its own list's rows of the
+    assembled union.  At 70001 tokens the 16 bitmaps exceed the LDS and live in the workspace."""
+    say("union-16-sets", N)
+    B, T, Hq, Hkv, d, k = 2, 4, 16, 4, 128, 300
+    G = Hq // Hkv
+    q = _rand((B, T, Hq, d), torch.bfloat16, 31)
+    kc = _rand((B, Hkv, N, d), torch.bfloat16, 32)
+    vc = _rand((B, Hkv, N, d), torch.bfloat16, 33)
+    rows = B * T * Hq
+    sel = _sorted_sets(rows, N, k, 34)
+    cnt = np.full(rows, k, np.int32)
+    cnt[3] = 0                                     # an empty list
+    cnt[5] = 17
+    cnt[rows - 1] = 299
+    selt = torch.tensor(sel.reshape(B, T, Hq, k), device=DEV)
+    cntt = torch.tensor(cnt.reshape(B, T, Hq), device=DEV)
+    out, lse = spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_q_head", N, n_sink=4,
+                                      n_recent=64)
+    torch.cuda.synchronize()
+    scale = oracle.softmax_scale(d)
+    o_all, l_all = out.cpu().numpy(), lse.cpu().numpy()
+    qh = host(q)
+    for b in range(B):
+        for h in range(Hkv):
+            kh, vh = host(kc[b, h]), host(vc[b, h])
+            for t in range(T):
+                for j in range(G):
+                    hq = h * G + j
+                    r = (b * T + t) * Hq + hq
+                    toks = oracle.selection_tokens(sel[r, :cnt[r]], 1, N, 4, 64)
+                    o_ref, l_ref, _ = oracle.attend(qh[b, t, hq:hq + 1], kh[toks], vh[toks], scale)
+                    check_rows(o_all[b, t, hq], o_ref[0], what=f"union set {r}")
+                    assert abs(l_all[b, t, hq] - l_ref[0]) <= TOL * abs(l_ref[0]) + 1e-6
+
+
 def test_block_intervals_logits_follow_union_order():
     """Scaled logits come back at each row's position in the ascending union of blocks, sinks
     and recent window."""
