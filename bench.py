@@ -274,11 +274,11 @@ def base_result(w, K, W, ms_step, step_bytes, config):
 COPY_KIB = 512 * 1024
 FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
-    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "0e8ae462b6a874e1", 41398.9, 1442.31),
-    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "0e8ae462b6a874e1", 41523.5, 1442.27),
-    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "df66777984c8f245", 524481.0, 65536.0),
-    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "0e8ae462b6a874e1", 271789.0, 8545.08),
-    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "0e8ae462b6a874e1", 401310.0, 51446.9),
+    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4422c57807dd7a2b", 41360.4, 1442.5),
+    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4422c57807dd7a2b", 41484.8, 1442.41),
+    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "cdc6e2d4efb6fbf1", 524481.0, 65536.0),
+    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4422c57807dd7a2b", 271802.0, 8544.97),
+    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4422c57807dd7a2b", 401308.0, 51441.5),
 }
 
 
