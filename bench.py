@@ -254,6 +254,31 @@ def timed_loop(run_step, K, W, stream):
     return e0.elapsed_time(e1), wall
 
 
+def cold_step_ms(run_step, reps, stream, flush_mib=1024):
+    """Median time of one step after a plain streaming read of `flush_mib` MiB (outside the
+    timed pair) has replaced whatever the last-level cache held: the step with every byte from
+    HBM.  With flush_mib = 0 the same event pairs time steps queued behind nothing, which
+    separates the cost of timing one step alone from the cache's part."""
+    import sparse_top_kv_gqa_amd as spk
+    flush = torch.empty(max(flush_mib, 1) << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    evs = []
+    with torch.cuda.stream(stream):
+        for i in range(reps):
+            if flush_mib > 0:
+                spk.stream_read(flush, 8192, sink, stream)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run_step(i)
+            b.record(stream)
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    del flush
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    return t[len(t) // 2]
+
+
 def base_result(w, K, W, ms_step, step_bytes, config):
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     return {
@@ -375,6 +400,8 @@ def bench_block(args, windowed=False):
     torch.cuda.synchronize()
     ms_total, wall = timed_loop(lambda i: graphs[i % L].replay(), K, Wm, stream)
     ms_step = ms_total / K
+    cold_ms = cold_step_ms(lambda i: graphs[i % L].replay(), 64, stream)
+    single_ms = cold_step_ms(lambda i: graphs[i % L].replay(), 64, stream, flush_mib=0)
     # graph replays reproduce an eager step bit for bit
     for l in range(min(L, 2)):
         graphs[l].replay()
@@ -408,6 +435,7 @@ def bench_block(args, windowed=False):
         "recent": w.n_recent, "layer_caches_rotated": L, "bytes_per_step": int(bytes_avg),
         "selected_rows_per_step": int(sum(sel_bytes) / L / ROW_BYTES),
         "wall_s_timed": round(wall, 4),
+        "single_step_ms": round(single_ms, 5), "cold_single_step_ms": round(cold_ms, 5),
         "attention_call_ms": round(att_ms, 4), "index_call_ms": round(idx_ms, 4),
         "index_GBs": round(index_bytes / (idx_ms * 1e-3) / 1e9, 1)})
     if windowed:
