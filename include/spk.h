@@ -273,7 +273,8 @@ SPK_API spk_status sparse_index_score_windowed(const void* pred, spk_dtype p_dty
  *              workspaces.
  *
  * The fetch-list bound per group is min(n_tokens, sets*sel_ld*gran + n_sink + n_recent) with
- * sets = 1 (PER_SEQ), T (PER_KV_HEAD) or T*G (PER_Q_HEAD); at most 32 sets per group.
+ * sets = 1 (PER_SEQ), T (PER_KV_HEAD) or T*G (PER_Q_HEAD); at most 16 sets per group (G*T is
+ * at most 16 anyway), and sets*sel_ld*gran must stay below 2^31, else SPK_EUNSUPPORTED.
  * A KV or host-pool row stride of 4 GiB or more returns SPK_EUNSUPPORTED.
  * ------------------------------------------------------------------------------------------ */
 SPK_API spk_status sparse_decode_attn_workspace_size(spk_sel_scope scope, int B, int T, int Hq,

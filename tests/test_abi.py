@@ -96,6 +96,8 @@ def test_attn_validation():
     assert _attn(logits=Bp, logits_ld=8) == 1                        # logits_ld below the bound
     assert _attn(gran=0) == 1
     assert _attn(hbm_slots=1000) == 1 and "exceeds" in _err()       # cache shorter than n_tokens
+    # 4 lists x 2^25 entries x granularity 2^7: more flattened rows than the assembly numbers
+    assert _attn(scope=2, sel_ld=1 << 25, gran=1 << 7) == 2 and "2^31" in _err()
     # host pools must be pinned host memory known to HIP: a plain malloc'ed buffer is refused
     buf = ctypes.create_string_buffer(1 << 16)
     addr = (ctypes.addressof(buf) + 15) // 16 * 16
