@@ -7,9 +7,11 @@
 //
 // One workgroup (1024 threads) per sequence.  The unprotected tokens get order-preserving keys
 // (evicted or NaN -> 0, the lowest), two radix searches (8-bit digits, one barrier per pass)
-// find the keys at ranks floor(M*t0/1000) and floor(M*t01/1000), and one pass in index order
-// assigns tiers (ties to the lower index),
-// marks new evictions and compacts the ascending T0 ∪ T1 list with block prefix sums.
+// find the keys at ranks floor(M*t0/1000) and floor(M*t01/1000); ranks in index order (ties at
+// the thresholds to the lower index, then positions in the ascending T0 ∪ T1 list) come from
+// per-(chunk, wave) ballot counts turned into prefixes by one wave scan, so assigning tiers,
+// marking new evictions and compacting the list take four barriers (sequences of up to 16384
+// tokens, whose keys stay in registers; longer ones rank chunk by chunk with block scans).
 #include "select_common.h"
 
 namespace spk {
@@ -26,6 +28,9 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
     int64_t sel_ld) {
   __shared__ __align__(16) uint32_t hist[4 * 256];
   __shared__ int scratch[kThreads / kWave + 1];
+  // per-(chunk, wave) counts of the register path, then their prefixes (+ the total)
+  __shared__ int cw_eq[(ITEMS > 0 ? ITEMS : 1) * (kThreads / kWave) + 1];
+  __shared__ int cw_sel[(ITEMS > 0 ? ITEMS : 1) * (kThreads / kWave) + 1];
   const int b = blockIdx.x;
   if (n <= 0) {
     if (sel_count && threadIdx.x == 0) sel_count[b] = 0;
@@ -45,10 +50,10 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
     return order_key(s[i]);
   };
   uint32_t reg[ITEMS > 0 ? ITEMS : 1];
+  uint8_t ev_v[ITEMS > 0 ? ITEMS : 1];  // the evicted flags as they were on entry
   if constexpr (ITEMS > 0) {
     // every load issued before any is used (clamped in bounds): one wait for the sequence
     float sv[ITEMS];
-    uint8_t ev_v[ITEMS];
 #pragma unroll
     for (int c = 0; c < ITEMS; ++c) {
       const int ic = min(c * kThreads + (int)threadIdx.x, n - 1);
@@ -87,6 +92,83 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
   if (n0 > 0) search(n0, &thr0, &need0);
   if (n01 > 0) search(n01, &thr1, &need1);
 
+  if constexpr (ITEMS > 0) {
+    // ranks in index order (chunk c, then wave, then lane) from per-(chunk, wave) counts: one
+    // barrier to publish the counts, one wave scan over them, one barrier to read the prefixes;
+    // first for the ties at each threshold, then for the T0 ∪ T1 list
+    constexpr int NWV = kThreads / kWave;
+    constexpr int NCW = ITEMS * NWV;
+    const int lane = lane_id(), wid = threadIdx.x / kWave;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    auto prefixes = [&](int* cw) {  // cw[NCW] counts -> exclusive prefixes; returns the total
+      __syncthreads();
+      if (wid == 0) {
+        int carry = 0;
+#pragma unroll
+        for (int base = 0; base < NCW; base += kWave) {
+          const int i = base + lane;
+          const int v = i < NCW ? cw[i] : 0;
+          const int incl = wave_incl_scan(v);
+          if (i < NCW) cw[i] = carry + incl - v;
+          carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+        if (lane == 0) cw[NCW] = carry;
+      }
+      __syncthreads();
+      return cw[NCW];
+    };
+    // round 1: ties at the thresholds (evicted candidates hold ranks too)
+#pragma unroll
+    for (int c = 0; c < ITEMS; ++c) {
+      const int i = c * kThreads + threadIdx.x;
+      const bool cand = i >= lo && i < hi;
+      const int e0 = __popcll(__ballot(cand && n0 > 0 && reg[c] == thr0));
+      const int e1 = __popcll(__ballot(cand && n01 > 0 && reg[c] == thr1));
+      if (lane == 0) cw_eq[c * NWV + wid] = e0 | (e1 << 16);
+    }
+    prefixes(cw_eq);
+    // round 2: tiers, evictions, and the per-(chunk, wave) counts of the list
+    uint32_t selbits = 0;
+#pragma unroll
+    for (int c = 0; c < ITEMS; ++c) {
+      const int i = c * kThreads + threadIdx.x;
+      const bool valid = i < n;
+      const bool cand = i >= lo && i < hi;
+      const uint32_t key = reg[c];
+      const bool eq0 = cand && n0 > 0 && key == thr0;
+      const bool eq1 = cand && n01 > 0 && key == thr1;
+      const int pre = cw_eq[c * NWV + wid];
+      const int eqrank0 = (pre & 0xFFFF) + __popcll(__ballot(eq0) & lt);
+      const int eqrank1 = (pre >> 16) + __popcll(__ballot(eq1) & lt);
+      const bool is_ev = cand && ev_v[c];
+      const bool top0 = cand && n0 > 0 && (key > thr0 || (eq0 && eqrank0 < need0));
+      const bool top1 = cand && n01 > 0 && (key > thr1 || (eq1 && eqrank1 < need1));
+      uint8_t t = 3;
+      if (!cand) t = 0;
+      else if (is_ev) t = 3;
+      else if (top0) t = 0;
+      else if (top1) t = 1;
+      const bool sel = valid && t <= 1;
+      selbits |= (sel ? 1u : 0u) << c;
+      if (valid) {
+        tier[i] = t;
+        if (ev && t == 3) ev[i] = 1;
+      }
+      const int nsel = __popcll(__ballot(sel));  // every lane votes: outside the lane-0 branch
+      if (lane == 0) cw_sel[c * NWV + wid] = nsel;
+    }
+    const int total_sel = prefixes(cw_sel);
+    if (sel_idx) {
+#pragma unroll
+      for (int c = 0; c < ITEMS; ++c) {
+        const bool sel = (selbits >> c) & 1u;
+        const int pos = cw_sel[c * NWV + wid] + __popcll(__ballot(sel) & lt);
+        if (sel) sel_idx[(int64_t)b * sel_ld + pos] = c * kThreads + threadIdx.x;
+      }
+    }
+    if (sel_count && threadIdx.x == 0) sel_count[b] = total_sel;
+    return;
+  }
   int run_eq0 = 0, run_eq1 = 0, run_sel = 0;
   const int chunks = (n + kThreads - 1) / kThreads;
   for (int c = 0; c < chunks; ++c) {
