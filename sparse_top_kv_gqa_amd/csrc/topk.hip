@@ -65,7 +65,7 @@ constexpr int kLargeWaves = kLargeThreads / kWave;
 constexpr int kBins = 4096;
 constexpr int kBinShift = 20;
 constexpr int kHistThreads = 256;
-constexpr int kListPerWave = 512;                     // LDS list entries per wave
+constexpr int kListPerWave = 496;  // LDS list entries per wave: two workgroups fit one CU's LDS
 constexpr int kCandMax = kLargeWaves * kListPerWave;  // candidates the LDS lists can hold
 
 int hist_chunks(int rows) {
@@ -146,8 +146,10 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
+// Two 1024-thread workgroups per CU (at most 64 VGPRs and 80 KB of LDS each), so rows beyond the
+// CU count still run in one round.
 template <bool ALIGNED>
-__global__ __launch_bounds__(kLargeThreads) void topk_final_kernel(
+__global__ __launch_bounds__(kLargeThreads) __attribute__((amdgpu_waves_per_eu(8))) void topk_final_kernel(
     const float* __restrict__ scores, int64_t s_ld, int n, int k, int C,
     const uint32_t* __restrict__ ws, int32_t* __restrict__ idx, int64_t idx_ld,
     int32_t* __restrict__ count) {
