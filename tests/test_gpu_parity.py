@@ -1142,11 +1142,12 @@ def test_residency_prefetch_other_shapes(d, dtype):
 
 
 def test_topk_decode_attn_d64_and_bound():
-    """sparse_topk_decode_attn at d = 64, and with the candidate row longer than 1024 (the
-    selection keeps its keys in LDS instead of registers): bit-identical to the two calls."""
+    """sparse_topk_decode_attn at d = 64, with candidate rows on both sides of the register
+    layouts' limits (512: two keys per thread, 1024: four) and longer than 1024 (the selection
+    keeps its keys in LDS instead of registers): bit-identical to the two calls."""
     say("topk-decode-attn-d64-lds")
     r = np.random.default_rng(8)
-    for d, nb in ((64, 300), (128, 3000)):
+    for d, nb in ((64, 300), (128, 512), (128, 513), (128, 1024), (128, 1025), (128, 3000)):
         B, Hq, Hkv, bs, k = 2, 8, 2, 16, 20
         N = nb * bs
         q = torch.tensor(r.standard_normal((B, 1, Hq, d)), dtype=torch.float32).to(torch.bfloat16).to(DEV)
