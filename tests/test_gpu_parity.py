@@ -88,6 +88,22 @@ def test_topk_bit_exact(n, kind):
             assert got[r, :kk].tolist() == exp.tolist(), (n, kind, k, r)
 
 
+@pytest.mark.parametrize("rows,n,ld", [(300, 16390, 16390), (260, 20480, 20480), (2, 131072, 131072)])
+def test_topk_wide_rows(rows, n, ld):
+    """Rows wider than 16384 (histogram, then one 1024-thread workgroup per row): more rows than
+    CUs, unaligned and aligned row strides, and few very wide rows with heavy ties.  Exact
+    against the oracle."""
+    say("topk-wide", rows, n, ld)
+    x = _rows("ties" if rows == 2 else "normal", n, rows, seed=rows)
+    xs = torch.tensor(x, device=DEV)
+    for k in (1, 700, 2622):
+        idx, cnt = spk.topk_select(xs, k)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for r in range(0, rows, max(1, rows // 7)):
+            assert got[r, :k].tolist() == oracle.topk(x[r], k).tolist(), (rows, n, k, r)
+
+
 def test_topk_strided_rows_and_ld():
     x = _rows("normal", 3000, 5, seed=9)
     big = torch.zeros((5, 3100), device=DEV)
