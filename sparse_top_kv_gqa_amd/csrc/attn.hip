@@ -788,16 +788,6 @@ __attribute__((amdgpu_waves_per_eu(SPK_ATTN_MIN_WAVES))) void attn_partial_kerne
   {
     Raw8<KT> k0[U], v0[U], k1[U], v1[U];
     int s0[U], s1[U];
-#ifndef SPK_ATTN_PIPELINE
-#define SPK_ATTN_PIPELINE 1
-#endif
-#if !SPK_ATTN_PIPELINE
-    for (int it = 0; it < iters; ++it) {
-      issue(it, k0, v0, s0);
-      consume(it, k0, v0, s0);
-    }
-    (void)k1; (void)v1; (void)s1;
-#else
     // software pipeline: the next batch's loads are in flight while this batch is consumed;
     // scheduling barriers keep the compiler from hoisting consumer work above the loads
     issue(0, k0, v0, s0);
@@ -812,7 +802,6 @@ __attribute__((amdgpu_waves_per_eu(SPK_ATTN_MIN_WAVES))) void attn_partial_kerne
       consume(it + 1, k1, v1, s1);
       __builtin_amdgcn_sched_barrier(0);
     }
-#endif
   }
 
   // merge the slots of this wave (lanes with equal `sub` hold the same dims)

@@ -1,6 +1,7 @@
 // Exact selection primitives on order-preserving uint32 keys (see order_key): a workgroup-wide
-// radix select (8-bit digits, most significant first) and a small LDS bitonic sort.  Shared by
-// topk_select and tier_classify.
+// radix select (8-bit digits, most significant first), a one-barrier-per-pass radix search and
+// the register and LDS top-k built on it.  Shared by topk_select, tier_classify, the residency
+// update and the attention's in-kernel selection.
 #pragma once
 
 #include "spk_internal.h"
@@ -274,25 +275,6 @@ __device__ __forceinline__ void lds_topk(const uint32_t* keys, int n, int kk, ui
     run_e += __popcll(be);
   }
   __syncthreads();
-}
-
-// In-place descending bitonic sort of P (a power of two) 64-bit values in LDS.
-__device__ __forceinline__ void bitonic_sort_desc(uint64_t* s, int P) {
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < (P >> 1); t += blockDim.x) {
-        const int i = 2 * stride * (t / stride) + (t % stride);
-        const int j = i + stride;
-        const bool desc = (i & size) == 0;
-        const uint64_t a = s[i], b = s[j];
-        if (desc ? (a < b) : (a > b)) {
-          s[i] = b;
-          s[j] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
 }
 
 }  // namespace spk

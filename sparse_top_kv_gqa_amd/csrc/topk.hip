@@ -22,7 +22,6 @@ constexpr int kSmallThreads = 256;
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr int kSmallMax = 64 * kSmallThreads;  // 16384
 
-__device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
 // Rows of up to 64*256 keys held in registers (KPT per thread); reg_topk selects with one
 // barrier per radix pass and one or two for the compaction counts.
