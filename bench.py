@@ -355,6 +355,73 @@ def union_rows_block(idx, n_tokens, bs, n_sink, n_recent):
     return int(mask.sum())
 
 
+def block_fetch_lists(idx, count, n_tokens, bs, n_sink, n_recent):
+    """Each (b, kvh) group's fetch list as token ids: the sinks, the recent window, then the
+    selected blocks' rows not already listed; -1 marks a hole.  The rows the attention reads,
+    for the gather reference (setup-time bookkeeping)."""
+    dev = idx.device
+    G = idx.shape[0] * idx.shape[2]
+    blocks = idx.reshape(G, -1).long()
+    nsel = count.reshape(G, 1).long()
+    tok = blocks[:, :, None] * bs + torch.arange(bs, device=dev)
+    live = (torch.arange(blocks.shape[1], device=dev)[None, :] < nsel)[:, :, None]
+    tok = tok.reshape(G, -1)
+    live = live.expand(-1, -1, bs).reshape(G, -1)
+    ns = min(n_sink, n_tokens)
+    rs = max(n_tokens - n_recent, 0)
+    forced_tok = torch.cat([torch.arange(ns, device=dev), torch.arange(max(rs, ns), n_tokens, device=dev)])
+    keep = live & (tok < n_tokens) & (tok >= ns) & (tok < rs)
+    sel = torch.where(keep, tok, torch.full_like(tok, -1))
+    return torch.cat([forced_tok[None, :].expand(G, -1), sel], dim=1).to(torch.int32).contiguous()
+
+
+def gather_ceiling_gbs(caches, lists, stream, reps=12):
+    """HBM rate of a plain gather of exactly the attention's rows: the best median over
+    workgroups per group of the library's gather reference (spk_gather_read), rotating over
+    the layer caches like the timed steps, with a long read queued first so each event pair
+    brackets one kernel."""
+    import ctypes
+    import sparse_top_kv_gqa_amd as spk
+    hip = _hip()
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pad = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    L = len(caches)
+    nbytes = [int((x >= 0).sum()) * (k.shape[-1] * k.element_size() * 2)
+              for x, (k, _) in zip(lists, caches)]
+    best = 0.0
+    for wpg in (11, 22, 44, 64):
+        pairs = []
+        for _ in range(reps):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if (hip.hipEventCreateWithFlags(ctypes.byref(a), HIP_EVENT_DISABLE_SYSTEM_FENCE) or
+                    hip.hipEventCreateWithFlags(ctypes.byref(b), HIP_EVENT_DISABLE_SYSTEM_FENCE)):
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            pairs.append((a, b))
+        with torch.cuda.stream(stream):
+            for i in range(L):
+                spk.gather_read(caches[i][0], caches[i][1], lists[i], wpg, sink, stream)
+            spk.stream_read(pad, 48, sink, stream)                 # the host runs ahead
+            for i, (a, b) in enumerate(pairs):
+                hip.hipEventRecord(a, sh)
+                spk.gather_read(caches[i % L][0], caches[i % L][1], lists[i % L], wpg, sink, stream)
+                hip.hipEventRecord(b, sh)
+        torch.cuda.synchronize()
+        rates = []
+        for i, (a, b) in enumerate(pairs):
+            f = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(f), a, b):
+                raise RuntimeError("hipEventElapsedTime failed")
+            rates.append(nbytes[i % L] / (f.value * 1e-3) / 1e9)
+            hip.hipEventDestroy(a)
+            hip.hipEventDestroy(b)
+        rates.sort()
+        best = max(best, rates[len(rates) // 2])
+    del pad
+    return round(best, 1)
+
+
 def bench_block(args, windowed=False):
     import workloads as W
     from sparse_top_kv_gqa_amd import sparse_decode_attn, window_count
@@ -445,6 +512,12 @@ def bench_block(args, windowed=False):
              else "attn_partial_mfma_kernel (sparse_decode_attn gather)")
     res["roofline"] = roofline(kname, att_bytes, gather_ms,
                                traffic=measured_traffic("block_windowed" if windowed else "block"))
+    # the rate a plain gather of the same rows reaches (no selection, no arithmetic)
+    lists = [block_fetch_lists(d.idx, d.count, d.n_tokens, d.bs, d.n_sink, d.n_recent)
+             for d in decs]
+    gc = gather_ceiling_gbs([(d.k, d.v) for d in decs], lists, stream)
+    res["roofline"]["gather_read_ceiling_GBs"] = gc
+    res["roofline"]["frac_of_gather_ceiling"] = round(res["roofline"]["achieved"] / gc, 4)
     ctx = dict(w=w, dec=decs[0], q=qs[0], pred=preds[0], windowed=windowed)
     return res, ctx
 

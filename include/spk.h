@@ -101,6 +101,24 @@ SPK_API spk_status spk_set_attn_timing_events(void* begin, void* end);
 SPK_API spk_status spk_stream_read(const void* p, size_t bytes, int workgroups, uint32_t* sink,
                                    void* stream);
 
+/* Measurement reference: reads the K and V rows named by per-group row lists, each listed row
+ * once, and computes nothing of the method.  Its rate is the HBM rate a plain gather of exactly
+ * that set of rows reaches on the device at hand (the rows of a sparse selection are scattered,
+ * which a contiguous streaming read does not capture).  Group g's list is
+ * rows[g*rows_ld .. g*rows_ld + rows_ld); entry t names the rows at
+ * k + g*group_stride + t*row_stride and v + g*group_stride + t*row_stride (byte offsets), of
+ * which the first row_bytes bytes are read; entries < 0 or >= n_rows are skipped.  Each group's
+ * list is cut into wg_per_group contiguous parts, one workgroup each.  The caller guarantees
+ * that every row of every group lies inside its k and v buffers.  `sink`: as spk_stream_read.
+ * Enqueues on `stream` and returns.  SPK_EINVAL on a null pointer, row_bytes not in {64, 128,
+ * 256, 512, 1024}, k, v or a stride not a multiple of 16 bytes, row_stride < row_bytes, negative
+ * sizes, rows_ld >= 2^31, groups or wg_per_group outside [0, 65535] / [1, 65535]; nothing is
+ * launched when groups, rows_ld or n_rows is 0. */
+SPK_API spk_status spk_gather_read(const void* k, const void* v, int64_t row_bytes,
+                                   int64_t group_stride, int64_t row_stride, int64_t n_rows,
+                                   const int32_t* rows, int64_t rows_ld, int groups,
+                                   int wg_per_group, uint32_t* sink, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * sparse_index_score — compact indexer scores, no softmax.
  *

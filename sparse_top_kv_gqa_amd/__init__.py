@@ -35,7 +35,7 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "spk_set_attn_timing_events", "sparse_index_topk",
            "sparse_topk_decode_attn_workspace_size", "sparse_topk_decode_attn",
            "sparse_window_pool", "sparse_index_score_windowed", "residency_update",
-           "residency_prefetch", "spk_stream_read")
+           "residency_prefetch", "spk_stream_read", "spk_gather_read")
 
 
 class SpkError(RuntimeError):
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.spk_set_attn_timing_events.argtypes = [P, P]
     L.spk_stream_read.restype = I
     L.spk_stream_read.argtypes = [P, SZ, I, P, P]
+    L.spk_gather_read.restype = I
+    L.spk_gather_read.argtypes = [P, P, I64, I64, I64, I64, P, I64, I, I, P, P]
     L.sparse_topk_decode_attn_workspace_size.restype = I
     L.sparse_topk_decode_attn_workspace_size.argtypes = [I, I, I, I, I, I, I, I, I, I,
                                                          ctypes.POINTER(SZ)]
@@ -428,6 +430,31 @@ def stream_read(buf: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=N
         raise ValueError("stream_read: buf and sink must be device tensors")
     _check(lib().spk_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(workgroups),
                                  _ptr(sink), _stream(stream)), "spk_stream_read")
+
+
+def gather_read(k: torch.Tensor, v: torch.Tensor, rows: torch.Tensor, wg_per_group: int,
+                sink: torch.Tensor, stream=None):
+    """Measurement reference: reads the K and V rows each group's list names (``rows`` int32
+    [groups, rows_ld], entries < 0 skipped), once each, for caches ``k``, ``v``
+    [B, Hkv, N, d] (or [groups, N, d]) views sharing strides, with ``wg_per_group``
+    workgroups per group (``sink`` as in stream_read)."""
+    if not (k.is_cuda and v.is_cuda and rows.is_cuda and sink.is_cuda):
+        raise ValueError("gather_read: device tensors expected")
+    if k.dim() == 4:
+        if k.stride(0) != k.shape[1] * k.stride(1) or v.stride() != k.stride():
+            raise ValueError("gather_read: k and v must share strides, groups evenly spaced")
+        groups, sg, sn = k.shape[0] * k.shape[1], k.stride(1), k.stride(2)
+    elif k.dim() == 3 and v.stride() == k.stride():
+        groups, sg, sn = k.shape[0], k.stride(0), k.stride(1)
+    else:
+        raise ValueError("gather_read: k, v must be [B, H, N, d] or [groups, N, d] views")
+    if k.stride(-1) != 1 or rows.dim() != 2 or rows.shape[0] != groups or rows.dtype != torch.int32:
+        raise ValueError("gather_read: contiguous rows of k/v and an int32 [groups, ld] list")
+    _contig(rows, "rows")
+    e = k.element_size()
+    _check(lib().spk_gather_read(_ptr(k), _ptr(v), k.shape[-1] * e, sg * e, sn * e, k.shape[-2],
+                                 _ptr(rows), rows.shape[1], groups, int(wg_per_group), _ptr(sink),
+                                 _stream(stream)), "spk_gather_read")
 
 
 def topk_attn_workspace_size(B, Hq, Hkv, d, n_tokens, n_cand, k, gran=1, n_sink=0,

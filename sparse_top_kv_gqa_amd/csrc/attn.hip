@@ -404,7 +404,7 @@ struct AttnArgs {
 template <int D, int NQ, int NW>
 __device__ void finish_split(const AttnArgs& a, float (&red)[NW][NQ][D + 2], int g, int split) {
   const int64_t pbase = ((int64_t)g * a.smax + split) * NQ;
-  for (int e = threadIdx.x; e < NQ * D; e += blockDim.x) {
+  for (int e = threadIdx.x; e < NQ * D; e += kThreads) {
     const int n = e / D, dim = e % D;
     float mx = -INFINITY;
 #pragma unroll
@@ -613,14 +613,14 @@ __device__ __forceinline__ void fill_slot_table(const AttnArgs& a, int b, int kv
   const uint32_t* mrow = kMask ? a.mask + (int64_t)g * a.list_ld : nullptr;
   const int n = a.n_tokens;
   const int ns = min(a.n_sink, n), rs = max(n - a.n_recent, 0);
-  for (int it = 0, i = threadIdx.x; i < tab_rows; ++it, i += blockDim.x) {
+  for (int it = 0, i = threadIdx.x; i < tab_rows; ++it, i += kThreads) {
     int slot_v = kDead;
     if (i < nrows) {
       int tok;
       if constexpr (MODE == kListVirtual || MODE == kListScores) {
         const int p = r0 + i;
         const int ps = p - forced_rows(ns, rs, n);  // position in the selection part
-        // pre_e[it]: the entry of row r0 + threadIdx.x + it*blockDim.x, read earlier
+        // pre_e[it]: the entry of row r0 + threadIdx.x + it*kThreads, read earlier
         const int e = it < n_pre ? (it == 0 ? pre_e[0] : pre_e[1])
                                  : (ps >= 0 && ps < n_sel * a.gran ? vlist[ps / a.gran] : 0);
         tok = virtual_token(p, a.gran, e, ns, rs, n);
@@ -924,7 +924,7 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   int n_sel = 0;
   int pre_e[2] = {0, 0}, n_pre = 0;  // kListVirtual: entries read ahead of the count
   // the split that publishes the group's row count (and, selecting from scores, the selection)
-  const int pub_split = MODE == kListScores ? (int)gridDim.x - 1 : 0;
+  const int pub_split = MODE == kListScores ? a.smax - 1 : 0;  // the grid is (smax, groups)
   if constexpr (MODE == kListScores) {
     const float* srow = a.sc_scores + (int64_t)g * a.sc_ld;
     const int n = a.sc_n, kk = min(a.sc_k, n);

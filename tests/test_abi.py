@@ -156,6 +156,29 @@ def test_stream_read_validation():
     assert L.spk_stream_read(A, 0, 8, A, None) == 0      # nothing to read: no launch
 
 
+def test_gather_read_validation():
+    L = spk.lib()
+    P = ctypes.c_void_p
+    ok = dict(k=A, v=A, rb=256, sg=1 << 20, sn=256, n=4096, rows=A, ld=64, groups=8, wpg=4)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.spk_gather_read(a["k"], a["v"], a["rb"], a["sg"], a["sn"], a["n"], a["rows"],
+                                 a["ld"], a["groups"], a["wpg"], A, None)
+    assert call(k=None) == 1 and "null" in _err()
+    assert call(rows=None) == 1
+    assert call(rows=None, ld=0) == 0                   # no list, nothing to read
+    for rb in (0, 16, 48, 96, 2048):
+        assert call(rb=rb) == 1 and "row_bytes" in _err()
+    assert call(v=P(0x100008)) == 1 and "16" in _err()
+    assert call(sn=264) == 1 and call(sg=(1 << 20) + 8) == 1
+    assert call(sn=128) == 1 and "strides" in _err()    # rows overlap
+    assert call(n=-1) == 1 and call(ld=1 << 31) == 1 and call(groups=65536) == 1
+    assert call(wpg=0) == 1 and "wg_per_group" in _err()
+    assert call(wpg=65536) == 1
+    assert call(groups=0) == 0 and call(ld=0) == 0 and call(n=0) == 0   # nothing to launch
+
+
 def test_index_topk_validation():
     L = spk.lib()
     P = ctypes.c_void_p

@@ -1186,6 +1186,45 @@ def test_topk_decode_attn_d64_and_bound():
 
 # ------------------------------------------------------------------------- measurement reference
 
+def test_gather_read_reference_reads_listed_rows():
+    """The gather reference folds exactly the listed K and V rows: a word planted in a listed row
+    reaches the sink whatever the workgroup split; one planted in an unlisted row, or in row 0
+    (which skipped entries re-read without folding), does not."""
+    say("gather-read")
+    G, N, d = 6, 700, 128
+    magic = 0x9E3779B9 - (1 << 32)
+    k = torch.zeros(G, N, d, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    gen = torch.Generator().manual_seed(5)
+    rows = torch.full((G, 301), -1, dtype=torch.int32)
+    for g in range(G):
+        rows[g, :250] = (torch.randperm(N - 1, generator=gen)[:250] + 1).int()   # never row 0
+    rows[:, 250] = N + 7                                   # out of range: skipped
+    rows_d = rows.to(DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+
+    def folded():
+        out = []
+        for wpg in (1, 3, 7, 1000):
+            sink.zero_()
+            spk.gather_read(k, v, rows_d, wpg, sink)
+            torch.cuda.synchronize()
+            out.append(int(sink.item()) & 0xFFFFFFFF)
+        return out
+    assert folded() == [0] * 4
+    unlisted = next(t for t in range(1, N) if t not in set(rows[2].tolist()))
+    k.view(torch.int32)[2, unlisted, 5] = magic
+    v.view(torch.int32)[2, 0, 7] = magic
+    assert folded() == [0] * 4
+    k.zero_()
+    v.zero_()
+    v.view(torch.int32)[4, int(rows[4, 249]), 63] = magic    # the last listed row of group 4
+    assert folded() == [0x9E3779B9] * 4
+    v.zero_()
+    k.view(torch.int32)[0, int(rows[0, 0]), 0] = magic
+    assert folded() == [0x9E3779B9] * 4
+
+
 def test_stream_read_reference_reads_every_word():
     """The streaming-read reference reads the whole buffer in any chunking (ragged tails
     included): its sink stays untouched unless the folded words hit the constant, which a
