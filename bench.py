@@ -768,6 +768,14 @@ def bench_tiers(args):
     res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather, one layer at "
                                f"{n_last} tokens)", att_bytes, gather_ms,
                                traffic=measured_traffic("tiers"))
+    # the rate a plain gather of the same rows reaches: each KV group reads its sequence's list
+    ld = dec.sel.shape[-1]
+    live = torch.arange(ld, device=dec.sel.device)[None, :] < dec.count.reshape(-1, 1)
+    seq_rows = torch.where(live, dec.sel.reshape(-1, ld), torch.full_like(dec.sel.reshape(-1, ld), -1))
+    lists = [seq_rows.repeat_interleave(w.Hkv, dim=0).contiguous()]
+    gc = gather_ceiling_gbs([(k0, v0)], lists, stream)
+    res["roofline"]["gather_read_ceiling_GBs"] = gc
+    res["roofline"]["frac_of_gather_ceiling"] = round(res["roofline"]["achieved"] / gc, 4)
     ctx = dict(w=w, caches=caches, qs=qs, n_last=n_last)
     return res, ctx
 
