@@ -769,9 +769,11 @@ def bench_tiers(args):
                                f"{n_last} tokens)", att_bytes, gather_ms,
                                traffic=measured_traffic("tiers"))
     # the rate a plain gather of the same rows reaches: each KV group reads its sequence's list
-    ld = dec.sel.shape[-1]
-    live = torch.arange(ld, device=dec.sel.device)[None, :] < dec.count.reshape(-1, 1)
-    seq_rows = torch.where(live, dec.sel.reshape(-1, ld), torch.full_like(dec.sel.reshape(-1, ld), -1))
+    # (trimmed to the longest list: a skipped entry still costs the reference a cached load)
+    ld = int(dec.count.max())
+    sel = dec.sel.reshape(dec.sel.shape[0], -1)[:, :ld]
+    live = torch.arange(ld, device=sel.device)[None, :] < dec.count.reshape(-1, 1)
+    seq_rows = torch.where(live, sel, torch.full_like(sel, -1))
     lists = [seq_rows.repeat_interleave(w.Hkv, dim=0).contiguous()]
     gc = gather_ceiling_gbs([(k0, v0)], lists, stream)
     res["roofline"]["gather_read_ceiling_GBs"] = gc
