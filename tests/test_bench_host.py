@@ -1,0 +1,39 @@
+"""Host-side bookkeeping of bench.py: the fetch lists the gather reference reads must be exactly
+the rows the block attention reads (sinks, recent window and the selected blocks, each once)."""
+import os
+import sys
+
+import torch
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import bench  # noqa: E402
+
+
+def _expected(blocks, n_tokens, bs, n_sink, n_recent):
+    rows = set(range(min(n_sink, n_tokens))) | set(range(max(n_tokens - n_recent, 0), n_tokens))
+    for e in blocks:
+        rows |= set(t for t in range(e * bs, e * bs + bs) if t < n_tokens)
+    return rows
+
+
+def test_block_fetch_lists_match_the_attended_rows():
+    gen = torch.Generator().manual_seed(11)
+    for (B, H, k, bs, N, ns, nr) in [(2, 3, 5, 64, 2048, 4, 512), (1, 2, 7, 16, 1000, 0, 37),
+                                     (3, 1, 4, 64, 300, 8, 0), (1, 1, 3, 64, 256, 300, 300)]:
+        nb = N // bs
+        idx = torch.stack([torch.stack([torch.sort(torch.randperm(nb, generator=gen)[:k]).values
+                                        for _ in range(H)]) for _ in range(B)]).unsqueeze(1).int()
+        cnt = torch.randint(0, k + 1, (B, 1, H), generator=gen, dtype=torch.int32)
+        lists = bench.block_fetch_lists(idx, cnt, N, bs, ns, nr)
+        assert lists.dtype == torch.int32 and lists.shape[0] == B * H
+        for g in range(B * H):
+            b, h = g // H, g % H
+            row = lists[g]
+            live = row[row >= 0].tolist()
+            assert len(live) == len(set(live)), "a row listed twice"
+            assert set(live) == _expected(idx[b, 0, h, :int(cnt[b, 0, h])].tolist(), N, bs, ns, nr)
+            assert all(0 <= t < N for t in live)
+        total = int((lists >= 0).sum())
+        full = torch.full_like(cnt, k)
+        if bool((cnt == full).all()):
+            assert total == bench.union_rows_block(idx, N, bs, ns, nr)
