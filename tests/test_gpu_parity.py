@@ -1186,6 +1186,53 @@ def test_topk_decode_attn_d64_and_bound():
 
 # ------------------------------------------------------------------------- measurement reference
 
+def _graph_replays_match_eager(step, outs, eager_between):
+    """Capture step() in a HIP graph and replay it three times, with the outputs poisoned
+    before each replay and other eager library work between replays: every replay must
+    reproduce the eager step's outputs bit for bit."""
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o in outs:
+            o.fill_(float("nan") if o.is_floating_point() else -7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, ref):
+            assert torch.equal(o, e), f"replay {r} differs from the eager step"
+        eager_between()
+        torch.cuda.synchronize()
+
+
+def test_graph_replays_of_decode_steps():
+    """The block step (scores, top-k inside the attention, combine) and the per-head token step
+    (scores, wide top-k, union assembly, attention) replay from a captured graph exactly."""
+    say("graph-replay")
+    wb = W.scaled(W.LLAMA8B_BLOCK, B=2, Hkv=2, Hq=8, N=64 * 40 + 17, k=6)
+    q, pred, k, v, dec, _, _ = _block_case(wb)
+    other = BlockSparseDecode(k, v, wb.N, wb.Hq, wb.block_size, wb.k, wb.n_sink, wb.n_recent)
+    other.pool(pred)
+    q2 = W.queries(wb, step=5, device=DEV)
+    _graph_replays_match_eager(lambda: dec.step(q, pred), [dec.out, dec.lse, dec.idx, dec.count],
+                               lambda: other.step(q2, pred))
+    wt = W.scaled(W.PER_HEAD_2PCT, B=2, Hkv=2, Hq=8, N=6000, k=120)
+    qt = W.queries(wt, device=DEV)
+    kt = W.kv_cache(wt, "k", device=DEV)
+    vt = W.kv_cache(wt, "v", device=DEV)
+    tok = TokenSparseDecode(kt, vt, wt.N, wt.Hq, 1, wt.k, "token_per_head")
+    tok2 = TokenSparseDecode(kt, vt, wt.N, wt.Hq, 1, wt.k, "token_per_head")
+    qt2 = W.queries(wt, step=3, device=DEV)
+    _graph_replays_match_eager(lambda: tok.step(qt), [tok.out, tok.lse, tok.idx, tok.count],
+                               lambda: tok2.step(qt2))
+
+
 def test_gather_read_reference_reads_listed_rows():
     """The gather reference folds exactly the listed K and V rows: a word planted in a listed row
     reaches the sink whatever the workgroup split; one planted in an unlisted row, or in row 0
