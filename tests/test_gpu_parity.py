@@ -1233,6 +1233,37 @@ def test_graph_replays_of_decode_steps():
                                lambda: tok2.step(qt2))
 
 
+def test_concurrent_streams_match_sequential_calls():
+    """Calls with distinct outputs and workspaces may run on concurrent streams: a block step and
+    a per-head token step issued on two streams, several times without waits between, give
+    exactly their results when run alone."""
+    say("two-streams")
+    wb = W.scaled(W.LLAMA8B_BLOCK, B=2, Hkv=2, Hq=8, N=64 * 52 + 9, k=7)
+    q, pred, k, v, dec, out_b, lse_b = _block_case(wb)
+    idx_b = dec.idx.clone()
+    wt = W.scaled(W.PER_HEAD_2PCT, B=2, Hkv=2, Hq=8, N=7000, k=140)
+    qt = W.queries(wt, device=DEV)
+    tok = TokenSparseDecode(W.kv_cache(wt, "k", device=DEV), W.kv_cache(wt, "v", device=DEV),
+                            wt.N, wt.Hq, 1, wt.k, "token_per_head")
+    tok.step(qt)
+    torch.cuda.synchronize()
+    out_t, lse_t, idx_t = tok.out.clone(), tok.lse.clone(), tok.idx.clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for r in range(4):
+        for o in (dec.out, dec.lse, tok.out, tok.lse):
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            dec.step(q, pred)
+        with torch.cuda.stream(s2):
+            tok.step(qt)
+        torch.cuda.synchronize()
+        assert torch.equal(dec.out, out_b) and torch.equal(dec.lse, lse_b)
+        assert torch.equal(dec.idx, idx_b)
+        assert torch.equal(tok.out, out_t) and torch.equal(tok.lse, lse_t)
+        assert torch.equal(tok.idx, idx_t)
+
+
 def test_gather_read_reference_reads_listed_rows():
     """The gather reference folds exactly the listed K and V rows: a word planted in a listed row
     reaches the sink whatever the workgroup split; one planted in an unlisted row, or in row 0
