@@ -1264,6 +1264,39 @@ def test_concurrent_streams_match_sequential_calls():
         assert torch.equal(tok.idx, idx_t)
 
 
+def test_host_pools_must_be_pinned():
+    """Host pools in pageable or device memory are refused before anything is launched, and no
+    HIP error is left behind: the same call with pinned pools then runs and reproduces the
+    all-HBM result bit for bit."""
+    say("host-pools-pinned")
+    B, Hq, Hkv, d, N, k = 1, 4, 1, 128, 512, 96
+    q = _rand((B, 1, Hq, d), torch.bfloat16, 61)
+    kc = _rand((B, Hkv, N, d), torch.bfloat16, 62)
+    vc = _rand((B, Hkv, N, d), torch.bfloat16, 63)
+    selt = torch.tensor(_sorted_sets(B, N, k, 64), device=DEV)
+    cntt = torch.full((B,), k, dtype=torch.int32, device=DEV)
+    o_a, l_a = spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_seq", N)
+    loc = torch.arange(N, dtype=torch.int32).repeat(B, Hkv, 1)
+    odd = torch.arange(1, N, 2)
+    loc[:, :, odd] = ~torch.arange(odd.numel(), dtype=torch.int32)
+    loc = loc.to(DEV)
+    shape = (B, Hkv, odd.numel(), d)
+    for kh, vh in [(torch.empty(shape, dtype=torch.bfloat16), torch.empty(shape, dtype=torch.bfloat16)),
+                   (torch.empty(shape, dtype=torch.bfloat16, device=DEV),
+                    torch.empty(shape, dtype=torch.bfloat16, device=DEV))]:
+        with pytest.raises(spk.SpkError) as err:
+            spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_seq", N, k_host=kh, v_host=vh, loc=loc)
+        assert err.value.status == 1 and ("pinned" in str(err.value) or "known to HIP" in str(err.value))
+    kh = torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
+    kh.copy_(kc[:, :, odd.to(DEV)].cpu())
+    vh.copy_(vc[:, :, odd.to(DEV)].cpu())
+    o_b, l_b = spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_seq", N, k_host=kh, v_host=vh,
+                                      loc=loc)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+
+
 def test_gather_read_reference_reads_listed_rows():
     """The gather reference folds exactly the listed K and V rows: a word planted in a listed row
     reaches the sink whatever the workgroup split; one planted in an unlisted row, or in row 0
