@@ -25,9 +25,11 @@ Every function cites the passage it follows by page title and section:
 * "Nem Todos os Pensamentos Necessitam de HBM" §4 "Implementação do Sistema"
   (differential prefetch of newly promoted rows) — residency_update.
 
-Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 closed forms, invariants, brute force on tiny inputs or an independent library
-routine.  Nothing in this package is "parity unpinned" except the pages'
+routine, and so are the checkers every parity assertion goes through
+(``steps.rel_err``, ``steps.elem_rel_err``, ``steps.topk_band_ok``: hand values, sign
+flips, outliers, zero references, wrong counts, duplicates and out-of-range indices).  Nothing in this package is "parity unpinned" except the pages'
 published throughput figures, which it does not model.
 """
 from .core import (  # noqa: F401

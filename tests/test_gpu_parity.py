@@ -19,7 +19,8 @@ from sparse_top_kv_gqa_amd.decode import BlockSparseDecode, TieredDecode, TokenS
 import workloads as W
 
 pytestmark = pytest.mark.gpu
-TOL = 2e-3
+TOL = osteps.TOL
+ATTN_REG = osteps.ATTN_REGRESSION_BOUND
 DEV = "cuda"
 
 
@@ -40,14 +41,27 @@ def rel(x, ref):
     return osteps.rel_err(x, ref)
 
 
-def check_rows(x, ref, tol=TOL, what=""):
+def check_rows(x, ref, tol=TOL, what="", reg=None):
+    """Per row: normwise relative error <= tol, and elementwise relative error (each element
+    against max(|ref_i|, 1e-2·max|ref|)) <= tol; with `reg`, also normwise <= reg (the
+    regression bound of the attention outputs)."""
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, f"{what}: shape {x.shape} vs {ref.shape}"
     x2 = x.reshape(-1, x.shape[-1])
     r2 = ref.reshape(-1, ref.shape[-1])
     worst = max(rel(a, b) for a, b in zip(x2, r2))
+    worst_el = max(osteps.elem_rel_err(a, b) for a, b in zip(x2, r2))
     assert worst <= tol, f"{what}: normwise rel err {worst:.3e} > {tol}"
+    assert worst_el <= tol, f"{what}: elementwise rel err {worst_el:.3e} > {tol}"
+    if reg is not None:
+        assert worst <= reg, f"{what}: normwise rel err {worst:.3e} above the regression bound {reg}"
     return worst
+
+
+def check_attn(x, ref, what=""):
+    """Attention outputs: the parity bar and the regression bound."""
+    return check_rows(x, ref, what=what, reg=ATTN_REG)
 
 
 # ------------------------------------------------------------------------------------ top-k
@@ -133,13 +147,13 @@ def test_tiny_workload_end_to_end_and_dense():
     assert osteps.topk_band_ok(sel, ref_scores, w.k, TOL)
     scale = oracle.softmax_scale(w.d)
     o_ref, l_ref, _ = oracle.attend(qh, kh[sel], vh[sel], scale)
-    check_rows(out.cpu().numpy()[0, 0], o_ref, what="attention")
+    check_attn(out.cpu().numpy()[0, 0], o_ref, what="attention")
     np.testing.assert_allclose(lse.cpu().numpy()[0, 0], l_ref, rtol=TOL)
     # k = N: sparse attention is dense attention
     dense = TokenSparseDecode(k, v, w.N, w.Hq, w.T, w.N, "token_group_mean")
     out_d, lse_d = dense.step(q)
     o_ref, l_ref, _ = oracle.attend(qh, kh, vh, scale)
-    check_rows(out_d.cpu().numpy()[0, 0], o_ref, what="dense attention")
+    check_attn(out_d.cpu().numpy()[0, 0], o_ref, what="dense attention")
     np.testing.assert_allclose(lse_d.cpu().numpy()[0, 0], l_ref, rtol=TOL)
 
 
@@ -178,7 +192,7 @@ def test_block_workload_small(N):
             assert osteps.topk_band_ok(blocks, ref, w.k, TOL)
             toks = oracle.selection_tokens(blocks, w.block_size, w.N, w.n_sink, w.n_recent)
             o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], kh[toks], vh[toks], scale)
-            check_rows(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="block attention")
+            check_attn(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="block attention")
             np.testing.assert_allclose(lse.cpu().numpy()[b, 0, h * G:(h + 1) * G], l_ref, rtol=TOL)
     # BLOCK_RAW scores equal BLOCK_POOLED scores up to rounding (pooling is linear)
     raw = spk.sparse_index_score("block_raw", pred, k, w.N, w.block_size)
@@ -207,7 +221,7 @@ def test_block_workload_full_size_sampled_and_deterministic():
         assert osteps.topk_band_ok(blocks, ref, w.k, TOL)
         toks = oracle.selection_tokens(blocks, w.block_size, w.N, w.n_sink, w.n_recent)
         o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], kh[toks], vh[toks], scale)
-        check_rows(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="block attention")
+        check_attn(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="block attention")
 
 
 def test_block_nan_poisoning_unselected_rows():
@@ -258,7 +272,7 @@ def test_per_head_workload_small(N):
                 assert sel.tolist() == oracle.topk(sc[b, 0, hq], w.k).tolist()
                 assert osteps.topk_band_ok(sel, ref[j], w.k, TOL)
                 o_ref, l_ref, _ = oracle.attend(qg[j:j + 1], kh[sel], vh[sel], scale)
-                check_rows(out.cpu().numpy()[b, 0, hq], o_ref[0], what="per-head attention")
+                check_attn(out.cpu().numpy()[b, 0, hq], o_ref[0], what="per-head attention")
                 assert abs(lse.cpu().numpy()[b, 0, hq] - l_ref[0]) <= TOL * abs(l_ref[0]) + 1e-6
     # outliers present as built: exactly 1% of rows scaled by 4 in every group
     assert W.outlier_rows(w, 0, 0).numel() == round(0.01 * w.N)
@@ -326,7 +340,7 @@ def test_spec_verify_union_host_rows_residency_invariance(N):
                 assert sel.tolist() == oracle.topk(sc[b, t, h], w.k).tolist()
                 assert osteps.topk_band_ok(sel, r["scores"][t], w.k, TOL)
                 o_ref, l_ref, _ = oracle.attend(qt[t], kh[sel], vh[sel], scale)
-                check_rows(out_h.cpu().numpy()[b, t, h * G:(h + 1) * G], o_ref, what="verify attention")
+                check_attn(out_h.cpu().numpy()[b, t, h * G:(h + 1) * G], o_ref, what="verify attention")
 
 
 # ------------------------------------------------------------------------------------ tiers
@@ -381,7 +395,7 @@ def test_tiered_decode_small_matches_oracle():
                 assert dec.tier.cpu().numpy()[b, :n].tolist() == r["tier"].tolist()
                 c = int(dec.count.cpu()[b])
                 assert dec.sel.cpu().numpy()[b, :c].tolist() == r["tokens"].tolist()
-            check_rows(out.cpu().numpy()[:, b, 0], r["out"], what="tiered attention")
+            check_attn(out.cpu().numpy()[:, b, 0], r["out"], what="tiered attention")
             check_rows(dec.s.cpu().numpy()[b, :n][None], r["s"][None], what="importance")
             assert abs(float(dec.s.cpu().numpy()[b, :n].astype(np.float64).sum()) - (t + 1)) < 1e-3
 
@@ -433,7 +447,7 @@ def test_empty_and_degenerate_selections():
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
     kh, vh = host(k[1, 0]), host(v[1, 0])
     o_ref, l_ref, _ = oracle.attend(host(q)[1, 0], kh[[5, 299]], vh[[5, 299]], oracle.softmax_scale(w.d))
-    check_rows(out.cpu().numpy()[1, 0], o_ref, what="ragged selection")
+    check_attn(out.cpu().numpy()[1, 0], o_ref, what="ragged selection")
     # no tokens at all
     out0, lse0 = spk.sparse_decode_attn(q, k, v, sel, cnt, "per_kv_head", 0)
     torch.cuda.synchronize()
@@ -472,7 +486,7 @@ def test_per_head_full_size_sampled():
             assert sel.tolist() == oracle.topk(gs, w.k).tolist()
             assert osteps.topk_band_ok(sel, ref[j], w.k, TOL)
             o_ref, l_ref, _ = oracle.attend(qg[j:j + 1], kh[sel], vh[sel], scale)
-            check_rows(out[b, 0, hq].cpu().numpy(), o_ref[0], what="per-head attention")
+            check_attn(out[b, 0, hq].cpu().numpy(), o_ref[0], what="per-head attention")
     del k, v, dec
     _free()
 
@@ -519,7 +533,7 @@ def test_spec_verify_full_size_sampled_with_host_rows():
             assert sel.tolist() == oracle.topk(gs, w.k).tolist()
             assert osteps.topk_band_ok(sel, ref, w.k, TOL)
             o_ref, _, _ = oracle.attend(qt[t], kh[sel], vh[sel], scale)
-            check_rows(out[b, t, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="verify attention")
+            check_attn(out[b, t, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="verify attention")
     del k, v, k_att, v_att, dec, kh_pool, vh_pool
     _free()
 
@@ -555,7 +569,7 @@ def test_tiered_full_size_sampled_steps():
                 assert dec.tier[b, :n].cpu().numpy().tolist() == r["tier"].tolist()
                 c = int(dec.count[b])
                 assert dec.sel[b, :c].cpu().numpy().tolist() == r["tokens"].tolist()
-            check_rows(out[:, b, 0].cpu().numpy(), r["out"], what="tiered attention")
+            check_attn(out[:, b, 0].cpu().numpy(), r["out"], what="tiered attention")
             check_rows(dec.s[b, :n].cpu().numpy()[None], r["s"][None], what="importance")
     del caches, dec
     _free()
@@ -646,9 +660,31 @@ def test_block_decode_fused_and_separate_paths_agree():
         for b in range(w.B):
             for h in range(w.Hkv):
                 assert dec.idx[b, 0, h].cpu().numpy().tolist() == oracle.topk(sc[b, 0, h], w.k).tolist()
-        outs.append((dec.idx.clone(), out.clone()))
+        # each path's output against the oracle over its own selection
+        kh, vh, qh = host(k), host(v), host(q)
+        scale = oracle.softmax_scale(w.d)
+        G = w.G
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                blocks = dec.idx[b, 0, h].cpu().numpy()
+                toks = oracle.selection_tokens(blocks, w.block_size, w.N, w.n_sink, w.n_recent)
+                o_ref, _, _ = oracle.attend(qh[b, 0, h * G:(h + 1) * G], kh[b, h][toks],
+                                            vh[b, h][toks], scale)
+                check_attn(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref,
+                           what=f"block attention (fused={fused})")
+        outs.append((dec.idx.clone(), out.clone(), sc))
     if torch.equal(outs[0][0], outs[1][0]):
+        # same selection: the same attention launch over the same rows, bit for bit
         assert torch.equal(outs[0][1], outs[1][1])
+    else:
+        # the two scorings differ in the last bits only: both selections lie in the tie band
+        # of the oracle's own scores
+        kp = oracle.block_pool
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                ref = oracle.scores_block(host(pred)[b, 0, h], kp(host(k[b, h]), w.block_size))
+                for idx_, _, _ in outs:
+                    assert osteps.topk_band_ok(idx_[b, 0, h].cpu().numpy(), ref, w.k, TOL)
 
 
 # ------------------------------------------------------------------------------------ attention paths
@@ -690,7 +726,7 @@ def test_attention_kernel_paths(d, qdt, kvdt):
             toks = sel[r, :cnt[r]]
             o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], host(kc[b, h])[toks],
                                             host(vc[b, h])[toks], scale)
-            check_rows(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="attention")
+            check_attn(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="attention")
             np.testing.assert_allclose(lse[b, 0, h * G:(h + 1) * G].cpu().numpy(), l_ref, rtol=TOL)
 
 
@@ -715,7 +751,7 @@ def test_long_block_list_with_forced_rows_uses_assembly():
             toks = oracle.selection_tokens(sel[b * Hkv + h], gran, N, 4, 100)
             o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], host(kc[b, h])[toks],
                                             host(vc[b, h])[toks], scale)
-            check_rows(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="assembled union")
+            check_attn(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="assembled union")
 
 
 @pytest.mark.parametrize("N", [3000 + 7, 70001])
@@ -752,7 +788,7 @@ def test_union_assembly_sixteen_sets_ragged_lists(N):
                     r = (b * T + t) * Hq + hq
                     toks = oracle.selection_tokens(sel[r, :cnt[r]], 1, N, 4, 64)
                     o_ref, l_ref, _ = oracle.attend(qh[b, t, hq:hq + 1], kh[toks], vh[toks], scale)
-                    check_rows(o_all[b, t, hq], o_ref[0], what=f"union set {r}")
+                    check_attn(o_all[b, t, hq], o_ref[0], what=f"union set {r}")
                     assert abs(l_all[b, t, hq] - l_ref[0]) <= TOL * abs(l_ref[0]) + 1e-6
 
 
@@ -784,7 +820,7 @@ def test_block_intervals_logits_follow_union_order():
             toks = oracle.selection_tokens(sel[b * Hkv + h], gran, N, 4, 256)
             o_ref, l_ref, lg_ref = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G],
                                                  host(kc[b, h])[toks], host(vc[b, h])[toks], scale)
-            check_rows(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="block attention")
+            check_attn(out[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="block attention")
             lg = logits[b, 0, h * G:(h + 1) * G, :len(toks)].cpu().numpy()
             check_rows(lg, lg_ref, what="logits in union order")
 
@@ -833,7 +869,7 @@ def test_per_seq_host_rows_with_logits_bit_identical():
             toks = sel[b, :c]
             o_ref, l_ref, lg_ref = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G],
                                                  host(kc[b, h])[toks], host(vc[b, h])[toks], scale)
-            check_rows(o_a[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="per-seq attention")
+            check_attn(o_a[b, 0, h * G:(h + 1) * G].cpu().numpy(), o_ref, what="per-seq attention")
             check_rows(lg_a[b, 0, h * G:(h + 1) * G, :c].cpu().numpy(), lg_ref, what="per-seq logits")
 
 
@@ -953,7 +989,7 @@ def test_block_windowed_small(N, window, stride, bs, k):
             toks = oracle.selection_tokens(blocks, bs, N, w.n_sink, w.n_recent)
             o_ref, l_ref, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], kh[toks], vh[toks],
                                             scale)
-            check_rows(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="attention")
+            check_attn(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="attention")
             np.testing.assert_allclose(lse.cpu().numpy()[b, 0, h * G:(h + 1) * G], l_ref, rtol=TOL)
     if window == stride == bs:
         # the block grid itself: the same scores as pooled blocks, up to rounding
@@ -992,7 +1028,7 @@ def test_block_windowed_full_size_sampled():
         assert osteps.topk_band_ok(blocks, r["scores"], w.k, TOL)
         toks = oracle.selection_tokens(blocks, w.block_size, w.N, w.n_sink, w.n_recent)
         o_ref, _, _ = oracle.attend(host(q)[b, 0, h * G:(h + 1) * G], kh[toks], vh[toks], scale)
-        check_rows(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="attention")
+        check_attn(out.cpu().numpy()[b, 0, h * G:(h + 1) * G], o_ref, what="attention")
 
 
 # ---------------------------------------------------------------- T1 in host memory, residency

@@ -495,3 +495,114 @@ def test_residency_update_invariants_and_idempotence():
     freed = {int(loc1[i]) for i in set(R) - R3}
     assert {sl for _, sl in c3} == set(sorted(freed)[: len(c3)])
     assert len({int(loc3[i]) for i in R3}) == len(R3)
+
+
+# ------------------------------------------------------------------ the parity checkers
+
+def test_rel_err_hand_values():
+    """Normwise relative error max|x - ref| / max|ref| on hand arrays."""
+    # exact agreement, empty rows
+    assert steps.rel_err([1.0, -2.0], [1.0, -2.0]) == 0.0
+    assert steps.rel_err(np.zeros(0), np.zeros(0)) == 0.0
+    # a sign flip of the largest element: |3 - (-3)| / 3 = 2 (a missing abs on the
+    # difference would give 0 here, one on the denominator 6)
+    assert steps.rel_err([1.0, -3.0], [1.0, 3.0]) == pytest.approx(2.0, rel=0, abs=0)
+    assert steps.rel_err([1.0, 3.0], [1.0, -3.0]) == pytest.approx(2.0, rel=0, abs=0)
+    # the denominator is the largest |ref|, not a sum or a mean: 0.5 / 4
+    assert steps.rel_err([1.0, -4.0, 2.5], [1.0, -4.0, 2.0]) == 0.125
+    # a single outlier in a small element counts with its absolute size
+    ref = np.array([100.0, 1.0, -1.0, 0.5])
+    x = ref.copy()
+    x[3] = 0.7
+    assert steps.rel_err(x, ref) == pytest.approx(0.2 / 100.0, rel=1e-15)
+    # an all-zero reference: the absolute error
+    assert steps.rel_err([0.0, 3e-3, -1e-3], [0.0, 0.0, 0.0]) == 3e-3
+    # NaN is never within a bar
+    assert not steps.rel_err([np.nan, 1.0], [1.0, 1.0]) <= 1.0
+    with pytest.raises(ValueError):
+        steps.rel_err([1.0, 2.0], [1.0])
+
+
+def test_elem_rel_err_hand_values():
+    """Elementwise relative error with an absolute floor of floor_frac·max|ref|."""
+    ref = np.array([100.0, 1.0, -1.0, 0.5])
+    x = ref.copy()
+    x[3] = 0.7
+    # 0.2 against max(0.5, 1) = 1: the small element is held to the floor, not to 100
+    assert steps.elem_rel_err(x, ref, floor_frac=1e-2) == pytest.approx(0.2, rel=1e-15)
+    # a 19 % error on an element at 2 % of the row's scale passes the normwise bar but not this
+    ref2 = np.array([1.0, 0.02, 0.5])
+    x2 = ref2 * np.array([1.0, 1.19, 1.0])
+    assert steps.rel_err(x2, ref2) <= 2e-3 * 2
+    assert steps.elem_rel_err(x2, ref2) == pytest.approx(0.19, rel=1e-12)
+    # below the floor an element's error counts against the floor
+    ref3 = np.array([10.0, 1e-6])
+    assert steps.elem_rel_err([10.0, 2e-6], ref3, floor_frac=1e-2) == pytest.approx(1e-6 / 0.1)
+    # signs: a flip of a large element is an error of 2
+    assert steps.elem_rel_err([-5.0, 1.0], [5.0, 1.0]) == 2.0
+    assert steps.elem_rel_err([1.0], [1.0]) == 0.0
+    assert steps.elem_rel_err(np.zeros(3), np.zeros(3)) == 0.0
+    assert steps.elem_rel_err([np.nan], [1.0]) == float("inf")
+
+
+def test_topk_band_ok_accepts_and_rejects():
+    x = np.array([5.0, 4.0, 3.0, 2.9995, 1.0, 0.0])     # max|x| = 5, band at tol 1e-3 = 0.005
+    assert steps.topk_band_ok([0, 1, 2], x, 3, 1e-3)
+    assert steps.topk_band_ok(np.array([2, 0, 1], np.int32), x, 3, 1e-3)   # order is free
+    # a swap inside the band around the k-th score (3.0 vs 2.9995) is accepted
+    assert steps.topk_band_ok([0, 1, 3], x, 3, 1e-3)
+    # and rejected when the band is narrower than the gap
+    assert not steps.topk_band_ok([0, 1, 3], x, 3, 1e-5)
+    # a swap outside the band: 1.0 chosen instead of 3.0
+    assert not steps.topk_band_ok([0, 1, 4], x, 3, 1e-3)
+    # a clearly-above element left out
+    assert not steps.topk_band_ok([1, 2, 3], x, 3, 1e-3)
+    # wrong count, duplicates, out-of-range and negative indices
+    assert not steps.topk_band_ok([0, 1], x, 3, 1e-3)
+    assert not steps.topk_band_ok([0, 1, 2, 3], x, 3, 1e-3)
+    assert not steps.topk_band_ok([0, 1, 1], x, 3, 1e-3)
+    assert not steps.topk_band_ok([0, 1, 1], x, 2, 1e-3)
+    assert not steps.topk_band_ok([0, 1, 6], x, 3, 1e-3)
+    assert not steps.topk_band_ok([0, 1, -1], x, 3, 1e-3)
+    # k = 0, k = n and k > n
+    assert steps.topk_band_ok([], x, 0, 1e-3)
+    assert not steps.topk_band_ok([0], x, 0, 1e-3)
+    assert steps.topk_band_ok(list(range(6)), x, 6, 1e-3)
+    assert steps.topk_band_ok(list(range(6)), x, 9, 1e-3)
+    assert not steps.topk_band_ok(list(range(5)), x, 9, 1e-3)
+    # the exact top-k always passes, on random rows with ties
+    for seed in range(20):
+        r = np.random.default_rng(seed)
+        y = r.integers(-3, 4, size=50).astype(np.float64)
+        for k in (0, 1, 7, 25, 50):
+            assert steps.topk_band_ok(oracle.topk(y, k), y, k, 0.0)
+
+
+def _bf16_round(x):
+    return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("rows", [512, 2532, 9700])
+def test_attention_regression_bound_from_the_arithmetic(rows):
+    """The regression bound of the attention outputs separates the two ways of feeding the
+    probabilities P to a bf16 P·V product, on bf16 N(0,1) keys and values, d = 128, four
+    query vectors, at the selection sizes of the block (2532), per-head (9700) workloads:
+    P split into an exact bf16 high part and a bf16-rounded remainder (~16 bits kept) stays far
+    below it, while P rounded to bf16 alone (a mistake planted here, in the oracle's own
+    arithmetic) lands far above it, around the 2e-3 bar (1.5e-3 to 2.9e-3 on these shapes), so
+    that bar alone does not reliably catch it."""
+    r = np.random.default_rng(rows)
+    d = 128
+    k = _bf16_round(r.standard_normal((rows, d)))
+    v = _bf16_round(r.standard_normal((rows, d)))
+    q = _bf16_round(r.standard_normal((4, d)))
+    out, lse, logits = oracle.attend(q, k, v, oracle.softmax_scale(d))
+    p = np.exp(logits - lse[:, None])
+    hi = _bf16_round(p)
+    split = (hi + _bf16_round(p - hi)) @ v
+    trap = hi @ v
+    e_split = max(steps.rel_err(a, b) for a, b in zip(split, out))
+    e_trap = max(steps.rel_err(a, b) for a, b in zip(trap, out))
+    assert e_split < steps.ATTN_REGRESSION_BOUND / 10
+    assert steps.ATTN_REGRESSION_BOUND * 10 < e_trap
+    assert steps.TOL / 2 < e_trap < steps.TOL * 2
