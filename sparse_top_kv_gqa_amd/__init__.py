@@ -121,6 +121,101 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# ----------------------------------------------------------------------------- validation
+#
+# The C ABI receives bare pointers and cannot see extents, so every wrapper checks here, before
+# any library call, that each tensor has the dtype, device, shape and row layout the kernels
+# will index: a mis-shaped tensor raises ValueError and nothing is launched.
+
+def _is_dev(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
+def _is_pinned(t: torch.Tensor) -> bool:
+    return (not t.is_cuda) and t.is_pinned()
+
+
+def _need_dev(t, name: str, dtypes=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if not _is_dev(t):
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)} (got {t.dtype})")
+    return t
+
+
+def _need_shape(t: torch.Tensor, name: str, shape):
+    """`shape`: one entry per dim; an int must match exactly, ('>=', m) is a lower bound,
+    None matches anything."""
+    if t.dim() != len(shape):
+        raise ValueError(f"{name} must have {len(shape)} dims (got shape {tuple(t.shape)})")
+    for i, want in enumerate(shape):
+        got = t.shape[i]
+        if want is None:
+            continue
+        if isinstance(want, tuple):
+            if got < want[1]:
+                raise ValueError(f"{name} dim {i} is {got}, needs >= {want[1]} "
+                                 f"(shape {tuple(t.shape)})")
+        elif got != want:
+            raise ValueError(f"{name} dim {i} is {got}, needs {want} (shape {tuple(t.shape)})")
+    return t
+
+
+def _row_ld(t: torch.Tensor, name: str, rows: int, min_len: int) -> int:
+    """Checks that `t` is `rows` rows of at least `min_len` contiguous elements, row r starting
+    at r·ld (the layout of a [rows, ld] matrix, possibly a column slice of a wider one), and
+    returns ld."""
+    if t.dim() < 1 or (t.numel() and t.stride(-1) != 1 and t.shape[-1] > 1):
+        raise ValueError(f"{name} must have a contiguous last dim")
+    lead = t.shape[:-1]
+    nrows = int(math.prod(lead)) if len(lead) else 1
+    if nrows != rows:
+        raise ValueError(f"{name} holds {nrows} rows (shape {tuple(t.shape)}), needs {rows}")
+    if t.shape[-1] < min_len:
+        raise ValueError(f"{name} rows hold {t.shape[-1]} elements, need >= {min_len}")
+    if t.numel() == 0:
+        return t.shape[-1]          # empty rows (or none): no element is ever addressed
+    ld = t.stride(-2) if t.dim() >= 2 else t.shape[-1]
+    expect = ld
+    for i in range(t.dim() - 2, -1, -1):
+        if t.shape[i] != 1 and t.stride(i) != expect:
+            raise ValueError(f"{name}: rows are not evenly spaced (strides {t.stride()})")
+        expect *= t.shape[i]
+    if rows > 1 and ld < t.shape[-1]:
+        raise ValueError(f"{name}: rows overlap (row stride {ld} < {t.shape[-1]})")
+    return max(ld, t.shape[-1]) if rows <= 1 else ld
+
+
+def _need_contig_n(t, name: str, n: int, dtypes):
+    """A contiguous device tensor of exactly n elements."""
+    _need_dev(t, name, dtypes)
+    if t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous with {n} elements (shape {tuple(t.shape)})")
+    return t
+
+
+def _need_cache(t, name: str, B: int, H: int, n_min: int, d: int, dtypes=(torch.float32, torch.bfloat16),
+                device=True):
+    """A [>=B, H, >=n_min, d] cache view with a contiguous last dim (device or pinned host)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if device:
+        _need_dev(t, name, dtypes)
+    else:
+        if not _is_pinned(t):
+            raise ValueError(f"{name} must be pinned host memory")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{name} has dtype {t.dtype}")
+    _need_shape(t, name, [(">=", B), H, (">=", n_min), d])
+    _rows_view(t, name)
+    return t
+
+
+F32S, KVS, I32S, U8S = (torch.float32,), (torch.float32, torch.bfloat16), (torch.int32,), (torch.uint8,)
+
+
 def _dt(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return F32
@@ -157,19 +252,40 @@ def sparse_index_score(mode, q: torch.Tensor, keys: torch.Tensor, n_tokens: int,
     (block modes); keys: [B,Hkv,*,d] cache view (or pooled keys).  Returns fp32
     [B,T,Hs,n_cand] (Hs = Hq for per-head, else Hkv)."""
     m = MODES[mode] if isinstance(mode, str) else int(mode)
+    _need_dev(q, "q", KVS)
     _contig(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d]")
     B, T, Hx, d = q.shape
+    if keys.dim() != 4:
+        raise ValueError("keys must be a [B, Hkv, N, d] view")
     Hkv = keys.shape[1]
     block = m in (IDX_BLOCK_POOLED, IDX_BLOCK_RAW)
     if Hq is None:
         Hq = Hkv if block else Hx
+    if block_size < 1 or n_tokens < 0:
+        raise ValueError("block_size must be >= 1 and n_tokens >= 0")
+    if Hx != (Hkv if block else Hq):
+        raise ValueError(f"q has {Hx} heads, needs {Hkv if block else Hq}")
     n_cand = n_tokens // block_size if block else n_tokens
+    key_rows = n_cand if m == IDX_BLOCK_POOLED else n_tokens
+    _need_cache(keys, "keys", B, Hkv, key_rows, d)
     Hs = Hq if m == IDX_TOKEN_PER_HEAD else Hkv
     if scores is None:
         scores = torch.empty((B, T, Hs, n_cand), dtype=torch.float32, device=q.device)
+    _need_dev(scores, "scores", F32S)
+    s_ld = _row_ld(scores, "scores", B * T * Hs, n_cand)
+    if pooled_out is not None:
+        if m != IDX_BLOCK_RAW:
+            raise ValueError("pooled_out is written by the block_raw mode only")
+        _need_dev(pooled_out, "pooled_out", F32S)
+        _contig(pooled_out, "pooled_out")
+        _need_shape(pooled_out, "pooled_out", [B, Hkv, (">=", n_cand), d])
+        if pooled_out.shape[2] != n_cand:
+            raise ValueError(f"pooled_out must be [B, Hkv, {n_cand}, d]")
     sb, sh, sn = _rows_view(keys, "keys")
     st = lib().sparse_index_score(m, _ptr(q), _dt(q), _ptr(keys), _dt(keys), sb, sh, sn, B, T, Hq,
-                                  Hkv, d, n_tokens, block_size, _ptr(scores), scores.stride(-2),
+                                  Hkv, d, n_tokens, block_size, _ptr(scores), s_ld,
                                   _ptr(pooled_out), _stream(stream))
     _check(st, "sparse_index_score")
     return scores
@@ -185,11 +301,18 @@ def sparse_window_pool(keys: torch.Tensor, n_tokens: int, window: int, stride: i
     """Mean of the keys of every complete overlapping compression window.  keys: [B,Hkv,*,d]
     cache view; returns fp32 [B,Hkv,w_cap,d] (w_cap >= the window count; rows past it are not
     written)."""
+    if keys.dim() != 4:
+        raise ValueError("keys must be a [B, Hkv, N, d] view")
     B, Hkv, _, d = keys.shape
+    _need_cache(keys, "keys", B, Hkv, n_tokens, d)
+    if window < 1 or stride < 1 or n_tokens < 0:
+        raise ValueError("window and stride must be >= 1, n_tokens >= 0")
     nw = window_count(n_tokens, window, stride)
     if out is None:
         out = torch.empty((B, Hkv, max(nw, 1), d), dtype=torch.float32, device=keys.device)
+    _need_dev(out, "out", F32S)
     _contig(out, "out")
+    _need_shape(out, "out", [B, Hkv, (">=", nw), d])
     sb, sh, sn = _rows_view(keys, "keys")
     st = lib().sparse_window_pool(_ptr(keys), _dt(keys), sb, sh, sn, B, Hkv, d, n_tokens, window,
                                   stride, _ptr(out), out.shape[2], _stream(stream))
@@ -203,15 +326,24 @@ def sparse_index_score_windowed(pred: torch.Tensor, kwin: torch.Tensor, n_tokens
     """Block scores from overlapping compression windows: the predictor [B,T,Hkv,d] scores
     every window of kwin [B,Hkv,w_cap,d] (fp32) and each block takes the largest score of the
     windows it overlaps.  Returns fp32 [B,T,Hkv,n_tokens // block_size]."""
+    _need_dev(pred, "pred", KVS)
     _contig(pred, "pred")
+    if pred.dim() != 4:
+        raise ValueError("pred must be [B, T, Hkv, d]")
+    _need_dev(kwin, "kwin", F32S)
     _contig(kwin, "kwin")
     B, T, Hkv, d = pred.shape
+    if window < 1 or stride < 1 or block_size < 1 or n_tokens < 0:
+        raise ValueError("window, stride and block_size must be >= 1, n_tokens >= 0")
+    _need_shape(kwin, "kwin", [B, Hkv, (">=", window_count(n_tokens, window, stride)), d])
     nb = n_tokens // block_size
     if scores is None:
         scores = torch.empty((B, T, Hkv, max(nb, 1)), dtype=torch.float32, device=pred.device)
+    _need_dev(scores, "scores", F32S)
+    s_ld = _row_ld(scores, "scores", B * T * Hkv, nb)
     st = lib().sparse_index_score_windowed(_ptr(pred), _dt(pred), _ptr(kwin), kwin.shape[2], B, T,
                                            Hkv, d, n_tokens, window, stride, block_size,
-                                           _ptr(scores), scores.stride(-2), _stream(stream))
+                                           _ptr(scores), s_ld, _stream(stream))
     _check(st, "sparse_index_score_windowed")
     return scores
 
@@ -235,13 +367,21 @@ def sparse_index_topk(mode, q: torch.Tensor, keys: torch.Tensor, n_tokens: int, 
     """Indexer scores and their top-k in one launch (short candidate rows).  Returns
     (idx int32 [B,T,Hs,min(k,n_cand)] ascending, count int32 [B,T,Hs], scores or None)."""
     m = MODES[mode] if isinstance(mode, str) else int(mode)
+    _need_dev(q, "q", KVS)
     _contig(q, "q")
+    if q.dim() != 4 or keys.dim() != 4:
+        raise ValueError("q must be [B, T, H, d] and keys a [B, Hkv, N, d] view")
     B, T, Hx, d = q.shape
     Hkv = keys.shape[1]
     block = m in (IDX_BLOCK_POOLED, IDX_BLOCK_RAW)
     if Hq is None:
         Hq = Hkv if block else Hx
+    if block_size < 1 or n_tokens < 0:
+        raise ValueError("block_size must be >= 1 and n_tokens >= 0")
+    if Hx != (Hkv if block else Hq):
+        raise ValueError(f"q has {Hx} heads, needs {Hkv if block else Hq}")
     n_cand = n_tokens // block_size if block else n_tokens
+    _need_cache(keys, "keys", B, Hkv, n_cand if m == IDX_BLOCK_POOLED else n_tokens, d)
     Hs = Hq if m == IDX_TOKEN_PER_HEAD else Hkv
     kk = max(0, min(k, n_cand))
     if scores is None and want_scores:
@@ -250,11 +390,17 @@ def sparse_index_topk(mode, q: torch.Tensor, keys: torch.Tensor, n_tokens: int, 
         idx = torch.empty((B, T, Hs, max(kk, 1)), dtype=torch.int32, device=q.device)
     if count is None:
         count = torch.empty((B, T, Hs), dtype=torch.int32, device=q.device)
+    s_ld = 0
+    if scores is not None:
+        _need_dev(scores, "scores", F32S)
+        s_ld = _row_ld(scores, "scores", B * T * Hs, n_cand)
+    _need_dev(idx, "idx", I32S)
+    i_ld = _row_ld(idx, "idx", B * T * Hs, kk)
+    _need_contig_n(count, "count", B * T * Hs, I32S)
     sb, sh, sn = _rows_view(keys, "keys")
     st = lib().sparse_index_topk(m, _ptr(q), _dt(q), _ptr(keys), _dt(keys), sb, sh, sn, B, T, Hq,
-                                 Hkv, d, n_tokens, block_size, k, _ptr(scores),
-                                 scores.stride(-2) if scores is not None else 0, _ptr(idx),
-                                 idx.stride(-2), _ptr(count), _stream(stream))
+                                 Hkv, d, n_tokens, block_size, k, _ptr(scores), s_ld, _ptr(idx),
+                                 i_ld, _ptr(count), _stream(stream))
     _check(st, "sparse_index_topk")
     return idx, count, scores
 
@@ -273,22 +419,29 @@ def topk_select(scores: torch.Tensor, k: int, n: Optional[int] = None,
                 ws: Optional[torch.Tensor] = None, stream=None):
     """Exact top-k of each row of ``scores`` (any leading shape, last dim contiguous).
     Returns (idx int32 [..., min(k, n)] ascending, count int32 [...])."""
-    if scores.stride(-1) != 1:
-        raise ValueError("scores must have a contiguous last dim")
+    _need_dev(scores, "scores", F32S)
+    if scores.dim() < 1:
+        raise ValueError("scores must have at least one dim")
     lead = scores.shape[:-1]
     rows = int(math.prod(lead)) if len(lead) else 1
     n = scores.shape[-1] if n is None else n
+    if n < 0 or n > scores.shape[-1]:
+        raise ValueError(f"n = {n} outside [0, {scores.shape[-1]}]")
     kk = max(0, min(k, n))
-    s2 = scores.reshape(rows, scores.shape[-1]) if rows else scores.reshape(0, scores.shape[-1])
+    s_ld = _row_ld(scores, "scores", rows, n)
     if idx is None:
         idx = torch.empty((*lead, kk), dtype=torch.int32, device=scores.device)
     if count is None:
         count = torch.empty(lead, dtype=torch.int32, device=scores.device)
-    i2 = idx.reshape(rows, idx.shape[-1])
+    _need_dev(idx, "idx", I32S)
+    i_ld = _row_ld(idx, "idx", rows, kk)
+    _need_contig_n(count, "count", rows, I32S)
     wsz = topk_workspace_size(rows, n, k)
     if wsz and (ws is None or ws.numel() < wsz):
         ws = torch.empty(wsz, dtype=torch.uint8, device=scores.device)
-    st = lib().topk_select(_ptr(s2), s2.stride(0), rows, n, k, _ptr(i2), i2.stride(0), _ptr(count),
+    if wsz:
+        _need_dev(ws, "ws", U8S)
+    st = lib().topk_select(_ptr(scores), s_ld, rows, n, k, _ptr(idx), i_ld, _ptr(count),
                            _ptr(ws) if wsz else None, wsz, _stream(stream))
     _check(st, "topk_select")
     return idx, count
@@ -325,43 +478,76 @@ def sparse_decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel_id
     Host pools k_host/v_host: pinned [B,Hkv,*,d] views, used where loc [B,Hkv,>=n_tokens] < 0.
     Returns (out fp32 [B,T,Hq,d], lse fp32 [B,T,Hq])."""
     sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
+    if sc not in (SEL_PER_SEQ, SEL_PER_KV_HEAD, SEL_PER_Q_HEAD):
+        raise ValueError(f"unknown scope {scope}")
+    _need_dev(q, "q", KVS)
     _contig(q, "q")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B, T, Hq, d] and k, v [B, Hkv, N, d] views")
     B, T, Hq, d = q.shape
     Hkv = k.shape[1]
-    sel_ld = sel_idx.shape[-1]
-    if sel_idx.stride(-1) != 1 or sel_idx.dim() < 1:
-        raise ValueError("sel_idx must have a contiguous last dim")
-    sel_rows = int(math.prod(sel_idx.shape[:-1])) if sel_idx.dim() > 1 else 1
-    sel2 = sel_idx.reshape(sel_rows, sel_ld)
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq = {Hq} is not a multiple of Hkv = {Hkv}")
+    if n_tokens < 0 or gran < 1 or n_sink < 0 or n_recent < 0:
+        raise ValueError("negative n_tokens, n_sink, n_recent or gran < 1")
+    _need_cache(k, "k", B, Hkv, 0 if loc is not None else n_tokens, d)
+    _need_cache(v, "v", B, Hkv, 0 if loc is not None else n_tokens, d, dtypes=(k.dtype,))
+    _need_dev(sel_idx, "sel_idx", I32S)
+    sel_rows = {SEL_PER_SEQ: B, SEL_PER_KV_HEAD: B * T * Hkv, SEL_PER_Q_HEAD: B * T * Hq}[sc]
+    if sel_idx.dim() < 1:
+        raise ValueError("sel_idx must have at least one dim")
+    sel_ld = _row_ld(sel_idx, "sel_idx", sel_rows, 0)
+    sel_ld = sel_idx.shape[-1] if sel_rows <= 1 else sel_ld
+    if sel_rows > 1 and sel_ld != sel_idx.shape[-1]:
+        raise ValueError("sel_idx rows must be contiguous (row stride = row length)")
+    _need_contig_n(sel_count, "sel_count", sel_rows, I32S)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     kb, kh, kn = _rows_view(k, "k")
     if _rows_view(v, "v") != (kb, kh, kn):
         raise ValueError("k and v must share strides")
     hb = hh = hn = host_slots = 0
+    if (k_host is None) != (v_host is None):
+        raise ValueError("give both host pools or neither")
     if k_host is not None:
+        if loc is None:
+            raise ValueError("host pools need loc")
+        _need_cache(k_host, "k_host", B, Hkv, 0, d, dtypes=(k.dtype,), device=False)
+        _need_cache(v_host, "v_host", B, Hkv, 0, d, dtypes=(k.dtype,), device=False)
         hb, hh, hn = _rows_view(k_host, "k_host")
-        if v_host is None or _rows_view(v_host, "v_host") != (hb, hh, hn):
+        if _rows_view(v_host, "v_host") != (hb, hh, hn):
             raise ValueError("k_host and v_host must share strides")
         host_slots = min(k_host.shape[2], v_host.shape[2])
     lb = lh = 0
     if loc is not None:
-        if loc.dtype != torch.int32 or loc.dim() != 3 or loc.stride(2) != 1:
+        if k_host is None:
+            raise ValueError("loc needs the host pools k_host, v_host")
+        _need_dev(loc, "loc", I32S)
+        if loc.dim() != 3 or loc.stride(2) != 1:
             raise ValueError("loc must be int32 [B, Hkv, N] with a contiguous last dim")
+        _need_shape(loc, "loc", [(">=", B), Hkv, (">=", n_tokens)])
         lb, lh = loc.stride(0), loc.stride(1)
     hbm_slots = min(k.shape[2], v.shape[2])
     if out is None:
         out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    _need_contig_n(out, "out", B * T * Hq * d, F32S)
+    _need_shape(out, "out", [B, T, Hq, d])
+    _need_contig_n(lse, "lse", B * T * Hq, F32S)
+    lg_ld = 0
+    if logits is not None:
+        _need_dev(logits, "logits", F32S)
+        lg_ld = _row_ld(logits, "logits", B * T * Hq,
+                        fetch_list_bound(sc, T, Hq // Hkv, sel_ld, gran, n_sink, n_recent, n_tokens))
     wsz = attn_workspace_size(sc, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent)
     if ws is None or ws.numel() < wsz:
         ws = torch.zeros(max(wsz, 1), dtype=torch.uint8, device=q.device)
-    lg_ld = logits.stride(-2) if logits is not None else 0
+    _need_dev(ws, "ws", U8S)
     st = lib().sparse_decode_attn(_ptr(q), _dt(q), _ptr(k), _ptr(v), _dt(k), kb, kh, kn,
                                   _ptr(k_host), _ptr(v_host), hb, hh, hn, host_slots, _ptr(loc),
                                   lb, lh, hbm_slots,
-                                  _ptr(sel2), _ptr(sel_count), sel_ld, sc, gran, n_sink, n_recent,
+                                  _ptr(sel_idx), _ptr(sel_count), sel_ld, sc, gran, n_sink, n_recent,
                                   B, T, Hq, Hkv, d, n_tokens, float(sm_scale), _ptr(out),
                                   _ptr(lse), _ptr(logits), lg_ld, _ptr(ws), ws.numel(),
                                   _stream(stream))
@@ -375,12 +561,28 @@ def importance_accumulate(s: torch.Tensor, sel_idx: torch.Tensor, sel_count: tor
                           logits: torch.Tensor, lse: torch.Tensor, n_tokens: int, stream=None):
     """s [B, s_ld] fp32 updated in place; sel_idx [B, sel_ld]; logits [L, B, Hq, logits_ld]
     (or [L, B, 1, Hq, logits_ld]); lse [L, B, Hq] (or [L, B, 1, Hq])."""
+    _need_dev(s, "s", F32S)
+    if s.dim() != 2 or n_tokens < 0:
+        raise ValueError("s must be [B, >= n_tokens] and n_tokens >= 0")
     B = s.shape[0]
+    s_ld = _row_ld(s, "s", B, n_tokens)
+    _need_dev(sel_idx, "sel_idx", I32S)
+    _contig(sel_idx, "sel_idx")
+    _need_shape(sel_idx, "sel_idx", [B, None])
+    sel_ld = sel_idx.shape[-1]
+    _need_contig_n(sel_count, "sel_count", B, I32S)
+    _need_dev(logits, "logits", F32S)
+    if logits.dim() not in (4, 5) or (logits.dim() == 5 and logits.shape[2] != 1):
+        raise ValueError("logits must be [L, B, Hq, ld] or [L, B, 1, Hq, ld]")
     L = logits.shape[0]
     Hq = logits.shape[-2]
-    st = lib().importance_accumulate(_ptr(s), s.stride(0), B, n_tokens, _ptr(sel_idx),
-                                     _ptr(sel_count), sel_idx.shape[-1], _ptr(logits),
-                                     logits.stride(-2), _ptr(lse), L, Hq, _stream(stream))
+    if logits.shape[1] != B:
+        raise ValueError(f"logits batch {logits.shape[1]} != {B}")
+    lg_ld = _row_ld(logits, "logits", L * B * Hq, sel_ld)
+    _need_contig_n(lse, "lse", L * B * Hq, F32S)
+    st = lib().importance_accumulate(_ptr(s), s_ld, B, n_tokens, _ptr(sel_idx),
+                                     _ptr(sel_count), sel_ld, _ptr(logits), lg_ld, _ptr(lse), L, Hq,
+                                     _stream(stream))
     _check(st, "importance_accumulate")
     return s
 
@@ -392,18 +594,30 @@ def tier_classify(s: torch.Tensor, n_tokens: int, n_sink: int, n_recent: int,
                   stream=None):
     """Tiers of each sequence's tokens.  s [B, s_ld] fp32.  Returns (tier uint8 [B, n_tokens],
     sel_idx int32 [B, n_tokens] (T0 ∪ T1 ascending), sel_count int32 [B])."""
+    _need_dev(s, "s", F32S)
+    if s.dim() != 2 or n_tokens < 0:
+        raise ValueError("s must be [B, >= n_tokens] and n_tokens >= 0")
     B = s.shape[0]
     dev = s.device
+    s_ld = _row_ld(s, "s", B, n_tokens)
     if tier is None:
         tier = torch.empty((B, n_tokens), dtype=torch.uint8, device=dev)
     if sel_idx is None:
         sel_idx = torch.empty((B, max(n_tokens, 1)), dtype=torch.int32, device=dev)
     if sel_count is None:
         sel_count = torch.empty((B,), dtype=torch.int32, device=dev)
-    st = lib().tier_classify(_ptr(s), s.stride(0), B, n_tokens, n_sink, n_recent, t0_permille,
-                             t01_permille, _ptr(evicted), evicted.stride(0) if evicted is not None else 0,
-                             _ptr(tier), tier.stride(0), _ptr(sel_idx), _ptr(sel_count),
-                             sel_idx.stride(0), None, 0, _stream(stream))
+    _need_dev(tier, "tier", U8S)
+    t_ld = _row_ld(tier, "tier", B, n_tokens)
+    ev_ld = 0
+    if evicted is not None:
+        _need_dev(evicted, "evicted", U8S)
+        ev_ld = _row_ld(evicted, "evicted", B, n_tokens)
+    _need_dev(sel_idx, "sel_idx", I32S)
+    sl = _row_ld(sel_idx, "sel_idx", B, n_tokens)
+    _need_contig_n(sel_count, "sel_count", B, I32S)
+    st = lib().tier_classify(_ptr(s), s_ld, B, n_tokens, n_sink, n_recent, t0_permille,
+                             t01_permille, _ptr(evicted), ev_ld, _ptr(tier), t_ld, _ptr(sel_idx),
+                             _ptr(sel_count), sl, None, 0, _stream(stream))
     _check(st, "tier_classify")
     return tier, sel_idx, sel_count
 
@@ -476,14 +690,23 @@ def sparse_topk_decode_attn(scores: torch.Tensor, k: int, q: torch.Tensor, kc: t
     """Top-k of each (b, kvh) score row and exact attention over the selection, one launch.
     scores [B, 1, Hkv, >=n_cand] fp32 (n_cand = scores.shape[-1]); q [B, 1, Hq, d] bf16.
     Returns (out fp32 [B,1,Hq,d], lse fp32 [B,1,Hq])."""
+    _need_dev(q, "q", KVS)
     _contig(q, "q")
+    if q.dim() != 4 or kc.dim() != 4 or vc.dim() != 4:
+        raise ValueError("q must be [B, 1, Hq, d] and k, v [B, Hkv, N, d] views")
     B, T, Hq, d = q.shape
     if T != 1:
         raise ValueError("one query token per sequence")
     Hkv = kc.shape[1]
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq = {Hq} is not a multiple of Hkv = {Hkv}")
+    if n_tokens < 0 or gran < 1 or n_sink < 0 or n_recent < 0:
+        raise ValueError("negative n_tokens, n_sink, n_recent or gran < 1")
+    _need_dev(scores, "scores", F32S)
     n_cand = scores.shape[-1]
-    if scores.stride(-1) != 1:
-        raise ValueError("scores must have a contiguous last dim")
+    s_ld = _row_ld(scores, "scores", B * Hkv, n_cand)
+    _need_cache(kc, "k", B, Hkv, n_tokens, d)
+    _need_cache(vc, "v", B, Hkv, n_tokens, d, dtypes=(kc.dtype,))
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     kb, kh, kn = _rows_view(kc, "k")
@@ -493,11 +716,20 @@ def sparse_topk_decode_attn(scores: torch.Tensor, k: int, q: torch.Tensor, kc: t
         out = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=q.device)
+    _need_contig_n(out, "out", B * Hq * d, F32S)
+    _need_contig_n(lse, "lse", B * Hq, F32S)
+    if (sel_idx is None) != (sel_count is None):
+        raise ValueError("give sel_idx and sel_count together")
+    sl = 0
+    if sel_idx is not None:
+        _need_dev(sel_idx, "sel_idx", I32S)
+        sl = _row_ld(sel_idx, "sel_idx", B * Hkv, max(0, min(k, n_cand)))
+        _need_contig_n(sel_count, "sel_count", B * Hkv, I32S)
     wsz = topk_attn_workspace_size(B, Hq, Hkv, d, n_tokens, n_cand, k, gran, n_sink, n_recent)
     if ws is None or ws.numel() < wsz:
         ws = torch.zeros(max(wsz, 1), dtype=torch.uint8, device=q.device)
-    sl = sel_idx.stride(-2) if sel_idx is not None else 0
-    st = lib().sparse_topk_decode_attn(_ptr(scores), scores.stride(-2), n_cand, k, _ptr(q), _dt(q),
+    _need_dev(ws, "ws", U8S)
+    st = lib().sparse_topk_decode_attn(_ptr(scores), s_ld, n_cand, k, _ptr(q), _dt(q),
                                        _ptr(kc), _ptr(vc), _dt(kc), kb, kh, kn, gran, n_sink,
                                        n_recent, B, Hq, Hkv, d, n_tokens, float(sm_scale),
                                        _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(sel_count), sl,
@@ -515,9 +747,20 @@ def residency_update(tier: torch.Tensor, s: torch.Tensor, n_tokens: int, capacit
     tier uint8 [B,*], s fp32 [B,*], loc int32 [B,*]; copy_tok/copy_slot int32 [B,copy_ld],
     copy_count int32 [B]."""
     B = tier.shape[0]
-    for t, nm in ((tier, "tier"), (s, "s"), (loc, "loc"), (copy_tok, "copy_tok"),
-                  (copy_slot, "copy_slot"), (copy_count, "copy_count")):
+    for t, nm, dts in ((tier, "tier", U8S), (s, "s", F32S), (loc, "loc", I32S),
+                       (copy_tok, "copy_tok", I32S), (copy_slot, "copy_slot", I32S),
+                       (copy_count, "copy_count", I32S)):
+        _need_dev(t, nm, dts)
         _contig(t, nm)
+    if n_tokens < 0 or capacity < 0:
+        raise ValueError("n_tokens and capacity must be >= 0")
+    for t, nm in ((tier, "tier"), (s, "s"), (loc, "loc")):
+        _need_shape(t, nm, [B, (">=", n_tokens)])
+    for t, nm in ((copy_tok, "copy_tok"), (copy_slot, "copy_slot")):
+        _need_shape(t, nm, [B, (">=", min(capacity, n_tokens))])
+    if copy_slot.shape != copy_tok.shape:
+        raise ValueError("copy_tok and copy_slot must have one shape")
+    _need_contig_n(copy_count, "copy_count", B, I32S)
     st = lib().residency_update(_ptr(tier), tier.shape[1], _ptr(s), s.shape[1], B, n_tokens,
                                 capacity, _ptr(loc), loc.shape[1], _ptr(copy_tok), _ptr(copy_slot),
                                 copy_tok.shape[1], _ptr(copy_count), _stream(stream))
@@ -529,11 +772,22 @@ def residency_prefetch(k_host: torch.Tensor, v_host: torch.Tensor, k_hbm: torch.
                        copy_count: torch.Tensor, max_copies: int, stream=None):
     """Copy the listed rows of the pinned host pools [B,Hkv,Nh,d] into their slots of the HBM
     pools [B,Hkv,C,d] (one layer, every KV head)."""
+    if k_hbm.dim() != 4:
+        raise ValueError("k_hbm must be a [B, Hkv, C, d] view")
+    B, Hkv, _, d = k_hbm.shape
+    _need_cache(k_hbm, "k_hbm", B, Hkv, 0, d)
+    _need_cache(v_hbm, "v_hbm", B, Hkv, 0, d, dtypes=(k_hbm.dtype,))
+    _need_cache(k_host, "k_host", B, Hkv, 0, d, dtypes=(k_hbm.dtype,), device=False)
+    _need_cache(v_host, "v_host", B, Hkv, 0, d, dtypes=(k_hbm.dtype,), device=False)
+    for t, nm in ((copy_tok, "copy_tok"), (copy_slot, "copy_slot")):
+        _need_dev(t, nm, I32S)
+        _contig(t, nm)
+        _need_shape(t, nm, [B, (">=", max_copies)])
+    _need_contig_n(copy_count, "copy_count", B, I32S)
     hsb, hsh, hsn = _rows_view(k_host, "k_host")
     dsb, dsh, dsn = _rows_view(k_hbm, "k_hbm")
     if _rows_view(v_host, "v_host") != (hsb, hsh, hsn) or _rows_view(v_hbm, "v_hbm") != (dsb, dsh, dsn):
         raise ValueError("k and v pools must share their strides")
-    B, Hkv, _, d = k_hbm.shape
     st = lib().residency_prefetch(_ptr(k_host), _ptr(v_host), hsb, hsh, hsn, k_host.shape[2],
                                   _ptr(k_hbm), _ptr(v_hbm), dsb, dsh, dsn, k_hbm.shape[2],
                                   _dt(k_hbm), B, Hkv, d, _ptr(copy_tok), _ptr(copy_slot),

@@ -1300,10 +1300,11 @@ def test_concurrent_streams_match_sequential_calls():
         assert torch.equal(tok.idx, idx_t)
 
 
-def test_host_pools_must_be_pinned():
-    """Host pools in pageable or device memory are refused before anything is launched, and no
-    HIP error is left behind: the same call with pinned pools then runs and reproduces the
-    all-HBM result bit for bit."""
+def test_host_pools_must_be_pinned(monkeypatch):
+    """Host pools in pageable or device memory are refused before anything is launched, by the
+    binding and, with the binding's check bypassed, by the library itself, and no HIP error is
+    left behind: the same call with pinned pools then runs and reproduces the all-HBM result
+    bit for bit."""
     say("host-pools-pinned")
     B, Hq, Hkv, d, N, k = 1, 4, 1, 128, 512, 96
     q = _rand((B, 1, Hq, d), torch.bfloat16, 61)
@@ -1320,8 +1321,13 @@ def test_host_pools_must_be_pinned():
     for kh, vh in [(torch.empty(shape, dtype=torch.bfloat16), torch.empty(shape, dtype=torch.bfloat16)),
                    (torch.empty(shape, dtype=torch.bfloat16, device=DEV),
                     torch.empty(shape, dtype=torch.bfloat16, device=DEV))]:
-        with pytest.raises(spk.SpkError) as err:
+        with pytest.raises(ValueError, match="pinned"):
             spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_seq", N, k_host=kh, v_host=vh, loc=loc)
+        with monkeypatch.context() as m:
+            m.setattr(spk, "_is_pinned", lambda t: True)
+            with pytest.raises(spk.SpkError) as err:
+                spk.sparse_decode_attn(q, kc, vc, selt, cntt, "per_seq", N, k_host=kh, v_host=vh,
+                                       loc=loc)
         assert err.value.status == 1 and ("pinned" in str(err.value) or "known to HIP" in str(err.value))
     kh = torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
     vh = torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
