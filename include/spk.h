@@ -316,6 +316,37 @@ SPK_API spk_status sparse_decode_attn(const void* q, spk_dtype q_dtype,
                                       void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * sparse_decode_attn_noalloc — sparse_decode_attn without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).
+ *
+ * Arguments, layouts, results and errors are those of sparse_decode_attn, minus ws / ws_bytes:
+ * the workspace is a fixed array in device memory owned by the library, one per GPU it runs on,
+ * of sparse_decode_attn_noalloc_max_bytes() bytes (32 MiB), held until the process ends.  The
+ * call allocates and frees nothing.  A call whose workspace (sparse_decode_attn_workspace_size)
+ * exceeds that size returns SPK_EWORKSPACE before any launch.  Every call on one GPU uses the
+ * same array and leaves its contents behind (nothing in it needs initial contents): calls that
+ * may overlap in time on one GPU (on concurrent streams) race and must not be issued.
+ * ---------------------------------------------------------------------------------------- */
+SPK_API size_t sparse_decode_attn_noalloc_max_bytes(void);
+
+SPK_API spk_status sparse_decode_attn_noalloc(const void* q, spk_dtype q_dtype,
+                                              const void* k, const void* v, spk_dtype kv_dtype,
+                                              int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                                              const void* k_host, const void* v_host,
+                                              int64_t host_sb, int64_t host_sh, int64_t host_sn,
+                                              int64_t host_slots,
+                                              const int32_t* loc, int64_t loc_sb, int64_t loc_sh,
+                                              int64_t hbm_slots,
+                                              const int32_t* sel_idx, const int32_t* sel_count,
+                                              int64_t sel_ld, spk_sel_scope scope, int gran,
+                                              int n_sink, int n_recent,
+                                              int B, int T, int Hq, int Hkv, int d, int n_tokens,
+                                              float sm_scale,
+                                              float* out, float* lse, float* logits,
+                                              int64_t logits_ld, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * sparse_topk_decode_attn — topk_select of one score row per (b, kvh) group followed by
  * sparse_decode_attn over the selected ids, in the attention's own launch.
  *

@@ -35,7 +35,8 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "spk_set_attn_timing_events", "sparse_index_topk",
            "sparse_topk_decode_attn_workspace_size", "sparse_topk_decode_attn",
            "sparse_window_pool", "sparse_index_score_windowed", "residency_update",
-           "residency_prefetch", "spk_stream_read", "spk_gather_read")
+           "residency_prefetch", "spk_stream_read", "spk_gather_read",
+           "sparse_decode_attn_noalloc", "sparse_decode_attn_noalloc_max_bytes")
 
 
 class SpkError(RuntimeError):
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
     L.sparse_decode_attn.argtypes = [P, I, P, P, I, I64, I64, I64, P, P, I64, I64, I64, I64, P, I64,
                                      I64, I64, P, P, I64, I, I, I, I, I, I, I, I, I, I, FL, P, P, P, I64, P,
                                      SZ, P]
+    L.sparse_decode_attn_noalloc.restype = I
+    L.sparse_decode_attn_noalloc.argtypes = L.sparse_decode_attn.argtypes[:-3] + [P]
+    L.sparse_decode_attn_noalloc_max_bytes.restype = SZ
+    L.sparse_decode_attn_noalloc_max_bytes.argtypes = []
     L.importance_accumulate.restype = I
     L.importance_accumulate.argtypes = [P, I64, I, I, P, P, I64, P, I64, P, I, I, P]
     L.tier_classify_workspace_size.restype = I
@@ -466,17 +471,11 @@ def fetch_list_bound(scope, T, G, sel_ld, gran, n_sink, n_recent, n_tokens) -> i
     return min(n_tokens, sets * sel_ld * gran + n_sink + n_recent)
 
 
-def sparse_decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel_idx: torch.Tensor,
-                       sel_count: torch.Tensor, scope, n_tokens: int, gran: int = 1,
-                       n_sink: int = 0, n_recent: int = 0, sm_scale: Optional[float] = None,
-                       k_host: Optional[torch.Tensor] = None, v_host: Optional[torch.Tensor] = None,
-                       loc: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                       lse: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-                       ws: Optional[torch.Tensor] = None, stream=None):
-    """Exact attention over the selected rows.  q [B,T,Hq,d]; k, v [B,Hkv,*,d] views;
-    sel_idx [rows, sel_ld] int32 (rows per `scope`), sel_count [rows] int32.
-    Host pools k_host/v_host: pinned [B,Hkv,*,d] views, used where loc [B,Hkv,>=n_tokens] < 0.
-    Returns (out fp32 [B,T,Hq,d], lse fp32 [B,T,Hq])."""
+def _attn_call_args(q, k, v, sel_idx, sel_count, scope, n_tokens, gran, n_sink, n_recent, sm_scale,
+                    k_host, v_host, loc, out, lse, logits):
+    """Validates the arguments of sparse_decode_attn (every tensor against the shapes the
+    kernels index) and returns (C arguments up to logits_ld, out, lse, sizes for the
+    workspace query)."""
     sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
     if sc not in (SEL_PER_SEQ, SEL_PER_KV_HEAD, SEL_PER_Q_HEAD):
         raise ValueError(f"unknown scope {scope}")
@@ -540,18 +539,61 @@ def sparse_decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel_id
         _need_dev(logits, "logits", F32S)
         lg_ld = _row_ld(logits, "logits", B * T * Hq,
                         fetch_list_bound(sc, T, Hq // Hkv, sel_ld, gran, n_sink, n_recent, n_tokens))
-    wsz = attn_workspace_size(sc, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent)
+    cargs = [_ptr(q), _dt(q), _ptr(k), _ptr(v), _dt(k), kb, kh, kn,
+             _ptr(k_host), _ptr(v_host), hb, hh, hn, host_slots, _ptr(loc), lb, lh, hbm_slots,
+             _ptr(sel_idx), _ptr(sel_count), sel_ld, sc, gran, n_sink, n_recent,
+             B, T, Hq, Hkv, d, n_tokens, float(sm_scale), _ptr(out), _ptr(lse), _ptr(logits), lg_ld]
+    return cargs, out, lse, (sc, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent)
+
+
+def sparse_decode_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel_idx: torch.Tensor,
+                       sel_count: torch.Tensor, scope, n_tokens: int, gran: int = 1,
+                       n_sink: int = 0, n_recent: int = 0, sm_scale: Optional[float] = None,
+                       k_host: Optional[torch.Tensor] = None, v_host: Optional[torch.Tensor] = None,
+                       loc: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None, stream=None):
+    """Exact attention over the selected rows.  q [B,T,Hq,d]; k, v [B,Hkv,*,d] views;
+    sel_idx [rows, sel_ld] int32 (rows per `scope`), sel_count [rows] int32.
+    Host pools k_host/v_host: pinned [B,Hkv,*,d] views, used where loc [B,Hkv,>=n_tokens] < 0.
+    Returns (out fp32 [B,T,Hq,d], lse fp32 [B,T,Hq])."""
+    cargs, out, lse, sizes = _attn_call_args(q, k, v, sel_idx, sel_count, scope, n_tokens, gran,
+                                             n_sink, n_recent, sm_scale, k_host, v_host, loc, out,
+                                             lse, logits)
+    wsz = attn_workspace_size(*sizes)
     if ws is None or ws.numel() < wsz:
         ws = torch.zeros(max(wsz, 1), dtype=torch.uint8, device=q.device)
     _need_dev(ws, "ws", U8S)
-    st = lib().sparse_decode_attn(_ptr(q), _dt(q), _ptr(k), _ptr(v), _dt(k), kb, kh, kn,
-                                  _ptr(k_host), _ptr(v_host), hb, hh, hn, host_slots, _ptr(loc),
-                                  lb, lh, hbm_slots,
-                                  _ptr(sel_idx), _ptr(sel_count), sel_ld, sc, gran, n_sink, n_recent,
-                                  B, T, Hq, Hkv, d, n_tokens, float(sm_scale), _ptr(out),
-                                  _ptr(lse), _ptr(logits), lg_ld, _ptr(ws), ws.numel(),
-                                  _stream(stream))
+    st = lib().sparse_decode_attn(*cargs, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "sparse_decode_attn")
+    return out, lse
+
+
+def noalloc_max_bytes() -> int:
+    """Size of the library's fixed scratch array (the workspace sparse_decode_attn_noalloc
+    uses on each GPU)."""
+    return int(lib().sparse_decode_attn_noalloc_max_bytes())
+
+
+def sparse_decode_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               sel_idx: torch.Tensor, sel_count: torch.Tensor, scope,
+                               n_tokens: int, out: torch.Tensor, lse: torch.Tensor, gran: int = 1,
+                               n_sink: int = 0, n_recent: int = 0,
+                               sm_scale: Optional[float] = None,
+                               k_host: Optional[torch.Tensor] = None,
+                               v_host: Optional[torch.Tensor] = None,
+                               loc: Optional[torch.Tensor] = None,
+                               logits: Optional[torch.Tensor] = None, stream=None):
+    """sparse_decode_attn with no workspace argument: the library's fixed scratch array serves
+    as the workspace and nothing is allocated (the caller passes out and lse).  Calls that
+    overlap in time on one GPU race."""
+    if out is None or lse is None:
+        raise ValueError("sparse_decode_attn_noalloc: pass out and lse (it allocates nothing)")
+    cargs, out, lse, _ = _attn_call_args(q, k, v, sel_idx, sel_count, scope, n_tokens, gran,
+                                         n_sink, n_recent, sm_scale, k_host, v_host, loc, out,
+                                         lse, logits)
+    st = lib().sparse_decode_attn_noalloc(*cargs, _stream(stream))
+    _check(st, "sparse_decode_attn_noalloc")
     return out, lse
 
 

@@ -1461,7 +1461,10 @@ extern "C" SPK_API spk_status sparse_decode_attn_workspace_size(
   return SPK_OK;
 }
 
-extern "C" SPK_API spk_status sparse_decode_attn(
+// The body of sparse_decode_attn and sparse_decode_attn_noalloc: `ws` is the caller's
+// workspace or the library's scratch array.  With validate_only, every argument check runs and
+// the call returns before the workspace check and any launch.
+static spk_status decode_attn_impl(bool validate_only,
     const void* q, spk_dtype q_dtype, const void* k, const void* v, spk_dtype kv_dtype,
     int64_t kv_sb, int64_t kv_sh, int64_t kv_sn, const void* k_host, const void* v_host,
     int64_t host_sb, int64_t host_sh, int64_t host_sn, int64_t host_slots, const int32_t* loc,
@@ -1512,6 +1515,10 @@ extern "C" SPK_API spk_status sparse_decode_attn(
   SPK_REQUIRE(!logits || logits_ld >= p.ubound, SPK_EINVAL,
               "sparse_decode_attn: logits_ld %lld < fetch-list bound %d", (long long)logits_ld,
               p.ubound);
+  if (validate_only) {
+    clear_error();
+    return SPK_OK;
+  }
   SPK_REQUIRE(ws_bytes >= p.bytes && (p.bytes == 0 || ws), SPK_EWORKSPACE,
               "sparse_decode_attn: workspace %zu bytes < %zu needed", ws_bytes, p.bytes);
   clear_error();
@@ -1647,6 +1654,104 @@ extern "C" SPK_API spk_status sparse_decode_attn(
     hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(p.groups * a.nq), dim3(kWave), 0, st, a,
                        p.nq_pad, out, lse);
   return check_launch("sparse_decode_attn/combine");
+}
+
+extern "C" SPK_API spk_status sparse_decode_attn(
+    const void* q, spk_dtype q_dtype, const void* k, const void* v, spk_dtype kv_dtype,
+    int64_t kv_sb, int64_t kv_sh, int64_t kv_sn, const void* k_host, const void* v_host,
+    int64_t host_sb, int64_t host_sh, int64_t host_sn, int64_t host_slots, const int32_t* loc,
+    int64_t loc_sb, int64_t loc_sh, int64_t hbm_slots, const int32_t* sel_idx, const int32_t* sel_count, int64_t sel_ld,
+    spk_sel_scope scope, int gran, int n_sink, int n_recent, int B, int T, int Hq, int Hkv, int d,
+    int n_tokens, float sm_scale, float* out, float* lse, float* logits, int64_t logits_ld,
+    void* ws, size_t ws_bytes, void* stream) {
+  return decode_attn_impl(false, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host, v_host,
+                          host_sb, host_sh, host_sn, host_slots, loc, loc_sb, loc_sh, hbm_slots,
+                          sel_idx, sel_count, sel_ld, scope, gran, n_sink, n_recent, B, T, Hq,
+                          Hkv, d, n_tokens, sm_scale, out, lse, logits, logits_ld, ws, ws_bytes,
+                          stream);
+}
+
+// ------------------------------------------------------------------- allocation-free variant
+//
+// For callers that cannot allocate (code under HIP graph capture, tight serving loops): the
+// attention's workspace is a fixed array in device memory that the library owns.  Each GPU the
+// library runs on holds its own copy (kScratchBytes, until the process ends).  The workspace
+// needs no initial contents (every call writes what it reads), so nothing is cleared between
+// calls; calls on one GPU share the array, so calls that overlap in time on one GPU (concurrent
+// streams) race and must not be issued.
+namespace spk {
+namespace {
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kScratchDevices = 64;
+}  // namespace
+}  // namespace spk
+
+__device__ __align__(256) unsigned char scratch[spk::kScratchBytes];
+
+namespace spk {
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The device address of this GPU's scratch array: resolved once per device, with that device
+// current.  The host-side symbol `scratch` is not a device address and is never used directly.
+spk_status scratch_for_current_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(SPK_EHIP, "sparse_decode_attn_noalloc: hipGetDevice failed");
+  }
+  if (dev < 0 || dev >= kScratchDevices)
+    return set_error(SPK_EUNSUPPORTED, "sparse_decode_attn_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return set_error(SPK_EHIP, "sparse_decode_attn_noalloc: hipGetSymbolAddress failed (%s)",
+                       hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SPK_OK;
+}
+}  // namespace
+}  // namespace spk
+
+extern "C" SPK_API size_t sparse_decode_attn_noalloc_max_bytes(void) { return spk::kScratchBytes; }
+
+extern "C" SPK_API spk_status sparse_decode_attn_noalloc(
+    const void* q, spk_dtype q_dtype, const void* k, const void* v, spk_dtype kv_dtype,
+    int64_t kv_sb, int64_t kv_sh, int64_t kv_sn, const void* k_host, const void* v_host,
+    int64_t host_sb, int64_t host_sh, int64_t host_sn, int64_t host_slots, const int32_t* loc,
+    int64_t loc_sb, int64_t loc_sh, int64_t hbm_slots, const int32_t* sel_idx, const int32_t* sel_count, int64_t sel_ld,
+    spk_sel_scope scope, int gran, int n_sink, int n_recent, int B, int T, int Hq, int Hkv, int d,
+    int n_tokens, float sm_scale, float* out, float* lse, float* logits, int64_t logits_ld,
+    void* stream) {
+  using namespace spk;
+  size_t need = 0;
+  spk_status st = sparse_decode_attn_workspace_size(scope, B, T, Hq, Hkv, d, n_tokens, sel_ld,
+                                                    gran, n_sink, n_recent, &need);
+  if (st != SPK_OK) return st;
+  SPK_REQUIRE(need <= kScratchBytes, SPK_EWORKSPACE,
+              "sparse_decode_attn_noalloc: this call needs %zu bytes of workspace, more than the "
+              "library's fixed %zu-byte scratch array; use sparse_decode_attn with a workspace",
+              need, kScratchBytes);
+  st = decode_attn_impl(true, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host, v_host,
+                        host_sb, host_sh, host_sn, host_slots, loc, loc_sb, loc_sh, hbm_slots,
+                        sel_idx, sel_count, sel_ld, scope, gran, n_sink, n_recent, B, T, Hq, Hkv,
+                        d, n_tokens, sm_scale, out, lse, logits, logits_ld, nullptr, 0, stream);
+  if (st != SPK_OK) return st;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != SPK_OK) return st;
+  return decode_attn_impl(false, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host, v_host,
+                          host_sb, host_sh, host_sn, host_slots, loc, loc_sb, loc_sh, hbm_slots,
+                          sel_idx, sel_count, sel_ld, scope, gran, n_sink, n_recent, B, T, Hq,
+                          Hkv, d, n_tokens, sm_scale, out, lse, logits, logits_ld, ws,
+                          kScratchBytes, stream);
 }
 
 extern "C" SPK_API spk_status sparse_topk_decode_attn_workspace_size(int B, int Hq, int Hkv,

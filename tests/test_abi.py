@@ -253,3 +253,30 @@ def test_residency_validation():
     st = L.residency_prefetch(hp, hp, 128, 128, 128, 8, Bp, Bp, 128, 128, 128, 8, 1, 1, 1, 128, A,
                               A, 8, A, 8, None)
     assert st in (1, 4) and "k_host" in _err()
+
+
+def _attn_noalloc(**kw):
+    args = dict(q=A, q_dt=1, k=A, v=A, kv_dt=1, kv_sb=8 * 1024 * 128, kv_sh=1024 * 128, kv_sn=128,
+                k_host=None, v_host=None, host_sb=0, host_sh=0, host_sn=0, host_slots=0, loc=None,
+                loc_sb=0, loc_sh=0, hbm_slots=1024, sel_idx=Bp, sel_count=Bp, sel_ld=32, scope=1,
+                gran=1, n_sink=0, n_recent=0, B=2, T=1, Hq=32, Hkv=8, d=128, n=1024, scale=0.1,
+                out=Bp, lse=None, logits=None, logits_ld=0, stream=None)
+    args.update(kw)
+    return spk.lib().sparse_decode_attn_noalloc(*args.values())
+
+
+def test_attn_noalloc_validation_and_size_limit():
+    """The allocation-free variant validates like sparse_decode_attn and refuses, before any
+    launch and with a clear error, a call whose workspace exceeds its fixed scratch array."""
+    cap = spk.lib().sparse_decode_attn_noalloc_max_bytes()
+    assert cap == 32 << 20
+    assert _attn_noalloc(Hq=30) == 1 and "Hq" in _err()
+    assert _attn_noalloc(q=None) == 1
+    assert _attn_noalloc(loc=Bp) == 1 and "host" in _err()
+    assert _attn_noalloc(d=80, kv_sn=80) == 2
+    # 256 sequences x 8 KV heads x 4 lists of 4096 ids over 1M tokens: far beyond 32 MiB
+    need = spk.attn_workspace_size("per_q_head", 256, 1, 32, 8, 128, 1 << 20, 4096)
+    assert need > cap
+    assert _attn_noalloc(B=256, scope=2, sel_ld=4096, n=1 << 20, hbm_slots=1 << 20,
+                         kv_sb=8 * (1 << 20) * 128, kv_sh=(1 << 20) * 128) == 3
+    assert "scratch" in _err() and str(need) in _err()
