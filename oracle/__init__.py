@@ -29,8 +29,8 @@ Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 closed forms, invariants, brute force on tiny inputs or an independent library
 routine, and so are the checkers every parity assertion goes through
 (``steps.rel_err``, ``steps.elem_rel_err``, ``steps.topk_band_ok``: hand values, sign
-flips, outliers, zero references, wrong counts, duplicates and out-of-range indices).  Nothing in this package is "parity unpinned" except the pages'
-published throughput figures, which it does not model.
+flips, outliers, zero references, wrong counts, duplicates and out-of-range indices).  Nothing in this package is "parity unpinned" except
+the pages' published throughput figures, which it does not model.
 """
 from .core import (  # noqa: F401
     decode_bf16,
