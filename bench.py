@@ -5,7 +5,13 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-
 A step is one pass of the whole hot path over one batch of synthetic input, with every input
 resident in HBM (or, for host-resident rows, in pinned host memory) before the timed region.
 
-Workloads (default: block):
+Default (--workload all): every workload below runs in this one process, one after the other.
+The headline — `value`, `ms_per_step`, `roofline`, `cpu_baseline` of the JSON line — is the
+largest single-GPU configuration, per_head (131072 tokens, 1.23 GB per step), timed over
+exactly --steps steps after --warmup untimed ones; every other workload is reported in the
+line's "workloads" object with its own step count, step GB/s, roofline and CPU baseline.
+
+Workloads:
   block        Llama-3-8B-shaped layer: batch 8, 32/8 heads, d 128, 32768 cached tokens, bf16.
                Predictor scores of mean-pooled 64-token blocks -> top-32 blocks -> attention over
                the blocks plus 4 sinks and the 512 most recent tokens.  Steps rotate through 8
@@ -53,8 +59,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="block",
-                    choices=["block", "block_windowed", "per_head", "spec_verify", "tiers",
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "block", "block_windowed", "per_head", "spec_verify", "tiers",
                              "tiers_offload"])
     ap.add_argument("--hbm-rows", type=int, default=8192,
                     help="tiers_offload: HBM slots per sequence (the rest stays in host memory)")
@@ -80,6 +86,17 @@ def host(t):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _cores():
@@ -914,6 +931,50 @@ def cpu_tiers(ctx, seconds):
                       f"{w.layers} layers ({spent:.1f} s), scaled to the whole batch"}
 
 
+HEADLINE = "per_head"
+ORDER = ["per_head", "block", "block_windowed", "spec_verify", "tiers", "tiers_offload"]
+
+
+def run_workload(name, args):
+    """Runs one workload: its timed steps, the read ceiling at its roofline kernel's size and
+    (unless switched off) the oracle on the host cores.  Returns the result record."""
+    if name in ("block", "block_windowed"):
+        res, ctx = bench_block(args, windowed=name == "block_windowed")
+        cpu = cpu_block
+    elif name in ("per_head", "spec_verify"):
+        res, ctx = bench_token(args, name)
+        cpu = cpu_token
+    elif name == "tiers_offload":
+        res, ctx = bench_tiers_offload(args)
+        cpu = cpu_tiers
+    else:
+        res, ctx = bench_tiers(args)
+        cpu = cpu_tiers
+    log(f"{name}: measuring the HBM read ceiling at the roofline kernel's size")
+    res["roofline"] = with_ceiling(res["roofline"], torch.cuda.Stream())
+    if not args.no_cpu_baseline:
+        log(f"{name}: timing the CPU oracle")
+        cb = cpu(ctx, args.cpu_seconds)
+        cb["cpu_model"] = _cpu_model()
+        res["cpu_baseline"] = cb
+    del ctx
+    return res
+
+
+def _free():
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def sub_record(res):
+    """The per-workload object of the combined line."""
+    keep = ("value", "unit", "ms_per_step", "steps_per_s", "pct_of_hbm_peak", "steps", "warmup",
+            "config", "roofline", "cpu_baseline")
+    return {k: res[k] for k in keep if k in res}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -925,28 +986,31 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    import copy
     import sparse_top_kv_gqa_amd as spk
     spk.lib()
     if args.calibrate_copy_mib > 0:
         copy_calibration(args.calibrate_copy_mib)
-    if args.workload in ("block", "block_windowed"):
-        res, ctx = bench_block(args, windowed=args.workload == "block_windowed")
-        cpu = cpu_block
-    elif args.workload in ("per_head", "spec_verify"):
-        res, ctx = bench_token(args, args.workload)
-        cpu = cpu_token
-    elif args.workload == "tiers_offload":
-        res, ctx = bench_tiers_offload(args)
-        cpu = cpu_tiers
-    else:
-        res, ctx = bench_tiers(args)
-        cpu = cpu_tiers
-    log("measuring the HBM read ceiling at the roofline kernel's size")
-    res["roofline"] = with_ceiling(res["roofline"], torch.cuda.Stream())
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle")
-        res["cpu_baseline"] = cpu(ctx, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    if args.workload != "all":
+        res = run_workload(args.workload, args)
+        print(json.dumps(res), flush=True)
+        return
+    t_all = time.perf_counter()
+    head = run_workload(HEADLINE, args)
+    _free()
+    subs = {}
+    for name in ORDER:
+        if name == HEADLINE:
+            continue
+        sub_args = copy.copy(args)
+        sub_args.steps = None          # each workload's own step count
+        sub_args.warmup = None
+        log(f"workload {name}")
+        subs[name] = sub_record(run_workload(name, sub_args))
+        _free()
+    head["workloads"] = subs
+    head["config"]["all_workloads_wall_s"] = round(time.perf_counter() - t_all, 1)
+    print(json.dumps(head), flush=True)
 
 
 if __name__ == "__main__":
