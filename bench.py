@@ -638,23 +638,20 @@ def bench_token(args, which):
     sel_bytes = [u * ROW_BYTES for u in union]
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
-    ms_total, wall = timed_loop(lambda i: dec.step(qs[i % P]), K, Wm, stream)
+    ms_total, wall = timed_loop(lambda i: dec.step(qs[i % P], stream=stream), K, Wm, stream)
     ms_step = ms_total / K
-    idx_ms = event_time_ms(lambda i: spk.sparse_index_score(mode, qs[i % P], dec.index_keys, w.N,
-                                                            scores=dec.scores, stream=stream),
-                           10, stream)
-    dec.select(qs[0])
+    idx_ms = event_time_ms(lambda i: dec.index(qs[i % P], stream=stream), 10, stream)
+    dec.select(qs[0], stream=stream)
     torch.cuda.synchronize()
-    att_ms = event_time_ms(lambda i: dec.attend(qs[0]), 10, stream)
-    gather_ms = gather_kernel_ms(lambda i: dec.attend(qs[0]), 10, stream)
-    topk_ms = event_time_ms(lambda i: spk.topk_select(dec.scores, dec.topk, idx=dec.idx,
-                                                      count=dec.count, ws=dec.topk_ws,
-                                                      stream=stream), 10, stream)
+    att_ms = event_time_ms(lambda i: dec.attend(qs[0], stream=stream), 10, stream)
+    gather_ms = gather_kernel_ms(lambda i: dec.attend(qs[0], stream=stream), 10, stream)
+    topk_ms = event_time_ms(lambda i: dec.select_topk(stream=stream), 10, stream)
     bytes_avg = index_bytes + sum(sel_bytes) / P
     cfg = {"workload": w.name, "batch": w.B, "query_tokens": w.T, "q_heads": w.Hq,
            "kv_heads": w.Hkv, "head_dim": w.d, "context": w.N, "topk": w.k,
            "bytes_per_step": int(bytes_avg), "index_bytes": index_bytes,
            "selected_rows_per_step": int(sum(union) / P), "wall_s_timed": round(wall, 4),
+           "union_pipeline": bool(dec.union),
            "index_ms": round(idx_ms, 4), "topk_ms": round(topk_ms, 4),
            "attention_ms": round(att_ms, 4), "attention_gather_kernel_ms": round(gather_ms, 4),
            "attention_selected_GBs": round(union[0] * ROW_BYTES / (gather_ms * 1e-3) / 1e9, 1)}
@@ -673,8 +670,8 @@ def bench_token(args, which):
                                    note="traffic counts every byte the kernel reads (HBM rows "
                                         "and host rows)")
     else:
-        res["roofline"] = roofline(f"index_rows_kernel (sparse_index_score {mode})", index_bytes,
-                                   idx_ms, traffic=measured_traffic(which))
+        kname = f"index_rows_kernel (sparse_index_score {mode})"
+        res["roofline"] = roofline(kname, index_bytes, idx_ms, traffic=measured_traffic(which))
     ctx = dict(w=w, k=k, v=v, q=qs[0], which=which)
     return res, ctx
 

@@ -8,6 +8,10 @@
  *   sparse_topk_decode_attn  top-k of a score row and the attention over it, in one launch
  *   sparse_decode_attn   gathers the chosen K/V rows once per GQA group (HBM or pinned host
  *                        memory) and runs exact softmax attention over them only
+ *   topk_select_union, sparse_decode_attn_union
+ *                        for wide rows with up to 4 selection sets per KV head: the per-set
+ *                        top-k and the group's union with set masks, and the attention over
+ *                        that union
  *   importance_accumulate  cumulative attention importance s_i += mean over layers, heads of α[i]
  *   tier_classify        T0/T1/T3 tiers by importance, sinks and recent window protected
  *
@@ -23,8 +27,9 @@
  *     at the caller's next synchronisation.
  *   - Ownership: the caller owns every buffer (inputs, outputs, workspace, host pools).  The
  *     library never allocates or frees memory and keeps no state between calls except a cached
- *     per-device property table; calls are re-entrant and may run on concurrent streams when
- *     their output buffers and workspaces are distinct.
+ *     per-device property table and the fixed scratch array of sparse_decode_attn_noalloc;
+ *     calls are re-entrant and may run on concurrent streams when their output buffers and
+ *     workspaces are distinct.
  *   - Errors: arguments are validated before any launch; on a non-OK return nothing was
  *     launched and nothing was written, and spk_last_error() (thread-local) says why.
  *       SPK_EINVAL       null required pointer, inconsistent shapes, bad strides or sizes
@@ -168,6 +173,39 @@ SPK_API spk_status topk_select_workspace_size(int rows, int n, int k, size_t* by
 SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int rows, int n, int k,
                                int32_t* idx, int64_t idx_ld, int32_t* count,
                                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * topk_select_union — the exact top-k of every score row of each (b, kvh) group's S <= 4
+ * selection sets, and the group's union of the S selections with a set mask per row.
+ *
+ * Passages: "Esparsidade de Contexto no Tempo de Inferência", §2 "Oracle Top-K" and
+ * "Implementação de Hardware" (each query head keeps its own top-k tokens); "O Fim do Gargalo
+ * de Memória ... Adaptive DHiSparse", "Metodologia e Eficiência de Carga" (queries verified
+ * together share the retrieval of their rows: the union is read once).
+ *
+ *   scores     device fp32 score rows, row stride s_ld >= n: PER_Q_HEAD: rows (b, t, query
+ *              head), S = T * G sets per group (set s = t*G + j is head kvh*G + j of token t);
+ *              PER_KV_HEAD: rows (b, t, kvh), S = T sets (set s = token t)
+ *   n, k       candidates per row (n <= 2^22) and how many to keep (k >= 0; k > n keeps all n)
+ *   idx        device int32 [rows][idx_ld], idx_ld >= min(k, n): each row's kept indices in
+ *              ascending order (ties to the lowest index), as topk_select
+ *   count      device int32 [rows]: min(k, n)
+ *   u_list     device int32 [B*Hkv][u_ld], u_ld >= min(n, S * min(k, n)): each group's union,
+ *              ascending; u_mask the same shape, uint32, bit s set when set s keeps the row;
+ *              u_count device int32 [B*Hkv], the union lengths
+ *   ws         device workspace of topk_select_union_workspace_size() bytes, no initial
+ *              contents needed
+ * Errors: SPK_EINVAL (scope not PER_Q_HEAD / PER_KV_HEAD, sizes, null buffers, short leading
+ * dims), SPK_EUNSUPPORTED (S > 4), SPK_EWORKSPACE.
+ * ---------------------------------------------------------------------------------------- */
+SPK_API spk_status topk_select_union_workspace_size(int B, int T, int Hq, int Hkv,
+                                                    spk_sel_scope scope, int n, int k,
+                                                    size_t* bytes);
+SPK_API spk_status topk_select_union(const float* scores, int64_t s_ld,
+                                     int B, int T, int Hq, int Hkv, spk_sel_scope scope,
+                                     int n, int k, int32_t* idx, int64_t idx_ld, int32_t* count,
+                                     int32_t* u_list, uint32_t* u_mask, int32_t* u_count,
+                                     int64_t u_ld, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * sparse_index_topk — sparse_index_score followed by topk_select, in one launch, for short
@@ -314,6 +352,41 @@ SPK_API spk_status sparse_decode_attn(const void* q, spk_dtype q_dtype,
                                       float sm_scale,
                                       float* out, float* lse, float* logits, int64_t logits_ld,
                                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * sparse_decode_attn_union — sparse_decode_attn over fetch lists the caller has assembled
+ * already (topk_select_union's union), so no assembly runs.
+ *
+ * Passages: as sparse_decode_attn.
+ *
+ *   u_list, u_mask, u_count, u_ld   each group's ascending fetch rows (token ids), the mask of
+ *              the selection sets holding each row (bit s: set s) and the row count; rows past
+ *              n_tokens or past u_ld are never read.  PER_Q_HEAD: query head kvh*G + j of
+ *              token t reads the rows with bit t*G + j; PER_KV_HEAD: every head of token t reads
+ *              the rows with bit t.
+ *   every other argument as sparse_decode_attn (host pools and loc included); logits rows are
+ *              indexed by the union position.
+ *   ws         device workspace of sparse_decode_attn_union_workspace_size() bytes.
+ * Errors: as sparse_decode_attn; SPK_EINVAL for another scope or u_ld <= 0.
+ * ---------------------------------------------------------------------------------------- */
+SPK_API spk_status sparse_decode_attn_union_workspace_size(spk_sel_scope scope, int B, int T,
+                                                           int Hq, int Hkv, int d, int n_tokens,
+                                                           int64_t u_ld, size_t* bytes);
+SPK_API spk_status sparse_decode_attn_union(const void* q, spk_dtype q_dtype,
+                                            const void* k, const void* v, spk_dtype kv_dtype,
+                                            int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                                            const void* k_host, const void* v_host,
+                                            int64_t host_sb, int64_t host_sh, int64_t host_sn,
+                                            int64_t host_slots,
+                                            const int32_t* loc, int64_t loc_sb, int64_t loc_sh,
+                                            int64_t hbm_slots,
+                                            const int32_t* u_list, const uint32_t* u_mask,
+                                            const int32_t* u_count, int64_t u_ld,
+                                            spk_sel_scope scope,
+                                            int B, int T, int Hq, int Hkv, int d, int n_tokens,
+                                            float sm_scale, float* out, float* lse,
+                                            float* logits, int64_t logits_ld,
+                                            void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * sparse_decode_attn_noalloc — sparse_decode_attn without a caller workspace, for callers that

@@ -36,7 +36,9 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "sparse_topk_decode_attn_workspace_size", "sparse_topk_decode_attn",
            "sparse_window_pool", "sparse_index_score_windowed", "residency_update",
            "residency_prefetch", "spk_stream_read", "spk_gather_read",
-           "sparse_decode_attn_noalloc", "sparse_decode_attn_noalloc_max_bytes")
+           "sparse_decode_attn_noalloc", "sparse_decode_attn_noalloc_max_bytes",
+           "topk_select_union_workspace_size", "topk_select_union",
+           "sparse_decode_attn_union_workspace_size", "sparse_decode_attn_union")
 
 
 class SpkError(RuntimeError):
@@ -83,6 +85,17 @@ def lib() -> ctypes.CDLL:
     L.sparse_decode_attn_noalloc.argtypes = L.sparse_decode_attn.argtypes[:-3] + [P]
     L.sparse_decode_attn_noalloc_max_bytes.restype = SZ
     L.sparse_decode_attn_noalloc_max_bytes.argtypes = []
+    L.topk_select_union_workspace_size.restype = I
+    L.topk_select_union_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(SZ)]
+    L.topk_select_union.restype = I
+    L.topk_select_union.argtypes = [P, I64, I, I, I, I, I, I, I, P, I64, P, P, P, P, I64, P, SZ, P]
+    L.sparse_decode_attn_union_workspace_size.restype = I
+    L.sparse_decode_attn_union_workspace_size.argtypes = [I, I, I, I, I, I, I, I64,
+                                                          ctypes.POINTER(SZ)]
+    L.sparse_decode_attn_union.restype = I
+    L.sparse_decode_attn_union.argtypes = [P, I, P, P, I, I64, I64, I64, P, P, I64, I64, I64, I64, P,
+                                           I64, I64, I64, P, P, P, I64, I, I, I, I, I, I, I, FL, P, P,
+                                           P, I64, P, SZ, P]
     L.importance_accumulate.restype = I
     L.importance_accumulate.argtypes = [P, I64, I, I, P, P, I64, P, I64, P, I, I, P]
     L.tier_classify_workspace_size.restype = I
@@ -452,6 +465,82 @@ def topk_select(scores: torch.Tensor, k: int, n: Optional[int] = None,
     return idx, count
 
 
+def union_sets(scope, T: int, Hq: int, Hkv: int) -> int:
+    """Selection sets per KV group: T * G per-head sets, or T per-token sets."""
+    sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
+    return T * (Hq // Hkv) if sc == SEL_PER_Q_HEAD else T
+
+
+def topk_union_workspace_size(B, T, Hq, Hkv, scope, n, k) -> int:
+    sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
+    out = SZ(0)
+    _check(lib().topk_select_union_workspace_size(B, T, Hq, Hkv, sc, n, k, ctypes.byref(out)),
+           "topk_select_union_workspace_size")
+    return out.value
+
+
+def topk_select_union(scores: torch.Tensor, k: int, scope, Hkv: int, n: Optional[int] = None,
+                      idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                      u_list: Optional[torch.Tensor] = None, u_mask: Optional[torch.Tensor] = None,
+                      u_count: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Per-set exact top-k of scores [B, T, Hs, n] (Hs = Hq for per_q_head, Hkv for
+    per_kv_head) and each KV group's union of its sets with a set mask per row.
+    Returns (idx int32 [B,T,Hs,min(k,n)], count int32 [B,T,Hs], u_list int32 [B*Hkv, u_ld],
+    u_mask int32 [B*Hkv, u_ld], u_count int32 [B*Hkv])."""
+    sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
+    if sc not in (SEL_PER_Q_HEAD, SEL_PER_KV_HEAD):
+        raise ValueError("topk_select_union: scope must be per_q_head or per_kv_head")
+    _need_dev(scores, "scores", F32S)
+    if scores.dim() != 4:
+        raise ValueError("scores must be [B, T, Hs, n]")
+    B, T, Hs, _ = scores.shape
+    n = scores.shape[-1] if n is None else n
+    if n < 0 or n > scores.shape[-1]:
+        raise ValueError(f"n = {n} outside [0, {scores.shape[-1]}]")
+    Hq = Hs if sc == SEL_PER_Q_HEAD else Hkv
+    if sc == SEL_PER_KV_HEAD and Hs != Hkv:
+        raise ValueError(f"per_kv_head scores need {Hkv} rows per token, got {Hs}")
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"{Hq} heads are not a multiple of Hkv = {Hkv}")
+    rows = B * T * Hs
+    s_ld = _row_ld(scores, "scores", rows, n)
+    kk = max(0, min(k, n))
+    S = union_sets(sc, T, Hq, Hkv)
+    u_ld = max(1, min(n, S * kk))
+    dev = scores.device
+    if idx is None:
+        idx = torch.empty((B, T, Hs, max(kk, 1)), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((B, T, Hs), dtype=torch.int32, device=dev)
+    if u_list is None:
+        u_list = torch.empty((B * Hkv, u_ld), dtype=torch.int32, device=dev)
+    if u_mask is None:
+        u_mask = torch.empty((B * Hkv, u_ld), dtype=torch.int32, device=dev)
+    if u_count is None:
+        u_count = torch.empty((B * Hkv,), dtype=torch.int32, device=dev)
+    _need_dev(idx, "idx", I32S)
+    i_ld = _row_ld(idx, "idx", rows, kk)
+    _need_contig_n(count, "count", rows, I32S)
+    for t, nm in ((u_list, "u_list"), (u_mask, "u_mask")):
+        _need_dev(t, nm, I32S)
+        _contig(t, nm)
+        _need_shape(t, nm, [B * Hkv, (">=", min(n, S * kk))])
+    if u_mask.shape != u_list.shape:
+        raise ValueError("u_list and u_mask must have one shape")
+    _need_contig_n(u_count, "u_count", B * Hkv, I32S)
+    wsz = topk_union_workspace_size(B, T, Hq, Hkv, sc, n, k)
+    if ws is None or ws.numel() < wsz:
+        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+    _need_dev(ws, "ws", U8S)
+    st = lib().topk_select_union(_ptr(scores), s_ld, B, T, Hq, Hkv, sc, n, k,
+                                 _ptr(idx), i_ld, _ptr(count), _ptr(u_list), _ptr(u_mask),
+                                 _ptr(u_count), u_list.shape[1], _ptr(ws), ws.numel(),
+                                 _stream(stream))
+    _check(st, "topk_select_union")
+    return idx, count, u_list, u_mask, u_count
+
+
 # ----------------------------------------------------------------------------- attention
 
 def attn_workspace_size(scope, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran=1, n_sink=0,
@@ -472,7 +561,7 @@ def fetch_list_bound(scope, T, G, sel_ld, gran, n_sink, n_recent, n_tokens) -> i
 
 
 def _attn_call_args(q, k, v, sel_idx, sel_count, scope, n_tokens, gran, n_sink, n_recent, sm_scale,
-                    k_host, v_host, loc, out, lse, logits):
+                    k_host, v_host, loc, out, lse, logits, u_mask=None):
     """Validates the arguments of sparse_decode_attn (every tensor against the shapes the
     kernels index) and returns (C arguments up to logits_ld, out, lse, sizes for the
     workspace query)."""
@@ -492,13 +581,21 @@ def _attn_call_args(q, k, v, sel_idx, sel_count, scope, n_tokens, gran, n_sink, 
     _need_cache(k, "k", B, Hkv, 0 if loc is not None else n_tokens, d)
     _need_cache(v, "v", B, Hkv, 0 if loc is not None else n_tokens, d, dtypes=(k.dtype,))
     _need_dev(sel_idx, "sel_idx", I32S)
-    sel_rows = {SEL_PER_SEQ: B, SEL_PER_KV_HEAD: B * T * Hkv, SEL_PER_Q_HEAD: B * T * Hq}[sc]
+    if u_mask is None:
+        sel_rows = {SEL_PER_SEQ: B, SEL_PER_KV_HEAD: B * T * Hkv, SEL_PER_Q_HEAD: B * T * Hq}[sc]
+    else:
+        sel_rows = B * Hkv                    # one assembled union per (b, kvh) group
+        _need_dev(u_mask, "u_mask", I32S)
+        if u_mask.shape != sel_idx.shape or not u_mask.is_contiguous():
+            raise ValueError("u_mask must be contiguous with the shape of u_list")
     if sel_idx.dim() < 1:
         raise ValueError("sel_idx must have at least one dim")
     sel_ld = _row_ld(sel_idx, "sel_idx", sel_rows, 0)
     sel_ld = sel_idx.shape[-1] if sel_rows <= 1 else sel_ld
     if sel_rows > 1 and sel_ld != sel_idx.shape[-1]:
         raise ValueError("sel_idx rows must be contiguous (row stride = row length)")
+    if u_mask is not None and sel_ld < 1:
+        raise ValueError("u_list rows must hold at least one entry")
     _need_contig_n(sel_count, "sel_count", sel_rows, I32S)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
@@ -537,8 +634,9 @@ def _attn_call_args(q, k, v, sel_idx, sel_count, scope, n_tokens, gran, n_sink, 
     lg_ld = 0
     if logits is not None:
         _need_dev(logits, "logits", F32S)
-        lg_ld = _row_ld(logits, "logits", B * T * Hq,
-                        fetch_list_bound(sc, T, Hq // Hkv, sel_ld, gran, n_sink, n_recent, n_tokens))
+        bound = (min(n_tokens, sel_ld) if u_mask is not None else
+                 fetch_list_bound(sc, T, Hq // Hkv, sel_ld, gran, n_sink, n_recent, n_tokens))
+        lg_ld = _row_ld(logits, "logits", B * T * Hq, bound)
     cargs = [_ptr(q), _dt(q), _ptr(k), _ptr(v), _dt(k), kb, kh, kn,
              _ptr(k_host), _ptr(v_host), hb, hh, hn, host_slots, _ptr(loc), lb, lh, hbm_slots,
              _ptr(sel_idx), _ptr(sel_count), sel_ld, sc, gran, n_sink, n_recent,
@@ -594,6 +692,46 @@ def sparse_decode_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                                          lse, logits)
     st = lib().sparse_decode_attn_noalloc(*cargs, _stream(stream))
     _check(st, "sparse_decode_attn_noalloc")
+    return out, lse
+
+
+def attn_union_workspace_size(scope, B, T, Hq, Hkv, d, n_tokens, u_ld) -> int:
+    sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
+    out = SZ(0)
+    _check(lib().sparse_decode_attn_union_workspace_size(sc, B, T, Hq, Hkv, d, n_tokens, u_ld,
+                                                         ctypes.byref(out)),
+           "sparse_decode_attn_union_workspace_size")
+    return out.value
+
+
+def sparse_decode_attn_union(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             u_list: torch.Tensor, u_mask: torch.Tensor, u_count: torch.Tensor,
+                             scope, n_tokens: int, sm_scale: Optional[float] = None,
+                             k_host: Optional[torch.Tensor] = None,
+                             v_host: Optional[torch.Tensor] = None,
+                             loc: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None,
+                             logits: Optional[torch.Tensor] = None,
+                             ws: Optional[torch.Tensor] = None, stream=None):
+    """Exact attention over fetch lists already assembled (topk_select_union's union):
+    u_list / u_mask int32 [B*Hkv, u_ld], u_count int32 [B*Hkv].  Other arguments as
+    sparse_decode_attn.  Returns (out fp32 [B,T,Hq,d], lse fp32 [B,T,Hq])."""
+    sc = SCOPES[scope] if isinstance(scope, str) else int(scope)
+    if sc not in (SEL_PER_Q_HEAD, SEL_PER_KV_HEAD):
+        raise ValueError("sparse_decode_attn_union: scope must be per_q_head or per_kv_head")
+    cargs, out, lse, sizes = _attn_call_args(q, k, v, u_list, u_count, sc, n_tokens, 1, 0, 0,
+                                             sm_scale, k_host, v_host, loc, out, lse, logits,
+                                             u_mask=u_mask)
+    sc_, B, T, Hq, Hkv, d, n, u_ld = sizes[:8]
+    wsz = attn_union_workspace_size(sc, B, T, Hq, Hkv, d, n, u_ld)
+    if ws is None or ws.numel() < wsz:
+        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=q.device)
+    _need_dev(ws, "ws", U8S)
+    # C argument order of the union call: the selection arguments are (list, mask, count, ld)
+    head, tail = cargs[:18], cargs[25:]
+    st = lib().sparse_decode_attn_union(*head, _ptr(u_list), _ptr(u_mask), _ptr(u_count), u_ld, sc,
+                                        *tail, _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "sparse_decode_attn_union")
     return out, lse
 
 

@@ -79,8 +79,12 @@ inline size_t table_bytes(int R, bool mask) { return (size_t)(R + kTabPad) * 4 *
 // rounds(R) * (R + fixed cost), where rounds(R) is how many times the group's splits fill every
 // CU's resident workgroup slots (at the occupancy the slot table's LDS allows).  Workgroups
 // then see the same amount of work and the last round is not left half empty.
+// pre_ld > 0: the caller hands over each group's fetch list already assembled (ascending rows,
+// a set mask per row, at most pre_ld rows); nothing is assembled and the workspace holds only
+// the split partials.
 Plan make_plan(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_tokens,
-               int64_t sel_ld, int gran, int n_sink, int n_recent, bool from_scores = false) {
+               int64_t sel_ld, int gran, int n_sink, int n_recent, bool from_scores = false,
+               int64_t pre_ld = 0) {
   Plan p;
   const int G = Hq / Hkv;
   p.groups = B * Hkv;
@@ -90,9 +94,9 @@ Plan make_plan(spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_
   p.mask = p.sets > 1;
   const bool expand = gran > 1 || n_sink > 0 || n_recent > 0;
   // a selection made from scores inside the attention is always expanded there
-  p.intervals = p.sets == 1 && (expand || from_scores) && sel_ld + 2 <= 64;
-  p.assemble = p.sets > 1 || (expand && !p.intervals);
-  int64_t ub = (int64_t)p.sets * sel_ld * gran + n_sink + n_recent;
+  p.intervals = pre_ld == 0 && p.sets == 1 && (expand || from_scores) && sel_ld + 2 <= 64;
+  p.assemble = pre_ld == 0 && (p.sets > 1 || (expand && !p.intervals));
+  int64_t ub = pre_ld > 0 ? pre_ld : (int64_t)p.sets * sel_ld * gran + n_sink + n_recent;
   if (ub > n_tokens) ub = n_tokens;
   p.ubound = (int)ub;
   const PartialInfo info = partial_info(d, p.nq_pad, p.mask, p.intervals ? 1 : 0);
@@ -1464,7 +1468,7 @@ extern "C" SPK_API spk_status sparse_decode_attn_workspace_size(
 // The body of sparse_decode_attn and sparse_decode_attn_noalloc: `ws` is the caller's
 // workspace or the library's scratch array.  With validate_only, every argument check runs and
 // the call returns before the workspace check and any launch.
-static spk_status decode_attn_impl(bool validate_only,
+static spk_status decode_attn_impl(bool validate_only, const uint32_t* pre_mask,
     const void* q, spk_dtype q_dtype, const void* k, const void* v, spk_dtype kv_dtype,
     int64_t kv_sb, int64_t kv_sh, int64_t kv_sn, const void* k_host, const void* v_host,
     int64_t host_sb, int64_t host_sh, int64_t host_sn, int64_t host_slots, const int32_t* loc,
@@ -1511,7 +1515,8 @@ static spk_status decode_attn_impl(bool validate_only,
               "sparse_decode_attn: n_tokens %d exceeds the %lld rows of the HBM caches", n_tokens,
               (long long)hbm_slots);
   SPK_REQUIRE(!(sm_scale != sm_scale), SPK_EINVAL, "sparse_decode_attn: sm_scale is NaN");
-  const Plan p = make_plan(scope, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent);
+  const Plan p = make_plan(scope, B, T, Hq, Hkv, d, n_tokens, sel_ld, gran, n_sink, n_recent,
+                           false, pre_mask ? sel_ld : 0);
   SPK_REQUIRE(!logits || logits_ld >= p.ubound, SPK_EINVAL,
               "sparse_decode_attn: logits_ld %lld < fetch-list bound %d", (long long)logits_ld,
               p.ubound);
@@ -1572,9 +1577,19 @@ static spk_status decode_attn_impl(bool validate_only,
   // part also holds are skipped), and splits are sized from the bound so they are known before
   // the count.
   const bool expand = gran > 1 || n_sink > 0 || n_recent > 0;
-  const bool virt = !logits && kv_dtype == SPK_BF16 && q_dtype == SPK_BF16 && p.sets == 1 &&
-                    expand && (int64_t)n_tokens >= sel_ld * gran + n_sink + n_recent;
-  if (virt) {
+  const bool virt = !pre_mask && !logits && kv_dtype == SPK_BF16 && q_dtype == SPK_BF16 &&
+                    p.sets == 1 && expand && (int64_t)n_tokens >= sel_ld * gran + n_sink + n_recent;
+  if (pre_mask) {
+    // the caller's assembled union: rows list[g*sel_ld + i], i < count[g], masks alongside
+    a.list = sel_idx;
+    a.count = sel_count;
+    a.list_ld = sel_ld;
+    a.count_clamp = p.ubound;
+    a.lrow_is_batch = 0;
+    a.mask = pre_mask;
+    a.ucount = const_cast<int32_t*>(sel_count);
+    a.ucount_valid = 1;
+  } else if (virt) {
     a.list_mode = kListVirtual;
     a.list = sel_idx;
     a.count = sel_count;
@@ -1664,11 +1679,47 @@ extern "C" SPK_API spk_status sparse_decode_attn(
     spk_sel_scope scope, int gran, int n_sink, int n_recent, int B, int T, int Hq, int Hkv, int d,
     int n_tokens, float sm_scale, float* out, float* lse, float* logits, int64_t logits_ld,
     void* ws, size_t ws_bytes, void* stream) {
-  return decode_attn_impl(false, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host, v_host,
+  return decode_attn_impl(false, nullptr, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host, v_host,
                           host_sb, host_sh, host_sn, host_slots, loc, loc_sb, loc_sh, hbm_slots,
                           sel_idx, sel_count, sel_ld, scope, gran, n_sink, n_recent, B, T, Hq,
                           Hkv, d, n_tokens, sm_scale, out, lse, logits, logits_ld, ws, ws_bytes,
                           stream);
+}
+
+extern "C" SPK_API spk_status sparse_decode_attn_union_workspace_size(
+    spk_sel_scope scope, int B, int T, int Hq, int Hkv, int d, int n_tokens, int64_t u_ld,
+    size_t* bytes) {
+  using namespace spk;
+  SPK_REQUIRE(bytes, SPK_EINVAL, "sparse_decode_attn_union_workspace_size: null bytes");
+  SPK_REQUIRE(scope == SPK_SEL_PER_Q_HEAD || scope == SPK_SEL_PER_KV_HEAD, SPK_EINVAL,
+              "sparse_decode_attn_union: scope must be per_q_head or per_kv_head");
+  SPK_REQUIRE(u_ld > 0, SPK_EINVAL, "sparse_decode_attn_union: u_ld must be > 0");
+  spk_status st = check_common(scope, B, T, Hq, Hkv, d, n_tokens, u_ld, 1, 0, 0);
+  if (st != SPK_OK) return st;
+  *bytes = make_plan(scope, B, T, Hq, Hkv, d, n_tokens, u_ld, 1, 0, 0, false, u_ld).bytes;
+  clear_error();
+  return SPK_OK;
+}
+
+extern "C" SPK_API spk_status sparse_decode_attn_union(
+    const void* q, spk_dtype q_dtype, const void* k, const void* v, spk_dtype kv_dtype,
+    int64_t kv_sb, int64_t kv_sh, int64_t kv_sn, const void* k_host, const void* v_host,
+    int64_t host_sb, int64_t host_sh, int64_t host_sn, int64_t host_slots, const int32_t* loc,
+    int64_t loc_sb, int64_t loc_sh, int64_t hbm_slots, const int32_t* u_list,
+    const uint32_t* u_mask, const int32_t* u_count, int64_t u_ld, spk_sel_scope scope, int B,
+    int T, int Hq, int Hkv, int d, int n_tokens, float sm_scale, float* out, float* lse,
+    float* logits, int64_t logits_ld, void* ws, size_t ws_bytes, void* stream) {
+  using namespace spk;
+  SPK_REQUIRE(scope == SPK_SEL_PER_Q_HEAD || scope == SPK_SEL_PER_KV_HEAD, SPK_EINVAL,
+              "sparse_decode_attn_union: scope must be per_q_head or per_kv_head");
+  SPK_REQUIRE(u_ld > 0, SPK_EINVAL, "sparse_decode_attn_union: u_ld must be > 0");
+  SPK_REQUIRE(B == 0 || (u_list && u_mask && u_count), SPK_EINVAL,
+              "sparse_decode_attn_union: null union list, mask or count");
+  const uint32_t* pm = u_mask ? u_mask : reinterpret_cast<const uint32_t*>(u_list);
+  return decode_attn_impl(false, pm, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host,
+                          v_host, host_sb, host_sh, host_sn, host_slots, loc, loc_sb, loc_sh,
+                          hbm_slots, u_list, u_count, u_ld, scope, 1, 0, 0, B, T, Hq, Hkv, d,
+                          n_tokens, sm_scale, out, lse, logits, logits_ld, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------- allocation-free variant
@@ -1739,7 +1790,7 @@ extern "C" SPK_API spk_status sparse_decode_attn_noalloc(
               "sparse_decode_attn_noalloc: this call needs %zu bytes of workspace, more than the "
               "library's fixed %zu-byte scratch array; use sparse_decode_attn with a workspace",
               need, kScratchBytes);
-  st = decode_attn_impl(true, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host, v_host,
+  st = decode_attn_impl(true, nullptr, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host, v_host,
                         host_sb, host_sh, host_sn, host_slots, loc, loc_sb, loc_sh, hbm_slots,
                         sel_idx, sel_count, sel_ld, scope, gran, n_sink, n_recent, B, T, Hq, Hkv,
                         d, n_tokens, sm_scale, out, lse, logits, logits_ld, nullptr, 0, stream);
@@ -1747,7 +1798,7 @@ extern "C" SPK_API spk_status sparse_decode_attn_noalloc(
   void* ws = nullptr;
   st = scratch_for_current_device(&ws);
   if (st != SPK_OK) return st;
-  return decode_attn_impl(false, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host, v_host,
+  return decode_attn_impl(false, nullptr, q, q_dtype, k, v, kv_dtype, kv_sb, kv_sh, kv_sn, k_host, v_host,
                           host_sb, host_sh, host_sn, host_slots, loc, loc_sb, loc_sh, hbm_slots,
                           sel_idx, sel_count, sel_ld, scope, gran, n_sink, n_recent, B, T, Hq,
                           Hkv, d, n_tokens, sm_scale, out, lse, logits, logits_ld, ws,

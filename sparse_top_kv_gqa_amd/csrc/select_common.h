@@ -8,6 +8,11 @@
 
 namespace spk {
 
+// Key histogram of the wide-row selection: the top kHistBits bits of an order key name its bin.
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistShift = 32 - kHistBits;
+
 // Wave 0 finds the digit where the running count (from the largest digit down) reaches kk.
 // Writes sh[0] = digit, sh[1] = number of candidates with a larger digit.
 __device__ __forceinline__ void find_digit(const uint32_t* h, int kk, int* sh) {

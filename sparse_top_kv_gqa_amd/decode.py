@@ -21,7 +21,10 @@ from . import (attn_workspace_size, fused_index_topk_ok, sparse_decode_attn, spa
                sparse_index_score_windowed, sparse_index_topk, sparse_topk_decode_attn,
                sparse_window_pool, topk_attn_workspace_size, topk_select, topk_workspace_size,
                importance_accumulate, tier_classify, window_count, residency_update,
-               residency_prefetch)
+               residency_prefetch, topk_select_union, topk_union_workspace_size,
+               sparse_decode_attn_union, attn_union_workspace_size, union_sets)
+
+UNION_MIN_TOKENS = 16385   # wide rows: the union pipeline (narrower rows fit one workgroup)
 
 
 class BlockSparseDecode:
@@ -134,11 +137,16 @@ class TokenSparseDecode:
     mode "token_group_mean": each (token, KV head) keeps the top-k of the group-mean score
     (scope per_kv_head).  ``index_keys`` is the key array the indexer streams (defaults to k);
     host pools and ``loc`` put some rows in pinned host memory for the attention gather.
+
+    With wide rows and at most 4 selection sets per KV head (``union`` None = automatic) the
+    step runs the union pipeline: the per-set top-k and the group's union in one call, then the
+    attention over that union (no assembly).
     """
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, n_tokens: int, Hq: int, T: int, topk: int,
                  mode: str, sm_scale: Optional[float] = None,
-                 index_keys: Optional[torch.Tensor] = None, k_host=None, v_host=None, loc=None):
+                 index_keys: Optional[torch.Tensor] = None, k_host=None, v_host=None, loc=None,
+                 union: Optional[bool] = None):
         self.k, self.v = k, v
         self.index_keys = k if index_keys is None else index_keys
         self.k_host, self.v_host, self.loc = k_host, v_host, loc
@@ -155,24 +163,60 @@ class TokenSparseDecode:
         self.count = torch.empty((B, T, Hs), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
-        ws = attn_workspace_size(self.scope, B, T, Hq, Hkv, d, n_tokens, kk)
-        self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
-        tws = topk_workspace_size(B * T * Hs, n_tokens, topk)
-        self.topk_ws = torch.empty(max(tws, 1), dtype=torch.uint8, device=dev)
+        S = union_sets(self.scope, T, Hq, Hkv)
+        self.union = (S <= 4 and n_tokens >= UNION_MIN_TOKENS) if union is None else bool(union)
+        if self.union:
+            rows = B * T * Hs
+            u_ld = max(1, min(n_tokens, S * min(topk, n_tokens)))
+            self.u_list = torch.empty((B * Hkv, u_ld), dtype=torch.int32, device=dev)
+            self.u_mask = torch.empty((B * Hkv, u_ld), dtype=torch.int32, device=dev)
+            self.u_count = torch.empty((B * Hkv,), dtype=torch.int32, device=dev)
+            uws = topk_union_workspace_size(B, T, Hq, Hkv, self.scope, n_tokens, topk)
+            self.topk_ws = torch.empty(max(uws, 1), dtype=torch.uint8, device=dev)
+            aws = attn_union_workspace_size(self.scope, B, T, Hq, Hkv, d, n_tokens, u_ld)
+            self.ws = torch.empty(max(aws, 1), dtype=torch.uint8, device=dev)
+        else:
+            ws = attn_workspace_size(self.scope, B, T, Hq, Hkv, d, n_tokens, kk)
+            self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
+            tws = topk_workspace_size(B * T * Hs, n_tokens, topk)
+            self.topk_ws = torch.empty(max(tws, 1), dtype=torch.uint8, device=dev)
 
-    def select(self, q: torch.Tensor):
-        sparse_index_score(self.mode, q, self.index_keys, self.n_tokens, scores=self.scores)
-        topk_select(self.scores, self.topk, idx=self.idx, count=self.count, ws=self.topk_ws)
+    def index(self, q: torch.Tensor, stream=None):
+        """The indexer's scores."""
+        sparse_index_score(self.mode, q, self.index_keys, self.n_tokens, scores=self.scores,
+                           stream=stream)
 
-    def attend(self, q: torch.Tensor):
-        sparse_decode_attn(q, self.k, self.v, self.idx, self.count, self.scope, self.n_tokens,
-                           sm_scale=self.sm_scale, k_host=self.k_host, v_host=self.v_host,
-                           loc=self.loc, out=self.out, lse=self.lse, ws=self.ws)
+    def select_topk(self, stream=None):
+        """Top-k of the current scores (and, on the union pipeline, each group's union)."""
+        if self.union:
+            topk_select_union(self.scores, self.topk, self.scope, self.Hkv,
+                              idx=self.idx, count=self.count, u_list=self.u_list,
+                              u_mask=self.u_mask, u_count=self.u_count, ws=self.topk_ws,
+                              stream=stream)
+        else:
+            topk_select(self.scores, self.topk, idx=self.idx, count=self.count, ws=self.topk_ws,
+                        stream=stream)
+
+    def select(self, q: torch.Tensor, stream=None):
+        self.index(q, stream)
+        self.select_topk(stream)
+
+    def attend(self, q: torch.Tensor, stream=None):
+        if self.union:
+            sparse_decode_attn_union(q, self.k, self.v, self.u_list, self.u_mask, self.u_count,
+                                     self.scope, self.n_tokens, sm_scale=self.sm_scale,
+                                     k_host=self.k_host, v_host=self.v_host, loc=self.loc,
+                                     out=self.out, lse=self.lse, ws=self.ws, stream=stream)
+        else:
+            sparse_decode_attn(q, self.k, self.v, self.idx, self.count, self.scope, self.n_tokens,
+                               sm_scale=self.sm_scale, k_host=self.k_host, v_host=self.v_host,
+                               loc=self.loc, out=self.out, lse=self.lse, ws=self.ws,
+                               stream=stream)
         return self.out, self.lse
 
-    def step(self, q: torch.Tensor):
-        self.select(q)
-        return self.attend(q)
+    def step(self, q: torch.Tensor, stream=None):
+        self.select(q, stream)
+        return self.attend(q, stream)
 
 
 class TieredDecode:

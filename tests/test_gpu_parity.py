@@ -1396,3 +1396,89 @@ def test_stream_read_reference_reads_every_word():
     torch.cuda.synchronize()
     assert int(sink.item()) & 0xFFFFFFFF == 0x9E3779B9
 
+
+
+# ------------------------------------------------------------------------------------ union pipeline
+
+@pytest.mark.parametrize("n", [16385, 20000, 70001])
+@pytest.mark.parametrize("kind", ["normal", "ties", "allsame", "special"])
+@pytest.mark.parametrize("scope,T,G", [("per_q_head", 1, 4), ("per_kv_head", 4, 4), ("per_q_head", 1, 2)])
+def test_topk_union_bit_exact(n, kind, scope, T, G):
+    """topk_select_union against the oracle: every set's selection equals oracle.topk of its row
+    bit for bit, the union is the sorted set union and each mask bit says which sets hold the
+    row; heavy ties take the fallback inside the threshold pass."""
+    say("topk-union", n, kind, scope, T, G)
+    B, Hkv = 2, 2
+    Hq = Hkv * G
+    Hs = Hq if scope == "per_q_head" else Hkv
+    rows = B * T * Hs
+    x = _rows(kind, n, rows, seed=n + T + G).reshape(B, T, Hs, n)
+    xs = torch.tensor(x, device=DEV)
+    S = T * G if scope == "per_q_head" else T
+    for k in sorted({0, 1, 700, 2622, n - 1, n, n + 3}):
+        idx, cnt, ul, um, uc = spk.topk_select_union(xs, k, scope, Hkv)
+        torch.cuda.synchronize()
+        kk = min(k, n)
+        got = idx.cpu().numpy()
+        assert cnt.cpu().numpy().ravel().tolist() == [kk] * rows, (k, kind)
+        ulh, umh, uch = ul.cpu().numpy(), um.cpu().numpy(), uc.cpu().numpy()
+        for b in range(B):
+            for h in range(Hkv):
+                g = b * Hkv + h
+                sets = []
+                for s in range(S):
+                    if scope == "per_q_head":
+                        t, j = divmod(s, G)
+                        r = (b, t, h * G + j)
+                    else:
+                        r = (b, s, h)
+                    exp = oracle.topk(x[r], k)
+                    assert got[r][:kk].tolist() == exp.tolist(), (n, kind, k, r)
+                    sets.append(exp)
+                union = np.unique(np.concatenate(sets)) if kk else np.zeros(0, np.int64)
+                c = int(uch[g])
+                assert c == union.shape[0], (k, g)
+                assert ulh[g, :c].tolist() == union.tolist()
+                mask = np.zeros(c, np.int64)
+                for s, sel in enumerate(sets):
+                    mask |= np.isin(union, sel).astype(np.int64) << s
+                assert umh[g, :c].tolist() == mask.tolist()
+
+
+@pytest.mark.parametrize("which", ["per_head", "spec_verify"])
+def test_union_decode_matches_assembled_path(which):
+    """The union pipeline's step (scores with histograms, top-k with the union, attention over
+    the union) gives the selections and, bit for bit, the attention of the separate calls with
+    the assembly; and matches the oracle on every group."""
+    base = W.PER_HEAD_2PCT if which == "per_head" else W.SPEC_VERIFY
+    w = W.scaled(base, B=2, Hkv=2, Hq=8, N=20000 + 5, k=700)
+    say("union-decode", which, w.name)
+    q = W.queries(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    mode = "token_per_head" if which == "per_head" else "token_group_mean"
+    du = TokenSparseDecode(k, v, w.N, w.Hq, w.T, w.k, mode, union=True)
+    da = TokenSparseDecode(k, v, w.N, w.Hq, w.T, w.k, mode, union=False)
+    assert du.union and not da.union
+    ou, lu = du.step(q)
+    oa, la = da.step(q)
+    torch.cuda.synchronize()
+    assert torch.equal(du.scores, da.scores)
+    assert torch.equal(du.idx, da.idx) and torch.equal(du.count, da.count)
+    assert torch.equal(ou, oa) and torch.equal(lu, la)
+    qh, kh, vh = host(q), host(k), host(v)
+    scale = oracle.softmax_scale(w.d)
+    G = w.G
+    sc = du.scores.cpu().numpy()
+    idx = du.idx.cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            for t in range(w.T):
+                heads = range(h * G, (h + 1) * G)
+                for hq in heads:
+                    row = (b, t, hq) if which == "per_head" else (b, t, h)
+                    sel = idx[row][:w.k]
+                    assert sel.tolist() == oracle.topk(sc[row][:w.N], w.k).tolist()
+                    o_ref, l_ref, _ = oracle.attend(qh[b, t, hq:hq + 1], kh[b, h][sel], vh[b, h][sel],
+                                                    scale)
+                    check_attn(ou.cpu().numpy()[b, t, hq:hq + 1], o_ref, what=f"union {which}")
