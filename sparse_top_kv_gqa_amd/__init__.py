@@ -17,7 +17,9 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspk.so")
+# SPK_LIB names another build of the same library (the AddressSanitizer build of the host code)
+LIB_PATH = os.environ.get("SPK_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libspk.so")
 
 # enums of spk.h
 F32, BF16 = 0, 1

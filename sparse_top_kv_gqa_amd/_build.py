@@ -17,6 +17,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libspk.so")
+OBJ_ASAN = os.path.join(HERE, "_build_asan")
+LIB_ASAN = os.path.join(HERE, "libspk_asan.so")
+# AddressSanitizer on the host code only (argument validation, planning, launches); the device
+# code is built as usual
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 ARCH = "gfx950"
 
 
@@ -46,9 +51,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, asan: bool = False) -> str:
+    obj = os.path.join(OBJ_ASAN if asan else OBJ, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + FLAGS + (ASAN_HOST if asan else []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,23 +64,33 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libspk.so; returns the library path."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, asan: bool = False) -> str:
+    """Compile every source and link libspk.so (or, with asan, libspk_asan.so: host code under
+    AddressSanitizer, loadable with the sanitizer runtime preloaded); returns the path."""
+    os.makedirs(OBJ_ASAN if asan else OBJ, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, verbose, asan), srcs))
+    lib = LIB_ASAN if asan else LIB
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + \
+        (["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-shared-libasan"] if asan else []) + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def asan_runtime() -> str:
+    """Path of the host AddressSanitizer runtime of the ROCm toolchain."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    return r.stdout.strip()
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, asan="--asan" in sys.argv))

@@ -211,7 +211,7 @@ def test_block_workload_full_size_sampled_and_deterministic():
     idx = dec.idx.cpu().numpy()
     scale = oracle.softmax_scale(w.d)
     G = w.G
-    for (b, h) in [(0, 0), (3, 5), (7, 7)]:
+    for (b, h) in [(b, h) for b in range(w.B) for h in range(w.Hkv)]:   # every group
         kh, vh = host(k[b, h]), host(v[b, h])
         kpool = oracle.block_pool(kh, w.block_size)
         ref = oracle.scores_block(host(pred)[b, 0, h], kpool)
@@ -474,7 +474,7 @@ def test_per_head_full_size_sampled():
     torch.cuda.synchronize()
     scale = oracle.softmax_scale(w.d)
     G = w.G
-    for (b, h) in [(0, 0), (3, 6)]:
+    for (b, h) in [(b, h) for b in range(w.B) for h in range(w.Hkv)]:   # every group
         kh, vh = host(k[b, h]), host(v[b, h])
         qg = host(q)[b, 0, h * G:(h + 1) * G]
         ref = oracle.scores_token_per_head(qg, kh)
@@ -522,7 +522,7 @@ def test_spec_verify_full_size_sampled_with_host_rows():
     assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
     scale = oracle.softmax_scale(w.d)
     G = w.G
-    for (b, h) in [(0, 0), (15, 7)]:
+    for (b, h) in [(b, (3 * b) % w.Hkv) for b in range(w.B)]:   # one group of every sequence
         kh, vh = host(k[b, h]), host(v[b, h])
         qt = host(q)[b, :, h * G:(h + 1) * G]
         for t in range(w.T):
@@ -546,7 +546,7 @@ def test_tiered_full_size_sampled_steps():
     dec = TieredDecode(caches, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille)
     scale = oracle.softmax_scale(w.d)
     check_at = {0, 1, 2, w.steps - 1}
-    sample_b = [0, 21]
+    sample_b = [0, 9, 21, 31]
     for t in range(w.steps):
         n = w.n_start + w.grow_per_step * (t + 1)
         qs = [W.queries(w, step=t, layer=l, device=DEV) for l in range(w.layers)]
