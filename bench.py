@@ -27,6 +27,11 @@ Workloads:
                host memory and are read over PCIe inside the attention kernel.
   tiers        batch 32, 28 layers, 28/4 heads, 64 decode steps growing 4096 -> 16384 tokens:
                tier classification -> attention over T0 ∪ T1 in all layers -> importance update.
+  block_lookahead  the block layer through 8 layers whose caches keep a seeded 1.8 % of the
+               blocks (about 1.4 % of the selected rows) only in pinned host memory: timed with
+               lookahead (layer l+1's blocks chosen before layer l attends, their host rows
+               copied into HBM by a persistent kernel on a second stream meanwhile), without it
+               (host rows read inside the attention) and with every row in HBM.
   tiers_offload  the same episode with every row in pinned host memory and --hbm-rows slots
                per sequence in HBM (default 8192): every --reassign-every steps (default 8) the
                resident set is recomputed and only newly resident rows are copied over PCIe;
@@ -61,12 +66,18 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="all",
                     choices=["all", "block", "block_windowed", "per_head", "spec_verify", "tiers",
-                             "tiers_offload"])
+                             "tiers_offload", "block_lookahead"])
     ap.add_argument("--hbm-rows", type=int, default=8192,
                     help="tiers_offload: HBM slots per sequence (the rest stays in host memory)")
     ap.add_argument("--reassign-every", type=int, default=8,
                     help="tiers_offload: tiered steps between residency reassignments")
     ap.add_argument("--layers", type=int, default=8, help="block: layer caches to rotate")
+    ap.add_argument("--host-frac", type=float, default=None,
+                    help="block_lookahead: fraction of the eligible blocks kept only in host memory "
+                         "(default: the workload's)")
+    ap.add_argument("--copy-workgroups", type=int, default=None,
+                    help="block_lookahead: workgroups of the persistent copy kernel (default: one "
+                         "per (batch, kv-head) group)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -564,11 +575,12 @@ def cpu_block(ctx, seconds):
         done += 1
         if spent >= seconds:
             break
-    per_step = spent / done * len(groups)
+    layers = ctx.get("layers", 1)
+    per_step = spent / done * len(groups) * layers
     return {"value": round(1.0 / per_step, 4), "unit": "decode steps/s", "cores": _cores(),
             "kind": "oracle",
-            "sample": f"{done} of {len(groups)} (batch, kv-head) groups of one step "
-                      f"({spent:.1f} s), scaled to the whole step"}
+            "sample": f"{done} of {len(groups)} (batch, kv-head) groups of one layer "
+                      f"({spent:.1f} s), scaled to the whole step ({layers} layer(s))"}
 
 
 # ------------------------------------------------------------------------------ token sparse
@@ -900,6 +912,153 @@ def bench_tiers_offload(args):
     return res, ctx
 
 
+def bench_lookahead(args):
+    """Block decode through 8 layers with host-only blocks: lookahead vs none vs all in HBM."""
+    import workloads as W
+    from sparse_top_kv_gqa_amd.decode import BlockLookaheadDecode, BlockSparseDecode
+
+    w = W.LOOKAHEAD_BLOCK
+    if args.host_frac is not None:
+        w = W.scaled(w, host_frac=args.host_frac)
+    K = args.steps or 50
+    Wm = args.warmup if args.warmup is not None else 5
+    bs, kb = w.block_size, w.k
+    P = 4
+    log(f"generating {w.layers} layers of {w.name}")
+    full, layers, host_rows_total = [], [], 0
+    for l in range(w.layers):
+        kf = W.kv_cache(w, "k", layer=l, device="cuda")
+        vf = W.kv_cache(w, "v", layer=l, device="cuda")
+        full.append((kf, vf))
+        home = torch.arange(w.N, dtype=torch.int32).repeat(w.B, w.Hkv, 1)
+        rows_g = []
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                blks = W.host_blocks(w, b, h, l)
+                rows = (blks[:, None] * bs + torch.arange(bs)).reshape(-1)
+                home[b, h, rows] = ~torch.arange(rows.numel(), dtype=torch.int32)
+                rows_g.append(rows)
+        nh = max(1, max(r.numel() for r in rows_g))
+        kh = torch.zeros((w.B, w.Hkv, nh, w.d), dtype=torch.bfloat16, pin_memory=True)
+        vh = torch.zeros_like(kh).pin_memory()
+        k = torch.empty((w.B, w.Hkv, w.N + kb * bs, w.d), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        k[:, :, :w.N] = kf
+        v[:, :, :w.N] = vf
+        i = 0
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                rows = rows_g[i]
+                i += 1
+                host_rows_total += rows.numel()
+                rd = rows.to("cuda")
+                kh[b, h, :rows.numel()].copy_(kf[b, h, rd].cpu())
+                vh[b, h, :rows.numel()].copy_(vf[b, h, rd].cpu())
+                k[b, h, rd] = float("nan")           # the HBM copies of host rows are never read
+                v[b, h, rd] = float("nan")
+        layers.append((k, v, kh, vh, home.to("cuda")))
+    pool_keys = [kf for kf, _ in full]
+    qs = [[W.queries(w, step=s, layer=l, device="cuda") for l in range(w.layers)] for s in range(P)]
+    preds = [[W.predictors(w, step=s, layer=l, device="cuda") for l in range(w.layers)]
+             for s in range(P)]
+    la = BlockLookaheadDecode(layers, pool_keys, w.N, w.Hq, bs, kb, w.n_sink, w.n_recent,
+                              lookahead=True, workgroups=args.copy_workgroups)
+    no = BlockLookaheadDecode(layers, pool_keys, w.N, w.Hq, bs, kb, w.n_sink, w.n_recent,
+                              lookahead=False)
+    hbm = [BlockSparseDecode(kf, vf, w.N, w.Hq, bs, kb, w.n_sink, w.n_recent, topk_in_attn=False)
+           for kf, vf in full]
+    pred0 = [W.predictors(w, step=99, layer=l, device="cuda") for l in range(w.layers)]
+    la.pool(pred0)
+    no.pool(pred0)
+    for d_, p_ in zip(hbm, pred0):
+        d_.pool(p_)
+    stream = torch.cuda.Stream()
+
+    def hbm_step(i):
+        for l in range(w.layers):
+            hbm[l].select(preds[i % P][l])
+            hbm[l].attend(qs[i % P][l])
+
+    # rows per step, host rows among them, bit identity of the three ways
+    sel_rows, host_sel = [], []
+    with torch.cuda.stream(stream):
+        for s_ in range(P):
+            la.step(qs[s_], preds[s_], stream=stream)
+            o_la = la.out.clone()
+            no.step(qs[s_], preds[s_], stream=stream)
+            hbm_step(s_)
+            torch.cuda.synchronize()
+            tot = host = 0
+            for l in range(w.layers):
+                assert torch.equal(o_la[l], hbm[l].out) and torch.equal(no.out[l], hbm[l].out), \
+                    "lookahead, in-kernel host reads and all-HBM differ"
+                tot += union_rows_block(hbm[l].idx, w.N, bs, w.n_sink, w.n_recent)
+                sel = hbm[l].idx.reshape(w.B * w.Hkv, -1).long()
+                toks = (sel[:, :, None] * bs + torch.arange(bs, device="cuda")).reshape(w.B * w.Hkv, -1)
+                hm = layers[l][4].reshape(w.B * w.Hkv, w.N)
+                host += int((torch.gather(hm, 1, toks.clamp(max=w.N - 1)) < 0).sum())
+            sel_rows.append(tot)
+            host_sel.append(host)
+    index_bytes = w.layers * w.B * w.Hkv * (w.N // bs) * w.d * 4
+    step_bytes = index_bytes + sum(sel_rows) / P * ROW_BYTES
+    # every variant's step (all layers) captured once per input set and replayed: the timed loops
+    # measure the GPU, not the host's launch rate
+    def capture(fn):
+        gs = []
+        with torch.cuda.stream(stream):
+            for s_ in range(P):
+                fn(s_)
+            torch.cuda.synchronize()
+            for s_ in range(P):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    fn(s_)
+                gs.append(g)
+        torch.cuda.synchronize()
+        return gs
+    g_la = capture(lambda i: la.step(qs[i], preds[i], stream=stream))
+    g_no = capture(lambda i: no.step(qs[i], preds[i], stream=stream))
+    g_hbm = capture(hbm_step)
+    # replays reproduce the eager results bit for bit
+    for s_ in range(P):
+        g_la[s_].replay()
+        g_hbm[s_].replay()
+        torch.cuda.synchronize()
+        for l in range(w.layers):
+            assert torch.equal(la.out[l], hbm[l].out), "graph replay differs"
+    ms_la, wall = timed_loop(lambda i: g_la[i % P].replay(), K, Wm, stream)
+    ms_no, _ = timed_loop(lambda i: g_no[i % P].replay(), K, Wm, stream)
+    ms_hbm, _ = timed_loop(lambda i: g_hbm[i % P].replay(), K, Wm, stream)
+    ms_step = ms_la / K
+    pcie = sum(host_sel) / P * ROW_BYTES
+    # the attention of one layer after its prefetch (every row it reads is in HBM)
+    l0 = w.layers - 1
+
+    def attn(i):
+        la._attend(l0, qs[0][l0], la.loc[l0], stream)
+    la.step(qs[0], preds[0], stream=stream)
+    torch.cuda.synchronize()
+    gather_ms = gather_kernel_ms(attn, 20, stream)
+    att_bytes = sel_rows[0] / w.layers * ROW_BYTES
+    res = base_result(w, K, Wm, ms_step, step_bytes, {
+        "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+        "context": w.N, "layers": w.layers, "block_size": bs, "top_blocks": kb,
+        "sinks": w.n_sink, "recent": w.n_recent, "bytes_per_step": int(step_bytes),
+        "host_rows_resident": host_rows_total,
+        "host_block_fraction": w.host_frac,
+        "host_fraction_of_selected_rows": round(sum(host_sel) / max(1, sum(sel_rows)), 4),
+        "pcie_bytes_per_step": int(pcie), "wall_s_timed": round(wall, 4),
+        "ms_per_step_lookahead": round(ms_la / K, 5),
+        "ms_per_step_no_lookahead": round(ms_no / K, 5),
+        "ms_per_step_all_hbm": round(ms_hbm / K, 5),
+        "lookahead_speedup": round(ms_no / ms_la, 3),
+        "copy_kernel_workgroups": la.workgroups or w.B * w.Hkv, "timing": "HIP graph replays of the whole step"})
+    res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather, one layer, "
+                               "host blocks already staged)", att_bytes, gather_ms)
+    ctx = dict(w=w, dec=hbm[0], q=qs[0][0], pred=preds[0][0], windowed=False, layers=w.layers)
+    return res, ctx
+
+
 def cpu_tiers(ctx, seconds):
     """One dense decode step of whole sequences (all layers), the oracle as it stands."""
     import numpy as np
@@ -929,7 +1088,8 @@ def cpu_tiers(ctx, seconds):
 
 
 HEADLINE = "per_head"
-ORDER = ["per_head", "block", "block_windowed", "spec_verify", "tiers", "tiers_offload"]
+ORDER = ["per_head", "block", "block_windowed", "spec_verify", "tiers", "tiers_offload",
+         "block_lookahead"]
 
 
 def run_workload(name, args):
@@ -944,6 +1104,9 @@ def run_workload(name, args):
     elif name == "tiers_offload":
         res, ctx = bench_tiers_offload(args)
         cpu = cpu_tiers
+    elif name == "block_lookahead":
+        res, ctx = bench_lookahead(args)
+        cpu = cpu_block
     else:
         res, ctx = bench_tiers(args)
         cpu = cpu_tiers

@@ -12,6 +12,8 @@
  *                        for wide rows with up to 4 selection sets per KV head: the per-set
  *                        top-k and the group's union with set masks, and the attention over
  *                        that union
+ *   lookahead_prefetch   copies the host rows of the next layer's chosen blocks into HBM
+ *                        staging rows while the current layer attends
  *   importance_accumulate  cumulative attention importance s_i += mean over layers, heads of α[i]
  *   tier_classify        T0/T1/T3 tiers by importance, sinks and recent window protected
  *
@@ -418,6 +420,48 @@ SPK_API spk_status sparse_decode_attn_noalloc(const void* q, spk_dtype q_dtype,
                                               float sm_scale,
                                               float* out, float* lse, float* logits,
                                               int64_t logits_ld, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * lookahead_prefetch — copy the host-resident rows of the blocks a selection names into HBM
+ * staging rows, ahead of the attention that will read them, and point the row locations there.
+ *
+ * Passages: SparDA §2 "Seleção Esparsa de Lookahead Treinável" (layer l+1's blocks are chosen
+ * while layer l runs) and "Inovações Principais" (a persistent kernel of a few workgroups copies
+ * the missing blocks meanwhile); "Nem Todos os Pensamentos Necessitam de HBM" §3 (Proposition 1:
+ * the copy is exact, results do not change).
+ *
+ *   sel_idx, sel_count, sel_ld   block ids per (b, kvh) group [B*Hkv][sel_ld] and their counts
+ *              (topk_select's output of the next layer's block scores); block_size rows each
+ *   k_host, v_host, host strides, host_slots   pinned host pools [B,Hkv,host_slots,d]
+ *   k, v, kv strides, hbm_slots   the HBM caches [B,Hkv,hbm_slots,d]; rows
+ *              [stage_base, stage_base + sel_ld*block_size) are the staging rows (past n_tokens)
+ *   loc_home   device int32 [B,Hkv,>=n_tokens] (strides loc_sb, loc_sh): each row's home, >= 0
+ *              an HBM row, < 0 the host row ~loc_home (read only)
+ *   loc        device int32, same layout: the locations the attention reads; the rows this call
+ *              redirects point to staging rows, and the rows the previous call redirected are
+ *              first set back to their home
+ *   staged, staged_count   device int32 [B*Hkv][sel_ld*block_size] and [B*Hkv]: per group the
+ *              tokens a call redirected, as a compact list of staged_count entries, kept for the
+ *              next call on the same buffers (which must use the same sel_ld and block_size);
+ *              staged_count zero before the first call
+ *   workgroups the fixed number of workgroups of the persistent copy kernel (its grid); each
+ *              takes whole groups in turn, so more than B*Hkv add nothing
+ * Run it on a stream of its own beside the attention of the layer before, and make the
+ * attention that reads these rows wait for it.  Errors: SPK_EINVAL (sizes, strides, staging
+ * range, pageable pools), SPK_EUNSUPPORTED (d, dtype).
+ * ---------------------------------------------------------------------------------------- */
+SPK_API spk_status lookahead_prefetch(const int32_t* sel_idx, const int32_t* sel_count,
+                                      int64_t sel_ld, int block_size, int B, int Hkv, int d,
+                                      spk_dtype kv_dtype, int n_tokens,
+                                      const void* k_host, const void* v_host,
+                                      int64_t host_sb, int64_t host_sh, int64_t host_sn,
+                                      int64_t host_slots, void* k, void* v,
+                                      int64_t kv_sb, int64_t kv_sh, int64_t kv_sn,
+                                      int64_t hbm_slots, int64_t stage_base,
+                                      const int32_t* loc_home, int32_t* loc,
+                                      int64_t loc_sb, int64_t loc_sh,
+                                      int32_t* staged, int32_t* staged_count, int workgroups,
+                                      void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * sparse_topk_decode_attn — topk_select of one score row per (b, kvh) group followed by

@@ -33,6 +33,25 @@ def block_group(pred, keys, vals, q_group, k_blocks, block_size, n_sink, n_recen
     return dict(kpool=kp, scores=sc, blocks=blocks, tokens=toks, out=out, lse=lse)
 
 
+def block_layers(preds, keys_layers, vals_layers, q_layers, k_blocks, block_size, n_sink,
+                 n_recent, sm_scale):
+    """Block-sparse decode of one GQA group through L layers with lookahead selection.
+
+    SparDA §2 "Seleção Esparsa de Lookahead Treinável": the blocks layer l+1 reads are chosen
+    by that layer's predictor vector, which is available while layer l still runs, so the
+    selection of every layer is made before the layer before it attends and never depends on
+    another layer's attention; each layer then reads its chosen blocks (with the sinks and the
+    recent window) and attends exactly, as block_group.  Where a row lives (HBM, or host memory
+    copied in ahead of use) does not enter: "Nem Todos os Pensamentos ...", §3 (Proposition 1).
+
+    preds ``[L, d]``; keys_layers / vals_layers ``[L, n, d]``; q_layers ``[L, G, d]``.
+    Returns the list of block_group results, one per layer.
+    """
+    L = len(preds)
+    return [block_group(preds[l], keys_layers[l], vals_layers[l], q_layers[l], k_blocks,
+                        block_size, n_sink, n_recent, sm_scale) for l in range(L)]
+
+
 def block_windowed_group(pred, keys, vals, q_group, k_blocks, block_size, window, stride,
                          n_sink, n_recent, sm_scale, kwin=None):
     """Block-sparse step of one GQA group with the predictor scoring overlapping compression

@@ -40,7 +40,8 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "residency_prefetch", "spk_stream_read", "spk_gather_read",
            "sparse_decode_attn_noalloc", "sparse_decode_attn_noalloc_max_bytes",
            "topk_select_union_workspace_size", "topk_select_union",
-           "sparse_decode_attn_union_workspace_size", "sparse_decode_attn_union")
+           "sparse_decode_attn_union_workspace_size", "sparse_decode_attn_union",
+           "lookahead_prefetch")
 
 
 class SpkError(RuntimeError):
@@ -98,6 +99,9 @@ def lib() -> ctypes.CDLL:
     L.sparse_decode_attn_union.argtypes = [P, I, P, P, I, I64, I64, I64, P, P, I64, I64, I64, I64, P,
                                            I64, I64, I64, P, P, P, I64, I, I, I, I, I, I, I, FL, P, P,
                                            P, I64, P, SZ, P]
+    L.lookahead_prefetch.restype = I
+    L.lookahead_prefetch.argtypes = [P, P, I64, I, I, I, I, I, I, P, P, I64, I64, I64, I64, P, P,
+                                     I64, I64, I64, I64, I64, P, P, I64, I64, P, P, I, P]
     L.importance_accumulate.restype = I
     L.importance_accumulate.argtypes = [P, I64, I, I, P, P, I64, P, I64, P, I, I, P]
     L.tier_classify_workspace_size.restype = I
@@ -918,6 +922,60 @@ def sparse_topk_decode_attn(scores: torch.Tensor, k: int, q: torch.Tensor, kc: t
                                        _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "sparse_topk_decode_attn")
     return out, lse
+
+
+def lookahead_prefetch(sel_idx: torch.Tensor, sel_count: torch.Tensor, block_size: int,
+                       n_tokens: int, k_host: torch.Tensor, v_host: torch.Tensor, k: torch.Tensor,
+                       v: torch.Tensor, stage_base: int, loc_home: torch.Tensor,
+                       loc: torch.Tensor, staged: torch.Tensor, staged_count: torch.Tensor,
+                       workgroups: Optional[int] = None, stream=None):
+    """Copy the host-resident rows of the selected blocks (sel_idx [B, 1, Hkv, sel_ld] block ids,
+    sel_count [B, 1, Hkv]) into the staging rows [stage_base, stage_base + sel_ld*block_size) of
+    the HBM caches k, v [B, Hkv, C, d], pointing loc [B, Hkv, >=n_tokens] there; the rows the
+    previous call redirected go back to loc_home first.  staged int32 [B*Hkv, sel_ld*block_size],
+    staged_count int32 [B*Hkv] (zero before the first call): the compact list of the tokens the
+    last call redirected, for the next call with the same sel_ld and block_size.  A persistent
+    kernel of ``workgroups`` workgroups (default one per (b, kvh) group)."""
+    if k.dim() != 4:
+        raise ValueError("k must be a [B, Hkv, C, d] view")
+    B, Hkv, C, d = k.shape
+    _need_cache(k, "k", B, Hkv, 0, d)
+    _need_cache(v, "v", B, Hkv, 0, d, dtypes=(k.dtype,))
+    _need_cache(k_host, "k_host", B, Hkv, 0, d, dtypes=(k.dtype,), device=False)
+    _need_cache(v_host, "v_host", B, Hkv, 0, d, dtypes=(k.dtype,), device=False)
+    _need_dev(sel_idx, "sel_idx", I32S)
+    sel_ld = _row_ld(sel_idx, "sel_idx", B * Hkv, 0)
+    if B * Hkv > 1 and sel_ld != sel_idx.shape[-1]:
+        raise ValueError("sel_idx rows must be contiguous")
+    sel_ld = sel_idx.shape[-1]
+    _need_contig_n(sel_count, "sel_count", B * Hkv, I32S)
+    for t, nm in ((loc_home, "loc_home"), (loc, "loc")):
+        _need_dev(t, nm, I32S)
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{nm} must be int32 [B, Hkv, N] with a contiguous last dim")
+        _need_shape(t, nm, [(">=", B), Hkv, (">=", n_tokens)])
+    if loc.stride() != loc_home.stride():
+        raise ValueError("loc and loc_home must share strides")
+    _need_contig_n(staged, "staged", B * Hkv * sel_ld * block_size, I32S)
+    _need_contig_n(staged_count, "staged_count", B * Hkv, I32S)
+    if not (n_tokens <= stage_base and stage_base + sel_ld * block_size <= C):
+        raise ValueError(f"staging rows [{stage_base}, {stage_base + sel_ld * block_size}) must lie "
+                         f"past the {n_tokens} tokens and inside the {C} HBM rows")
+    hb, hh, hn = _rows_view(k_host, "k_host")
+    if _rows_view(v_host, "v_host") != (hb, hh, hn):
+        raise ValueError("k_host and v_host must share strides")
+    kb, kh, kn = _rows_view(k, "k")
+    if _rows_view(v, "v") != (kb, kh, kn):
+        raise ValueError("k and v must share strides")
+    st = lib().lookahead_prefetch(_ptr(sel_idx), _ptr(sel_count), sel_ld, block_size, B, Hkv, d,
+                                  _dt(k), n_tokens, _ptr(k_host), _ptr(v_host), hb, hh, hn,
+                                  min(k_host.shape[2], v_host.shape[2]), _ptr(k), _ptr(v), kb, kh,
+                                  kn, min(k.shape[2], v.shape[2]), stage_base, _ptr(loc_home),
+                                  _ptr(loc), loc.stride(0), loc.stride(1), _ptr(staged),
+                                  _ptr(staged_count),
+                                  int(B * Hkv if workgroups is None else workgroups),
+                                  _stream(stream))
+    _check(st, "lookahead_prefetch")
 
 
 # ----------------------------------------------------------------------------- residency

@@ -9,6 +9,9 @@ TokenSparseDecode   per-head or group-mean token scores -> top-k tokens -> atten
                     pinned host memory)
 TieredDecode        tier classification by cumulative importance -> attention over T0 ∪ T1 in
                     every layer -> importance update
+BlockLookaheadDecode  the block step through several layers whose caches keep some blocks only
+                    in pinned host memory; with lookahead, layer l+1's blocks are chosen before
+                    layer l attends and their host rows are copied into HBM meanwhile
 """
 from __future__ import annotations
 
@@ -22,7 +25,8 @@ from . import (attn_workspace_size, fused_index_topk_ok, sparse_decode_attn, spa
                sparse_window_pool, topk_attn_workspace_size, topk_select, topk_workspace_size,
                importance_accumulate, tier_classify, window_count, residency_update,
                residency_prefetch, topk_select_union, topk_union_workspace_size,
-               sparse_decode_attn_union, attn_union_workspace_size, union_sets)
+               sparse_decode_attn_union, attn_union_workspace_size, union_sets,
+               lookahead_prefetch)
 
 UNION_MIN_TOKENS = 16385   # wide rows: the union pipeline (narrower rows fit one workgroup)
 
@@ -307,4 +311,114 @@ class TieredDecode:
                                    sm_scale=self.sm_scale, out=self.out[l], lse=self.lse[l],
                                    logits=self.logits[l], ws=self.ws)
         importance_accumulate(self.s, sel, self.count, self.logits, self.lse, n_tokens)
+        return self.out, self.lse
+
+
+class BlockLookaheadDecode:
+    """Block-sparse decode through L layers with some blocks of every layer only in pinned host
+    memory (SparDA §2, lookahead selection and the persistent copy kernel).
+
+    layers: per layer (k, v, k_host, v_host, loc_home): HBM caches ``[B, Hkv, C, d]`` with
+    C >= n_tokens + k_blocks * block_size (the rows past n_tokens are staging rows), pinned host
+    pools ``[B, Hkv, Nh, d]`` and the int32 home location of every row ``[B, Hkv, n_tokens]``
+    (>= 0: HBM row, < 0: host row ~loc).  The pooled keys are taken from ``pool_keys`` (the keys
+    of every row, pooled before any row left HBM).
+
+    lookahead=True: layer l+1's blocks are selected on the caller's stream before layer l
+    attends; a second stream (default priority) runs lookahead_prefetch, a persistent kernel of
+    ``workgroups`` workgroups (default one per (b, kvh) group), which copies the selected blocks' host rows into staging rows and
+    redirects their locations while layer l attends; layer l+1's attention waits for it.
+    lookahead=False: every layer selects, then attends, reading its host rows in the attention
+    kernel itself.  Both give bit-identical results (the reduction order never depends on where
+    a row is read from).
+    """
+
+    def __init__(self, layers, pool_keys, n_tokens: int, Hq: int, block_size: int, k_blocks: int,
+                 n_sink: int, n_recent: int, lookahead: bool = True,
+                 workgroups: Optional[int] = None,
+                 sm_scale: Optional[float] = None):
+        self.layers = list(layers)
+        self.L = len(self.layers)
+        k0 = self.layers[0][0]
+        B, Hkv, C, d = k0.shape
+        self.B, self.Hkv, self.Hq, self.d = B, Hkv, Hq, d
+        self.n_tokens, self.bs, self.kb = n_tokens, block_size, k_blocks
+        self.n_sink, self.n_recent = n_sink, n_recent
+        self.lookahead, self.workgroups = lookahead, workgroups
+        self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+        self.stage_base = n_tokens
+        if C < n_tokens + k_blocks * block_size:
+            raise ValueError("HBM caches need n_tokens + k_blocks * block_size rows")
+        dev = k0.device
+        # selection per layer: pooled keys, scores, top-k blocks (two launches)
+        self.sel = []
+        for l, (k, v, _, _, _) in enumerate(self.layers):
+            d_l = BlockSparseDecode(k, v, n_tokens, Hq, block_size, k_blocks, n_sink, n_recent,
+                                    sm_scale=self.sm_scale, fused=False, topk_in_attn=False)
+            self.sel.append(d_l)
+        kk = self.sel[0].idx.shape[-1]
+        self.loc = [h.clone() for (_, _, _, _, h) in self.layers]
+        self.staged = [torch.full((B * Hkv, kk * block_size), -1, dtype=torch.int32, device=dev)
+                       for _ in range(self.L)]
+        self.staged_count = [torch.zeros((B * Hkv,), dtype=torch.int32, device=dev)
+                             for _ in range(self.L)]
+        self.out = torch.empty((self.L, B, 1, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((self.L, B, 1, Hq), dtype=torch.float32, device=dev)
+        ws = attn_workspace_size("per_kv_head", B, 1, Hq, Hkv, d, n_tokens, kk, block_size, n_sink,
+                                 n_recent)
+        self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.copy_stream = torch.cuda.Stream(device=dev)
+        self.pool_keys = pool_keys
+
+    def pool(self, preds):
+        """Pool every layer's complete blocks (from the keys of every row) into its selection."""
+        for l, d_l in enumerate(self.sel):
+            sparse_index_score("block_raw", preds[l], self.pool_keys[l], self.n_tokens, self.bs,
+                               scores=d_l.scores, pooled_out=d_l.kpool)
+
+    def _attend(self, l: int, q: torch.Tensor, loc: torch.Tensor, stream):
+        k, v, kh, vh, _ = self.layers[l]
+        d_l = self.sel[l]
+        sparse_decode_attn(q, k, v, d_l.idx, d_l.count, "per_kv_head", self.n_tokens, gran=self.bs,
+                           n_sink=self.n_sink, n_recent=self.n_recent, sm_scale=self.sm_scale,
+                           k_host=kh, v_host=vh, loc=loc, out=self.out[l], lse=self.lse[l],
+                           ws=self.ws, stream=stream)
+
+    def _prefetch(self, l: int, stream):
+        k, v, kh, vh, home = self.layers[l]
+        d_l = self.sel[l]
+        lookahead_prefetch(d_l.idx, d_l.count, self.bs, self.n_tokens, kh, vh, k, v,
+                           self.stage_base, home, self.loc[l], self.staged[l],
+                           self.staged_count[l], self.workgroups, stream=stream)
+
+    def step(self, qs, preds, stream=None):
+        """One decode step through every layer.  qs / preds: per layer ``[B, 1, Hq, d]`` and
+        ``[B, 1, Hkv, d]``."""
+        s1 = torch.cuda.current_stream() if stream is None else stream
+        if not self.lookahead:
+            with torch.cuda.stream(s1):
+                for l in range(self.L):
+                    self.sel[l].select(preds[l])
+                    self._attend(l, qs[l], self.layers[l][4], s1)
+            return self.out, self.lse
+        s2 = self.copy_stream
+        with torch.cuda.stream(s1):
+            self.sel[0].select(preds[0])
+        done = []
+        s2.wait_stream(s1)
+        self._prefetch(0, s2)
+        e = torch.cuda.Event()
+        e.record(s2)
+        done.append(e)
+        for l in range(self.L):
+            if l + 1 < self.L:
+                with torch.cuda.stream(s1):
+                    self.sel[l + 1].select(preds[l + 1])      # layer l+1's blocks, ahead of time
+                s2.wait_stream(s1)
+                self._prefetch(l + 1, s2)                     # overlaps layer l's attention
+                e = torch.cuda.Event()
+                e.record(s2)
+                done.append(e)
+            s1.wait_event(done[l])
+            self._attend(l, qs[l], self.loc[l], s1)
         return self.out, self.lse

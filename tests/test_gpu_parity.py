@@ -15,7 +15,8 @@ import torch
 import oracle
 from oracle import steps as osteps
 import sparse_top_kv_gqa_amd as spk
-from sparse_top_kv_gqa_amd.decode import BlockSparseDecode, TieredDecode, TokenSparseDecode
+from sparse_top_kv_gqa_amd.decode import (BlockLookaheadDecode, BlockSparseDecode, TieredDecode,
+                                          TokenSparseDecode)
 import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -1482,3 +1483,121 @@ def test_union_decode_matches_assembled_path(which):
                     o_ref, l_ref, _ = oracle.attend(qh[b, t, hq:hq + 1], kh[b, h][sel], vh[b, h][sel],
                                                     scale)
                     check_attn(ou.cpu().numpy()[b, t, hq:hq + 1], o_ref, what=f"union {which}")
+
+
+# ------------------------------------------------------------------------------------ lookahead
+
+def _lookahead_layers(w, dev=DEV):
+    """Per layer: full HBM caches (the reference), then the hierarchy the lookahead runner uses:
+    HBM caches with staging rows whose host-block rows are NaN, pinned host pools with those
+    rows, and each row's home location."""
+    bs, kb = w.block_size, w.k
+    full, layers = [], []
+    for l in range(w.layers):
+        kf = W.kv_cache(w, "k", layer=l, device=dev)
+        vf = W.kv_cache(w, "v", layer=l, device=dev)
+        full.append((kf, vf))
+        home = torch.arange(w.N, dtype=torch.int32).repeat(w.B, w.Hkv, 1)
+        per_group = []
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                blks = W.host_blocks(w, b, h, l)
+                rows = (blks[:, None] * bs + torch.arange(bs)).reshape(-1)
+                home[b, h, rows] = ~torch.arange(rows.numel(), dtype=torch.int32)
+                per_group.append(rows)
+        nh = max(1, max(r.numel() for r in per_group))
+        kh = torch.zeros((w.B, w.Hkv, nh, w.d), dtype=torch.bfloat16, pin_memory=True)
+        vh = torch.zeros_like(kh).pin_memory()
+        k = torch.zeros((w.B, w.Hkv, w.N + kb * bs, w.d), dtype=torch.bfloat16, device=dev)
+        v = torch.zeros_like(k)
+        k[:, :, :w.N] = kf
+        v[:, :, :w.N] = vf
+        i = 0
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                rows = per_group[i]
+                i += 1
+                if rows.numel():
+                    kh[b, h, :rows.numel()].copy_(kf[b, h, rows.to(dev)].cpu())
+                    vh[b, h, :rows.numel()].copy_(vf[b, h, rows.to(dev)].cpu())
+                    k[b, h, rows.to(dev)] = float("nan")
+                    v[b, h, rows.to(dev)] = float("nan")
+        layers.append((k, v, kh, vh, home.to(dev)))
+    return full, layers
+
+
+def test_lookahead_prefetch_matches_all_hbm_and_oracle():
+    """Lookahead selection with the persistent copy kernel: over three steps (each restores the
+    one before's redirections) the locations are home but for the rows just staged, whose
+    staging rows hold them exactly; the outputs of every layer are bit-identical to the all-HBM
+    run and to the run that reads host rows inside the attention, and match the oracle; host
+    blocks were actually selected and staged."""
+    w = W.scaled(W.LOOKAHEAD_BLOCK, B=2, Hkv=2, Hq=8, N=64 * 60 + 5, k=6, n_recent=64, layers=3,
+                 host_frac=0.3)
+    say("lookahead", w.name)
+    full, layers = _lookahead_layers(w)
+    pool_keys = [kf for kf, _ in full]
+    la = BlockLookaheadDecode(layers, pool_keys, w.N, w.Hq, w.block_size, w.k, w.n_sink,
+                              w.n_recent, lookahead=True, workgroups=3)   # fewer than the groups
+    no = BlockLookaheadDecode(layers, pool_keys, w.N, w.Hq, w.block_size, w.k, w.n_sink,
+                              w.n_recent, lookahead=False)
+    refs = [BlockSparseDecode(kf, vf, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent,
+                              topk_in_attn=False) for kf, vf in full]
+    preds0 = [W.predictors(w, step=0, layer=l, device=DEV) for l in range(w.layers)]
+    la.pool(preds0)
+    no.pool(preds0)
+    for r, p in zip(refs, preds0):
+        r.pool(p)
+    G, scale = w.G, oracle.softmax_scale(w.d)
+    staged_any = 0
+    for step in (1, 2, 3):
+        qs = [W.queries(w, step=step, layer=l, device=DEV) for l in range(w.layers)]
+        preds = [W.predictors(w, step=step, layer=l, device=DEV) for l in range(w.layers)]
+        out_la, lse_la = la.step(qs, preds)
+        out_la, lse_la = out_la.clone(), lse_la.clone()
+        out_no, lse_no = no.step(qs, preds)
+        torch.cuda.synchronize()
+        staged_any += sum(int(c.sum()) for c in la.staged_count)
+        # the locations: home everywhere but the rows this step redirected (the previous step's
+        # went back home), which point to staging rows holding exactly the row
+        for l in range(w.layers):
+            k_l, v_l = layers[l][0], layers[l][1]
+            home, loc = layers[l][4].cpu(), la.loc[l].cpu()
+            cnt, st = la.staged_count[l].cpu(), la.staged[l].cpu()
+            for g in range(w.B * w.Hkv):
+                b, h = divmod(g, w.Hkv)
+                toks = st[g, :int(cnt[g])].long()
+                assert toks.unique().numel() == toks.numel()
+                assert (home[b, h, toks] < 0).all()
+                moved = torch.nonzero(loc[b, h] != home[b, h]).reshape(-1)
+                assert sorted(moved.tolist()) == sorted(toks.tolist()), (step, l, g)
+                dst = loc[b, h, toks].long().to(DEV)
+                assert ((dst >= w.N) & (dst < k_l.shape[2])).all()
+                td = toks.to(DEV)
+                assert torch.equal(k_l[b, h, dst], full[l][0][b, h, td])
+                assert torch.equal(v_l[b, h, dst], full[l][1][b, h, td])
+        for l in range(w.layers):
+            o_ref, l_ref = refs[l].step(qs[l], preds[l])
+            torch.cuda.synchronize()
+            assert torch.equal(la.sel[l].idx, refs[l].idx)
+            assert torch.isfinite(out_la[l]).all()
+            assert torch.equal(out_la[l], o_ref) and torch.equal(lse_la[l], l_ref), (step, l)
+            assert torch.equal(out_no[l], o_ref) and torch.equal(lse_no[l], l_ref), (step, l)
+        # the oracle's lookahead composition on every group
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                res = osteps.block_layers(
+                    [host(preds[l])[b, 0, h] for l in range(w.layers)],
+                    [host(full[l][0][b, h]) for l in range(w.layers)],
+                    [host(full[l][1][b, h]) for l in range(w.layers)],
+                    [host(qs[l])[b, 0, h * G:(h + 1) * G] for l in range(w.layers)],
+                    w.k, w.block_size, w.n_sink, w.n_recent, scale)
+                for l in range(w.layers):
+                    sc = la.sel[l].scores.cpu().numpy()[b, 0, h]
+                    sel = la.sel[l].idx.cpu().numpy()[b, 0, h]
+                    assert sel.tolist() == oracle.topk(sc, w.k).tolist()
+                    assert osteps.topk_band_ok(sel, res[l]["scores"], w.k, TOL)
+                    if sel.tolist() == res[l]["blocks"].tolist():
+                        check_attn(out_la[l].cpu().numpy()[b, 0, h * G:(h + 1) * G], res[l]["out"],
+                                   what=f"lookahead layer {l}")
+    assert staged_any > 0, "no host block was selected: the case does not exercise the copy"

@@ -606,3 +606,42 @@ def test_attention_regression_bound_from_the_arithmetic(rows):
     assert e_split < steps.ATTN_REGRESSION_BOUND / 10
     assert steps.ATTN_REGRESSION_BOUND * 10 < e_trap
     assert steps.TOL / 2 < e_trap < steps.TOL * 2
+
+
+def test_block_layers_lookahead_composition():
+    """The lookahead composition of the block step over layers: one layer is the block step
+    itself; a layer's selection depends only on its own predictor and keys (changing another
+    layer's queries, keys or values leaves it unchanged); identical layers give identical
+    results; and with every block selected each layer is dense attention over its rows."""
+    r = np.random.default_rng(77)
+    L, n, d, G, bs = 3, 64 * 12 + 5, 16, 2, 64
+    keys = r.standard_normal((L, n, d))
+    vals = r.standard_normal((L, n, d))
+    preds = r.standard_normal((L, d))
+    qs = r.standard_normal((L, G, d))
+    scale = 0.25
+    res = steps.block_layers(preds, keys, vals, qs, 3, bs, 2, 20, scale)
+    one = steps.block_group(preds[1], keys[1], vals[1], qs[1], 3, bs, 2, 20, scale)
+    assert res[1]["blocks"].tolist() == one["blocks"].tolist()
+    np.testing.assert_array_equal(res[1]["out"], one["out"])
+    # layer 2's selection ignores layer 1's queries, keys and values
+    k2, v2, q2 = keys.copy(), vals.copy(), qs.copy()
+    k2[1] += 5.0
+    v2[1] *= -1.0
+    q2[1] = r.standard_normal((G, d))
+    res2 = steps.block_layers(preds, k2, v2, q2, 3, bs, 2, 20, scale)
+    assert res2[2]["blocks"].tolist() == res[2]["blocks"].tolist()
+    np.testing.assert_array_equal(res2[2]["out"], res[2]["out"])
+    assert res2[1]["blocks"].tolist() != res[1]["blocks"].tolist() or \
+        not np.allclose(res2[1]["out"], res[1]["out"])
+    # identical layers
+    same = steps.block_layers(np.stack([preds[0]] * L), np.stack([keys[0]] * L),
+                              np.stack([vals[0]] * L), np.stack([qs[0]] * L), 3, bs, 2, 20, scale)
+    for l in range(1, L):
+        np.testing.assert_array_equal(same[l]["out"], same[0]["out"])
+    # every complete block selected: dense attention over all rows of each layer
+    nb = n // bs
+    full = steps.block_layers(preds, keys, vals, qs, nb, bs, 0, n - nb * bs, scale)
+    for l in range(L):
+        o, _, _ = oracle.attend(qs[l], keys[l], vals[l], scale)
+        np.testing.assert_allclose(full[l]["out"], o, rtol=1e-12, atol=1e-12)

@@ -109,8 +109,17 @@ REASONING_TIERS = Workload("tiers_b32_l28_h28x4_n4k_to_16k", B=32, T=1, Hq=28, H
                            k=0, n_sink=4, n_recent=512, layers=28, n_start=4096,
                            grow_per_step=192, steps=64)
 
+# The block layer over 8 layers with a few blocks of every (group, layer) living only in pinned
+# host memory: host_frac is the fraction of the eligible blocks (complete blocks other than
+# block 0 and those reaching into the recent window) that are host-resident, chosen so that about
+# 1.4 % of the selected rows are host rows.
+LOOKAHEAD_BLOCK = Workload("llama3_8b_b8_n32k_block64_top32_l8_hostblocks",
+                           B=8, T=1, Hq=32, Hkv=8, d=128, N=32768, kv_dtype="bf16",
+                           index_mode="block_pooled", scope="per_kv_head", k=32, block_size=64,
+                           n_sink=4, n_recent=512, layers=8, host_frac=0.018)
+
 ALL = {w.name: w for w in (TINY, LLAMA8B_BLOCK, LLAMA8B_BLOCK_WIN, PER_HEAD_2PCT, SPEC_VERIFY,
-                           REASONING_TIERS)}
+                           REASONING_TIERS, LOOKAHEAD_BLOCK)}
 
 
 def scaled(w: Workload, **changes) -> Workload:
@@ -194,6 +203,18 @@ def host_rows(w: Workload, b: int, h: int, candidates: torch.Tensor) -> torch.Te
     n_host = int(round(w.host_frac * n))
     perm = torch.randperm(n, generator=_gen("cpu", w.name, "host", b, h), device="cpu")
     return candidates.cpu()[perm[:n_host]].sort().values
+
+
+def host_blocks(w: Workload, b: int, h: int, layer: int = 0) -> torch.Tensor:
+    """Block ids of group (b, h) in layer ``layer`` that live only in pinned host memory: exactly
+    round(host_frac * eligible) of the eligible blocks [1, (N - n_recent) // block_size - 1),
+    chosen by a seeded permutation, ascending."""
+    bs = w.block_size
+    n_elig = max(0, (w.N - w.n_recent) // bs - 1)
+    n_host = int(round(w.host_frac * n_elig))
+    perm = torch.randperm(n_elig, generator=_gen("cpu", w.name, "hostblk", b, h, layer),
+                          device="cpu")
+    return (perm[:n_host] + 1).sort().values
 
 
 def bf16_bits(t: torch.Tensor):
