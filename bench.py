@@ -35,7 +35,11 @@ Workloads:
   tiers_offload  the same episode with every row in pinned host memory and --hbm-rows slots
                per sequence in HBM (default 8192): every --reassign-every steps (default 8) the
                resident set is recomputed and only newly resident rows are copied over PCIe;
-               the attention reads the other selected rows from host memory.
+               the attention reads the other selected rows from host memory.  Timed with the
+               copies before the first layer and overlapped layer by layer with the attention.
+  tiers_offload_32k  the offload episode at batch 8 growing 8192 -> 32768 tokens, 16384 HBM
+               slots per sequence; every step's outputs are checked bit for bit against the
+               same episode with every row in HBM.
 
 Prints ONE JSON line.  `value` is the step's algorithmic bytes (index keys read + selected K/V
 rows) per second; `roofline` reports the dominant kernel against the 8 TB/s HBM peak with its
@@ -66,9 +70,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="all",
                     choices=["all", "block", "block_windowed", "per_head", "spec_verify", "tiers",
-                             "tiers_offload", "block_lookahead"])
-    ap.add_argument("--hbm-rows", type=int, default=8192,
-                    help="tiers_offload: HBM slots per sequence (the rest stays in host memory)")
+                             "tiers_offload", "tiers_offload_32k", "block_lookahead"])
+    ap.add_argument("--hbm-rows", type=int, default=None,
+                    help="tiers_offload: HBM slots per sequence (the rest stays in host memory; "
+                         "default half the final context)")
     ap.add_argument("--reassign-every", type=int, default=8,
                     help="tiers_offload: tiered steps between residency reassignments")
     ap.add_argument("--layers", type=int, default=8, help="block: layer caches to rotate")
@@ -808,71 +813,103 @@ def bench_tiers(args):
     return res, ctx
 
 
-def bench_tiers_offload(args):
+def bench_tiers_offload(args, w=None, check_identity=False):
     """The tiered episode with the memory hierarchy: every row lives in pinned host memory
     (the DDR tier), HBM holds HBM_ROWS slots per sequence; every REASSIGN tiered steps the
     resident set is recomputed (T0, then the most important T1 rows while slots remain) and
     only rows that newly need a slot are copied host -> HBM.  The attention reads every other
     selected row over PCIe.  Rows appended since the last reassignment have no slot yet and are
-    read from host memory until the next one."""
+    read from host memory until the next one.  The episode is timed twice: with the copies of
+    a reassignment done before the first layer, and overlapped layer by layer with the
+    attention on a second stream.  check_identity: the warm-up episode runs beside the same
+    episode with every row in HBM, and every step's outputs, lse and the importance state must
+    match bit for bit (Proposition 1)."""
     import workloads as W
     import sparse_top_kv_gqa_amd as spk
     from sparse_top_kv_gqa_amd.decode import TieredDecode
 
-    w = W.REASONING_TIERS
+    w = W.REASONING_TIERS if w is None else w
     steps = w.steps
     K = args.steps or steps
-    cap, every = args.hbm_rows, args.reassign_every
+    cap, every = (args.hbm_rows or w.N // 2), args.reassign_every
     log(f"generating {w.layers} layer caches of {w.name} into pinned host memory")
-    host_pools, hbm = [], []
+    host_pools, hbm, full = [], [], []
     for l in range(w.layers):
-        pair = []
+        pair, fpair = [], []
         for which in ("k", "v"):
             t = W.kv_cache(w, which, l, "cuda", n_cap=w.N)
             h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
             h.copy_(t)
             pair.append(h)
+            if check_identity:
+                fpair.append(t)
             del t
         host_pools.append(tuple(pair))
+        full.append(tuple(fpair))
         hbm.append((torch.zeros((w.B, w.Hkv, cap, w.d), dtype=torch.bfloat16, device="cuda"),
                     torch.zeros((w.B, w.Hkv, cap, w.d), dtype=torch.bfloat16, device="cuda")))
     torch.cuda.synchronize()
     qs = [[W.queries(w, step=t, layer=l, device="cuda") for l in range(w.layers)]
           for t in range(steps)]
-    dec = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
-                       host_caches=host_pools, hbm_rows=cap, reassign_every=every)
+    mk = dict(host_caches=host_pools, hbm_rows=cap, reassign_every=every)
+    dec = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille, **mk)
+    dec_ov = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
+                          overlap_prefetch=True, **mk)
+    ref = (TieredDecode(full, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille)
+           if check_identity else None)
     n_at = [w.n_start + w.grow_per_step * (t + 1) for t in range(steps)]
     n_steps = min(K, steps)
     stream = torch.cuda.Stream()
 
-    def run_episode(record=None):
-        dec.s.zero_()
-        dec.evicted.zero_()
-        dec.loc.copy_(~torch.arange(w.N, dtype=torch.int32, device="cuda").repeat(w.B, 1))
-        dec.tiered_steps = 0
-        dec.copies.zero_()
+    def reset(d):
+        d.s.zero_()
+        d.evicted.zero_()
+        if d.host is not None:
+            d.loc.copy_(~torch.arange(w.N, dtype=torch.int32, device="cuda").repeat(w.B, 1))
+            d.tiered_steps = 0
+            d.copies.zero_()
+
+    def run_episode(d, record=None):
+        reset(d)
+        if ref is not None and record is not None:
+            reset(ref)
         for t in range(n_steps):
-            dec.step(qs[t], n_at[t], dense=(t == 0))
+            d.step(qs[t], n_at[t], dense=(t == 0))
             if record is not None:
-                sel = dec.dense_idx if t == 0 else dec.sel
-                m = torch.arange(w.N, device="cuda")[None, :] < dec.count[:, None].long()
+                sel = d.dense_idx if t == 0 else d.sel
+                m = torch.arange(w.N, device="cuda")[None, :] < d.count[:, None].long()
                 ids = sel.long().clamp(0, w.N - 1)     # entries past the count are unused
-                host_rows = ((torch.gather(dec.loc, 1, ids) < 0) & m).sum()
-                record.append((int(dec.count.sum()), int(host_rows), int(dec.copies)))
+                host_rows = ((torch.gather(d.loc, 1, ids) < 0) & m).sum()
+                record.append((int(d.count.sum()), int(host_rows), int(d.copies)))
+                if ref is not None:
+                    ref.step(qs[t], n_at[t], dense=(t == 0))
+                    assert torch.equal(d.out, ref.out) and torch.equal(d.lse, ref.lse), \
+                        f"offload step {t} differs from the all-HBM step"
+                    assert torch.equal(d.s, ref.s), f"importance after step {t} differs"
 
     rec = []
     with torch.cuda.stream(stream):
-        run_episode(rec)            # warm-up episode: rows read, rows read from host, copies
+        run_episode(dec, rec)       # warm-up episode: rows read, rows read from host, copies
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        run_episode()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    ms_total = e0.elapsed_time(e1)
+
+        def timed(d):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            run_episode(d)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1), time.perf_counter() - t0
+        ms_total, wall = timed(dec)
+        run_episode(dec_ov)         # warm-up of the overlapped variant
+        s_seq = dec.s.clone()
+        ms_total_ov, _ = timed(dec_ov)
+        assert torch.equal(dec_ov.s, s_seq) and torch.equal(dec_ov.out, dec.out), \
+            "overlapped prefetch changed a result"
+    if ref is not None:
+        del ref
+        full.clear()
     ms_step = ms_total / n_steps
     per_layer = w.Hkv * w.layers * ROW_BYTES
     sel_bytes = [r * per_layer for r, _, _ in rec]
@@ -896,7 +933,10 @@ def bench_tiers_offload(args):
         "kv_heads": w.Hkv, "head_dim": w.d, "context_start": w.n_start,
         "context_end": n_last, "grow_per_step": w.grow_per_step, "decode_steps": n_steps,
         "hbm_rows_per_sequence": cap, "reassign_every": every,
+        "ms_per_step_prefetch_overlapped": round(ms_total_ov / n_steps, 5),
+        "bit_identical_to_all_hbm_every_step": bool(check_identity),
         "bytes_per_step_avg": int(bytes_avg),
+        "pcie_share_of_step_bytes": round((pcie_attn + pcie_copy) / max(1, sum(sel_bytes)), 4),
         "host_fetch_fraction": round(sum(h for _, h, _ in rec) / max(1, sum(r for r, _, _ in rec)), 4),
         "pcie_attention_bytes_per_step": int(pcie_attn / n_steps),
         "prefetch_bytes_episode": int(pcie_copy), "rows_copied_episode": copies,
@@ -1089,7 +1129,7 @@ def cpu_tiers(ctx, seconds):
 
 HEADLINE = "per_head"
 ORDER = ["per_head", "block", "block_windowed", "spec_verify", "tiers", "tiers_offload",
-         "block_lookahead"]
+         "tiers_offload_32k", "block_lookahead"]
 
 
 def run_workload(name, args):
@@ -1103,6 +1143,10 @@ def run_workload(name, args):
         cpu = cpu_token
     elif name == "tiers_offload":
         res, ctx = bench_tiers_offload(args)
+        cpu = cpu_tiers
+    elif name == "tiers_offload_32k":
+        import workloads as W
+        res, ctx = bench_tiers_offload(args, W.REASONING_TIERS_32K, check_identity=True)
         cpu = cpu_tiers
     elif name == "block_lookahead":
         res, ctx = bench_lookahead(args)

@@ -569,9 +569,11 @@ SPK_API spk_status tier_classify(const float* s, int64_t s_ld, int B, int n_toke
  *              from host memory).  Entries >= n_tokens are not touched.
  *   copy_tok, copy_slot  device int32 [B,copy_ld]: the r-th newly resident row and its slot,
  *              r < min(copy_count[b], copy_ld) (copy_ld >= capacity lists every copy).
- *   copy_count device int32 [B]: number of newly resident rows.
- * Limits: n_tokens and capacity at most 16384 (SPK_EUNSUPPORTED).  One launch, one workgroup
- * per sequence; no workspace.
+ *   copy_count device int32 [B]: number of rows listed for the copy (the newly resident rows
+ *              that received a slot: all of them when the slots held on entry are distinct).
+ * Limits: n_tokens below 2^30 and capacity at most 131072 (SPK_EUNSUPPORTED).  Sequences of up
+ * to 16384 tokens (with capacity <= 16384) keep their tokens in registers; longer ones are read
+ * from memory chunk by chunk.  One launch, one workgroup per sequence; no workspace.
  * ------------------------------------------------------------------------------------------ */
 SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier_ld,
                                     const float* s, int64_t s_ld, int B, int n_tokens,

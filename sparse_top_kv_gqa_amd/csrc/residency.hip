@@ -22,6 +22,13 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kItems = 16;                        // tokens per thread: n_tokens <= 16384
 constexpr int kMaxTokens = kItems * kThreads;
 constexpr int kSlotWords = kMaxTokens / 32;       // slot bitmap: capacity <= 16384
+// Longer sequences: tokens are taken chunk by chunk from memory, the slot bitmap covers up to
+// 131072 slots (16 KB of LDS, and as much again for the free-slot prefixes).
+constexpr int kChunkCap = 131072;
+constexpr int kChunkWords = kChunkCap / 32;
+constexpr int kWordsPerThread = kChunkWords / kThreads;
+constexpr int kMaxTokensChunked = 1 << 30;
+constexpr int32_t kNeedsSlot = INT32_MIN;         // loc between the passes: resident, no slot yet
 
 // The k-th zero bit (k counted from 0, least significant first) of w.
 __device__ __forceinline__ int nth_zero_bit(uint32_t w, int k) {
@@ -170,7 +177,140 @@ __global__ __launch_bounds__(kThreads) void residency_kernel(
       loc[i] = ~i;  // no slot left (only when loc held a slot twice): read from host memory
     }
   }
-  if (tid == 0) copy_count[b] = run;
+  if (tid == 0) copy_count[b] = min(run, tot_free);  // the copies listed
+}
+
+// The same policy for sequences longer than the register path holds: the tokens' tiers and
+// importance are read from memory on every pass (counts, each radix pass, the two index-order
+// passes), and between the passes a resident row that still needs a slot is marked in loc
+// itself (kNeedsSlot; every other value is a slot >= 0 or ~tok), so no workspace is needed.
+// Each thread handles the same tokens in both passes.
+__global__ __launch_bounds__(kThreads) void residency_chunked_kernel(
+    const uint8_t* __restrict__ tier_all, int64_t tier_ld, const float* __restrict__ s_all,
+    int64_t s_ld, int n, int capacity, int32_t* __restrict__ loc_all, int64_t loc_ld,
+    int32_t* __restrict__ copy_tok, int32_t* __restrict__ copy_slot, int64_t copy_ld,
+    int32_t* __restrict__ copy_count) {
+  __shared__ __align__(16) uint32_t hist[4 * 256];
+  __shared__ uint32_t held_bits[kChunkWords];
+  __shared__ int free_pre[kChunkWords + 1];  // free slots before each bitmap word
+  __shared__ int scratch[kWaves + 1];
+  __shared__ int counts[2];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint8_t* tier = tier_all + (int64_t)b * tier_ld;
+  const float* s = s_all + (int64_t)b * s_ld;
+  int32_t* loc = loc_all + (int64_t)b * loc_ld;
+
+  int c0 = 0, c1 = 0;
+  for (int i = tid; i < n; i += kThreads) {
+    const uint8_t t = tier[i];
+    c0 += t == 0;
+    c1 += t == 1;
+  }
+  for (int i = tid; i < 4 * 256; i += kThreads) hist[i] = 0u;
+  for (int i = tid; i < kChunkWords; i += kThreads) held_bits[i] = 0u;
+  if (tid == 0) counts[0] = counts[1] = 0;
+  __syncthreads();
+  atomicAdd(&counts[0], c0);
+  atomicAdd(&counts[1], c1);
+  __syncthreads();
+  const int n0 = counts[0], n1 = counts[1];
+
+  const int cut_tier = capacity >= n0 + n1 ? -1 : (capacity >= n0 ? 1 : 0);
+  const int cut = cut_tier == 1 ? capacity - n0 : (cut_tier == 0 ? capacity : 0);
+  uint32_t thr = 0;
+  int need = 0;
+  bool whole = false;
+  if (cut > 0) {
+    radix_threshold(
+        [&](auto visit) {
+          for (int i = tid; i < n; i += kThreads)
+            if (tier[i] == cut_tier) visit(order_key(s[i]));
+        },
+        cut, hist, &thr, &need, &whole);
+  }
+
+  // Pass A, in index order: the resident set, the slots kept rows hold, loc of non-resident
+  // rows, and the mark on resident rows that need a slot
+  const int chunks = (n + kThreads - 1) / kThreads;
+  int run_eq = 0;
+  for (int c = 0; c < chunks; ++c) {
+    const int i = c * kThreads + tid;
+    const bool valid = i < n;
+    const int t = valid ? tier[i] : 3;
+    const uint32_t key = valid ? order_key(s[i]) : 0u;
+    const bool in_cut = t == cut_tier && cut_tier >= 0;
+    const bool gt = in_cut && cut > 0 && (whole ? key >= thr : key > thr);
+    const bool eq = in_cut && cut > 0 && !whole && key == thr;
+    int tot_eq;
+    const int pre = block_excl_scan(eq ? 1 : 0, scratch, &tot_eq);
+    const bool kept_cut = gt || (eq && run_eq + pre < need);
+    run_eq += tot_eq;
+    bool res;
+    if (cut_tier < 0) res = t <= 1;
+    else if (cut_tier == 1) res = t == 0 || kept_cut;
+    else res = kept_cut;
+    if (valid) {
+      const int old = loc[i];
+      const bool held = res && old >= 0 && old < capacity;
+      if (held) atomicOr(&held_bits[old >> 5], 1u << (old & 31));
+      if (!res) loc[i] = ~i;
+      else if (!held) loc[i] = kNeedsSlot;
+    }
+  }
+  __syncthreads();
+  // free slots per bitmap word (slots >= capacity are not free), then their prefix: each
+  // thread owns kWordsPerThread consecutive words
+  const int words = (capacity + 31) / 32;
+  int fz[kWordsPerThread];
+  int fsum = 0;
+#pragma unroll
+  for (int j = 0; j < kWordsPerThread; ++j) {
+    const int w = tid * kWordsPerThread + j;
+    fz[j] = 0;
+    if (w < words) {
+      const int lim = min(32, capacity - w * 32);
+      const uint32_t valid = lim == 32 ? 0xFFFFFFFFu : ((1u << lim) - 1u);
+      fz[j] = __popc(~held_bits[w] & valid);
+    }
+    fsum += fz[j];
+  }
+  int tot_free;
+  int fp = block_excl_scan(fsum, scratch, &tot_free);
+#pragma unroll
+  for (int j = 0; j < kWordsPerThread; ++j) {
+    free_pre[tid * kWordsPerThread + j] = fp;
+    fp += fz[j];
+  }
+  if (tid == 0) free_pre[kChunkWords] = tot_free;
+  __syncthreads();
+
+  // Pass B, in index order: the r-th marked row takes the r-th free slot
+  int run = 0;
+  for (int c = 0; c < chunks; ++c) {
+    const int i = c * kThreads + tid;
+    const bool f = i < n && loc[i] == kNeedsSlot;
+    int tot;
+    const int r = run + block_excl_scan(f ? 1 : 0, scratch, &tot);
+    run += tot;
+    if (f && r < tot_free) {
+      int lo = 0, hi = words;  // free_pre[lo] <= r < free_pre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (free_pre[mid] <= r) lo = mid;
+        else hi = mid;
+      }
+      const int slot = lo * 32 + nth_zero_bit(held_bits[lo], r - free_pre[lo]);
+      loc[i] = slot;
+      if (r < copy_ld) {
+        copy_tok[(int64_t)b * copy_ld + r] = i;
+        copy_slot[(int64_t)b * copy_ld + r] = slot;
+      }
+    } else if (f) {
+      loc[i] = ~i;  // no slot left (only when loc held a slot twice): read from host memory
+    }
+  }
+  if (tid == 0) copy_count[b] = min(run, tot_free);  // the copies listed
 }
 
 // Copy of newly resident rows: row copy_tok[b, r] of the host pools to slot copy_slot[b, r] of
@@ -233,9 +373,9 @@ extern "C" SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier
   using namespace spk;
   SPK_REQUIRE(B >= 0 && n_tokens >= 0 && capacity >= 0, SPK_EINVAL,
               "residency_update: negative size");
-  SPK_REQUIRE(n_tokens <= kMaxTokens && capacity <= kMaxTokens, SPK_EUNSUPPORTED,
-              "residency_update: n_tokens %d / capacity %d above %d", n_tokens, capacity,
-              kMaxTokens);
+  SPK_REQUIRE(n_tokens < kMaxTokensChunked && capacity <= kChunkCap, SPK_EUNSUPPORTED,
+              "residency_update: n_tokens %d / capacity %d: at most %d tokens and %d slots",
+              n_tokens, capacity, kMaxTokensChunked - 1, kChunkCap);
   SPK_REQUIRE(B == 0 || (tier && s && loc && copy_count), SPK_EINVAL,
               "residency_update: null tier, s, loc or copy_count");
   SPK_REQUIRE(tier_ld >= n_tokens && s_ld >= n_tokens && loc_ld >= n_tokens, SPK_EINVAL,
@@ -245,8 +385,13 @@ extern "C" SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier
   clear_error();
   if (B == 0) return SPK_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(residency_kernel, dim3(B), dim3(kThreads), 0, st, tier, tier_ld, s, s_ld,
-                     n_tokens, capacity, loc, loc_ld, copy_tok, copy_slot, copy_ld, copy_count);
+  if (n_tokens <= kMaxTokens && capacity <= kMaxTokens)
+    hipLaunchKernelGGL(residency_kernel, dim3(B), dim3(kThreads), 0, st, tier, tier_ld, s, s_ld,
+                       n_tokens, capacity, loc, loc_ld, copy_tok, copy_slot, copy_ld, copy_count);
+  else
+    hipLaunchKernelGGL(residency_chunked_kernel, dim3(B), dim3(kThreads), 0, st, tier, tier_ld, s,
+                       s_ld, n_tokens, capacity, loc, loc_ld, copy_tok, copy_slot, copy_ld,
+                       copy_count);
   return check_launch("residency_update");
 }
 

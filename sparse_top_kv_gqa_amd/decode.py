@@ -236,12 +236,16 @@ class TieredDecode:
     recomputed (T0 first, then the most important T1 rows while slots remain) and only rows
     that newly need a slot are copied host -> HBM; the attention reads every other selected
     row from the host pools over PCIe.  The results are bit-identical to the all-HBM layout.
+
+    overlap_prefetch: the copies of a reassignment run layer by layer on a second stream
+    (default priority), and each layer's attention waits only for its own layer's copy, so
+    layer l+1's copy overlaps layer l's attention.
     """
 
     def __init__(self, caches: Sequence, Hq: int, n_cap: int, n_sink: int, n_recent: int,
                  t0_permille: int = 250, t01_permille: int = 750,
                  sm_scale: Optional[float] = None, host_caches: Optional[Sequence] = None,
-                 hbm_rows: int = 0, reassign_every: int = 1):
+                 hbm_rows: int = 0, reassign_every: int = 1, overlap_prefetch: bool = False):
         self.caches = list(caches)
         k0 = self.caches[0][0]
         B, Hkv, _, d = k0.shape
@@ -274,16 +278,30 @@ class TieredDecode:
             self.copy_slot = torch.zeros((B, max(hbm_rows, 1)), dtype=torch.int32, device=dev)
             self.copy_count = torch.zeros((B,), dtype=torch.int32, device=dev)
             self.copies = torch.zeros((), dtype=torch.int64, device=dev)   # rows copied so far
+        self.overlap = overlap_prefetch and self.host is not None
+        self.copy_stream = torch.cuda.Stream(device=dev) if self.overlap else None
+        self._copied = None      # per-layer events of the pending overlapped copies
 
     def reassign(self, n_tokens: int):
         """Resident set of every sequence for the current tiers, and the differential copy of
         the rows that newly hold a slot, in every layer."""
         residency_update(self.tier, self.s, n_tokens, self.hbm_rows, self.loc, self.copy_tok,
                          self.copy_slot, self.copy_count)
+        self.copies += self.copy_count.sum()
+        if not self.overlap:
+            for (kh, vh), (k, v) in zip(self.host, self.caches):
+                residency_prefetch(kh, vh, k, v, self.copy_tok, self.copy_slot, self.copy_count,
+                                   self.hbm_rows)
+            return
+        s1, s2 = torch.cuda.current_stream(), self.copy_stream
+        s2.wait_stream(s1)            # the copy list, and the previous step's reads of the pools
+        self._copied = []
         for (kh, vh), (k, v) in zip(self.host, self.caches):
             residency_prefetch(kh, vh, k, v, self.copy_tok, self.copy_slot, self.copy_count,
-                               self.hbm_rows)
-        self.copies += self.copy_count.sum()
+                               self.hbm_rows, stream=s2)
+            e = torch.cuda.Event()
+            e.record(s2)
+            self._copied.append(e)
 
     def step(self, qs: Sequence[torch.Tensor], n_tokens: int, dense: bool = False):
         """One decode step at ``n_tokens`` cached tokens.  qs: per-layer Q ``[B, 1, Hq, d]``.
@@ -302,6 +320,8 @@ class TieredDecode:
         for l, (k, v) in enumerate(self.caches):
             if self.host is not None:
                 kh, vh = self.host[l]
+                if self._copied is not None:
+                    torch.cuda.current_stream().wait_event(self._copied[l])
                 sparse_decode_attn(qs[l], k, v, sel, self.count, "per_seq", n_tokens,
                                    sm_scale=self.sm_scale, out=self.out[l], lse=self.lse[l],
                                    logits=self.logits[l], ws=self.ws, k_host=kh, v_host=vh,
@@ -310,6 +330,7 @@ class TieredDecode:
                 sparse_decode_attn(qs[l], k, v, sel, self.count, "per_seq", n_tokens,
                                    sm_scale=self.sm_scale, out=self.out[l], lse=self.lse[l],
                                    logits=self.logits[l], ws=self.ws)
+        self._copied = None
         importance_accumulate(self.s, sel, self.count, self.logits, self.lse, n_tokens)
         return self.out, self.lse
 
@@ -326,8 +347,9 @@ class BlockLookaheadDecode:
 
     lookahead=True: layer l+1's blocks are selected on the caller's stream before layer l
     attends; a second stream (default priority) runs lookahead_prefetch, a persistent kernel of
-    ``workgroups`` workgroups (default one per (b, kvh) group), which copies the selected blocks' host rows into staging rows and
-    redirects their locations while layer l attends; layer l+1's attention waits for it.
+    ``workgroups`` workgroups (default one per (b, kvh) group), which copies the selected
+    blocks' host rows into staging rows and redirects their locations while layer l attends;
+    layer l+1's attention waits for it.
     lookahead=False: every layer selects, then attends, reading its host rows in the attention
     kernel itself.  Both give bit-identical results (the reduction order never depends on where
     a row is read from).

@@ -237,9 +237,10 @@ def test_window_entries_validation():
 
 def test_residency_validation():
     L = spk.lib()
-    # residency_update: n_tokens above the limit; loc_ld < n_tokens; null loc
-    assert L.residency_update(A, 20000, A, 20000, 1, 20000, 100, A, 20000, A, A, 100, A,
+    # residency_update: capacity above the limit; loc_ld < n_tokens; null loc
+    assert L.residency_update(A, 200000, A, 200000, 1, 200000, 131073, A, 200000, A, A, 100, A,
                               None) == 2
+    assert "131072" in _err()
     assert L.residency_update(A, 64, A, 64, 1, 64, 16, A, 32, A, A, 16, A, None) == 1
     assert "loc_ld" in _err()
     assert L.residency_update(A, 64, A, 64, 1, 64, 16, None, 64, A, A, 16, A, None) == 1

@@ -1042,10 +1042,14 @@ def _random_tiers(r, B, n, p=(0.3, 0.45, 0.25)):
 
 
 @pytest.mark.parametrize("n,cap", [(1000, 300), (1000, 1000), (5000, 700), (16384, 8192),
-                                   (16384, 16384), (777, 0), (3000, 64)])
+                                   (16384, 16384), (777, 0), (3000, 64),
+                                   # sequences past the register path: read chunk by chunk
+                                   (16385, 8192), (20000, 0), (32768, 16384), (32768, 20000),
+                                   (65536, 32768), (65536, 65536), (70001, 50000)])
 def test_residency_update_matches_oracle(n, cap):
     """Three reassignments in a row (importance and tiers change between them): resident
-    set, slots and copy list bit-exact against the oracle, from the GPU's own previous loc."""
+    set, slots and copy list bit-exact against the oracle, from the GPU's own previous loc; up
+    to 65536 tokens and beyond (the chunked path)."""
     say("residency", n, cap)
     r = np.random.default_rng(n + cap)
     B = 3
@@ -1108,6 +1112,21 @@ def test_tiered_offload_bit_identical_to_all_hbm(hbm_rows, every):
     w = W.scaled(W.REASONING_TIERS, B=3, layers=3, Hq=8, Hkv=2, N=1200, n_start=600,
                  grow_per_step=100, steps=6, n_recent=64)
     say("tiered-offload", hbm_rows, every)
+    _offload_vs_all_hbm(w, hbm_rows, every, overlap=every == 2)
+
+
+@pytest.mark.parametrize("n_end,hbm_rows", [(32768, 16384), (65536, 24576)])
+def test_tiered_offload_long_context_bit_identical_to_all_hbm(n_end, hbm_rows):
+    """The hierarchy at 32768 and 65536 tokens (tier classification and residency past their
+    register paths; 20000+ T0 ∪ T1 rows per sequence): every step bit-identical to all-HBM,
+    the second case with the copies overlapped layer by layer."""
+    w = W.scaled(W.REASONING_TIERS, B=2, layers=2, Hq=8, Hkv=2, N=n_end, n_start=n_end - 4000,
+                 grow_per_step=1000, steps=4, n_recent=512)
+    say("tiered-offload-long", n_end, hbm_rows)
+    _offload_vs_all_hbm(w, hbm_rows, 2, overlap=n_end > 32768)
+
+
+def _offload_vs_all_hbm(w, hbm_rows, every, overlap):
     caches = [(W.kv_cache(w, "k", l, DEV, n_cap=w.N), W.kv_cache(w, "v", l, DEV, n_cap=w.N))
               for l in range(w.layers)]
     host_pools = [(k.cpu().pin_memory(), v.cpu().pin_memory()) for k, v in caches]
@@ -1116,7 +1135,8 @@ def test_tiered_offload_bit_identical_to_all_hbm(hbm_rows, every):
            for _ in range(w.layers)]
     ref = TieredDecode(caches, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille)
     off = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
-                       host_caches=host_pools, hbm_rows=hbm_rows, reassign_every=every)
+                       host_caches=host_pools, hbm_rows=hbm_rows, reassign_every=every,
+                       overlap_prefetch=overlap)
     for t in range(w.steps):
         n = w.n_start + w.grow_per_step * t
         qs = [W.queries(w, step=t, layer=l, device=DEV) for l in range(w.layers)]

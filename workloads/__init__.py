@@ -109,6 +109,13 @@ REASONING_TIERS = Workload("tiers_b32_l28_h28x4_n4k_to_16k", B=32, T=1, Hq=28, H
                            k=0, n_sink=4, n_recent=512, layers=28, n_start=4096,
                            grow_per_step=192, steps=64)
 
+# The same reasoning episode at twice the context (8192 -> 32768 tokens over 64 steps) for the
+# memory hierarchy: batch 8 keeps the pinned host pools of all 28 layers at 15 GB.
+REASONING_TIERS_32K = Workload("tiers_b8_l28_h28x4_n8k_to_32k", B=8, T=1, Hq=28, Hkv=4, d=128,
+                               N=32768, kv_dtype="bf16", index_mode=None, scope="per_seq",
+                               k=0, n_sink=4, n_recent=512, layers=28, n_start=8192,
+                               grow_per_step=384, steps=64)
+
 # The block layer over 8 layers with a few blocks of every (group, layer) living only in pinned
 # host memory: host_frac is the fraction of the eligible blocks (complete blocks other than
 # block 0 and those reaching into the recent window) that are host-resident, chosen so that about
@@ -119,7 +126,7 @@ LOOKAHEAD_BLOCK = Workload("llama3_8b_b8_n32k_block64_top32_l8_hostblocks",
                            n_sink=4, n_recent=512, layers=8, host_frac=0.018)
 
 ALL = {w.name: w for w in (TINY, LLAMA8B_BLOCK, LLAMA8B_BLOCK_WIN, PER_HEAD_2PCT, SPEC_VERIFY,
-                           REASONING_TIERS, LOOKAHEAD_BLOCK)}
+                           REASONING_TIERS, REASONING_TIERS_32K, LOOKAHEAD_BLOCK)}
 
 
 def scaled(w: Workload, **changes) -> Workload:
