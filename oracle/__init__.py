@@ -17,8 +17,8 @@ Every function cites the passage it follows by page title and section:
   — §2 Metodologia "Oracle Top-K" (exact top-k tokens) and "Implementação de
   Hardware" (per-token, per-query, per-head sparsity); §3C (traffic O(k·d)).
 * "Nem Todos os Pensamentos Necessitam de HBM" — Metodologia §1 (four-tier
-  classification), §2 (cumulative importance equation), §3 (Proposition 1),
-  §4 (reassignment period Δ).
+  classification, T2 kept at 8 bits), §2 (cumulative importance equation), §3
+  (Proposition 1), §4 (reassignment period Δ).
 * "O Fim do Gargalo de Memória: ... Adaptive DHiSparse" — "Metodologia e
   Eficiência de Carga" (queries share the retrieval of missing rows), "A Inovação"
   (optional residency of rows in HBM while memory allows).
@@ -34,6 +34,9 @@ the pages' published throughput figures, which it does not model.
 """
 from .core import (  # noqa: F401
     decode_bf16,
+    encode_bf16,
+    quantize_int8,
+    dequantize_int8,
     to_f64,
     block_pool,
     window_count,

@@ -19,6 +19,17 @@ def decode_bf16(bits) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def encode_bf16(x) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns (uint16): round to nearest, ties to even (the low 16
+    bits decide, with the kept part's last bit breaking ties); a NaN stays a quiet NaN."""
+    xf = np.asarray(x, dtype=np.float32)
+    u = xf.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) & np.uint64(0xFFFF)
+    r = np.where(np.isnan(xf), ((u >> np.uint64(16)) | np.uint64(0x40)) & np.uint64(0xFFFF), r)
+    return r.astype(np.uint16)
+
+
 def to_f64(x) -> np.ndarray:
     """Exact fp64 copy of a float array, or of bf16 bit patterns given as uint16."""
     x = np.asarray(x)
@@ -209,23 +220,28 @@ def importance_update(s_prev, alpha) -> np.ndarray:
 # --------------------------------------------------------------------------- a7
 
 def tier_classify(s, n_tokens: int, n_sink: int, n_recent: int, t0_permille: int = 250,
-                  t01_permille: int = 750, evicted=None):
-    """Four-tier classification by cumulative importance (T2 not used).
+                  t01_permille: int = 750, evicted=None, t012_permille=None):
+    """Four-tier classification by cumulative importance.
 
     "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro
     Níveis": protected tokens (attention sinks, recent window) and the most
     important tokens stay in T0; middle importance goes to T1 (full precision,
-    fetched before attention); only the least important tail goes to T3
-    (evicted for good).  Readings taken:
+    fetched before attention); low importance may go to T2 (kept at reduced
+    precision); only the least important tail goes to T3 (evicted for good).
+    Readings taken:
 
     * protected = tokens [0, n_sink) and [n_tokens - n_recent, n_tokens) -> T0;
     * the M other tokens are ranked by (not evicted first, s descending, index
       ascending); rank < floor(M·t0/1000) -> T0, rank < floor(M·t01/1000) -> T1,
-      every other token -> T3;
+      rank < floor(M·t012/1000) -> T2, every other token -> T3 (t012 = t01, the
+      default, uses no T2);
     * an evicted token stays T3 whatever its rank (eviction is permanent).
 
-    Returns (tier ``[n_tokens]`` uint8 with 0/1/3, ascending int64 list of T0∪T1).
+    Returns (tier ``[n_tokens]`` uint8 with 0/1/2/3, ascending int64 list of the
+    attended rows T0 ∪ T1 ∪ T2).
     """
+    if t012_permille is None:
+        t012_permille = t01_permille
     s = np.asarray(s, dtype=np.float64)[:n_tokens]
     ev = np.zeros(n_tokens, dtype=bool) if evicted is None else \
         np.asarray(evicted, dtype=bool)[:n_tokens]
@@ -238,6 +254,7 @@ def tier_classify(s, n_tokens: int, n_sink: int, n_recent: int, t0_permille: int
     M = cand.shape[0]
     n0 = (M * t0_permille) // 1000
     n01 = (M * t01_permille) // 1000
+    n012 = (M * t012_permille) // 1000
     # sort key: live before evicted, then larger s, then lower index.  A NaN score
     # ranks with the evicted rows (after every number), by index.
     def key(i):
@@ -251,8 +268,47 @@ def tier_classify(s, n_tokens: int, n_sink: int, n_recent: int, t0_permille: int
             tier[i] = 0
         elif r < n01:
             tier[i] = 1
-    lst = np.nonzero(tier <= 1)[0].astype(np.int64)
+        elif r < n012:
+            tier[i] = 2
+    lst = np.nonzero(tier <= 2)[0].astype(np.int64)
     return tier, lst
+
+
+def quantize_int8(rows):
+    """T2 storage of K or V rows: symmetric 8-bit codes with one fp32 scale per row.
+
+    "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro Níveis" (T2:
+    low-importance rows kept on the CPU at reduced precision, for instance 8-bit quantization;
+    §4 "Sensibilidade à Precisão" reports what it costs in accuracy).  The pages name no
+    scheme; reading taken: per row (one token of one KV head, K and V separately) m is the
+    largest |x| over the row's finite elements, scale = fp32(m / 127), and every element gets
+    the code rint(fp32(x · fp32(127 / m))) (ties to even) clamped to [-127, 127]; a non-finite
+    element gets code 0; a row with m = 0 gets codes 0 and scale 0.  The fp32 quotients and
+    products decide integers, so they are taken in fp32, as the kernel takes them.
+
+    rows: ``[..., d]`` values (float, or bf16 bit patterns as uint16).
+    Returns (codes int8 ``[..., d]``, scale fp32 ``[...]``).
+    """
+    x = np.asarray(rows)
+    x = decode_bf16(x).astype(np.float32) if x.dtype == np.uint16 else x.astype(np.float32)
+    fin = np.isfinite(x)
+    a = np.where(fin, np.abs(x), np.float32(0)).astype(np.float32)
+    m = a.max(axis=-1) if x.shape[-1] else np.zeros(x.shape[:-1], np.float32)
+    pos = m > 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        scale = np.where(pos, m / np.float32(127), np.float32(0)).astype(np.float32)
+        inv = np.where(pos, np.float32(127) / m, np.float32(0)).astype(np.float32)
+        y = (x * inv[..., None]).astype(np.float32)
+    c = np.clip(np.rint(np.where(fin, y, np.float32(0))), -127, 127)
+    return c.astype(np.int8), scale
+
+
+def dequantize_int8(codes, scale) -> np.ndarray:
+    """A T2 row as the attention reads it: fp32(code · scale), rounded to bf16 (ties to even),
+    the dtype of the cache it stands in for.  Returns bf16 bit patterns (uint16)."""
+    c = np.asarray(codes).astype(np.float32)
+    sc = np.asarray(scale, dtype=np.float32)[..., None]
+    return encode_bf16((c * sc).astype(np.float32))
 
 
 def residency_update(tier, s, loc_old, n_tokens: int, capacity: int):

@@ -7,8 +7,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .core import (attend, block_pool, importance_update, scores_block, scores_block_windowed,
-                   window_pool,
+from .core import (attend, block_pool, decode_bf16, dequantize_int8, importance_update,
+                   quantize_int8, scores_block, scores_block_windowed, window_pool,
                    scores_token_group_mean, scores_token_per_head, selection_tokens,
                    tier_classify, to_f64, topk)
 
@@ -113,15 +113,17 @@ def per_head_group(q_group, keys, vals, k, sm_scale):
 
 
 def tiered_sequence_step(s_prev, evicted, q_layers, k_layers, v_layers, n_tokens, sm_scale,
-                         n_sink, n_recent, t0_permille=250, t01_permille=750, dense=False):
+                         n_sink, n_recent, t0_permille=250, t01_permille=750, dense=False,
+                         t012_permille=None):
     """One decode step of one sequence under the tiered KV hierarchy.
 
     "Nem Todos os Pensamentos Necessitam de HBM": classify tokens into tiers by the
-    importance of the previous step (§1), attend exactly over T0 ∪ T1 in every
-    layer and head (T1 rows come back at full precision, §3), then add this step's
-    attention, averaged over layers and heads, to the importance (§2).
+    importance of the previous step (§1), attend exactly over T0 ∪ T1 ∪ T2 in every
+    layer and head (T1 rows come back at full precision, §3; T2 rows are read from
+    their 8-bit copy, ``core.quantize_int8`` then ``core.dequantize_int8``, §1), then
+    add this step's attention, averaged over layers and heads, to the importance (§2).
     ``dense=True`` is the first step, before any importance exists: attend over
-    every token and classify nothing.
+    every token and classify nothing.  ``t012_permille`` None: no T2.
 
     q_layers ``[L, Hq, d]``; k_layers / v_layers ``[L, Hkv, >=n_tokens, d]``;
     ``s_prev`` fp32 ``[>=n_tokens]``; ``evicted`` bool ``[>=n_tokens]`` or None.
@@ -139,14 +141,22 @@ def tiered_sequence_step(s_prev, evicted, q_layers, k_layers, v_layers, n_tokens
         toks = np.arange(n_tokens, dtype=np.int64)
     else:
         tier, toks = tier_classify(s_prev, n_tokens, n_sink, n_recent, t0_permille,
-                                   t01_permille, ev)
+                                   t01_permille, ev, t012_permille)
+    t2 = tier[toks] == 2                    # attended rows read from their 8-bit copy
     alpha = np.zeros((L, Hq, n_tokens))
     outs = np.zeros((L, Hq, q.shape[2]))
     lses = np.zeros((L, Hq))
+
+    def rows(src):
+        x = np.asarray(src)[:n_tokens][toks]
+        f = to_f64(x)
+        if t2.any():
+            f[t2] = decode_bf16(dequantize_int8(*quantize_int8(x[t2])))
+        return f
     for l in range(L):
         for kvh in range(Hkv):
-            kf = to_f64(np.asarray(k_layers[l, kvh])[:n_tokens])[toks]
-            vf = to_f64(np.asarray(v_layers[l, kvh])[:n_tokens])[toks]
+            kf = rows(k_layers[l, kvh])
+            vf = rows(v_layers[l, kvh])
             out, lse, logits = attend(q[l, kvh * G:(kvh + 1) * G], kf, vf, sm_scale)
             outs[l, kvh * G:(kvh + 1) * G] = out
             lses[l, kvh * G:(kvh + 1) * G] = lse

@@ -278,11 +278,12 @@ def test_importance_conservation_and_identical_keys_closed_form():
 
 # ------------------------------------------------------------------ tiers
 
-def _brute_tiers(s, n, n_sink, n_recent, p0, p01, ev):
+def _brute_tiers(s, n, n_sink, n_recent, p0, p01, ev, p012=None):
     prot = [i < n_sink or i >= n - n_recent for i in range(n)]
     cand = [i for i in range(n) if not prot[i]]
     M = len(cand)
     n0, n01 = M * p0 // 1000, M * p01 // 1000
+    n012 = M * (p01 if p012 is None else p012) // 1000
 
     def before(j, i):  # j ranks ahead of i
         if ev[j] != ev[i]:
@@ -297,24 +298,27 @@ def _brute_tiers(s, n, n_sink, n_recent, p0, p01, ev):
             tier.append(0)
             continue
         r = sum(before(j, i) for j in cand if j != i)
-        if ev[i] or r >= n01:
+        if ev[i] or r >= n012:
             tier.append(3)
         else:
-            tier.append(0 if r < n0 else 1)
+            tier.append(0 if r < n0 else (1 if r < n01 else 2))
     return tier
 
 
-@pytest.mark.parametrize("trial", range(30))
+@pytest.mark.parametrize("trial", range(40))
 def test_tiers_brute_force(trial):
     r = np.random.default_rng(100 + trial)
     n = int(r.integers(0, 60))
     n_sink, n_recent = int(r.integers(0, 5)), int(r.integers(0, 12))
     s = r.integers(0, 6, size=n).astype(np.float32) / 4          # ties on purpose
     ev = r.random(n) < (0.3 if trial % 2 else 0.0)
-    p0, p01 = [(250, 750), (100, 900), (0, 1000), (500, 500)][trial % 4]
-    tier, lst = oracle.tier_classify(s, n, n_sink, n_recent, p0, p01, ev)
-    assert tier.tolist() == _brute_tiers(list(s), n, n_sink, n_recent, p0, p01, list(ev))
-    assert lst.tolist() == [i for i in range(n) if tier[i] <= 1]
+    p0, p01, p012 = [(250, 750, None), (100, 900, None), (0, 1000, None), (500, 500, None),
+                     (250, 750, 950), (100, 400, 1000), (0, 0, 600), (300, 300, 300)][trial % 8]
+    tier, lst = oracle.tier_classify(s, n, n_sink, n_recent, p0, p01, ev, p012)
+    assert tier.tolist() == _brute_tiers(list(s), n, n_sink, n_recent, p0, p01, list(ev), p012)
+    assert lst.tolist() == [i for i in range(n) if tier[i] <= 2]
+    if p012 is None:
+        assert 2 not in tier.tolist()
 
 
 def test_tier_invariants_reasoning_shape():
@@ -343,6 +347,94 @@ def test_tier_hand_example_and_sticky_eviction():
     ev[8] = True
     tier, _ = oracle.tier_classify(s, 12, 1, 2, 250, 750, ev)
     assert tier.tolist() == [0, 0, 3, 0, 1, 1, 3, 1, 3, 1, 0, 0]
+    # with a T2 quota: 25 % / 50 % / 90 % of M = 9 -> ranks < 2 T0, < 4 T1, < 8 T2, the last T3
+    tier, lst = oracle.tier_classify(s, 12, 1, 2, 250, 500, None, 900)
+    assert tier.tolist() == [0, 1, 2, 0, 2, 2, 3, 2, 0, 1, 0, 0]
+    assert lst.tolist() == [0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 11]
+
+
+def test_tier_invariants_with_t2():
+    n, ns, nr = 16384, 4, 512
+    s = rng.random(n).astype(np.float32)
+    tier, lst = oracle.tier_classify(s, n, ns, nr, 250, 750, None, 950)
+    M = n - ns - nr
+    prot = np.zeros(n, bool)
+    prot[:ns] = prot[n - nr:] = True
+    assert (tier[~prot] == 0).sum() == M // 4
+    assert (tier[~prot] == 1).sum() == 3 * M // 4 - M // 4
+    assert (tier[~prot] == 2).sum() == 95 * M // 100 - 3 * M // 4
+    assert (tier == 3).sum() == M - 95 * M // 100
+    assert len(lst) == ns + nr + 95 * M // 100
+    assert s[tier == 1].min() >= s[tier == 2].max() >= s[tier == 3].max()
+
+
+# ------------------------------------------------------------------ T2: 8-bit rows
+
+def test_encode_bf16_matches_torch_rounding():
+    r = np.random.default_rng(5)
+    x = np.concatenate([r.standard_normal(20000).astype(np.float32) * 10.0 ** r.integers(-30, 30, 20000),
+                        np.array([0.0, -0.0, 1.0, -1.0, 3.4028235e38, -3.4028235e38, 1e-40, -1e-40,
+                                  np.inf, -np.inf], np.float32)]).astype(np.float32)
+    # exact ties: low 16 bits 0x8000 with the kept last bit even and odd
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0xBF818000, 0x7F7F8000], np.uint32)
+    x = np.concatenate([x, ties.view(np.float32)])
+    ref = torch.tensor(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert oracle.encode_bf16(x).tolist() == ref.tolist()
+    assert oracle.encode_bf16(np.array([np.nan], np.float32)).tolist() == [0x7FC0]
+    assert np.isnan(oracle.decode_bf16(oracle.encode_bf16(
+        np.array([0x7F800001], np.uint32).view(np.float32))))[0]
+
+
+def test_quantize_int8_hand_example_and_ties_to_even():
+    row = np.array([127, -63.5, 0.5, 1.5, -2.5, 0, 126.4, -127], np.float32)
+    c, sc = oracle.quantize_int8(row)
+    assert float(sc) == 1.0
+    assert c.tolist() == [127, -64, 0, 2, -2, 0, 126, -127]
+    # dequantized through bf16: integers up to 127 are exact
+    assert oracle.decode_bf16(oracle.dequantize_int8(c, sc)).tolist() == c.astype(float).tolist()
+
+
+def test_quantize_int8_zero_and_non_finite_rows():
+    c, sc = oracle.quantize_int8(np.zeros((2, 8), np.float32))
+    assert (c == 0).all() and (sc == 0).all()
+    assert (oracle.decode_bf16(oracle.dequantize_int8(c, sc)) == 0).all()
+    row = np.array([np.nan, 2.0, -np.inf, -4.0, np.inf, 1.0], np.float32)
+    c, sc = oracle.quantize_int8(row)
+    assert float(sc) == np.float32(4.0) / np.float32(127)
+    assert c.tolist() == [0, 64, 0, -127, 0, 32]          # 2*127/4 = 63.5 -> 64 (even)
+
+
+def test_quantize_int8_power_of_two_scaling_is_exact():
+    r = np.random.default_rng(6)
+    x = r.standard_normal((64, 128)).astype(np.float32)
+    c, sc = oracle.quantize_int8(x)
+    for e in (-20, -3, 1, 7, 30):
+        c2, sc2 = oracle.quantize_int8((x * np.float32(2.0 ** e)).astype(np.float32))
+        assert np.array_equal(c, c2)
+        assert np.array_equal(sc2, (sc * np.float32(2.0 ** e)).astype(np.float32))
+
+
+def test_quantize_int8_codes_by_python_rounding_and_error_bound():
+    r = np.random.default_rng(7)
+    x = (r.standard_normal((40, 128)) * r.uniform(0.01, 50, (40, 1))).astype(np.float32)
+    xb = oracle.encode_bf16(x)                        # the bf16 cache rows the tier reads
+    c, sc = oracle.quantize_int8(xb)
+    xv = oracle.decode_bf16(xb)
+    for i in range(x.shape[0]):
+        m = float(np.abs(xv[i]).max())
+        assert float(sc[i]) == float(np.float32(np.float32(m) / np.float32(127)))
+        inv = float(np.float32(np.float32(127) / np.float32(m)))
+        # the product of two fp32 values is exact in fp64; fp32 rounding of it, then Python's
+        # round (ties to even)
+        want = [round(float(np.float32(float(v) * inv))) for v in xv[i]]
+        assert c[i].tolist() == want
+        assert int(np.abs(c[i]).max()) == 127
+        # the fp32 product q·scale lies within half a step of x (plus the fp32 roundings)
+        deq32 = c[i].astype(np.float32) * sc[i]
+        assert np.all(np.abs(deq32.astype(np.float64) - xv[i]) <= 0.5 * float(sc[i]) * (1 + 1e-5) + 1e-7 * m)
+        # and the bf16 rounding of it (8 significant bits) adds at most 2^-8 relative
+        deq = oracle.decode_bf16(oracle.dequantize_int8(c[i], sc[i]))
+        assert np.all(np.abs(deq - deq32) <= np.abs(deq32) * 2.0 ** -8)
 
 
 # ------------------------------------------------------------------ composite steps reduce to dense
@@ -395,6 +487,45 @@ def test_tiered_step_dense_first_step_conserves_mass():
     assert len(r2["tokens"]) == 68 + 3 * M // 4
     assert abs(float(r2["s"].astype(np.float64).sum()) - 2.0) < 1e-5
     assert np.all(r2["s"][r2["tier"] == 3] == r["s"][r2["tier"] == 3])
+
+
+def _tiered_inputs(L, Hq, Hkv, d, n, integer=False):
+    q = rng.standard_normal((L, Hq, d))
+    if integer:
+        # every row exactly representable by its 8-bit codes: integers with max |x| = 127
+        k = rng.integers(-127, 128, size=(L, Hkv, n, d)).astype(np.float32)
+        v = rng.integers(-127, 128, size=(L, Hkv, n, d)).astype(np.float32)
+        k[..., 0] = 127
+        v[..., 0] = -127
+        q = q / 64
+    else:
+        k = rng.standard_normal((L, Hkv, n, d)).astype(np.float32)
+        v = rng.standard_normal((L, Hkv, n, d)).astype(np.float32)
+    return q, k, v
+
+
+def test_tiered_step_t2_reduces_and_is_bounded():
+    L, Hq, Hkv, d, n = 2, 8, 2, 32, 600
+    s0 = rng.random(n).astype(np.float32)
+    # no T2 quota: the step without T2
+    q, k, v = _tiered_inputs(L, Hq, Hkv, d, n)
+    a = steps.tiered_sequence_step(s0, None, q, k, v, n, 0.25, 4, 64, 250, 750)
+    b = steps.tiered_sequence_step(s0, None, q, k, v, n, 0.25, 4, 64, 250, 750, t012_permille=750)
+    for key in ("tier", "tokens", "out", "lse", "s"):
+        assert np.array_equal(a[key], b[key])
+    # rows the codes hold exactly: T2 = T1 at full precision over the same set
+    q, k, v = _tiered_inputs(L, Hq, Hkv, d, n, integer=True)
+    t2 = steps.tiered_sequence_step(s0, None, q, k, v, n, 0.25, 4, 64, 250, 750, t012_permille=950)
+    t1 = steps.tiered_sequence_step(s0, None, q, k, v, n, 0.25, 4, 64, 250, 950)
+    assert (t2["tier"] == 2).sum() > 0 and np.array_equal(t2["tokens"], t1["tokens"])
+    assert np.array_equal(t2["out"], t1["out"]) and np.array_equal(t2["s"], t1["s"])
+    assert np.array_equal(t2["tier"] == 3, t1["tier"] == 3)
+    # ordinary rows: T2 changes the output, by about what 8-bit codes of K and V cost
+    q, k, v = _tiered_inputs(L, Hq, Hkv, d, n)
+    t2 = steps.tiered_sequence_step(s0, None, q, k, v, n, 0.25, 4, 64, 250, 750, t012_permille=950)
+    t1 = steps.tiered_sequence_step(s0, None, q, k, v, n, 0.25, 4, 64, 250, 950)
+    e = steps.rel_err(t2["out"], t1["out"])
+    assert 1e-5 < e < 2e-2, e
 
 
 # ------------------------------------------------------------------ sizes printed on the pages
