@@ -522,25 +522,28 @@ SPK_API spk_status importance_accumulate(float* s, int64_t s_ld, int B, int n_to
  *
  * Passages: "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro
  * Níveis" (T0 HBM: protected tokens and the most important; T1 host DDR at full precision,
- * fetched before attention; T2 8-bit, not used here; T3 evicted for good) and §4 (tiers are
- * reassigned periodically; the period is the caller's loop).
+ * fetched before attention; T2 kept at reduced precision, for instance 8 bits; T3 evicted for
+ * good) and §4 (tiers are reassigned periodically; the period is the caller's loop).
  * Definition: protected = tokens [0, n_sink) and [n_tokens - n_recent, n_tokens) -> T0.  The
  * M other tokens are ranked by (live before evicted, s descending, index ascending; NaN ranks
  * with the evicted); rank < floor(M*t0_permille/1000) -> T0, rank < floor(M*t01_permille/1000)
- * -> T1, the rest -> T3.  An evicted token is always T3.
+ * -> T1, rank < floor(M*t012_permille/1000) -> T2, the rest -> T3 (t012_permille =
+ * t01_permille: no T2).  An evicted token is always T3.
  *
  *   s        device fp32 [B, s_ld].
+ *   t0_permille <= t01_permille <= t012_permille <= 1000, else SPK_EINVAL.
  *   evicted  device uint8 [B, ev_ld] or NULL: nonzero = evicted earlier (sticky).  On return,
  *            every token classified T3 has evicted = 1.
- *   tier     device uint8 [B, tier_ld]: 0 (T0), 1 (T1) or 3 (T3) for tokens [0, n_tokens).
- *   sel_idx, sel_count  device int32 [B, sel_ld] / [B] or NULL: the ascending list of T0 ∪ T1
- *            tokens (the rows attention reads).  sel_ld >= n_tokens.
+ *   tier     device uint8 [B, tier_ld]: 0 (T0), 1 (T1), 2 (T2) or 3 (T3) for tokens
+ *            [0, n_tokens).
+ *   sel_idx, sel_count  device int32 [B, sel_ld] / [B] or NULL: the ascending list of
+ *            T0 ∪ T1 ∪ T2 tokens (the rows attention reads).  sel_ld >= n_tokens.
  *   ws       device workspace of at least tier_classify_workspace_size() bytes (NULL if 0).
  * ------------------------------------------------------------------------------------------ */
 SPK_API spk_status tier_classify_workspace_size(int B, int n_tokens, size_t* bytes);
 SPK_API spk_status tier_classify(const float* s, int64_t s_ld, int B, int n_tokens,
                                  int n_sink, int n_recent, int t0_permille, int t01_permille,
-                                 uint8_t* evicted, int64_t ev_ld,
+                                 int t012_permille, uint8_t* evicted, int64_t ev_ld,
                                  uint8_t* tier, int64_t tier_ld,
                                  int32_t* sel_idx, int32_t* sel_count, int64_t sel_ld,
                                  void* ws, size_t ws_bytes, void* stream);
@@ -603,6 +606,81 @@ SPK_API spk_status residency_prefetch(const void* k_host, const void* v_host,
                                       const int32_t* copy_tok, const int32_t* copy_slot,
                                       int64_t copy_ld, const int32_t* copy_count, int max_copies,
                                       void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * residency_update_tiers — residency_update with the tiers' roles given: tier_classes holds 2
+ * bits per tier code t = 0..3 (bits 2t, 2t+1): 0 = ranked first, 1 = ranked second, 2 or 3 =
+ * never resident.  residency_update is tier_classes = 0xF4 (T0 first, then T1).  0xCF makes
+ * every T2 row resident (T2 alone ranked, the others never): with a capacity of at least the
+ * T2 count, the T2 rows hold distinct slots, a row that stays in T2 keeps its slot, and the
+ * copy list names the rows new to T2 — the staging of the 8-bit tier (t2_fetch).  Arguments,
+ * errors and limits otherwise as residency_update.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status residency_update_tiers(const uint8_t* tier, int64_t tier_ld,
+                                          const float* s, int64_t s_ld, int B, int n_tokens,
+                                          int capacity, int tier_classes, int32_t* loc,
+                                          int64_t loc_ld, int32_t* copy_tok, int32_t* copy_slot,
+                                          int64_t copy_ld, int32_t* copy_count, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * kv_quantize_int8 — the 8-bit copy of K or V rows that the T2 tier keeps.
+ *
+ * Passage: "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro Níveis"
+ * (T2: low-importance rows on the CPU at reduced precision, for instance 8-bit quantization).
+ * Reading taken (the pages name no scheme): per row (one token of one KV head), m = the
+ * largest |x| over its finite elements; scale = fp32(m / 127); code = rint(fp32(x *
+ * fp32(127 / m))), ties to even, clamped to [-127, 127]; non-finite elements get code 0; a row
+ * with m = 0 gets codes 0 and scale 0.  IEEE fp32 division and multiplication.
+ *
+ *   src        rows (b, kvh, tok) at src + b*s_sb + kvh*s_sh + tok*s_sn, bf16 or fp32, device
+ *              memory or pinned host memory; 16-byte aligned rows (strides multiples of 8).
+ *   row_begin, row_end  the tokens [row_begin, row_end) quantized, for every (b, kvh).
+ *   codes      int8 [B, Hkv, >= row_end, d] at codes + b*c_sb + kvh*c_sh + tok*c_sn (strides
+ *              multiples of 8), device or pinned host memory.
+ *   scales     fp32 [B, Hkv, >= row_end] at scales + b*sc_sb + kvh*sc_sh + tok, device or
+ *              pinned host memory.
+ * Errors: SPK_EINVAL (sizes, strides, alignment, memory HIP does not know), SPK_EUNSUPPORTED
+ * (d, dtype).  One launch.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status kv_quantize_int8(const void* src, spk_dtype src_dtype, int64_t s_sb,
+                                    int64_t s_sh, int64_t s_sn, int B, int Hkv, int d,
+                                    int row_begin, int row_end, int8_t* codes, int64_t c_sb,
+                                    int64_t c_sh, int64_t c_sn, float* scales, int64_t sc_sb,
+                                    int64_t sc_sh, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * t2_fetch — bring the listed T2 rows of one layer back to bf16 in HBM staging rows.
+ *
+ * Passage: "Nem Todos os Pensamentos Necessitam de HBM", §1 (T2 rows are kept at 8 bits on the
+ * CPU).  Row copy_tok[b, r] of the code pools (codes_k/codes_v with scale_k/scale_v, as
+ * kv_quantize_int8 wrote them; device or pinned host memory, read through the device alias)
+ * becomes bf16(fp32(code * scale)), rounded to nearest even, in row stage_base +
+ * copy_slot[b, r] of the HBM pools k, v [B, Hkv, hbm_rows, d], for every KV head, for
+ * r < min(copy_count[b], copy_ld, max_copies).  The copy list is the one
+ * residency_update_tiers (tier_classes 0xCF) wrote.  Entries whose token is outside
+ * [0, code_rows) or whose row is outside the pools are skipped.
+ * Errors: SPK_EINVAL, SPK_EUNSUPPORTED (d not 64/128, pools not bf16).  One launch.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status t2_fetch(const int8_t* codes_k, const int8_t* codes_v, int64_t c_sb,
+                            int64_t c_sh, int64_t c_sn, const float* scale_k,
+                            const float* scale_v, int64_t sc_sb, int64_t sc_sh, int64_t code_rows,
+                            void* k, void* v, spk_dtype kv_dtype, int64_t kv_sb, int64_t kv_sh,
+                            int64_t kv_sn, int64_t hbm_rows, int64_t stage_base, int B, int Hkv,
+                            int d, const int32_t* copy_tok, const int32_t* copy_slot,
+                            int64_t copy_ld, const int32_t* copy_count, int max_copies,
+                            void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * t2_locations — the row locations the attention reads under a T2 tier: for tokens
+ * [0, n_tokens) of each sequence, loc_out = stage_base + loc_t2 where tier == 2 and loc_t2 >= 0
+ * (its staging row), else loc_res (its residency location: an HBM slot, or ~tok for the host
+ * pool).  All arrays are device [B, *_ld] (uint8 tier, int32 locations).
+ * Errors: SPK_EINVAL (sizes, row strides, stage_base + n_tokens beyond int32).  One launch.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status t2_locations(const uint8_t* tier, int64_t tier_ld, const int32_t* loc_res,
+                                int64_t res_ld, const int32_t* loc_t2, int64_t t2_ld,
+                                int32_t* loc_out, int64_t out_ld, int B, int n_tokens,
+                                int64_t stage_base, void* stream);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,8 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "sparse_decode_attn_noalloc", "sparse_decode_attn_noalloc_max_bytes",
            "topk_select_union_workspace_size", "topk_select_union",
            "sparse_decode_attn_union_workspace_size", "sparse_decode_attn_union",
-           "lookahead_prefetch")
+           "lookahead_prefetch", "residency_update_tiers", "kv_quantize_int8", "t2_fetch",
+           "t2_locations")
 
 
 class SpkError(RuntimeError):
@@ -107,7 +108,7 @@ def lib() -> ctypes.CDLL:
     L.tier_classify_workspace_size.restype = I
     L.tier_classify_workspace_size.argtypes = [I, I, ctypes.POINTER(SZ)]
     L.tier_classify.restype = I
-    L.tier_classify.argtypes = [P, I64, I, I, I, I, I, I, P, I64, P, I64, P, P, I64, P, SZ, P]
+    L.tier_classify.argtypes = [P, I64, I, I, I, I, I, I, I, P, I64, P, I64, P, P, I64, P, SZ, P]
     L.spk_set_attn_timing_events.restype = I
     L.spk_set_attn_timing_events.argtypes = [P, P]
     L.spk_stream_read.restype = I
@@ -129,6 +130,16 @@ def lib() -> ctypes.CDLL:
     L.sparse_index_score_windowed.argtypes = [P, I, P, I64, I, I, I, I, I, I, I, I, P, I64, P]
     L.residency_update.restype = I
     L.residency_update.argtypes = [P, I64, P, I64, I, I, I, P, I64, P, P, I64, P, P]
+    L.residency_update_tiers.restype = I
+    L.residency_update_tiers.argtypes = [P, I64, P, I64, I, I, I, I, P, I64, P, P, I64, P, P]
+    L.kv_quantize_int8.restype = I
+    L.kv_quantize_int8.argtypes = [P, I, I64, I64, I64, I, I, I, I, I, P, I64, I64, I64, P, I64,
+                                   I64, P]
+    L.t2_fetch.restype = I
+    L.t2_fetch.argtypes = [P, P, I64, I64, I64, P, P, I64, I64, I64, P, P, I, I64, I64, I64, I64,
+                           I64, I, I, I, P, P, I64, P, I, P]
+    L.t2_locations.restype = I
+    L.t2_locations.argtypes = [P, I64, P, I64, P, I64, P, I64, I, I, I64, P]
     L.residency_prefetch.restype = I
     L.residency_prefetch.argtypes = [P, P, I64, I64, I64, I64, P, P, I64, I64, I64, I64, I, I, I,
                                      I, P, P, I64, P, I, P]
@@ -777,9 +788,12 @@ def tier_classify(s: torch.Tensor, n_tokens: int, n_sink: int, n_recent: int,
                   t0_permille: int = 250, t01_permille: int = 750,
                   evicted: Optional[torch.Tensor] = None, tier: Optional[torch.Tensor] = None,
                   sel_idx: Optional[torch.Tensor] = None, sel_count: Optional[torch.Tensor] = None,
-                  stream=None):
+                  stream=None, t012_permille: Optional[int] = None):
     """Tiers of each sequence's tokens.  s [B, s_ld] fp32.  Returns (tier uint8 [B, n_tokens],
-    sel_idx int32 [B, n_tokens] (T0 ∪ T1 ascending), sel_count int32 [B])."""
+    sel_idx int32 [B, n_tokens] (T0 ∪ T1 ∪ T2 ascending), sel_count int32 [B]).
+    t012_permille None: no T2 (the T2 quota equals t01_permille)."""
+    if t012_permille is None:
+        t012_permille = t01_permille
     _need_dev(s, "s", F32S)
     if s.dim() != 2 or n_tokens < 0:
         raise ValueError("s must be [B, >= n_tokens] and n_tokens >= 0")
@@ -802,7 +816,8 @@ def tier_classify(s: torch.Tensor, n_tokens: int, n_sink: int, n_recent: int,
     sl = _row_ld(sel_idx, "sel_idx", B, n_tokens)
     _need_contig_n(sel_count, "sel_count", B, I32S)
     st = lib().tier_classify(_ptr(s), s_ld, B, n_tokens, n_sink, n_recent, t0_permille,
-                             t01_permille, _ptr(evicted), ev_ld, _ptr(tier), t_ld, _ptr(sel_idx),
+                             t01_permille, t012_permille, _ptr(evicted), ev_ld, _ptr(tier), t_ld,
+                             _ptr(sel_idx),
                              _ptr(sel_count), sl, None, 0, _stream(stream))
     _check(st, "tier_classify")
     return tier, sel_idx, sel_count
@@ -980,12 +995,17 @@ def lookahead_prefetch(sel_idx: torch.Tensor, sel_count: torch.Tensor, block_siz
 
 # ----------------------------------------------------------------------------- residency
 
+TIERS_T0_T1 = 0xF4   # residency classes: T0 ranked first, T1 second, T2 and T3 never resident
+TIERS_T2 = 0xCF      # every T2 row resident (the staging of the 8-bit tier)
+
+
 def residency_update(tier: torch.Tensor, s: torch.Tensor, n_tokens: int, capacity: int,
                      loc: torch.Tensor, copy_tok: torch.Tensor, copy_slot: torch.Tensor,
-                     copy_count: torch.Tensor, stream=None):
+                     copy_count: torch.Tensor, stream=None, tier_classes: int = TIERS_T0_T1):
     """HBM slots after a tier reassignment (loc updated in place) and the rows to copy.
     tier uint8 [B,*], s fp32 [B,*], loc int32 [B,*]; copy_tok/copy_slot int32 [B,copy_ld],
-    copy_count int32 [B]."""
+    copy_count int32 [B].  tier_classes: the tiers' roles (2 bits per tier code; the default
+    ranks T0 then T1, TIERS_T2 stages every T2 row)."""
     B = tier.shape[0]
     for t, nm, dts in ((tier, "tier", U8S), (s, "s", F32S), (loc, "loc", I32S),
                        (copy_tok, "copy_tok", I32S), (copy_slot, "copy_slot", I32S),
@@ -1001,9 +1021,10 @@ def residency_update(tier: torch.Tensor, s: torch.Tensor, n_tokens: int, capacit
     if copy_slot.shape != copy_tok.shape:
         raise ValueError("copy_tok and copy_slot must have one shape")
     _need_contig_n(copy_count, "copy_count", B, I32S)
-    st = lib().residency_update(_ptr(tier), tier.shape[1], _ptr(s), s.shape[1], B, n_tokens,
-                                capacity, _ptr(loc), loc.shape[1], _ptr(copy_tok), _ptr(copy_slot),
-                                copy_tok.shape[1], _ptr(copy_count), _stream(stream))
+    st = lib().residency_update_tiers(_ptr(tier), tier.shape[1], _ptr(s), s.shape[1], B,
+                                      n_tokens, capacity, int(tier_classes), _ptr(loc),
+                                      loc.shape[1], _ptr(copy_tok), _ptr(copy_slot),
+                                      copy_tok.shape[1], _ptr(copy_count), _stream(stream))
     _check(st, "residency_update")
 
 
@@ -1033,3 +1054,97 @@ def residency_prefetch(k_host: torch.Tensor, v_host: torch.Tensor, k_hbm: torch.
                                   _dt(k_hbm), B, Hkv, d, _ptr(copy_tok), _ptr(copy_slot),
                                   copy_tok.shape[1], _ptr(copy_count), max_copies, _stream(stream))
     _check(st, "residency_prefetch")
+
+
+# ----------------------------------------------------------------------------- T2 (8-bit tier)
+
+def _dev_or_pinned(t, name: str, dtypes):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if not (_is_dev(t) or _is_pinned(t)):
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)} (got {t.dtype})")
+    return t
+
+
+def _codes_view(codes: torch.Tensor, scales: torch.Tensor, name: str, B: int, Hkv: int,
+                n_min: int, d: int):
+    _dev_or_pinned(codes, f"{name} codes", (torch.int8,))
+    _dev_or_pinned(scales, f"{name} scales", F32S)
+    _need_shape(codes, f"{name} codes", [(">=", B), Hkv, (">=", n_min), d])
+    _need_shape(scales, f"{name} scales", [(">=", B), Hkv, (">=", n_min)])
+    if codes.stride(3) != 1 or scales.stride(2) != 1:
+        raise ValueError(f"{name}: codes and scales need a contiguous last dim")
+    if min(codes.shape[2], scales.shape[2]) < n_min:
+        raise ValueError(f"{name}: fewer than {n_min} rows")
+    return codes.stride(0), codes.stride(1), codes.stride(2), scales.stride(0), scales.stride(1)
+
+
+def kv_quantize_int8(src: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                     row_begin: int = 0, row_end: Optional[int] = None, stream=None):
+    """8-bit codes and fp32 scales of the rows [row_begin, row_end) of a K or V cache view
+    src [B, Hkv, N, d] (bf16 or fp32; device or pinned host) into codes int8 [B, Hkv, >=N, d]
+    and scales fp32 [B, Hkv, >=N] (device or pinned host)."""
+    _dev_or_pinned(src, "src", KVS)
+    sb, sh, sn = _rows_view(src, "src")
+    B, Hkv, N, d = src.shape
+    row_end = N if row_end is None else row_end
+    if not 0 <= row_begin <= row_end <= N:
+        raise ValueError(f"rows [{row_begin}, {row_end}) outside the {N} rows of src")
+    csb, csh, csn, ssb, ssh = _codes_view(codes, scales, "kv_quantize_int8", B, Hkv, row_end, d)
+    st = lib().kv_quantize_int8(_ptr(src), _dt(src), sb, sh, sn, B, Hkv, d, row_begin, row_end,
+                                _ptr(codes), csb, csh, csn, _ptr(scales), ssb, ssh,
+                                _stream(stream))
+    _check(st, "kv_quantize_int8")
+
+
+def t2_fetch(codes_k: torch.Tensor, codes_v: torch.Tensor, scale_k: torch.Tensor,
+             scale_v: torch.Tensor, k: torch.Tensor, v: torch.Tensor, stage_base: int,
+             copy_tok: torch.Tensor, copy_slot: torch.Tensor, copy_count: torch.Tensor,
+             max_copies: int, stream=None):
+    """Rows copy_tok[b, r] of the 8-bit pools, dequantized to bf16 into rows
+    stage_base + copy_slot[b, r] of the HBM pools k, v [B, Hkv, C, d] (one layer, every KV
+    head), r < min(copy_count[b], max_copies)."""
+    if k.dim() != 4:
+        raise ValueError("k must be a [B, Hkv, C, d] view")
+    B, Hkv, C, d = k.shape
+    _need_cache(k, "k", B, Hkv, 0, d, dtypes=(torch.bfloat16,))
+    _need_cache(v, "v", B, Hkv, 0, d, dtypes=(torch.bfloat16,))
+    kb, kh, kn = _rows_view(k, "k")
+    if _rows_view(v, "v") != (kb, kh, kn) or v.shape[2] != C:
+        raise ValueError("k and v must share shape and strides")
+    g = _codes_view(codes_k, scale_k, "t2_fetch K", B, Hkv, 0, d)
+    if _codes_view(codes_v, scale_v, "t2_fetch V", B, Hkv, 0, d) != g:
+        raise ValueError("the K and V code pools must share strides")
+    rows = min(codes_k.shape[2], codes_v.shape[2], scale_k.shape[2], scale_v.shape[2])
+    for t, nm in ((copy_tok, "copy_tok"), (copy_slot, "copy_slot")):
+        _need_dev(t, nm, I32S)
+        _contig(t, nm)
+        _need_shape(t, nm, [B, (">=", max_copies)])
+    if copy_slot.shape != copy_tok.shape:
+        raise ValueError("copy_tok and copy_slot must have one shape")
+    _need_contig_n(copy_count, "copy_count", B, I32S)
+    if stage_base < 0:
+        raise ValueError("stage_base must be >= 0")
+    st = lib().t2_fetch(_ptr(codes_k), _ptr(codes_v), g[0], g[1], g[2], _ptr(scale_k),
+                        _ptr(scale_v), g[3], g[4], rows, _ptr(k), _ptr(v), _dt(k), kb, kh, kn, C,
+                        stage_base, B, Hkv, d, _ptr(copy_tok), _ptr(copy_slot), copy_tok.shape[1],
+                        _ptr(copy_count), max_copies, _stream(stream))
+    _check(st, "t2_fetch")
+
+
+def t2_locations(tier: torch.Tensor, loc_res: torch.Tensor, loc_t2: torch.Tensor,
+                 loc_out: torch.Tensor, n_tokens: int, stage_base: int, stream=None):
+    """loc_out = stage_base + loc_t2 for T2 rows holding a staging slot, else loc_res; every
+    array [B, >= n_tokens] on the device (tier uint8, the locations int32)."""
+    B = tier.shape[0]
+    for t, nm, dts in ((tier, "tier", U8S), (loc_res, "loc_res", I32S), (loc_t2, "loc_t2", I32S),
+                       (loc_out, "loc_out", I32S)):
+        _need_dev(t, nm, dts)
+        _contig(t, nm)
+        _need_shape(t, nm, [B, (">=", n_tokens)])
+    st = lib().t2_locations(_ptr(tier), tier.shape[1], _ptr(loc_res), loc_res.shape[1],
+                            _ptr(loc_t2), loc_t2.shape[1], _ptr(loc_out), loc_out.shape[1], B,
+                            n_tokens, stage_base, _stream(stream))
+    _check(st, "t2_locations")

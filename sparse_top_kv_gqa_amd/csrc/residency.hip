@@ -37,11 +37,17 @@ __device__ __forceinline__ int nth_zero_bit(uint32_t w, int k) {
   return __builtin_ctz(z);
 }
 
+// The class of a tier for the ranking: 0 and 1 are the two ranked classes (class 0 first),
+// any other value is not resident; `classes` holds 2 bits per tier code 0..3.
+__device__ __forceinline__ uint8_t tier_class(uint32_t classes, uint8_t t) {
+  return (uint8_t)((classes >> (2u * (t & 3u))) & 3u);
+}
+
 __global__ __launch_bounds__(kThreads) void residency_kernel(
     const uint8_t* __restrict__ tier_all, int64_t tier_ld, const float* __restrict__ s_all,
-    int64_t s_ld, int n, int capacity, int32_t* __restrict__ loc_all, int64_t loc_ld,
-    int32_t* __restrict__ copy_tok, int32_t* __restrict__ copy_slot, int64_t copy_ld,
-    int32_t* __restrict__ copy_count) {
+    int64_t s_ld, int n, int capacity, uint32_t classes, int32_t* __restrict__ loc_all,
+    int64_t loc_ld, int32_t* __restrict__ copy_tok, int32_t* __restrict__ copy_slot,
+    int64_t copy_ld, int32_t* __restrict__ copy_count) {
   __shared__ __align__(16) uint32_t hist[4 * 256];
   __shared__ uint32_t held_bits[kSlotWords];
   __shared__ int free_pre[kSlotWords + 1];   // free slots before each bitmap word
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void residency_kernel(
 #pragma unroll
     for (int c = 0; c < kItems; ++c) {
       const bool in = c * kThreads + tid < n;
-      tr[c] = in ? tv[c] : (uint8_t)3;
+      tr[c] = in ? tier_class(classes, tv[c]) : (uint8_t)3;
       key[c] = in ? order_key(sv[c]) : 0u;
       c0 += tr[c] == 0;
       c1 += tr[c] == 1;
@@ -187,9 +193,9 @@ __global__ __launch_bounds__(kThreads) void residency_kernel(
 // Each thread handles the same tokens in both passes.
 __global__ __launch_bounds__(kThreads) void residency_chunked_kernel(
     const uint8_t* __restrict__ tier_all, int64_t tier_ld, const float* __restrict__ s_all,
-    int64_t s_ld, int n, int capacity, int32_t* __restrict__ loc_all, int64_t loc_ld,
-    int32_t* __restrict__ copy_tok, int32_t* __restrict__ copy_slot, int64_t copy_ld,
-    int32_t* __restrict__ copy_count) {
+    int64_t s_ld, int n, int capacity, uint32_t classes, int32_t* __restrict__ loc_all,
+    int64_t loc_ld, int32_t* __restrict__ copy_tok, int32_t* __restrict__ copy_slot,
+    int64_t copy_ld, int32_t* __restrict__ copy_count) {
   __shared__ __align__(16) uint32_t hist[4 * 256];
   __shared__ uint32_t held_bits[kChunkWords];
   __shared__ int free_pre[kChunkWords + 1];  // free slots before each bitmap word
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void residency_chunked_kernel(
 
   int c0 = 0, c1 = 0;
   for (int i = tid; i < n; i += kThreads) {
-    const uint8_t t = tier[i];
+    const uint8_t t = tier_class(classes, tier[i]);
     c0 += t == 0;
     c1 += t == 1;
   }
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void residency_chunked_kernel(
     radix_threshold(
         [&](auto visit) {
           for (int i = tid; i < n; i += kThreads)
-            if (tier[i] == cut_tier) visit(order_key(s[i]));
+            if (tier_class(classes, tier[i]) == cut_tier) visit(order_key(s[i]));
         },
         cut, hist, &thr, &need, &whole);
   }
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void residency_chunked_kernel(
   for (int c = 0; c < chunks; ++c) {
     const int i = c * kThreads + tid;
     const bool valid = i < n;
-    const int t = valid ? tier[i] : 3;
+    const int t = valid ? tier_class(classes, tier[i]) : 3;
     const uint32_t key = valid ? order_key(s[i]) : 0u;
     const bool in_cut = t == cut_tier && cut_tier >= 0;
     const bool gt = in_cut && cut > 0 && (whole ? key >= thr : key > thr);
@@ -364,13 +370,16 @@ spk_status host_device_ptr(const void* p, const void** dev, const char* name) {
 }  // namespace
 }  // namespace spk
 
-extern "C" SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier_ld,
-                                               const float* s, int64_t s_ld, int B, int n_tokens,
-                                               int capacity, int32_t* loc, int64_t loc_ld,
-                                               int32_t* copy_tok, int32_t* copy_slot,
-                                               int64_t copy_ld, int32_t* copy_count,
-                                               void* stream) {
+extern "C" SPK_API spk_status residency_update_tiers(const uint8_t* tier, int64_t tier_ld,
+                                                     const float* s, int64_t s_ld, int B,
+                                                     int n_tokens, int capacity, int tier_classes,
+                                                     int32_t* loc, int64_t loc_ld,
+                                                     int32_t* copy_tok, int32_t* copy_slot,
+                                                     int64_t copy_ld, int32_t* copy_count,
+                                                     void* stream) {
   using namespace spk;
+  SPK_REQUIRE(tier_classes >= 0 && tier_classes <= 0xFF, SPK_EINVAL,
+              "residency_update: tier_classes 0x%x is not 2 bits per tier code", tier_classes);
   SPK_REQUIRE(B >= 0 && n_tokens >= 0 && capacity >= 0, SPK_EINVAL,
               "residency_update: negative size");
   SPK_REQUIRE(n_tokens < kMaxTokensChunked && capacity <= kChunkCap, SPK_EUNSUPPORTED,
@@ -387,12 +396,24 @@ extern "C" SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (n_tokens <= kMaxTokens && capacity <= kMaxTokens)
     hipLaunchKernelGGL(residency_kernel, dim3(B), dim3(kThreads), 0, st, tier, tier_ld, s, s_ld,
-                       n_tokens, capacity, loc, loc_ld, copy_tok, copy_slot, copy_ld, copy_count);
+                       n_tokens, capacity, (uint32_t)tier_classes, loc, loc_ld, copy_tok,
+                       copy_slot, copy_ld, copy_count);
   else
     hipLaunchKernelGGL(residency_chunked_kernel, dim3(B), dim3(kThreads), 0, st, tier, tier_ld, s,
-                       s_ld, n_tokens, capacity, loc, loc_ld, copy_tok, copy_slot, copy_ld,
-                       copy_count);
+                       s_ld, n_tokens, capacity, (uint32_t)tier_classes, loc, loc_ld, copy_tok,
+                       copy_slot, copy_ld, copy_count);
   return check_launch("residency_update");
+}
+
+extern "C" SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier_ld,
+                                               const float* s, int64_t s_ld, int B, int n_tokens,
+                                               int capacity, int32_t* loc, int64_t loc_ld,
+                                               int32_t* copy_tok, int32_t* copy_slot,
+                                               int64_t copy_ld, int32_t* copy_count,
+                                               void* stream) {
+  // T0 ranks first, T1 second, T2 and T3 are never resident
+  return residency_update_tiers(tier, tier_ld, s, s_ld, B, n_tokens, capacity, 0xF4, loc, loc_ld,
+                                copy_tok, copy_slot, copy_ld, copy_count, stream);
 }
 
 extern "C" SPK_API spk_status residency_prefetch(

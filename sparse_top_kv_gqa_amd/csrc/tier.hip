@@ -1,16 +1,19 @@
-// tier_classify: T0 / T1 / T3 tiers by cumulative importance, sinks and recent window protected.
+// tier_classify: T0 / T1 / T2 / T3 tiers by cumulative importance, sinks and recent window
+// protected.
 //
 // "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro Níveis": protected
 // tokens and the most important ones stay in T0 (HBM); the middle goes to T1 (full precision in
-// host DDR, fetched before attention); only the least important tail is T3 (evicted for good).
-// §4: the classification is redone periodically; the period is the caller's loop.
+// host DDR, fetched before attention); low importance may go to T2 (kept at 8 bits); only the
+// least important tail is T3 (evicted for good).  §4: the classification is redone
+// periodically; the period is the caller's loop.
 //
 // One workgroup (1024 threads) per sequence.  The unprotected tokens get order-preserving keys
-// (evicted or NaN -> 0, the lowest), two radix searches (8-bit digits, one barrier per pass)
-// find the keys at ranks floor(M*t0/1000) and floor(M*t01/1000); ranks in index order (ties at
-// the thresholds to the lower index, then positions in the ascending T0 ∪ T1 list) come from
-// per-(chunk, wave) ballot counts turned into prefixes by one wave scan, so assigning tiers,
-// marking new evictions and compacting the list take four barriers (sequences of up to 16384
+// (evicted or NaN -> 0, the lowest), radix searches (8-bit digits, one barrier per pass) find
+// the keys at ranks floor(M*t0/1000), floor(M*t01/1000) and, with a T2 quota,
+// floor(M*t012/1000); ranks in index order (ties at the thresholds to the lower index, then
+// positions in the ascending list of attended rows T0 ∪ T1 ∪ T2) come from per-(chunk, wave)
+// ballot counts turned into prefixes by one wave scan, so assigning tiers, marking new
+// evictions and compacting the list take four barriers, six with T2 (sequences of up to 16384
 // tokens, whose keys stay in registers; longer ones rank chunk by chunk with block scans).
 #include "select_common.h"
 
@@ -23,13 +26,14 @@ constexpr int kItems = 16;
 template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void tier_kernel(
     const float* __restrict__ s_all, int64_t s_ld, int n, int n_sink, int n_recent, int p0,
-    int p01, uint8_t* __restrict__ evicted, int64_t ev_ld, uint8_t* __restrict__ tier_all,
+    int p01, int p012, uint8_t* __restrict__ evicted, int64_t ev_ld, uint8_t* __restrict__ tier_all,
     int64_t tier_ld, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
     int64_t sel_ld) {
   __shared__ __align__(16) uint32_t hist[4 * 256];
   __shared__ int scratch[kThreads / kWave + 1];
   // per-(chunk, wave) counts of the register path, then their prefixes (+ the total)
   __shared__ int cw_eq[(ITEMS > 0 ? ITEMS : 1) * (kThreads / kWave) + 1];
+  __shared__ int cw_eq2[(ITEMS > 0 ? ITEMS : 1) * (kThreads / kWave) + 1];
   __shared__ int cw_sel[(ITEMS > 0 ? ITEMS : 1) * (kThreads / kWave) + 1];
   const int b = blockIdx.x;
   if (n <= 0) {
@@ -44,6 +48,8 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
   const int M = hi - lo;
   const int n0 = (int)(((int64_t)M * p0) / 1000);
   const int n01 = (int)(((int64_t)M * p01) / 1000);
+  const int n012 = (int)(((int64_t)M * p012) / 1000);
+  const bool has_t2 = n012 > n01;  // uniform: the T2 search and tie counts run only then
 
   auto key_of = [&](int i) -> uint32_t {
     if (ev && ev[i]) return 0u;
@@ -79,8 +85,8 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
   };
   // thresholds at ranks n0 and n01: one-barrier-per-pass radix searches; when a search ends on
   // a bin that holds exactly the missing keys, every key >= the threshold is kept (need = all)
-  uint32_t thr0 = 0xFFFFFFFFu, thr1 = 0xFFFFFFFFu;
-  int need0 = 0, need1 = 0;
+  uint32_t thr0 = 0xFFFFFFFFu, thr1 = 0xFFFFFFFFu, thr2 = 0xFFFFFFFFu;
+  int need0 = 0, need1 = 0, need2 = 0;
   auto search = [&](int rank, uint32_t* thr, int* need) {
     for (int i = threadIdx.x; i < 4 * 256; i += kThreads) hist[i] = 0u;
     __syncthreads();
@@ -91,6 +97,7 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
   };
   if (n0 > 0) search(n0, &thr0, &need0);
   if (n01 > 0) search(n01, &thr1, &need1);
+  if (has_t2) search(n012, &thr2, &need2);
 
   if constexpr (ITEMS > 0) {
     // ranks in index order (chunk c, then wave, then lane) from per-(chunk, wave) counts: one
@@ -124,9 +131,14 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
       const bool cand = i >= lo && i < hi;
       const int e0 = __popcll(__ballot(cand && n0 > 0 && reg[c] == thr0));
       const int e1 = __popcll(__ballot(cand && n01 > 0 && reg[c] == thr1));
-      if (lane == 0) cw_eq[c * NWV + wid] = e0 | (e1 << 16);
+      const int e2 = __popcll(__ballot(cand && has_t2 && reg[c] == thr2));
+      if (lane == 0) {
+        cw_eq[c * NWV + wid] = e0 | (e1 << 16);
+        cw_eq2[c * NWV + wid] = e2;
+      }
     }
     prefixes(cw_eq);
+    if (has_t2) prefixes(cw_eq2);
     // round 2: tiers, evictions, and the per-(chunk, wave) counts of the list
     uint32_t selbits = 0;
 #pragma unroll
@@ -137,18 +149,22 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
       const uint32_t key = reg[c];
       const bool eq0 = cand && n0 > 0 && key == thr0;
       const bool eq1 = cand && n01 > 0 && key == thr1;
+      const bool eq2 = cand && has_t2 && key == thr2;
       const int pre = cw_eq[c * NWV + wid];
       const int eqrank0 = (pre & 0xFFFF) + __popcll(__ballot(eq0) & lt);
       const int eqrank1 = (pre >> 16) + __popcll(__ballot(eq1) & lt);
+      const int eqrank2 = (has_t2 ? cw_eq2[c * NWV + wid] : 0) + __popcll(__ballot(eq2) & lt);
       const bool is_ev = cand && ev_v[c];
       const bool top0 = cand && n0 > 0 && (key > thr0 || (eq0 && eqrank0 < need0));
       const bool top1 = cand && n01 > 0 && (key > thr1 || (eq1 && eqrank1 < need1));
+      const bool top2 = cand && has_t2 && (key > thr2 || (eq2 && eqrank2 < need2));
       uint8_t t = 3;
       if (!cand) t = 0;
       else if (is_ev) t = 3;
       else if (top0) t = 0;
       else if (top1) t = 1;
-      const bool sel = valid && t <= 1;
+      else if (top2) t = 2;
+      const bool sel = valid && t <= 2;
       selbits |= (sel ? 1u : 0u) << c;
       if (valid) {
         tier[i] = t;
@@ -169,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
     if (sel_count && threadIdx.x == 0) sel_count[b] = total_sel;
     return;
   }
-  int run_eq0 = 0, run_eq1 = 0, run_sel = 0;
+  int run_eq0 = 0, run_eq1 = 0, run_eq2 = 0, run_sel = 0;
   const int chunks = (n + kThreads - 1) / kThreads;
   for (int c = 0; c < chunks; ++c) {
     const int i = c * kThreads + threadIdx.x;
@@ -189,19 +205,24 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
     // they hold ranks too)
     const int eq0 = cand && n0 > 0 && key == thr0;
     const int eq1 = cand && n01 > 0 && key == thr1;
-    int tot;
+    const int eq2 = cand && has_t2 && key == thr2;
+    int tot, tot2 = 0;
     const int pre = block_excl_scan(eq0 | (eq1 << 16), scratch, &tot);
+    const int pre2 = has_t2 ? block_excl_scan(eq2, scratch, &tot2) : 0;
     const int eqrank0 = run_eq0 + (pre & 0xFFFF);
     const int eqrank1 = run_eq1 + (pre >> 16);
+    const int eqrank2 = run_eq2 + pre2;
     const bool is_ev = cand && ev && ev[i];
     const bool top0 = cand && n0 > 0 && (key > thr0 || (eq0 && eqrank0 < need0));
     const bool top1 = cand && n01 > 0 && (key > thr1 || (eq1 && eqrank1 < need1));
+    const bool top2 = cand && has_t2 && (key > thr2 || (eq2 && eqrank2 < need2));
     uint8_t t = 3;
     if (!cand) t = 0;
     else if (is_ev) t = 3;
     else if (top0) t = 0;
     else if (top1) t = 1;
-    const int sel = valid && t <= 1;
+    else if (top2) t = 2;
+    const int sel = valid && t <= 2;
     int tot_sel;
     const int pos = block_excl_scan(sel, scratch, &tot_sel);
     if (valid) {
@@ -211,6 +232,7 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
     }
     run_eq0 += tot & 0xFFFF;
     run_eq1 += tot >> 16;
+    run_eq2 += tot2;
     run_sel += tot_sel;
   }
   if (sel_count && threadIdx.x == 0) sel_count[b] = run_sel;
@@ -230,7 +252,8 @@ extern "C" SPK_API spk_status tier_classify_workspace_size(int B, int n_tokens, 
 
 extern "C" SPK_API spk_status tier_classify(const float* s, int64_t s_ld, int B, int n_tokens,
                                             int n_sink, int n_recent, int t0_permille,
-                                            int t01_permille, uint8_t* evicted, int64_t ev_ld,
+                                            int t01_permille, int t012_permille,
+                                            uint8_t* evicted, int64_t ev_ld,
                                             uint8_t* tier, int64_t tier_ld, int32_t* sel_idx,
                                             int32_t* sel_count, int64_t sel_ld, void* ws,
                                             size_t ws_bytes, void* stream) {
@@ -240,9 +263,12 @@ extern "C" SPK_API spk_status tier_classify(const float* s, int64_t s_ld, int B,
   SPK_REQUIRE(B >= 0 && n_tokens >= 0 && n_sink >= 0 && n_recent >= 0, SPK_EINVAL,
               "tier_classify: negative size");
   SPK_REQUIRE(n_tokens < (1 << 30), SPK_EINVAL, "tier_classify: n_tokens too large");
-  SPK_REQUIRE(0 <= t0_permille && t0_permille <= t01_permille && t01_permille <= 1000, SPK_EINVAL,
-              "tier_classify: need 0 <= t0_permille (%d) <= t01_permille (%d) <= 1000",
-              t0_permille, t01_permille);
+  SPK_REQUIRE(0 <= t0_permille && t0_permille <= t01_permille && t01_permille <= t012_permille &&
+                  t012_permille <= 1000,
+              SPK_EINVAL,
+              "tier_classify: need 0 <= t0_permille (%d) <= t01_permille (%d) <= t012_permille "
+              "(%d) <= 1000",
+              t0_permille, t01_permille, t012_permille);
   SPK_REQUIRE(B == 0 || n_tokens == 0 || (s && tier), SPK_EINVAL, "tier_classify: null s or tier");
   SPK_REQUIRE(s_ld >= n_tokens && tier_ld >= n_tokens, SPK_EINVAL,
               "tier_classify: s_ld/tier_ld smaller than n_tokens");
@@ -255,12 +281,12 @@ extern "C" SPK_API spk_status tier_classify(const float* s, int64_t s_ld, int B,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (n_tokens <= kItems * kThreads) {
     hipLaunchKernelGGL(tier_kernel<kItems>, dim3(B), dim3(kThreads), 0, st, s, s_ld, n_tokens,
-                       n_sink, n_recent, t0_permille, t01_permille, evicted, ev_ld, tier, tier_ld,
-                       sel_idx, sel_count, sel_ld);
+                       n_sink, n_recent, t0_permille, t01_permille, t012_permille, evicted, ev_ld,
+                       tier, tier_ld, sel_idx, sel_count, sel_ld);
   } else {
     hipLaunchKernelGGL(tier_kernel<0>, dim3(B), dim3(kThreads), 0, st, s, s_ld, n_tokens, n_sink,
-                       n_recent, t0_permille, t01_permille, evicted, ev_ld, tier, tier_ld, sel_idx,
-                       sel_count, sel_ld);
+                       n_recent, t0_permille, t01_permille, t012_permille, evicted, ev_ld, tier,
+                       tier_ld, sel_idx, sel_count, sel_ld);
   }
   return check_launch("tier_classify");
 }

@@ -7,8 +7,8 @@ BlockSparseDecode   predictor scores pooled blocks -> top-k blocks -> attention 
 TokenSparseDecode   per-head or group-mean token scores -> top-k tokens -> attention over each
                     query's own set, the group's union fetched once (optionally with some rows in
                     pinned host memory)
-TieredDecode        tier classification by cumulative importance -> attention over T0 ∪ T1 in
-                    every layer -> importance update
+TieredDecode        tier classification by cumulative importance -> attention over T0 ∪ T1
+                    (∪ T2, read from its 8-bit copy) in every layer -> importance update
 BlockLookaheadDecode  the block step through several layers whose caches keep some blocks only
                     in pinned host memory; with lookahead, layer l+1's blocks are chosen before
                     layer l attends and their host rows are copied into HBM meanwhile
@@ -26,7 +26,7 @@ from . import (attn_workspace_size, fused_index_topk_ok, sparse_decode_attn, spa
                importance_accumulate, tier_classify, window_count, residency_update,
                residency_prefetch, topk_select_union, topk_union_workspace_size,
                sparse_decode_attn_union, attn_union_workspace_size, union_sets,
-               lookahead_prefetch)
+               lookahead_prefetch, TIERS_T2, t2_fetch, t2_locations)
 
 UNION_MIN_TOKENS = 16385   # wide rows: the union pipeline (narrower rows fit one workgroup)
 
@@ -240,12 +240,20 @@ class TieredDecode:
     overlap_prefetch: the copies of a reassignment run layer by layer on a second stream
     (default priority), and each layer's attention waits only for its own layer's copy, so
     layer l+1's copy overlaps layer l's attention.
+
+    t012_permille / t2_codes: the T2 tier (rows ranked between t01 and t012 are attended from
+    their 8-bit copy).  t2_codes are per-layer (codes_k, codes_v, scale_k, scale_v) written by
+    kv_quantize_int8 (pinned host memory, or device memory), and needs host_caches.  Every
+    tiered step the T2 rows hold staging rows [hbm_rows, hbm_rows + stage_rows) of the HBM
+    pools (a row that stays in T2 keeps its staging row; only rows new to T2 are fetched and
+    dequantized), and the attention reads them there.
     """
 
     def __init__(self, caches: Sequence, Hq: int, n_cap: int, n_sink: int, n_recent: int,
                  t0_permille: int = 250, t01_permille: int = 750,
                  sm_scale: Optional[float] = None, host_caches: Optional[Sequence] = None,
-                 hbm_rows: int = 0, reassign_every: int = 1, overlap_prefetch: bool = False):
+                 hbm_rows: int = 0, reassign_every: int = 1, overlap_prefetch: bool = False,
+                 t012_permille: Optional[int] = None, t2_codes: Optional[Sequence] = None):
         self.caches = list(caches)
         k0 = self.caches[0][0]
         B, Hkv, _, d = k0.shape
@@ -281,6 +289,37 @@ class TieredDecode:
         self.overlap = overlap_prefetch and self.host is not None
         self.copy_stream = torch.cuda.Stream(device=dev) if self.overlap else None
         self._copied = None      # per-layer events of the pending overlapped copies
+        self.p012 = t01_permille if t012_permille is None else t012_permille
+        self.t2 = self.p012 > t01_permille
+        if self.t2:
+            if self.host is None or t2_codes is None or len(t2_codes) != self.L:
+                raise ValueError("the T2 tier needs host_caches and per-layer t2_codes")
+            self.codes = list(t2_codes)
+            # at most floor(M*t012/1000) - floor(M*t01/1000) <= this many T2 rows per sequence
+            self.stage_rows = (n_cap * (self.p012 - t01_permille)) // 1000 + 1
+            if self.caches[0][0].shape[2] < hbm_rows + self.stage_rows:
+                raise ValueError(f"HBM pools need hbm_rows + {self.stage_rows} staging rows")
+            self.loc_t2 = (~torch.arange(n_cap, dtype=torch.int32, device=dev)).repeat(B, 1)
+            self.loc_attn = torch.empty((B, n_cap), dtype=torch.int32, device=dev)
+            self.loc_attn_view = self.loc_attn.unsqueeze(1).expand(B, Hkv, n_cap)
+            self.t2_tok = torch.zeros((B, self.stage_rows), dtype=torch.int32, device=dev)
+            self.t2_slot = torch.zeros((B, self.stage_rows), dtype=torch.int32, device=dev)
+            self.t2_count = torch.zeros((B,), dtype=torch.int32, device=dev)
+            self.t2_fetched = torch.zeros((), dtype=torch.int64, device=dev)   # rows so far
+
+    def reset(self):
+        """Back to an empty history: importance, evictions, residency and T2 staging."""
+        self.s.zero_()
+        self.evicted.zero_()
+        if self.host is not None:
+            dev = self.loc.device
+            home = ~torch.arange(self.n_cap, dtype=torch.int32, device=dev)
+            self.loc.copy_(home.repeat(self.B, 1))
+            self.tiered_steps = 0
+            self.copies.zero_()
+        if self.t2:
+            self.loc_t2.copy_(home.repeat(self.B, 1))
+            self.t2_fetched.zero_()
 
     def reassign(self, n_tokens: int):
         """Resident set of every sequence for the current tiers, and the differential copy of
@@ -312,20 +351,31 @@ class TieredDecode:
         else:
             tier_classify(self.s, n_tokens, self.n_sink, self.n_recent, self.p0, self.p01,
                           evicted=self.evicted, tier=self.tier, sel_idx=self.sel,
-                          sel_count=self.count)
+                          sel_count=self.count, t012_permille=self.p012)
             sel = self.sel
             if self.host is not None and self.tiered_steps % self.reassign_every == 0:
                 self.reassign(n_tokens)
             self.tiered_steps += 1
+        staged = self.t2 and not dense
+        if staged:
+            # T2 rows keep their staging rows while they stay in T2; rows new to T2 are listed
+            residency_update(self.tier, self.s, n_tokens, self.stage_rows, self.loc_t2,
+                             self.t2_tok, self.t2_slot, self.t2_count, tier_classes=TIERS_T2)
+            t2_locations(self.tier, self.loc, self.loc_t2, self.loc_attn, n_tokens, self.hbm_rows)
+            self.t2_fetched += self.t2_count.sum()
         for l, (k, v) in enumerate(self.caches):
             if self.host is not None:
                 kh, vh = self.host[l]
                 if self._copied is not None:
                     torch.cuda.current_stream().wait_event(self._copied[l])
+                if staged:
+                    ck, cv, sk, sv = self.codes[l]
+                    t2_fetch(ck, cv, sk, sv, k, v, self.hbm_rows, self.t2_tok, self.t2_slot,
+                             self.t2_count, self.stage_rows)
                 sparse_decode_attn(qs[l], k, v, sel, self.count, "per_seq", n_tokens,
                                    sm_scale=self.sm_scale, out=self.out[l], lse=self.lse[l],
                                    logits=self.logits[l], ws=self.ws, k_host=kh, v_host=vh,
-                                   loc=self.loc_view)
+                                   loc=self.loc_attn_view if staged else self.loc_view)
             else:
                 sparse_decode_attn(qs[l], k, v, sel, self.count, "per_seq", n_tokens,
                                    sm_scale=self.sm_scale, out=self.out[l], lse=self.lse[l],

@@ -117,15 +117,48 @@ def test_importance_and_tier_validation():
     assert L.importance_accumulate(A, 100, 2, 100, Bp, Bp, 50, A, 50, A, 0, 4, None) == 1
     assert L.importance_accumulate(A, 100, 2, 100, Bp, Bp, 50, A, 50, A, 100, 100, None) == 2
     assert L.importance_accumulate(A, 100, 2, 100, Bp, Bp, 50, A, 40, A, 2, 4, None) == 1
-    # t0 > t01
-    assert L.tier_classify(A, 100, 2, 100, 4, 8, 800, 700, None, 0, Bp, 100, None, None, 0,
+    # t0 > t01; t01 > t012; t012 > 1000
+    assert L.tier_classify(A, 100, 2, 100, 4, 8, 800, 700, 700, None, 0, Bp, 100, None, None, 0,
+                           None, 0, None) == 1
+    assert L.tier_classify(A, 100, 2, 100, 4, 8, 250, 750, 700, None, 0, Bp, 100, None, None, 0,
+                           None, 0, None) == 1
+    assert "t012_permille" in _err()
+    assert L.tier_classify(A, 100, 2, 100, 4, 8, 250, 750, 1001, None, 0, Bp, 100, None, None, 0,
                            None, 0, None) == 1
     # sel_ld < n_tokens
-    assert L.tier_classify(A, 100, 2, 100, 4, 8, 250, 750, None, 0, Bp, 100, Bp, Bp, 50,
+    assert L.tier_classify(A, 100, 2, 100, 4, 8, 250, 750, 950, None, 0, Bp, 100, Bp, Bp, 50,
                            None, 0, None) == 1
     # sel_idx without sel_count
-    assert L.tier_classify(A, 100, 2, 100, 4, 8, 250, 750, None, 0, Bp, 100, Bp, None, 100,
+    assert L.tier_classify(A, 100, 2, 100, 4, 8, 250, 750, 750, None, 0, Bp, 100, Bp, None, 100,
                            None, 0, None) == 1
+
+
+def test_t2_validation():
+    L = spk.lib()
+    # residency classes outside a byte
+    assert L.residency_update_tiers(A, 64, A, 64, 1, 64, 16, 0x100, A, 64, A, A, 16, A,
+                                    None) == 1
+    assert "tier_classes" in _err()
+    # quantize: d = 96; row range reversed; src not memory HIP knows (host, not pinned)
+    assert L.kv_quantize_int8(A, 1, 128, 128, 128, 1, 1, 96, 0, 8, A, 128, 128, 128, A, 8, 8,
+                              None) == 2
+    assert L.kv_quantize_int8(A, 1, 128, 128, 128, 1, 1, 128, 8, 4, A, 128, 128, 128, A, 8, 8,
+                              None) == 1
+    assert L.kv_quantize_int8(A, 1, 128, 128, 130, 1, 1, 128, 0, 8, A, 128, 128, 128, A, 8, 8,
+                              None) == 1
+    # nothing to do: no rows
+    assert L.kv_quantize_int8(A, 1, 128, 128, 128, 1, 1, 128, 8, 8, A, 128, 128, 128, A, 8, 8,
+                              None) == 0
+    # fetch: fp32 pools; d = 96; negative stage_base
+    assert L.t2_fetch(A, A, 128, 128, 128, A, A, 8, 8, 8, Bp, Bp, 0, 128, 128, 128, 8, 0, 1, 1,
+                      128, A, A, 8, A, 8, None) == 2
+    assert L.t2_fetch(A, A, 128, 128, 128, A, A, 8, 8, 8, Bp, Bp, 1, 128, 128, 128, 8, 0, 1, 1,
+                      96, A, A, 8, A, 8, None) == 2
+    assert L.t2_fetch(A, A, 128, 128, 128, A, A, 8, 8, 8, Bp, Bp, 1, 128, 128, 128, 8, -1, 1, 1,
+                      128, A, A, 8, A, 8, None) == 1
+    # locations: row stride below n_tokens; stage rows beyond int32
+    assert L.t2_locations(A, 50, A, 100, A, 100, A, 100, 1, 100, 0, None) == 1
+    assert L.t2_locations(A, 100, A, 100, A, 100, A, 100, 1, 100, 2 ** 31 - 50, None) == 1
 
 
 def test_binding_raises_without_library(monkeypatch):

@@ -286,8 +286,45 @@ def test_residency_checks(fake):
                     copy_slot=cs, copy_count=cc, max_copies=cap), **b}
         with pytest.raises(ValueError):
             spk.residency_prefetch(**a)
-    assert fake.calls.count("residency_update") == 1
+    assert fake.calls.count("residency_update_tiers") == 1
     assert fake.calls.count("residency_prefetch") == 1
+
+
+def test_t2_checks(fake):
+    Bs, Hk, n, cap = 2, 2, 500, 128
+    src = d(Bs, Hk, n, D)
+    codes = d(Bs, Hk, n, D, dtype=torch.int8)
+    sc = d(Bs, Hk, n, dtype=torch.float32)
+    spk.kv_quantize_int8(src, codes, sc)
+    spk.kv_quantize_int8(src, codes, sc, 100, 200)
+    for b in [dict(codes=d(Bs, Hk, n - 1, D, dtype=torch.int8)),
+              dict(codes=d(Bs, Hk, n, D, dtype=torch.uint8)),
+              dict(scales=d(Bs, Hk, n - 1, dtype=torch.float32)),
+              dict(row_begin=10, row_end=5), dict(row_end=n + 1),
+              dict(src=torch.empty((Bs, Hk, n, D), dtype=torch.bfloat16).transpose(2, 3))]:
+        with pytest.raises(ValueError):
+            spk.kv_quantize_int8(**{**dict(src=src, codes=codes, scales=sc), **b})
+    k, v = d(Bs, Hk, cap + 64, D), d(Bs, Hk, cap + 64, D)
+    ct, cs, cc = d(Bs, 64, dtype=torch.int32), d(Bs, 64, dtype=torch.int32), d(Bs, dtype=torch.int32)
+    base = dict(codes_k=codes, codes_v=codes.clone(), scale_k=sc, scale_v=sc.clone(), k=k, v=v,
+                stage_base=cap, copy_tok=ct, copy_slot=cs, copy_count=cc, max_copies=64)
+    spk.t2_fetch(**base)
+    for b in [dict(k=d(Bs, Hk, cap + 64, D, dtype=torch.float32)),
+              dict(v=d(Bs, Hk, cap + 32, D)), dict(codes_v=d(Bs, Hk + 1, n, D, dtype=torch.int8)),
+              dict(scale_k=d(Bs, Hk, n, dtype=torch.bfloat16)), dict(max_copies=65),
+              dict(copy_count=d(Bs + 1, dtype=torch.int32)), dict(stage_base=-1)]:
+        with pytest.raises(ValueError):
+            spk.t2_fetch(**{**base, **b})
+    tier, lr = d(Bs, n, dtype=torch.uint8), d(Bs, n, dtype=torch.int32)
+    spk.t2_locations(tier, lr, lr.clone(), lr.clone(), n, cap)
+    for b in [dict(tier=d(Bs, n, dtype=torch.int32)), dict(loc_t2=d(Bs, n - 1, dtype=torch.int32)),
+              dict(loc_out=d(Bs + 1, n, dtype=torch.int32))]:
+        with pytest.raises(ValueError):
+            spk.t2_locations(**{**dict(tier=tier, loc_res=lr, loc_t2=lr.clone(), loc_out=lr.clone(),
+                                       n_tokens=n, stage_base=cap), **b})
+    assert fake.calls.count("kv_quantize_int8") == 2
+    assert fake.calls.count("t2_fetch") == 1
+    assert fake.calls.count("t2_locations") == 1
 
 
 def test_empty_selection_rows_are_accepted(fake):

@@ -353,18 +353,21 @@ def test_tier_classify_bit_exact_random():
         r = np.random.default_rng(trial)
         s = (r.integers(0, 50, size=(B, max(n, 1))) / 7).astype(np.float32)
         ev = (r.random((B, max(n, 1))) < 0.1).astype(np.uint8)
-        st = torch.tensor(s, device=DEV)
-        evt = torch.tensor(ev, device=DEV)
-        tier, sel, cnt = spk.tier_classify(st, n, ns, nr, 250, 750, evicted=evt)
-        torch.cuda.synchronize()
-        for b in range(B):
-            t_ref, l_ref = oracle.tier_classify(s[b], n, ns, nr, 250, 750, ev[b].astype(bool))
-            assert tier.cpu().numpy()[b, :n].tolist() == t_ref.tolist(), (trial, b)
-            c = int(cnt.cpu()[b])
-            assert c == len(l_ref)
-            assert sel.cpu().numpy()[b, :c].tolist() == l_ref.tolist()
-            ev_new = ev[b, :n].astype(bool) | (t_ref == 3)
-            assert (evt.cpu().numpy()[b, :n] != 0).tolist() == ev_new.tolist()
+        for p0, p01, p012 in ((250, 750, None), (250, 750, 950), (100, 400, 1000), (0, 0, 600)):
+            st = torch.tensor(s, device=DEV)
+            evt = torch.tensor(ev, device=DEV)
+            tier, sel, cnt = spk.tier_classify(st, n, ns, nr, p0, p01, evicted=evt,
+                                               t012_permille=p012)
+            torch.cuda.synchronize()
+            for b in range(B):
+                t_ref, l_ref = oracle.tier_classify(s[b], n, ns, nr, p0, p01, ev[b].astype(bool),
+                                                    p012)
+                assert tier.cpu().numpy()[b, :n].tolist() == t_ref.tolist(), (trial, b, p012)
+                c = int(cnt.cpu()[b])
+                assert c == len(l_ref)
+                assert sel.cpu().numpy()[b, :c].tolist() == l_ref.tolist()
+                ev_new = ev[b, :n].astype(bool) | (t_ref == 3)
+                assert (evt.cpu().numpy()[b, :n] != 0).tolist() == ev_new.tolist()
 
 
 def test_tiered_decode_small_matches_oracle():
@@ -1158,6 +1161,184 @@ def _offload_vs_all_hbm(w, hbm_rows, every, overlap):
                     sl = torch.tensor(L[b, res].astype(np.int64))
                     assert torch.equal(hbm[0][0][b][:, sl].cpu(), caches[0][0][b][:, torch.tensor(res)].cpu())
     assert int(off.copies) > 0
+
+
+# ---------------------------------------------------------------------- T2: the 8-bit tier
+
+def _t2_rows(r, B, Hkv, n, d, dtype):
+    x = torch.tensor(r.standard_normal((B, Hkv, n, d)) * r.uniform(0.01, 30, (B, Hkv, n, 1)),
+                     dtype=torch.float32)
+    x[0, 0, 3] = 0.0                                   # an all-zero row
+    x[0, 0, 5, 7] = float("nan")
+    x[0, 0, 6, 1] = float("inf")
+    x[0, 0, 6, 2] = -float("inf")
+    x[0, Hkv - 1, n - 1, :] = 2.5                      # a constant row: codes 127
+    return x.to(dtype)
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64),
+                                     (torch.float32, 128)])
+@pytest.mark.parametrize("pinned", [False, True])
+def test_kv_quantize_int8_bit_exact(dtype, d, pinned):
+    """Codes and scales of every row equal the oracle's (the same fp32 decisions), for device
+    and pinned host destinations, a row range, zero, constant and non-finite rows."""
+    say("kv-quantize", dtype, d, pinned)
+    r = np.random.default_rng(d + pinned)
+    B, Hkv, n = 2, 3, 777
+    x = _t2_rows(r, B, Hkv, n, d, dtype)
+    src = x.to(DEV) if not pinned else x.pin_memory()
+    if pinned:
+        codes = torch.full((B, Hkv, n, d), 99, dtype=torch.int8).pin_memory()
+        sc = torch.full((B, Hkv, n), -1.0).pin_memory()
+    else:
+        codes = torch.full((B, Hkv, n, d), 99, dtype=torch.int8, device=DEV)
+        sc = torch.full((B, Hkv, n), -1.0, device=DEV)
+    lo, hi = 5, n - 3
+    spk.kv_quantize_int8(src, codes, sc, lo, hi)
+    torch.cuda.synchronize()
+    ref_c, ref_s = oracle.quantize_int8(host(x)[:, :, lo:hi])
+    got_c, got_s = codes.cpu().numpy(), sc.cpu().numpy()
+    assert np.array_equal(got_c[:, :, lo:hi], ref_c)
+    assert np.array_equal(got_s[:, :, lo:hi].view(np.uint32), ref_s.view(np.uint32))
+    assert (got_c[:, :, :lo] == 99).all() and (got_c[:, :, hi:] == 99).all()
+    assert (got_s[:, :, :lo] == -1).all() and (got_s[:, :, hi:] == -1).all()
+
+
+def test_t2_fetch_dequantizes_bit_exact_into_staging_rows():
+    """The listed rows' codes (in pinned host memory) come back as the oracle's bf16 rows, in
+    row stage_base + slot of every KV head; nothing else of the pools is written."""
+    say("t2-fetch")
+    r = np.random.default_rng(31)
+    B, Hkv, n, d, base, cap = 2, 3, 500, 128, 200, 64
+    x = _t2_rows(r, B, Hkv, n, d, torch.bfloat16)
+    ck = torch.empty((B, Hkv, n, d), dtype=torch.int8).pin_memory()
+    cv = torch.empty_like(ck).pin_memory()
+    sk = torch.empty((B, Hkv, n)).pin_memory()
+    sv = torch.empty_like(sk).pin_memory()
+    spk.kv_quantize_int8(x.to(DEV), ck, sk)
+    spk.kv_quantize_int8((x * 3).to(DEV), cv, sv)
+    k = torch.full((B, Hkv, base + cap, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    v = torch.full_like(k, 7.0)
+    cnt = [37, 0]
+    tok = torch.zeros((B, cap), dtype=torch.int32)
+    slot = torch.zeros((B, cap), dtype=torch.int32)
+    tok[0, :37] = torch.tensor(r.choice(n, 37, replace=False))
+    slot[0, :37] = torch.tensor(r.permutation(cap)[:37])
+    spk.t2_fetch(ck, cv, sk, sv, k, v, base, tok.to(DEV), slot.to(DEV),
+                 torch.tensor(cnt, dtype=torch.int32, device=DEV), cap)
+    torch.cuda.synchronize()
+    kk, vv = host(k), host(v)
+    rk = oracle.dequantize_int8(ck.numpy(), sk.numpy())
+    rv = oracle.dequantize_int8(cv.numpy(), sv.numpy())
+    written = np.zeros((B, base + cap), bool)
+    for j in range(cnt[0]):
+        t, sl = int(tok[0, j]), base + int(slot[0, j])
+        written[0, sl] = True
+        assert np.array_equal(kk[0, :, sl], rk[0, :, t]) and np.array_equal(vv[0, :, sl], rv[0, :, t])
+    seven = oracle.encode_bf16(np.float32(7.0))
+    assert (kk[~written[:, None, :].repeat(Hkv, 1)] == seven).all()
+    assert (vv[~written[:, None, :].repeat(Hkv, 1)] == seven).all()
+
+
+@pytest.mark.parametrize("n,cap", [(1000, 260), (20000, 5000)])
+def test_residency_tier_classes_stage_t2_rows(n, cap):
+    """residency_update with the T2 classes against the oracle's residency of the T2 rows
+    alone, over three tier changes: every T2 row holds a staging slot, a row that stays in T2
+    keeps it, and the copy list holds exactly the rows new to T2."""
+    say("t2-staging", n, cap)
+    r = np.random.default_rng(n)
+    B = 2
+    loc = torch.tensor(np.array([[~i for i in range(n)]] * B, np.int32), device=DEV)
+    ct = torch.full((B, cap), -7, dtype=torch.int32, device=DEV)
+    cs = torch.full((B, cap), -7, dtype=torch.int32, device=DEV)
+    cc = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    tier = r.choice(np.array([0, 1, 2, 3], np.uint8), size=(B, n), p=[0.3, 0.35, 0.2, 0.15])
+    for it in range(3):
+        # a few rows change tier each time
+        flip = r.random((B, n)) < 0.1
+        tier = np.where(flip, r.choice(np.array([0, 1, 2, 3], np.uint8), size=(B, n)), tier)
+        for b in range(B):                              # keep the T2 count within the capacity
+            t2 = np.nonzero(tier[b] == 2)[0]
+            tier[b, t2[cap:]] = 3
+        s = (r.integers(0, 50, size=(B, n)) / 7).astype(np.float32)
+        loc_in = loc.cpu().numpy().copy()
+        spk.residency_update(torch.tensor(tier, device=DEV), torch.tensor(s, device=DEV), n, cap,
+                             loc, ct, cs, cc, tier_classes=spk.TIERS_T2)
+        torch.cuda.synchronize()
+        for b in range(B):
+            only_t2 = np.where(tier[b] == 2, 0, 3).astype(np.uint8)
+            ref_loc, ref_cp = oracle.residency_update(only_t2, s[b], loc_in[b], n, cap)
+            assert loc.cpu().numpy()[b].tolist() == ref_loc.tolist(), (it, b)
+            k = int(cc[b])
+            assert k == len(ref_cp)
+            got = list(zip(ct.cpu().numpy()[b, :k].tolist(), cs.cpu().numpy()[b, :k].tolist()))
+            assert got == ref_cp
+            assert set(np.nonzero(ref_loc >= 0)[0].tolist()) == set(np.nonzero(tier[b] == 2)[0].tolist())
+
+
+def _t2_decoder(w, caches, hbm_rows, p012, every=2):
+    host_pools = [(k.cpu().pin_memory(), v.cpu().pin_memory()) for k, v in caches]
+    codes = []
+    for k, v in caches:
+        c = []
+        for x in (k, v):
+            cx = torch.empty(x.shape, dtype=torch.int8).pin_memory()
+            sx = torch.empty(x.shape[:3]).pin_memory()
+            spk.kv_quantize_int8(x, cx, sx)
+            c.append((cx, sx))
+        codes.append((c[0][0], c[1][0], c[0][1], c[1][1]))
+    stage = (w.N * (p012 - w.t01_permille)) // 1000 + 1
+    hbm = [(torch.zeros((w.B, w.Hkv, hbm_rows + stage, w.d), dtype=torch.bfloat16, device=DEV),
+            torch.zeros((w.B, w.Hkv, hbm_rows + stage, w.d), dtype=torch.bfloat16, device=DEV))
+           for _ in range(w.layers)]
+    return TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
+                        host_caches=host_pools, hbm_rows=hbm_rows, reassign_every=every,
+                        t012_permille=p012, t2_codes=codes)
+
+
+def test_tiered_t2_matches_oracle_and_is_bit_identical_across_capacities():
+    """The T2 tier end to end: tiers bit-exact from the GPU's own state, attention and
+    importance against the oracle (which quantizes the rows itself), and the outputs identical
+    bit for bit whatever the HBM capacity (rows staged, resident or read from host memory)."""
+    w = W.scaled(W.REASONING_TIERS, B=2, layers=2, Hq=8, Hkv=2, N=1400, n_start=900,
+                 grow_per_step=100, steps=5, n_recent=64)
+    p012 = 950
+    say("tiered-t2", w.name)
+    caches = [(W.kv_cache(w, "k", l, DEV, n_cap=w.N), W.kv_cache(w, "v", l, DEV, n_cap=w.N))
+              for l in range(w.layers)]
+    small = _t2_decoder(w, caches, 300, p012)
+    large = _t2_decoder(w, caches, w.N, p012, every=1)
+    scale = oracle.softmax_scale(w.d)
+    staged_total = 0
+    for t in range(w.steps):
+        n = w.n_start + w.grow_per_step * t
+        qs = [W.queries(w, step=t, layer=l, device=DEV) for l in range(w.layers)]
+        s_in = small.s.cpu().numpy().copy()
+        ev_in = small.evicted.cpu().numpy().astype(bool)
+        o1, l1 = small.step(qs, n, dense=(t == 0))
+        o1, l1 = o1.clone(), l1.clone()
+        o2, l2 = large.step(qs, n, dense=(t == 0))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), t
+        assert torch.equal(small.s, large.s) and torch.equal(small.tier, large.tier), t
+        if t > 0:
+            staged_total += int((small.tier[:, :n] == 2).sum())
+        for b in range(w.B):
+            qb = np.stack([host(qs[l])[b, 0] for l in range(w.layers)])
+            kb = np.stack([np.stack([host(caches[l][0][b, h]) for h in range(w.Hkv)]) for l in range(w.layers)])
+            vb = np.stack([np.stack([host(caches[l][1][b, h]) for h in range(w.Hkv)]) for l in range(w.layers)])
+            r = osteps.tiered_sequence_step(s_in[b], ev_in[b], qb, kb, vb, n, scale, w.n_sink,
+                                            w.n_recent, w.t0_permille, w.t01_permille,
+                                            dense=(t == 0), t012_permille=p012)
+            if t > 0:
+                assert small.tier.cpu().numpy()[b, :n].tolist() == r["tier"].tolist()
+                c = int(small.count.cpu()[b])
+                assert small.sel.cpu().numpy()[b, :c].tolist() == r["tokens"].tolist()
+            check_attn(o1.cpu().numpy()[:, b, 0], r["out"], what="tiered T2 attention")
+            check_rows(small.s.cpu().numpy()[b, :n][None], r["s"][None], what="importance")
+    assert staged_total > 0 and int(small.t2_fetched) > 0
+    # a row that stays in T2 is fetched once: fewer fetches than staged rows over the steps
+    assert int(small.t2_fetched) < staged_total
 
 
 def test_windowed_scores_several_predictors_and_d64():
