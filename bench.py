@@ -37,6 +37,9 @@ Workloads:
                resident set is recomputed and only newly resident rows are copied over PCIe;
                the attention reads the other selected rows from host memory.  Timed with the
                copies before the first layer and overlapped layer by layer with the attention.
+  tiers_offload_t2  the offload episode with a T2 tier: the rows ranked 75-95 % are attended
+               from their 8-bit copy in pinned host memory (staged into HBM, fetched when new
+               to T2), the last 5 % evicted; timed against the same rows at full precision.
   tiers_offload_32k  the offload episode at batch 8 growing 8192 -> 32768 tokens, 16384 HBM
                slots per sequence; every step's outputs are checked bit for bit against the
                same episode with every row in HBM.
@@ -70,7 +73,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="all",
                     choices=["all", "block", "block_windowed", "per_head", "spec_verify", "tiers",
-                             "tiers_offload", "tiers_offload_32k", "block_lookahead"])
+                             "tiers_offload", "tiers_offload_32k", "tiers_offload_t2",
+                             "block_lookahead"])
     ap.add_argument("--hbm-rows", type=int, default=None,
                     help="tiers_offload: HBM slots per sequence (the rest stays in host memory; "
                          "default half the final context)")
@@ -952,6 +956,122 @@ def bench_tiers_offload(args, w=None, check_identity=False):
     return res, ctx
 
 
+def bench_tiers_t2(args):
+    """The offload episode with the T2 tier: rows ranked between 75 % and 95 % of the unprotected
+    ones are attended from their 8-bit copy in pinned host memory (staged into HBM rows,
+    fetched only when new to T2), the last 5 % evicted.  Timed against the same episode with
+    those rows in T1 (full precision, read from host memory where they hold no HBM slot): the
+    same attended rows, twice the PCIe bytes for each."""
+    import workloads as W
+    import sparse_top_kv_gqa_amd as spk
+    from sparse_top_kv_gqa_amd.decode import TieredDecode
+
+    w = W.REASONING_TIERS
+    p012 = 950
+    steps = w.steps
+    n_steps = min(args.steps or steps, steps)
+    cap, every = (args.hbm_rows or w.N // 2), args.reassign_every
+    stage = (w.N * (p012 - w.t01_permille)) // 1000 + 1
+    log(f"generating {w.layers} layer caches of {w.name}, pinned host pools and 8-bit codes")
+    host_pools, codes, hbm = [], [], []
+    for l in range(w.layers):
+        pair, cpair = [], []
+        for which in ("k", "v"):
+            t = W.kv_cache(w, which, l, "cuda", n_cap=w.N)
+            h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+            h.copy_(t)
+            c = torch.empty(t.shape, dtype=torch.int8, pin_memory=True)
+            sc = torch.empty(t.shape[:3], dtype=torch.float32, pin_memory=True)
+            spk.kv_quantize_int8(t, c, sc)
+            torch.cuda.synchronize()
+            pair.append(h)
+            cpair.append((c, sc))
+            del t
+        host_pools.append(tuple(pair))
+        codes.append((cpair[0][0], cpair[1][0], cpair[0][1], cpair[1][1]))
+        hbm.append((torch.zeros((w.B, w.Hkv, cap + stage, w.d), dtype=torch.bfloat16, device="cuda"),
+                    torch.zeros((w.B, w.Hkv, cap + stage, w.d), dtype=torch.bfloat16, device="cuda")))
+    qs = [[W.queries(w, step=t, layer=l, device="cuda") for l in range(w.layers)]
+          for t in range(steps)]
+    t2 = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
+                      host_caches=host_pools, hbm_rows=cap, reassign_every=every,
+                      t012_permille=p012, t2_codes=codes)
+    full = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, p012,
+                        host_caches=host_pools, hbm_rows=cap, reassign_every=every)
+    n_at = [w.n_start + w.grow_per_step * (t + 1) for t in range(steps)]
+    stream = torch.cuda.Stream()
+
+    def run_episode(d, record=None):
+        d.reset()
+        for t in range(n_steps):
+            d.step(qs[t], n_at[t], dense=(t == 0))
+            if record is not None:
+                ids = (d.dense_idx if t == 0 else d.sel).long().clamp(0, w.N - 1)
+                m = torch.arange(w.N, device="cuda")[None, :] < d.count[:, None].long()
+                loc = d.loc_attn if (d.t2 and t > 0) else d.loc
+                host_rows = ((torch.gather(loc, 1, ids) < 0) & m).sum()
+                t2_rows = ((d.tier[:, :n_at[t]] == 2).sum() if t > 0 else torch.zeros(()))
+                record.append((int(d.count.sum()), int(host_rows), int(t2_rows),
+                               int(d.t2_fetched) if d.t2 else 0))
+
+    def timed(d):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run_episode(d)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    rec_t2, rec_full = [], []
+    with torch.cuda.stream(stream):
+        run_episode(t2, rec_t2)
+        torch.cuda.synchronize()
+        out_t2 = t2.out.clone()
+        run_episode(full, rec_full)
+        torch.cuda.synchronize()
+        diff = (t2.out - full.out).abs().max().item() / full.out.abs().max().item()
+        ms_t2 = timed(t2)
+        ms_full = timed(full)
+        assert torch.equal(t2.out, out_t2), "T2 episode not reproducible"
+    per_row = w.Hkv * w.layers * ROW_BYTES                        # K and V, every layer and head
+    per_code = w.Hkv * w.layers * (2 * w.d + 2 * 4)               # codes and scales of K and V
+    fetched = rec_t2[-1][3]
+    pcie_t2 = (sum(h for _, h, _, _ in rec_t2) * per_row + fetched * per_code) / n_steps
+    pcie_full = sum(h for _, h, _, _ in rec_full) * per_row / n_steps
+    sel_bytes = sum(r for r, _, _, _ in rec_t2) * per_row / n_steps
+    res = base_result(w, n_steps, 0, ms_t2 / n_steps, sel_bytes, {
+        "workload": w.name + "_offload_t2", "batch": w.B, "layers": w.layers, "q_heads": w.Hq,
+        "kv_heads": w.Hkv, "head_dim": w.d, "context_start": w.n_start,
+        "context_end": n_at[n_steps - 1], "decode_steps": n_steps,
+        "tier_permille": [w.t0_permille, w.t01_permille, p012],
+        "hbm_rows_per_sequence": cap, "t2_staging_rows_per_sequence": stage,
+        "reassign_every": every,
+        "ms_per_step_same_rows_full_precision": round(ms_full / n_steps, 5),
+        "pcie_bytes_per_step_t2": int(pcie_t2), "pcie_bytes_per_step_full_precision": int(pcie_full),
+        "t2_rows_per_step_avg": round(sum(r for _, _, r, _ in rec_t2) / max(1, n_steps - 1), 1),
+        "t2_rows_fetched_per_step_avg": round(fetched / max(1, n_steps - 1), 1),
+        "max_rel_output_change_vs_full_precision_last_step": float(f"{diff:.3e}")})
+    # the last step's attention of one layer, rows staged or resident in HBM or on the host
+    k0, v0 = hbm[0]
+    kh0, vh0 = host_pools[0]
+    n_last = n_at[n_steps - 1]
+
+    def attn(i):
+        spk.sparse_decode_attn(qs[n_steps - 1][0], k0, v0, t2.sel, t2.count, "per_seq", n_last,
+                               out=t2.out[0], lse=t2.lse[0], logits=t2.logits[0], ws=t2.ws,
+                               k_host=kh0, v_host=vh0, loc=t2.loc_attn_view, stream=stream)
+    gather_ms = gather_kernel_ms(attn, 5, stream)
+    host_last = rec_t2[-1][1] * w.Hkv * ROW_BYTES
+    res["roofline"] = roofline(f"attn_partial_mfma_kernel (host rows of one layer at {n_last} "
+                               "tokens, T2 rows staged in HBM)", host_last, gather_ms,
+                               bound="pcie", peak=PCIE_PEAK_GBS,
+                               note=f"HBM rows of the same launch: "
+                                    f"{(rec_t2[-1][0] - rec_t2[-1][1]) * w.Hkv * ROW_BYTES} bytes")
+    ctx = dict(w=w, caches=host_pools, qs=qs, n_last=n_last, t012=p012)
+    return res, ctx
+
+
 def bench_lookahead(args):
     """Block decode through 8 layers with host-only blocks: lookahead vs none vs all in HBM."""
     import workloads as W
@@ -1115,7 +1235,8 @@ def cpu_tiers(ctx, seconds):
         s_prev = np.random.default_rng(b).random(n).astype(np.float32)
         t0 = time.perf_counter()
         osteps.tiered_sequence_step(s_prev, None, qb, kb, vb, n, scale, w.n_sink, w.n_recent,
-                                    w.t0_permille, w.t01_permille)
+                                    w.t0_permille, w.t01_permille,
+                                    t012_permille=ctx.get("t012"))
         spent += time.perf_counter() - t0
         done += 1
         if spent >= seconds:
@@ -1129,7 +1250,7 @@ def cpu_tiers(ctx, seconds):
 
 HEADLINE = "per_head"
 ORDER = ["per_head", "block", "block_windowed", "spec_verify", "tiers", "tiers_offload",
-         "tiers_offload_32k", "block_lookahead"]
+         "tiers_offload_32k", "tiers_offload_t2", "block_lookahead"]
 
 
 def run_workload(name, args):
@@ -1143,6 +1264,9 @@ def run_workload(name, args):
         cpu = cpu_token
     elif name == "tiers_offload":
         res, ctx = bench_tiers_offload(args)
+        cpu = cpu_tiers
+    elif name == "tiers_offload_t2":
+        res, ctx = bench_tiers_t2(args)
         cpu = cpu_tiers
     elif name == "tiers_offload_32k":
         import workloads as W
