@@ -11,6 +11,9 @@
 // the 8-dim slice of every query vector the group scores (NS <= 16 of them) in registers, forms
 // partial dots, and a 16-lane DPP reduction finishes them.  Scores are staged in LDS and written
 // back as contiguous runs per output row.
+#include <algorithm>
+#include <type_traits>
+
 #include "select_common.h"
 
 namespace spk {
@@ -20,11 +23,16 @@ namespace {
 #define SPK_INDEX_UNROLL 4        // key loads in flight per lane
 #endif
 #ifndef SPK_INDEX_MAX_ROWS
-#define SPK_INDEX_MAX_ROWS 256    // candidate rows per workgroup (LDS score tile)
+#define SPK_INDEX_MAX_ROWS 256    // candidate rows per workgroup of the block kernels
 #endif
 constexpr int kThreads = 256;
 constexpr int kUnroll = SPK_INDEX_UNROLL;
 constexpr int kMaxRowsPerWg = SPK_INDEX_MAX_ROWS;
+// Token scoring: a 16 KB LDS score tile, so a workgroup takes 4096 / NS rows (1024 for four
+// score vectors) and writes each score row's part as one run of up to 4 KB: fewer, longer
+// write runs than 1 KB ones interleave less with the key reads.
+constexpr int kTileFloats = 4096;
+constexpr int rows_cap(int ns_pad) { return kTileFloats / ns_pad; }
 
 // Fetch 8 elements [off, off+8) of the query tensor as floats.
 __device__ __forceinline__ void load_q8(const void* q, int q_bf16, int64_t off, float (&x)[8]) {
@@ -70,7 +78,24 @@ __device__ __forceinline__ int64_t score_row(int mode, int b, int kvh, int n, in
   return (int64_t)(b * T + n) * Hkv + kvh;
 }
 
-template <int D, typename KT, int NS>
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Dot product of 8 bf16 keys (four packed pairs) with 8 bf16 query elements: four
+// v_dot2c_f32_bf16, whose products of two bf16 values are exact in fp32.
+__device__ __forceinline__ float dot8_bf16(const uint4& k, const uint32_t (&qp)[4]) {
+  float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.x),
+                                            __builtin_bit_cast(bf16x2_t, qp[0]), 0.f, false);
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.y),
+                                      __builtin_bit_cast(bf16x2_t, qp[1]), a, false);
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.z),
+                                      __builtin_bit_cast(bf16x2_t, qp[2]), a, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.w),
+                                         __builtin_bit_cast(bf16x2_t, qp[3]), a, false);
+}
+
+// DOT2: bf16 keys and bf16 query vectors used as they are (per-head token scores): the query
+// slice stays packed and each key load feeds dot2 instructions instead of conversions and FMAs.
+template <int D, typename KT, int NS, bool DOT2 = false>
 __global__ __launch_bounds__(kThreads) void index_rows_kernel(
     int mode, const void* __restrict__ q, int q_bf16, const KT* __restrict__ keys, int64_t k_sb,
     int64_t k_sh, int64_t k_sn, int T, int Hq, int Hkv, int G, int ns, int n_cand,
@@ -79,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void index_rows_kernel(
   constexpr int RPS = kWave / LPR;    // rows per wave per load
   constexpr int WAVES = kThreads / kWave;
   constexpr int STEP = WAVES * RPS;   // rows per workgroup per load
-  __shared__ float tile[NS][kMaxRowsPerWg];
+  __shared__ float tile[NS][rows_cap(NS)];
 
   const int group = blockIdx.y;
   const int b = group / Hkv, kvh = group % Hkv;
@@ -89,37 +114,70 @@ __global__ __launch_bounds__(kThreads) void index_rows_kernel(
   const int row1 = min(row0 + rows_per_wg, n_cand);
   if (row0 >= n_cand) return;
 
-  float qv[NS][8];
+  static_assert(!DOT2 || std::is_same<KT, uint16_t>::value, "the dot2 path takes bf16 keys");
+  const KT* base_ptr = keys + (int64_t)b * k_sb + (int64_t)kvh * k_sh + sub * 8;
+  // The first batch of key loads goes out before the query slices are fetched, and every later
+  // batch before the previous one is used, so the workgroup always has key bytes in flight.
+  Raw8<KT> raw[kUnroll];
+  auto issue = [&](Raw8<KT> (&dst)[kUnroll], int base) {
 #pragma unroll
-  for (int n = 0; n < NS; ++n) {
-    if (n < ns) {
-      query_slice<D>(mode, q, q_bf16, b, kvh, n, T, Hq, Hkv, G, sub, qv[n]);
-    } else {
+    for (int u = 0; u < kUnroll; ++u) {
+      const int row = base + (u * WAVES + wid) * RPS + slot;
+      dst[u].load(base_ptr + (int64_t)min(row, row1 - 1) * k_sn);  // past the end: re-read, unused
+    }
+  };
+  issue(raw, row0);
+  float qv[DOT2 ? 1 : NS][8];
+  uint32_t qp[DOT2 ? NS : 1][4];
+  if constexpr (DOT2) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qv[n][i] = 0.f;
+    for (int n = 0; n < NS; ++n) {
+      // per-head: score vector n is head n % G of token n / G (vectors past ns load the last
+      // one and are zeroed: no branch around the loads)
+      const int nn = min(n, ns - 1);
+      const int t = nn / G, hl = nn % G;
+      uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) +
+                                                ((int64_t)(b * T + t) * Hq + kvh * G + hl) * D +
+                                                sub * 8);
+      const bool keep = n < ns;
+      qp[n][0] = keep ? u.x : 0u;
+      qp[n][1] = keep ? u.y : 0u;
+      qp[n][2] = keep ? u.z : 0u;
+      qp[n][3] = keep ? u.w : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      if (n < ns) {
+        query_slice<D>(mode, q, q_bf16, b, kvh, n, T, Hq, Hkv, G, sub, qv[n]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[n][i] = 0.f;
+      }
     }
   }
 
-  const KT* base_ptr = keys + (int64_t)b * k_sb + (int64_t)kvh * k_sh + sub * 8;
   for (int base = row0; base < row1; base += STEP * kUnroll) {
-    Raw8<KT> raw[kUnroll];
+    Raw8<KT> nxt[kUnroll];
+    const bool more = base + STEP * kUnroll < row1;   // uniform over the workgroup
+    if (more) issue(nxt, base + STEP * kUnroll);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int row = base + (u * WAVES + wid) * RPS + slot;
-      raw[u].load(base_ptr + (int64_t)min(row, row1 - 1) * k_sn);  // past the end: re-read, unused
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int row = base + (u * WAVES + wid) * RPS + slot;
-      float x[8];
-      raw[u].to_float(x);
       float acc[NS];
+      if constexpr (DOT2) {
 #pragma unroll
-      for (int n = 0; n < NS; ++n) {
-        float a = 0.f;
+        for (int n = 0; n < NS; ++n) acc[n] = group_sum<LPR>(dot8_bf16(raw[u].u, qp[n]));
+      } else {
+        float x[8];
+        raw[u].to_float(x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = fmaf(qv[n][i], x[i], a);
-        acc[n] = group_sum<LPR>(a);
+        for (int n = 0; n < NS; ++n) {
+          float a = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = fmaf(qv[n][i], x[i], a);
+          acc[n] = group_sum<LPR>(a);
+        }
       }
       if (row < row1) {
 #pragma unroll
@@ -127,12 +185,18 @@ __global__ __launch_bounds__(kThreads) void index_rows_kernel(
           if (n % LPR == sub && n < ns) tile[n][row - row0] = acc[n];
       }
     }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) raw[u] = nxt[u];
+    }
   }
   __syncthreads();
   const int cnt = row1 - row0;
   for (int i = threadIdx.x; i < ns * cnt; i += kThreads) {
     const int n = i / cnt, r = i % cnt;
-    scores[score_row(mode, b, kvh, n, T, Hq, Hkv, G) * s_ld + row0 + r] = tile[n][r];
+    // streamed out: the scores are read once, by the selection that follows
+    __builtin_nontemporal_store(tile[n][r],
+                                scores + score_row(mode, b, kvh, n, T, Hq, Hkv, G) * s_ld + row0 + r);
   }
 }
 
@@ -224,14 +288,30 @@ spk_status launch_rows(int ns_pad, dim3 grid, hipStream_t st, int mode, const vo
                        const void* keys, int64_t k_sb, int64_t k_sh, int64_t k_sn, int T, int Hq,
                        int Hkv, int G, int ns, int n_cand, int rpw, float* scores, int64_t s_ld) {
   const KT* kp = reinterpret_cast<const KT*>(keys);
-#define SPK_ROWS(NSV)                                                                         \
-  hipLaunchKernelGGL((index_rows_kernel<D, KT, NSV>), grid, dim3(kThreads), 0, st, mode, q, \
-                     q_bf16, kp, k_sb, k_sh, k_sn, T, Hq, Hkv, G, ns, n_cand, rpw, scores, s_ld)
-  switch (ns_pad) {
-    case 1: SPK_ROWS(1); break;
-    case 4: SPK_ROWS(4); break;
-    case 8: SPK_ROWS(8); break;
-    default: SPK_ROWS(16); break;
+  // bf16 keys scored against bf16 query heads as they are: the dot2 path
+  const bool dot2 = std::is_same<KT, uint16_t>::value && q_bf16 && mode == SPK_IDX_TOKEN_PER_HEAD;
+#define SPK_ROWS(NSV, DT)                                                                     \
+  hipLaunchKernelGGL((index_rows_kernel<D, KT, NSV, DT>), grid, dim3(kThreads), 0, st, mode, \
+                     q, q_bf16, kp, k_sb, k_sh, k_sn, T, Hq, Hkv, G, ns, n_cand, rpw, scores,  \
+                     s_ld)
+  if constexpr (std::is_same<KT, uint16_t>::value) {
+    if (dot2) {
+      switch (ns_pad) {
+        case 1: SPK_ROWS(1, true); break;
+        case 4: SPK_ROWS(4, true); break;
+        case 8: SPK_ROWS(8, true); break;
+        default: SPK_ROWS(16, true); break;
+      }
+      return check_launch("sparse_index_score");
+    }
+  }
+  {
+    switch (ns_pad) {
+      case 1: SPK_ROWS(1, false); break;
+      case 4: SPK_ROWS(4, false); break;
+      case 8: SPK_ROWS(8, false); break;
+      default: SPK_ROWS(16, false); break;
+    }
   }
 #undef SPK_ROWS
   return check_launch("sparse_index_score");
@@ -551,9 +631,9 @@ spk_status launch_fused(int ns_pad, int groups, hipStream_t st, int mode, const 
 }
 
 // Rows per workgroup: enough workgroups to fill the chip several times over, within 16..256.
-int pick_rows_per_wg(int64_t rows_total, int step) {
+int pick_rows_per_wg(int64_t rows_total, int step, int max_rows = kMaxRowsPerWg) {
   const int64_t target_wgs = 4LL * num_cus();
-  int rpw = kMaxRowsPerWg;
+  int rpw = max_rows;
   while (rpw > step && rows_total / rpw < target_wgs) rpw /= 2;
   return rpw;
 }
@@ -615,7 +695,13 @@ extern "C" SPK_API spk_status sparse_index_score(spk_index_mode mode, const void
                : launch_blockraw<64, float>(ns_pad, grid, st, q, q_bf16, keys, k_sb, k_sh, k_sn, T,
                                             Hkv, ns, n_cand, block_size, bpw, scores, s_ld, pooled_out);
   }
-  const int rpw = pick_rows_per_wg((int64_t)n_cand * groups, step * kUnroll);
+  // Rows per workgroup: per-head scoring loads one query slice per score vector and prefers
+  // many small workgroups, one batch of key loads each (64 rows at d = 128: 186 us, against
+  // 206 at 128 rows, 214 at 256 and 220 at 1024 on the per-head 131072-token workload); the
+  // group mean sums G heads per vector first, a setup that larger workgroups amortize (the full
+  // 16 KB tile: 439 us against 509 at 256 rows on the speculative-verify workload).
+  const int max_rows = mode == SPK_IDX_TOKEN_PER_HEAD ? step * kUnroll : rows_cap(ns_pad);
+  const int rpw = pick_rows_per_wg((int64_t)n_cand * groups, step * kUnroll, max_rows);
   dim3 grid(ceil_div(n_cand, rpw), groups);
   if (d == 128)
     return k_dtype == SPK_BF16
