@@ -630,7 +630,8 @@ spk_status launch_fused(int ns_pad, int groups, hipStream_t st, int mode, const 
   return check_launch("sparse_index_topk");
 }
 
-// Rows per workgroup: enough workgroups to fill the chip several times over, within 16..256.
+// Rows per workgroup: max_rows, halved (not below `step`) while the launch would have fewer than
+// four workgroups per CU.
 int pick_rows_per_wg(int64_t rows_total, int step, int max_rows = kMaxRowsPerWg) {
   const int64_t target_wgs = 4LL * num_cus();
   int rpw = max_rows;
