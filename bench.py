@@ -336,11 +336,11 @@ def base_result(w, K, W, ms_step, step_bytes, config):
 COPY_KIB = 512 * 1024
 FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
-    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "86a3bcd5da6ea64f", 41362.1, 1442.48),
-    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "86a3bcd5da6ea64f", 41486.0, 1442.4),
-    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "8c1e000459e283fa", 524481.0, 65536.0),
-    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "86a3bcd5da6ea64f", 272565.0, 8544.53),
-    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "86a3bcd5da6ea64f", 401321.0, 51393.8),
+    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "f75036e77e260061", 524455.29, 65536.0),
+    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 41342.09, 1442.43),
+    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 41488.8, 1442.38),
+    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 272555.53, 8544.73),
+    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 401317.12, 51409.21),
 }
 
 
