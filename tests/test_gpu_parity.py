@@ -1341,6 +1341,99 @@ def test_tiered_t2_matches_oracle_and_is_bit_identical_across_capacities():
     assert int(small.t2_fetched) < staged_total
 
 
+def test_tiered_t2_full_context_sampled_steps():
+    """T2 at the offload episode's real context and heads (4096 -> 16384 tokens over 64 steps,
+    28/4 heads, 8192 HBM rows, reassignment every 8 steps, T0/T1/T2/T3 25/50/20/5 %), batch and
+    layers cut to 4: sampled sequences of the first steps and the last against the oracle's
+    T2 step from the GPU's own state."""
+    w = W.scaled(W.REASONING_TIERS, B=4, layers=4)
+    p012 = 950
+    say("tiered-t2-full", w.name)
+    caches = [(W.kv_cache(w, "k", l, DEV, n_cap=w.N), W.kv_cache(w, "v", l, DEV, n_cap=w.N))
+              for l in range(w.layers)]
+    dec = _t2_decoder(w, caches, 8192, p012, every=8)
+    scale = oracle.softmax_scale(w.d)
+    check_at = {1, 2, 9, w.steps - 1}
+    for t in range(w.steps):
+        n = w.n_start + w.grow_per_step * (t + 1)
+        qs = [W.queries(w, step=t, layer=l, device=DEV) for l in range(w.layers)]
+        if t in check_at:
+            s_in = dec.s.cpu().numpy().copy()
+            ev_in = dec.evicted.cpu().numpy().astype(bool)
+        out, lse = dec.step(qs, n, dense=(t == 0))
+        if t not in check_at:
+            continue
+        torch.cuda.synchronize()
+        say("tiered-t2-full step", t, "n", n)
+        assert int((dec.tier[:, :n] == 2).sum()) > 0
+        for b in (0, w.B - 1):
+            qb = np.stack([host(qs[l])[b, 0] for l in range(w.layers)])
+            kb = np.stack([host(caches[l][0][b, :, :n]) for l in range(w.layers)])
+            vb = np.stack([host(caches[l][1][b, :, :n]) for l in range(w.layers)])
+            r = osteps.tiered_sequence_step(s_in[b], ev_in[b], qb, kb, vb, n, scale, w.n_sink,
+                                            w.n_recent, w.t0_permille, w.t01_permille,
+                                            t012_permille=p012)
+            assert dec.tier[b, :n].cpu().numpy().tolist() == r["tier"].tolist()
+            c = int(dec.count[b])
+            assert dec.sel[b, :c].cpu().numpy().tolist() == r["tokens"].tolist()
+            check_attn(out[:, b, 0].cpu().numpy(), r["out"], what="tiered T2 attention")
+            check_rows(dec.s[b, :n].cpu().numpy()[None], r["s"][None], what="importance")
+    del caches, dec
+    _free()
+
+
+def test_lookahead_full_shape_sampled():
+    """Lookahead at the workload's real shape (32768 tokens, 8 layers, 32/8 heads, 32 blocks of
+    64, a seeded 1.8 % of the blocks host-only), batch 1: two steps bit-identical to all-HBM and
+    to in-kernel host reads, and two sampled groups of every layer against the oracle."""
+    w = W.scaled(W.LOOKAHEAD_BLOCK, B=1)
+    say("lookahead-full", w.name)
+    full, layers = _lookahead_layers(w)
+    pool_keys = [kf for kf, _ in full]
+    la = BlockLookaheadDecode(layers, pool_keys, w.N, w.Hq, w.block_size, w.k, w.n_sink,
+                              w.n_recent, lookahead=True)
+    no = BlockLookaheadDecode(layers, pool_keys, w.N, w.Hq, w.block_size, w.k, w.n_sink,
+                              w.n_recent, lookahead=False)
+    refs = [BlockSparseDecode(kf, vf, w.N, w.Hq, w.block_size, w.k, w.n_sink, w.n_recent,
+                              topk_in_attn=False) for kf, vf in full]
+    preds0 = [W.predictors(w, step=0, layer=l, device=DEV) for l in range(w.layers)]
+    for d_ in (la, no):
+        d_.pool(preds0)
+    for r_, p_ in zip(refs, preds0):
+        r_.pool(p_)
+    G, scale = w.G, oracle.softmax_scale(w.d)
+    staged = 0
+    for step in (1, 2):
+        qs = [W.queries(w, step=step, layer=l, device=DEV) for l in range(w.layers)]
+        preds = [W.predictors(w, step=step, layer=l, device=DEV) for l in range(w.layers)]
+        out_la = la.step(qs, preds)[0].clone()
+        out_no = no.step(qs, preds)[0]
+        torch.cuda.synchronize()
+        staged += sum(int(c.sum()) for c in la.staged_count)
+        for l in range(w.layers):
+            o_ref, _ = refs[l].step(qs[l], preds[l])
+            torch.cuda.synchronize()
+            assert torch.equal(out_la[l], o_ref) and torch.equal(out_no[l], o_ref), (step, l)
+        for h in (0, w.Hkv - 1):
+            res = osteps.block_layers(
+                [host(preds[l])[0, 0, h] for l in range(w.layers)],
+                [host(full[l][0][0, h]) for l in range(w.layers)],
+                [host(full[l][1][0, h]) for l in range(w.layers)],
+                [host(qs[l])[0, 0, h * G:(h + 1) * G] for l in range(w.layers)],
+                w.k, w.block_size, w.n_sink, w.n_recent, scale)
+            for l in range(w.layers):
+                sc = la.sel[l].scores.cpu().numpy()[0, 0, h]
+                sel = la.sel[l].idx.cpu().numpy()[0, 0, h]
+                assert sel.tolist() == oracle.topk(sc, w.k).tolist()
+                assert osteps.topk_band_ok(sel, res[l]["scores"], w.k, TOL)
+                if sel.tolist() == res[l]["blocks"].tolist():
+                    check_attn(out_la[l].cpu().numpy()[0, 0, h * G:(h + 1) * G], res[l]["out"],
+                               what=f"lookahead full layer {l}")
+    assert staged > 0
+    del full, layers, la, no, refs
+    _free()
+
+
 def test_windowed_scores_several_predictors_and_d64():
     """Windowed scoring with T = 3 predictor vectors per KV head (several score rows per
     group), d = 64 and fp32 predictors: every score row against the oracle."""
