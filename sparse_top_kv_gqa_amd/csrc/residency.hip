@@ -11,7 +11,9 @@
 // ascending, importance descending, index ascending).  A resident row that already holds a
 // slot keeps it; the other resident rows, in ascending token order, take the free slots in
 // ascending order.  Every row also lives in host memory at its token index, so loc[tok] is the
-// HBM slot of a resident row and ~tok otherwise — the form sparse_decode_attn reads.
+// HBM slot of a resident row and ~tok otherwise — the form sparse_decode_attn reads.  The
+// tiers' roles come as a table (2 bits per tier code: ranked first, ranked second, or never
+// resident): T0 then T1 for the HBM residency, T2 alone for the staging rows of the 8-bit tier.
 #include "select_common.h"
 
 namespace spk {
@@ -19,9 +21,9 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kItems = 16;                        // tokens per thread: n_tokens <= 16384
+constexpr int kItems = 16;                        // register path: n_tokens <= 16384
 constexpr int kMaxTokens = kItems * kThreads;
-constexpr int kSlotWords = kMaxTokens / 32;       // slot bitmap: capacity <= 16384
+constexpr int kSlotWords = kMaxTokens / 32;       // its slot bitmap: capacity <= 16384
 // Longer sequences: tokens are taken chunk by chunk from memory, the slot bitmap covers up to
 // 131072 slots (16 KB of LDS, and as much again for the free-slot prefixes).
 constexpr int kChunkCap = 131072;

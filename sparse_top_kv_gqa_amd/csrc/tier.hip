@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
   if constexpr (ITEMS > 0) {
     // ranks in index order (chunk c, then wave, then lane) from per-(chunk, wave) counts: one
     // barrier to publish the counts, one wave scan over them, one barrier to read the prefixes;
-    // first for the ties at each threshold, then for the T0 ∪ T1 list
+    // first for the ties at each threshold, then for the list of attended rows
     constexpr int NWV = kThreads / kWave;
     constexpr int NCW = ITEMS * NWV;
     const int lane = lane_id(), wid = threadIdx.x / kWave;
