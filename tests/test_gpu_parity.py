@@ -1564,6 +1564,39 @@ def test_graph_replays_of_decode_steps():
                                lambda: tok2.step(qt2))
 
 
+def test_graph_replays_of_union_and_lookahead_steps():
+    """The per-head step on rows wide enough for the union pipeline (histogram, bin, gather,
+    threshold, write, attention over the union) and the two-stream lookahead step (selection
+    ahead on one stream, the persistent copy kernel on another) replay from captured graphs
+    exactly, with other library work between replays."""
+    say("graph-replay-union-lookahead")
+    wt = W.scaled(W.PER_HEAD_2PCT, B=2, Hkv=2, Hq=8, N=20000, k=400)
+    kt = W.kv_cache(wt, "k", device=DEV)
+    vt = W.kv_cache(wt, "v", device=DEV)
+    tok = TokenSparseDecode(kt, vt, wt.N, wt.Hq, 1, wt.k, "token_per_head")
+    tok2 = TokenSparseDecode(kt, vt, wt.N, wt.Hq, 1, wt.k, "token_per_head")
+    assert tok.union
+    qt, qt2 = W.queries(wt, device=DEV), W.queries(wt, step=3, device=DEV)
+    _graph_replays_match_eager(lambda: tok.step(qt), [tok.out, tok.lse, tok.idx, tok.count],
+                               lambda: tok2.step(qt2))
+    w = W.scaled(W.LOOKAHEAD_BLOCK, B=2, Hkv=2, Hq=8, N=64 * 60 + 5, k=6, n_recent=64, layers=3,
+                 host_frac=0.3)
+    full, layers = _lookahead_layers(w)
+    pool_keys = [kf for kf, _ in full]
+    la = BlockLookaheadDecode(layers, pool_keys, w.N, w.Hq, w.block_size, w.k, w.n_sink,
+                              w.n_recent, lookahead=True)
+    other = BlockLookaheadDecode(layers, pool_keys, w.N, w.Hq, w.block_size, w.k, w.n_sink,
+                                 w.n_recent, lookahead=False)
+    preds0 = [W.predictors(w, step=0, layer=l, device=DEV) for l in range(w.layers)]
+    la.pool(preds0)
+    other.pool(preds0)
+    qs = [W.queries(w, step=1, layer=l, device=DEV) for l in range(w.layers)]
+    preds = [W.predictors(w, step=1, layer=l, device=DEV) for l in range(w.layers)]
+    qs2 = [W.queries(w, step=2, layer=l, device=DEV) for l in range(w.layers)]
+    _graph_replays_match_eager(lambda: la.step(qs, preds, stream=torch.cuda.current_stream()),
+                               [la.out, la.lse], lambda: other.step(qs2, preds))
+
+
 def test_concurrent_streams_match_sequential_calls():
     """Calls with distinct outputs and workspaces may run on concurrent streams: a block step and
     a per-head token step issued on two streams, several times without waits between, give
