@@ -146,14 +146,37 @@ __global__ __launch_bounds__(kThreads) void index_rows_kernel(
       qp[n][3] = keep ? u.w : 0u;
     }
   } else {
+    // the query slices fetched once per workgroup (a group-mean vector sums G head slices): the
+    // first row slot of wave w builds vectors w, w + 4, ... into LDS and every lane reads its
+    // slice back after one barrier, instead of every row slot issuing the same loads
+    __shared__ uint4 qsh[NS][2 * LPR];
+    if (slot == 0) {
+      for (int n = wid; n < NS; n += WAVES) {
+        float x[8];
+        if (n < ns) {
+          query_slice<D>(mode, q, q_bf16, b, kvh, n, T, Hq, Hkv, G, sub, x);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = 0.f;
+        }
+        qsh[n][2 * sub] = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]),
+                                     __float_as_uint(x[2]), __float_as_uint(x[3]));
+        qsh[n][2 * sub + 1] = make_uint4(__float_as_uint(x[4]), __float_as_uint(x[5]),
+                                         __float_as_uint(x[6]), __float_as_uint(x[7]));
+      }
+    }
+    __syncthreads();
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-      if (n < ns) {
-        query_slice<D>(mode, q, q_bf16, b, kvh, n, T, Hq, Hkv, G, sub, qv[n]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[n][i] = 0.f;
-      }
+      const uint4 a0 = qsh[n][2 * sub], a1 = qsh[n][2 * sub + 1];
+      qv[n][0] = __uint_as_float(a0.x);
+      qv[n][1] = __uint_as_float(a0.y);
+      qv[n][2] = __uint_as_float(a0.z);
+      qv[n][3] = __uint_as_float(a0.w);
+      qv[n][4] = __uint_as_float(a1.x);
+      qv[n][5] = __uint_as_float(a1.y);
+      qv[n][6] = __uint_as_float(a1.z);
+      qv[n][7] = __uint_as_float(a1.w);
     }
   }
 
@@ -699,9 +722,12 @@ extern "C" SPK_API spk_status sparse_index_score(spk_index_mode mode, const void
   // Rows per workgroup: per-head scoring loads one query slice per score vector and prefers
   // many small workgroups, one batch of key loads each (64 rows at d = 128: 186 us, against
   // 206 at 128 rows, 214 at 256 and 220 at 1024 on the per-head 131072-token workload); the
-  // group mean sums G heads per vector first, a setup that larger workgroups amortize (the full
-  // 16 KB tile: 439 us against 509 at 256 rows on the speculative-verify workload).
-  const int max_rows = mode == SPK_IDX_TOKEN_PER_HEAD ? step * kUnroll : rows_cap(ns_pad);
+  // group mean builds its vectors once per workgroup in LDS and does best at 256 rows (416 us,
+  // against 441 at 1024 and 551 at 64 on the speculative-verify workload); block scores take
+  // the whole tile, halved until the launch fills the chip.
+  const int max_rows = mode == SPK_IDX_TOKEN_PER_HEAD   ? step * kUnroll
+                       : mode == SPK_IDX_TOKEN_GROUP_MEAN ? std::min(256, rows_cap(ns_pad))
+                                                          : rows_cap(ns_pad);
   const int rpw = pick_rows_per_wg((int64_t)n_cand * groups, step * kUnroll, max_rows);
   dim3 grid(ceil_div(n_cand, rpw), groups);
   if (d == 128)
