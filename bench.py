@@ -336,7 +336,7 @@ def base_result(w, K, W, ms_step, step_bytes, config):
 COPY_KIB = 512 * 1024
 FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
-    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "f75036e77e260061", 524455.29, 65536.0),
+    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "287cc4daa3667617", 524455.28, 65536.0),
     "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 41342.09, 1442.43),
     "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 41488.8, 1442.38),
     "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 272555.53, 8544.73),
