@@ -23,7 +23,8 @@ Every function cites the passage it follows by page title and section:
   Eficiência de Carga" (queries share the retrieval of missing rows), "A Inovação"
   (optional residency of rows in HBM while memory allows).
 * "Nem Todos os Pensamentos Necessitam de HBM" §4 "Implementação do Sistema"
-  (differential prefetch of newly promoted rows) — residency_update.
+  (differential prefetch of newly promoted rows) — residency_update; §1 (the recent window is
+  protected T0) — residency_append, the slots of rows added since the last step.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 closed forms, invariants, brute force on tiny inputs or an independent library
@@ -51,6 +52,7 @@ from .core import (  # noqa: F401
     importance_update,
     tier_classify,
     residency_update,
+    residency_append,
     softmax_scale,
 )
 from . import steps  # noqa: F401

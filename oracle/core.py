@@ -358,6 +358,31 @@ def residency_update(tier, s, loc_old, n_tokens: int, capacity: int):
     return loc, copies
 
 
+def residency_append(loc_old, n_old: int, n_new: int, capacity: int):
+    """HBM slots of the rows a sequence gained since the last step.
+
+    "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro Níveis" (the
+    recent window is protected, so a new row is T0, and T0 stays in HBM); "O Fim do Gargalo de
+    Memória ...", "A Inovação" (rows are kept in HBM while memory allows).  Reading taken: a
+    row's K/V are produced on the GPU, so each new row is written into an HBM slot if one is
+    free: the new rows [n_old, n_new), in ascending token order, take the slots 0..capacity-1
+    that no row below n_old holds (0 <= loc_old < capacity), in ascending slot order; rows left
+    without a slot are read from host memory (~tok) until the next reassignment.
+
+    Returns (loc_new ``[n_new]`` int64, copies: list of (tok, slot), ascending tok).
+    """
+    old = np.asarray(loc_old, dtype=np.int64)[:n_old]
+    held = {int(x) for x in old if 0 <= x < capacity}
+    free = [sl for sl in range(capacity) if sl not in held]
+    loc = np.concatenate([old, np.array([~t for t in range(n_old, n_new)], dtype=np.int64)])
+    copies = []
+    for t in range(n_old, n_new):
+        if len(copies) < len(free):
+            loc[t] = free[len(copies)]
+            copies.append((t, free[len(copies)]))
+    return loc, copies
+
+
 def softmax_scale(d: int) -> float:
     """Softmax temperature 1/sqrt(d) (the pages do not state one; the usual choice)."""
     return 1.0 / math.sqrt(d)

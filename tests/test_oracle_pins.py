@@ -368,6 +368,58 @@ def test_tier_invariants_with_t2():
     assert s[tier == 1].min() >= s[tier == 2].max() >= s[tier == 3].max()
 
 
+# ------------------------------------------------------------------ appended rows
+
+def test_residency_append_hand_example_and_edges():
+    # capacity 6; rows 0..4 hold slots 2, 0, 5 (rows 1 and 4 on the host): free 1, 3, 4
+    loc_old = np.array([2, ~1, 0, 5, ~4])
+    loc, cp = oracle.residency_append(loc_old, 5, 9, 6)
+    assert cp == [(5, 1), (6, 3), (7, 4)]
+    assert loc.tolist() == [2, ~1, 0, 5, ~4, 1, 3, 4, ~8]
+    # nothing new; no capacity; a slot at or past the capacity is not held
+    assert oracle.residency_append(loc_old, 5, 5, 6)[1] == []
+    loc, cp = oracle.residency_append(loc_old, 5, 7, 0)
+    assert cp == [] and loc.tolist()[5:] == [~5, ~6]
+    loc, cp = oracle.residency_append(np.array([7, 0]), 2, 4, 3)
+    assert cp == [(2, 1), (3, 2)] and loc.tolist()[:2] == [7, 0]
+
+
+@pytest.mark.parametrize("trial", range(20))
+def test_residency_append_invariants(trial):
+    r = np.random.default_rng(300 + trial)
+    cap = int(r.integers(0, 40))
+    n_old = int(r.integers(0, 60))
+    n_new = n_old + int(r.integers(0, 30))
+    slots = r.permutation(max(cap, 1))[:min(cap, n_old)] if cap else np.array([], int)
+    loc_old = np.array([~t for t in range(n_old)], dtype=np.int64)
+    who = r.permutation(n_old)[:len(slots)]
+    loc_old[who] = slots[:len(who)]
+    loc, cp = oracle.residency_append(loc_old, n_old, n_new, cap)
+    held = {int(x) for x in loc_old if 0 <= x < cap}
+    free = sorted(set(range(cap)) - held)
+    assert np.array_equal(loc[:n_old], loc_old)                       # held rows untouched
+    assert len(cp) == min(n_new - n_old, len(free))
+    assert [t for t, _ in cp] == list(range(n_old, n_old + len(cp)))   # oldest new rows first
+    assert [sl for _, sl in cp] == free[:len(cp)]                      # lowest free slots
+    res = [int(x) for x in loc if 0 <= x < cap]
+    assert len(res) == len(set(res))                                   # slots distinct
+    for t in range(n_old + len(cp), n_new):
+        assert loc[t] == ~t
+
+
+def test_residency_append_then_reassignment_keeps_the_slots():
+    # after an append, a reassignment that keeps the new rows resident leaves them in place
+    n_old, n_new, cap = 40, 48, 60
+    tier = np.ones(n_new, np.uint8)
+    s = np.linspace(1, 2, n_new).astype(np.float32)
+    loc0, _ = oracle.residency_update(tier[:n_old], s[:n_old], [~t for t in range(n_old)],
+                                      n_old, cap)
+    loc1, cp = oracle.residency_append(loc0, n_old, n_new, cap)
+    assert len(cp) == n_new - n_old
+    loc2, cp2 = oracle.residency_update(tier, s, loc1, n_new, cap)
+    assert cp2 == [] and np.array_equal(loc2, loc1)
+
+
 # ------------------------------------------------------------------ T2: 8-bit rows
 
 def test_encode_bf16_matches_torch_rounding():
