@@ -845,8 +845,7 @@ def bench_tiers_offload(args, w=None, check_identity=False):
             h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
             h.copy_(t)
             pair.append(h)
-            if check_identity:
-                fpair.append(t)
+            fpair.append(t)     # the rows as the layer produced them, on the device
             del t
         host_pools.append(tuple(pair))
         full.append(tuple(fpair))
@@ -855,7 +854,7 @@ def bench_tiers_offload(args, w=None, check_identity=False):
     torch.cuda.synchronize()
     qs = [[W.queries(w, step=t, layer=l, device="cuda") for l in range(w.layers)]
           for t in range(steps)]
-    mk = dict(host_caches=host_pools, hbm_rows=cap, reassign_every=every)
+    mk = dict(host_caches=host_pools, hbm_rows=cap, reassign_every=every, producer_caches=full)
     dec = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille, **mk)
     dec_ov = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
                           overlap_prefetch=True, **mk)
@@ -865,18 +864,10 @@ def bench_tiers_offload(args, w=None, check_identity=False):
     n_steps = min(K, steps)
     stream = torch.cuda.Stream()
 
-    def reset(d):
-        d.s.zero_()
-        d.evicted.zero_()
-        if d.host is not None:
-            d.loc.copy_(~torch.arange(w.N, dtype=torch.int32, device="cuda").repeat(w.B, 1))
-            d.tiered_steps = 0
-            d.copies.zero_()
-
     def run_episode(d, record=None):
-        reset(d)
+        d.reset()
         if ref is not None and record is not None:
-            reset(ref)
+            ref.reset()
         for t in range(n_steps):
             d.step(qs[t], n_at[t], dense=(t == 0))
             if record is not None:
@@ -884,7 +875,8 @@ def bench_tiers_offload(args, w=None, check_identity=False):
                 m = torch.arange(w.N, device="cuda")[None, :] < d.count[:, None].long()
                 ids = sel.long().clamp(0, w.N - 1)     # entries past the count are unused
                 host_rows = ((torch.gather(d.loc, 1, ids) < 0) & m).sum()
-                record.append((int(d.count.sum()), int(host_rows), int(d.copies)))
+                record.append((int(d.count.sum()), int(host_rows), int(d.copies),
+                               int(d.appended)))
                 if ref is not None:
                     ref.step(qs[t], n_at[t], dense=(t == 0))
                     assert torch.equal(d.out, ref.out) and torch.equal(d.lse, ref.lse), \
@@ -913,12 +905,12 @@ def bench_tiers_offload(args, w=None, check_identity=False):
             "overlapped prefetch changed a result"
     if ref is not None:
         del ref
-        full.clear()
     ms_step = ms_total / n_steps
     per_layer = w.Hkv * w.layers * ROW_BYTES
-    sel_bytes = [r * per_layer for r, _, _ in rec]
-    pcie_attn = sum(h for _, h, _ in rec) * per_layer
+    sel_bytes = [r[0] * per_layer for r in rec]
+    pcie_attn = sum(r[1] for r in rec) * per_layer
     copies = rec[-1][2]
+    appended = rec[-1][3]
     pcie_copy = copies * per_layer
     bytes_avg = sum(sel_bytes) / n_steps
     # the last step's attention in one layer: its host rows cross PCIe inside the gather
@@ -941,7 +933,8 @@ def bench_tiers_offload(args, w=None, check_identity=False):
         "bit_identical_to_all_hbm_every_step": bool(check_identity),
         "bytes_per_step_avg": int(bytes_avg),
         "pcie_share_of_step_bytes": round((pcie_attn + pcie_copy) / max(1, sum(sel_bytes)), 4),
-        "host_fetch_fraction": round(sum(h for _, h, _ in rec) / max(1, sum(r for r, _, _ in rec)), 4),
+        "host_fetch_fraction": round(sum(r[1] for r in rec) / max(1, sum(r[0] for r in rec)), 4),
+        "rows_appended_to_hbm_episode": appended,
         "pcie_attention_bytes_per_step": int(pcie_attn / n_steps),
         "prefetch_bytes_episode": int(pcie_copy), "rows_copied_episode": copies,
         "episode_s": round(ms_total / 1e3, 4), "wall_s_timed": round(wall, 4),
@@ -973,9 +966,9 @@ def bench_tiers_t2(args):
     cap, every = (args.hbm_rows or w.N // 2), args.reassign_every
     stage = (w.N * (p012 - w.t01_permille)) // 1000 + 1
     log(f"generating {w.layers} layer caches of {w.name}, pinned host pools and 8-bit codes")
-    host_pools, codes, hbm = [], [], []
+    host_pools, codes, hbm, produced = [], [], [], []
     for l in range(w.layers):
-        pair, cpair = [], []
+        pair, cpair, ppair = [], [], []
         for which in ("k", "v"):
             t = W.kv_cache(w, which, l, "cuda", n_cap=w.N)
             h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
@@ -986,8 +979,10 @@ def bench_tiers_t2(args):
             torch.cuda.synchronize()
             pair.append(h)
             cpair.append((c, sc))
+            ppair.append(t)     # the rows as the layer produced them, on the device
             del t
         host_pools.append(tuple(pair))
+        produced.append(tuple(ppair))
         codes.append((cpair[0][0], cpair[1][0], cpair[0][1], cpair[1][1]))
         hbm.append((torch.zeros((w.B, w.Hkv, cap + stage, w.d), dtype=torch.bfloat16, device="cuda"),
                     torch.zeros((w.B, w.Hkv, cap + stage, w.d), dtype=torch.bfloat16, device="cuda")))
@@ -995,9 +990,10 @@ def bench_tiers_t2(args):
           for t in range(steps)]
     t2 = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
                       host_caches=host_pools, hbm_rows=cap, reassign_every=every,
-                      t012_permille=p012, t2_codes=codes)
+                      t012_permille=p012, t2_codes=codes, producer_caches=produced)
     full = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, p012,
-                        host_caches=host_pools, hbm_rows=cap, reassign_every=every)
+                        host_caches=host_pools, hbm_rows=cap, reassign_every=every,
+                        producer_caches=produced)
     n_at = [w.n_start + w.grow_per_step * (t + 1) for t in range(steps)]
     stream = torch.cuda.Stream()
 

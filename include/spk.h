@@ -585,13 +585,38 @@ SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier_ld,
                                     int32_t* copy_count, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * residency_append — HBM slots for the rows each sequence gained since the last step.
+ *
+ * Passages: "Nem Todos os Pensamentos Necessitam de HBM", §1 "Classificação de Quatro Níveis"
+ * (the recent window is protected, so a new row is T0, and T0 stays in HBM); "O Fim do Gargalo
+ * de Memória ...", "A Inovação" (rows are kept in HBM while memory allows).  Reading taken: a
+ * row's K/V are produced on the GPU, so the new rows [n_old, n_new), in ascending token order,
+ * take the slots 0..capacity-1 that no row below n_old holds (0 <= loc < capacity), in
+ * ascending slot order; rows left without a slot get loc = ~tok (read from host memory until
+ * the next reassignment).
+ *
+ *   loc        device int32 [B, loc_ld] (loc_ld >= n_new), in/out: entries below n_old are read,
+ *              entries [n_old, n_new) written.
+ *   copy_tok, copy_slot  device int32 [B, copy_ld], copy_ld >= min(n_new - n_old, capacity): the
+ *              r-th new row given a slot, and that slot (write its K/V there with
+ *              residency_prefetch from the pools that produced it).
+ *   copy_count device int32 [B]: the rows given a slot.
+ * Limits: capacity <= 131072 (SPK_EUNSUPPORTED).  One launch, one workgroup per sequence.
+ * ------------------------------------------------------------------------------------------ */
+SPK_API spk_status residency_append(int32_t* loc, int64_t loc_ld, int B, int n_old, int n_new,
+                                    int capacity, int32_t* copy_tok, int32_t* copy_slot,
+                                    int64_t copy_ld, int32_t* copy_count, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * residency_prefetch — copy the rows residency_update listed from the host pools into their
  * HBM slots, for every KV head of one layer (the differential prefetch of §4 "Implementação do
  * Sistema", "Nem Todos os Pensamentos Necessitam de HBM": rows cross PCIe only when they newly
  * need HBM; full precision, so the attention result is unchanged — Proposition 1).
  *
- *   k_host, v_host  pinned host pools (hipHostMalloc'ed; other memory: SPK_EINVAL), row
- *              (b,kvh,tok) at k_host + b*host_sb + kvh*host_sh + tok*host_sn, tok < host_slots.
+ *   k_host, v_host  the source pools: pinned host memory (hipHostMalloc'ed, read through its
+ *              device alias) or device memory (rows produced on the GPU, see residency_append);
+ *              other memory: SPK_EINVAL.  Row (b,kvh,tok) at k_host + b*host_sb + kvh*host_sh +
+ *              tok*host_sn, tok < host_slots.
  *   k_hbm, v_hbm    device pools, row (b,kvh,slot) at k_hbm + b*hbm_sb + kvh*hbm_sh +
  *              slot*hbm_sn, slot < hbm_slots.  Strides in elements; rows 16-byte aligned.
  *   copy_tok, copy_slot, copy_ld, copy_count: as residency_update wrote them.

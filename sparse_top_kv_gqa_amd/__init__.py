@@ -42,7 +42,7 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "topk_select_union_workspace_size", "topk_select_union",
            "sparse_decode_attn_union_workspace_size", "sparse_decode_attn_union",
            "lookahead_prefetch", "residency_update_tiers", "kv_quantize_int8", "t2_fetch",
-           "t2_locations")
+           "t2_locations", "residency_append")
 
 
 class SpkError(RuntimeError):
@@ -140,6 +140,8 @@ def lib() -> ctypes.CDLL:
                            I64, I, I, I, P, P, I64, P, I, P]
     L.t2_locations.restype = I
     L.t2_locations.argtypes = [P, I64, P, I64, P, I64, P, I64, I, I, I64, P]
+    L.residency_append.restype = I
+    L.residency_append.argtypes = [P, I64, I, I, I, I, P, P, I64, P, P]
     L.residency_prefetch.restype = I
     L.residency_prefetch.argtypes = [P, P, I64, I64, I64, I64, P, P, I64, I64, I64, I64, I, I, I,
                                      I, P, P, I64, P, I, P]
@@ -1028,18 +1030,46 @@ def residency_update(tier: torch.Tensor, s: torch.Tensor, n_tokens: int, capacit
     _check(st, "residency_update")
 
 
+def residency_append(loc: torch.Tensor, n_old: int, n_new: int, capacity: int,
+                     copy_tok: torch.Tensor, copy_slot: torch.Tensor, copy_count: torch.Tensor,
+                     stream=None):
+    """HBM slots for the rows [n_old, n_new) of every sequence (loc int32 [B, >= n_new] updated
+    in place): the free slots, lowest first, in token order; the rows given one are listed in
+    copy_tok / copy_slot int32 [B, >= min(n_new - n_old, capacity)], their number in
+    copy_count int32 [B]."""
+    for t, nm in ((loc, "loc"), (copy_tok, "copy_tok"), (copy_slot, "copy_slot")):
+        _need_dev(t, nm, I32S)
+        _contig(t, nm)
+    B = loc.shape[0]
+    if not 0 <= n_old <= n_new or capacity < 0:
+        raise ValueError("need 0 <= n_old <= n_new and capacity >= 0")
+    _need_shape(loc, "loc", [B, (">=", n_new)])
+    listed = min(n_new - n_old, capacity)
+    for t, nm in ((copy_tok, "copy_tok"), (copy_slot, "copy_slot")):
+        _need_shape(t, nm, [B, (">=", listed)])
+    if copy_slot.shape != copy_tok.shape:
+        raise ValueError("copy_tok and copy_slot must have one shape")
+    _need_contig_n(copy_count, "copy_count", B, I32S)
+    st = lib().residency_append(_ptr(loc), loc.shape[1], B, n_old, n_new, capacity,
+                                _ptr(copy_tok), _ptr(copy_slot), copy_tok.shape[1],
+                                _ptr(copy_count), _stream(stream))
+    _check(st, "residency_append")
+
+
 def residency_prefetch(k_host: torch.Tensor, v_host: torch.Tensor, k_hbm: torch.Tensor,
                        v_hbm: torch.Tensor, copy_tok: torch.Tensor, copy_slot: torch.Tensor,
                        copy_count: torch.Tensor, max_copies: int, stream=None):
-    """Copy the listed rows of the pinned host pools [B,Hkv,Nh,d] into their slots of the HBM
-    pools [B,Hkv,C,d] (one layer, every KV head)."""
+    """Copy the listed rows of the source pools [B,Hkv,Nh,d] (pinned host memory, or device
+    memory holding rows produced on the GPU) into their slots of the HBM pools [B,Hkv,C,d]
+    (one layer, every KV head)."""
     if k_hbm.dim() != 4:
         raise ValueError("k_hbm must be a [B, Hkv, C, d] view")
     B, Hkv, _, d = k_hbm.shape
     _need_cache(k_hbm, "k_hbm", B, Hkv, 0, d)
     _need_cache(v_hbm, "v_hbm", B, Hkv, 0, d, dtypes=(k_hbm.dtype,))
-    _need_cache(k_host, "k_host", B, Hkv, 0, d, dtypes=(k_hbm.dtype,), device=False)
-    _need_cache(v_host, "v_host", B, Hkv, 0, d, dtypes=(k_hbm.dtype,), device=False)
+    for t, nm in ((k_host, "k_host"), (v_host, "v_host")):
+        _dev_or_pinned(t, nm, (k_hbm.dtype,))
+        _need_cache(t, nm, B, Hkv, 0, d, dtypes=(k_hbm.dtype,), device=_is_dev(t))
     for t, nm in ((copy_tok, "copy_tok"), (copy_slot, "copy_slot")):
         _need_dev(t, nm, I32S)
         _contig(t, nm)

@@ -188,6 +188,49 @@ __global__ __launch_bounds__(kThreads) void residency_kernel(
   if (tid == 0) copy_count[b] = min(run, tot_free);  // the copies listed
 }
 
+// Free slots of a bitmap of held slots (up to kChunkCap): free_pre[w] = free slots in words
+// below w (slots >= capacity are not free), free_pre[kChunkWords] = the total, which is
+// returned.  Each thread owns kWordsPerThread consecutive words; ends with a barrier.
+__device__ int free_slot_prefix(const uint32_t* held_bits, int capacity, int* free_pre,
+                                int* scratch) {
+  const int tid = threadIdx.x;
+  const int words = (capacity + 31) / 32;
+  int fz[kWordsPerThread];
+  int fsum = 0;
+#pragma unroll
+  for (int j = 0; j < kWordsPerThread; ++j) {
+    const int w = tid * kWordsPerThread + j;
+    fz[j] = 0;
+    if (w < words) {
+      const int lim = min(32, capacity - w * 32);
+      const uint32_t valid = lim == 32 ? 0xFFFFFFFFu : ((1u << lim) - 1u);
+      fz[j] = __popc(~held_bits[w] & valid);
+    }
+    fsum += fz[j];
+  }
+  int tot_free;
+  int fp = block_excl_scan(fsum, scratch, &tot_free);
+#pragma unroll
+  for (int j = 0; j < kWordsPerThread; ++j) {
+    free_pre[tid * kWordsPerThread + j] = fp;
+    fp += fz[j];
+  }
+  if (tid == 0) free_pre[kChunkWords] = tot_free;
+  __syncthreads();
+  return tot_free;
+}
+
+// The r-th free slot (r < the free total), by binary search over the word prefixes.
+__device__ int nth_free_slot(const uint32_t* held_bits, const int* free_pre, int capacity, int r) {
+  int lo = 0, hi = (capacity + 31) / 32;  // free_pre[lo] <= r < free_pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (free_pre[mid] <= r) lo = mid;
+    else hi = mid;
+  }
+  return lo * 32 + nth_zero_bit(held_bits[lo], r - free_pre[lo]);
+}
+
 // The same policy for sequences longer than the register path holds: the tokens' tiers and
 // importance are read from memory on every pass (counts, each radix pass, the two index-order
 // passes), and between the passes a resident row that still needs a slot is marked in loc
@@ -267,31 +310,7 @@ __global__ __launch_bounds__(kThreads) void residency_chunked_kernel(
     }
   }
   __syncthreads();
-  // free slots per bitmap word (slots >= capacity are not free), then their prefix: each
-  // thread owns kWordsPerThread consecutive words
-  const int words = (capacity + 31) / 32;
-  int fz[kWordsPerThread];
-  int fsum = 0;
-#pragma unroll
-  for (int j = 0; j < kWordsPerThread; ++j) {
-    const int w = tid * kWordsPerThread + j;
-    fz[j] = 0;
-    if (w < words) {
-      const int lim = min(32, capacity - w * 32);
-      const uint32_t valid = lim == 32 ? 0xFFFFFFFFu : ((1u << lim) - 1u);
-      fz[j] = __popc(~held_bits[w] & valid);
-    }
-    fsum += fz[j];
-  }
-  int tot_free;
-  int fp = block_excl_scan(fsum, scratch, &tot_free);
-#pragma unroll
-  for (int j = 0; j < kWordsPerThread; ++j) {
-    free_pre[tid * kWordsPerThread + j] = fp;
-    fp += fz[j];
-  }
-  if (tid == 0) free_pre[kChunkWords] = tot_free;
-  __syncthreads();
+  const int tot_free = free_slot_prefix(held_bits, capacity, free_pre, scratch);
 
   // Pass B, in index order: the r-th marked row takes the r-th free slot
   int run = 0;
@@ -302,13 +321,7 @@ __global__ __launch_bounds__(kThreads) void residency_chunked_kernel(
     const int r = run + block_excl_scan(f ? 1 : 0, scratch, &tot);
     run += tot;
     if (f && r < tot_free) {
-      int lo = 0, hi = words;  // free_pre[lo] <= r < free_pre[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (free_pre[mid] <= r) lo = mid;
-        else hi = mid;
-      }
-      const int slot = lo * 32 + nth_zero_bit(held_bits[lo], r - free_pre[lo]);
+      const int slot = nth_free_slot(held_bits, free_pre, capacity, r);
       loc[i] = slot;
       if (r < copy_ld) {
         copy_tok[(int64_t)b * copy_ld + r] = i;
@@ -319,6 +332,49 @@ __global__ __launch_bounds__(kThreads) void residency_chunked_kernel(
     }
   }
   if (tid == 0) copy_count[b] = min(run, tot_free);  // the copies listed
+}
+
+// Rows a sequence gained since the last step, [n_old, n_new): the slots held by the rows below
+// n_old (0 <= loc < capacity) are marked in an LDS bitmap, and the r-th new row, in token order,
+// takes the r-th free slot (ascending), or stays in host memory (~tok) when none is left.
+__global__ __launch_bounds__(kThreads) void residency_append_kernel(
+    int32_t* __restrict__ loc_all, int64_t loc_ld, int n_old, int n_new, int capacity,
+    int32_t* __restrict__ copy_tok, int32_t* __restrict__ copy_slot, int64_t copy_ld,
+    int32_t* __restrict__ copy_count) {
+  __shared__ uint32_t held_bits[kChunkWords];
+  __shared__ int free_pre[kChunkWords + 1];
+  __shared__ int scratch[kWaves + 1];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  int32_t* loc = loc_all + (int64_t)b * loc_ld;
+  for (int i = tid; i < kChunkWords; i += kThreads) held_bits[i] = 0u;
+  __syncthreads();
+  for (int i0 = 0; i0 < n_old; i0 += kThreads * 8) {
+    int x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // every load of the batch before the first use
+      const int i = i0 + j * kThreads + tid;
+      x[j] = i < n_old ? loc[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (x[j] >= 0 && x[j] < capacity) atomicOr(&held_bits[x[j] >> 5], 1u << (x[j] & 31));
+  }
+  __syncthreads();
+  const int tot_free = free_slot_prefix(held_bits, capacity, free_pre, scratch);
+  const int m = n_new - n_old;
+  for (int r = tid; r < m; r += kThreads) {
+    const int tok = n_old + r;
+    if (r < tot_free) {
+      const int slot = nth_free_slot(held_bits, free_pre, capacity, r);
+      loc[tok] = slot;
+      copy_tok[(int64_t)b * copy_ld + r] = tok;    // r < min(m, capacity) <= copy_ld
+      copy_slot[(int64_t)b * copy_ld + r] = slot;
+    } else {
+      loc[tok] = ~tok;
+    }
+  }
+  if (tid == 0) copy_count[b] = min(m, tot_free);
 }
 
 // Copy of newly resident rows: row copy_tok[b, r] of the host pools to slot copy_slot[b, r] of
@@ -352,9 +408,9 @@ __global__ __launch_bounds__(256) void prefetch_kernel(
   }
 }
 
-// A host pool must be page-locked, device-mapped host memory; the kernel reads it through the
-// device address HIP reports for it.
-spk_status host_device_ptr(const void* p, const void** dev, const char* name) {
+// A source pool is page-locked, device-mapped host memory (read through the device address HIP
+// reports for it) or device memory (rows produced on the GPU); anything else is refused.
+spk_status source_device_ptr(const void* p, const void** dev, const char* name) {
   hipPointerAttribute_t at{};
   const hipError_t e = hipPointerGetAttributes(&at, p);
   if (e != hipSuccess) {
@@ -362,10 +418,16 @@ spk_status host_device_ptr(const void* p, const void** dev, const char* name) {
     return set_error(SPK_EINVAL, "residency_prefetch: %s is not memory known to HIP (%s)", name,
                      hipGetErrorString(e));
   }
+  if (at.type == hipMemoryTypeDevice) {
+    *dev = p;
+    return SPK_OK;
+  }
   if (at.type != hipMemoryTypeHost || at.devicePointer == nullptr)
-    return set_error(SPK_EINVAL, "residency_prefetch: %s must be pinned, device-mapped host memory",
-                     name);
-  *dev = at.devicePointer;
+    return set_error(SPK_EINVAL,
+                     "residency_prefetch: %s must be device memory or pinned, device-mapped host "
+                     "memory", name);
+  *dev = static_cast<const char*>(at.devicePointer) +
+         (static_cast<const char*>(p) - static_cast<const char*>(at.hostPointer));
   return SPK_OK;
 }
 
@@ -418,6 +480,33 @@ extern "C" SPK_API spk_status residency_update(const uint8_t* tier, int64_t tier
                                 copy_tok, copy_slot, copy_ld, copy_count, stream);
 }
 
+extern "C" SPK_API spk_status residency_append(int32_t* loc, int64_t loc_ld, int B, int n_old,
+                                               int n_new, int capacity, int32_t* copy_tok,
+                                               int32_t* copy_slot, int64_t copy_ld,
+                                               int32_t* copy_count, void* stream) {
+  using namespace spk;
+  SPK_REQUIRE(B >= 0 && n_old >= 0 && n_new >= n_old && capacity >= 0, SPK_EINVAL,
+              "residency_append: need 0 <= n_old <= n_new, capacity >= 0");
+  SPK_REQUIRE(capacity <= kChunkCap && n_new < kMaxTokensChunked, SPK_EUNSUPPORTED,
+              "residency_append: capacity %d above %d or n_new %d too large", capacity,
+              kChunkCap, n_new);
+  SPK_REQUIRE(loc_ld >= n_new, SPK_EINVAL, "residency_append: loc_ld %lld < n_new %d",
+              (long long)loc_ld, n_new);
+  const int m = n_new - n_old;
+  const int listed = m < capacity ? m : capacity;
+  SPK_REQUIRE(copy_ld >= listed, SPK_EINVAL,
+              "residency_append: copy_ld %lld < min(n_new - n_old, capacity) %d",
+              (long long)copy_ld, listed);
+  SPK_REQUIRE(B == 0 || (loc && copy_count && (listed == 0 || (copy_tok && copy_slot))),
+              SPK_EINVAL, "residency_append: null loc, copy list or copy_count");
+  clear_error();
+  if (B == 0) return SPK_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(residency_append_kernel, dim3(B), dim3(kThreads), 0, st, loc, loc_ld, n_old,
+                     n_new, capacity, copy_tok, copy_slot, copy_ld, copy_count);
+  return check_launch("residency_append");
+}
+
 extern "C" SPK_API spk_status residency_prefetch(
     const void* k_host, const void* v_host, int64_t host_sb, int64_t host_sh, int64_t host_sn,
     int64_t host_slots, void* k_hbm, void* v_hbm, int64_t hbm_sb, int64_t hbm_sh, int64_t hbm_sn,
@@ -444,9 +533,9 @@ extern "C" SPK_API spk_status residency_prefetch(
   if (B == 0 || max_copies == 0) return SPK_OK;
   const void* kh = nullptr;
   const void* vh = nullptr;
-  spk_status hs = host_device_ptr(k_host, &kh, "k_host");
+  spk_status hs = source_device_ptr(k_host, &kh, "k_host");
   if (hs != SPK_OK) return hs;
-  hs = host_device_ptr(v_host, &vh, "v_host");
+  hs = source_device_ptr(v_host, &vh, "v_host");
   if (hs != SPK_OK) return hs;
   SPK_REQUIRE(reinterpret_cast<uintptr_t>(kh) % 16 == 0 && reinterpret_cast<uintptr_t>(vh) % 16 == 0 &&
                   reinterpret_cast<uintptr_t>(k_hbm) % 16 == 0 &&

@@ -26,7 +26,7 @@ from . import (attn_workspace_size, fused_index_topk_ok, sparse_decode_attn, spa
                importance_accumulate, tier_classify, window_count, residency_update,
                residency_prefetch, topk_select_union, topk_union_workspace_size,
                sparse_decode_attn_union, attn_union_workspace_size, union_sets,
-               lookahead_prefetch, TIERS_T2, t2_fetch, t2_locations)
+               lookahead_prefetch, TIERS_T2, t2_fetch, t2_locations, residency_append)
 
 UNION_MIN_TOKENS = 16385   # wide rows: the union pipeline (narrower rows fit one workgroup)
 
@@ -241,6 +241,12 @@ class TieredDecode:
     (default priority), and each layer's attention waits only for its own layer's copy, so
     layer l+1's copy overlaps layer l's attention.
 
+    producer_caches: per-layer device (k, v) pools ``[B, Hkv, >= n_cap, d]`` holding the K/V
+    each layer produced for every row (with host_caches).  The rows a sequence gains between two
+    steps are then written into free HBM slots (residency_append, lowest slots first; a row
+    finding none stays in host memory until the next reassignment), so the protected recent
+    rows are read from HBM while memory allows.
+
     t012_permille / t2_codes: the T2 tier (rows ranked between t01 and t012 are attended from
     their 8-bit copy).  t2_codes are per-layer (codes_k, codes_v, scale_k, scale_v) written by
     kv_quantize_int8 (pinned host memory, or device memory), and needs host_caches.  Every
@@ -253,7 +259,8 @@ class TieredDecode:
                  t0_permille: int = 250, t01_permille: int = 750,
                  sm_scale: Optional[float] = None, host_caches: Optional[Sequence] = None,
                  hbm_rows: int = 0, reassign_every: int = 1, overlap_prefetch: bool = False,
-                 t012_permille: Optional[int] = None, t2_codes: Optional[Sequence] = None):
+                 t012_permille: Optional[int] = None, t2_codes: Optional[Sequence] = None,
+                 producer_caches: Optional[Sequence] = None):
         self.caches = list(caches)
         k0 = self.caches[0][0]
         B, Hkv, _, d = k0.shape
@@ -289,6 +296,16 @@ class TieredDecode:
         self.overlap = overlap_prefetch and self.host is not None
         self.copy_stream = torch.cuda.Stream(device=dev) if self.overlap else None
         self._copied = None      # per-layer events of the pending overlapped copies
+        self.producer = list(producer_caches) if producer_caches is not None else None
+        if self.producer is not None:
+            if self.host is None or len(self.producer) != self.L:
+                raise ValueError("producer_caches need host_caches, one pair per layer")
+            self.app_tok = torch.zeros((B, max(1, min(hbm_rows, n_cap))), dtype=torch.int32,
+                                       device=dev)
+            self.app_slot = torch.zeros_like(self.app_tok)
+            self.app_count = torch.zeros((B,), dtype=torch.int32, device=dev)
+            self.appended = torch.zeros((), dtype=torch.int64, device=dev)   # rows so far
+        self.n_prev = None       # tokens at the previous step (rows past it are new)
         self.p012 = t01_permille if t012_permille is None else t012_permille
         self.t2 = self.p012 > t01_permille
         if self.t2:
@@ -320,6 +337,22 @@ class TieredDecode:
         if self.t2:
             self.loc_t2.copy_(home.repeat(self.B, 1))
             self.t2_fetched.zero_()
+        if self.producer is not None:
+            self.appended.zero_()
+        self.n_prev = None
+
+    def append(self, n_tokens: int):
+        """Free HBM slots for the rows gained since the previous step, and their K/V written
+        there from the pools that produced them, in every layer."""
+        n_old = self.n_prev
+        if self.producer is None or n_old is None or n_tokens <= n_old:
+            return
+        residency_append(self.loc, n_old, n_tokens, self.hbm_rows, self.app_tok, self.app_slot,
+                         self.app_count)
+        m = min(n_tokens - n_old, self.app_tok.shape[1])
+        for (pk, pv), (k, v) in zip(self.producer, self.caches):
+            residency_prefetch(pk, pv, k, v, self.app_tok, self.app_slot, self.app_count, m)
+        self.appended += self.app_count.sum()
 
     def reassign(self, n_tokens: int):
         """Resident set of every sequence for the current tiers, and the differential copy of
@@ -345,6 +378,7 @@ class TieredDecode:
     def step(self, qs: Sequence[torch.Tensor], n_tokens: int, dense: bool = False):
         """One decode step at ``n_tokens`` cached tokens.  qs: per-layer Q ``[B, 1, Hq, d]``.
         dense=True attends over every token (no importance exists yet)."""
+        self.append(n_tokens)
         if dense:
             self.count.fill_(n_tokens)
             sel = self.dense_idx
@@ -382,6 +416,7 @@ class TieredDecode:
                                    logits=self.logits[l], ws=self.ws)
         self._copied = None
         importance_accumulate(self.s, sel, self.count, self.logits, self.lse, n_tokens)
+        self.n_prev = n_tokens
         return self.out, self.lse
 
 

@@ -133,6 +133,18 @@ def test_importance_and_tier_validation():
                            None, 0, None) == 1
 
 
+def test_residency_append_validation():
+    L = spk.lib()
+    # n_new < n_old; capacity above the limit; loc_ld < n_new; copy_ld too short
+    assert L.residency_append(A, 100, 1, 50, 40, 16, A, A, 16, A, None) == 1
+    assert L.residency_append(A, 100, 1, 50, 60, 131073, A, A, 16, A, None) == 2
+    assert L.residency_append(A, 50, 1, 40, 60, 16, A, A, 16, A, None) == 1
+    assert "loc_ld" in _err()
+    assert L.residency_append(A, 100, 1, 40, 60, 16, A, A, 15, A, None) == 1
+    assert "copy_ld" in _err()
+    assert L.residency_append(A, 100, 0, 40, 60, 16, A, A, 16, A, None) == 0
+
+
 def test_t2_validation():
     L = spk.lib()
     # residency classes outside a byte

@@ -277,7 +277,10 @@ def test_residency_checks(fake):
     kh = torch.empty((Bs, 2, n, D), dtype=torch.bfloat16)
     kd = d(Bs, 2, cap, D)
     spk.residency_prefetch(kh, kh.clone(), kd, d(Bs, 2, cap, D), ct, cs, cc, cap)
-    for b in [dict(k_host=d(Bs, 2, n, D), v_host=d(Bs, 2, n, D)),
+    # device-memory source pools (rows produced on the GPU) are accepted too
+    spk.residency_prefetch(d(Bs, 2, n, D), d(Bs, 2, n, D), kd, d(Bs, 2, cap, D), ct, cs, cc, cap)
+    for b in [dict(k_host=torch.empty((Bs, 2, n, D), dtype=torch.float32),
+                   v_host=torch.empty((Bs, 2, n, D), dtype=torch.float32)),
               dict(k_host=torch.empty((Bs - 1, 2, n, D), dtype=torch.bfloat16),
                    v_host=torch.empty((Bs - 1, 2, n, D), dtype=torch.bfloat16)),
               dict(v_hbm=d(Bs, 2, cap, 64)),
@@ -287,7 +290,15 @@ def test_residency_checks(fake):
         with pytest.raises(ValueError):
             spk.residency_prefetch(**a)
     assert fake.calls.count("residency_update_tiers") == 1
-    assert fake.calls.count("residency_prefetch") == 1
+    assert fake.calls.count("residency_prefetch") == 2
+    spk.residency_append(loc, 400, n, cap, ct, cs, cc)
+    for b in [dict(n_old=n + 1), dict(loc=d(Bs, n - 1, dtype=torch.int32)),
+              dict(copy_tok=d(Bs, 50, dtype=torch.int32), copy_slot=d(Bs, 50, dtype=torch.int32)),
+              dict(copy_count=d(Bs + 1, dtype=torch.int32)), dict(capacity=-1)]:
+        with pytest.raises(ValueError):
+            spk.residency_append(**{**dict(loc=loc, n_old=400, n_new=n, capacity=cap,
+                                           copy_tok=ct, copy_slot=cs, copy_count=cc), **b})
+    assert fake.calls.count("residency_append") == 1
 
 
 def test_t2_checks(fake):

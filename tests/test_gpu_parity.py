@@ -1115,7 +1115,7 @@ def test_tiered_offload_bit_identical_to_all_hbm(hbm_rows, every):
     w = W.scaled(W.REASONING_TIERS, B=3, layers=3, Hq=8, Hkv=2, N=1200, n_start=600,
                  grow_per_step=100, steps=6, n_recent=64)
     say("tiered-offload", hbm_rows, every)
-    _offload_vs_all_hbm(w, hbm_rows, every, overlap=every == 2)
+    _offload_vs_all_hbm(w, hbm_rows, every, overlap=every == 2, append=every == 3)
 
 
 @pytest.mark.parametrize("n_end,hbm_rows", [(32768, 16384), (65536, 24576)])
@@ -1126,10 +1126,10 @@ def test_tiered_offload_long_context_bit_identical_to_all_hbm(n_end, hbm_rows):
     w = W.scaled(W.REASONING_TIERS, B=2, layers=2, Hq=8, Hkv=2, N=n_end, n_start=n_end - 4000,
                  grow_per_step=1000, steps=4, n_recent=512)
     say("tiered-offload-long", n_end, hbm_rows)
-    _offload_vs_all_hbm(w, hbm_rows, 2, overlap=n_end > 32768)
+    _offload_vs_all_hbm(w, hbm_rows, 2, overlap=n_end > 32768, append=n_end > 32768)
 
 
-def _offload_vs_all_hbm(w, hbm_rows, every, overlap):
+def _offload_vs_all_hbm(w, hbm_rows, every, overlap, append=False):
     caches = [(W.kv_cache(w, "k", l, DEV, n_cap=w.N), W.kv_cache(w, "v", l, DEV, n_cap=w.N))
               for l in range(w.layers)]
     host_pools = [(k.cpu().pin_memory(), v.cpu().pin_memory()) for k, v in caches]
@@ -1139,7 +1139,7 @@ def _offload_vs_all_hbm(w, hbm_rows, every, overlap):
     ref = TieredDecode(caches, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille)
     off = TieredDecode(hbm, w.Hq, w.N, w.n_sink, w.n_recent, w.t0_permille, w.t01_permille,
                        host_caches=host_pools, hbm_rows=hbm_rows, reassign_every=every,
-                       overlap_prefetch=overlap)
+                       overlap_prefetch=overlap, producer_caches=caches if append else None)
     for t in range(w.steps):
         n = w.n_start + w.grow_per_step * t
         qs = [W.queries(w, step=t, layer=l, device=DEV) for l in range(w.layers)]
@@ -1161,6 +1161,38 @@ def _offload_vs_all_hbm(w, hbm_rows, every, overlap):
                     sl = torch.tensor(L[b, res].astype(np.int64))
                     assert torch.equal(hbm[0][0][b][:, sl].cpu(), caches[0][0][b][:, torch.tensor(res)].cpu())
     assert int(off.copies) > 0
+    if append:
+        assert int(off.appended) > 0, "no appended row was written into HBM"
+
+
+def test_residency_append_matches_oracle():
+    """Slots of appended rows against the oracle over three steps that follow a reassignment
+    (rows held, rows on the host, a capacity that runs out), at 1000 and 40000 tokens."""
+    for n, cap, grow in ((1000, 700, 120), (40000, 30000, 3000)):
+        say("residency-append", n, cap)
+        r = np.random.default_rng(n)
+        B = 2
+        tier, s = _random_tiers(r, B, n)
+        loc = torch.tensor(np.array([[~i for i in range(n)]] * B, np.int32), device=DEV)
+        ld = max(cap, 1)
+        ct = torch.full((B, ld), -7, dtype=torch.int32, device=DEV)
+        cs = torch.full((B, ld), -7, dtype=torch.int32, device=DEV)
+        cc = torch.zeros((B,), dtype=torch.int32, device=DEV)
+        n0 = n - 3 * grow
+        spk.residency_update(torch.tensor(tier, device=DEV), torch.tensor(s, device=DEV), n0, cap,
+                             loc, ct, cs, cc)
+        for step in range(3):
+            lo, hi = n0 + step * grow, n0 + (step + 1) * grow
+            loc_in = loc.cpu().numpy().copy()
+            spk.residency_append(loc, lo, hi, cap, ct, cs, cc)
+            torch.cuda.synchronize()
+            for b in range(B):
+                ref_loc, ref_cp = oracle.residency_append(loc_in[b], lo, hi, cap)
+                assert loc.cpu().numpy()[b, :hi].tolist() == ref_loc.tolist(), (n, step, b)
+                k = int(cc[b])
+                assert k == len(ref_cp)
+                got = list(zip(ct.cpu().numpy()[b, :k].tolist(), cs.cpu().numpy()[b, :k].tolist()))
+                assert got == ref_cp
 
 
 # ---------------------------------------------------------------------- T2: the 8-bit tier
