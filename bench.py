@@ -205,7 +205,8 @@ def gather_kernel_ms(call, reps, stream):
 
 def stream_ceiling_gbs(nbytes, stream, reps=12):
     """HBM read ceiling at this size: the best median rate of the library's plain streaming read
-    (spk_stream_read) over a buffer of `nbytes`, across workgroup counts.  The buffers cycle
+    (spk_stream_read, nontemporal 16-byte loads) over a buffer of `nbytes`, across workgroup
+    counts.  The buffers cycle
     through at least 768 MiB so none is still in the 256 MB last-level cache, and a long read
     queued first lets the host enqueue every timed launch ahead of the GPU, so each event pair
     brackets one kernel and no host time."""
@@ -220,7 +221,7 @@ def stream_ceiling_gbs(nbytes, stream, reps=12):
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     sh = ctypes.c_void_p(stream.cuda_stream)
     best = 0.0
-    for wgs in (1024, 2048, 4096, 8192, 16384):
+    for wgs in (1024, 2048, 4096, 8192, 16384, 32768):
         pairs = []
         for _ in range(reps):
             a, b = ctypes.c_void_p(), ctypes.c_void_p()

@@ -27,6 +27,11 @@ namespace {
 #endif
 constexpr int kThreads = 256;
 constexpr int kUnroll = SPK_INDEX_UNROLL;
+#ifndef SPK_INDEX_UNROLL_PER_HEAD
+#define SPK_INDEX_UNROLL_PER_HEAD 8   // key loads per lane in flight in per-head (dot2) scoring
+#endif
+constexpr int kUnrollPerHead = SPK_INDEX_UNROLL_PER_HEAD;
+
 constexpr int kMaxRowsPerWg = SPK_INDEX_MAX_ROWS;
 // Token scoring: a 16 KB LDS score tile, so a workgroup takes 4096 / NS rows (1024 for four
 // score vectors) and writes each score row's part as one run of up to 4 KB: fewer, longer
@@ -95,7 +100,9 @@ __device__ __forceinline__ float dot8_bf16(const uint4& k, const uint32_t (&qp)[
 
 // DOT2: bf16 keys and bf16 query vectors used as they are (per-head token scores): the query
 // slice stays packed and each key load feeds dot2 instructions instead of conversions and FMAs.
-template <int D, typename KT, int NS, bool DOT2 = false>
+// U: key loads per lane in one batch (registers are held for two batches: the next one is
+// issued before the current one is used).
+template <int D, typename KT, int NS, bool DOT2 = false, int U = kUnroll>
 __global__ __launch_bounds__(kThreads) void index_rows_kernel(
     int mode, const void* __restrict__ q, int q_bf16, const KT* __restrict__ keys, int64_t k_sb,
     int64_t k_sh, int64_t k_sn, int T, int Hq, int Hkv, int G, int ns, int n_cand,
@@ -118,12 +125,12 @@ __global__ __launch_bounds__(kThreads) void index_rows_kernel(
   const KT* base_ptr = keys + (int64_t)b * k_sb + (int64_t)kvh * k_sh + sub * 8;
   // The first batch of key loads goes out before the query slices are fetched, and every later
   // batch before the previous one is used, so the workgroup always has key bytes in flight.
-  Raw8<KT> raw[kUnroll];
-  auto issue = [&](Raw8<KT> (&dst)[kUnroll], int base) {
+  Raw8<KT> raw[U];
+  auto issue = [&](Raw8<KT> (&dst)[U], int base) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int row = base + (u * WAVES + wid) * RPS + slot;
-      dst[u].load(base_ptr + (int64_t)min(row, row1 - 1) * k_sn);  // past the end: re-read, unused
+      dst[u].load_nt(base_ptr + (int64_t)min(row, row1 - 1) * k_sn);  // past the end: re-read, unused
     }
   };
   issue(raw, row0);
@@ -180,12 +187,12 @@ __global__ __launch_bounds__(kThreads) void index_rows_kernel(
     }
   }
 
-  for (int base = row0; base < row1; base += STEP * kUnroll) {
-    Raw8<KT> nxt[kUnroll];
-    const bool more = base + STEP * kUnroll < row1;   // uniform over the workgroup
-    if (more) issue(nxt, base + STEP * kUnroll);
+  for (int base = row0; base < row1; base += STEP * U) {
+    Raw8<KT> nxt[U];
+    const bool more = base + STEP * U < row1;   // uniform over the workgroup
+    if (more) issue(nxt, base + STEP * U);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int row = base + (u * WAVES + wid) * RPS + slot;
       float acc[NS];
       if constexpr (DOT2) {
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void index_rows_kernel(
     }
     if (more) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) raw[u] = nxt[u];
+      for (int u = 0; u < U; ++u) raw[u] = nxt[u];
     }
   }
   __syncthreads();
@@ -314,9 +321,9 @@ spk_status launch_rows(int ns_pad, dim3 grid, hipStream_t st, int mode, const vo
   // bf16 keys scored against bf16 query heads as they are: the dot2 path
   const bool dot2 = std::is_same<KT, uint16_t>::value && q_bf16 && mode == SPK_IDX_TOKEN_PER_HEAD;
 #define SPK_ROWS(NSV, DT)                                                                     \
-  hipLaunchKernelGGL((index_rows_kernel<D, KT, NSV, DT>), grid, dim3(kThreads), 0, st, mode, \
-                     q, q_bf16, kp, k_sb, k_sh, k_sn, T, Hq, Hkv, G, ns, n_cand, rpw, scores,  \
-                     s_ld)
+  hipLaunchKernelGGL((index_rows_kernel<D, KT, NSV, DT, DT ? kUnrollPerHead : kUnroll>),        \
+                     grid, dim3(kThreads), 0, st, mode, q, q_bf16, kp, k_sb, k_sh, k_sn, T, Hq, \
+                     Hkv, G, ns, n_cand, rpw, scores, s_ld)
   if constexpr (std::is_same<KT, uint16_t>::value) {
     if (dot2) {
       switch (ns_pad) {
@@ -720,15 +727,22 @@ extern "C" SPK_API spk_status sparse_index_score(spk_index_mode mode, const void
                                             Hkv, ns, n_cand, block_size, bpw, scores, s_ld, pooled_out);
   }
   // Rows per workgroup: per-head scoring loads one query slice per score vector and prefers
-  // many small workgroups, one batch of key loads each (64 rows at d = 128: 186 us, against
-  // 206 at 128 rows, 214 at 256 and 220 at 1024 on the per-head 131072-token workload); the
+  // many small workgroups, one batch of key loads each: on the per-head 131072-token workload
+  // 128 rows at d = 128 with eight nontemporal loads per lane take 173-177 us, against 182-186
+  // at 64 rows with four, 190 at 256 rows with sixteen, and 180-195 for the same 128-row batch
+  // at 8 or at 4-7 workgroups per CU (the registers for two batches hold it at five); the
   // group mean builds its vectors once per workgroup in LDS and does best at 256 rows (416 us,
   // against 441 at 1024 and 551 at 64 on the speculative-verify workload); block scores take
   // the whole tile, halved until the launch fills the chip.
-  const int max_rows = mode == SPK_IDX_TOKEN_PER_HEAD   ? step * kUnroll
+  const bool dot2 = k_dtype == SPK_BF16 && q_bf16 && mode == SPK_IDX_TOKEN_PER_HEAD;
+  const int batch = step * (dot2 ? kUnrollPerHead : kUnroll);
+  const int max_rows = mode == SPK_IDX_TOKEN_PER_HEAD   ? std::min(batch, rows_cap(ns_pad))
                        : mode == SPK_IDX_TOKEN_GROUP_MEAN ? std::min(256, rows_cap(ns_pad))
                                                           : rows_cap(ns_pad);
-  const int rpw = pick_rows_per_wg((int64_t)n_cand * groups, step * kUnroll, max_rows);
+  const int rpw = pick_rows_per_wg((int64_t)n_cand * groups, std::min(batch, max_rows), max_rows);
+  // the score tile holds rows_cap(ns_pad) rows of every vector
+  SPK_REQUIRE(rpw >= 1 && rpw <= rows_cap(ns_pad), SPK_EINVAL,
+              "sparse_index_score: internal: %d rows per workgroup exceed the tile", rpw);
   dim3 grid(ceil_div(n_cand, rpw), groups);
   if (d == 128)
     return k_dtype == SPK_BF16

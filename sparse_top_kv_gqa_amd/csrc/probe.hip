@@ -3,7 +3,10 @@
 //
 // spk_stream_read: a plain streaming read of a device buffer (the HBM roofline as a kernel of
 // this library reaches it, beside the vendor's peak).  Each workgroup reads one contiguous
-// chunk with 16-byte loads, four in flight per lane.
+// chunk with 16-byte nontemporal loads, four in flight per lane: of the read shapes measured
+// (64 to 1024 threads, 4 to 16 loads in flight, chunks of 8 KB to 512 KB, plain or
+// nontemporal loads) the fastest, at about 6.9-7.0 TB/s over 1 GiB against 6.1-6.5 TB/s for
+// plain loads.
 //
 // spk_gather_read: the K and V rows of per-group row lists, read once each and nothing else
 // (the rate the HBM allows for that exact set of rows, scattered as the selection scattered
@@ -27,7 +30,8 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
   uint32_t acc = 0;
   uint64_t i = beg + threadIdx.x;
   for (; i + 3 * kThreads < end; i += 4 * kThreads) {
-    const uint4 a = p[i], b = p[i + kThreads], c = p[i + 2 * kThreads], d = p[i + 3 * kThreads];
+    const uint4 a = gload16_nt(p + i), b = gload16_nt(p + i + kThreads),
+                c = gload16_nt(p + i + 2 * kThreads), d = gload16_nt(p + i + 3 * kThreads);
     acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^
            (d.x ^ d.y ^ d.z ^ d.w);
   }

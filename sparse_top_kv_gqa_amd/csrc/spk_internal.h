@@ -58,6 +58,23 @@ __device__ __forceinline__ uint4 gload16(uint64_t addr) {
 #endif
 }
 
+// 16-byte nontemporal load (streaming: the line is not kept in the caches).  For data read once
+// per pass over HBM it streams measurably faster than a plain load.
+__device__ __forceinline__ uint4 gload16_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint4 gload16_nt(uint64_t addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<global_u32x4*>(addr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4*>(addr);
+#endif
+}
+
 // Eight consecutive elements of a row, kept raw until they are needed (lets a loop issue
 // many loads before the first use).
 template <typename T> struct Raw8;
@@ -65,6 +82,7 @@ template <> struct Raw8<uint16_t> {  // bf16
   uint4 u;
   __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
   __device__ __forceinline__ void load_addr(uint64_t a) { u = gload16(a); }
+  __device__ __forceinline__ void load_nt(const uint16_t* p) { u = gload16_nt(p); }
   __device__ __forceinline__ void to_float(float (&x)[8]) const {
     x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
     x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
@@ -79,6 +97,13 @@ template <> struct Raw8<float> {
   }
   __device__ __forceinline__ void load_addr(uint64_t x) {
     const uint4 u0 = gload16(x), u1 = gload16(x + 16);
+    a = make_float4(__uint_as_float(u0.x), __uint_as_float(u0.y), __uint_as_float(u0.z),
+                    __uint_as_float(u0.w));
+    b = make_float4(__uint_as_float(u1.x), __uint_as_float(u1.y), __uint_as_float(u1.z),
+                    __uint_as_float(u1.w));
+  }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    const uint4 u0 = gload16_nt(p), u1 = gload16_nt(p + 4);
     a = make_float4(__uint_as_float(u0.x), __uint_as_float(u0.y), __uint_as_float(u0.z),
                     __uint_as_float(u0.w));
     b = make_float4(__uint_as_float(u1.x), __uint_as_float(u1.y), __uint_as_float(u1.z),
