@@ -387,7 +387,7 @@ def union_rows_block(idx, n_tokens, bs, n_sink, n_recent):
     blocks = idx.reshape(G, -1).long()
     mask = torch.zeros((G, n_tokens), dtype=torch.bool, device=idx.device)
     tok = (blocks[:, :, None] * bs + torch.arange(bs, device=idx.device)).reshape(G, -1)
-    mask.scatter_(1, tok.clamp(max=n_tokens - 1), True)
+    mask.scatter_(1, tok.clamp(0, n_tokens - 1), True)
     mask[:, :n_sink] = True
     mask[:, n_tokens - n_recent:] = True
     return int(mask.sum())
@@ -595,15 +595,36 @@ def cpu_block(ctx, seconds):
 
 # ------------------------------------------------------------------------------ token sparse
 
+def _row_mask(ids, N):
+    """[G, N] mask of the values in [0, N) of each row of ids [G, M] (int64); anything else
+    marks nothing (column N of a scratch mask takes it)."""
+    ids = torch.where((ids >= 0) & (ids < N), ids, torch.full_like(ids, N))
+    mask = torch.zeros((ids.shape[0], N + 1), dtype=torch.bool, device=ids.device)
+    mask.scatter_(1, ids, True)
+    return mask[:, :N]
+
+
+def _distinct_rows(ids, N):
+    """Distinct values in [0, N) per row of ids [G, M]."""
+    return _row_mask(ids, N).sum(dim=1)
+
+
+def _counted(idx, count):
+    """idx [..., k] as int64 with the entries at or past count[...] set to -1."""
+    k = idx.shape[-1]
+    live = torch.arange(k, device=idx.device) < count.unsqueeze(-1).long()
+    return torch.where(live, idx.long(), torch.full_like(idx, -1, dtype=torch.long))
+
+
 def union_rows_tokens(idx, count, per_group_rows, N):
     """Rows each (b, kvh) group fetches: union of the selection rows that map to it.
-    idx [B, T, Hs, k] int32; per_group_rows: selection rows per group along (T, Hs/Hkv)."""
+    idx [B, T, Hs, k] int32; count [B, T, Hs]; per_group_rows: selection rows per group along
+    (T, Hs/Hkv).  Only the first count entries of a row are read."""
     B, T, Hs, k = idx.shape
     Hkv = Hs // per_group_rows
-    sel = idx.long().reshape(B, T, Hkv, per_group_rows, k).permute(0, 2, 1, 3, 4).reshape(B * Hkv, -1)
-    mask = torch.zeros((B * Hkv, N), dtype=torch.bool, device=idx.device)
-    mask.scatter_(1, sel, True)
-    return mask.sum(dim=1)
+    ids = _counted(idx, count)
+    sel = ids.reshape(B, T, Hkv, per_group_rows, k).permute(0, 2, 1, 3, 4).reshape(B * Hkv, -1)
+    return _distinct_rows(sel, N)
 
 
 def bench_token(args, which):
@@ -649,9 +670,8 @@ def bench_token(args, which):
         if which != "per_head":
             # spec verify: rows of (b, kvh) = union over the T draft tokens
             B, T, Hkv, kk = dec.idx.shape
-            sel = dec.idx.long().permute(0, 2, 1, 3).reshape(B * Hkv, T * kk)
-            m = torch.zeros((B * Hkv, w.N), dtype=torch.bool, device="cuda")
-            m.scatter_(1, sel, True)
+            sel = _counted(dec.idx, dec.count).permute(0, 2, 1, 3).reshape(B * Hkv, T * kk)
+            m = _row_mask(sel, w.N)
             u = m.sum(dim=1)
             hm = (loc.reshape(B * Hkv, w.N) < 0) & m
             host_frac.append(float(hm.sum()) / float(m.sum()))
@@ -1153,7 +1173,7 @@ def bench_lookahead(args):
                 sel = hbm[l].idx.reshape(w.B * w.Hkv, -1).long()
                 toks = (sel[:, :, None] * bs + torch.arange(bs, device="cuda")).reshape(w.B * w.Hkv, -1)
                 hm = layers[l][4].reshape(w.B * w.Hkv, w.N)
-                host += int((torch.gather(hm, 1, toks.clamp(max=w.N - 1)) < 0).sum())
+                host += int((torch.gather(hm, 1, toks.clamp(0, w.N - 1)) < 0).sum())
             sel_rows.append(tot)
             host_sel.append(host)
     index_bytes = w.layers * w.B * w.Hkv * (w.N // bs) * w.d * 4

@@ -11,25 +11,33 @@
 // index, indices ascending.  The union is ascending, each entry with a mask bit per set.
 //
 // Pipeline for wide rows, every pass spread over the whole chip:
-//  (0) union_hist_kernel: the histogram of the top 12 key bits of every row, per chunk of the
-//      row (stored whole, so nothing is cleared or added atomically);
-//  (1) union_bin_kernel, one workgroup per row: sums the row's chunk histograms; the bin b* of
-//      the k-th largest key and the number of keys above it;
-//  (2) union_gather_kernel, a wave per contiguous token segment of a group: one read of the
-//      S score rows; every token with a key above b* in some set, or in bin b* of some set, is
-//      appended, in token order, to the segment's candidate list with an 8-bit mask (4 bits
-//      "above", 4 bits "in b*"); every set's in-b* candidates are also appended, with their
-//      keys, to a short list of the segment and set;
-//  (3) union_thr_kernel, one workgroup per row: its set's short lists are loaded at once (one
-//      prefix over the segments' counts places every entry), a radix search over their low 20
-//      key bits finds the exact threshold and, for ties, the last tied candidate taken (lowest
-//      indices first), and a "taken" bit is or-ed into every taken candidate's entry (a row
-//      whose lists overflow falls back to a full radix select over its scores);
-//  (4) union_write_kernel, one workgroup per group: a prefix over the segments' counts makes the
-//      group's candidates one array, every wave owns a contiguous run of it; the final mask of a
-//      candidate is its above bits plus its taken bits; two sweeps (counts, then ballot-ranked
-//      stores) write the union list, its masks and count, and every set's ascending index list
-//      and count.
+//  (0) union_range_kernel, two workgroups per row: a key range [lo, hi] expected to hold the
+//      row's k-th largest key, from a sample of the row (16-token pieces at 256 evenly spaced
+//      offsets, the whole row when it has at most 4096 keys): hi is the sample's key of rank
+//      r - delta, lo the key of rank r + delta, r = k * samples / n its expected rank and delta
+//      four standard deviations of a sampled count plus two.  Nothing below depends on the
+//      range being right: the threshold pass checks it and falls back to exact whole-row work;
+//      the range only decides how much work the exact answer takes;
+//  (1) union_gather_kernel, a wave per contiguous token segment of a group: one read of the
+//      S score rows; every token with a key above hi in some set, or inside [lo, hi] in some
+//      set, is appended, in token order, to the segment's candidate list with an 8-bit mask (4
+//      bits "above", 4 bits "in range"); every set's in-range candidates are also appended, with
+//      their keys, to a short list of the segment and set, and the keys above hi are counted;
+//  (2) union_thr_kernel, one workgroup per row: when fewer than k keys lie above hi and the
+//      in-range lists hold the rest (none overflowed), the lists are loaded at once (one prefix
+//      over the segments' counts places every entry) and a radix search finds the exact
+//      threshold and, for ties, the last tied candidate taken (lowest indices first); a "taken"
+//      bit is or-ed into every taken candidate's entry.  Otherwise a radix select over the
+//      whole row finds the threshold: if no selected key lies below lo, the taken bits are set
+//      on the row's candidates (above or in range) and the row's "above" bits are ignored;
+//      else the group is marked for direct selection;
+//  (3) union_write_kernel, one workgroup per group and output: a prefix over the segments'
+//      counts makes the group's candidates one array, every wave owns a contiguous run of it;
+//      the final mask of a candidate is its honoured above bits plus its taken bits; two sweeps
+//      (counts, then ballot-ranked stores) write the union list, its masks and count, and every
+//      set's ascending index list and count.  A group marked for direct selection instead
+//      selects from its score rows with every set's exact threshold (the same two sweeps over
+//      the tokens).
 //
 // A candidate entry is (token offset in its segment) << 8 | mask, with the taken bits at
 // 18..21 (segments hold at most 1024 tokens).
@@ -43,13 +51,23 @@ constexpr int kWaves4 = kThreads / kWave;
 constexpr int kWriteThreads = 1024;
 constexpr int kWriteWaves = kWriteThreads / kWave;
 constexpr int kMaxSets = 4;
-constexpr int kThrCap = 4096;     // in-b* candidates of a row held in LDS by union_thr_kernel
-constexpr int kListCap = 128;     // in-b* entries kept per (segment, set) list
+constexpr int kThrCap = 6144;     // in-range candidates of a row held in LDS by union_thr_kernel
+constexpr int kListCap = 128;     // in-range entries kept per (segment, set) list
 constexpr int kGatherU = 8;       // 64-token sub-rows in flight per wave in union_gather_kernel
 constexpr int kWriteU = 16;       // candidates per lane in flight in union_write_kernel
 constexpr int kTakenShift = 18;   // taken bits of a candidate entry (above the 10-bit offset)
 constexpr int kMaxSegLen = 1024;
 constexpr int kMaxSegs = 4096;    // segments per group held in LDS prefixes (n <= 2^22)
+constexpr int kSlotBits = 22;     // candidate slots of a group: nseg * seg_len <= 2^22
+constexpr uint32_t kSlotMask = (1u << kSlotBits) - 1u;
+constexpr int kPieces = 256;      // sample pieces per row
+constexpr int kPieceLen = 16;     // consecutive tokens per piece
+constexpr int kSampleMax = kPieces * kPieceLen;
+constexpr int kSamplePerThread = kSampleMax / kThreads;
+// thr_out[row].w: how the write pass treats the row's set
+constexpr int kRowRange = 0;      // threshold found inside the range: above bits and taken bits
+constexpr int kRowTakenOnly = 1;  // whole-row threshold inside the range: taken bits only
+constexpr int kRowDirect = 2;     // a selected key lies below the range: select from the scores
 
 struct Shape {
   int B, T, Hq, Hkv, G, S, per_head;
@@ -66,19 +84,10 @@ __host__ __device__ inline int64_t set_row(const Shape& u, int g, int s) {
   return (int64_t)(b * u.T + s) * u.Hkv + kvh;
 }
 
-// Chunks per row of the histogram pass: about four workgroups per CU over the launch, chunks of
-// at least 2048 scores.
-int hist_chunks(int64_t rows, int n) {
-  int64_t c = ceil_div(4LL * num_cus(), rows > 0 ? rows : 1);
-  const int64_t most = ceil_div(n > 0 ? n : 1, 2048);
-  if (c > most) c = most;
-  return (int)(c < 1 ? 1 : c);
-}
-
 struct Layout {
-  int nseg = 0, seg_len = 0, parts = 0, hist_chunks = 1;
+  int nseg = 0, seg_len = 0, parts = 0;
   size_t off_info = 0, off_thr = 0, off_cand = 0, off_ccnt = 0, off_ibl = 0, off_ibc = 0,
-         off_hist = 0, bytes = 0;
+         off_iac = 0, bytes = 0;
 };
 
 Layout make_layout(int groups, int S, int n) {
@@ -103,8 +112,7 @@ Layout make_layout(int groups, int S, int n) {
   l.off_ccnt = take((size_t)groups * l.nseg * 4);
   l.off_ibl = take((size_t)groups * l.nseg * kMaxSets * kListCap * 8);
   l.off_ibc = take((size_t)groups * l.nseg * kMaxSets * 4);
-  l.hist_chunks = hist_chunks(rows, n);
-  l.off_hist = take((size_t)rows * l.hist_chunks * kHistBins * 4);
+  l.off_iac = take((size_t)groups * l.nseg * kMaxSets * 4);
   l.bytes = off;
   return l;
 }
@@ -114,120 +122,176 @@ __device__ __forceinline__ int kth_set_bit(uint64_t u, int r) {  // r < popcount
   return (int)__builtin_ctzll(u);
 }
 
-// ---------------------------------------------------------------- (0) histogram of the scores
+// ---------------------------------------------------------------- (0) key range per row
 
-// Histogram of chunk blockIdx.x of score row blockIdx.y, stored whole (no atomics, nothing to
-// clear beforehand) at ghist[(row * C + chunk) * kHistBins].
-__global__ __launch_bounds__(kThreads) void union_hist_kernel(const float* __restrict__ scores,
-                                                              int64_t s_ld, int n, int chunk,
-                                                              uint32_t* __restrict__ ghist) {
-  __shared__ __align__(16) uint32_t hist[kHistBins];
-  const int row = blockIdx.y;
-  const int beg = blockIdx.x * chunk, end = min(n, beg + chunk);
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[i] = 0u;
-  __syncthreads();
-  const float* x = scores + (int64_t)row * s_ld;
-  constexpr int U = 8;
-  for (int i0 = beg; i0 < end; i0 += kThreads * U) {
-    float v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = x[min(i0 + u * kThreads + (int)threadIdx.x, end - 1)];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (i0 + u * kThreads + (int)threadIdx.x < end)
-        atomicAdd(&hist[order_key(v[u]) >> kHistShift], 1u);
-  }
-  __syncthreads();
-  uint32_t* gh = ghist + ((int64_t)row * gridDim.x + blockIdx.x) * kHistBins;
-  for (int i = threadIdx.x * 4; i < kHistBins; i += kThreads * 4)
-    *reinterpret_cast<uint4*>(gh + i) = *reinterpret_cast<const uint4*>(hist + i);
+// Token of sample i (< min(n, kSampleMax)) of a row of n: the row itself up to kSampleMax keys,
+// else token i % kPieceLen of piece i / kPieceLen, piece j starting at floor(j * n / kPieces)
+// (pieces never overlap: n / kPieces >= kPieceLen).
+__device__ __forceinline__ int sample_token(int i, int n) {
+  if (n <= kSampleMax) return i;
+  return (int)(((int64_t)(i / kPieceLen) * n) / kPieces) + i % kPieceLen;
 }
 
-// ---------------------------------------------------------------- (1) bin of the k-th key
-
-// info[row] = (b*, keys above b*, rank of the k-th key inside b* (1-based), kk); b* = kHistBins
-// when nothing is selected.
-// The row's histogram is the sum of its C chunk histograms (C = 1: a whole-row histogram).
-__global__ __launch_bounds__(kThreads) void union_bin_kernel(const uint32_t* __restrict__ ghist,
-                                                             int C, int n, int k,
-                                                             int4* __restrict__ info) {
-  __shared__ int red[kWaves4 + 1];
-  const int row = blockIdx.x;
+// Workgroup (0, row) writes info[row].y = hi, workgroup (1, row) info[row].x = lo and
+// info[row].z = min(k, n).  Every row key above hi is meant to be kept, the row's k-th largest
+// key is meant to lie in [lo, hi]; hi = 0xFFFFFFFF (no order key is larger) when the sample
+// puts fewer than one key above the range, lo = 0 when it puts the range's end past the
+// sample.  With the whole row as the sample the range is exact: hi and lo are the k-th
+// largest key (up to a prefix with the same count for lo).  The sample's key of rank q: a
+// 4096-bin histogram of the top 12 key bits names its bin, a radix search over the low 20
+// bits of that bin's keys the key itself.
+__global__ __launch_bounds__(kThreads) void union_range_kernel(const float* __restrict__ scores,
+                                                               int64_t s_ld, int n, int k,
+                                                               int4* __restrict__ info) {
+  __shared__ __align__(16) uint32_t bins[kHistBins];
+  __shared__ __align__(16) uint32_t hist[4 * 256];
+  __shared__ int red[kWaves4 + 1], sh[2];
+  __shared__ uint32_t kmin;
+  const int row = blockIdx.y, upper = blockIdx.x == 0, tid = threadIdx.x;
+  int* out = reinterpret_cast<int*>(info + row);
   const int kk = min(k, n);
   if (kk <= 0) {
-    if (threadIdx.x == 0) info[row] = make_int4(kHistBins, 0, 0, 0);
-    return;
-  }
-  // thread t holds bins [b0, b0 + 16), b0 = kHistBins - 16 (t + 1): thread 0 the largest keys
-  constexpr int BPT = kHistBins / kThreads;
-  const int b0 = kHistBins - BPT * ((int)threadIdx.x + 1);
-  uint32_t c[BPT];
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) c[j] = 0u;
-  for (int ch0 = 0; ch0 < C; ch0 += 4) {
-    uint4 v[4][BPT / 4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const uint4* h4 = reinterpret_cast<const uint4*>(
-          ghist + ((int64_t)row * C + min(ch0 + cc, C - 1)) * kHistBins + b0);
-#pragma unroll
-      for (int j = 0; j < BPT / 4; ++j) v[cc][j] = h4[j];
-    }
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      if (ch0 + cc >= C) break;
-#pragma unroll
-      for (int j = 0; j < BPT / 4; ++j) {
-        c[4 * j] += v[cc][j].x;
-        c[4 * j + 1] += v[cc][j].y;
-        c[4 * j + 2] += v[cc][j].z;
-        c[4 * j + 3] += v[cc][j].w;
+    if (tid == 0) {
+      if (upper) out[1] = -1;
+      else {
+        out[0] = -1;
+        out[2] = 0;
       }
     }
+    return;
+  }
+  const int m = min(n, kSampleMax);
+  int q = kk;
+  if (n > kSampleMax) {
+    const float r = (float)kk * (float)m / (float)n;
+    const float delta = 4.f * sqrtf(r) + 2.f;
+    q = upper ? (int)floorf(r - delta) : (int)ceilf(r + delta);
+  }
+  if (upper && q < 1) {
+    if (tid == 0) out[1] = -1;
+    return;
+  }
+  if (!upper && q > m) {
+    if (tid == 0) {
+      out[0] = 0;
+      out[2] = kk;
+    }
+    return;
+  }
+  const float* x = scores + (int64_t)row * s_ld;
+  float v[kSamplePerThread];
+#pragma unroll
+  for (int u = 0; u < kSamplePerThread; ++u) {
+    const int i = u * kThreads + tid;
+    v[u] = x[sample_token(min(i, m - 1), n)];
+  }
+  for (int i = tid * 4; i < kHistBins; i += kThreads * 4)
+    *reinterpret_cast<uint4*>(bins + i) = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < 4 * 256; i += kThreads) hist[i] = 0u;
+  if (tid == 0) kmin = 0xFFFFFFFFu;
+  uint32_t key[kSamplePerThread];
+#pragma unroll
+  for (int u = 0; u < kSamplePerThread; ++u) key[u] = order_key(v[u]);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kSamplePerThread; ++u)
+    if (u * kThreads + tid < m) atomicAdd(&bins[key[u] >> kHistShift], 1u);
+  __syncthreads();
+  // thread t holds bins [b0, b0 + 16), b0 = kHistBins - 16 (t + 1): thread 0 the largest keys
+  constexpr int BPT = kHistBins / kThreads;
+  const int b0 = kHistBins - BPT * (tid + 1);
+  uint32_t c[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; j += 4) {
+    const uint4 w = *reinterpret_cast<const uint4*>(bins + b0 + j);
+    c[j] = w.x;
+    c[j + 1] = w.y;
+    c[j + 2] = w.z;
+    c[j + 3] = w.w;
   }
   int sum = 0;
 #pragma unroll
   for (int j = 0; j < BPT; ++j) sum += (int)c[j];
   int total;
   const int excl = block_excl_scan(sum, red, &total);
-  if (excl < kk && kk <= excl + sum) {
+  if (excl < q && q <= excl + sum) {
     int acc = excl;
 #pragma unroll
     for (int j = BPT - 1; j >= 0; --j) {
-      if (acc + (int)c[j] >= kk) {
-        info[row] = make_int4(b0 + j, acc, kk - acc, kk);
+      if (acc + (int)c[j] >= q) {
+        sh[0] = b0 + j;
+        sh[1] = q - acc;  // rank inside the bin, 1-based
         break;
       }
       acc += (int)c[j];
     }
   }
+  __syncthreads();
+  const uint32_t bq = (uint32_t)sh[0];
+  const int qin = sh[1];
+  uint32_t low;
+  int need;
+  bool whole;
+  radix_threshold(
+      [&](auto visit) {
+#pragma unroll
+        for (int u = 0; u < kSamplePerThread; ++u)
+          if (u * kThreads + tid < m && (key[u] >> kHistShift) == bq) visit(key[u] << kHistBits);
+      },
+      qin, hist, &low, &need, &whole);
+  uint32_t thr = (bq << kHistShift) | (low >> kHistBits);
+  if (upper && whole) {
+    // thr is a prefix that exactly the q largest keys reach: hi is the smallest of them
+    uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int u = 0; u < kSamplePerThread; ++u)
+      if (u * kThreads + tid < m && key[u] >= thr) mn = min(mn, key[u]);
+    atomicMin(&kmin, mn);
+    __syncthreads();
+    thr = kmin;
+  }
+  if (tid == 0) {
+    if (upper) out[1] = (int)thr;
+    else {
+      out[0] = (int)thr;
+      out[2] = kk;
+    }
+  }
 }
 
-// ---------------------------------------------------------------- (2) candidates per segment
+// ---------------------------------------------------------------- (1) candidates per segment
 
+// A wave per segment; kGatherU rows of 64 tokens of every set are loaded (one element per lane,
+// clamped in bounds) before the first is classified.  (Loading a whole 1024-token segment at
+// once with 16-byte loads measured about 3 us slower: the registers it takes leave one round of
+// workgroups per CU with no slack.)
 __global__ __launch_bounds__(kThreads) void union_gather_kernel(
     const float* __restrict__ scores, int64_t s_ld, Shape u, int n, const int4* __restrict__ info,
     int nseg, int seg_len, uint32_t* __restrict__ cand, int32_t* __restrict__ ccnt,
-    uint2* __restrict__ ibl, int32_t* __restrict__ ibc) {
+    uint2* __restrict__ ibl, int32_t* __restrict__ ibc, int32_t* __restrict__ iac) {
   const int g = blockIdx.y;
   const int lane = lane_id(), wid = threadIdx.x / kWave;
   const int seg = blockIdx.x * kWaves4 + wid;
   if (seg >= nseg) return;
   const int beg = min(n, seg * seg_len), end = min(n, beg + seg_len);
-  uint32_t bst[kMaxSets];
+  uint32_t lo[kMaxSets], hi[kMaxSets];
+  bool on[kMaxSets];
   const float* xs[kMaxSets];
 #pragma unroll
   for (int s = 0; s < kMaxSets; ++s) {
     const int sr = s < u.S ? s : 0;
     const int64_t row = set_row(u, g, sr);
-    bst[s] = s < u.S ? (uint32_t)info[row].x : 0xFFFFFFFFu;
+    const int4 inf = info[row];
+    lo[s] = (uint32_t)inf.x;
+    hi[s] = (uint32_t)inf.y;
+    on[s] = s < u.S && inf.z > 0;
     xs[s] = scores + row * s_ld;
   }
   const int64_t gs = (int64_t)g * nseg + seg;
   uint32_t* out = cand + gs * seg_len;
   uint2* lists = ibl + gs * kMaxSets * kListCap;
   const uint64_t lt = (1ull << lane) - 1ull;
-  int run = 0, runs[kMaxSets] = {0, 0, 0, 0};
+  int run = 0, runs[kMaxSets] = {0, 0, 0, 0}, nab[kMaxSets] = {0, 0, 0, 0};
   for (int t0 = beg; t0 < end; t0 += kWave * kGatherU) {
     float v[kGatherU][kMaxSets];
 #pragma unroll
@@ -242,44 +306,57 @@ __global__ __launch_bounds__(kThreads) void union_gather_kernel(
 #pragma unroll
       for (int s = 0; s < kMaxSets; ++s) {
         key[s] = order_key(v[q][s]);
-        const uint32_t bin = key[s] >> kHistShift;
-        m |= (uint32_t)(live && bin > bst[s]) << s;
-        m |= (uint32_t)(live && bin == bst[s]) << (4 + s);
+        const bool ab = live && on[s] && key[s] > hi[s];
+        const bool ir = live && on[s] && key[s] >= lo[s] && key[s] <= hi[s];
+        nab[s] += ab;
+        m |= (uint32_t)ab << s;
+        m |= (uint32_t)ir << (4 + s);
       }
       const uint64_t bal = __ballot(m != 0);
       const int p = run + __popcll(bal & lt);
       if (m) out[p] = ((uint32_t)(t - beg) << 8) | m;
       run += __popcll(bal);
-      if (__ballot(m >> 4)) {  // some lane holds an in-b* key (a few per cent of the tokens)
+      if (__ballot(m >> 4)) {  // some lane holds an in-range key (a few per cent of the tokens)
 #pragma unroll
         for (int s = 0; s < kMaxSets; ++s) {
           const bool ib = (m >> (4 + s)) & 1u;
           const uint64_t bs = __ballot(ib);
           const int ps = runs[s] + __popcll(bs & lt);
           if (ib && ps < kListCap)
-            lists[s * kListCap + ps] = make_uint2((uint32_t)(seg * seg_len + p), key[s]);
+            lists[s * kListCap + ps] =
+                make_uint2((uint32_t)(seg * seg_len + p) | ((uint32_t)(t - beg) << kSlotBits),
+                           key[s]);
           runs[s] += __popcll(bs);
         }
       }
     }
   }
+#pragma unroll
+  for (int s = 0; s < kMaxSets; ++s)
+    nab[s] = __builtin_amdgcn_readlane(wave_incl_scan(nab[s]), kWave - 1);
   if (lane == 0) ccnt[gs] = run;
-  if (lane < kMaxSets) ibc[gs * kMaxSets + lane] = runs[0] * (lane == 0) + runs[1] * (lane == 1) +
-                                                   runs[2] * (lane == 2) + runs[3] * (lane == 3);
+  if (lane < kMaxSets) {
+    ibc[gs * kMaxSets + lane] = runs[0] * (lane == 0) + runs[1] * (lane == 1) +
+                                runs[2] * (lane == 2) + runs[3] * (lane == 3);
+    iac[gs * kMaxSets + lane] = nab[0] * (lane == 0) + nab[1] * (lane == 1) +
+                                nab[2] * (lane == 2) + nab[3] * (lane == 3);
+  }
 }
 
-// ---------------------------------------------------------------- (3) exact threshold per row
+// ---------------------------------------------------------------- (2) exact threshold per row
 
 // Exclusive prefix of the per-segment counts cnt[i * stride] (i < nseg) into pre[0..nseg] (LDS),
-// by the whole workgroup; returns the total.  `red` holds NT/64 + 1 ints of LDS.
+// by the whole workgroup; returns the total and, in *extra_sum, the sum of extra[i * stride]
+// (loaded beside the counts).  `red` holds NT/64 + 1 ints of LDS.
 template <int NT>
-__device__ int segment_prefix(const int32_t* cnt, int64_t stride, int nseg, int cap, int* pre,
-                              int* red, bool* over) {
-  int carry = 0;
+__device__ int segment_prefix(const int32_t* cnt, const int32_t* extra, int64_t stride, int nseg,
+                              int cap, int* pre, int* red, bool* over, int* extra_sum) {
+  int carry = 0, xs = 0;
   bool ov = false;
   for (int i0 = 0; i0 < nseg; i0 += NT) {
     const int i = i0 + (int)threadIdx.x;
     const int c = i < nseg ? cnt[(int64_t)i * stride] : 0;
+    xs += i < nseg ? extra[(int64_t)i * stride] : 0;
     ov = ov || c > cap;
     int tot;
     const int ex = block_excl_scan(min(c, cap), red, &tot);
@@ -288,6 +365,7 @@ __device__ int segment_prefix(const int32_t* cnt, int64_t stride, int nseg, int 
   }
   if (threadIdx.x == 0) pre[nseg] = carry;
   *over = __syncthreads_or(ov);
+  block_excl_scan(xs, red, extra_sum);
   return carry;
 }
 
@@ -305,29 +383,34 @@ __device__ __forceinline__ int segment_of(const int* pre, int nseg, int e) {
 }
 
 
-// thr[row] = (threshold key, position of the last tied candidate taken, whole, 0); every taken
-// in-b* candidate of the row's set gets its taken bit in its entry.
+// thr[row] = (threshold key, token of the last tied key taken, whole, kind): the row keeps every
+// key above the threshold key and, when whole is 0, the keys equal to it up to that token
+// (whole = 1: every key equal to it); kind is kRowRange, kRowTakenOnly or kRowDirect (see the
+// pipeline above).  Every taken in-range candidate of the row's set (kRowTakenOnly: every
+// taken candidate) gets its taken bit in its entry.
 __global__ __launch_bounds__(kThreads) void union_thr_kernel(
     const float* __restrict__ scores, int64_t s_ld, Shape u, int n,
     const int4* __restrict__ info, int nseg, int seg_len, uint32_t* __restrict__ cand,
     const int32_t* __restrict__ ccnt, const uint2* __restrict__ ibl,
-    const int32_t* __restrict__ ibc, int4* __restrict__ thr_out) {
+    const int32_t* __restrict__ ibc, const int32_t* __restrict__ iac, int4* __restrict__ thr_out) {
   __shared__ uint32_t lkey[kThrCap];
   __shared__ int32_t lpos[kThrCap];
   __shared__ int pre[kMaxSegs + 1];
   __shared__ __align__(16) uint32_t hist[4 * 256];
   __shared__ int red[kWaves4 + 1], weq[kWaves4], sh[8];
+  __shared__ uint32_t kand, kor;
   const int s = blockIdx.x, g = blockIdx.y;
   const int lane = lane_id(), wid = threadIdx.x / kWave, tid = threadIdx.x;
   const int64_t row = set_row(u, g, s);
   const int4 inf = info[row];
-  const int bstar = inf.x, kin = inf.z, kk = inf.w;
-  if (kk <= 0) {
-    if (tid == 0) thr_out[row] = make_int4(0, -1, 0, 0);
+  const uint32_t lo_key = (uint32_t)inf.x;
+  const int kk = inf.z;
+  if (kk <= 0) {  // no order key reaches 0xFFFFFFFF: nothing is kept
+    if (tid == 0) thr_out[row] = make_int4(-1, -1, 0, kRowRange);
     return;
   }
   const float* x = scores + row * s_ld;
-  const uint32_t sbit = 1u << (4 + s);
+  const uint32_t abit = 1u << s, sbit = 1u << (4 + s);
   const uint32_t tbit = 1u << (kTakenShift + s);
   const int64_t gbase = (int64_t)g * nseg;
   uint32_t* gcand = cand + gbase * seg_len;
@@ -335,16 +418,22 @@ __global__ __launch_bounds__(kThreads) void union_thr_kernel(
   if (tid == 0) {
     sh[1] = -1;
     sh[2] = -1;
+    kand = 0xFFFFFFFFu;
+    kor = 0u;
   }
+  // in-range list lengths and keys above the range, over all segments
   bool over;
-  const int total = segment_prefix<kThreads>(ibc + gbase * kMaxSets + s, kMaxSets, nseg, kListCap,
-                                             pre, red, &over);
-  over = over || total > kThrCap || total < kin;
+  int above;
+  const int total = segment_prefix<kThreads>(ibc + gbase * kMaxSets + s, iac + gbase * kMaxSets + s,
+                                             kMaxSets, nseg, kListCap, pre, red, &over, &above);
+  const int kin = kk - above;  // keys of the top kk that lie in the range
+  over = over || total > kThrCap || kin < 1 || kin > total;
 
   if (!over) {
-    // ---- this set's in-b* candidates, in token order, into LDS (all loads of a batch at once)
+    // ---- this set's in-range candidates, in token order, into LDS (all loads of a batch at once)
     const uint2* lists = ibl + gbase * kMaxSets * kListCap + s * kListCap;
     constexpr int U = 8;
+    uint32_t a_and = 0xFFFFFFFFu, a_or = 0u;
     for (int e0 = 0; e0 < total; e0 += kThreads * U) {
       uint2 ev[U];
       int ee[U];
@@ -357,22 +446,37 @@ __global__ __launch_bounds__(kThreads) void union_thr_kernel(
       }
 #pragma unroll
       for (int q = 0; q < U; ++q) {
+        a_and &= ev[q].y;  // clamped entries repeat a listed key: harmless to the and / or
+        a_or |= ev[q].y;
         if (e0 + q * kThreads + tid < total) {
-          lpos[ee[q]] = (int)ev[q].x;
+          lpos[ee[q]] = (int)ev[q].x;  // candidate slot | token offset << kSlotBits
           lkey[ee[q]] = ev[q].y;
         }
       }
     }
+    // the bits every listed key shares: the radix search starts below them
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      a_and &= (uint32_t)__shfl_xor((int)a_and, o);
+      a_or |= (uint32_t)__shfl_xor((int)a_or, o);
+    }
+    if (lane == 0) {
+      atomicAnd(&kand, a_and);
+      atomicOr(&kor, a_or);
+    }
     __syncthreads();
-    uint32_t tthr;
+    const uint32_t diff = kand ^ kor;
+    const int shift = diff ? __builtin_clz(diff) : 0;
+    const uint32_t common = shift ? kand & (0xFFFFFFFFu << (32 - shift)) : 0u;
+    uint32_t t_key;
     int need;
     bool whole;
     radix_threshold(
         [&](auto visit) {
-          for (int j = tid; j < total; j += kThreads) visit(lkey[j] << kHistBits);
+          for (int j = tid; j < total; j += kThreads) visit(lkey[j] << shift);
         },
-        kin, hist, &tthr, &need, &whole);
-    const uint32_t t_key = ((uint32_t)bstar << kHistShift) | (tthr >> kHistBits);
+        kin, hist, &t_key, &need, &whole);
+    t_key = common | (t_key >> shift);
     int cut = 0x7FFFFFFF;
     if (!whole) {
       // the need-th tie in token order: wave w counts over its contiguous part of the entries
@@ -405,67 +509,84 @@ __global__ __launch_bounds__(kThreads) void union_thr_kernel(
     }
     for (int j = tid; j < total; j += kThreads) {
       const uint32_t kv = lkey[j];
-      if (kv > t_key || (kv == t_key && (whole || j <= cut))) atomicOr(&gcand[lpos[j]], tbit);
+      if (kv > t_key || (kv == t_key && (whole || j <= cut)))
+        atomicOr(&gcand[lpos[j] & kSlotMask], tbit);
     }
-    if (tid == 0) thr_out[row] = make_int4((int)t_key, cut, whole ? 1 : 0, 0);
+    if (tid == 0) {
+      // in whole-row terms: "whole" keeps every key >= max(prefix, lo) (no key below lo is in
+      // range); otherwise the cut entry's token
+      int cut_tok = -1;
+      uint32_t tk = t_key;
+      if (whole) {
+        tk = t_key > lo_key ? t_key : lo_key;
+      } else if (cut >= 0) {
+        const uint32_t e = (uint32_t)lpos[cut];
+        cut_tok = (int)((e & kSlotMask) / seg_len) * seg_len + (int)(e >> kSlotBits);
+      }
+      thr_out[row] = make_int4((int)tk, cut_tok, whole ? 1 : 0, kRowRange);
+    }
     return;
   }
 
-  // ---- fallback (lists overflowed): radix select over the whole row, the cut among the ties
-  // by a count in token order, then the taken bit of every in-b* candidate of the set
-  {
-    uint32_t t_key;
-    int need;
-    radix_select<kThreads>(
-        [&](auto&& visit) {
-          for (int i = tid; i < n; i += kThreads) visit(order_key(x[i]));
-        },
-        kk, hist, sh, &t_key, &need);
-    const int seg_r = ((n + kWaves4 - 1) / kWaves4 + kWave - 1) / kWave * kWave;
-    const int lo = min(n, wid * seg_r), hi = min(n, lo + seg_r);
-    int e = 0;
+  // ---- fallback (the range missed the k-th key, or lists overflowed): radix select over the
+  // whole row, the cut among the ties by a count in token order
+  uint32_t t_key;
+  int need;
+  radix_select<kThreads>(
+      [&](auto&& visit) {
+        for (int i = tid; i < n; i += kThreads) visit(order_key(x[i]));
+      },
+      kk, hist, sh, &t_key, &need);
+  const int seg_r = ((n + kWaves4 - 1) / kWaves4 + kWave - 1) / kWave * kWave;
+  const int lo = min(n, wid * seg_r), hi = min(n, lo + seg_r);
+  int e = 0;
+  for (int i0 = lo; i0 < hi; i0 += kWave) {
+    const int i = i0 + lane;
+    e += __popcll(__ballot(i < hi && order_key(x[min(i, n - 1)]) == t_key));
+  }
+  if (lane == 0) weq[wid] = e;
+  __syncthreads();
+  int pr = 0;
+  for (int w = 0; w < wid; ++w) pr += weq[w];
+  if (pr < need && need <= pr + e) {
+    int rem = need - pr;
     for (int i0 = lo; i0 < hi; i0 += kWave) {
       const int i = i0 + lane;
-      e += __popcll(__ballot(i < hi && order_key(x[min(i, n - 1)]) == t_key));
-    }
-    if (lane == 0) weq[wid] = e;
-    __syncthreads();
-    int pr = 0;
-    for (int w = 0; w < wid; ++w) pr += weq[w];
-    if (pr < need && need <= pr + e) {
-      int rem = need - pr;
-      for (int i0 = lo; i0 < hi; i0 += kWave) {
-        const int i = i0 + lane;
-        const uint64_t bal = __ballot(i < hi && order_key(x[min(i, n - 1)]) == t_key);
-        const int c = __popcll(bal);
-        if (rem <= c) {
-          if (lane == 0) sh[2] = i0 + kth_set_bit(bal, rem - 1);
-          break;
-        }
-        rem -= c;
+      const uint64_t bal = __ballot(i < hi && order_key(x[min(i, n - 1)]) == t_key);
+      const int c = __popcll(bal);
+      if (rem <= c) {
+        if (lane == 0) sh[2] = i0 + kth_set_bit(bal, rem - 1);
+        break;
       }
+      rem -= c;
     }
-    __syncthreads();
-    const int cut = sh[2];
-    for (int sg = wid; sg < nseg; sg += kWaves4) {
-      const int cnt = ccnt[gbase + sg];
-      for (int i = lane; i < cnt; i += kWave) {
-        const uint32_t ev = gcand[(int64_t)sg * seg_len + i];
-        if (!(ev & sbit)) continue;
-        const int tok = sg * seg_len + (int)((ev >> 8) & (kMaxSegLen - 1));
-        const uint32_t kv = order_key(x[tok]);
-        if (kv > t_key || (kv == t_key && tok <= cut))
-          atomicOr(&gcand[(int64_t)sg * seg_len + i], tbit);
-      }
-    }
-    if (tid == 0) thr_out[row] = make_int4((int)t_key, cut, 0, 0);
   }
+  __syncthreads();
+  const int cut = sh[2];
+  if (t_key < lo_key) {
+    // some kept key is not a candidate: the write pass selects this group from its scores
+    if (tid == 0) thr_out[row] = make_int4((int)t_key, cut, 0, kRowDirect);
+    return;
+  }
+  // every kept key is a candidate (above or in range) of the set: mark the kept ones
+  for (int sg = wid; sg < nseg; sg += kWaves4) {
+    const int cnt = ccnt[gbase + sg];
+    for (int i = lane; i < cnt; i += kWave) {
+      const uint32_t ev = gcand[(int64_t)sg * seg_len + i];
+      if (!(ev & (abit | sbit))) continue;
+      const int tok = sg * seg_len + (int)((ev >> 8) & (kMaxSegLen - 1));
+      const uint32_t kv = order_key(x[tok]);
+      if (kv > t_key || (kv == t_key && tok <= cut))
+        atomicOr(&gcand[(int64_t)sg * seg_len + i], tbit);
+    }
+  }
+  if (tid == 0) thr_out[row] = make_int4((int)t_key, cut, 0, kRowTakenOnly);
 }
 
-// ---------------------------------------------------------------- (4) union and index lists
+// ---------------------------------------------------------------- (3) union and index lists
 
-__device__ __forceinline__ uint32_t final_mask(uint32_t e) {
-  return (e & 15u) | ((e >> kTakenShift) & 15u);
+__device__ __forceinline__ uint32_t final_mask(uint32_t e, uint32_t honoured) {
+  return (e & honoured) | ((e >> kTakenShift) & 15u);
 }
 
 // Workgroup (o, g): o = 0 writes group g's union list, its masks and count; o = 1 + s writes
@@ -474,12 +595,15 @@ __device__ __forceinline__ uint32_t final_mask(uint32_t e) {
 // of segment l of the current 64; for a batch of kWave * kWriteU entries the wave first writes,
 // into its own LDS map, every entry's address base (segment start minus the segment's first
 // entry number), so each lane finds an entry's address with one LDS read; every entry's load is
-// issued before the first is used.
+// issued before the first is used.  A group with a kRowDirect set is selected from its score
+// rows instead: wave w owns the tokens [w * per, (w + 1) * per).
 __global__ __launch_bounds__(kWriteThreads) void union_write_kernel(
-    Shape u, int nseg, int seg_len, const uint32_t* __restrict__ cand,
-    const int32_t* __restrict__ ccnt, int32_t* __restrict__ idx, int64_t idx_ld,
-    int32_t* __restrict__ count, int32_t* __restrict__ ulist, uint32_t* __restrict__ umask,
-    int32_t* __restrict__ ucount, int64_t u_ld) {
+    const float* __restrict__ scores, int64_t s_ld, Shape u, int n,
+    const int4* __restrict__ thr, int nseg, int seg_len,
+    const uint32_t* __restrict__ cand, const int32_t* __restrict__ ccnt,
+    int32_t* __restrict__ idx, int64_t idx_ld, int32_t* __restrict__ count,
+    int32_t* __restrict__ ulist, uint32_t* __restrict__ umask, int32_t* __restrict__ ucount,
+    int64_t u_ld) {
   constexpr int kBatch = kWave * kWriteU;
   __shared__ int amap[kWriteWaves][kBatch];
   __shared__ int wc[kWriteWaves];
@@ -493,9 +617,60 @@ __global__ __launch_bounds__(kWriteThreads) void union_write_kernel(
   // the output bit this workgroup tracks: any set (union) or set o - 1
   const uint32_t want = o == 0 ? 15u : 1u << (o - 1);
   int* map = amap[wid];
+  // the sets' thresholds: whose above bits count, and whether the group is selected directly
+  uint32_t honoured = 0u;
+  bool direct = false;
+  uint32_t tk[kMaxSets];
+  int tcut[kMaxSets];
+  bool twhole[kMaxSets], ton[kMaxSets];
+  const float* xs[kMaxSets];
+#pragma unroll
+  for (int s = 0; s < kMaxSets; ++s) {
+    const int64_t row = set_row(u, g, s < u.S ? s : 0);
+    const int4 th = thr[row];
+    ton[s] = s < u.S;
+    tk[s] = (uint32_t)th.x;
+    tcut[s] = th.y;
+    twhole[s] = th.z != 0;
+    xs[s] = scores + row * s_ld;
+    if (s < u.S && th.w == kRowRange) honoured |= 1u << s;
+    direct = direct || (s < u.S && th.w == kRowDirect);
+  }
 
-  // body(f[], tok[]) for each batch of this wave's entries, in order (f = 0 past the end)
-  auto for_batches = [&](auto&& body) {
+  // body(f[], tok[]) for each batch of this wave's entries, in order (f = 0 past the end); the
+  // first batch of the first sweep stays in registers (token | mask << kSlotBits) for the second
+  uint32_t keep[kWriteU];
+  auto for_batches = [&](bool second, auto&& body) {
+    if (direct) {
+      const int per = ((n + kWriteWaves - 1) / kWriteWaves + kWave - 1) / kWave * kWave;
+      const int t_lo = min(n, wid * per), t_hi = min(n, t_lo + per);
+      for (int t0 = t_lo; t0 < t_hi; t0 += kBatch) {
+        float v[kWriteU][kMaxSets];
+#pragma unroll
+        for (int q = 0; q < kWriteU; ++q)
+#pragma unroll
+          for (int s = 0; s < kMaxSets; ++s)
+            v[q][s] = xs[s][min(t0 + q * kWave + lane, t_hi - 1)];
+        uint32_t f[kWriteU];
+        int tok[kWriteU];
+#pragma unroll
+        for (int q = 0; q < kWriteU; ++q) {
+          const int t = t0 + q * kWave + lane;
+          uint32_t m = 0u;
+#pragma unroll
+          for (int s = 0; s < kMaxSets; ++s) {
+            const uint32_t key = order_key(v[q][s]);
+            const bool kept =
+                key > tk[s] || (key == tk[s] && (twhole[s] || t <= tcut[s]));
+            m |= (uint32_t)(ton[s] && kept) << s;
+          }
+          f[q] = t < t_hi ? m & want : 0u;
+          tok[q] = t;
+        }
+        body(f, tok);
+      }
+      return;
+    }
     for (int c0 = sg_lo; c0 < sg_hi; c0 += kWave) {
       const int nsw = min(kWave, sg_hi - c0);
       const int c = lane < nsw ? ccnt[gbase + c0 + lane] : 0;
@@ -503,26 +678,39 @@ __global__ __launch_bounds__(kWriteThreads) void union_write_kernel(
       const int excl = incl - c;
       const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
       for (int e0 = 0; e0 < tot; e0 += kBatch) {
-        for (int j = 0; j < nsw; ++j) {
-          const int sj = __builtin_amdgcn_readlane(excl, j), cj = __builtin_amdgcn_readlane(c, j);
-          const int a = max(sj, e0), z = min(sj + cj, e0 + kBatch);
-          const int base = (c0 + j) * seg_len - sj;
-          for (int x = a + lane; x < z; x += kWave) map[x - e0] = base;
-        }
-        uint32_t e[kWriteU];
-        int addr[kWriteU];
-#pragma unroll
-        for (int q = 0; q < kWriteU; ++q) {
-          const int ei = min(e0 + q * kWave + lane, tot - 1);
-          addr[q] = map[ei - e0] + ei;
-          e[q] = gcand[addr[q]];
-        }
+        const bool first_batch = c0 == sg_lo && e0 == 0;
         uint32_t f[kWriteU];
         int tok[kWriteU];
+        if (second && first_batch) {
 #pragma unroll
-        for (int q = 0; q < kWriteU; ++q) {
-          f[q] = e0 + q * kWave + lane < tot ? final_mask(e[q]) & want : 0u;
-          tok[q] = (addr[q] & ~(seg_len - 1)) + (int)((e[q] >> 8) & (kMaxSegLen - 1));
+          for (int q = 0; q < kWriteU; ++q) {
+            f[q] = keep[q] >> kSlotBits;
+            tok[q] = (int)(keep[q] & kSlotMask);
+          }
+        } else {
+          for (int j = 0; j < nsw; ++j) {
+            const int sj = __builtin_amdgcn_readlane(excl, j), cj = __builtin_amdgcn_readlane(c, j);
+            const int a = max(sj, e0), z = min(sj + cj, e0 + kBatch);
+            const int base = (c0 + j) * seg_len - sj;
+            for (int x = a + lane; x < z; x += kWave) map[x - e0] = base;
+          }
+          uint32_t e[kWriteU];
+          int addr[kWriteU];
+#pragma unroll
+          for (int q = 0; q < kWriteU; ++q) {
+            const int ei = min(e0 + q * kWave + lane, tot - 1);
+            addr[q] = map[ei - e0] + ei;
+            e[q] = gcand[addr[q]];
+          }
+#pragma unroll
+          for (int q = 0; q < kWriteU; ++q) {
+            f[q] = e0 + q * kWave + lane < tot ? final_mask(e[q], honoured) & want : 0u;
+            tok[q] = (addr[q] & ~(seg_len - 1)) + (int)((e[q] >> 8) & (kMaxSegLen - 1));
+          }
+          if (!second && first_batch) {
+#pragma unroll
+            for (int q = 0; q < kWriteU; ++q) keep[q] = (uint32_t)tok[q] | (f[q] << kSlotBits);
+          }
         }
         body(f, tok);
       }
@@ -531,7 +719,7 @@ __global__ __launch_bounds__(kWriteThreads) void union_write_kernel(
 
   // sweep 1: this wave's count (per lane, summed over the wave once)
   int cw = 0;
-  for_batches([&](const uint32_t (&f)[kWriteU], const int (&tok)[kWriteU]) {
+  for_batches(false, [&](const uint32_t (&f)[kWriteU], const int (&tok)[kWriteU]) {
 #pragma unroll
     for (int q = 0; q < kWriteU; ++q) cw += f[q] != 0;
   });
@@ -558,7 +746,7 @@ __global__ __launch_bounds__(kWriteThreads) void union_write_kernel(
   uint32_t* om = umask + (int64_t)g * u_ld;
 
   // sweep 2: the same entries, each stored at its ballot rank
-  for_batches([&](const uint32_t (&f)[kWriteU], const int (&tok)[kWriteU]) {
+  for_batches(true, [&](const uint32_t (&f)[kWriteU], const int (&tok)[kWriteU]) {
 #pragma unroll
     for (int q = 0; q < kWriteU; ++q) {
       const uint64_t bal = __ballot(f[q] != 0);
@@ -631,35 +819,28 @@ extern "C" SPK_API spk_status topk_select_union(
   const Shape u{B, T, Hq, Hkv, Hq / Hkv, S, scope == SPK_SEL_PER_Q_HEAD ? 1 : 0};
   const int rows = groups * S;
   // rows are indexed by blockIdx.y over the (b, t, head) rows in memory order; every row
-  // belongs to exactly one (group, set).  With n == 0 nothing is selected and the bin pass
-  // reads no histogram.
-  uint32_t* hist = reinterpret_cast<uint32_t*>(w + l.off_hist);
-  const int hc = l.hist_chunks;
-  if (n > 0) {
-    const int chunk = (int)ceil_div(n, hc);
-    hipLaunchKernelGGL(union_hist_kernel, dim3(hc, rows), dim3(kThreads), 0, st, scores, s_ld, n,
-                       chunk, hist);
-    spk_status e = check_launch("topk_select_union/histogram");
-    if (e != SPK_OK) return e;
-  }
+  // belongs to exactly one (group, set)
   int4* info = reinterpret_cast<int4*>(w + l.off_info);
   int4* thr = reinterpret_cast<int4*>(w + l.off_thr);
   uint32_t* cand = reinterpret_cast<uint32_t*>(w + l.off_cand);
   int32_t* ccnt = reinterpret_cast<int32_t*>(w + l.off_ccnt);
   uint2* ibl = reinterpret_cast<uint2*>(w + l.off_ibl);
   int32_t* ibc = reinterpret_cast<int32_t*>(w + l.off_ibc);
-  hipLaunchKernelGGL(union_bin_kernel, dim3(rows), dim3(kThreads), 0, st, hist, hc, n, k, info);
-  spk_status e = check_launch("topk_select_union/bin");
+  int32_t* iac = reinterpret_cast<int32_t*>(w + l.off_iac);
+  hipLaunchKernelGGL(union_range_kernel, dim3(2, rows), dim3(kThreads), 0, st, scores, s_ld, n, k,
+                     info);
+  spk_status e = check_launch("topk_select_union/range");
   if (e != SPK_OK) return e;
   hipLaunchKernelGGL(union_gather_kernel, dim3(l.parts, groups), dim3(kThreads), 0, st, scores,
-                     s_ld, u, n, info, l.nseg, l.seg_len, cand, ccnt, ibl, ibc);
+                     s_ld, u, n, info, l.nseg, l.seg_len, cand, ccnt, ibl, ibc, iac);
   e = check_launch("topk_select_union/gather");
   if (e != SPK_OK) return e;
   hipLaunchKernelGGL(union_thr_kernel, dim3(S, groups), dim3(kThreads), 0, st, scores, s_ld, u, n,
-                     info, l.nseg, l.seg_len, cand, ccnt, ibl, ibc, thr);
+                     info, l.nseg, l.seg_len, cand, ccnt, ibl, ibc, iac, thr);
   e = check_launch("topk_select_union/threshold");
   if (e != SPK_OK) return e;
-  hipLaunchKernelGGL(union_write_kernel, dim3(1 + S, groups), dim3(kWriteThreads), 0, st, u, l.nseg,
-                     l.seg_len, cand, ccnt, idx, idx_ld, count, u_list, u_mask, u_count, u_ld);
+  hipLaunchKernelGGL(union_write_kernel, dim3(1 + S, groups), dim3(kWriteThreads), 0, st, scores,
+                     s_ld, u, n, thr, l.nseg, l.seg_len, cand, ccnt, idx, idx_ld, count,
+                     u_list, u_mask, u_count, u_ld);
   return check_launch("topk_select_union/write");
 }

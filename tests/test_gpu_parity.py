@@ -75,6 +75,14 @@ def _rows(kind, n, rows, seed):
         x = r.integers(-4, 5, size=(rows, n)).astype(np.float32)
     elif kind == "allsame":
         x = np.full((rows, n), 1.5, np.float32)
+    elif kind in ("sample_high", "sample_low"):
+        # rows that mislead topk_select_union's key-range estimate: its sample (16-token pieces
+        # starting at floor(j * n / 256), j < 256; the whole row up to 4096 keys) holds the
+        # row's largest keys, or its smallest
+        x = r.standard_normal((rows, n)).astype(np.float32)
+        t = _union_sample_tokens(n)
+        v = r.standard_normal((rows, t.shape[0])).astype(np.float32)
+        x[:, t] = v + 10 if kind == "sample_high" else v - 10
     else:  # "special": signed zeros, infinities, NaN among ties
         x = r.integers(-2, 3, size=(rows, n)).astype(np.float32)
         x[r.random((rows, n)) < 0.2] = -0.0
@@ -82,6 +90,13 @@ def _rows(kind, n, rows, seed):
         x[r.random((rows, n)) < 0.05] = -np.inf
         x[r.random((rows, n)) < 0.05] = np.nan
     return x
+
+
+def _union_sample_tokens(n):
+    if n <= 4096:
+        return np.arange(n)
+    i = np.arange(4096)
+    return (i // 16) * n // 256 + i % 16
 
 
 @pytest.mark.parametrize("n", [1, 7, 64, 512, 1000, 4096, 4097, 10000, 16384, 16385, 70001])
@@ -1761,12 +1776,15 @@ def test_stream_read_reference_reads_every_word():
 # ------------------------------------------------------------------------------------ union pipeline
 
 @pytest.mark.parametrize("n", [16385, 20000, 70001])
-@pytest.mark.parametrize("kind", ["normal", "ties", "allsame", "special"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "allsame", "special", "sample_high", "sample_low"])
 @pytest.mark.parametrize("scope,T,G", [("per_q_head", 1, 4), ("per_kv_head", 4, 4), ("per_q_head", 1, 2)])
 def test_topk_union_bit_exact(n, kind, scope, T, G):
     """topk_select_union against the oracle: every set's selection equals oracle.topk of its row
     bit for bit, the union is the sorted set union and each mask bit says which sets hold the
-    row; heavy ties take the fallback inside the threshold pass."""
+    row.  Heavy ties overflow the in-range lists and take the whole-row threshold; rows whose
+    sampled keys are their largest put kept keys below the estimated range (direct selection
+    from the scores), rows whose sampled keys are their smallest put too many keys above it
+    (whole-row threshold, taken bits only)."""
     say("topk-union", n, kind, scope, T, G)
     B, Hkv = 2, 2
     Hq = Hkv * G
@@ -1775,6 +1793,12 @@ def test_topk_union_bit_exact(n, kind, scope, T, G):
     x = _rows(kind, n, rows, seed=n + T + G).reshape(B, T, Hs, n)
     xs = torch.tensor(x, device=DEV)
     S = T * G if scope == "per_q_head" else T
+    if kind == "sample_high":
+        # the range's lower end is the sample's key of rank about r + 4 sqrt(r) + 2: for k = 700
+        # fewer than k row keys reach it (only sampled keys are that large), so kept keys lie
+        # below the range
+        r = 700 * 4096 / n
+        assert np.ceil(r + 4 * np.sqrt(r) + 2) < 700
     for k in sorted({0, 1, 700, 2622, n - 1, n, n + 3}):
         idx, cnt, ul, um, uc = spk.topk_select_union(xs, k, scope, Hkv)
         torch.cuda.synchronize()
