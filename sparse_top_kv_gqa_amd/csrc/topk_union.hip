@@ -261,10 +261,25 @@ __global__ __launch_bounds__(kThreads) void union_range_kernel(const float* __re
 
 // ---------------------------------------------------------------- (1) candidates per segment
 
+// Number of lanes below this one whose bit is set in the wave mask m.
+__device__ __forceinline__ int rank_in_wave(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Float of an order key (the inverse of order_key on the keys it produces; key 0, the key of
+// NaN, and the sentinel 0xFFFFFFFF come out as NaN, which compares false).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // A wave per segment; kGatherU rows of 64 tokens of every set are loaded (one element per lane,
-// clamped in bounds) before the first is classified.  (Loading a whole 1024-token segment at
-// once with 16-byte loads measured about 3 us slower: the registers it takes leave one round of
-// workgroups per CU with no slack.)
+// clamped in bounds) before the first is classified.  A score is compared as a float with the
+// range's ends (key order and float order agree on every non-NaN score, and -0 == +0 in both);
+// a NaN score (key 0) is in range only when lo is 0.  The classes are wave ballots, so counting
+// and compaction run on scalar masks; order keys are formed only for in-range list entries.
+// (Loading a whole 1024-token segment at once with 16-byte loads measured about 3 us slower:
+// the registers it takes leave one round of workgroups per CU with no slack.)
 __global__ __launch_bounds__(kThreads) void union_gather_kernel(
     const float* __restrict__ scores, int64_t s_ld, Shape u, int n, const int4* __restrict__ info,
     int nseg, int seg_len, uint32_t* __restrict__ cand, int32_t* __restrict__ ccnt,
@@ -274,66 +289,72 @@ __global__ __launch_bounds__(kThreads) void union_gather_kernel(
   const int seg = blockIdx.x * kWaves4 + wid;
   if (seg >= nseg) return;
   const int beg = min(n, seg * seg_len), end = min(n, beg + seg_len);
-  uint32_t lo[kMaxSets], hi[kMaxSets];
-  bool on[kMaxSets];
+  float hf[kMaxSets], lf[kMaxSets];
+  uint32_t lo_all[kMaxSets];
   const float* xs[kMaxSets];
 #pragma unroll
   for (int s = 0; s < kMaxSets; ++s) {
     const int sr = s < u.S ? s : 0;
     const int64_t row = set_row(u, g, sr);
     const int4 inf = info[row];
-    lo[s] = (uint32_t)inf.x;
-    hi[s] = (uint32_t)inf.y;
-    on[s] = s < u.S && inf.z > 0;
+    const bool on = s < u.S && inf.z > 0;
+    hf[s] = on ? key_float((uint32_t)inf.y) : __uint_as_float(0x7FFFFFFFu);
+    lf[s] = on ? key_float((uint32_t)inf.x) : __uint_as_float(0x7FFFFFFFu);
+    lo_all[s] = on && inf.x == 0 ? 1u : 0u;
     xs[s] = scores + row * s_ld;
   }
   const int64_t gs = (int64_t)g * nseg + seg;
   uint32_t* out = cand + gs * seg_len;
   uint2* lists = ibl + gs * kMaxSets * kListCap;
-  const uint64_t lt = (1ull << lane) - 1ull;
   int run = 0, runs[kMaxSets] = {0, 0, 0, 0}, nab[kMaxSets] = {0, 0, 0, 0};
-  for (int t0 = beg; t0 < end; t0 += kWave * kGatherU) {
+  // kGatherU * 64 tokens from t0; FULL: all of them inside the segment (no clamping)
+  auto chunk = [&](int t0, auto full) {
+    constexpr bool FULL = decltype(full)::value;
     float v[kGatherU][kMaxSets];
 #pragma unroll
     for (int q = 0; q < kGatherU; ++q)
 #pragma unroll
-      for (int s = 0; s < kMaxSets; ++s) v[q][s] = xs[s][min(t0 + q * kWave + lane, end - 1)];
+      for (int s = 0; s < kMaxSets; ++s)
+        v[q][s] = FULL ? xs[s][t0 + q * kWave + lane] : xs[s][min(t0 + q * kWave + lane, end - 1)];
 #pragma unroll
     for (int q = 0; q < kGatherU; ++q) {
       const int t = t0 + q * kWave + lane;
-      const bool live = t < end;
-      uint32_t m = 0, key[kMaxSets];
+      const uint64_t live = FULL ? ~0ull : __ballot(t < end);
+      uint64_t A[kMaxSets], R[kMaxSets], any = 0ull, anyr = 0ull;
 #pragma unroll
       for (int s = 0; s < kMaxSets; ++s) {
-        key[s] = order_key(v[q][s]);
-        const bool ab = live && on[s] && key[s] > hi[s];
-        const bool ir = live && on[s] && key[s] >= lo[s] && key[s] <= hi[s];
-        nab[s] += ab;
-        m |= (uint32_t)ab << s;
-        m |= (uint32_t)ir << (4 + s);
+        A[s] = __ballot(v[q][s] > hf[s]) & live;
+        R[s] = (lo_all[s] ? live : __ballot(v[q][s] >= lf[s]) & live) & ~A[s];
+        nab[s] += __popcll(A[s]);
+        any |= A[s] | R[s];
+        anyr |= R[s];
       }
-      const uint64_t bal = __ballot(m != 0);
-      const int p = run + __popcll(bal & lt);
-      if (m) out[p] = ((uint32_t)(t - beg) << 8) | m;
-      run += __popcll(bal);
-      if (__ballot(m >> 4)) {  // some lane holds an in-range key (a few per cent of the tokens)
+      const int p = run + rank_in_wave(any);
+      if (__builtin_amdgcn_inverse_ballot_w64(any)) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int s = 0; s < kMaxSets; ++s)
+          m |= (__builtin_amdgcn_inverse_ballot_w64(A[s]) ? 1u << s : 0u) |
+               (__builtin_amdgcn_inverse_ballot_w64(R[s]) ? 1u << (4 + s) : 0u);
+        out[p] = ((uint32_t)(t - beg) << 8) | m;
+      }
+      run += __popcll(any);
+      if (anyr) {  // some lane holds an in-range key (a few per cent of the tokens)
 #pragma unroll
         for (int s = 0; s < kMaxSets; ++s) {
-          const bool ib = (m >> (4 + s)) & 1u;
-          const uint64_t bs = __ballot(ib);
-          const int ps = runs[s] + __popcll(bs & lt);
-          if (ib && ps < kListCap)
+          const int ps = runs[s] + rank_in_wave(R[s]);
+          if (__builtin_amdgcn_inverse_ballot_w64(R[s]) && ps < kListCap)
             lists[s * kListCap + ps] =
                 make_uint2((uint32_t)(seg * seg_len + p) | ((uint32_t)(t - beg) << kSlotBits),
-                           key[s]);
-          runs[s] += __popcll(bs);
+                           order_key(v[q][s]));
+          runs[s] += __popcll(R[s]);
         }
       }
     }
-  }
-#pragma unroll
-  for (int s = 0; s < kMaxSets; ++s)
-    nab[s] = __builtin_amdgcn_readlane(wave_incl_scan(nab[s]), kWave - 1);
+  };
+  int t0 = beg;
+  for (; t0 + kWave * kGatherU <= end; t0 += kWave * kGatherU) chunk(t0, std::true_type{});
+  if (t0 < end) chunk(t0, std::false_type{});
   if (lane == 0) ccnt[gs] = run;
   if (lane < kMaxSets) {
     ibc[gs * kMaxSets + lane] = runs[0] * (lane == 0) + runs[1] * (lane == 1) +
