@@ -63,7 +63,8 @@ constexpr uint32_t kSlotMask = (1u << kSlotBits) - 1u;
 constexpr int kPieces = 256;      // sample pieces per row
 constexpr int kPieceLen = 16;     // consecutive tokens per piece
 constexpr int kSampleMax = kPieces * kPieceLen;
-constexpr int kSamplePerThread = kSampleMax / kThreads;
+constexpr int kRangeThreads = 256;   // 1024 measured slightly slower
+constexpr int kSamplePerThread = kSampleMax / kRangeThreads;
 // thr_out[row].w: how the write pass treats the row's set
 constexpr int kRowRange = 0;      // threshold found inside the range: above bits and taken bits
 constexpr int kRowTakenOnly = 1;  // whole-row threshold inside the range: taken bits only
@@ -140,12 +141,12 @@ __device__ __forceinline__ int sample_token(int i, int n) {
 // largest key (up to a prefix with the same count for lo).  The sample's key of rank q: a
 // 4096-bin histogram of the top 12 key bits names its bin, a radix search over the low 20
 // bits of that bin's keys the key itself.
-__global__ __launch_bounds__(kThreads) void union_range_kernel(const float* __restrict__ scores,
+__global__ __launch_bounds__(kRangeThreads) void union_range_kernel(const float* __restrict__ scores,
                                                                int64_t s_ld, int n, int k,
                                                                int4* __restrict__ info) {
   __shared__ __align__(16) uint32_t bins[kHistBins];
   __shared__ __align__(16) uint32_t hist[4 * 256];
-  __shared__ int red[kWaves4 + 1], sh[2];
+  __shared__ int red[kRangeThreads / kWave + 1], sh[2];
   __shared__ uint32_t kmin;
   const int row = blockIdx.y, upper = blockIdx.x == 0, tid = threadIdx.x;
   int* out = reinterpret_cast<int*>(info + row);
@@ -182,12 +183,12 @@ __global__ __launch_bounds__(kThreads) void union_range_kernel(const float* __re
   float v[kSamplePerThread];
 #pragma unroll
   for (int u = 0; u < kSamplePerThread; ++u) {
-    const int i = u * kThreads + tid;
+    const int i = u * kRangeThreads + tid;
     v[u] = x[sample_token(min(i, m - 1), n)];
   }
-  for (int i = tid * 4; i < kHistBins; i += kThreads * 4)
+  for (int i = tid * 4; i < kHistBins; i += kRangeThreads * 4)
     *reinterpret_cast<uint4*>(bins + i) = make_uint4(0u, 0u, 0u, 0u);
-  for (int i = tid; i < 4 * 256; i += kThreads) hist[i] = 0u;
+  for (int i = tid; i < 4 * 256; i += kRangeThreads) hist[i] = 0u;
   if (tid == 0) kmin = 0xFFFFFFFFu;
   uint32_t key[kSamplePerThread];
 #pragma unroll
@@ -195,10 +196,10 @@ __global__ __launch_bounds__(kThreads) void union_range_kernel(const float* __re
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < kSamplePerThread; ++u)
-    if (u * kThreads + tid < m) atomicAdd(&bins[key[u] >> kHistShift], 1u);
+    if (u * kRangeThreads + tid < m) atomicAdd(&bins[key[u] >> kHistShift], 1u);
   __syncthreads();
   // thread t holds bins [b0, b0 + 16), b0 = kHistBins - 16 (t + 1): thread 0 the largest keys
-  constexpr int BPT = kHistBins / kThreads;
+  constexpr int BPT = kHistBins / kRangeThreads;
   const int b0 = kHistBins - BPT * (tid + 1);
   uint32_t c[BPT];
 #pragma unroll
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void union_range_kernel(const float* __re
       [&](auto visit) {
 #pragma unroll
         for (int u = 0; u < kSamplePerThread; ++u)
-          if (u * kThreads + tid < m && (key[u] >> kHistShift) == bq) visit(key[u] << kHistBits);
+          if (u * kRangeThreads + tid < m && (key[u] >> kHistShift) == bq) visit(key[u] << kHistBits);
       },
       qin, hist, &low, &need, &whole);
   uint32_t thr = (bq << kHistShift) | (low >> kHistBits);
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void union_range_kernel(const float* __re
     uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
     for (int u = 0; u < kSamplePerThread; ++u)
-      if (u * kThreads + tid < m && key[u] >= thr) mn = min(mn, key[u]);
+      if (u * kRangeThreads + tid < m && key[u] >= thr) mn = min(mn, key[u]);
     atomicMin(&kmin, mn);
     __syncthreads();
     thr = kmin;
@@ -368,10 +369,11 @@ __global__ __launch_bounds__(kThreads) void union_gather_kernel(
 
 // Exclusive prefix of the per-segment counts cnt[i * stride] (i < nseg) into pre[0..nseg] (LDS),
 // by the whole workgroup; returns the total and, in *extra_sum, the sum of extra[i * stride]
-// (loaded beside the counts).  `red` holds NT/64 + 1 ints of LDS.
+// (loaded beside the counts, its wave totals published under the barrier of the overflow
+// vote).  `red` and `xred` hold NT/64 + 1 ints of LDS each.
 template <int NT>
 __device__ int segment_prefix(const int32_t* cnt, const int32_t* extra, int64_t stride, int nseg,
-                              int cap, int* pre, int* red, bool* over, int* extra_sum) {
+                              int cap, int* pre, int* red, int* xred, bool* over, int* extra_sum) {
   int carry = 0, xs = 0;
   bool ov = false;
   for (int i0 = 0; i0 < nseg; i0 += NT) {
@@ -385,8 +387,13 @@ __device__ int segment_prefix(const int32_t* cnt, const int32_t* extra, int64_t 
     carry += tot;
   }
   if (threadIdx.x == 0) pre[nseg] = carry;
+  const int xw = __builtin_amdgcn_readlane(wave_incl_scan(xs), kWave - 1);
+  if (lane_id() == 0) xred[threadIdx.x / kWave] = xw;
   *over = __syncthreads_or(ov);
-  block_excl_scan(xs, red, extra_sum);
+  int xsum = 0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) xsum += xred[w];
+  *extra_sum = xsum;
   return carry;
 }
 
@@ -418,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void union_thr_kernel(
   __shared__ int32_t lpos[kThrCap];
   __shared__ int pre[kMaxSegs + 1];
   __shared__ __align__(16) uint32_t hist[4 * 256];
-  __shared__ int red[kWaves4 + 1], weq[kWaves4], sh[8];
+  __shared__ int red[kWaves4 + 1], xred[kWaves4 + 1], weq[kWaves4], sh[8];
   __shared__ uint32_t kand, kor;
   const int s = blockIdx.x, g = blockIdx.y;
   const int lane = lane_id(), wid = threadIdx.x / kWave, tid = threadIdx.x;
@@ -446,14 +453,15 @@ __global__ __launch_bounds__(kThreads) void union_thr_kernel(
   bool over;
   int above;
   const int total = segment_prefix<kThreads>(ibc + gbase * kMaxSets + s, iac + gbase * kMaxSets + s,
-                                             kMaxSets, nseg, kListCap, pre, red, &over, &above);
+                                             kMaxSets, nseg, kListCap, pre, red, xred, &over,
+                                             &above);
   const int kin = kk - above;  // keys of the top kk that lie in the range
   over = over || total > kThrCap || kin < 1 || kin > total;
 
   if (!over) {
     // ---- this set's in-range candidates, in token order, into LDS (all loads of a batch at once)
     const uint2* lists = ibl + gbase * kMaxSets * kListCap + s * kListCap;
-    constexpr int U = 8;
+    constexpr int U = 12;  // 3072 entries per batch: one batch for the usual 2000-3000
     uint32_t a_and = 0xFFFFFFFFu, a_or = 0u;
     for (int e0 = 0; e0 < total; e0 += kThreads * U) {
       uint2 ev[U];
@@ -848,8 +856,8 @@ extern "C" SPK_API spk_status topk_select_union(
   uint2* ibl = reinterpret_cast<uint2*>(w + l.off_ibl);
   int32_t* ibc = reinterpret_cast<int32_t*>(w + l.off_ibc);
   int32_t* iac = reinterpret_cast<int32_t*>(w + l.off_iac);
-  hipLaunchKernelGGL(union_range_kernel, dim3(2, rows), dim3(kThreads), 0, st, scores, s_ld, n, k,
-                     info);
+  hipLaunchKernelGGL(union_range_kernel, dim3(2, rows), dim3(kRangeThreads), 0, st, scores, s_ld, n,
+                     k, info);
   spk_status e = check_launch("topk_select_union/range");
   if (e != SPK_OK) return e;
   hipLaunchKernelGGL(union_gather_kernel, dim3(l.parts, groups), dim3(kThreads), 0, st, scores,
