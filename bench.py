@@ -337,11 +337,11 @@ def base_result(w, K, W, ms_step, step_bytes, config):
 COPY_KIB = 512 * 1024
 FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
-    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "287cc4daa3667617", 524455.28, 65536.0),
-    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 41342.09, 1442.43),
-    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 41488.8, 1442.38),
-    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 272555.53, 8544.73),
-    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "4307410d969c13c4", 401317.12, 51409.21),
+    "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "b5e7d593716d4c9d", 524470.5, 65536.0),
+    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "8fb09157e9943624", 41343.79, 1442.52),
+    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "8fb09157e9943624", 41488.88, 1442.47),
+    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "8fb09157e9943624", 272562.41, 8544.63),
+    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "8fb09157e9943624", 401315.5, 51452.57),
 }
 
 
