@@ -138,9 +138,9 @@ __device__ __forceinline__ int sample_token(int i, int n) {
 // key is meant to lie in [lo, hi]; hi = 0xFFFFFFFF (no order key is larger) when the sample
 // puts fewer than one key above the range, lo = 0 when it puts the range's end past the
 // sample.  With the whole row as the sample the range is exact: hi and lo are the k-th
-// largest key (up to a prefix with the same count for lo).  The sample's key of rank q: a
-// 4096-bin histogram of the top 12 key bits names its bin, a radix search over the low 20
-// bits of that bin's keys the key itself.
+// largest key.  The sample's key of rank q: a 4096-bin histogram of the top 12 key bits names
+// its bin, a radix search over the low 20 bits of that bin's keys the key itself.  Both ends
+// are keys of sample scores (or the two sentinels).
 __global__ __launch_bounds__(kRangeThreads) void union_range_kernel(const float* __restrict__ scores,
                                                                int64_t s_ld, int n, int k,
                                                                int4* __restrict__ info) {
@@ -241,8 +241,10 @@ __global__ __launch_bounds__(kRangeThreads) void union_range_kernel(const float*
       },
       qin, hist, &low, &need, &whole);
   uint32_t thr = (bq << kHistShift) | (low >> kHistBits);
-  if (upper && whole) {
-    // thr is a prefix that exactly the q largest keys reach: hi is the smallest of them
+  if (whole) {
+    // thr is a prefix that exactly the q largest keys reach, not necessarily a key (the gather
+    // compares scores with the float of each end): both ends become the smallest of those keys,
+    // which the same q sample keys reach
     uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
     for (int u = 0; u < kSamplePerThread; ++u)
@@ -277,7 +279,9 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // A wave per segment; kGatherU rows of 64 tokens of every set are loaded (one element per lane,
 // clamped in bounds) before the first is classified.  A score is compared as a float with the
 // range's ends (key order and float order agree on every non-NaN score, and -0 == +0 in both);
-// a NaN score (key 0) is in range only when lo is 0.  The classes are wave ballots, so counting
+// a NaN score (key 0) is in range only when lo is 0.  One end differs: hi = 0 (NaN's key, from a
+// sample that is mostly NaN) compares false, so every token is in range and none above (lo is
+// then 0 too) — still a valid split for the threshold pass, which lists or re-reads them all.  The classes are wave ballots, so counting
 // and compaction run on scalar masks; order keys are formed only for in-range list entries.
 // (Loading a whole 1024-token segment at once with 16-byte loads measured about 3 us slower:
 // the registers it takes leave one round of workgroups per CU with no slack.)

@@ -75,6 +75,9 @@ def _rows(kind, n, rows, seed):
         x = r.integers(-4, 5, size=(rows, n)).astype(np.float32)
     elif kind == "allsame":
         x = np.full((rows, n), 1.5, np.float32)
+    elif kind == "mostly_nan":
+        x = r.standard_normal((rows, n)).astype(np.float32)
+        x[r.random((rows, n)) < 0.9] = np.nan
     elif kind in ("sample_high", "sample_low"):
         # rows that mislead topk_select_union's key-range estimate: its sample (16-token pieces
         # starting at floor(j * n / 256), j < 256; the whole row up to 4096 keys) holds the
@@ -1775,8 +1778,9 @@ def test_stream_read_reference_reads_every_word():
 
 # ------------------------------------------------------------------------------------ union pipeline
 
-@pytest.mark.parametrize("n", [16385, 20000, 70001])
-@pytest.mark.parametrize("kind", ["normal", "ties", "allsame", "special", "sample_high", "sample_low"])
+@pytest.mark.parametrize("n", [1, 100, 4096, 4097, 16385, 20000, 70001])
+@pytest.mark.parametrize("kind", ["normal", "ties", "allsame", "special", "sample_high", "sample_low",
+                                  "mostly_nan"])
 @pytest.mark.parametrize("scope,T,G", [("per_q_head", 1, 4), ("per_kv_head", 4, 4), ("per_q_head", 1, 2)])
 def test_topk_union_bit_exact(n, kind, scope, T, G):
     """topk_select_union against the oracle: every set's selection equals oracle.topk of its row
@@ -1784,7 +1788,8 @@ def test_topk_union_bit_exact(n, kind, scope, T, G):
     row.  Heavy ties overflow the in-range lists and take the whole-row threshold; rows whose
     sampled keys are their largest put kept keys below the estimated range (direct selection
     from the scores), rows whose sampled keys are their smallest put too many keys above it
-    (whole-row threshold, taken bits only)."""
+    (whole-row threshold, taken bits only); rows of at most 4096 keys are their own sample (an
+    exact range); mostly-NaN rows give the range NaN's key as its upper end."""
     say("topk-union", n, kind, scope, T, G)
     B, Hkv = 2, 2
     Hq = Hkv * G
@@ -1793,10 +1798,10 @@ def test_topk_union_bit_exact(n, kind, scope, T, G):
     x = _rows(kind, n, rows, seed=n + T + G).reshape(B, T, Hs, n)
     xs = torch.tensor(x, device=DEV)
     S = T * G if scope == "per_q_head" else T
-    if kind == "sample_high":
+    if kind == "sample_high" and n > 16384:
         # the range's lower end is the sample's key of rank about r + 4 sqrt(r) + 2: for k = 700
         # fewer than k row keys reach it (only sampled keys are that large), so kept keys lie
-        # below the range
+        # below the range (at these widths; near 4096 keys the sample is most of the row)
         r = 700 * 4096 / n
         assert np.ceil(r + 4 * np.sqrt(r) + 2) < 700
     for k in sorted({0, 1, 700, 2622, n - 1, n, n + 3}):
