@@ -1067,6 +1067,12 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
   // transposing read address: row 4rg + (lane%16)/4, columns 4(lane%4)..+3 of each 16-wide chunk
   const unsigned char* vt_rd = vt + (4 * rg + (lane % 16) / 4) * VST + 8 * (lane % 4);
 
+  // K and V rows: block selections (runs of consecutive rows) stream with nontemporal loads;
+  // explicit lists of scattered single rows read faster with plain ones (measured both ways)
+  auto kv_load = [](uint64_t addr) {
+    if constexpr (MODE == kListExplicit) return gload16(addr);
+    else return gload16_nt(addr);
+  };
   auto issue = [&](int it, uint4 (&kr)[KCH], uint4 (&vr)[PVI], bool& klive) {
     const int tb = it * STEP + wid * TILE;
     const int sk = slot_s[tb + qc];
@@ -1077,11 +1083,11 @@ __attribute__((amdgpu_waves_per_eu(SPK_MFMA_MIN_WAVES))) void attn_partial_mfma_
     uint64_t ka, va;
     row_addr(rbase, sk, ka, va);
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) kr[j] = gload16(ka + kcol + 64 * j);
+    for (int j = 0; j < KCH; ++j) kr[j] = kv_load(ka + kcol + 64 * j);
 #pragma unroll
     for (int i = 0; i < PVI; ++i) {
       row_addr(rbase, sv[i], ka, va);
-      vr[i] = gload16(va + vcol);
+      vr[i] = kv_load(va + vcol);
     }
   };
   // scaled logits of this lane's 4 rows (query qc)
