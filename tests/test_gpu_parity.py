@@ -1615,8 +1615,8 @@ def test_graph_replays_of_decode_steps():
 
 
 def test_graph_replays_of_union_and_lookahead_steps():
-    """The per-head step on rows wide enough for the union pipeline (histogram, bin, gather,
-    threshold, write, attention over the union) and the two-stream lookahead step (selection
+    """The per-head step on rows wide enough for the union pipeline (key range, candidate
+    gather, threshold, write, attention over the union) and the two-stream lookahead step (selection
     ahead on one stream, the persistent copy kernel on another) replay from captured graphs
     exactly, with other library work between replays."""
     say("graph-replay-union-lookahead")
