@@ -1836,9 +1836,9 @@ def test_topk_union_bit_exact(n, kind, scope, T, G):
 
 @pytest.mark.parametrize("which", ["per_head", "spec_verify"])
 def test_union_decode_matches_assembled_path(which):
-    """The union pipeline's step (scores with histograms, top-k with the union, attention over
-    the union) gives the selections and, bit for bit, the attention of the separate calls with
-    the assembly; and matches the oracle on every group."""
+    """The union pipeline's step (scores, top-k with the union, attention over the union) gives
+    the selections and, bit for bit, the attention of the separate calls with the assembly; and
+    matches the oracle on every group."""
     base = W.PER_HEAD_2PCT if which == "per_head" else W.SPEC_VERIFY
     w = W.scaled(base, B=2, Hkv=2, Hq=8, N=20000 + 5, k=700)
     say("union-decode", which, w.name)
