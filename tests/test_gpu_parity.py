@@ -1781,7 +1781,8 @@ def test_stream_read_reference_reads_every_word():
 @pytest.mark.parametrize("n", [1, 100, 4096, 4097, 16385, 20000, 70001])
 @pytest.mark.parametrize("kind", ["normal", "ties", "allsame", "special", "sample_high", "sample_low",
                                   "mostly_nan"])
-@pytest.mark.parametrize("scope,T,G", [("per_q_head", 1, 4), ("per_kv_head", 4, 4), ("per_q_head", 1, 2)])
+@pytest.mark.parametrize("scope,T,G", [("per_q_head", 1, 4), ("per_kv_head", 4, 4), ("per_q_head", 1, 2),
+                                       ("per_kv_head", 1, 4), ("per_kv_head", 3, 2)])
 def test_topk_union_bit_exact(n, kind, scope, T, G):
     """topk_select_union against the oracle: every set's selection equals oracle.topk of its row
     bit for bit, the union is the sorted set union and each mask bit says which sets hold the
