@@ -1538,11 +1538,14 @@ def test_residency_prefetch_other_shapes(d, dtype):
         assert torch.equal(vd[b][:, slots].cpu(), vh[b][:, toks])
 
 
-def test_topk_decode_attn_d64_and_bound():
+@pytest.mark.parametrize("kind", ["normal", "ties", "special"])
+def test_topk_decode_attn_d64_and_bound(kind):
     """sparse_topk_decode_attn at d = 64, with candidate rows on both sides of the register
     layouts' limits (512: two keys per thread, 1024: four) and longer than 1024 (the selection
-    keeps its keys in LDS instead of registers): bit-identical to the two calls."""
-    say("topk-decode-attn-d64-lds")
+    keeps its keys in LDS instead of registers), on ordinary scores, heavy ties and special
+    values (signed zeros, infinities, NaN): bit-identical to the two calls (topk_select's
+    selection is itself checked against the oracle on the same kinds of rows)."""
+    say("topk-decode-attn-d64-lds", kind)
     r = np.random.default_rng(8)
     for d, nb in ((64, 300), (128, 512), (128, 513), (128, 1024), (128, 1025), (128, 3000)):
         B, Hq, Hkv, bs, k = 2, 8, 2, 16, 20
@@ -1550,7 +1553,7 @@ def test_topk_decode_attn_d64_and_bound():
         q = torch.tensor(r.standard_normal((B, 1, Hq, d)), dtype=torch.float32).to(torch.bfloat16).to(DEV)
         kc = torch.tensor(r.standard_normal((B, Hkv, N, d)), dtype=torch.float32).to(torch.bfloat16).to(DEV)
         vc = torch.tensor(r.standard_normal((B, Hkv, N, d)), dtype=torch.float32).to(torch.bfloat16).to(DEV)
-        sc = torch.tensor(r.standard_normal((B, 1, Hkv, nb)), dtype=torch.float32, device=DEV)
+        sc = torch.tensor(_rows(kind, nb, B * Hkv, seed=nb + d).reshape(B, 1, Hkv, nb), device=DEV)
         o1, l1 = torch.empty((B, 1, Hq, d), device=DEV), torch.empty((B, 1, Hq), device=DEV)
         sel = torch.empty((B * Hkv, k), dtype=torch.int32, device=DEV)
         cnt = torch.empty((B * Hkv,), dtype=torch.int32, device=DEV)
