@@ -364,12 +364,17 @@ def test_spec_verify_union_host_rows_residency_invariance(N):
 
 # ------------------------------------------------------------------------------------ tiers
 
-def test_tier_classify_bit_exact_random():
-    say("tiers-random")
+@pytest.mark.parametrize("kind", ["few_values", "all_zero"])
+def test_tier_classify_bit_exact_random(kind):
+    """tier_classify against the oracle: importance with 50 distinct values (heavy ties), or all
+    zero (every row tied, as rows stand before any step has scored them)."""
+    say("tiers-random", kind)
     for trial, (B, n, ns, nr) in enumerate([(3, 1000, 4, 64), (2, 16384, 4, 512), (1, 20000, 4, 512),
                                              (2, 10, 4, 8), (1, 0, 4, 8), (2, 517, 4, 512)]):
         r = np.random.default_rng(trial)
         s = (r.integers(0, 50, size=(B, max(n, 1))) / 7).astype(np.float32)
+        if kind == "all_zero":
+            s[:] = 0.0
         ev = (r.random((B, max(n, 1))) < 0.1).astype(np.uint8)
         for p0, p01, p012 in ((250, 750, None), (250, 750, 950), (100, 400, 1000), (0, 0, 600)):
             st = torch.tensor(s, device=DEV)
