@@ -338,10 +338,10 @@ COPY_KIB = 512 * 1024
 FETCH_COPY_KIB, WRITE_COPY_KIB = 262167.0, 524288.0
 TRAFFIC = {
     "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "b5e7d593716d4c9d", 524470.5, 65536.0),
-    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "28b104011fc5d979", 41677.75, 1442.0),
-    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "28b104011fc5d979", 41826.93, 1442.0),
-    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "28b104011fc5d979", 272557.64, 8544.66),
-    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "28b104011fc5d979", 401312.64, 51457.38),
+    "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "618b9af45143852f", 41685.54, 1442.0),
+    "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "618b9af45143852f", 41823.41, 1442.01),
+    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "618b9af45143852f", 272556.59, 8544.83),
+    "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "618b9af45143852f", 401309.22, 51551.92),
 }
 
 
