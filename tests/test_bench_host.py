@@ -37,3 +37,35 @@ def test_block_fetch_lists_match_the_attended_rows():
         full = torch.full_like(cnt, k)
         if bool((cnt == full).all()):
             assert total == bench.union_rows_block(idx, N, bs, ns, nr)
+
+
+def test_union_rows_read_only_counted_entries_in_range():
+    """union_rows_tokens counts each group's distinct rows over the first count entries of its
+    selection rows only: entries past a row's count (never written by a selection call) and
+    values outside [0, N) count for nothing, so uninitialised index memory cannot send the
+    scatter out of bounds."""
+    gen = torch.Generator().manual_seed(5)
+    B, T, Hs, k, N, G = 2, 1, 8, 6, 40, 4
+    idx = torch.randint(0, N, (B, T, Hs, k), generator=gen, dtype=torch.int32)
+    cnt = torch.randint(0, k + 1, (B, T, Hs), generator=gen, dtype=torch.int32)
+    garbage = idx.clone()
+    live = torch.arange(k) < cnt.unsqueeze(-1)
+    garbage[~live] = torch.randint(-(1 << 30), 1 << 30, (int((~live).sum()),), generator=gen,
+                                   dtype=torch.int32)
+    got = bench.union_rows_tokens(garbage, cnt, G, N).tolist()
+    want = []
+    for b in range(B):
+        for h in range(Hs // G):
+            rows = set()
+            for j in range(h * G, (h + 1) * G):
+                rows |= set(idx[b, 0, j, :int(cnt[b, 0, j])].tolist())
+            want.append(len(rows))
+    assert got == want
+    # out-of-range values inside the counted part count for nothing either
+    bad = idx.clone()
+    bad[..., 0] = N + 3
+    full = torch.full((B, T, Hs), k, dtype=torch.int32)
+    got = bench.union_rows_tokens(bad, full, G, N).tolist()
+    want = [len(set(bad[b, 0, h * G:(h + 1) * G, 1:].reshape(-1).tolist()))
+            for b in range(B) for h in range(Hs // G)]
+    assert got == want
