@@ -197,6 +197,10 @@ SPK_API spk_status topk_select(const float* scores, int64_t s_ld, int rows, int 
  *              u_count device int32 [B*Hkv], the union lengths
  *   ws         device workspace of topk_select_union_workspace_size() bytes, no initial
  *              contents needed
+ * Cost: a sample of each row (1/32 of it past 4096 keys) sets a key range expected to hold the
+ * k-th key, and one pass over the scores collects the keys above and inside it; the result is
+ * the exact top-k whatever the sample says, but a row whose sample misjudges its range (scores
+ * ordered against the sampling pattern, or heavy ties) costs a whole-row pass of its own.
  * Errors: SPK_EINVAL (scope not PER_Q_HEAD / PER_KV_HEAD, sizes, null buffers, short leading
  * dims), SPK_EUNSUPPORTED (S > 4), SPK_EWORKSPACE.
  * ---------------------------------------------------------------------------------------- */
