@@ -53,7 +53,7 @@ constexpr int kWriteWaves = kWriteThreads / kWave;
 constexpr int kMaxSets = 4;
 constexpr int kThrCap = 6144;     // in-range candidates of a row held in LDS by union_thr_kernel
 constexpr int kListCap = 128;     // in-range entries kept per (segment, set) list
-constexpr int kGatherU = 8;       // 64-token sub-rows in flight per wave in union_gather_kernel
+constexpr int kGatherU = 4;       // 64-token sub-rows in flight per wave in union_gather_kernel
 constexpr int kWriteU = 16;       // candidates per lane in flight in union_write_kernel
 constexpr int kTakenShift = 18;   // taken bits of a candidate entry (above the 10-bit offset)
 constexpr int kMaxSegLen = 1024;
@@ -283,8 +283,9 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // sample that is mostly NaN) compares false, so every token is in range and none above (lo is
 // then 0 too) — still a valid split for the threshold pass, which lists or re-reads them all.  The classes are wave ballots, so counting
 // and compaction run on scalar masks; order keys are formed only for in-range list entries.
-// (Loading a whole 1024-token segment at once with 16-byte loads measured about 3 us slower:
-// the registers it takes leave one round of workgroups per CU with no slack.)
+// Four 64-token rows per batch: per-wave timestamps put the launch's span at 17.7 us with four,
+// 19.0 with two or eight, 22.4 with sixteen (the whole segment's loads at once); a whole segment
+// loaded with 16-byte loads measured about 3 us slower still.
 __global__ __launch_bounds__(kThreads) void union_gather_kernel(
     const float* __restrict__ scores, int64_t s_ld, Shape u, int n, const int4* __restrict__ info,
     int nseg, int seg_len, uint32_t* __restrict__ cand, int32_t* __restrict__ ccnt,
