@@ -87,6 +87,9 @@ def parse():
     ap.add_argument("--copy-workgroups", type=int, default=None,
                     help="block_lookahead: workgroups of the persistent copy kernel (default: one "
                          "per (batch, kv-head) group)")
+    ap.add_argument("--slices", type=int, default=None,
+                    help="spec_verify: batch slices the step pipelines over two streams "
+                         "(default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -656,13 +659,18 @@ def bench_token(args, which):
                 loc[b, h, rows] = ~torch.arange(rows.numel(), dtype=torch.int32, device="cuda")
         host_rows_total = w.B * w.Hkv * n_host
     mode = "token_per_head" if which == "per_head" else "token_group_mean"
+    slices = (args.slices if args.slices is not None else w.slices) \
+        if which == "spec_verify" else 1
     dec = TokenSparseDecode(k, v, w.N, w.Hq, w.T, w.k, mode, k_host=kh_pool, v_host=vh_pool,
-                            loc=loc)
+                            loc=loc, slices=slices)
     torch.cuda.synchronize()
     # bytes: every key read by the indexer + the union rows of each step
     per_group_rows = w.G if which == "per_head" else 1
     union = []
     host_frac = []
+    # the rows of one gather launch: the last slice's groups (the whole batch unsliced)
+    b0, b1 = dec.ranges[-1] if dec.parts is not None else (0, w.B)
+    launch_rows = launch_host_rows = None
     for s in range(P):
         dec.step(qs[s])
         u = union_rows_tokens(dec.idx, dec.count, per_group_rows if which == "per_head" else 1, w.N) \
@@ -675,7 +683,12 @@ def bench_token(args, which):
             u = m.sum(dim=1)
             hm = (loc.reshape(B * Hkv, w.N) < 0) & m
             host_frac.append(float(hm.sum()) / float(m.sum()))
+            if s == 0:
+                launch_rows = int(u[b0 * Hkv:b1 * Hkv].sum())
+                launch_host_rows = int(hm[b0 * Hkv:b1 * Hkv].sum())
         union.append(int(u.sum()))
+        if s == 0 and launch_rows is None:
+            launch_rows = int(u.sum())
     index_bytes = w.B * w.Hkv * w.N * w.d * 2
     sel_bytes = [u * ROW_BYTES for u in union]
     stream = torch.cuda.Stream()
@@ -696,19 +709,24 @@ def bench_token(args, which):
            "union_pipeline": bool(dec.union),
            "index_ms": round(idx_ms, 4), "topk_ms": round(topk_ms, 4),
            "attention_ms": round(att_ms, 4), "attention_gather_kernel_ms": round(gather_ms, 4),
-           "attention_selected_GBs": round(union[0] * ROW_BYTES / (gather_ms * 1e-3) / 1e9, 1)}
+           "attention_selected_GBs": round(launch_rows * ROW_BYTES / (gather_ms * 1e-3) / 1e9, 1)}
+    if dec.parts is not None:
+        # attention_ms sums the slices' attentions run one after another; the gather kernel's
+        # time and rates are those of one launch, the last slice's (sequences b0 .. b1 - 1)
+        cfg["batch_slices"] = len(dec.parts)
+        cfg["gather_launch_sequences"] = b1 - b0
     res = base_result(w, K, Wm, ms_step, bytes_avg, cfg)
     if w.host_frac > 0:
         # the gather kernel dominates; its host-resident rows cross PCIe inside it
-        hf = host_frac[0]
         cfg["host_fraction_of_selected_rows"] = round(sum(host_frac) / len(host_frac), 4)
         cfg["host_rows_resident"] = host_rows_total
-        hb = hf * union[0] * ROW_BYTES
-        cfg["hbm_part_GBs_in_gather"] = round((1 - hf) * union[0] * ROW_BYTES /
+        hb = launch_host_rows * ROW_BYTES
+        cfg["hbm_part_GBs_in_gather"] = round((launch_rows - launch_host_rows) * ROW_BYTES /
                                               (gather_ms * 1e-3) / 1e9, 1)
         res["roofline"] = roofline("attn_partial_mfma_kernel (sparse_decode_attn gather), "
                                    "host-resident rows", hb, gather_ms, bound="pcie",
-                                   peak=PCIE_PEAK_GBS, traffic=measured_traffic(which),
+                                   peak=PCIE_PEAK_GBS,
+                                   traffic=measured_traffic(which) if slices == w.slices else None,
                                    note="traffic counts every byte the kernel reads (HBM rows "
                                         "and host rows)")
     else:

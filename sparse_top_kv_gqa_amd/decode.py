@@ -28,6 +28,8 @@ from . import (attn_workspace_size, fused_index_topk_ok, sparse_decode_attn, spa
                sparse_decode_attn_union, attn_union_workspace_size, union_sets,
                lookahead_prefetch, TIERS_T2, t2_fetch, t2_locations, residency_append)
 
+from .streams import cu_partition_streams
+
 UNION_MIN_TOKENS = 16385   # wide rows: the union pipeline (narrower rows fit one workgroup)
 
 
@@ -145,12 +147,31 @@ class TokenSparseDecode:
     With wide rows and at most 4 selection sets per KV head (``union`` None = automatic) the
     step runs the union pipeline: the per-set top-k and the group's union in one call, then the
     attention over that union (no assembly).
+
+    slices > 1 splits the batch into that many runs of whole sequences and pipelines them over
+    two streams: the caller's stream scores and selects slice after slice, and a second stream
+    attends to each slice as soon as its selection is made, so the indexer (bound by HBM) of
+    slice i + 1 runs while the attention of slice i reads its host-resident rows (bound by
+    PCIe).  The buffers (scores, idx, count, out, lse) are the same full-batch tensors, each
+    slice working on its own rows of them.  Scores and selections are bit-identical to
+    slices = 1; each slice's attention is bit-identical to the slice run as a batch of its own,
+    and against slices = 1 it can differ in rounding, since a launch cuts a group's rows into
+    split-K workgroups by its own group count.  It pays where the attention's host reads are
+    long against the selection; with every row in HBM both phases share one bound and nothing
+    is gained.
+
+    attn_cus > 0 (with slices > 1) would also split the compute units: the attentions on a
+    stream limited to attn_cus CUs, the selections on one limited to the rest.  The attention's
+    workgroups stay resident for as long as their host reads take; on shared CUs they hold the
+    slots the indexer needs, and each phase runs slower beside the other than alone.  The
+    CU-partitioned streams are switched off for now (streams.cu_partition_streams raises).
     """
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, n_tokens: int, Hq: int, T: int, topk: int,
                  mode: str, sm_scale: Optional[float] = None,
                  index_keys: Optional[torch.Tensor] = None, k_host=None, v_host=None, loc=None,
-                 union: Optional[bool] = None):
+                 union: Optional[bool] = None, slices: int = 1, attn_cus: int = 0,
+                 _buffers=None):
         self.k, self.v = k, v
         self.index_keys = k if index_keys is None else index_keys
         self.k_host, self.v_host, self.loc = k_host, v_host, loc
@@ -161,12 +182,39 @@ class TokenSparseDecode:
         self.sm_scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
         dev = k.device
         Hs = Hq if mode == "token_per_head" else Hkv
-        self.scores = torch.empty((B, T, Hs, n_tokens), dtype=torch.float32, device=dev)
         kk = max(1, min(topk, n_tokens))
-        self.idx = torch.empty((B, T, Hs, kk), dtype=torch.int32, device=dev)
-        self.count = torch.empty((B, T, Hs), dtype=torch.int32, device=dev)
-        self.out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
-        self.lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+        if _buffers is not None:
+            self.scores, self.idx, self.count, self.out, self.lse = _buffers
+        else:
+            self.scores = torch.empty((B, T, Hs, n_tokens), dtype=torch.float32, device=dev)
+            self.idx = torch.empty((B, T, Hs, kk), dtype=torch.int32, device=dev)
+            self.count = torch.empty((B, T, Hs), dtype=torch.int32, device=dev)
+            self.out = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+            self.lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+        slices = max(1, min(int(slices), B))
+        self.parts = None
+        if slices > 1:
+            # runs of whole sequences, the last ones one longer when slices does not divide B
+            cuts = [b * B // slices for b in range(slices + 1)]
+            self.ranges = [(cuts[i], cuts[i + 1]) for i in range(slices)]
+            sl = lambda t, b0, b1: None if t is None else t[b0:b1]
+            self.parts = [
+                TokenSparseDecode(k[b0:b1], v[b0:b1], n_tokens, Hq, T, topk, mode, self.sm_scale,
+                                  self.index_keys[b0:b1], sl(k_host, b0, b1), sl(v_host, b0, b1),
+                                  sl(loc, b0, b1), union,
+                                  _buffers=(self.scores[b0:b1], self.idx[b0:b1],
+                                            self.count[b0:b1], self.out[b0:b1], self.lse[b0:b1]))
+                for b0, b1 in self.ranges]
+            self.union = self.parts[0].union
+            if attn_cus > 0:
+                self.select_stream, self.attn_stream = cu_partition_streams(attn_cus, dev)
+            else:
+                self.select_stream, self.attn_stream = None, torch.cuda.Stream(device=dev)
+            self.attn_cus = attn_cus
+            self._chosen = [torch.cuda.Event() for _ in self.parts]
+            self._called = torch.cuda.Event()
+            self._attended = torch.cuda.Event()
+            return
         S = union_sets(self.scope, T, Hq, Hkv)
         self.union = (S <= 4 and n_tokens >= UNION_MIN_TOKENS) if union is None else bool(union)
         if self.union:
@@ -185,13 +233,25 @@ class TokenSparseDecode:
             tws = topk_workspace_size(B * T * Hs, n_tokens, topk)
             self.topk_ws = torch.empty(max(tws, 1), dtype=torch.uint8, device=dev)
 
+    def _each(self, name: str, q: Optional[torch.Tensor], stream):
+        """The phase ``name`` of every slice in turn, on one stream (phase timings)."""
+        for p, (b0, b1) in zip(self.parts, self.ranges):
+            if q is None:
+                getattr(p, name)(stream)
+            else:
+                getattr(p, name)(q[b0:b1], stream)
+
     def index(self, q: torch.Tensor, stream=None):
         """The indexer's scores."""
+        if self.parts is not None:
+            return self._each("index", q, stream)
         sparse_index_score(self.mode, q, self.index_keys, self.n_tokens, scores=self.scores,
                            stream=stream)
 
     def select_topk(self, stream=None):
         """Top-k of the current scores (and, on the union pipeline, each group's union)."""
+        if self.parts is not None:
+            return self._each("select_topk", None, stream)
         if self.union:
             topk_select_union(self.scores, self.topk, self.scope, self.Hkv,
                               idx=self.idx, count=self.count, u_list=self.u_list,
@@ -206,6 +266,9 @@ class TokenSparseDecode:
         self.select_topk(stream)
 
     def attend(self, q: torch.Tensor, stream=None):
+        if self.parts is not None:
+            self._each("attend", q, stream)
+            return self.out, self.lse
         if self.union:
             sparse_decode_attn_union(q, self.k, self.v, self.u_list, self.u_mask, self.u_count,
                                      self.scope, self.n_tokens, sm_scale=self.sm_scale,
@@ -219,8 +282,30 @@ class TokenSparseDecode:
         return self.out, self.lse
 
     def step(self, q: torch.Tensor, stream=None):
-        self.select(q, stream)
-        return self.attend(q, stream)
+        if self.parts is None:
+            self.select(q, stream)
+            return self.attend(q, stream)
+        caller = torch.cuda.current_stream() if stream is None else stream
+        s0, s1 = self.select_stream, self.attn_stream
+        if s0 is None:
+            s0 = caller
+        else:
+            # the selection stream starts after everything queued on the caller's stream
+            self._called.record(caller)
+            s0.wait_event(self._called)
+        for p, (b0, b1), ev in zip(self.parts, self.ranges, self._chosen):
+            qi = q[b0:b1]
+            p.select(qi, s0)
+            # the attention stream starts slice i's attention once its selection is made (and,
+            # through the same event, after everything queued before it)
+            ev.record(s0)
+            s1.wait_event(ev)
+            p.attend(qi, s1)
+        # the caller's stream resumes after the last attention, which comes after the last
+        # selection: the next step's selection may then overwrite what the attentions read
+        self._attended.record(s1)
+        caller.wait_event(self._attended)
+        return self.out, self.lse
 
 
 class TieredDecode:

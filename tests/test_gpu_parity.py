@@ -518,16 +518,12 @@ def test_per_head_full_size_sampled():
     _free()
 
 
-def test_spec_verify_full_size_sampled_with_host_rows():
-    w = W.SPEC_VERIFY
-    say("spec-verify-full", w.name)
-    q = W.queries(w, device=DEV)
-    k = W.kv_cache(w, "k", device=DEV)
-    v = W.kv_cache(w, "v", device=DEV)
-    # as in the bench: a seeded 10% of every group's rows live in pinned host memory
+def _host_resident(w, k, v):
+    """A seeded host_frac of every group's rows in pinned host pools (as the bench lays them
+    out); the HBM copies of those rows are overwritten with NaN, so reading one shows."""
     n_host = int(round(w.host_frac * w.N))
     loc = torch.arange(w.N, dtype=torch.int32, device=DEV).repeat(w.B, w.Hkv, 1)
-    kh_pool = torch.empty((w.B, w.Hkv, n_host, w.d), dtype=torch.bfloat16, pin_memory=True)
+    kh_pool = torch.empty((w.B, w.Hkv, n_host, w.d), dtype=k.dtype, pin_memory=True)
     vh_pool = torch.empty_like(kh_pool).pin_memory()
     k_att, v_att = k.clone(), v.clone()
     for b in range(w.B):
@@ -536,14 +532,81 @@ def test_spec_verify_full_size_sampled_with_host_rows():
             kh_pool[b, h].copy_(k[b, h, rows].cpu())
             vh_pool[b, h].copy_(v[b, h, rows].cpu())
             loc[b, h, rows] = ~torch.arange(rows.numel(), dtype=torch.int32, device=DEV)
-            k_att[b, h, rows] = float("nan")      # HBM copies of host rows are never read
+            k_att[b, h, rows] = float("nan")
             v_att[b, h, rows] = float("nan")
+    return k_att, v_att, kh_pool, vh_pool, loc
+
+
+@pytest.mark.parametrize("attn_cus", [
+    0, pytest.param(64, marks=pytest.mark.skip(
+        reason="CU-partitioned streams are switched off: a bench process that used them ended "
+               "in a segmentation fault at exit, cause not found"))])
+@pytest.mark.parametrize("union", [True, False])
+@pytest.mark.parametrize("slices", [2, 3])
+def test_spec_verify_batch_slices(slices, union, attn_cus):
+    """The step pipelined over batch slices (selection on the caller's stream, attention on a
+    second one), with host-resident rows, over two consecutive steps; 5 sequences do not divide
+    into the slices evenly.  Scores and selections are those of the whole-batch step, bit for
+    bit; each slice's attention is, bit for bit, that of the slice run as a batch of its own
+    (a launch plans its split-K cut from its own group count, so against the whole-batch step
+    the attention agrees to the attention tolerance).  attn_cus > 0 runs the two streams on
+    disjoint CU sets, which changes nothing in the results."""
+    w = W.scaled(W.SPEC_VERIFY, B=5, Hkv=2, Hq=8, N=20000 + 5, k=700)
+    say("spec-verify-slices", slices, union, attn_cus, w.name)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    k_att, v_att, kh_pool, vh_pool, loc = _host_resident(w, k, v)
+    kw = dict(index_keys=k, k_host=kh_pool, v_host=vh_pool, loc=loc, union=union)
+    one = TokenSparseDecode(k_att, v_att, w.N, w.Hq, w.T, w.k, "token_group_mean", **kw)
+    sl = TokenSparseDecode(k_att, v_att, w.N, w.Hq, w.T, w.k, "token_group_mean", slices=slices,
+                           attn_cus=attn_cus, **kw)
+    assert (sl.select_stream is None) == (attn_cus == 0)
+    assert len(sl.parts) == slices and sl.union == one.union == union
+    assert [b1 - b0 for b0, b1 in sl.ranges] == [5 // slices + (i >= slices - 5 % slices)
+                                                 for i in range(slices)]
+    solo = [TokenSparseDecode(k_att[b0:b1], v_att[b0:b1], w.N, w.Hq, w.T, w.k, "token_group_mean",
+                              index_keys=k[b0:b1], k_host=kh_pool[b0:b1], v_host=vh_pool[b0:b1],
+                              loc=loc[b0:b1], union=union) for b0, b1 in sl.ranges]
+    stream = torch.cuda.Stream()
+    for step in range(2):
+        q = W.queries(w, step=step, device=DEV)
+        o1, l1 = one.step(q)
+        torch.cuda.synchronize()
+        o2, l2 = sl.step(q, stream=stream)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o2).all()
+        assert torch.equal(sl.scores, one.scores)
+        assert torch.equal(sl.count, one.count) and torch.equal(sl.idx, one.idx)
+        for (b0, b1), p in zip(sl.ranges, solo):
+            op, lp = p.step(q[b0:b1])
+            torch.cuda.synchronize()
+            assert torch.equal(o2[b0:b1], op) and torch.equal(l2[b0:b1], lp)
+        check_attn(o2.cpu().numpy(), o1.cpu().numpy(), what="sliced vs whole-batch attention")
+        check_rows(l2.cpu().numpy(), l1.cpu().numpy(), what="sliced vs whole-batch lse")
+
+
+def test_spec_verify_full_size_sampled_with_host_rows():
+    w = W.SPEC_VERIFY
+    say("spec-verify-full", w.name)
+    q = W.queries(w, device=DEV)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    # as in the bench: a seeded 10% of every group's rows live in pinned host memory, and the
+    # step runs over the bench's batch slices
+    k_att, v_att, kh_pool, vh_pool, loc = _host_resident(w, k, v)
     dec = TokenSparseDecode(k_att, v_att, w.N, w.Hq, w.T, w.k, "token_group_mean", index_keys=k,
-                            k_host=kh_pool, v_host=vh_pool, loc=loc)
-    out, lse = dec.step(q)
+                            k_host=kh_pool, v_host=vh_pool, loc=loc, slices=w.slices)
+    assert w.slices == 1 or len(dec.parts) == w.slices
+    out, lse = dec.step(q, stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
     out, lse = out.clone(), lse.clone()
-    # Proposition 1 at full size: the all-HBM run gives the same bits
-    ref_out, ref_lse = spk.sparse_decode_attn(q, k, v, dec.idx, dec.count, "per_kv_head", w.N)
+    # Proposition 1 at full size: the all-HBM attention over the same selections, launched per
+    # slice as the step launches it (the split-K cut follows the launch), gives the same bits
+    ref_out, ref_lse = torch.empty_like(out), torch.empty_like(lse)
+    for b0, b1 in (dec.ranges if dec.parts is not None else [(0, w.B)]):
+        o, l = spk.sparse_decode_attn(q[b0:b1], k[b0:b1], v[b0:b1], dec.idx[b0:b1],
+                                      dec.count[b0:b1], "per_kv_head", w.N)
+        ref_out[b0:b1], ref_lse[b0:b1] = o, l
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
     assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)

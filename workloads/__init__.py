@@ -49,6 +49,9 @@ class Workload:
     block_size   1 for token selection, else the pooling block
     n_sink, n_recent   always-kept rows
     window, stride     overlapping compression windows scored instead of whole blocks (0: none)
+    slices       runs of whole sequences the token decode step pipelines over two streams (the
+                 selection of one run beside the attention of the previous one); a schedule only,
+                 the results do not depend on it
     """
 
     name: str
@@ -77,6 +80,7 @@ class Workload:
     t01_permille: int = 750
     window: int = 0
     stride: int = 0
+    slices: int = 1
 
     @property
     def G(self) -> int:
