@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
       __syncthreads();
       return cw[NCW];
     };
-    // round 1: ties at the thresholds (evicted candidates hold ranks too)
+    // first sweep: ties at the thresholds (evicted candidates hold ranks too)
 #pragma unroll
     for (int c = 0; c < ITEMS; ++c) {
       const int i = c * kThreads + threadIdx.x;
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void tier_kernel(
     }
     prefixes(cw_eq);
     if (has_t2) prefixes(cw_eq2);
-    // round 2: tiers, evictions, and the per-(chunk, wave) counts of the list
+    // second sweep: tiers, evictions, and the per-(chunk, wave) counts of the list
     uint32_t selbits = 0;
 #pragma unroll
     for (int c = 0; c < ITEMS; ++c) {
