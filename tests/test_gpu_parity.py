@@ -585,6 +585,36 @@ def test_spec_verify_batch_slices(slices, union, attn_cus):
         check_rows(l2.cpu().numpy(), l1.cpu().numpy(), what="sliced vs whole-batch lse")
 
 
+@pytest.mark.parametrize("union", [True, False])
+def test_per_head_batch_slices(union):
+    """Per-head scope through the batch-slice runner: scores and selections equal the
+    whole-batch step's, each slice's attention equals that slice run as a batch of its own, bit
+    for bit, over two consecutive steps on a caller's stream."""
+    w = W.scaled(W.PER_HEAD_2PCT, B=3, Hkv=2, Hq=8, N=20000 + 5, k=700)
+    say("per-head-slices", union, w.name)
+    k = W.kv_cache(w, "k", device=DEV)
+    v = W.kv_cache(w, "v", device=DEV)
+    one = TokenSparseDecode(k, v, w.N, w.Hq, 1, w.k, "token_per_head", union=union)
+    sl = TokenSparseDecode(k, v, w.N, w.Hq, 1, w.k, "token_per_head", union=union, slices=2)
+    assert sl.ranges == [(0, 1), (1, 3)] and sl.union == union
+    solo = [TokenSparseDecode(k[b0:b1], v[b0:b1], w.N, w.Hq, 1, w.k, "token_per_head",
+                              union=union) for b0, b1 in sl.ranges]
+    stream = torch.cuda.Stream()
+    for step in range(2):
+        q = W.queries(w, step=step, device=DEV)
+        o1, l1 = one.step(q)
+        torch.cuda.synchronize()
+        o2, l2 = sl.step(q, stream=stream)
+        torch.cuda.synchronize()
+        assert torch.equal(sl.scores, one.scores)
+        assert torch.equal(sl.count, one.count) and torch.equal(sl.idx, one.idx)
+        for (b0, b1), p in zip(sl.ranges, solo):
+            op, lp = p.step(q[b0:b1])
+            torch.cuda.synchronize()
+            assert torch.equal(o2[b0:b1], op) and torch.equal(l2[b0:b1], lp)
+        check_attn(o2.cpu().numpy(), o1.cpu().numpy(), what="sliced vs whole-batch attention")
+
+
 def test_spec_verify_full_size_sampled_with_host_rows():
     w = W.SPEC_VERIFY
     say("spec-verify-full", w.name)
