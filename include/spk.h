@@ -314,8 +314,10 @@ SPK_API spk_status sparse_index_score_windowed(const void* pred, spk_dtype p_dty
  *   k, v       device caches, row (b,kvh,slot) at k + b*kv_sb + kvh*kv_sh + slot*kv_sn
  *              (same strides for v), slot < hbm_slots; kv_dtype F32 or BF16.  Without `loc`
  *              n_tokens <= hbm_slots is required.
- *   k_host, v_host  pinned host pools (hipHostMalloc'ed: page-locked and device-mapped; any
- *              other memory is rejected with SPK_EINVAL), row (b,kvh,slot) at
+ *   k_host, v_host  pinned host pools (hipHostMalloc'ed: page-locked and device-mapped).  The
+ *              library asks hipPointerGetAttributes and returns SPK_EINVAL unless HIP reports
+ *              host memory with a device address; that query is its only check, so pass no
+ *              other memory.  Row (b,kvh,slot) at
  *              k_host + b*host_sb + kvh*host_sh + slot*host_sn, slot < host_slots; NULL if unused.
  *   loc        device int32 or NULL.  loc[b*loc_sb + kvh*loc_sh + tok] >= 0: token tok is HBM
  *              slot loc (< hbm_slots); < 0: host slot ~loc (< host_slots; requires k_host and
@@ -452,7 +454,7 @@ SPK_API spk_status sparse_decode_attn_noalloc(const void* q, spk_dtype q_dtype,
  *              takes whole groups in turn, so more than B*Hkv add nothing
  * Run it on a stream of its own beside the attention of the layer before, and make the
  * attention that reads these rows wait for it.  Errors: SPK_EINVAL (sizes, strides, staging
- * range, pageable pools), SPK_EUNSUPPORTED (d, dtype).
+ * range, pools HIP does not report as device-mapped host memory), SPK_EUNSUPPORTED (d, dtype).
  * ---------------------------------------------------------------------------------------- */
 SPK_API spk_status lookahead_prefetch(const int32_t* sel_idx, const int32_t* sel_count,
                                       int64_t sel_ld, int block_size, int B, int Hkv, int d,
