@@ -510,6 +510,38 @@ def test_steps_with_everything_selected_equal_dense_attention():
     np.testing.assert_allclose(r["out"], dense, rtol=1e-11)
 
 
+def test_windowed_block_step_reduces_to_block_step_and_to_dense():
+    """steps.block_windowed_group against what the overlapping grid must reduce to: with the
+    window and the stride both the block size the windows are the blocks, so the step picks the
+    same blocks and tokens and gives the same scores and output as steps.block_group; with every
+    complete block kept (and the recent window reaching the first incomplete one) it is dense
+    attention over all rows.  A block's score at (32, 16) is the largest of the scores of the
+    windows sharing a token with it, computed here by brute force."""
+    d, bs = 16, 64
+    n = bs * 12 + 20
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    q = rng.standard_normal((4, d))
+    pred = rng.standard_normal(d)
+    scale = 0.25
+    a = steps.block_windowed_group(pred, k, v, q, 3, bs, bs, bs, 4, 100, scale)
+    b = steps.block_group(pred, k, v, q, 3, bs, 4, 100, scale)
+    assert a["blocks"].tolist() == b["blocks"].tolist()
+    assert a["tokens"].tolist() == b["tokens"].tolist()
+    np.testing.assert_allclose(a["scores"], b["scores"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-12)
+    everything = steps.block_windowed_group(pred, k, v, q, n // bs, bs, 32, 16, 0, 100, scale)
+    assert everything["tokens"].tolist() == list(range(n))
+    np.testing.assert_allclose(everything["out"], _dense(q, k, v, scale), rtol=1e-11)
+    w = steps.block_windowed_group(pred, k, v, q, 3, bs, 32, 16, 4, 100, scale)
+    nw = (n - 32) // 16 + 1
+    wsc = [float(pred @ k[16 * i:16 * i + 32].mean(axis=0)) for i in range(nw)]
+    for j in range(n // bs):
+        near = [wsc[i] for i in range(nw) if 16 * i < bs * (j + 1) and 16 * i + 32 > bs * j]
+        assert w["scores"][j] == pytest.approx(max(near), rel=1e-12, abs=1e-12)
+    assert len(w["blocks"]) == 3 and set(range(4)) <= set(w["tokens"].tolist())
+
+
 def test_block_step_forced_rows_and_counts():
     d, n, bs = 16, 64 * 20 + 10, 64
     k = rng.standard_normal((n, d))
