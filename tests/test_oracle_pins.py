@@ -542,6 +542,43 @@ def test_windowed_block_step_reduces_to_block_step_and_to_dense():
     assert len(w["blocks"]) == 3 and set(range(4)) <= set(w["tokens"].tolist())
 
 
+def test_token_steps_keep_each_token_and_head_on_its_own_set():
+    """The union is only the fetch unit: steps.group_mean_group over T draft tokens gives, token
+    by token, what it gives for that token alone, and steps.per_head_group, head by head, what
+    it gives for that head alone, while the sets differ (attending over the union would change
+    the outputs); each output is softmax attention over its own rows; the union is the set union
+    of the selections; and with identical heads the group-mean score is that head's own score
+    (a mean, not a sum) with the same selection."""
+    d, n, G, T, kk = 16, 300, 4, 3, 20
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    scale = 0.25
+    qt = rng.standard_normal((T, G, d))
+    r = steps.group_mean_group(qt, k, v, kk, scale)
+    for t in range(T):
+        one = steps.group_mean_group(qt[t:t + 1], k, v, kk, scale)
+        assert r["sel"][t].tolist() == one["sel"][0].tolist()
+        np.testing.assert_array_equal(r["out"][t], one["out"][0])
+        np.testing.assert_allclose(r["out"][t], _sdpa(qt[t], k[r["sel"][t]], v[r["sel"][t]], scale),
+                                   rtol=1e-11)
+    assert len(r["union"]) > kk
+    assert r["union"].tolist() == sorted(set(np.concatenate(r["sel"]).tolist()))
+    qh = rng.standard_normal((G, d))
+    p = steps.per_head_group(qh, k, v, kk, scale)
+    for h in range(G):
+        one = steps.per_head_group(qh[h:h + 1], k, v, kk, scale)
+        assert p["sel"][h].tolist() == one["sel"][0].tolist()
+        np.testing.assert_array_equal(p["out"][h], one["out"][0])
+        np.testing.assert_allclose(p["out"][h], _sdpa(qh[h:h + 1], k[p["sel"][h]], v[p["sel"][h]],
+                                                      scale)[0], rtol=1e-11)
+    assert len(p["union"]) > kk
+    same = np.repeat(qh[:1], G, axis=0)
+    gm = steps.group_mean_group(same[None], k, v, kk, scale)
+    ph = steps.per_head_group(qh[:1], k, v, kk, scale)
+    np.testing.assert_allclose(gm["scores"][0], ph["scores"][0], rtol=1e-12, atol=1e-12)
+    assert gm["sel"][0].tolist() == ph["sel"][0].tolist()
+
+
 def test_block_step_forced_rows_and_counts():
     d, n, bs = 16, 64 * 20 + 10, 64
     k = rng.standard_normal((n, d))
