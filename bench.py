@@ -255,13 +255,60 @@ def stream_ceiling_gbs(nbytes, stream, reps=12):
     return round(best, 1)
 
 
+def host_read_ceiling_gbs(nbytes, stream, reps=6, cap=256 << 20):
+    """Host-link read ceiling at this size (at most `cap` bytes): the best median rate of the
+    library's streaming read of pinned host memory (spk_stream_read_host, the device address of
+    the pinned buffer, as the attention reads host-resident rows) across workgroup counts."""
+    import ctypes
+    import sparse_top_kv_gqa_amd as spk
+    hip = _hip()
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = (min(int(nbytes), cap) + 15) // 16 * 16
+    if nbytes <= 0:
+        return None
+    buf = torch.zeros(nbytes, dtype=torch.uint8, pin_memory=True)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    best = 0.0
+    for wgs in (256, 1024, 4096):
+        pairs = []
+        for _ in range(reps):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if (hip.hipEventCreateWithFlags(ctypes.byref(a), HIP_EVENT_DISABLE_SYSTEM_FENCE) or
+                    hip.hipEventCreateWithFlags(ctypes.byref(b), HIP_EVENT_DISABLE_SYSTEM_FENCE)):
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            pairs.append((a, b))
+        spk.stream_read_host(buf, wgs, sink, stream)             # lead-in: the host runs ahead
+        for a, b in pairs:
+            hip.hipEventRecord(a, sh)
+            spk.stream_read_host(buf, wgs, sink, stream)
+            hip.hipEventRecord(b, sh)
+        torch.cuda.synchronize()
+        t = []
+        for a, b in pairs:
+            f = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(f), a, b):
+                raise RuntimeError("hipEventElapsedTime failed")
+            t.append(f.value)
+            hip.hipEventDestroy(a)
+            hip.hipEventDestroy(b)
+        t.sort()
+        best = max(best, nbytes / (t[len(t) // 2] * 1e-3) / 1e9)
+    del buf
+    return round(best, 1)
+
+
 def with_ceiling(roof, stream):
-    """Adds the measured HBM read ceiling at the roofline kernel's byte count to an HBM-bound
-    roofline record."""
+    """Adds the measured read ceiling at the roofline kernel's byte count: HBM for an HBM-bound
+    roofline record, the host link (pinned host memory read by a kernel) for a PCIe-bound one."""
     if roof.get("bound") == "hbm":
         c = stream_ceiling_gbs(roof["algorithmic_bytes_per_launch"], stream)
         roof["stream_read_ceiling_GBs"] = c
         roof["frac_of_stream_ceiling"] = round(roof["achieved"] / c, 4) if c > 0 else None
+    elif roof.get("bound") == "pcie":
+        c = host_read_ceiling_gbs(roof["algorithmic_bytes_per_launch"], stream)
+        roof["host_read_ceiling_GBs"] = c
+        roof["frac_of_host_read_ceiling"] = round(roof["achieved"] / c, 4) if c else None
     return roof
 
 
@@ -1313,7 +1360,7 @@ def run_workload(name, args):
     else:
         res, ctx = bench_tiers(args)
         cpu = cpu_tiers
-    log(f"{name}: measuring the HBM read ceiling at the roofline kernel's size")
+    log(f"{name}: measuring the read ceiling at the roofline kernel's size")
     res["roofline"] = with_ceiling(res["roofline"], torch.cuda.Stream())
     if not args.no_cpu_baseline:
         log(f"{name}: timing the CPU oracle")

@@ -108,6 +108,17 @@ SPK_API spk_status spk_set_attn_timing_events(void* begin, void* end);
 SPK_API spk_status spk_stream_read(const void* p, size_t bytes, int workgroups, uint32_t* sink,
                                    void* stream);
 
+/* Measurement reference: spk_stream_read of `bytes` bytes of pinned host memory at `host` (from
+ * hipHostMalloc: page-locked and device-mapped), read through the device address HIP reports for
+ * it, as the attention reads host-resident rows.  Its rate is the ceiling of kernel reads over
+ * the host link, reported beside the link's nominal rate.  The library asks
+ * hipPointerGetAttributes and returns SPK_EINVAL unless HIP reports host memory with a device
+ * address; that query is its only check, so pass no other memory.  The caller guarantees that
+ * [host, host + bytes) lies inside one allocation.  `sink`, errors and bytes = 0 as
+ * spk_stream_read (bytes = 0 launches nothing and queries nothing). */
+SPK_API spk_status spk_stream_read_host(const void* host, size_t bytes, int workgroups,
+                                        uint32_t* sink, void* stream);
+
 /* Measurement reference: reads the K and V rows named by per-group row lists, each listed row
  * once, and computes nothing of the method.  Its rate is the HBM rate a plain gather of exactly
  * that set of rows reaches on the device at hand (the rows of a sparse selection are scattered,

@@ -37,7 +37,7 @@ EXPORTS = ("spk_last_error", "spk_version", "sparse_index_score", "topk_select_w
            "spk_set_attn_timing_events", "sparse_index_topk",
            "sparse_topk_decode_attn_workspace_size", "sparse_topk_decode_attn",
            "sparse_window_pool", "sparse_index_score_windowed", "residency_update",
-           "residency_prefetch", "spk_stream_read", "spk_gather_read",
+           "residency_prefetch", "spk_stream_read", "spk_stream_read_host", "spk_gather_read",
            "sparse_decode_attn_noalloc", "sparse_decode_attn_noalloc_max_bytes",
            "topk_select_union_workspace_size", "topk_select_union",
            "sparse_decode_attn_union_workspace_size", "sparse_decode_attn_union",
@@ -113,6 +113,8 @@ def lib() -> ctypes.CDLL:
     L.spk_set_attn_timing_events.argtypes = [P, P]
     L.spk_stream_read.restype = I
     L.spk_stream_read.argtypes = [P, SZ, I, P, P]
+    L.spk_stream_read_host.restype = I
+    L.spk_stream_read_host.argtypes = [P, SZ, I, P, P]
     L.spk_gather_read.restype = I
     L.spk_gather_read.argtypes = [P, P, I64, I64, I64, I64, P, I64, I, I, P, P]
     L.sparse_topk_decode_attn_workspace_size.restype = I
@@ -847,6 +849,17 @@ def stream_read(buf: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=N
         raise ValueError("stream_read: buf and sink must be device tensors")
     _check(lib().spk_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(workgroups),
                                  _ptr(sink), _stream(stream)), "spk_stream_read")
+
+
+def stream_read_host(buf: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=None):
+    """Measurement reference: a plain streaming read of the whole pinned host tensor ``buf``
+    over the host link, split into ``workgroups`` chunks (``sink`` as in stream_read)."""
+    _contig(buf, "buf")
+    if not _is_pinned(buf) or not sink.is_cuda:
+        raise ValueError("stream_read_host: buf must be a pinned host tensor, sink a device tensor")
+    _check(lib().spk_stream_read_host(_ptr(buf), buf.numel() * buf.element_size(),
+                                      int(workgroups), _ptr(sink), _stream(stream)),
+           "spk_stream_read_host")
 
 
 def gather_read(k: torch.Tensor, v: torch.Tensor, rows: torch.Tensor, wg_per_group: int,

@@ -124,6 +124,37 @@ extern "C" SPK_API spk_status spk_gather_read(const void* k, const void* v, int6
   return check_launch("spk_gather_read");
 }
 
+extern "C" SPK_API spk_status spk_stream_read_host(const void* host, size_t bytes, int workgroups,
+                                                   uint32_t* sink, void* stream) {
+  using namespace spk;
+  SPK_REQUIRE(host && sink, SPK_EINVAL, "spk_stream_read_host: null buffer or sink");
+  SPK_REQUIRE(reinterpret_cast<uintptr_t>(host) % 16 == 0 && bytes % 16 == 0, SPK_EINVAL,
+              "spk_stream_read_host: buffer and size must be multiples of 16 bytes");
+  SPK_REQUIRE(workgroups >= 1 && workgroups <= (1 << 20), SPK_EINVAL,
+              "spk_stream_read_host: workgroups %d not in [1, 2^20]", workgroups);
+  clear_error();
+  if (bytes == 0) return SPK_OK;
+  // the caller states that this is host memory; it is read through the device address HIP
+  // reports for it, and only memory HIP reports as host memory with such an address is taken
+  // (the check of the attention's host pools)
+  hipPointerAttribute_t at{};
+  const hipError_t e = hipPointerGetAttributes(&at, host);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(SPK_EINVAL, "spk_stream_read_host: the buffer is not memory known to HIP (%s)",
+                     hipGetErrorString(e));
+  }
+  SPK_REQUIRE(at.type == hipMemoryTypeHost && at.devicePointer != nullptr, SPK_EINVAL,
+              "spk_stream_read_host: the buffer must be pinned, device-mapped host memory");
+  const uint64_t n16 = bytes / 16;
+  const uint64_t per = (n16 + workgroups - 1) / workgroups;
+  const int wgs = (int)((n16 + per - 1) / per);
+  hipLaunchKernelGGL(stream_read_kernel, dim3(wgs), dim3(kThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<const uint4*>(at.devicePointer), n16, per, sink);
+  return check_launch("spk_stream_read_host");
+}
+
 extern "C" SPK_API spk_status spk_stream_read(const void* p, size_t bytes, int workgroups,
                                               uint32_t* sink, void* stream) {
   using namespace spk;

@@ -187,6 +187,21 @@ def test_timing_hook_validation():
     assert L.spk_set_attn_timing_events(None, None) == 0
 
 
+def test_stream_read_host_validation():
+    """The host streaming read refuses bad arguments before touching HIP: null buffer or sink,
+    unaligned pointer or size, workgroups out of range; zero bytes is a no-op."""
+    L = spk.lib()
+    assert L.spk_stream_read_host(None, 1024, 8, A, None) == 1
+    assert "null" in _err()
+    assert L.spk_stream_read_host(A, 1024, 8, None, None) == 1
+    assert L.spk_stream_read_host(ctypes.c_void_p(0x100004), 1024, 8, A, None) == 1
+    assert L.spk_stream_read_host(A, 1000, 8, A, None) == 1
+    assert L.spk_stream_read_host(A, 1024, 0, A, None) == 1
+    assert L.spk_stream_read_host(A, 1024, (1 << 20) + 1, A, None) == 1
+    assert "workgroups" in _err()
+    assert L.spk_stream_read_host(A, 0, 8, A, None) == 0      # nothing to read: no query, no launch
+
+
 def test_stream_read_validation():
     L = spk.lib()
     assert L.spk_stream_read(None, 1024, 8, A, None) == 1

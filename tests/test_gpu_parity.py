@@ -1878,6 +1878,26 @@ def test_stream_read_reference_reads_every_word():
     assert int(sink.item()) & 0xFFFFFFFF == 0x9E3779B9
 
 
+def test_stream_read_host_reference_reads_pinned_memory():
+    """The host streaming read reads pinned host memory through its device address in any
+    chunking (ragged tail included): the sink stays untouched for zeros and takes the constant
+    from a word planted in the host buffer.  The binding hands it nothing but pinned tensors."""
+    say("stream-read-host-pinned")
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    words = torch.zeros(4 * 1024 + 4, dtype=torch.int32, pin_memory=True)
+    for wgs in (1, 5, 1000):
+        spk.stream_read_host(words, wgs, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    words[-1] = 0x9E3779B9 - (1 << 32)                  # the last word of the last chunk
+    spk.stream_read_host(words, 3, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) & 0xFFFFFFFF == 0x9E3779B9
+    for bad in (torch.zeros(64, dtype=torch.int32), torch.zeros(64, dtype=torch.int32, device=DEV)):
+        with pytest.raises(ValueError, match="pinned"):
+            spk.stream_read_host(bad, 1, sink)
+
+
 @pytest.mark.skip(reason="taken out: a streaming read of host memory chose device or host by "
                          "hipPointerGetAttributes, and a call on a pageable buffer that was "
                          "meant to be refused launched and faulted the GPU")
