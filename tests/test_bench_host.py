@@ -1,5 +1,6 @@
 """Host-side bookkeeping of bench.py: the fetch lists the gather reference reads must be exactly
-the rows the block attention reads (sinks, recent window and the selected blocks, each once)."""
+the rows the block attention reads (sinks, recent window and the selected blocks, each once);
+the union sizes read only counted entries; a request for more than one GPU is refused."""
 import os
 import sys
 
@@ -69,3 +70,13 @@ def test_union_rows_read_only_counted_entries_in_range():
     want = [len(set(bad[b, 0, h * G:(h + 1) * G, 1:].reshape(-1).tolist()))
             for b in range(B) for h in range(Hs // G)]
     assert got == want
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """bench.py --gpus N with N > 1 exits with status 2 and says why, before touching a GPU."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
