@@ -390,7 +390,7 @@ TRAFFIC = {
     "per_head": (('index_score.hip', 'spk_internal.h', 'select_common.h'), "b5e7d593716d4c9d", 524470.5, 65536.0),
     "block": (('attn.hip', 'spk_internal.h', 'select_common.h'), "618b9af45143852f", 41685.54, 1442.0),
     "block_windowed": (('attn.hip', 'spk_internal.h', 'select_common.h'), "618b9af45143852f", 41823.41, 1442.01),
-    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "618b9af45143852f", 272556.59, 8544.83),
+    "spec_verify": (('attn.hip', 'spk_internal.h', 'select_common.h'), "618b9af45143852f", 272558.97, 8544.51),
     "tiers": (('attn.hip', 'spk_internal.h', 'select_common.h'), "618b9af45143852f", 401309.22, 51551.92),
 }
 
